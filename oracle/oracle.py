@@ -1,0 +1,126 @@
+"""fp64 primal TTT oracle (ctypes wrapper around ``ttt_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, by the smoke check and
+by the CPU-baseline leg of the benchmark, never by the product path.  It shares
+no code with the HIP kernels.
+
+The C file computes the sequential primal mini-batch TTT forward of
+"论文速览 | TTT" (equinox-blog close reading of "Learning to (Learn at Test
+Time)"): §3.1 (update, then output), §3.3 (multi-view loss
+||f(k;W) - v||^2, output f(q; W_t)), §3.5 (mini-batch gradient point),
+§4.4 (TTT-Linear f = Wx, TTT-MLP f = W2 GELU(W1 x)), §4.6 (per-token eta).
+
+Parity pins live in ``tests/test_oracle_pins.py``; the only function here with
+no pin from the pages is the GELU form (exact erf), see the module docstring
+there.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ttt_oracle.c")
+_LIB = os.path.join(_HERE, "libttt_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+CFLAGS = ["-O2", "-ffp-contract=off", "-fPIC", "-shared", "-pthread", "-std=c99"]
+
+
+def build(src: str = _SRC, out: str = _LIB, extra_flags=()) -> str:
+    """Compile the oracle C file into a shared library with gcc."""
+    cmd = ["gcc", *CFLAGS, *extra_flags, src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    dp = ctypes.POINTER(ctypes.c_double)
+    L, I = ctypes.c_long, ctypes.c_int
+    lib.ttt_oracle_linear.argtypes = [dp, dp, dp, dp, dp, I, L, L, L, L, L, dp, dp, I]
+    lib.ttt_oracle_linear.restype = I
+    lib.ttt_oracle_mlp.argtypes = [dp, dp, dp, dp, dp, dp, I, L, L, L, L, L, L, dp, dp, dp, I]
+    lib.ttt_oracle_mlp.restype = I
+    return lib
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load the oracle library (building it first if it is absent or stale)."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    with _lock:
+        if _lib is None:
+            if (not os.path.exists(_LIB)) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+            _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def linear(q, k, v, eta, w0, b: int, nthreads: int | None = None, lib=None):
+    """TTT-Linear primal forward.
+
+    q, k, v: [B, H, T, d]; eta: [B, H, T]; w0: [H, d, d] (shared over the
+    batch) or [B, H, d, d] (one initial state per unit).
+    Returns (z [B, H, T, d], w_T [B, H, d, d]) in float64.
+    """
+    q, k, v, eta, w0 = map(_f64, (q, k, v, eta, w0))
+    B, H, T, d = q.shape
+    assert k.shape == q.shape and v.shape == q.shape and eta.shape == (B, H, T)
+    per_batch = 1 if w0.ndim == 4 else 0
+    assert w0.shape == ((B, H, d, d) if per_batch else (H, d, d))
+    z = np.zeros((B, H, T, d))
+    w_out = np.zeros((B, H, d, d))
+    lib = lib or load()
+    rc = lib.ttt_oracle_linear(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w0), per_batch,
+                               B, H, T, d, int(b), _ptr(z), _ptr(w_out),
+                               nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"ttt_oracle_linear failed with status {rc}")
+    return z, w_out
+
+
+def mlp(q, k, v, eta, w1_0, w2_0, b: int, nthreads: int | None = None, lib=None):
+    """TTT-MLP primal forward, f(x) = W2 GELU(W1 x).
+
+    w1_0: [H, hidden, d] or [B, H, hidden, d]; w2_0: [H, d, hidden] or
+    [B, H, d, hidden].  Returns (z, w1_T, w2_T) in float64.
+    """
+    q, k, v, eta, w1_0, w2_0 = map(_f64, (q, k, v, eta, w1_0, w2_0))
+    B, H, T, d = q.shape
+    per_batch = 1 if w1_0.ndim == 4 else 0
+    hidden = w1_0.shape[-2]
+    assert w1_0.shape == ((B, H, hidden, d) if per_batch else (H, hidden, d))
+    assert w2_0.shape == ((B, H, d, hidden) if per_batch else (H, d, hidden))
+    z = np.zeros((B, H, T, d))
+    w1 = np.zeros((B, H, hidden, d))
+    w2 = np.zeros((B, H, d, hidden))
+    lib = lib or load()
+    rc = lib.ttt_oracle_mlp(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w1_0), _ptr(w2_0),
+                            per_batch, B, H, T, d, hidden, int(b), _ptr(z), _ptr(w1), _ptr(w2),
+                            nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"ttt_oracle_mlp failed with status {rc}")
+    return z, w1, w2

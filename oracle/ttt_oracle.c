@@ -1,0 +1,254 @@
+/*
+ * TTT forward-scan oracle: plain, slow, sequential fp64 PRIMAL form.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark do.  It shares no code, header, table or helper with
+ * the HIP kernels.
+ *
+ * What it computes (sources: "论文速览 | TTT", the equinox-blog close reading
+ * of "Learning to (Learn at Test Time): RNNs with Expressive Hidden States"):
+ *
+ *  - §3.1 Naive TTT: the state is the parameter set W of an inner model f;
+ *    each token first takes a gradient step on its own loss and the output is
+ *    then read from the UPDATED state:  W_t = W_{t-1} - eta * grad l(W_?; x_t),
+ *    z_t = f(x_t; W_t).
+ *  - §3.3 Multi-view reconstruction: l(W; x_t) = || f(k_t; W) - v_t ||^2 and
+ *    z_t = f(q_t; W_t), with k, v, q the training, label and test views.  The
+ *    views arrive already projected, so k_t, v_t, q_t are inputs here.
+ *  - §3.5 Mini-batch GD: the sequence is cut into mini-batches of b tokens;
+ *    every token of a mini-batch takes its gradient at W_{t'}, the state at
+ *    the last position before that mini-batch, while the updates still
+ *    accumulate token by token: W_t = W_{t-1} - eta_t * G_t.
+ *  - §4.6 Learnable inner learning rate: eta depends on the token, so eta_t
+ *    is a per-token input that scales token t's own gradient (no 1/b).
+ *  - §4.4 Inner models: TTT-Linear f(x) = W x; TTT-MLP f(x) = W2 GELU(W1 x)
+ *    with a hidden width that the caller chooses (4x the input on the page).
+ *    The LayerNorm + residual wrapper of §4.4 is not part of this oracle.
+ *
+ * The loss is the squared L2 norm summed over output components, so its
+ * gradient carries the factor 2 (§3.6 linear derivation: G_t = 2(W0 x - x)x^T).
+ * GELU is the exact erf form x * Phi(x).  Mini-batches start at token 0, b,
+ * 2b, ...; a final partial mini-batch is simply shorter.
+ *
+ * Layouts (row-major, contiguous):
+ *   q, k, v : [B][H][T][d]        eta : [B][H][T]
+ *   Linear  : w0 [H][d][d] (w0_per_batch = 0) or [B][H][d][d] (= 1),
+ *             W[i][j] with i the output index, f(x)_i = sum_j W[i][j] x_j
+ *   MLP     : w1 [.][hidden][d], w2 [.][d][hidden] (same per-batch rule)
+ *   z       : [B][H][T][d]        state outputs : [B][H][...]
+ *
+ * Build: gcc -O2 -ffp-contract=off -fPIC -shared -pthread (no fused
+ * multiply-add contraction, so every product is rounded as written).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* TTT-Linear: one (batch, head) unit, primal mini-batch GD.           */
+/* ------------------------------------------------------------------ */
+static void linear_unit(const double *q, const double *k, const double *v,
+                        const double *eta, const double *w0, long T, long d,
+                        long b, double *z, double *w_out, double *Ws,
+                        double *g) {
+  double *W = w_out; /* the running state lives directly in the output */
+  memcpy(W, w0, sizeof(double) * (size_t)(d * d));
+  for (long m0 = 0; m0 < T; m0 += b) {
+    long m1 = m0 + b < T ? m0 + b : T;
+    /* gradient point W_{t'}: the state before this mini-batch (§3.5) */
+    memcpy(Ws, W, sizeof(double) * (size_t)(d * d));
+    for (long t = m0; t < m1; ++t) {
+      const double *kt = k + t * d, *vt = v + t * d, *qt = q + t * d;
+      const double et = eta[t];
+      /* G_t = 2 (Ws k_t - v_t) k_t^T ; keep the vector factor g */
+      for (long i = 0; i < d; ++i) {
+        double s = 0.0;
+        for (long j = 0; j < d; ++j) s += Ws[i * d + j] * kt[j];
+        g[i] = 2.0 * (s - vt[i]);
+      }
+      /* W_t = W_{t-1} - eta_t G_t */
+      for (long i = 0; i < d; ++i)
+        for (long j = 0; j < d; ++j) W[i * d + j] -= et * g[i] * kt[j];
+      /* z_t = f(q_t; W_t): output after the update (§3.1) */
+      for (long i = 0; i < d; ++i) {
+        double s = 0.0;
+        for (long j = 0; j < d; ++j) s += W[i * d + j] * qt[j];
+        z[t * d + i] = s;
+      }
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* TTT-MLP: f(x) = W2 GELU(W1 x), one unit, primal mini-batch GD.      */
+/* ------------------------------------------------------------------ */
+static double gelu(double x) { return 0.5 * x * (1.0 + erf(x / sqrt(2.0))); }
+
+/* d/dx [x Phi(x)] = Phi(x) + x phi(x) */
+static double gelu_grad(double x) {
+  const double pi = 3.14159265358979323846;
+  return 0.5 * (1.0 + erf(x / sqrt(2.0))) + x * exp(-0.5 * x * x) / sqrt(2.0 * pi);
+}
+
+typedef struct {
+  double *W1s, *W2s, *a, *x, *e, *delta, *hq;
+} mlp_scratch;
+
+static void mlp_unit(const double *q, const double *k, const double *v,
+                     const double *eta, const double *w1_0, const double *w2_0,
+                     long T, long d, long hd, long b, double *z, double *W1,
+                     double *W2, mlp_scratch *s) {
+  memcpy(W1, w1_0, sizeof(double) * (size_t)(hd * d));
+  memcpy(W2, w2_0, sizeof(double) * (size_t)(d * hd));
+  for (long m0 = 0; m0 < T; m0 += b) {
+    long m1 = m0 + b < T ? m0 + b : T;
+    memcpy(s->W1s, W1, sizeof(double) * (size_t)(hd * d));
+    memcpy(s->W2s, W2, sizeof(double) * (size_t)(d * hd));
+    for (long t = m0; t < m1; ++t) {
+      const double *kt = k + t * d, *vt = v + t * d, *qt = q + t * d;
+      const double et = eta[t];
+      /* forward at the gradient point: a = W1s k, x = GELU(a), y = W2s x */
+      for (long u = 0; u < hd; ++u) {
+        double acc = 0.0;
+        for (long j = 0; j < d; ++j) acc += s->W1s[u * d + j] * kt[j];
+        s->a[u] = acc;
+        s->x[u] = gelu(acc);
+      }
+      /* dl/dy = 2 (y - v) */
+      for (long i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (long u = 0; u < hd; ++u) acc += s->W2s[i * hd + u] * s->x[u];
+        s->e[i] = 2.0 * (acc - vt[i]);
+      }
+      /* dl/dW2 = e x^T ; dl/da = (W2s^T e) * GELU'(a) ; dl/dW1 = delta k^T */
+      for (long u = 0; u < hd; ++u) {
+        double acc = 0.0;
+        for (long i = 0; i < d; ++i) acc += s->W2s[i * hd + u] * s->e[i];
+        s->delta[u] = acc * gelu_grad(s->a[u]);
+      }
+      for (long i = 0; i < d; ++i)
+        for (long u = 0; u < hd; ++u) W2[i * hd + u] -= et * s->e[i] * s->x[u];
+      for (long u = 0; u < hd; ++u)
+        for (long j = 0; j < d; ++j) W1[u * d + j] -= et * s->delta[u] * kt[j];
+      /* z_t = W2_t GELU(W1_t q_t) with the updated state */
+      for (long u = 0; u < hd; ++u) {
+        double acc = 0.0;
+        for (long j = 0; j < d; ++j) acc += W1[u * d + j] * qt[j];
+        s->hq[u] = gelu(acc);
+      }
+      for (long i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (long u = 0; u < hd; ++u) acc += W2[i * hd + u] * s->hq[u];
+        z[t * d + i] = acc;
+      }
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* Threading: units (batch, head) are independent; static round robin. */
+/* ------------------------------------------------------------------ */
+typedef struct {
+  int kind; /* 0 linear, 1 mlp */
+  const double *q, *k, *v, *eta, *w0a, *w0b;
+  int w0_per_batch;
+  long B, H, T, d, hd, b;
+  double *z, *outa, *outb;
+  int tid, nthreads, status;
+} job;
+
+static void *worker(void *arg) {
+  job *jb = (job *)arg;
+  const long d = jb->d, hd = jb->hd, T = jb->T;
+  const long units = jb->B * jb->H;
+  double *buf = NULL;
+  size_t need = jb->kind == 0 ? (size_t)(d * d + d)
+                              : (size_t)(2 * hd * d + 4 * hd + d);
+  buf = (double *)malloc(sizeof(double) * need);
+  if (!buf) { jb->status = 1; return NULL; }
+  for (long u = jb->tid; u < units; u += jb->nthreads) {
+    long hh = u % jb->H;
+    long wsel = jb->w0_per_batch ? u : hh;
+    const double *qu = jb->q + u * T * d, *ku = jb->k + u * T * d,
+                 *vu = jb->v + u * T * d, *eu = jb->eta + u * T;
+    double *zu = jb->z + u * T * d;
+    if (jb->kind == 0) {
+      linear_unit(qu, ku, vu, eu, jb->w0a + wsel * d * d, T, d, jb->b, zu,
+                  jb->outa + u * d * d, buf, buf + d * d);
+    } else {
+      mlp_scratch s;
+      s.W1s = buf;
+      s.W2s = buf + hd * d;
+      s.a = buf + 2 * hd * d;
+      s.x = s.a + hd;
+      s.delta = s.x + hd;
+      s.hq = s.delta + hd;
+      s.e = s.hq + hd;
+      mlp_unit(qu, ku, vu, eu, jb->w0a + wsel * hd * d, jb->w0b + wsel * d * hd,
+               T, d, hd, jb->b, zu, jb->outa + u * hd * d, jb->outb + u * d * hd,
+               &s);
+    }
+  }
+  free(buf);
+  return NULL;
+}
+
+static int run(job proto, int nthreads) {
+  if (proto.B < 0 || proto.H < 0 || proto.T < 0 || proto.d <= 0 || proto.b <= 0)
+    return 2;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  job *jobs = (job *)calloc((size_t)nthreads, sizeof(job));
+  pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+  if (!jobs || !th) { free(jobs); free(th); return 1; }
+  int rc = 0;
+  for (int i = 0; i < nthreads; ++i) {
+    jobs[i] = proto;
+    jobs[i].tid = i;
+    jobs[i].nthreads = nthreads;
+    jobs[i].status = 0;
+  }
+  for (int i = 1; i < nthreads; ++i)
+    if (pthread_create(&th[i], NULL, worker, &jobs[i]) != 0) { jobs[i].status = 3; th[i] = 0; }
+  worker(&jobs[0]);
+  for (int i = 1; i < nthreads; ++i) {
+    if (jobs[i].status == 3) {
+      worker(&jobs[i]); /* thread creation failed: run its share inline */
+      jobs[i].status = 0;
+    } else {
+      pthread_join(th[i], NULL);
+    }
+  }
+  for (int i = 0; i < nthreads; ++i) rc |= jobs[i].status;
+  free(jobs);
+  free(th);
+  return rc;
+}
+
+int ttt_oracle_linear(const double *q, const double *k, const double *v,
+                      const double *eta, const double *w0, int w0_per_batch,
+                      long B, long H, long T, long d, long b, double *z,
+                      double *w_out, int nthreads) {
+  job p;
+  memset(&p, 0, sizeof p);
+  p.kind = 0; p.q = q; p.k = k; p.v = v; p.eta = eta; p.w0a = w0;
+  p.w0_per_batch = w0_per_batch; p.B = B; p.H = H; p.T = T; p.d = d; p.hd = 0;
+  p.b = b; p.z = z; p.outa = w_out;
+  return run(p, nthreads);
+}
+
+int ttt_oracle_mlp(const double *q, const double *k, const double *v,
+                   const double *eta, const double *w1_0, const double *w2_0,
+                   int w0_per_batch, long B, long H, long T, long d, long hidden,
+                   long b, double *z, double *w1_out, double *w2_out,
+                   int nthreads) {
+  if (hidden <= 0) return 2;
+  job p;
+  memset(&p, 0, sizeof p);
+  p.kind = 1; p.q = q; p.k = k; p.v = v; p.eta = eta; p.w0a = w1_0; p.w0b = w2_0;
+  p.w0_per_batch = w0_per_batch; p.B = B; p.H = H; p.T = T; p.d = d; p.hd = hidden;
+  p.b = b; p.z = z; p.outa = w1_out; p.outb = w2_out;
+  return run(p, nthreads);
+}

@@ -1,0 +1,96 @@
+"""Dual-form TTT in float64 numpy: an independent formulation used to pin the
+primal oracle (test helper, not collected by pytest).
+
+Follows "论文速览 | TTT" (equinox-blog), §3.6 (dual form for f = Wx:
+W_b = W0 - 2 eta (W0 X - X) X^T, Delta = (W0 X - X) mask(X^T X),
+Z = W0 X - 2 eta Delta, with X split into the K / V / Q views of §3.3) and
+§3.7 (dual form for MLPs: gradients of the whole mini-batch at the starting
+weights, outputs through a causal mask(A^T Q) per layer), with the scalar eta
+generalised to the per-token eta_t of §4.6 (column t of the gradient matrix
+is scaled by eta_t).  Matrices have tokens as columns (d x b), as on the page.
+The causal mask keeps s <= t (the inclusive diagonal: token t's output sees
+its own update, §3.1).
+"""
+from __future__ import annotations
+
+import numpy as np
+from scipy.special import erf
+
+
+def gelu(x):
+    return 0.5 * x * (1.0 + erf(x / np.sqrt(2.0)))
+
+
+def gelu_grad(x):
+    return 0.5 * (1.0 + erf(x / np.sqrt(2.0))) + x * np.exp(-0.5 * x * x) / np.sqrt(2.0 * np.pi)
+
+
+def linear_unit(q, k, v, eta, w0, b):
+    """One unit: q, k, v [T, d], eta [T], w0 [d, d] -> (z [T, d], W_T)."""
+    T, d = q.shape
+    W = np.array(w0, dtype=np.float64)
+    Z = np.zeros((T, d))
+    for m0 in range(0, T, b):
+        m1 = min(T, m0 + b)
+        XK, XV, XQ = k[m0:m1].T, v[m0:m1].T, q[m0:m1].T
+        e = eta[m0:m1]
+        G = 2.0 * (W @ XK - XV) * e[None, :]  # eta_t * dl_t/d(W x) per column
+        mask = np.triu(XK.T @ XQ)  # (s, t) kept for s <= t
+        Z[m0:m1] = (W @ XQ - G @ mask).T
+        W = W - G @ XK.T
+    return Z, W
+
+
+def mlp_unit(q, k, v, eta, w1, w2, b):
+    """One unit of TTT-MLP, f(x) = W2 GELU(W1 x)."""
+    T, d = q.shape
+    W1 = np.array(w1, dtype=np.float64)
+    W2 = np.array(w2, dtype=np.float64)
+    Z = np.zeros((T, d))
+    for m0 in range(0, T, b):
+        m1 = min(T, m0 + b)
+        XK, XV, XQ = k[m0:m1].T, v[m0:m1].T, q[m0:m1].T
+        e = eta[m0:m1]
+        # batch forward / backward at the starting weights (App. A)
+        Z1 = W1 @ XK
+        X2 = gelu(Z1)
+        Z2 = W2 @ X2
+        G2 = 2.0 * (Z2 - XV) * e[None, :]
+        G1 = (W2.T @ G2) * gelu_grad(Z1)
+        # outputs: each layer's input matrix A masked against its query side
+        Z1q = W1 @ XQ - G1 @ np.triu(XK.T @ XQ)
+        X2q = gelu(Z1q)
+        Z[m0:m1] = (W2 @ X2q - G2 @ np.triu(X2.T @ X2q)).T
+        W1 = W1 - G1 @ XK.T
+        W2 = W2 - G2 @ X2.T
+    return Z, W1, W2
+
+
+def _units(a, lead):
+    return a.reshape(lead, *a.shape[2:])
+
+
+def linear(q, k, v, eta, w0, b):
+    B, H, T, d = q.shape
+    Z = np.zeros((B, H, T, d))
+    WT = np.zeros((B, H, d, d))
+    for bi in range(B):
+        for h in range(H):
+            w = w0[bi, h] if w0.ndim == 4 else w0[h]
+            Z[bi, h], WT[bi, h] = linear_unit(q[bi, h], k[bi, h], v[bi, h], eta[bi, h], w, b)
+    return Z, WT
+
+
+def mlp(q, k, v, eta, w1, w2, b):
+    B, H, T, d = q.shape
+    hd = w1.shape[-2]
+    Z = np.zeros((B, H, T, d))
+    W1T = np.zeros((B, H, hd, d))
+    W2T = np.zeros((B, H, d, hd))
+    for bi in range(B):
+        for h in range(H):
+            a = w1[bi, h] if w1.ndim == 4 else w1[h]
+            c = w2[bi, h] if w2.ndim == 4 else w2[h]
+            Z[bi, h], W1T[bi, h], W2T[bi, h] = mlp_unit(q[bi, h], k[bi, h], v[bi, h], eta[bi, h],
+                                                       a, c, b)
+    return Z, W1T, W2T

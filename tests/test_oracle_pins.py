@@ -1,0 +1,359 @@
+"""Pins for the fp64 primal oracle (CPU only).
+
+The pages print no numeric example of the scan, so the oracle is pinned by
+identities the pages and the mathematics fix, each cited to
+"论文速览 | TTT" (equinox-blog close reading of "Learning to (Learn at Test
+Time): RNNs with Expressive Hidden States"):
+
+* primal == dual form (§3.6 for TTT-Linear, §3.7 / App. A for TTT-MLP);
+* Theorem 1 (§4.1): f = Wx, batch GD, eta = 1/2, W0 = 0 is causal linear
+  attention z_t = sum_{s<=t} v_s k_s^T q_t;
+* b = 1 is online GD, i.e. the delta rule of DeltaNet (§2.6, §3.5);
+* b >= T is batch GD, W_t = W0 - eta sum_{s<=t} G_s (§3.5);
+* eta = 0 leaves the state at W0 (then Z = W0 Q);
+* one mini-batch equals one gradient step on sum_s eta_s l_s, checked against
+  central finite differences of the loss (§3.5 / §3.6 closed form);
+* Figure 4 (§3.2): one step lowers the current token's loss; for f = Wx the
+  ratio is exactly (1 - 2 eta ||k||^2)^2;
+* hand-worked scalar examples (tests/golden/scalar_worked_examples.json);
+* MLP special cases: zero state stays zero; W2_0 = 0 with b = T is a
+  kernelised linear attention with feature map GELU(W1_0 x);
+* invariants: homogeneity, superposition, row permutation, state passing,
+  thread-count determinism.
+
+``test_planted_mistakes_are_caught`` rebuilds the oracle with one plausible
+mistake at a time (dropped factor 2, wrong sign, output before the update,
+gradient at the wrong state, transposed operand, ...) and checks that the pin
+set rejects every one of them.
+
+The GELU form (exact erf) is fixed by no passage of the pages; its parity is
+pinned only through the dual form and the finite-difference check, which use
+the same definition.
+"""
+from __future__ import annotations
+
+import json
+import os
+import re
+import shutil
+import tempfile
+
+import numpy as np
+import pytest
+
+import dual_form
+from oracle import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def rand_linear(rng, B, H, T, d, eta_scale=0.1, w_scale=0.2, per_batch=False):
+    q = rng.standard_normal((B, H, T, d)) / np.sqrt(d)
+    k = rng.standard_normal((B, H, T, d)) / np.sqrt(d)
+    v = rng.standard_normal((B, H, T, d)) / np.sqrt(d)
+    eta = rng.uniform(0.0, eta_scale, (B, H, T))
+    w0 = rng.standard_normal((B, H, d, d) if per_batch else (H, d, d)) * w_scale
+    return q, k, v, eta, w0
+
+
+def rand_mlp(rng, B, H, T, d, hd, eta_scale=0.1, w_scale=0.3):
+    q, k, v, eta, _ = rand_linear(rng, B, H, T, d, eta_scale)
+    w1 = rng.standard_normal((H, hd, d)) * w_scale
+    w2 = rng.standard_normal((H, d, hd)) * w_scale
+    return q, k, v, eta, w1, w2
+
+
+def rel(a, b):
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+# ---------------------------------------------------------------------------
+# Pin functions: each takes an oracle library handle (so the planted-mistake
+# test can run them against mutated builds) and raises AssertionError on a
+# mismatch.
+# ---------------------------------------------------------------------------
+
+def pin_linear_primal_equals_dual(lib):
+    rng = np.random.default_rng(11)
+    for (T, b) in [(37, 4), (32, 16), (20, 1), (9, 64), (48, 48)]:
+        q, k, v, eta, w0 = rand_linear(rng, 2, 2, T, 6)
+        z, w = oracle.linear(q, k, v, eta, w0, b, lib=lib)
+        zd, wd = dual_form.linear(q, k, v, eta, w0, b)
+        assert rel(z, zd) < 1e-12 and rel(w, wd) < 1e-12, (T, b, rel(z, zd), rel(w, wd))
+
+
+def pin_mlp_primal_equals_dual(lib):
+    rng = np.random.default_rng(12)
+    for (T, b) in [(23, 4), (16, 16), (7, 1), (10, 32)]:
+        q, k, v, eta, w1, w2 = rand_mlp(rng, 1, 2, T, 5, 9, eta_scale=0.5)
+        z, a, c = oracle.mlp(q, k, v, eta, w1, w2, b, lib=lib)
+        zd, ad, cd = dual_form.mlp(q, k, v, eta, w1, w2, b)
+        for x, y in ((z, zd), (a, ad), (c, cd)):
+            assert rel(x, y) < 1e-12, (T, b, rel(x, y))
+
+
+def pin_theorem1_linear_attention(lib):
+    rng = np.random.default_rng(13)
+    T, d = 24, 5
+    q, k, v, _, _ = rand_linear(rng, 1, 1, T, d)
+    eta = np.full((1, 1, T), 0.5)
+    z, w = oracle.linear(q, k, v, eta, np.zeros((1, d, d)), T, lib=lib)
+    # recurrent form of causal linear attention: S_t = S_{t-1} + v_t k_t^T, z_t = S_t q_t
+    S = np.zeros((d, d))
+    zt = np.zeros((T, d))
+    for t in range(T):
+        S = S + np.outer(v[0, 0, t], k[0, 0, t])
+        zt[t] = S @ q[0, 0, t]
+    assert rel(z[0, 0], zt) < 1e-13 and rel(w[0, 0], S) < 1e-13
+
+
+def pin_b1_delta_rule(lib):
+    rng = np.random.default_rng(14)
+    T, d = 30, 6
+    q, k, v, eta, w0 = rand_linear(rng, 1, 1, T, d, eta_scale=0.5)
+    z, w = oracle.linear(q, k, v, eta, w0, 1, lib=lib)
+    # DeltaNet's rule: W_t = W_{t-1} (I - beta k k^T) + beta v k^T with beta = 2 eta
+    W = w0[0].copy()
+    zt = np.zeros((T, d))
+    for t in range(T):
+        kk, beta = k[0, 0, t], 2.0 * eta[0, 0, t]
+        W = W @ (np.eye(d) - beta * np.outer(kk, kk)) + beta * np.outer(v[0, 0, t], kk)
+        zt[t] = W @ q[0, 0, t]
+    assert rel(z[0, 0], zt) < 1e-12 and rel(w[0, 0], W) < 1e-12
+
+
+def pin_bT_batch_gd(lib):
+    rng = np.random.default_rng(15)
+    T, d = 17, 4
+    q, k, v, eta, w0 = rand_linear(rng, 1, 1, T, d, eta_scale=0.5)
+    for b in (T, 2 * T):
+        z, w = oracle.linear(q, k, v, eta, w0, b, lib=lib)
+        W0 = w0[0]
+        G = np.stack([2.0 * np.outer(W0 @ k[0, 0, t] - v[0, 0, t], k[0, 0, t]) for t in range(T)])
+        Wt = W0[None] - np.cumsum(eta[0, 0][:, None, None] * G, axis=0)
+        zt = np.einsum("tij,tj->ti", Wt, q[0, 0])
+        assert rel(z[0, 0], zt) < 1e-12 and rel(w[0, 0], Wt[-1]) < 1e-12
+
+
+def pin_eta_zero(lib):
+    rng = np.random.default_rng(16)
+    q, k, v, eta, w0 = rand_linear(rng, 2, 3, 19, 5)
+    eta[:] = 0.0
+    z, w = oracle.linear(q, k, v, eta, w0, 4, lib=lib)
+    assert np.array_equal(w, np.broadcast_to(w0, w.shape))
+    assert rel(z, np.einsum("hij,bhtj->bhti", w0, q)) < 1e-14
+
+
+def pin_one_step_is_gradient_step(lib):
+    """T = b: W_T = W0 - grad_W sum_s eta_s ||W k_s - v_s||^2 at W0 (finite differences)."""
+    rng = np.random.default_rng(17)
+    T, d = 5, 4
+    q, k, v, eta, w0 = rand_linear(rng, 1, 1, T, d, eta_scale=0.5)
+    _, w = oracle.linear(q, k, v, eta, w0, T, lib=lib)
+    K, V, e, W0 = k[0, 0], v[0, 0], eta[0, 0], w0[0]
+
+    def L(W):
+        r = K @ W.T - V
+        return float(np.sum(e * np.sum(r * r, axis=1)))
+
+    grad = np.zeros((d, d))
+    h = 1e-3
+    for i in range(d):
+        for j in range(d):
+            E = np.zeros((d, d))
+            E[i, j] = h
+            grad[i, j] = (L(W0 + E) - L(W0 - E)) / (2 * h)
+    assert rel(w[0, 0], W0 - grad) < 1e-9
+
+
+def pin_fig4_loss_ratio(lib):
+    rng = np.random.default_rng(18)
+    T, d = 12, 5
+    q, k, v, eta, w0 = rand_linear(rng, 1, 1, T, d, eta_scale=0.5)
+    for t in (1, 5, 11):
+        _, w_prev = oracle.linear(q[:, :, :t], k[:, :, :t], v[:, :, :t], eta[:, :, :t], w0, 1, lib=lib)
+        _, w_next = oracle.linear(q[:, :, :t + 1], k[:, :, :t + 1], v[:, :, :t + 1],
+                                  eta[:, :, :t + 1], w0, 1, lib=lib)
+        kk, vv, et = k[0, 0, t], v[0, 0, t], eta[0, 0, t]
+        before = np.sum((w_prev[0, 0] @ kk - vv) ** 2)
+        after = np.sum((w_next[0, 0] @ kk - vv) ** 2)
+        assert abs(after / before - (1.0 - 2.0 * et * kk @ kk) ** 2) < 1e-10
+
+
+def pin_golden_scalar_examples(lib):
+    with open(os.path.join(HERE, "golden", "scalar_worked_examples.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        T = len(c["eta"])
+        sh = lambda key: np.asarray(c[key], dtype=np.float64).reshape(1, 1, T, c["d"])
+        z, w = oracle.linear(sh("q"), sh("k"), sh("v"), np.asarray(c["eta"]).reshape(1, 1, T),
+                             np.asarray(c["w0"]).reshape(1, c["d"], c["d"]), c["b"], lib=lib)
+        assert np.array_equal(z.reshape(T, c["d"]), np.asarray(c["z"])), c["name"]
+        assert np.array_equal(w.reshape(c["d"], c["d"]), np.asarray(c["w_T"])), c["name"]
+
+
+def pin_mlp_one_step_finite_differences(lib):
+    rng = np.random.default_rng(19)
+    T, d, hd = 4, 3, 5
+    q, k, v, eta, w1, w2 = rand_mlp(rng, 1, 1, T, d, hd, eta_scale=0.5, w_scale=0.8)
+    _, a, c = oracle.mlp(q, k, v, eta, w1, w2, T, lib=lib)
+    K, V, e = k[0, 0], v[0, 0], eta[0, 0]
+
+    def L(W1, W2):
+        r = dual_form.gelu(K @ W1.T) @ W2.T - V
+        return float(np.sum(e * np.sum(r * r, axis=1)))
+
+    h = 1e-5
+    for W, out, which in ((w1[0], a[0, 0], 0), (w2[0], c[0, 0], 1)):
+        g = np.zeros_like(W)
+        for idx in np.ndindex(*W.shape):
+            E = np.zeros_like(W)
+            E[idx] = h
+            if which == 0:
+                g[idx] = (L(W + E, w2[0]) - L(W - E, w2[0])) / (2 * h)
+            else:
+                g[idx] = (L(w1[0], W + E) - L(w1[0], W - E)) / (2 * h)
+        assert rel(out, W - g) < 1e-8, which
+
+
+def pin_mlp_zero_state(lib):
+    rng = np.random.default_rng(20)
+    q, k, v, eta, w1, w2 = rand_mlp(rng, 1, 2, 11, 4, 6)
+    z, a, c = oracle.mlp(q, k, v, eta, 0 * w1, 0 * w2, 4, lib=lib)
+    assert not z.any() and not a.any() and not c.any()
+
+
+def pin_mlp_w2_zero_kernel_attention(lib):
+    rng = np.random.default_rng(21)
+    T, d, hd = 9, 4, 6
+    q, k, v, eta, w1, w2 = rand_mlp(rng, 1, 1, T, d, hd, eta_scale=0.5)
+    z, a, c = oracle.mlp(q, k, v, eta, w1, 0 * w2, T, lib=lib)
+    phi = lambda x: dual_form.gelu(w1[0] @ x)
+    S = np.zeros((d, hd))
+    zt = np.zeros((T, d))
+    for t in range(T):
+        S = S + 2.0 * eta[0, 0, t] * np.outer(v[0, 0, t], phi(k[0, 0, t]))
+        zt[t] = S @ phi(q[0, 0, t])
+    assert rel(z[0, 0], zt) < 1e-12 and rel(c[0, 0], S) < 1e-12
+    assert np.array_equal(a[0, 0], w1[0])
+
+
+PINS = [
+    pin_linear_primal_equals_dual,
+    pin_mlp_primal_equals_dual,
+    pin_theorem1_linear_attention,
+    pin_b1_delta_rule,
+    pin_bT_batch_gd,
+    pin_eta_zero,
+    pin_one_step_is_gradient_step,
+    pin_fig4_loss_ratio,
+    pin_golden_scalar_examples,
+    pin_mlp_one_step_finite_differences,
+    pin_mlp_zero_state,
+    pin_mlp_w2_zero_kernel_attention,
+]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
+def test_pin(pin):
+    pin(oracle.load())
+
+
+# ---------------------------------------------------------------------------
+# Invariants of the oracle (no second formulation needed).
+# ---------------------------------------------------------------------------
+
+def test_linear_homogeneity_and_superposition():
+    rng = np.random.default_rng(30)
+    q, k, v, eta, w0 = rand_linear(rng, 2, 2, 29, 6)
+    z, w = oracle.linear(q, k, v, eta, w0, 8)
+    z2, w2 = oracle.linear(q, k, 2 * v, eta, 2 * w0, 8)
+    assert np.array_equal(z2, 2 * z) and np.array_equal(w2, 2 * w)  # power of two: exact
+    za, wa = oracle.linear(q, k, 0 * v, eta, w0, 8)
+    zb, wb = oracle.linear(q, k, v, eta, 0 * w0, 8)
+    assert rel(za + zb, z) < 1e-13 and rel(wa + wb, w) < 1e-13
+
+
+def test_linear_row_permutation():
+    rng = np.random.default_rng(31)
+    q, k, v, eta, w0 = rand_linear(rng, 1, 2, 21, 7)
+    p = rng.permutation(7)
+    z, w = oracle.linear(q, k, v, eta, w0, 4)
+    zp, wp = oracle.linear(q, k, v[..., p], eta, w0[:, p, :], 4)
+    assert np.array_equal(zp, z[..., p]) and np.array_equal(wp, w[:, :, p, :])
+
+
+@pytest.mark.parametrize("kind", ["linear", "mlp"])
+def test_state_passing(kind):
+    rng = np.random.default_rng(32)
+    T, T1, b = 40, 24, 8
+    if kind == "linear":
+        q, k, v, eta, w0 = rand_linear(rng, 2, 2, T, 5)
+        z, w = oracle.linear(q, k, v, eta, w0, b)
+        za, wa = oracle.linear(q[:, :, :T1], k[:, :, :T1], v[:, :, :T1], eta[:, :, :T1], w0, b)
+        zb, wb = oracle.linear(q[:, :, T1:], k[:, :, T1:], v[:, :, T1:], eta[:, :, T1:], wa, b)
+        assert np.array_equal(np.concatenate([za, zb], axis=2), z) and np.array_equal(wb, w)
+    else:
+        q, k, v, eta, w1, w2 = rand_mlp(rng, 2, 1, T, 4, 7)
+        z, a, c = oracle.mlp(q, k, v, eta, w1, w2, b)
+        za, aa, ca = oracle.mlp(q[:, :, :T1], k[:, :, :T1], v[:, :, :T1], eta[:, :, :T1], w1, w2, b)
+        zb, ab, cb = oracle.mlp(q[:, :, T1:], k[:, :, T1:], v[:, :, T1:], eta[:, :, T1:], aa, ca, b)
+        assert np.array_equal(np.concatenate([za, zb], axis=2), z)
+        assert np.array_equal(ab, a) and np.array_equal(cb, c)
+
+
+def test_thread_count_is_bit_exact():
+    rng = np.random.default_rng(33)
+    q, k, v, eta, w0 = rand_linear(rng, 3, 5, 33, 8)
+    z1, w1 = oracle.linear(q, k, v, eta, w0, 16, nthreads=1)
+    z7, w7 = oracle.linear(q, k, v, eta, w0, 16, nthreads=7)
+    assert np.array_equal(z1, z7) and np.array_equal(w1, w7)
+
+
+def test_empty_sequence_returns_initial_state():
+    rng = np.random.default_rng(34)
+    q, k, v, eta, w0 = rand_linear(rng, 2, 3, 0, 4)
+    z, w = oracle.linear(q, k, v, eta, w0, 16)
+    assert z.shape == (2, 3, 0, 4) and np.array_equal(w, np.broadcast_to(w0, w.shape))
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each mutated oracle must fail at least one pin.
+# ---------------------------------------------------------------------------
+
+MUTATIONS = {
+    "drop_factor_2": ("g[i] = 2.0 * (s - vt[i]);", "g[i] = (s - vt[i]);"),
+    "update_sign": ("W[i * d + j] -= et * g[i] * kt[j];", "W[i * d + j] += et * g[i] * kt[j];"),
+    "output_before_update": ("s += W[i * d + j] * qt[j];", "s += Ws[i * d + j] * qt[j];"),
+    "grad_at_current_state": ("s += Ws[i * d + j] * kt[j];", "s += W[i * d + j] * kt[j];"),
+    "transposed_state": ("s += Ws[i * d + j] * kt[j];", "s += Ws[j * d + i] * kt[j];"),
+    "output_reads_key": ("s += W[i * d + j] * qt[j];", "s += W[i * d + j] * kt[j];"),
+    "eta_of_first_token": ("const double et = eta[t];\n      /* G_t", "const double et = eta[m0];\n      /* G_t"),
+    "mlp_drop_gelu_grad": ("s->delta[u] = acc * gelu_grad(s->a[u]);", "s->delta[u] = acc;"),
+    "mlp_w2_update_sign": ("W2[i * hd + u] -= et * s->e[i] * s->x[u];", "W2[i * hd + u] += et * s->e[i] * s->x[u];"),
+    "mlp_backprop_through_current_w2": ("acc += s->W2s[i * hd + u] * s->e[i];", "acc += W2[i * hd + u] * s->e[i];"),
+    "mlp_output_from_start_w1": ("acc += W1[u * d + j] * qt[j];", "acc += s->W1s[u * d + j] * qt[j];"),
+    "mlp_gelu_scale": ("return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));", "return 0.5 * x * (1.0 + erf(x));"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistakes_are_caught(name):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    old, new = MUTATIONS[name]
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "ttt_oracle.c")).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+    with tempfile.TemporaryDirectory() as tmp:
+        path = os.path.join(tmp, "mut.c")
+        with open(path, "w") as f:
+            f.write(src.replace(old, new))
+        lib = oracle.load(oracle.build(path, os.path.join(tmp, "libmut.so")))
+        caught = []
+        for pin in PINS:
+            try:
+                with np.errstate(all="ignore"):
+                    pin(lib)
+            except AssertionError:
+                caught.append(pin.__name__)
+        assert caught, f"no pin rejects the planted mistake {name}"
