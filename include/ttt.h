@@ -1,0 +1,126 @@
+/*
+ * ttt.h — C ABI of the MI355X (gfx950) TTT forward-scan library, libttt.so.
+ *
+ * The library computes the forward pass of a TTT layer's inner loop:
+ * mini-batch test-time training of a fast-weight state W, evaluated in the
+ * dual form.  Sources ("论文速览 | TTT", the equinox-blog close reading of
+ * "Learning to (Learn at Test Time): RNNs with Expressive Hidden States"):
+ *   §3.1  each token updates the state, the output is read from the UPDATED
+ *         state: W_t = W_{t-1} - eta_t G_t, z_t = f(q_t; W_t);
+ *   §3.3  loss l(W; t) = || f(k_t; W) - v_t ||^2 (sum over components, so the
+ *         gradient carries a factor 2); k, v, q are the already-projected
+ *         training, label and test views;
+ *   §3.5  mini-batch GD: tokens [j*b, j*b + b) all take their gradient at the
+ *         state before that mini-batch; a final partial mini-batch is shorter;
+ *   §3.6  dual form for f(x) = W x;  §3.7 dual form for an MLP inner model;
+ *   §4.4  TTT-Linear f(x) = W x and TTT-MLP f(x) = W2 GELU(W1 x) (exact erf
+ *         GELU, hidden width 4d);
+ *   §4.6  a per-token inner learning rate eta_t scales token t's gradient.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers:  every tensor pointer is a DEVICE pointer on the current HIP
+ *            device, owned by the caller; the library allocates nothing,
+ *            frees nothing and keeps no state between calls.  Tensors are
+ *            dense, row-major, and 16-byte aligned.
+ * Streams:   `stream` is a hipStream_t (NULL = the null stream).  Work is
+ *            enqueued asynchronously; the call returns after the launch.
+ * Errors:    arguments are checked on the host before anything is enqueued;
+ *            a non-TTT_OK status means nothing was launched.  A failed launch
+ *            returns TTT_ERR_HIP.  Faults inside a kernel surface at the
+ *            caller's next synchronisation.  ttt_last_error() gives a
+ *            human-readable message for the calling thread's last failure.
+ * Layouts:   q, k, v   [B][H][T][d]   in qkv_dtype (fp32 or bf16)
+ *            eta       [B][H][T]      fp32
+ *            z         [B][H][T][d]   fp32 (output)
+ *            W[i][j]   i = output component, j = input component: f(x) = W x.
+ *            Initial states are shared by the batch ([H][...], w0_per_batch =
+ *            0, the learnt initial state of §4.5) or given per unit
+ *            ([B][H][...], w0_per_batch = 1, e.g. to resume a sequence from a
+ *            previous call's final state).  Final states are always per unit.
+ * Aliasing:  z must not overlap any input.  A final-state output may alias
+ *            its initial-state input only when w0_per_batch = 1 and the two
+ *            pointers are equal (in-place resume); any other overlap is
+ *            TTT_ERR_ALIAS.
+ * Support:   d = 64; TTT-MLP hidden = 256; mini-batch b with b | 16 or
+ *            16 | b (1, 2, 4, 8, 16, 32, 48, 64, ...); any T >= 0, B, H >= 0
+ *            with B*H*T*d < 2^31.  Anything else is TTT_ERR_UNSUPPORTED.
+ *            Empty work (B*H == 0) returns TTT_OK without launching; T == 0
+ *            copies the initial states to the final-state outputs.
+ */
+#ifndef TTT_H_
+#define TTT_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TTT_ABI_VERSION 1
+
+typedef enum {
+  TTT_OK = 0,
+  TTT_ERR_NULL = 1,        /* a required pointer is NULL                    */
+  TTT_ERR_SHAPE = 2,       /* negative size or size product overflow        */
+  TTT_ERR_DTYPE = 3,       /* qkv_dtype is not a ttt_dtype_t value          */
+  TTT_ERR_UNSUPPORTED = 4, /* d, hidden or b outside the supported set      */
+  TTT_ERR_ALIAS = 5,       /* an output overlaps an input (see Aliasing)    */
+  TTT_ERR_HIP = 6,         /* the HIP runtime reported an error             */
+  TTT_ERR_ALIGN = 7        /* a tensor pointer is not 16-byte aligned       */
+} ttt_status_t;
+
+typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype_t;
+
+/*
+ * TTT-Linear forward scan, f(x) = W x (§3.6 dual form, §4.4).
+ *
+ *   q, k, v : [B][H][T][d] qkv_dtype       eta : [B][H][T] fp32
+ *   w0      : [H][d][d] fp32 (w0_per_batch = 0) or [B][H][d][d] (= 1)
+ *   z       : out [B][H][T][d] fp32, z_t = W_t q_t with W_t after token t
+ *   w_out   : out [B][H][d][d] fp32, the state after the last token
+ *
+ * Per (batch, head) the state evolves as
+ *   W_t = W_{t-1} - 2 eta_t (W_{j*b} k_t - v_t) k_t^T,   j = t / b,
+ * with W_{j*b} the state before mini-batch j, which is what the dual form
+ * W_b = W0 - 2 (W0 K - V) diag(eta) K^T, Z = W0 Q - 2 (W0 K - V) diag(eta)
+ * triu(K^T Q) computes per mini-batch.
+ */
+ttt_status_t ttt_linear_fwd(const void* q, const void* k, const void* v,
+                            const float* eta, const float* w0,
+                            int32_t w0_per_batch, int32_t B, int32_t H,
+                            int32_t T, int32_t d, int32_t b,
+                            ttt_dtype_t qkv_dtype, float* z, float* w_out,
+                            void* stream);
+
+/*
+ * TTT-MLP forward scan, f(x) = W2 GELU(W1 x) (§3.7 dual form, §4.4).
+ *
+ *   w1_0 : [H][hidden][d] fp32 (or [B][H][hidden][d] when w0_per_batch = 1)
+ *   w2_0 : [H][d][hidden] fp32 (or [B][H][d][hidden])
+ *   z    : out [B][H][T][d] fp32, z_t = W2_t GELU(W1_t q_t)
+ *   w1_out, w2_out : out [B][H][hidden][d], [B][H][d][hidden] fp32
+ *
+ * Both layers take their gradient of sum_t eta_t ||f(k_t) - v_t||^2 at the
+ * state before the mini-batch; GELU is x * Phi(x) with the exact erf.
+ */
+ttt_status_t ttt_mlp_fwd(const void* q, const void* k, const void* v,
+                         const float* eta, const float* w1_0,
+                         const float* w2_0, int32_t w0_per_batch, int32_t B,
+                         int32_t H, int32_t T, int32_t d, int32_t hidden,
+                         int32_t b, ttt_dtype_t qkv_dtype, float* z,
+                         float* w1_out, float* w2_out, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* ttt_status_str(ttt_status_t status);
+
+/* Message for the calling thread's most recent non-OK status ("" if none). */
+const char* ttt_last_error(void);
+
+/* TTT_ABI_VERSION of the loaded library. */
+int32_t ttt_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TTT_H_ */

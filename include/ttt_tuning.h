@@ -1,0 +1,46 @@
+/*
+ * ttt_tuning.h — launch-shape control and measurement helpers of libttt.so.
+ *
+ * Not needed for correctness: ttt_linear_fwd picks its launch shape itself.
+ * These entry points exist so that benchmarks can sweep launch shapes and
+ * calibrate hardware counters.  Same pointer, stream and error conventions
+ * as include/ttt.h.
+ */
+#ifndef TTT_TUNING_H_
+#define TTT_TUNING_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ttt.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * ttt_linear_fwd with an explicit launch shape: rows_per_workgroup rows of
+ * each head's 64-row state per workgroup (16, 32 or 64; 0 = automatic).
+ * The rows of W evolve independently (the reconstruction loss is a sum over
+ * output components, "论文速览 | TTT" §3.3), so any split gives the same
+ * result bit for bit.  Other values: TTT_ERR_UNSUPPORTED.
+ */
+ttt_status_t ttt_linear_fwd_tuned(const void* q, const void* k, const void* v,
+                                  const float* eta, const float* w0,
+                                  int32_t w0_per_batch, int32_t B, int32_t H,
+                                  int32_t T, int32_t d, int32_t b,
+                                  ttt_dtype_t qkv_dtype, float* z,
+                                  float* w_out, void* stream,
+                                  int32_t rows_per_workgroup);
+
+/*
+ * Plain streaming copy of `bytes` bytes (a multiple of 16, both pointers
+ * 16-byte aligned, no overlap) from src to dst on `stream`: the reference
+ * kernel whose hardware byte counters calibrate those of the scans.
+ */
+ttt_status_t ttt_bench_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TTT_TUNING_H_ */

@@ -1,1 +1,7 @@
-"""MI355X-native TTT forward scan (TTT-Linear / TTT-MLP, mini-batch dual form)."""
+"""MI355X-native TTT forward scan (TTT-Linear / TTT-MLP, mini-batch dual form).
+
+The scan runs in hand-written gfx950 HIP kernels behind the C ABI of
+libttt.so (include/ttt.h); this package is its thin Python binding.
+"""
+from .api import bench_copy, ttt_linear_fwd, ttt_mlp_fwd  # noqa: F401
+from ._lib import TTTError  # noqa: F401

@@ -1,0 +1,127 @@
+"""Python binding of the TTT scan C ABI over torch tensors.
+
+Argument marshalling only: shapes, dtypes and the current HIP stream are read
+from the tensors and passed to libttt.so; every step of the scan runs in the
+HIP kernels.  Tensors must live on a GPU; there is no CPU path.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _lib.TTT_BF16
+    if t.dtype == torch.float32:
+        return _lib.TTT_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check_tensors(named: dict) -> torch.device:
+    dev = None
+    for name, t in named.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (got {t.device}); the scan runs only "
+                             "in the HIP kernels")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    return dev
+
+
+def _stream(dev, stream):
+    if stream is None:
+        return torch.cuda.current_stream(dev).cuda_stream
+    return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
+
+
+def ttt_linear_fwd(q, k, v, eta, w0, b: int, z=None, w_out=None, stream=None,
+                   rows_per_workgroup: int = 0):
+    """TTT-Linear forward scan (see include/ttt.h).
+
+    q, k, v: [B, H, T, d] bf16 or fp32; eta: [B, H, T] fp32; w0: [H, d, d] or
+    [B, H, d, d] fp32.  Outputs z [B, H, T, d] fp32 and w_out [B, H, d, d]
+    fp32 are allocated when not given.  Returns (z, w_out).
+    """
+    B, H, T, d = q.shape
+    if z is None:
+        z = torch.empty((B, H, T, d), dtype=torch.float32, device=q.device)
+    if w_out is None:
+        w_out = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+    dev = _check_tensors(dict(q=q, k=k, v=v, eta=eta, w0=w0, z=z, w_out=w_out))
+    for name, t in (("eta", eta), ("w0", w0), ("z", z), ("w_out", w_out)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if k.shape != q.shape or v.shape != q.shape or tuple(eta.shape) != (B, H, T):
+        raise ValueError("shape mismatch among q, k, v, eta")
+    per_batch = 1 if w0.dim() == 4 else 0
+    if tuple(w0.shape) != ((B, H, d, d) if per_batch else (H, d, d)):
+        raise ValueError(f"w0 has shape {tuple(w0.shape)}")
+    if tuple(z.shape) != (B, H, T, d) or tuple(w_out.shape) != (B, H, d, d):
+        raise ValueError("output shape mismatch")
+    L = _lib.lib()
+    with torch.cuda.device(dev):
+        args = (_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w0), per_batch, B, H, T, d, int(b),
+                _dtype_code(q), _ptr(z), _ptr(w_out), _stream(dev, stream))
+        if rows_per_workgroup:
+            _lib.check(L.ttt_linear_fwd_tuned(*args, int(rows_per_workgroup)))
+        else:
+            _lib.check(L.ttt_linear_fwd(*args))
+    return z, w_out
+
+
+def ttt_mlp_fwd(q, k, v, eta, w1_0, w2_0, b: int, z=None, w1_out=None, w2_out=None, stream=None):
+    """TTT-MLP forward scan, f(x) = W2 GELU(W1 x) (see include/ttt.h).
+
+    w1_0: [H, hidden, d] or [B, H, hidden, d]; w2_0: [H, d, hidden] or
+    [B, H, d, hidden] (fp32).  Returns (z, w1_out, w2_out).
+    """
+    B, H, T, d = q.shape
+    hidden = w1_0.shape[-2]
+    if z is None:
+        z = torch.empty((B, H, T, d), dtype=torch.float32, device=q.device)
+    if w1_out is None:
+        w1_out = torch.empty((B, H, hidden, d), dtype=torch.float32, device=q.device)
+    if w2_out is None:
+        w2_out = torch.empty((B, H, d, hidden), dtype=torch.float32, device=q.device)
+    dev = _check_tensors(dict(q=q, k=k, v=v, eta=eta, w1_0=w1_0, w2_0=w2_0, z=z, w1_out=w1_out,
+                              w2_out=w2_out))
+    for name, t in (("eta", eta), ("w1_0", w1_0), ("w2_0", w2_0), ("z", z), ("w1_out", w1_out),
+                    ("w2_out", w2_out)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    per_batch = 1 if w1_0.dim() == 4 else 0
+    lead = (B, H) if per_batch else (H,)
+    if tuple(w1_0.shape) != (*lead, hidden, d) or tuple(w2_0.shape) != (*lead, d, hidden):
+        raise ValueError("w1_0 / w2_0 shape mismatch")
+    L = _lib.lib()
+    with torch.cuda.device(dev):
+        _lib.check(L.ttt_mlp_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w1_0), _ptr(w2_0),
+                                 per_batch, B, H, T, d, hidden, int(b), _dtype_code(q), _ptr(z),
+                                 _ptr(w1_out), _ptr(w2_out), _stream(dev, stream)))
+    return z, w1_out, w2_out
+
+
+def bench_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """Streaming copy kernel used to calibrate hardware byte counters."""
+    dev = _check_tensors(dict(src=src, dst=dst))
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst too small")
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib().ttt_bench_copy(_ptr(src), _ptr(dst), n, _stream(dev, stream)))

@@ -1,0 +1,206 @@
+// C ABI of libttt.so: argument validation and dispatch to the gfx950 kernels.
+// Declarations, layouts and error semantics: include/ttt.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/ttt.h"
+#include "../../include/ttt_tuning.h"
+#include "ttt_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ttt_status_t fail(ttt_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ttt_status_t fail(ttt_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+struct Range {
+  const char* name;
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlap(const Range& a, const Range& b) {
+  return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+Range rng(const char* name, const void* p, int64_t bytes) {
+  uintptr_t lo = (uintptr_t)p;
+  return Range{name, lo, p ? lo + (uintptr_t)bytes : lo};
+}
+
+bool supported_b(int32_t b) { return b >= 1 && ((b <= 16 && 16 % b == 0) || b % 16 == 0); }
+
+// Shared checks of the two scans.  `inputs` and `outputs` list every tensor
+// with its byte extent; `state_pairs` names (input index, output index)
+// pairs allowed to coincide exactly when w0_per_batch = 1.
+ttt_status_t check_common(const char* fn, ttt_dtype_t dt, int32_t w0_per_batch, int32_t B,
+                          int32_t H, int32_t T, int32_t d, int32_t b, const Range* in, int nin,
+                          const Range* out, int nout, const int (*pairs)[2], int npairs,
+                          bool need_seq) {
+  if (dt != TTT_F32 && dt != TTT_BF16) return fail(TTT_ERR_DTYPE, "%s: unknown qkv_dtype %d", fn, (int)dt);
+  if (B < 0 || H < 0 || T < 0 || d < 0 || b < 0)
+    return fail(TTT_ERR_SHAPE, "%s: negative size (B=%d H=%d T=%d d=%d b=%d)", fn, B, H, T, d, b);
+  if (w0_per_batch != 0 && w0_per_batch != 1)
+    return fail(TTT_ERR_SHAPE, "%s: w0_per_batch must be 0 or 1, got %d", fn, w0_per_batch);
+  if (d != 64) return fail(TTT_ERR_UNSUPPORTED, "%s: head dim d=%d unsupported (only 64)", fn, d);
+  if (!supported_b(b))
+    return fail(TTT_ERR_UNSUPPORTED, "%s: mini-batch b=%d unsupported (need b | 16 or 16 | b)", fn, b);
+  const int64_t elems = (int64_t)B * H * T * d;
+  if (elems >= ((int64_t)1 << 31))
+    return fail(TTT_ERR_SHAPE, "%s: B*H*T*d = %lld exceeds 2^31 - 1", fn, (long long)elems);
+  if ((int64_t)B * H == 0) return TTT_OK;
+  for (int i = 0; i < nin; ++i) {
+    const bool seq = i < 4;  // q, k, v, eta come first
+    if (seq && !need_seq) continue;
+    if (!in[i].lo) return fail(TTT_ERR_NULL, "%s: %s is NULL", fn, in[i].name);
+    if (in[i].lo & 15) return fail(TTT_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, in[i].name);
+  }
+  for (int i = 0; i < nout; ++i) {
+    if (i == 0 && !need_seq) continue;  // z is empty when T == 0
+    if (!out[i].lo) return fail(TTT_ERR_NULL, "%s: %s is NULL", fn, out[i].name);
+    if (out[i].lo & 15) return fail(TTT_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, out[i].name);
+  }
+  for (int o = 0; o < nout; ++o) {
+    for (int i = 0; i < nin; ++i) {
+      if (!overlap(out[o], in[i])) continue;
+      bool allowed = false;
+      for (int p = 0; p < npairs; ++p)
+        if (pairs[p][0] == i && pairs[p][1] == o && w0_per_batch == 1 && out[o].lo == in[i].lo &&
+            out[o].hi == in[i].hi)
+          allowed = true;
+      if (!allowed)
+        return fail(TTT_ERR_ALIAS, "%s: output %s overlaps input %s%s", fn, out[o].name,
+                    in[i].name,
+                    w0_per_batch ? "" : " (in-place state update needs w0_per_batch = 1)");
+    }
+    for (int o2 = o + 1; o2 < nout; ++o2)
+      if (overlap(out[o], out[o2]))
+        return fail(TTT_ERR_ALIAS, "%s: outputs %s and %s overlap", fn, out[o].name, out[o2].name);
+  }
+  return TTT_OK;
+}
+
+int auto_rows(int64_t units) {
+  (void)units;
+  return 64;
+}
+
+ttt_status_t linear_impl(const void* q, const void* k, const void* v, const float* eta,
+                         const float* w0, int32_t w0_per_batch, int32_t B, int32_t H, int32_t T,
+                         int32_t d, int32_t b, ttt_dtype_t dt, float* z, float* w_out,
+                         void* stream, int32_t rows) {
+  static const char* fn = "ttt_linear_fwd";
+  if (rows != 0 && rows != 16 && rows != 32 && rows != 64)
+    return fail(TTT_ERR_UNSUPPORTED, "%s: rows_per_workgroup=%d (need 0, 16, 32 or 64)", fn, rows);
+  const int64_t units = (int64_t)B * H;
+  const int64_t es = dt == TTT_F32 ? 4 : 2;
+  const int64_t seq = units * T * d;
+  const Range in[] = {rng("q", q, seq * es), rng("k", k, seq * es), rng("v", v, seq * es),
+                      rng("eta", eta, units * T * 4),
+                      rng("w0", w0, (w0_per_batch ? units : (int64_t)H) * d * d * 4)};
+  const Range out[] = {rng("z", z, seq * 4), rng("w_out", w_out, units * d * d * 4)};
+  const int pairs[][2] = {{4, 1}};
+  ttt_status_t st = check_common(fn, dt, w0_per_batch, B, H, T, d, b, in, 5, out, 2, pairs, 1, T > 0);
+  if (st != TTT_OK || units == 0) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (T == 0) {
+    if (w0_per_batch && w0 == w_out) return TTT_OK;
+    e = ttt::launch_copy_state(w0, w0_per_batch, (int)units, H, d * d, w_out, s);
+  } else {
+    ttt::LinearArgs a{q, k, v, eta, w0, z, w_out, w0_per_batch, (int)units, H, T, b};
+    e = ttt::launch_linear(a, dt == TTT_F32, rows ? rows : auto_rows(units), s);
+  }
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return TTT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ttt_status_t ttt_linear_fwd(const void* q, const void* k, const void* v, const float* eta,
+                            const float* w0, int32_t w0_per_batch, int32_t B, int32_t H,
+                            int32_t T, int32_t d, int32_t b, ttt_dtype_t qkv_dtype, float* z,
+                            float* w_out, void* stream) {
+  return linear_impl(q, k, v, eta, w0, w0_per_batch, B, H, T, d, b, qkv_dtype, z, w_out, stream,
+                     0);
+}
+
+ttt_status_t ttt_linear_fwd_tuned(const void* q, const void* k, const void* v, const float* eta,
+                                  const float* w0, int32_t w0_per_batch, int32_t B, int32_t H,
+                                  int32_t T, int32_t d, int32_t b, ttt_dtype_t qkv_dtype,
+                                  float* z, float* w_out, void* stream,
+                                  int32_t rows_per_workgroup) {
+  return linear_impl(q, k, v, eta, w0, w0_per_batch, B, H, T, d, b, qkv_dtype, z, w_out, stream,
+                     rows_per_workgroup);
+}
+
+ttt_status_t ttt_mlp_fwd(const void* q, const void* k, const void* v, const float* eta,
+                         const float* w1_0, const float* w2_0, int32_t w0_per_batch, int32_t B,
+                         int32_t H, int32_t T, int32_t d, int32_t hidden, int32_t b,
+                         ttt_dtype_t qkv_dtype, float* z, float* w1_out, float* w2_out,
+                         void* stream) {
+  static const char* fn = "ttt_mlp_fwd";
+  if (hidden < 0) return fail(TTT_ERR_SHAPE, "%s: negative hidden=%d", fn, hidden);
+  const int64_t units = (int64_t)B * H;
+  const int64_t es = qkv_dtype == TTT_F32 ? 4 : 2;
+  const int64_t seq = units * T * d;
+  const int64_t wn = (w0_per_batch ? units : (int64_t)H) * hidden * d * 4;
+  const Range in[] = {rng("q", q, seq * es), rng("k", k, seq * es), rng("v", v, seq * es),
+                      rng("eta", eta, units * T * 4), rng("w1_0", w1_0, wn),
+                      rng("w2_0", w2_0, wn)};
+  const Range out[] = {rng("z", z, seq * 4), rng("w1_out", w1_out, units * hidden * d * 4),
+                       rng("w2_out", w2_out, units * hidden * d * 4)};
+  const int pairs[][2] = {{4, 1}, {5, 2}};
+  ttt_status_t st =
+      check_common(fn, qkv_dtype, w0_per_batch, B, H, T, d, b, in, 6, out, 3, pairs, 2, T > 0);
+  if (st != TTT_OK) return st;
+  if (hidden != 256)
+    return fail(TTT_ERR_UNSUPPORTED, "%s: hidden=%d unsupported (only 256)", fn, hidden);
+  if (units == 0) return TTT_OK;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (T == 0) {
+    if (!(w0_per_batch && w1_0 == w1_out))
+      e = ttt::launch_copy_state(w1_0, w0_per_batch, (int)units, H, hidden * d, w1_out, s);
+    if (e == hipSuccess && !(w0_per_batch && w2_0 == w2_out))
+      e = ttt::launch_copy_state(w2_0, w0_per_batch, (int)units, H, hidden * d, w2_out, s);
+  } else {
+    ttt::MlpArgs a{q, k, v, eta, w1_0, w2_0, z, w1_out, w2_out, w0_per_batch, (int)units, H, T, b};
+    e = ttt::launch_mlp(a, qkv_dtype == TTT_F32, s);
+  }
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return TTT_OK;
+}
+
+const char* ttt_status_str(ttt_status_t s) {
+  switch (s) {
+    case TTT_OK: return "TTT_OK";
+    case TTT_ERR_NULL: return "TTT_ERR_NULL: a required pointer is NULL";
+    case TTT_ERR_SHAPE: return "TTT_ERR_SHAPE: invalid sizes";
+    case TTT_ERR_DTYPE: return "TTT_ERR_DTYPE: unknown dtype";
+    case TTT_ERR_UNSUPPORTED: return "TTT_ERR_UNSUPPORTED: configuration not supported";
+    case TTT_ERR_ALIAS: return "TTT_ERR_ALIAS: an output overlaps an input";
+    case TTT_ERR_HIP: return "TTT_ERR_HIP: HIP runtime error";
+    case TTT_ERR_ALIGN: return "TTT_ERR_ALIGN: pointer not 16-byte aligned";
+  }
+  return "unknown ttt_status_t";
+}
+
+const char* ttt_last_error(void) { return g_last_error.c_str(); }
+
+int32_t ttt_abi_version(void) { return TTT_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,138 @@
+// Device helpers shared by the gfx950 TTT scan kernels: vector types, MFMA
+// wrappers, fp32 -> bf16 hi/lo splitting, LDS-DMA staging and the raw
+// workgroup barrier.
+//
+// MFMA operand layouts used throughout (wave64, lane l, c = l % 16,
+// g = l / 16), for a 16x16 output tile C[M][N]:
+//   accumulator   : lane (c,g) register r holds C[4g + r][c]
+//   16x16x32 bf16 : A-operand lane (c,g) holds A[c][8g .. 8g+7],
+//                   B-operand lane (c,g) holds B[8g .. 8g+7][c]
+//   16x16x4  f32  : A[c][g],          B[g][c]
+// The reduction index may be permuted freely as long as A and B agree, which
+// is how the kernels feed a register-resident accumulator straight back in as
+// an operand without a transpose.  Reductions of length 16 (over the tokens
+// of a tile) also use the K=32 shape: slots 8g..8g+3 carry the high bf16
+// halves and 8g+4..8g+7 the low halves of the same four indices, so one
+// instruction sums both halves.  The bf16 path uses no other MFMA shape: a
+// 16x16x16 MFMA that reads a 16x16x32 result as its accumulator right after
+// it was issued has been seen to read stale registers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttt {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define TTT_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ f32x4 mfma_k32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ short bf16_bits(float x) {
+  return __builtin_bit_cast(short, (bf16)x);  // round to nearest even
+}
+__device__ __forceinline__ float bf16_val(short h) {
+  return __builtin_bit_cast(float, ((uint32_t)(uint16_t)h) << 16);
+}
+
+// x = hi + lo + O(2^-16 |x|) with hi, lo bf16: products of such pairs with
+// exact bf16 operands keep ~16 significant bits, far below the fp32 budget.
+struct Split4 {
+  s16x4 hi, lo;
+};
+__device__ __forceinline__ Split4 split4(f32x4 x) {
+  Split4 s;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    short h = bf16_bits(x[r]);
+    s.hi[r] = h;
+    s.lo[r] = bf16_bits(x[r] - bf16_val(h));
+  }
+  return s;
+}
+struct Split8 {
+  bf16x8 hi, lo;
+};
+// Pack two accumulator registers (4 + 4 values) into one 8-wide operand.
+__device__ __forceinline__ Split8 split8(f32x4 a, f32x4 b) {
+  Split8 s;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    float x = r < 4 ? a[r] : b[r - 4];
+    bf16 h = (bf16)x;
+    s.hi[r] = h;
+    s.lo[r] = (bf16)(x - (float)h);
+  }
+  return s;
+}
+
+__device__ __forceinline__ bf16x8 cat8(uint2 a, uint2 b) {
+  uint4 u = make_uint4(a.x, a.y, b.x, b.y);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ bf16x8 cat44(s16x4 a, s16x4 b) {
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Product of two 16x16 fp32 matrices held in accumulator layout:
+// xt = accumulator layout of X^T, y = accumulator layout of Y; returns
+// acc + X*Y with the three significant hi/lo terms (the lo*lo term is
+// below 2^-16 relative).
+__device__ __forceinline__ f32x4 mm16_split(f32x4 xt, f32x4 y, f32x4 acc) {
+  const Split4 a = split4(xt), b = split4(y);
+  const s16x4 z = {0, 0, 0, 0};
+  acc = mfma_k32(cat44(a.hi, a.lo), cat44(b.hi, b.hi), acc);  // hi*hi + lo*hi
+  acc = mfma_k32(cat44(a.hi, z), cat44(b.lo, z), acc);        // hi*lo
+  return acc;
+}
+__device__ __forceinline__ f32x4 mm16_f32(f32x4 xt, f32x4 y, f32x4 acc) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = mfma_f32(xt[e], y[e], acc);
+  return acc;
+}
+
+// Compiler-level ordering around the hardware barrier.  No cache or counter
+// wait is implied: producers that write LDS with DMA wait on their own
+// vector-memory counter before arriving.
+__device__ __forceinline__ void wg_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Raw buffer descriptor over [base, base + bytes): loads past the end return
+// zeros, which is how partial tiles are padded.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Wave-wide DMA of 16 (or 4) bytes per lane from the buffer into LDS at
+// lds_base + 16 * lane (4 * lane).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TTT_LDS void*)lds_base, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TTT_LDS void*)lds_base, 4, voff, 0, 0, 0);
+}
+
+}  // namespace ttt

@@ -1,0 +1,47 @@
+// Internal launch interface between the C ABI (ttt_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttt {
+
+struct LinearArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* eta;
+  const float* w0;
+  float* z;
+  float* w_out;
+  int w0_per_batch;
+  int units;  // B * H
+  int H;
+  int T;
+  int b;
+};
+
+struct MlpArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* eta;
+  const float* w1_0;
+  const float* w2_0;
+  float* z;
+  float* w1_out;
+  float* w2_out;
+  int w0_per_batch;
+  int units;
+  int H;
+  int T;
+  int b;
+};
+
+// rows: rows of W per workgroup (64, 32 or 16).
+hipError_t launch_linear(const LinearArgs& a, bool f32in, int rows, hipStream_t s);
+hipError_t launch_mlp(const MlpArgs& a, bool f32in, hipStream_t s);
+hipError_t launch_copy_state(const float* src, int per_unit, int units, int H, int n,
+                             float* dst, hipStream_t s);
+
+}  // namespace ttt

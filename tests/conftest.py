@@ -28,3 +28,13 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name each GPU case on the real stderr before it touches the device, so
+    that a run cut short still says which case was executing."""
+    if "gpu" in request.node.keywords:
+        sys.__stderr__.write(f"\n[gpu-case] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield

@@ -1,0 +1,70 @@
+"""Helpers for GPU parity tests (not collected): device copies of the seeded
+inputs and the error metrics the tolerances are stated in."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import oracle
+
+# Tolerances: rel-L2 <= 1e-5 for fp32 inputs; for bf16 inputs rel-L2 <= 2e-3
+# and max|diff| / RMS(reference) <= 1e-2, applied to Z and the final state.
+TOL_F32_REL = 1e-5
+TOL_BF16_REL = 2e-3
+TOL_BF16_MAX = 1e-2
+
+
+def dev(x, name):
+    """Device tensor of an input array in its storage format."""
+    a = getattr(x, name + "_raw")
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def metrics(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    diff = got - ref
+    rms = np.sqrt(np.mean(ref * ref))
+    return {
+        "rel_l2": float(np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-300)),
+        "max_over_rms": float(np.abs(diff).max() / max(rms, 1e-300)) if diff.size else 0.0,
+    }
+
+
+def assert_close(got, ref, qkv_dtype, what=""):
+    m = metrics(got, ref)
+    if qkv_dtype == "f32":
+        assert m["rel_l2"] <= TOL_F32_REL, (what, m)
+    else:
+        assert m["rel_l2"] <= TOL_BF16_REL and m["max_over_rms"] <= TOL_BF16_MAX, (what, m)
+    return m
+
+
+def run_linear(x, b, rows=0):
+    from test_rnn_layers_head_amd import ttt_linear_fwd
+    z, w = ttt_linear_fwd(dev(x, "q"), dev(x, "k"), dev(x, "v"), f32(x.eta), f32(x.w0), b,
+                          rows_per_workgroup=rows)
+    torch.cuda.synchronize()
+    return z.cpu().numpy(), w.cpu().numpy()
+
+
+def oracle_linear(x, b):
+    return oracle.linear(x.q, x.k, x.v, x.eta, x.w0, b)
+
+
+def run_mlp(x, b):
+    from test_rnn_layers_head_amd import ttt_mlp_fwd
+    z, w1, w2 = ttt_mlp_fwd(dev(x, "q"), dev(x, "k"), dev(x, "v"), f32(x.eta), f32(x.w1),
+                            f32(x.w2), b)
+    torch.cuda.synchronize()
+    return z.cpu().numpy(), w1.cpu().numpy(), w2.cpu().numpy()
+
+
+def oracle_mlp(x, b):
+    return oracle.mlp(x.q, x.k, x.v, x.eta, x.w1, x.w2, b)

@@ -1,0 +1,170 @@
+"""TTT-Linear: HIP path (through the C ABI) against the fp64 primal oracle.
+
+Sizes: small cases span several 16-token tiles and a ragged tail for every
+supported mini-batch shape; the full workloads run on the GPU at their real
+size and launch shape and are compared on sampled (batch, head) units that
+the oracle recomputes from scratch.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as gu
+from test_rnn_layers_head_amd import TTTError, inputs, ttt_linear_fwd
+
+pytestmark = pytest.mark.gpu
+
+
+def small(B, H, T, dtype, seed, eta_dist="sigmoid"):
+    wl = inputs.Workload("small", "linear", B=B, H=H, T=T, qkv_dtype=dtype, eta_dist=eta_dist,
+                         seed=seed)
+    return inputs.make_inputs(wl)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("b", [1, 2, 4, 8, 16, 32, 64])
+@pytest.mark.parametrize("T", [1, 15, 16, 37, 130])
+def test_small_parity(dtype, b, T):
+    x = small(2, 3, T, dtype, seed=100 + T + b)
+    z, w = gu.run_linear(x, b)
+    zr, wr = gu.oracle_linear(x, b)
+    gu.assert_close(z, zr, dtype, "z")
+    gu.assert_close(w, wr, dtype, "w_T")
+
+
+def test_fp32_workload_full():
+    x = inputs.make_inputs(1)
+    z, w = gu.run_linear(x, 16)
+    zr, wr = gu.oracle_linear(x, 16)
+    m = gu.assert_close(z, zr, "f32", "z")
+    gu.assert_close(w, wr, "f32", "w_T")
+    print("fp32 T=256 z:", m)
+
+
+def test_125m_workload_full():
+    x = inputs.make_inputs(2)
+    z, w = gu.run_linear(x, 16)
+    zr, wr = gu.oracle_linear(x, 16)
+    print("125M z:", gu.assert_close(z, zr, "bf16", "z"), "w:", gu.assert_close(w, wr, "bf16", "w"))
+
+
+@pytest.fixture(scope="module")
+def big():
+    return inputs.make_inputs(3)
+
+
+@pytest.mark.parametrize("b", [1, 4, 16, 64])
+def test_1p3b_workload_sampled_units(big, b):
+    x = big
+    z, w = gu.run_linear(x, b)
+    idx = [0, 37, 77, 127]
+    sub = x.units(idx)
+    zr, wr = gu.oracle_linear(sub, b)
+    zs = z.reshape(-1, x.wl.T, 64)[idx][None]
+    ws = w.reshape(-1, 64, 64)[idx][None]
+    print(f"1.3B b={b} z:", gu.assert_close(zs, zr, "bf16", "z"),
+          "w:", gu.assert_close(ws, wr, "bf16", "w"))
+    assert np.isfinite(z).all()
+
+
+def test_longctx_workload_sampled_units():
+    x = inputs.make_inputs(5)
+    z, w = gu.run_linear(x, 16)
+    idx = [3, 30]
+    zr, wr = gu.oracle_linear(x.units(idx), 16)
+    zs = z.reshape(-1, x.wl.T, 64)[idx][None]
+    ws = w.reshape(-1, 64, 64)[idx][None]
+    print("long-ctx z:", gu.assert_close(zs, zr, "bf16", "z"),
+          "w:", gu.assert_close(ws, wr, "bf16", "w"))
+    # error must not grow along the sequence: compare the last 2k tokens alone
+    gu.assert_close(zs[:, :, -2048:], zr[:, :, -2048:], "bf16", "z tail")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("b", [4, 16, 32])
+def test_row_split_is_bit_identical(dtype, b):
+    x = small(3, 5, 77, dtype, seed=7)
+    ref = gu.run_linear(x, b, rows=64)
+    for rows in (16, 32):
+        got = gu.run_linear(x, b, rows=rows)
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]), rows
+
+
+def test_deterministic_reruns():
+    x = small(4, 8, 300, "bf16", seed=8)
+    a = gu.run_linear(x, 16)
+    b = gu.run_linear(x, 16)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("b", [4, 16, 64])
+def test_state_passing_in_place(b):
+    """Two calls (the second resuming in place from the first's final state)
+    equal one call, bit for bit, when the split falls on a mini-batch edge."""
+    x = small(2, 4, 320, "bf16", seed=9)
+    z, w = gu.run_linear(x, b)
+    T1 = 192
+    q, k, v = (gu.dev(x, n) for n in "qkv")
+    eta = gu.f32(x.eta)
+    state = gu.f32(np.broadcast_to(x.w0, (2, 4, 64, 64)))
+    z1, _ = ttt_linear_fwd(q[:, :, :T1].contiguous(), k[:, :, :T1].contiguous(),
+                           v[:, :, :T1].contiguous(), eta[:, :, :T1].contiguous(), state, b,
+                           w_out=state)
+    z2, _ = ttt_linear_fwd(q[:, :, T1:].contiguous(), k[:, :, T1:].contiguous(),
+                           v[:, :, T1:].contiguous(), eta[:, :, T1:].contiguous(), state, b,
+                           w_out=state)
+    torch.cuda.synchronize()
+    assert np.array_equal(torch.cat([z1, z2], dim=2).cpu().numpy(), z)
+    assert np.array_equal(state.cpu().numpy(), w)
+
+
+def test_side_stream_ordering():
+    x = small(2, 2, 64, "bf16", seed=10)
+    ref = gu.run_linear(x, 16)
+    q, k, v = (gu.dev(x, n) for n in "qkv")
+    eta, w0 = gu.f32(x.eta), gu.f32(x.w0)
+    z = torch.empty((2, 2, 64, 64), device="cuda")
+    w = torch.empty((2, 2, 64, 64), device="cuda")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        z.fill_(float("nan"))
+        w.fill_(float("nan"))
+        ttt_linear_fwd(q, k, v, eta, w0, 16, z=z, w_out=w, stream=s)
+    s.synchronize()
+    assert np.array_equal(z.cpu().numpy(), ref[0]) and np.array_equal(w.cpu().numpy(), ref[1])
+
+
+def test_empty_sequence_copies_state():
+    x = small(2, 3, 0, "bf16", seed=11)
+    z, w = gu.run_linear(x, 16)
+    assert z.shape == (2, 3, 0, 64)
+    assert np.array_equal(w, np.broadcast_to(x.w0, w.shape))
+
+
+def test_empty_batch_is_noop():
+    q = torch.empty((0, 3, 16, 64), dtype=torch.bfloat16, device="cuda")
+    z, w = ttt_linear_fwd(q, q, q, torch.empty((0, 3, 16), device="cuda"),
+                          torch.zeros((3, 64, 64), device="cuda"), 16)
+    assert z.numel() == 0 and w.numel() == 0
+
+
+def test_abi_errors_on_device_tensors():
+    x = small(1, 2, 32, "bf16", seed=12)
+    q, k, v = (gu.dev(x, n) for n in "qkv")
+    eta, w0 = gu.f32(x.eta), gu.f32(x.w0)
+    with pytest.raises(TTTError) as e:
+        ttt_linear_fwd(q, k, v, eta, w0, 3)
+    assert e.value.status == 4
+    buf = torch.zeros(1 * 2 * 32 * 64, device="cuda")  # z whose storage also holds q
+    qa = buf.view(torch.bfloat16)[: 2 * 32 * 64].view(1, 2, 32, 64)
+    with pytest.raises(TTTError) as e:
+        ttt_linear_fwd(qa, k, v, eta, w0, 16, z=buf.view(1, 2, 32, 64))
+    assert e.value.status == 5
+    with pytest.raises(TTTError) as e:  # in-place state with a shared initial state
+        ttt_linear_fwd(q, k, v, eta, w0, 16, w_out=w0.view(1, 2, 64, 64))
+    assert e.value.status == 5
+    wmis = torch.zeros(2 * 4096 + 1, device="cuda")[1:].view(2, 64, 64)
+    with pytest.raises(TTTError) as e:
+        ttt_linear_fwd(q, k, v, eta, wmis, 16)
+    assert e.value.status == 7
