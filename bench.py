@@ -1,0 +1,355 @@
+#!/usr/bin/env python3
+"""Benchmark of the TTT forward scan on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+One step = one call of ttt_linear_fwd over the whole TTT-Linear 1.3B-layer
+workload (B=4, H=32, T=8192, d=64, b=16, bf16 Q/K/V, fp32 eta / state / Z):
+every stage of the scan (tile staging, projections, gradient, causal
+attention-like mask, outputs, rank-b state update, final state) runs inside
+the timed kernel.  Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line: throughput in token*heads/s, the roofline of the scan
+kernel (algorithmic bytes / measured kernel time vs 8 TB/s HBM), the fp64
+oracle timed on the host cores as a baseline, and (unless --no-extras) the
+other workloads: the b sweep, the 125M and long-context TTT-Linear shapes,
+TTT-MLP, and a streaming-copy bandwidth reference.
+
+--pmc-calibrate additionally launches the streaming copy kernel on a known
+byte count, so that a hardware-counter run of this script can scale the
+scan's FETCH_SIZE / WRITE_SIZE readings (see --summarize-pmc).
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, vendor figure
+METRIC = "TTT fwd tokens·heads/s at 1 GPU; % of HBM/MFMA roofline (b=16)"
+UNIT = "tokens·heads/s"
+SCAN_SOURCES = ["ttt_linear.hip", "ttt_device.h", "ttt_launch.h"]
+MLP_SOURCES = ["ttt_mlp.hip", "ttt_device.h", "ttt_launch.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "test_rnn_layers_head_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# --------------------------------------------------------------------------
+# algorithmic work per launch
+# --------------------------------------------------------------------------
+def linear_alg_bytes(wl) -> int:
+    es = 2 if wl.qkv_dtype == "bf16" else 4
+    per_tok = 3 * wl.d * es + 4 + wl.d * 4  # q, k, v in; eta in; z out (fp32)
+    return wl.token_heads * per_tok + wl.H * wl.d * wl.d * 4 + wl.units * wl.d * wl.d * 4
+
+
+def linear_alg_flops(wl, b) -> int:
+    d = wl.d
+    return wl.token_heads * (6 * d * d + 4 * b * d)
+
+
+def mlp_alg_bytes(wl) -> int:
+    es = 2 if wl.qkv_dtype == "bf16" else 4
+    per_tok = 3 * wl.d * es + 4 + wl.d * 4
+    st = 2 * wl.hidden * wl.d * 4
+    return wl.token_heads * per_tok + wl.H * st + wl.units * st
+
+
+def mlp_alg_flops(wl, b) -> int:
+    d, h = wl.d, wl.hidden
+    return wl.token_heads * (14 * h * d + 4 * b * (h + d))
+
+
+# --------------------------------------------------------------------------
+def device_inputs(x):
+    import torch
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    d = dict(q=dev(x.q_raw), k=dev(x.k_raw), v=dev(x.v_raw), eta=dev(x.eta))
+    if x.w0 is not None:
+        d["w0"] = dev(x.w0)
+    else:
+        d["w1"], d["w2"] = dev(x.w1), dev(x.w2)
+    return d
+
+
+def time_launches(launch, steps, warmup):
+    """Times `steps` back-to-back launches (after `warmup`), bracketed by
+    device synchronisation, with events around each launch on the current
+    stream (the stream the kernels are enqueued on).  Returns
+    (wall ms per step, mean kernel us, median kernel us)."""
+    import torch
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        launch()
+        b.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    ks = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    return wall, float(ks.mean()), float(np.median(ks))
+
+
+def linear_case(wl, b, steps, warmup, x=None, rows=0):
+    import torch
+    from test_rnn_layers_head_amd import ttt_linear_fwd
+    from test_rnn_layers_head_amd import inputs
+    x = x or inputs.make_inputs(wl)
+    d = device_inputs(x)
+    z = torch.empty((wl.B, wl.H, wl.T, wl.d), device="cuda")
+    w = torch.empty((wl.B, wl.H, wl.d, wl.d), device="cuda")
+    launch = lambda: ttt_linear_fwd(d["q"], d["k"], d["v"], d["eta"], d["w0"], b, z=z, w_out=w,
+                                    rows_per_workgroup=rows)
+    wall, kmean, kmed = time_launches(launch, steps, warmup)
+    assert torch.isfinite(z).all().item()
+    byts = linear_alg_bytes(wl)
+    res = {
+        "workload": wl.name, "b": b, "token_heads_per_s": wl.token_heads / (wall * 1e-3),
+        "ms_per_step": wall, "kernel_us_mean": kmean, "kernel_us_median": kmed,
+        "alg_bytes": byts, "hbm_GBps": byts / (kmean * 1e-6) / 1e9,
+        "hbm_frac": byts / (kmean * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "mfma_frac": linear_alg_flops(wl, b) / (kmean * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+    }
+    del d, z, w
+    torch.cuda.empty_cache()
+    return res
+
+
+def mlp_case(wl, b, steps, warmup):
+    import torch
+    from test_rnn_layers_head_amd import inputs, ttt_mlp_fwd
+    x = inputs.make_inputs(wl)
+    d = device_inputs(x)
+    z = torch.empty((wl.B, wl.H, wl.T, wl.d), device="cuda")
+    w1 = torch.empty((wl.B, wl.H, wl.hidden, wl.d), device="cuda")
+    w2 = torch.empty((wl.B, wl.H, wl.d, wl.hidden), device="cuda")
+    launch = lambda: ttt_mlp_fwd(d["q"], d["k"], d["v"], d["eta"], d["w1"], d["w2"], b, z=z,
+                                 w1_out=w1, w2_out=w2)
+    wall, kmean, kmed = time_launches(launch, steps, warmup)
+    byts = mlp_alg_bytes(wl)
+    flops = mlp_alg_flops(wl, b)
+    # designed-traffic reading: the 2 x hidden x d fp32 state read and written
+    # once per mini-batch per unit
+    designed = byts + wl.units * ((wl.T + b - 1) // b) * 2 * (2 * wl.hidden * wl.d * 4)
+    t = kmean * 1e-6
+    return {
+        "workload": wl.name, "b": b, "token_heads_per_s": wl.token_heads / (wall * 1e-3),
+        "ms_per_step": wall, "kernel_us_mean": kmean, "kernel_us_median": kmed,
+        "alg_bytes": byts, "alg_flops": flops,
+        "mfma_frac_algorithmic": flops / t / 1e12 / BF16_PEAK_TFLOPS,
+        "hbm_frac_algorithmic": byts / t / 1e9 / HBM_PEAK_GBS,
+        "hbm_frac_designed_traffic": designed / t / 1e9 / HBM_PEAK_GBS,
+    }
+
+
+def stream_copy_GBps(nbytes=1 << 30, reps=10):
+    import torch
+    from test_rnn_layers_head_amd import bench_copy
+    src = torch.empty(nbytes // 4, device="cuda")
+    src.fill_(1.0)
+    dst = torch.empty_like(src)
+    launch = lambda: bench_copy(src, dst)
+    _, kmean, _ = time_launches(launch, reps, 2)
+    return 2 * nbytes / (kmean * 1e-6) / 1e9
+
+
+def cpu_baseline(x, b):
+    """The fp64 primal oracle as it stands, on the host cores."""
+    from oracle import oracle
+    n = oracle.default_threads()
+    q, k, v, eta = (a.astype(np.float64) for a in (x.q, x.k, x.v, x.eta))
+    t0 = time.perf_counter()
+    oracle.linear(q, k, v, eta, x.w0, b, nthreads=n)
+    dt = time.perf_counter() - t0
+    return {"value": x.wl.token_heads / dt, "unit": UNIT, "cores": n, "kind": "oracle",
+            "sample": f"all {x.wl.units} (batch, head) units of {x.wl.name}, b={b}, "
+                      f"fp64 sequential primal form, {dt:.2f} s wall"}
+
+
+def traffic_for(kernel_key: str, sources, launch_bytes_alg: int):
+    """HBM bytes per launch from committed counter readings (FETCH_SIZE +
+    WRITE_SIZE, scaled by the copy-kernel calibration), or None if the
+    readings are missing or were taken on different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    e = t.get(kernel_key)
+    if not e or e.get("source_hash") != source_hash(sources):
+        return None
+    return e["bytes_per_launch"]
+
+
+# --------------------------------------------------------------------------
+# Counter summary: rocprofv3 --pmc output -> profiles/traffic_counters.json
+# --------------------------------------------------------------------------
+def summarize_pmc(fetch_dir, write_dir):
+    import csv
+
+    def read(dirname, counter):
+        rows = []
+        for path in glob.glob(os.path.join(dirname, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if r.get("Counter_Name") == counter:
+                        rows.append((r["Kernel_Name"], float(r["Counter_Value"]), int(r["Dispatch_Id"])))
+        agg = {}
+        for name, val, disp in rows:  # sum over hardware instances per dispatch
+            agg.setdefault((name, disp), 0.0)
+            agg[(name, disp)] += val
+        out = {}
+        for (name, disp), val in agg.items():
+            out.setdefault(name, []).append(val)
+        return {k: float(np.median(v)) for k, v in out.items()}
+
+    fetch = read(fetch_dir, "FETCH_SIZE")
+    write = read(write_dir, "WRITE_SIZE")
+    copy_name = next(k for k in fetch if "stream_copy_kernel" in k)
+    copy_bytes = 1 << 30  # --pmc-calibrate copies 1 GiB
+    f_scale = copy_bytes / (fetch[copy_name] * 1024.0)
+    w_scale = copy_bytes / (write[copy_name] * 1024.0)
+    out = {"calibration": {"copy_bytes": copy_bytes, "fetch_kib": fetch[copy_name],
+                           "write_kib": write[copy_name], "fetch_scale": f_scale,
+                           "write_scale": w_scale}}
+    for key, pat, srcs in (("linear_scan", "linear_scan_kernel", SCAN_SOURCES),
+                           ("mlp_scan", "mlp_scan_kernel", MLP_SOURCES)):
+        names = [k for k in fetch if pat in k]
+        if not names:
+            continue
+        n = names[0]
+        out[key] = {"kernel": n, "fetch_kib": fetch[n], "write_kib": write.get(n, 0.0),
+                    "bytes_per_launch": fetch[n] * 1024 * f_scale + write.get(n, 0.0) * 1024 * w_scale,
+                    "source_hash": source_hash(srcs)}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extras", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--pmc-calibrate", action="store_true",
+                    help="also launch the 1 GiB streaming copy used to scale byte counters")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the scan shards over (batch, head) units with no communication, see DESIGN.md)",
+              file=sys.stderr)
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: multi-rank launch is not supported (one GPU only)", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    from test_rnn_layers_head_amd import _lib, inputs
+    _lib.lib()  # fail loudly if the HIP library is missing
+
+    wl = inputs.workload(3)
+    b = 16
+    log(f"[bench] generating {wl.name} inputs")
+    x = inputs.make_inputs(wl)
+    log(f"[bench] timing ttt_linear_fwd on {wl.name}: {args.warmup} warmup + {args.steps} steps")
+    head = linear_case(wl, b, args.steps, args.warmup, x=x)
+    log(f"[bench] {head['kernel_us_mean']:.1f} us/launch, {head['hbm_frac']:.3f} of HBM peak")
+
+    if args.pmc_calibrate:
+        log("[bench] streaming copy calibration (1 GiB)")
+        stream_copy_GBps(1 << 30, reps=3)
+
+    extras = {}
+    if not args.no_extras:
+        for bb in (1, 4, 64):
+            log(f"[bench] b sweep b={bb}")
+            extras[f"{wl.name}_b{bb}"] = linear_case(wl, bb, max(3, args.steps // 4), 2, x=x)
+        for wid in (2, 5):
+            w2 = inputs.workload(wid)
+            log(f"[bench] {w2.name}")
+            extras[w2.name] = linear_case(w2, 16, max(5, args.steps // 2), 2)
+        w4 = inputs.workload(4)
+        log(f"[bench] {w4.name}")
+        try:
+            extras[w4.name] = mlp_case(w4, 16, max(5, args.steps // 2), 2)
+        except Exception as e:  # reported, never silently replaced
+            extras[w4.name] = {"error": str(e)}
+        log("[bench] streaming copy reference")
+        extras["stream_copy_GBps"] = stream_copy_GBps()
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] timing the fp64 oracle on the host (CPU baseline)")
+        cpu = cpu_baseline(x, b)
+
+    traffic = traffic_for("linear_scan", SCAN_SOURCES, head["alg_bytes"])
+    rec = {
+        "metric": METRIC,
+        "value": head["token_heads_per_s"],
+        "unit": UNIT,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "d": wl.d, "b": b,
+                   "qkv_dtype": "bf16", "state_dtype": "f32", "global_batch": wl.B,
+                   "seq_len": wl.T, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": head["hbm_GBps"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": head["hbm_frac"], "traffic": traffic,
+                     "kernel": "linear_scan_kernel<bf16, b=16, 64 rows>",
+                     "alg_bytes_per_launch": head["alg_bytes"],
+                     "kernel_us_mean": head["kernel_us_mean"],
+                     "kernel_us_median": head["kernel_us_median"],
+                     "mfma_frac": head["mfma_frac"]},
+        "cpu_baseline": cpu,
+        "extras": extras,
+    }
+    print(json.dumps(rec))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
