@@ -91,9 +91,12 @@ ttt_status_t check_common(const char* fn, ttt_dtype_t dt, int32_t w0_per_batch, 
   return TTT_OK;
 }
 
+// Rows of W per workgroup: one workgroup per CU when there are enough
+// (batch, head) units, finer row slices (more workgroups) when there are few.
 int auto_rows(int64_t units) {
-  (void)units;
-  return 64;
+  if (units >= 256) return 64;
+  if (units > 64) return 32;
+  return 16;
 }
 
 ttt_status_t linear_impl(const void* q, const void* k, const void* v, const float* eta,

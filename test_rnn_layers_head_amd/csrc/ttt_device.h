@@ -49,29 +49,44 @@ __device__ __forceinline__ float bf16_val(short h) {
 struct Split4 {
   s16x4 hi, lo;
 };
-__device__ __forceinline__ Split4 split4(f32x4 x) {
-  Split4 s;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    short h = bf16_bits(x[r]);
-    s.hi[r] = h;
-    s.lo[r] = bf16_bits(x[r] - bf16_val(h));
-  }
-  return s;
-}
+__device__ __forceinline__ Split4 split4(f32x4 x);
 struct Split8 {
   bf16x8 hi, lo;
 };
+// hi/lo split of two fp32 values at once: one packed conversion for the
+// high halves, the exact residuals, one packed conversion for the low halves.
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+  const float r0 = x0 - __builtin_bit_cast(float, h << 16);
+  const float r1 = x1 - __builtin_bit_cast(float, h & 0xffff0000u);
+  hi = h;
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
+}
+__device__ __forceinline__ Split4 split4(f32x4 x) {
+  uint32_t h0, l0, h1, l1;
+  split_pair(x[0], x[1], h0, l0);
+  split_pair(x[2], x[3], h1, l1);
+  return Split4{__builtin_bit_cast(s16x4, make_uint2(h0, h1)),
+                __builtin_bit_cast(s16x4, make_uint2(l0, l1))};
+}
+// Two fp32 values that are exactly representable in bf16, packed.
+__device__ __forceinline__ uint32_t pack_exact(float x0, float x1) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+}
 // Pack two accumulator registers (4 + 4 values) into one 8-wide operand.
 __device__ __forceinline__ Split8 split8(f32x4 a, f32x4 b) {
+  uint32_t h[4], l[4];
+  split_pair(a[0], a[1], h[0], l[0]);
+  split_pair(a[2], a[3], h[1], l[1]);
+  split_pair(b[0], b[1], h[2], l[2]);
+  split_pair(b[2], b[3], h[3], l[3]);
   Split8 s;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    float x = r < 4 ? a[r] : b[r - 4];
-    bf16 h = (bf16)x;
-    s.hi[r] = h;
-    s.lo[r] = (bf16)(x - (float)h);
-  }
+  s.hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+  s.lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
   return s;
 }
 

@@ -40,6 +40,7 @@ struct MlpArgs {
 
 // rows: rows of W per workgroup (64, 32 or 16).
 hipError_t launch_linear(const LinearArgs& a, bool f32in, int rows, hipStream_t s);
+hipError_t launch_linear_bf16(const LinearArgs& a, int rows, hipStream_t s);
 hipError_t launch_mlp(const MlpArgs& a, bool f32in, hipStream_t s);
 hipError_t launch_copy_state(const float* src, int per_unit, int units, int H, int n,
                              float* dst, hipStream_t s);

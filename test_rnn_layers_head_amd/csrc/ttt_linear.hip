@@ -1,4 +1,5 @@
-// TTT-Linear forward scan for gfx950 (MI355X), mini-batch TTT in dual form.
+// TTT-Linear forward scan for gfx950 (MI355X), mini-batch TTT in dual form:
+// the fp32-input kernel (bf16 inputs take ttt_linear_bf16.hip).
 //
 // Method ("论文速览 | TTT", equinox-blog close reading of "Learning to
 // (Learn at Test Time)"): §3.5 mini-batch GD with the gradient point at the
@@ -324,15 +325,11 @@ static hipError_t launch_rows(const LinearArgs& a, int rows, hipStream_t s) {
 }
 
 hipError_t launch_linear(const LinearArgs& a, bool f32in, int rows, hipStream_t s) {
+  if (!f32in) return launch_linear_bf16(a, rows, s);
   const int mode = a.b == 16 ? MODE_B16 : (a.b < 16 ? MODE_SUB : MODE_MULTI);
-  if (f32in) {
-    if (mode == MODE_B16) return launch_rows<true, MODE_B16>(a, rows, s);
-    if (mode == MODE_SUB) return launch_rows<true, MODE_SUB>(a, rows, s);
-    return launch_rows<true, MODE_MULTI>(a, rows, s);
-  }
-  if (mode == MODE_B16) return launch_rows<false, MODE_B16>(a, rows, s);
-  if (mode == MODE_SUB) return launch_rows<false, MODE_SUB>(a, rows, s);
-  return launch_rows<false, MODE_MULTI>(a, rows, s);
+  if (mode == MODE_B16) return launch_rows<true, MODE_B16>(a, rows, s);
+  if (mode == MODE_SUB) return launch_rows<true, MODE_SUB>(a, rows, s);
+  return launch_rows<true, MODE_MULTI>(a, rows, s);
 }
 
 }  // namespace ttt

@@ -1,0 +1,449 @@
+// TTT-Linear forward scan, bf16 Q/K/V (the production path), gfx950.
+//
+// Method ("论文速览 | TTT", equinox-blog close reading of "Learning to
+// (Learn at Test Time)"): mini-batch GD with the gradient taken at the state
+// before the mini-batch (§3.5), evaluated per 16-token tile in the dual form
+// of §3.6 with the per-token eta of §4.6 and f(x) = W x (§4.4):
+//   P = W K, G = 2 (P - V) diag(eta), Z = W Q - G triu(K^T Q), W <- W - G K^T
+// (columns are tokens; the inclusive causal mask lets token t see its own
+// update, §3.1).  The kernels carry Gn = -G ("negative gradient").
+//
+// Workgroup = one (batch, head, slice of ROWS rows of W):
+//   waves 0 .. NCW-1  compute waves, 16 rows of W each, fp32 state resident
+//                     in MFMA accumulators for the whole sequence;
+//   waves NCW, NCW+1  helpers: build every per-tile operand that depends only
+//                     on K, Q, eta, one tile ahead, into a double-buffered
+//                     "prepared" LDS area laid out lane-linear (conflict-free
+//                     16-byte reads); helper 0 makes triu(K^T Q), K_{j-1}^T K_j,
+//                     2 eta (and the sub-batch inverse), helper 1 K_{j-1}^T Q_j
+//                     and the update operand;
+//   wave NCW+2        loader: buffer->LDS DMA of 16-token K/Q/V/eta tiles,
+//                     D tiles ahead, into a ring (zero-filled past T).
+//
+// Serial chain per tile.  Only P_j = W_j K_j feeds the recurrence.  Using
+//   P_{j+1} = W_j K_{j+1} + Gn_j (K_j^T K_{j+1})     (W_{j+1} = W_j + Gn_j K_j^T)
+// the large product W_j K_{j+1} (and W_j Q_{j+1}) is formed one tile early
+// from W_j, so the per-tile critical path is two MFMAs plus the gradient's
+// few VALU ops; the W update, the bf16 hi/lo split of W and the output
+// products overlap with it.  V enters the same accumulator exactly, as
+// (-I) applied to V's rows on MFMA, so the chain yields P - V directly.
+//
+// Precision: fp32 operands enter bf16 MFMA as hi + lo pairs (three products
+// kept, error ~2^-16 relative); K, Q, V are exact bf16; accumulation fp32.
+//
+// Column order.  Compute wave register W[m][r] of lane (c, g) holds
+// W[row c][sigma(m, 4g + r)] with sigma(m, 4g + r) = 32(m/2) + 8g + 4(m%2) + r,
+// the accumulator layout of the rank-16 update with a permuted output index.
+// With it, the reduction slots 8g..8g+7 of the K=32 MFMA that forms W K
+// are the 8 consecutive columns 32h + 8g .. +7, i.e. one 16-byte chunk of a
+// K row.  K/Q tiles are stored with chunk p of row r at position
+// p ^ (r & 7) (applied by the DMA's source addresses), which makes those
+// 16-row chunk reads bank-conflict free.
+#include "ttt_device.h"
+#include "ttt_launch.h"
+
+namespace ttt {
+namespace {
+
+enum { MODE_B16 = 0, MODE_SUB = 1, MODE_MULTI = 2 };
+
+template <int ROWS>
+struct Geom {
+  static constexpr int NCW = ROWS / 16;
+  static constexpr int KB = 16 * 64 * 2;         // K or Q tile (bf16)
+  static constexpr int VB = 16 * ROWS * 2;       // V tile, this slice's columns
+  static constexpr int RAW = 2 * KB + VB + 64;   // + eta (16 fp32)
+  static constexpr int NI = 4 + (VB + 1023) / 1024 + 1;  // DMA ops per tile
+  static constexpr int D = (63 / NI) < 10 ? (63 / NI) : 10;
+  static constexpr int NST = D + 2;
+  // prepared-operand slot (per tile), byte offsets
+  static constexpr int P_E2 = 0;                  // 2 eta_t, 16 fp32
+  static constexpr int P_A = 64;                  // triu(K^T Q), hi | lo
+  static constexpr int P_MKK = P_A + 1024;        // K_{j-1}^T K_j, hi | lo
+  static constexpr int P_MKQ = P_MKK + 1024;      // K_{j-1}^T Q_j, hi | lo
+  static constexpr int P_KT = P_MKQ + 1024;       // update operand K[t][j], x2
+  static constexpr int P_U = P_KT + 4096;         // sub-batch inverse (b < 16)
+  static constexpr int PREP = P_U + 1024;
+  static constexpr int LDS = NST * RAW + 2 * PREP;
+  static constexpr int THREADS = (NCW + 3) * 64;  // + 2 helpers + loader
+};
+
+__device__ __forceinline__ uint2 s4u(s16x4 v) { return __builtin_bit_cast(uint2, v); }
+__device__ __forceinline__ s16x4 u2s(uint2 v) { return __builtin_bit_cast(s16x4, v); }
+
+// s_waitcnt lgkmcnt(0): every LDS read issued so far has returned.
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+// byte offset of element (r, j) of a swizzled 16 x 64 bf16 K/Q tile
+__device__ __forceinline__ int swz(int r, int j) {
+  return r * 128 + ((((j >> 3) ^ (r & 7))) << 4) + ((j & 7) << 1);
+}
+// K=32 operand of row r: columns 32h + 8g .. 32h + 8g + 7
+__device__ __forceinline__ bf16x8 row_chunk(const char* tile, int r, int h, int g) {
+  return *(const bf16x8*)(tile + r * 128 + ((((4 * h + g) ^ (r & 7))) << 4));
+}
+__device__ __forceinline__ int sigma(int m, int row) {
+  return 32 * (m >> 1) + 8 * (row >> 2) + 4 * (m & 1) + (row & 3);
+}
+
+__device__ __forceinline__ void put_split(char* p, int lane, f32x4 x) {
+  const Split4 s = split4(x);
+  const uint2 h = s4u(s.hi), l = s4u(s.lo);
+  *(uint4*)(p + lane * 16) = make_uint4(h.x, h.y, l.x, l.y);
+}
+
+// Operand pair of a pre-split Y for products X*Y: [Yhi | Yhi] and [Ylo | 0].
+struct YOps {
+  bf16x8 hh, l0;
+};
+__device__ __forceinline__ YOps yops(const Split4& y) {
+  const s16x4 z = {0, 0, 0, 0};
+  return YOps{cat44(y.hi, y.hi), cat44(y.lo, z)};
+}
+// acc + X*Y, X given as [Xhi | Xlo] of the accumulator layout of X^T:
+// [Xhi|Xlo].[Yhi|Yhi] + [Xhi|Xlo].[Ylo|0] = Xhi Yhi + Xlo Yhi + Xhi Ylo.
+__device__ __forceinline__ f32x4 mm_pre(bf16x8 x, const YOps& y, f32x4 acc) {
+  acc = mfma_k32(x, y.hh, acc);
+  acc = mfma_k32(x, y.l0, acc);
+  return acc;
+}
+__device__ __forceinline__ bf16x8 get8(const char* p, int lane) {
+  return *(const bf16x8*)(p + lane * 16);
+}
+
+template <int MODE, int ROWS>
+__global__ void __launch_bounds__((Geom<ROWS>::THREADS))
+linear_scan_bf16_kernel(LinearArgs a) {
+  using G = Geom<ROWS>;
+  constexpr int NSPLIT = 64 / ROWS;
+  __shared__ __attribute__((aligned(16))) char smem[G::LDS];
+  char* const raw = smem;
+  char* const prep = smem + G::NST * G::RAW;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+
+  int unit, slice;
+  if (NSPLIT == 1) {
+    unit = blockIdx.x;
+    slice = 0;
+  } else {  // slices of one unit on one XCD (workgroups go round-robin over 8)
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    slice = slot % NSPLIT;
+    unit = (slot / NSPLIT) * 8 + xcd;
+  }
+  if (unit >= a.units) return;
+  const int head = unit % a.H;
+  const int T = a.T;
+  const int ntiles = (T + 15) >> 4;
+  const int row0 = slice * ROWS;
+
+  // ================================================================ loader
+  // Barrier B_j (j = -1 .. ntiles-1) releases compute iteration j (which
+  // reads raw tile j+1) and helper iteration j (which prepares tile j+1 from
+  // raw tile j+1); before it the loader makes sure raw tiles <= j+1 have
+  // landed.  Tile j+D+1 is issued after B_{j-1}, while the other waves read
+  // only raw tile j, hence NST = D + 2 ring slots.
+  if (wave == G::NCW + 2) {
+    const uint32_t ubytes = (uint32_t)T * 128;
+    const size_t uoff = (size_t)unit * T * 64;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc((const short*)a.k + uoff, ubytes);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const short*)a.q + uoff, ubytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const short*)a.v + uoff, ubytes);
+    const __amdgpu_buffer_rsrc_t re = make_rsrc(a.eta + (size_t)unit * T, (uint32_t)T * 4);
+    const int krow = lane >> 3, kpos = lane & 7;
+    auto issue = [&](int j) {
+      char* st = raw + (j % G::NST) * G::RAW;
+      const uint32_t tb = (uint32_t)j * 2048;
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const int r = 8 * n + krow;
+        const uint32_t off = tb + r * 128 + ((kpos ^ (r & 7)) << 4);
+        dma16(rk, st + n * 1024, off);
+        dma16(rq, st + G::KB + n * 1024, off);
+      }
+#pragma unroll
+      for (int n = 0; n < (G::VB + 1023) / 1024; ++n) {
+        const int byte = n * 1024 + lane * 16;
+        if (G::VB % 1024 == 0 || byte < G::VB) {
+          const int tok = byte / (ROWS * 2), cb = byte % (ROWS * 2);
+          dma16(rv, st + 2 * G::KB + n * 1024, (uint32_t)(j * 16 + tok) * 128 + row0 * 2 + cb);
+        }
+      }
+      if (lane < 16) dma4(re, st + 2 * G::KB + G::VB, (uint32_t)(j * 16 + lane) * 4);
+    };
+    const int pro = ntiles < G::D + 1 ? ntiles : G::D + 1;
+    for (int j = 0; j < pro; ++j) issue(j);
+    if (pro == G::D + 1) wait_vmcnt<G::NI * G::D>();  // tile 0 landed
+    else wait_vmcnt<0>();
+    wg_barrier();  // B_{-1}
+    for (int j = 0; j < ntiles; ++j) {
+      if (j + G::D + 1 < ntiles) {
+        issue(j + G::D + 1);
+        wait_vmcnt<G::NI * G::D>();  // tiles <= j+1 landed
+      } else {
+        wait_vmcnt<0>();
+      }
+      wg_barrier();  // B_j
+    }
+    return;
+  }
+
+  // ================================================================ helper
+  // Iteration j (between B_j and B_{j+1}, j = -1 .. ntiles-2) prepares tile
+  // j+1 into prepared slot (j+1) & 1, which compute iteration j+1 reads.
+  if (wave >= G::NCW) {
+    const bool h0 = wave == G::NCW;  // helper 0 or helper 1
+    bf16x8 kprev[2], sel[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      for (int e = 0; e < 8; ++e) {
+        kprev[h][e] = (bf16)0.f;
+        // slot 8g+e of block m/2 selects column sigma(m, c) for m % 2 == h
+        sel[h][e] = (bf16)((g == (c >> 2) && e == 4 * h + (c & 3)) ? 1.f : 0.f);
+      }
+    wg_barrier();  // B_{-1}
+    for (int j = -1; j < ntiles - 1; ++j) {
+      const int tn = j + 1;
+      const char* st = raw + (tn % G::NST) * G::RAW;
+      const char* Kt = st;
+      const char* Qt = st + G::KB;
+      const float* Et = (const float*)(st + 2 * G::KB + G::VB);
+      char* pp = prep + (tn & 1) * G::PREP;
+
+      bf16x8 kop[2], qop[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        kop[h] = row_chunk(Kt, c, h, g);
+        qop[h] = row_chunk(Qt, c, h, g);
+      }
+      // all products first (independent MFMAs back to back), then the
+      // conversions, then the stores
+      if (h0) {
+        f32x4 A = {0, 0, 0, 0}, Mkk = {0, 0, 0, 0};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          A = mfma_k32(kop[h], qop[h], A);        // A[s = 4g+r][t = c] = k_s . q_t
+          Mkk = mfma_k32(kprev[h], kop[h], Mkk);  // k^{prev}_s . k_t
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * g + r > c) A[r] = 0.f;
+        put_split(pp + G::P_A, lane, A);
+        put_split(pp + G::P_MKK, lane, Mkk);
+        if (lane < 16) ((float*)(pp + G::P_E2))[lane] = 2.f * Et[lane];
+      } else {
+        f32x4 Mkq = {0, 0, 0, 0}, KS[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) Mkq = mfma_k32(kprev[h], qop[h], Mkq);  // k^{prev}_s . q_t
+        // Update operand kt[m][e] = K[t = 4g+e][sigma(m, c)], formed exactly
+        // as K S_m with the one-hot selection S_m[j][c] = [j == sigma(m, c)]
+        // (only the 32 columns of block m/2 can be selected).
+#pragma unroll
+        for (int m = 0; m < 4; ++m) KS[m] = mfma_k32(kop[m >> 1], sel[m & 1], f32x4{0, 0, 0, 0});
+        put_split(pp + G::P_MKQ, lane, Mkq);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t p0 = pack_exact(KS[m][0], KS[m][1]), p1 = pack_exact(KS[m][2], KS[m][3]);
+          *(uint4*)(pp + G::P_KT + m * 1024 + lane * 16) = make_uint4(p0, p1, p0, p1);  // [kt | kt]
+        }
+      }
+
+      if (MODE == MODE_SUB && h0) {  // helper 0 only
+        // Sub-batches of b tokens inside the tile: G (I + N) = E with
+        // N[s][t] = 2 eta_t k_s.k_t for sub-batch(s) < sub-batch(t);
+        // U = (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8), cut at N^{16/b}.
+        const int bsub = a.b;
+        f32x4 M = {0, 0, 0, 0};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) M = mfma_k32(kop[h], kop[h], M);
+        const float eta_c = Et[c];
+        const f32x4 eta4 = *(const f32x4*)(Et + 4 * g);
+        f32x4 N, NT, I;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int s = 4 * g + r;
+          N[r] = (s / bsub < c / bsub) ? 2.f * eta_c * M[r] : 0.f;
+          NT[r] = (c / bsub < s / bsub) ? 2.f * eta4[r] * M[r] : 0.f;  // M symmetric
+          I[r] = (s == c) ? 1.f : 0.f;
+        }
+        const f32x4 Z0 = {0, 0, 0, 0};
+        auto mm = [&](f32x4 xt, f32x4 y) { return mm16_split(xt, y, Z0); };
+        const int nblk = 16 / bsub;
+        f32x4 U;
+        if (nblk == 2) {
+          U = I - N;
+        } else {
+          const f32x4 N2 = mm(NT, N), N2T = mm(N, NT);
+          f32x4 tail;
+          if (nblk == 4) {
+            tail = I + N2;
+          } else {
+            const f32x4 N4 = mm(N2T, N2);
+            f32x4 t4;
+            if (nblk == 8) {
+              t4 = I + N4;
+            } else {
+              const f32x4 N4T = mm(N2, N2T);
+              t4 = mm(I + N4T, I + mm(N4T, N4));
+            }
+            tail = mm(I + N2T, t4);
+          }
+          U = mm(I - NT, tail);
+        }
+        put_split(pp + G::P_U, lane, U);
+      }
+      kprev[0] = kop[0];
+      kprev[1] = kop[1];
+      wait_lgkm0();
+      wg_barrier();  // B_{j+1}
+    }
+    return;
+  }
+
+  // =============================================================== compute
+  // Iteration j enters with W = W_j (fp32 accumulators), XB = W_{j-1} K_j - V_j
+  // and RB = W_{j-1} Q_j (formed in iteration j-1), and gp = operands of Gn_{j-1}.
+  const int rbase = row0 + wave * 16;
+  const float* w0 = a.w0 + (size_t)(a.w0_per_batch ? unit : head) * 4096;
+  f32x4 W[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    W[m] = *(const f32x4*)(w0 + (rbase + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1));
+  const int tpm = MODE == MODE_MULTI ? (a.b >> 4) : 1;  // tiles per mini-batch
+  // -I on the 16 V columns of this wave: X = -V_block lands in accumulator
+  // layout when V's rows are the A-operand (slots 16..31 are unused).
+  bf16x8 negI;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) negI[e] = (bf16)((g < 2 && 8 * g + e == c) ? -1.f : 0.f);
+  const int voff = (16 * wave + 8 * (g & 1)) * 2;  // V row chunk of this lane
+  YOps gp;  // operands of the previous tile's negative gradient
+  gp.hh = cat44(s16x4{0, 0, 0, 0}, s16x4{0, 0, 0, 0});
+  gp.l0 = gp.hh;
+  Split8 wg[2];  // gradient point operands (b > 16)
+
+  wg_barrier();  // B_{-1}: raw tile 0 is in LDS
+  f32x4 XB = {0, 0, 0, 0}, RB = {0, 0, 0, 0};
+  {
+    const Split8 ws[2] = {split8(W[0], W[1]), split8(W[2], W[3])};
+    wg[0] = ws[0];
+    wg[1] = ws[1];
+    const char* st = raw;
+    XB = mfma_k32(*(const bf16x8*)(st + 2 * G::KB + c * (ROWS * 2) + voff), negI, XB);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bf16x8 kk = row_chunk(st, c, h, g), qq = row_chunk(st + G::KB, c, h, g);
+      XB = mfma_k32(kk, ws[h].hi, XB);
+      XB = mfma_k32(kk, ws[h].lo, XB);
+      RB = mfma_k32(qq, ws[h].hi, RB);
+      RB = mfma_k32(qq, ws[h].lo, RB);
+    }
+  }
+
+  // Z through a range-checked buffer: rows past T (padding of the last
+  // tile) are dropped by the hardware, so the loop body has no branches and
+  // the scheduler can interleave the serial chain with everything else.
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(a.z + (size_t)unit * T * 64, (uint32_t)T * 256);
+  uint32_t zoff = (uint32_t)((4 * g * 64 + rbase + c) * 4);
+
+  for (int j = 0; j < ntiles; ++j) {
+    wait_lgkm0();
+    wg_barrier();  // B_j
+    const char* pp = prep + (j & 1) * G::PREP;
+    const char* st = raw + ((j + 1) % G::NST) * G::RAW;  // tile j+1 (stale past the end)
+    const f32x4 e2 = *(const f32x4*)(pp + G::P_E2 + 16 * g);
+    const bool new_mb = MODE != MODE_MULTI || (j % tpm) == 0;
+    const bool next_new_mb = MODE != MODE_MULTI || ((j + 1) % tpm) == 0;
+
+    // ---- serial chain: X_j = P_j - V_j, then Gn_j = 2 eta (v - p).
+    // (gp is zero at j = 0; within a b > 16 mini-batch P keeps its gradient
+    // point and takes no correction.)
+    f32x4 X = mm_pre(get8(pp + G::P_MKK, lane), gp, XB);
+    if (MODE == MODE_MULTI) X = new_mb ? X : XB;
+    f32x4 E;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) E[r] = -e2[r] * X[r];
+    if constexpr (MODE == MODE_SUB) E = mm_pre(get8(pp + G::P_U, lane), yops(split4(E)), f32x4{0, 0, 0, 0});
+    const Split4 gs = split4(E);
+    const YOps gy = yops(gs);
+
+    // ---- split of W_j and the next tile's products with it
+    const Split8 ws[2] = {split8(W[0], W[1]), split8(W[2], W[3])};
+    if (MODE == MODE_MULTI) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        wg[h].hi = new_mb ? ws[h].hi : wg[h].hi;
+        wg[h].lo = new_mb ? ws[h].lo : wg[h].lo;
+      }
+    }
+    f32x4 XBn = mfma_k32(*(const bf16x8*)(st + 2 * G::KB + c * (ROWS * 2) + voff), negI,
+                         f32x4{0, 0, 0, 0});
+    f32x4 RBn = {0, 0, 0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bf16x8 kk = row_chunk(st, c, h, g), qq = row_chunk(st + G::KB, c, h, g);
+      bf16x8 whi = ws[h].hi, wlo = ws[h].lo;
+      if (MODE == MODE_MULTI) {
+        whi = next_new_mb ? whi : wg[h].hi;
+        wlo = next_new_mb ? wlo : wg[h].lo;
+      }
+      XBn = mfma_k32(kk, whi, XBn);
+      XBn = mfma_k32(kk, wlo, XBn);
+      RBn = mfma_k32(qq, ws[h].hi, RBn);
+      RBn = mfma_k32(qq, ws[h].lo, RBn);
+    }
+
+    // ---- outputs: Z_j = W_j Q_j + Gn_j triu(K_j^T Q_j)
+    f32x4 Z = mm_pre(get8(pp + G::P_MKQ, lane), gp, RB);
+    Z = mm_pre(get8(pp + G::P_A, lane), gy, Z);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float zr = Z[r];  // element by value (a bit_cast of Z[r] itself reads element 0)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(zr), rz, zoff + r * 256, 0, 2);
+    }
+    zoff += 16 * 64 * 4;
+
+    // ---- rank-16 update W_{j+1} = W_j + Gn_j K_j^T
+    const bf16x8 g2 = cat44(gs.hi, gs.lo);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) W[m] = mfma_k32(get8(pp + G::P_KT + m * 1024, lane), g2, W[m]);
+    XB = XBn;
+    RB = RBn;
+    gp = gy;
+  }
+
+  float* wo = a.w_out + (size_t)unit * 4096;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    *(f32x4*)(wo + (rbase + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1)) = W[m];
+}
+
+template <int MODE, int ROWS>
+hipError_t launch_one(const LinearArgs& a, hipStream_t s) {
+  constexpr int NSPLIT = 64 / ROWS;
+  const int blocks = NSPLIT == 1 ? a.units : ((a.units + 7) / 8) * 8 * NSPLIT;
+  hipLaunchKernelGGL((linear_scan_bf16_kernel<MODE, ROWS>), dim3(blocks),
+                     dim3(Geom<ROWS>::THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_rows(const LinearArgs& a, int rows, hipStream_t s) {
+  switch (rows) {
+    case 64: return launch_one<MODE, 64>(a, s);
+    case 32: return launch_one<MODE, 32>(a, s);
+    default: return launch_one<MODE, 16>(a, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_linear_bf16(const LinearArgs& a, int rows, hipStream_t s) {
+  if (a.b == 16) return launch_rows<MODE_B16>(a, rows, s);
+  if (a.b < 16) return launch_rows<MODE_SUB>(a, rows, s);
+  return launch_rows<MODE_MULTI>(a, rows, s);
+}
+
+}  // namespace ttt

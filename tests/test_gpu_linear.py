@@ -99,8 +99,10 @@ def test_deterministic_reruns():
 
 @pytest.mark.parametrize("b", [4, 16, 64])
 def test_state_passing_in_place(b):
-    """Two calls (the second resuming in place from the first's final state)
-    equal one call, bit for bit, when the split falls on a mini-batch edge."""
+    """Two calls, the second resuming in place from the first's final state,
+    give the same result as one call (within rounding: the resumed call forms
+    its first tile's products directly instead of through the one-tile
+    lookahead), and both match the oracle."""
     x = small(2, 4, 320, "bf16", seed=9)
     z, w = gu.run_linear(x, b)
     T1 = 192
@@ -114,8 +116,14 @@ def test_state_passing_in_place(b):
                            v[:, :, T1:].contiguous(), eta[:, :, T1:].contiguous(), state, b,
                            w_out=state)
     torch.cuda.synchronize()
-    assert np.array_equal(torch.cat([z1, z2], dim=2).cpu().numpy(), z)
-    assert np.array_equal(state.cpu().numpy(), w)
+    z12 = torch.cat([z1, z2], dim=2).cpu().numpy()
+    w12 = state.cpu().numpy()
+    assert gu.metrics(z12, z)["rel_l2"] < 1e-4 and gu.metrics(w12, w)["rel_l2"] < 1e-4
+    zr, wr = gu.oracle_linear(x, b)
+    gu.assert_close(z12, zr, "bf16", "z (two calls)")
+    gu.assert_close(w12, wr, "bf16", "w (two calls)")
+    # the first call alone is bit-identical to the first T1 tokens of one call
+    assert np.array_equal(z1.cpu().numpy(), z[:, :, :T1])
 
 
 def test_side_stream_ordering():
