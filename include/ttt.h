@@ -13,8 +13,8 @@
  *   §3.5  mini-batch GD: tokens [j*b, j*b + b) all take their gradient at the
  *         state before that mini-batch; a final partial mini-batch is shorter;
  *   §3.6  dual form for f(x) = W x;  §3.7 dual form for an MLP inner model;
- *   §4.4  TTT-Linear f(x) = W x and TTT-MLP f(x) = W2 GELU(W1 x) (exact erf
- *         GELU, hidden width 4d);
+ *   §4.4  TTT-Linear f(x) = W x and TTT-MLP f(x) = W2 GELU(W1 x) (GELU =
+ *         x Phi(x), hidden width 4d);
  *   §4.6  a per-token inner learning rate eta_t scales token t's gradient.
  *
  * Conventions shared by every entry point
@@ -42,9 +42,11 @@
  *            its initial-state input only when w0_per_batch = 1 and the two
  *            pointers are equal (in-place resume); any other overlap is
  *            TTT_ERR_ALIAS.
- * Support:   d = 64; TTT-MLP hidden = 256; mini-batch b with b | 16 or
- *            16 | b (1, 2, 4, 8, 16, 32, 48, 64, ...); any T >= 0, B, H >= 0
- *            with B*H*T*d < 2^31.  Anything else is TTT_ERR_UNSUPPORTED.
+ * Support:   d = 64; any T >= 0, B, H >= 0 with B*H*T*d < 2^31.
+ *            TTT-Linear: fp32 or bf16 q/k/v; mini-batch b with b | 16 or
+ *            16 | b (1, 2, 4, 8, 16, 32, 48, 64, ...).
+ *            TTT-MLP: hidden = 256, bf16 q/k/v, b | 16 (1, 2, 4, 8, 16).
+ *            Anything else is TTT_ERR_UNSUPPORTED.
  *            Empty work (B*H == 0) returns TTT_OK without launching; T == 0
  *            copies the initial states to the final-state outputs.
  */
@@ -102,7 +104,8 @@ ttt_status_t ttt_linear_fwd(const void* q, const void* k, const void* v,
  *   w1_out, w2_out : out [B][H][hidden][d], [B][H][d][hidden] fp32
  *
  * Both layers take their gradient of sum_t eta_t ||f(k_t) - v_t||^2 at the
- * state before the mini-batch; GELU is x * Phi(x) with the exact erf.
+ * state before the mini-batch.  GELU is x * Phi(x); on the device erf is the
+ * Abramowitz & Stegun 7.1.26 approximation (absolute error <= 1.5e-7).
  */
 ttt_status_t ttt_mlp_fwd(const void* q, const void* k, const void* v,
                          const float* eta, const float* w1_0,

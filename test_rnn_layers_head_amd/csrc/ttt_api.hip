@@ -172,6 +172,10 @@ ttt_status_t ttt_mlp_fwd(const void* q, const void* k, const void* v, const floa
   if (st != TTT_OK) return st;
   if (hidden != 256)
     return fail(TTT_ERR_UNSUPPORTED, "%s: hidden=%d unsupported (only 256)", fn, hidden);
+  if (qkv_dtype != TTT_BF16)
+    return fail(TTT_ERR_UNSUPPORTED, "%s: only bf16 q/k/v are supported", fn);
+  if (b > 16)
+    return fail(TTT_ERR_UNSUPPORTED, "%s: mini-batch b=%d unsupported (need b | 16)", fn, b);
   if (units == 0) return TTT_OK;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
