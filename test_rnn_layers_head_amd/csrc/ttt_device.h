@@ -71,8 +71,8 @@ __device__ __forceinline__ Split4 split4(f32x4 x) {
   return Split4{__builtin_bit_cast(s16x4, make_uint2(h0, h1)),
                 __builtin_bit_cast(s16x4, make_uint2(l0, l1))};
 }
-// Two fp32 values that are exactly representable in bf16, packed.
-__device__ __forceinline__ uint32_t pack_exact(float x0, float x1) {
+// Two fp32 values rounded to bf16 (nearest even) and packed.
+__device__ __forceinline__ uint32_t pack_rne(float x0, float x1) {
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
@@ -87,6 +87,35 @@ __device__ __forceinline__ Split8 split8(f32x4 a, f32x4 b) {
   Split8 s;
   s.hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
   s.lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
+  return s;
+}
+
+// Residual split on the matrix unit.  For two accumulator blocks a (operand
+// slots 0..3) and b (slots 4..7): hi = RNE bf16 of both (packed converts),
+// then a - hi(a) and b - hi(b) are formed exactly by a K=32 MFMA that adds
+// -hi through a negated one-hot selection (each output entry receives one
+// exact product), and converted to the lo halves.  8 VALU + 2 MFMA instead of
+// 24 VALU for the same 8 values.
+struct NegSel {
+  bf16x8 s0, s1;  // -I on slots 0..3 / on slots 4..7
+};
+__device__ __forceinline__ NegSel make_negsel(int c, int g) {
+  NegSel n;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    n.s0[e] = (bf16)((e < 4 && c == 4 * g + e) ? -1.f : 0.f);
+    n.s1[e] = (bf16)((e >= 4 && c == 4 * g + e - 4) ? -1.f : 0.f);
+  }
+  return n;
+}
+__device__ __forceinline__ Split8 split8_mfma(f32x4 a, f32x4 b, const NegSel& ns) {
+  Split8 s;
+  s.hi = __builtin_bit_cast(bf16x8, make_uint4(pack_rne(a[0], a[1]), pack_rne(a[2], a[3]),
+                                               pack_rne(b[0], b[1]), pack_rne(b[2], b[3])));
+  const f32x4 ra = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ns.s0, s.hi, a, 0, 0, 0);
+  const f32x4 rb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ns.s1, s.hi, b, 0, 0, 0);
+  s.lo = __builtin_bit_cast(bf16x8, make_uint4(pack_rne(ra[0], ra[1]), pack_rne(ra[2], ra[3]),
+                                               pack_rne(rb[0], rb[1]), pack_rne(rb[2], rb[3])));
   return s;
 }
 

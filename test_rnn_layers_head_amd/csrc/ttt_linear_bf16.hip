@@ -246,7 +246,7 @@ linear_scan_bf16_kernel(LinearArgs a) {
         put_split(pp + G::P_MKQ, lane, Mkq);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const uint32_t p0 = pack_exact(KS[m][0], KS[m][1]), p1 = pack_exact(KS[m][2], KS[m][3]);
+          const uint32_t p0 = pack_rne(KS[m][0], KS[m][1]), p1 = pack_rne(KS[m][2], KS[m][3]);
           *(uint4*)(pp + G::P_KT + m * 1024 + lane * 16) = make_uint4(p0, p1, p0, p1);  // [kt | kt]
         }
       }
@@ -313,6 +313,7 @@ linear_scan_bf16_kernel(LinearArgs a) {
   for (int m = 0; m < 4; ++m)
     W[m] = *(const f32x4*)(w0 + (rbase + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1));
   const int tpm = MODE == MODE_MULTI ? (a.b >> 4) : 1;  // tiles per mini-batch
+  const NegSel ns = make_negsel(c, g);
   // -I on the 16 V columns of this wave: X = -V_block lands in accumulator
   // layout when V's rows are the A-operand (slots 16..31 are unused).
   bf16x8 negI;
@@ -327,7 +328,7 @@ linear_scan_bf16_kernel(LinearArgs a) {
   wg_barrier();  // B_{-1}: raw tile 0 is in LDS
   f32x4 XB = {0, 0, 0, 0}, RB = {0, 0, 0, 0};
   {
-    const Split8 ws[2] = {split8(W[0], W[1]), split8(W[2], W[3])};
+    const Split8 ws[2] = {split8_mfma(W[0], W[1], ns), split8_mfma(W[2], W[3], ns)};
     wg[0] = ws[0];
     wg[1] = ws[1];
     const char* st = raw;
@@ -370,7 +371,7 @@ linear_scan_bf16_kernel(LinearArgs a) {
     const YOps gy = yops(gs);
 
     // ---- split of W_j and the next tile's products with it
-    const Split8 ws[2] = {split8(W[0], W[1]), split8(W[2], W[3])};
+    const Split8 ws[2] = {split8_mfma(W[0], W[1], ns), split8_mfma(W[2], W[3], ns)};
     if (MODE == MODE_MULTI) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
