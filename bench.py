@@ -17,7 +17,8 @@ TTT-MLP, and a streaming-copy bandwidth reference.
 
 --pmc-calibrate additionally launches the streaming copy kernel on a known
 byte count, so that a hardware-counter run of this script can scale the
-scan's FETCH_SIZE / WRITE_SIZE readings (see --summarize-pmc).
+scans' FETCH_SIZE / WRITE_SIZE readings (see --summarize-pmc), and the
+TTT-MLP scan, so that the same run covers both scan kernels.
 """
 from __future__ import annotations
 
@@ -38,7 +39,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, vendor figure
 METRIC = "TTT fwd tokens·heads/s at 1 GPU; % of HBM/MFMA roofline (b=16)"
 UNIT = "tokens·heads/s"
-SCAN_SOURCES = ["ttt_linear.hip", "ttt_device.h", "ttt_launch.h"]
+SCAN_SOURCES = ["ttt_linear_bf16.hip", "ttt_device.h", "ttt_launch.h"]
 MLP_SOURCES = ["ttt_mlp.hip", "ttt_device.h", "ttt_launch.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
@@ -194,6 +195,12 @@ def cpu_baseline(x, b):
                       f"fp64 sequential primal form, {dt:.2f} s wall"}
 
 
+def auto_rows(units: int) -> int:
+    """Rows of W per workgroup that the library picks for `units` (batch,
+    head) units when the caller passes 0."""
+    return 64 if units >= 256 else (32 if units > 64 else 16)
+
+
 def traffic_for(kernel_key: str, sources, launch_bytes_alg: int):
     """HBM bytes per launch from committed counter readings (FETCH_SIZE +
     WRITE_SIZE, scaled by the copy-kernel calibration), or None if the
@@ -239,7 +246,7 @@ def summarize_pmc(fetch_dir, write_dir):
     out = {"calibration": {"copy_bytes": copy_bytes, "fetch_kib": fetch[copy_name],
                            "write_kib": write[copy_name], "fetch_scale": f_scale,
                            "write_scale": w_scale}}
-    for key, pat, srcs in (("linear_scan", "linear_scan_kernel", SCAN_SOURCES),
+    for key, pat, srcs in (("linear_scan", "linear_scan_bf16_kernel", SCAN_SOURCES),
                            ("mlp_scan", "mlp_scan_kernel", MLP_SOURCES)):
         names = [k for k in fetch if pat in k]
         if not names:
@@ -296,6 +303,9 @@ def main():
     if args.pmc_calibrate:
         log("[bench] streaming copy calibration (1 GiB)")
         stream_copy_GBps(1 << 30, reps=3)
+        w4 = inputs.workload(4)
+        log(f"[bench] {w4.name} (counter coverage of the MLP scan)")
+        mlp_case(w4, 16, 2, 1)
 
     extras = {}
     if not args.no_extras:
@@ -339,7 +349,7 @@ def main():
                    "seq_len": wl.T, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": head["hbm_GBps"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": head["hbm_frac"], "traffic": traffic,
-                     "kernel": "linear_scan_kernel<bf16, b=16, 64 rows>",
+                     "kernel": f"linear_scan_bf16_kernel (b=16, {auto_rows(wl.units)} rows of W per workgroup)",
                      "alg_bytes_per_launch": head["alg_bytes"],
                      "kernel_us_mean": head["kernel_us_mean"],
                      "kernel_us_median": head["kernel_us_median"],
