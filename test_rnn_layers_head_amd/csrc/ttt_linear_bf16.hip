@@ -12,13 +12,16 @@
 //   waves 0 .. NCW-1  compute waves, 16 rows of W each, fp32 state resident
 //                     in MFMA accumulators for the whole sequence;
 //   waves NCW, NCW+1  helpers: build every per-tile operand that depends only
-//                     on K, Q, eta, one tile ahead, into a double-buffered
+//                     on K, Q, eta, two tiles ahead, into a double-buffered
 //                     "prepared" LDS area laid out lane-linear (conflict-free
 //                     16-byte reads); helper 0 makes triu(K^T Q), K_{j-1}^T K_j,
 //                     2 eta (and the sub-batch inverse), helper 1 K_{j-1}^T Q_j
 //                     and the update operand;
 //   wave NCW+2        loader: buffer->LDS DMA of 16-token K/Q/V/eta tiles,
 //                     D tiles ahead, into a ring (zero-filled past T).
+// The compute waves read every LDS operand of a tile one iteration before
+// they use it (registers double as a second pipeline stage), so no LDS
+// latency sits between a tile barrier and the serial chain that follows it.
 //
 // Serial chain per tile.  Only P_j = W_j K_j feeds the recurrence.  Using
 //   P_{j+1} = W_j K_{j+1} + Gn_j (K_j^T K_{j+1})     (W_{j+1} = W_j + Gn_j K_j^T)
@@ -141,11 +144,12 @@ linear_scan_bf16_kernel(LinearArgs a) {
   const int row0 = slice * ROWS;
 
   // ================================================================ loader
-  // Barrier B_j (j = -1 .. ntiles-1) releases compute iteration j (which
-  // reads raw tile j+1) and helper iteration j (which prepares tile j+1 from
-  // raw tile j+1); before it the loader makes sure raw tiles <= j+1 have
-  // landed.  Tile j+D+1 is issued after B_{j-1}, while the other waves read
-  // only raw tile j, hence NST = D + 2 ring slots.
+  // Barriers B_-2, B_-1, B_0 .. B_{ntiles-1}.  B_j (j >= 0) releases compute
+  // iteration j (which reads raw tile j+2 for the next iteration) and helper
+  // iteration j (which prepares tile j+2 from raw tile j+2); before it the
+  // loader makes sure raw tiles <= j+2 have landed.  B_-2 guarantees raw
+  // tiles 0 and 1.  Raw tile t is last read before B_{t-1}, so tile j+D+2
+  // is issued after B_{j-1} into the slot of tile j: NST = D + 2 slots.
   if (wave == G::NCW + 2) {
     const uint32_t ubytes = (uint32_t)T * 128;
     const size_t uoff = (size_t)unit * T * 64;
@@ -174,15 +178,16 @@ linear_scan_bf16_kernel(LinearArgs a) {
       }
       if (lane < 16) dma4(re, st + 2 * G::KB + G::VB, (uint32_t)(j * 16 + lane) * 4);
     };
-    const int pro = ntiles < G::D + 1 ? ntiles : G::D + 1;
+    const int pro = ntiles < G::D + 2 ? ntiles : G::D + 2;
     for (int j = 0; j < pro; ++j) issue(j);
-    if (pro == G::D + 1) wait_vmcnt<G::NI * G::D>();  // tile 0 landed
+    if (pro == G::D + 2) wait_vmcnt<G::NI * G::D>();  // tiles 0, 1 landed
     else wait_vmcnt<0>();
+    wg_barrier();  // B_{-2}
     wg_barrier();  // B_{-1}
     for (int j = 0; j < ntiles; ++j) {
-      if (j + G::D + 1 < ntiles) {
-        issue(j + G::D + 1);
-        wait_vmcnt<G::NI * G::D>();  // tiles <= j+1 landed
+      if (j + G::D + 2 < ntiles) {
+        issue(j + G::D + 2);
+        wait_vmcnt<G::NI * G::D>();  // tiles <= j+2 landed
       } else {
         wait_vmcnt<0>();
       }
@@ -192,8 +197,9 @@ linear_scan_bf16_kernel(LinearArgs a) {
   }
 
   // ================================================================ helper
-  // Iteration j (between B_j and B_{j+1}, j = -1 .. ntiles-2) prepares tile
-  // j+1 into prepared slot (j+1) & 1, which compute iteration j+1 reads.
+  // Iteration j (between B_j and B_{j+1}, j = -2 .. ntiles-2) prepares tile
+  // j+2 (if it exists) into prepared slot j & 1; compute iteration j+1 reads
+  // it into registers, and had read that slot's previous tile before B_j.
   if (wave >= G::NCW) {
     const bool h0 = wave == G::NCW;  // helper 0 or helper 1
     bf16x8 kprev[2], sel[2];
@@ -204,9 +210,13 @@ linear_scan_bf16_kernel(LinearArgs a) {
         // slot 8g+e of block m/2 selects column sigma(m, c) for m % 2 == h
         sel[h][e] = (bf16)((g == (c >> 2) && e == 4 * h + (c & 3)) ? 1.f : 0.f);
       }
-    wg_barrier();  // B_{-1}
-    for (int j = -1; j < ntiles - 1; ++j) {
-      const int tn = j + 1;
+    wg_barrier();  // B_{-2}
+    for (int j = -2; j < ntiles - 1; ++j) {
+      const int tn = j + 2;
+      if (tn >= ntiles) {  // nothing left to prepare: keep the barrier count
+        wg_barrier();      // B_{j+1}
+        continue;
+      }
       const char* st = raw + (tn % G::NST) * G::RAW;
       const char* Kt = st;
       const char* Qt = st + G::KB;
@@ -305,7 +315,9 @@ linear_scan_bf16_kernel(LinearArgs a) {
 
   // =============================================================== compute
   // Iteration j enters with W = W_j (fp32 accumulators), XB = W_{j-1} K_j - V_j
-  // and RB = W_{j-1} Q_j (formed in iteration j-1), and gp = operands of Gn_{j-1}.
+  // and RB = W_{j-1} Q_j (formed in iteration j-1), gp = operands of Gn_{j-1},
+  // and in registers the prepared operands of tile j and the raw K/Q/V
+  // operands of tile j+1 (read from LDS during iteration j-1).
   const int rbase = row0 + wave * 16;
   const float* w0 = a.w0 + (size_t)(a.w0_per_batch ? unit : head) * 4096;
   f32x4 W[4];
@@ -319,29 +331,63 @@ linear_scan_bf16_kernel(LinearArgs a) {
   bf16x8 negI;
 #pragma unroll
   for (int e = 0; e < 8; ++e) negI[e] = (bf16)((g < 2 && 8 * g + e == c) ? -1.f : 0.f);
-  const int voff = (16 * wave + 8 * (g & 1)) * 2;  // V row chunk of this lane
+  const int voff = 2 * G::KB + c * (ROWS * 2) + (16 * wave + 8 * (g & 1)) * 2;  // V row chunk
   YOps gp;  // operands of the previous tile's negative gradient
   gp.hh = cat44(s16x4{0, 0, 0, 0}, s16x4{0, 0, 0, 0});
   gp.l0 = gp.hh;
   Split8 wg[2];  // gradient point operands (b > 16)
 
-  wg_barrier();  // B_{-1}: raw tile 0 is in LDS
+  // raw operands of one tile for this lane: K and Q row chunks, V row chunk
+  struct RawOps {
+    bf16x8 k[2], q[2], v;
+  };
+  auto load_raw = [&](RawOps& r, const char* st) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      r.k[h] = row_chunk(st, c, h, g);
+      r.q[h] = row_chunk(st + G::KB, c, h, g);
+    }
+    r.v = *(const bf16x8*)(st + voff);
+  };
+  // prepared operands of one tile for this lane
+  struct PrepOps {
+    f32x4 e2;
+    bf16x8 mkk, mkq, att, kt[4], u;
+  };
+  auto load_prep = [&](PrepOps& p, const char* pp) {
+    p.e2 = *(const f32x4*)(pp + G::P_E2 + 16 * g);
+    p.mkk = get8(pp + G::P_MKK, lane);
+    p.mkq = get8(pp + G::P_MKQ, lane);
+    p.att = get8(pp + G::P_A, lane);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) p.kt[m] = get8(pp + G::P_KT + m * 1024, lane);
+    if constexpr (MODE == MODE_SUB) p.u = get8(pp + G::P_U, lane);
+  };
+
+  wg_barrier();  // B_{-2}: raw tiles 0 and 1 are in LDS
   f32x4 XB = {0, 0, 0, 0}, RB = {0, 0, 0, 0};
+  RawOps ra;  // raw operands of tile j+1
   {
     const Split8 ws[2] = {split8_mfma(W[0], W[1], ns), split8_mfma(W[2], W[3], ns)};
     wg[0] = ws[0];
     wg[1] = ws[1];
-    const char* st = raw;
-    XB = mfma_k32(*(const bf16x8*)(st + 2 * G::KB + c * (ROWS * 2) + voff), negI, XB);
+    RawOps r0;
+    load_raw(r0, raw);
+    XB = mfma_k32(r0.v, negI, XB);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const bf16x8 kk = row_chunk(st, c, h, g), qq = row_chunk(st + G::KB, c, h, g);
-      XB = mfma_k32(kk, ws[h].hi, XB);
-      XB = mfma_k32(kk, ws[h].lo, XB);
-      RB = mfma_k32(qq, ws[h].hi, RB);
-      RB = mfma_k32(qq, ws[h].lo, RB);
+      XB = mfma_k32(r0.k[h], ws[h].hi, XB);
+      XB = mfma_k32(r0.k[h], ws[h].lo, XB);
+      RB = mfma_k32(r0.q[h], ws[h].hi, RB);
+      RB = mfma_k32(r0.q[h], ws[h].lo, RB);
     }
+    load_raw(ra, raw + 1 * G::RAW);
   }
+  wait_lgkm0();
+  wg_barrier();  // B_{-1}: prepared tile 0 is in LDS
+  PrepOps pa, pb;  // prepared operands of tiles j and j+1 (two register sets)
+  RawOps rb;       // raw operands of tile j+2
+  load_prep(pa, prep);
 
   // Z through a range-checked buffer: rows past T (padding of the last
   // tile) are dropped by the hardware, so the loop body has no branches and
@@ -349,24 +395,28 @@ linear_scan_bf16_kernel(LinearArgs a) {
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(a.z + (size_t)unit * T * 64, (uint32_t)T * 256);
   uint32_t zoff = (uint32_t)((4 * g * 64 + rbase + c) * 4);
 
-  for (int j = 0; j < ntiles; ++j) {
+  // One tile: uses (pc, rc), fills (pn, rn) for the next one.  The loop
+  // below alternates two register sets, so nothing is copied between
+  // iterations and the reads have a whole tile of work to land.
+  auto tile = [&](const int j, const PrepOps& pc, const RawOps& rc, PrepOps& pn, RawOps& rn) {
     wait_lgkm0();
     wg_barrier();  // B_j
-    const char* pp = prep + (j & 1) * G::PREP;
-    const char* st = raw + ((j + 1) % G::NST) * G::RAW;  // tile j+1 (stale past the end)
-    const f32x4 e2 = *(const f32x4*)(pp + G::P_E2 + 16 * g);
+    // next iteration's operands: prepared tile j+1, raw tile j+2 (stale
+    // past the end of the sequence, where they are never used)
+    load_prep(pn, prep + ((j + 1) & 1) * G::PREP);
+    load_raw(rn, raw + ((j + 2) % G::NST) * G::RAW);
     const bool new_mb = MODE != MODE_MULTI || (j % tpm) == 0;
     const bool next_new_mb = MODE != MODE_MULTI || ((j + 1) % tpm) == 0;
 
     // ---- serial chain: X_j = P_j - V_j, then Gn_j = 2 eta (v - p).
     // (gp is zero at j = 0; within a b > 16 mini-batch P keeps its gradient
     // point and takes no correction.)
-    f32x4 X = mm_pre(get8(pp + G::P_MKK, lane), gp, XB);
+    f32x4 X = mm_pre(pc.mkk, gp, XB);
     if (MODE == MODE_MULTI) X = new_mb ? X : XB;
     f32x4 E;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) E[r] = -e2[r] * X[r];
-    if constexpr (MODE == MODE_SUB) E = mm_pre(get8(pp + G::P_U, lane), yops(split4(E)), f32x4{0, 0, 0, 0});
+    for (int r = 0; r < 4; ++r) E[r] = -pc.e2[r] * X[r];
+    if constexpr (MODE == MODE_SUB) E = mm_pre(pc.u, yops(split4(E)), f32x4{0, 0, 0, 0});
     const Split4 gs = split4(E);
     const YOps gy = yops(gs);
 
@@ -379,26 +429,24 @@ linear_scan_bf16_kernel(LinearArgs a) {
         wg[h].lo = new_mb ? ws[h].lo : wg[h].lo;
       }
     }
-    f32x4 XBn = mfma_k32(*(const bf16x8*)(st + 2 * G::KB + c * (ROWS * 2) + voff), negI,
-                         f32x4{0, 0, 0, 0});
+    f32x4 XBn = mfma_k32(rc.v, negI, f32x4{0, 0, 0, 0});
     f32x4 RBn = {0, 0, 0, 0};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const bf16x8 kk = row_chunk(st, c, h, g), qq = row_chunk(st + G::KB, c, h, g);
       bf16x8 whi = ws[h].hi, wlo = ws[h].lo;
       if (MODE == MODE_MULTI) {
         whi = next_new_mb ? whi : wg[h].hi;
         wlo = next_new_mb ? wlo : wg[h].lo;
       }
-      XBn = mfma_k32(kk, whi, XBn);
-      XBn = mfma_k32(kk, wlo, XBn);
-      RBn = mfma_k32(qq, ws[h].hi, RBn);
-      RBn = mfma_k32(qq, ws[h].lo, RBn);
+      XBn = mfma_k32(rc.k[h], whi, XBn);
+      XBn = mfma_k32(rc.k[h], wlo, XBn);
+      RBn = mfma_k32(rc.q[h], ws[h].hi, RBn);
+      RBn = mfma_k32(rc.q[h], ws[h].lo, RBn);
     }
 
     // ---- outputs: Z_j = W_j Q_j + Gn_j triu(K_j^T Q_j)
-    f32x4 Z = mm_pre(get8(pp + G::P_MKQ, lane), gp, RB);
-    Z = mm_pre(get8(pp + G::P_A, lane), gy, Z);
+    f32x4 Z = mm_pre(pc.mkq, gp, RB);
+    Z = mm_pre(pc.att, gy, Z);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float zr = Z[r];  // element by value (a bit_cast of Z[r] itself reads element 0)
@@ -409,11 +457,17 @@ linear_scan_bf16_kernel(LinearArgs a) {
     // ---- rank-16 update W_{j+1} = W_j + Gn_j K_j^T
     const bf16x8 g2 = cat44(gs.hi, gs.lo);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) W[m] = mfma_k32(get8(pp + G::P_KT + m * 1024, lane), g2, W[m]);
+    for (int m = 0; m < 4; ++m) W[m] = mfma_k32(pc.kt[m], g2, W[m]);
     XB = XBn;
     RB = RBn;
     gp = gy;
+  };
+  int j = 0;
+  for (; j + 1 < ntiles; j += 2) {
+    tile(j, pa, ra, pb, rb);
+    tile(j + 1, pb, rb, pa, ra);
   }
+  if (j < ntiles) tile(j, pa, ra, pb, rb);
 
   float* wo = a.w_out + (size_t)unit * 4096;
 #pragma unroll
