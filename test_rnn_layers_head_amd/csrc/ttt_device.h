@@ -155,6 +155,16 @@ __device__ __forceinline__ void wg_barrier() {
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
+// The same, and no instruction of any kind is scheduled across it: keeps a
+// software pipeline's stages (reads issued right after the barrier, their
+// use one iteration later) in the order they were written.
+__device__ __forceinline__ void wg_barrier_pinned() {
+  __builtin_amdgcn_sched_barrier(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
 template <int N>

@@ -22,6 +22,8 @@
 // The compute waves read every LDS operand of a tile one iteration before
 // they use it (registers double as a second pipeline stage), so no LDS
 // latency sits between a tile barrier and the serial chain that follows it.
+// Nothing is scheduled across a tile barrier, which keeps those stages in
+// place, and the compute waves run at the highest wave priority.
 //
 // Serial chain per tile.  Only P_j = W_j K_j feeds the recurrence.  Using
 //   P_{j+1} = W_j K_{j+1} + Gn_j (K_j^T K_{j+1})     (W_{j+1} = W_j + Gn_j K_j^T)
@@ -182,8 +184,8 @@ linear_scan_bf16_kernel(LinearArgs a) {
     for (int j = 0; j < pro; ++j) issue(j);
     if (pro == G::D + 2) wait_vmcnt<G::NI * G::D>();  // tiles 0, 1 landed
     else wait_vmcnt<0>();
-    wg_barrier();  // B_{-2}
-    wg_barrier();  // B_{-1}
+    wg_barrier_pinned();  // B_{-2}
+    wg_barrier_pinned();  // B_{-1}
     for (int j = 0; j < ntiles; ++j) {
       if (j + G::D + 2 < ntiles) {
         issue(j + G::D + 2);
@@ -191,7 +193,7 @@ linear_scan_bf16_kernel(LinearArgs a) {
       } else {
         wait_vmcnt<0>();
       }
-      wg_barrier();  // B_j
+      wg_barrier_pinned();  // B_j
     }
     return;
   }
@@ -210,11 +212,11 @@ linear_scan_bf16_kernel(LinearArgs a) {
         // slot 8g+e of block m/2 selects column sigma(m, c) for m % 2 == h
         sel[h][e] = (bf16)((g == (c >> 2) && e == 4 * h + (c & 3)) ? 1.f : 0.f);
       }
-    wg_barrier();  // B_{-2}
+    wg_barrier_pinned();  // B_{-2}
     for (int j = -2; j < ntiles - 1; ++j) {
       const int tn = j + 2;
       if (tn >= ntiles) {  // nothing left to prepare: keep the barrier count
-        wg_barrier();      // B_{j+1}
+        wg_barrier_pinned();      // B_{j+1}
         continue;
       }
       const char* st = raw + (tn % G::NST) * G::RAW;
@@ -308,12 +310,15 @@ linear_scan_bf16_kernel(LinearArgs a) {
       kprev[0] = kop[0];
       kprev[1] = kop[1];
       wait_lgkm0();
-      wg_barrier();  // B_{j+1}
+      wg_barrier_pinned();  // B_{j+1}
     }
     return;
   }
 
   // =============================================================== compute
+  // The compute waves carry the serial chain; the helpers and the loader
+  // share their SIMDs and must not delay it.
+  __builtin_amdgcn_s_setprio(3);
   // Iteration j enters with W = W_j (fp32 accumulators), XB = W_{j-1} K_j - V_j
   // and RB = W_{j-1} Q_j (formed in iteration j-1), gp = operands of Gn_{j-1},
   // and in registers the prepared operands of tile j and the raw K/Q/V
@@ -364,7 +369,7 @@ linear_scan_bf16_kernel(LinearArgs a) {
     if constexpr (MODE == MODE_SUB) p.u = get8(pp + G::P_U, lane);
   };
 
-  wg_barrier();  // B_{-2}: raw tiles 0 and 1 are in LDS
+  wg_barrier_pinned();  // B_{-2}: raw tiles 0 and 1 are in LDS
   f32x4 XB = {0, 0, 0, 0}, RB = {0, 0, 0, 0};
   RawOps ra;  // raw operands of tile j+1
   {
@@ -384,7 +389,7 @@ linear_scan_bf16_kernel(LinearArgs a) {
     load_raw(ra, raw + 1 * G::RAW);
   }
   wait_lgkm0();
-  wg_barrier();  // B_{-1}: prepared tile 0 is in LDS
+  wg_barrier_pinned();  // B_{-1}: prepared tile 0 is in LDS
   PrepOps pa, pb;  // prepared operands of tiles j and j+1 (two register sets)
   RawOps rb;       // raw operands of tile j+2
   load_prep(pa, prep);
@@ -400,11 +405,12 @@ linear_scan_bf16_kernel(LinearArgs a) {
   // iterations and the reads have a whole tile of work to land.
   auto tile = [&](const int j, const PrepOps& pc, const RawOps& rc, PrepOps& pn, RawOps& rn) {
     wait_lgkm0();
-    wg_barrier();  // B_j
+    wg_barrier_pinned();  // B_j
     // next iteration's operands: prepared tile j+1, raw tile j+2 (stale
     // past the end of the sequence, where they are never used)
     load_prep(pn, prep + ((j + 1) & 1) * G::PREP);
     load_raw(rn, raw + ((j + 2) % G::NST) * G::RAW);
+    __builtin_amdgcn_sched_barrier(0);  // the reads go out first
     const bool new_mb = MODE != MODE_MULTI || (j % tpm) == 0;
     const bool next_new_mb = MODE != MODE_MULTI || ((j + 1) % tpm) == 0;
 
