@@ -200,25 +200,30 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
   __amdgpu_buffer_rsrc_t rsrc[G::LOADS];
   int ldst[G::LOADS];
   uint32_t gsrc[G::LOADS], gstep[G::LOADS];
+  // The tensor a wave reads depends only on its first chunk (64-chunk
+  // blocks never straddle two tensors), so the descriptors are built from a
+  // wave-uniform index and stay in scalar registers.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll
   for (int l = 0; l < G::LOADS; ++l) {
-    const int q = w * 64 + lane + l * NW * 64;
+    const int q0 = wu * 64 + l * NW * 64;  // first chunk of this wave
+    const int q = q0 + lane;
     ldst[l] = -1;
     gsrc[l] = 0;
     gstep[l] = 2048;
-    if (q < 384) {
-      const int part = q >> 7, ch = q & 127, r = ch >> 3, p = ch & 7;
+    if (q0 < 384) {
+      const int part = q0 >> 7, ch = q & 127, r = ch >> 3, p = ch & 7;
       const void* base = part == 0 ? a.k : (part == 1 ? a.q : a.v);
       rsrc[l] = make_rsrc((const short*)base + uoff, (uint32_t)T * 128);
       gsrc[l] = r * 128 + p * 16;
       ldst[l] = part * 2048 + (part < 2 ? swz_chunk(r, p) : (int)gsrc[l]);
-    } else if (q < 400) {
-      rsrc[l] = make_rsrc(a.eta + (size_t)unit * T, (uint32_t)T * 4);
-      gsrc[l] = (q - 384) * 4;
-      gstep[l] = 64;
-      ldst[l] = 3 * 2048 + (q - 384) * 4;
     } else {
-      rsrc[l] = make_rsrc(a.eta, 0);
+      rsrc[l] = make_rsrc(a.eta + (size_t)unit * T, (uint32_t)T * 4);
+      if (q < 400) {
+        gsrc[l] = (q - 384) * 4;
+        gstep[l] = 64;
+        ldst[l] = 3 * 2048 + (q - 384) * 4;
+      }
     }
   }
   auto fetch = [&](int j, uint4* v) {
