@@ -98,25 +98,35 @@ def device_inputs(x):
 
 
 def time_launches(launch, steps, warmup):
-    """Times `steps` back-to-back launches (after `warmup`), bracketed by
-    device synchronisation, with events around each launch on the current
-    stream (the stream the kernels are enqueued on).  Returns
-    (wall ms per step, mean kernel us, median kernel us)."""
+    """Times `steps` back-to-back launches after `warmup` untimed ones, with
+    device synchronisation around the timed region and one pair of events
+    around it on the current stream (the stream the kernels are enqueued on).
+    A second pass of `steps` launches with an event pair around each gives
+    the spread of single launches.  Returns (wall ms per step, mean kernel us
+    over the timed region, median / p10 / p90 single-launch us)."""
     import torch
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        launch()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    region_us = e0.elapsed_time(e1) * 1e3 / steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
-    t0 = time.perf_counter()
     for a, b in ev:
         a.record()
         launch()
         b.record()
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps * 1e3
     ks = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
-    return wall, float(ks.mean()), float(np.median(ks))
+    return wall, region_us, {"median": float(np.median(ks)), "p10": float(np.percentile(ks, 10)),
+                             "p90": float(np.percentile(ks, 90))}
 
 
 def linear_case(wl, b, steps, warmup, x=None, rows=0):
@@ -129,12 +139,13 @@ def linear_case(wl, b, steps, warmup, x=None, rows=0):
     w = torch.empty((wl.B, wl.H, wl.d, wl.d), device="cuda")
     launch = lambda: ttt_linear_fwd(d["q"], d["k"], d["v"], d["eta"], d["w0"], b, z=z, w_out=w,
                                     rows_per_workgroup=rows)
-    wall, kmean, kmed = time_launches(launch, steps, warmup)
+    wall, kmean, spread = time_launches(launch, steps, warmup)
     assert torch.isfinite(z).all().item()
     byts = linear_alg_bytes(wl)
     res = {
         "workload": wl.name, "b": b, "token_heads_per_s": wl.token_heads / (wall * 1e-3),
-        "ms_per_step": wall, "kernel_us_mean": kmean, "kernel_us_median": kmed,
+        "ms_per_step": wall, "kernel_us_mean": kmean, "kernel_us_median": spread["median"],
+        "kernel_us_p10": spread["p10"], "kernel_us_p90": spread["p90"],
         "alg_bytes": byts, "hbm_GBps": byts / (kmean * 1e-6) / 1e9,
         "hbm_frac": byts / (kmean * 1e-6) / 1e9 / HBM_PEAK_GBS,
         "mfma_frac": linear_alg_flops(wl, b) / (kmean * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
@@ -154,7 +165,8 @@ def mlp_case(wl, b, steps, warmup):
     w2 = torch.empty((wl.B, wl.H, wl.d, wl.hidden), device="cuda")
     launch = lambda: ttt_mlp_fwd(d["q"], d["k"], d["v"], d["eta"], d["w1"], d["w2"], b, z=z,
                                  w1_out=w1, w2_out=w2)
-    wall, kmean, kmed = time_launches(launch, steps, warmup)
+    wall, kmean, spread = time_launches(launch, steps, warmup)
+    kmed = spread["median"]
     byts = mlp_alg_bytes(wl)
     flops = mlp_alg_flops(wl, b)
     # designed-traffic reading: the 2 x hidden x d fp32 state read and written
@@ -261,20 +273,57 @@ def summarize_pmc(fetch_dir, write_dir):
     print(json.dumps(out, indent=1))
 
 
+# --------------------------------------------------------------------------
+# Kernel-trace summary: rocprofv3 --kernel-trace --stats output -> text
+# --------------------------------------------------------------------------
+def summarize_trace(trace_dir, pattern, skip, take):
+    """Prints the per-kernel statistics of a rocprofv3 kernel-trace run and
+    the mean duration of dispatches [skip, skip + take) of the kernels whose
+    name contains `pattern` (in dispatch order): with skip = warmup and take
+    = steps of the bench run this is the timed region of the headline."""
+    import csv
+    stats = glob.glob(os.path.join(trace_dir, "**", "*_kernel_stats.csv"), recursive=True)
+    trace = glob.glob(os.path.join(trace_dir, "**", "*_kernel_trace.csv"), recursive=True)
+    print("rocprofv3 kernel statistics (all dispatches of the run):")
+    print(f"  {'calls':>6s} {'avg us':>10s} {'min us':>10s} {'max us':>10s}  kernel")
+    for path in stats:
+        for r in csv.DictReader(open(path)):
+            print(f"  {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.1f} "
+                  f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f}  {r['Name'][:90]}")
+    rows = []
+    for path in trace:
+        for r in csv.DictReader(open(path)):
+            if pattern in r["Kernel_Name"]:
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    rows.sort()
+    sel = rows[skip:skip + take]
+    if sel:
+        d = np.array([(e - b) / 1e3 for b, e, _ in sel])
+        print(f"\ndispatches {skip} .. {skip + len(sel) - 1} of '{pattern}' ({sel[0][2][:80]}):")
+        print(f"  mean {d.mean():.1f} us, median {np.median(d):.1f} us, min {d.min():.1f}, max {d.max():.1f}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed launches first (the clocks settle within ~0.1 s)")
     ap.add_argument("--no-extras", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="also launch the 1 GiB streaming copy used to scale byte counters")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "KERNEL", "SKIP", "TAKE"),
+                    help="summarise a rocprofv3 --kernel-trace --stats run of this script")
     args = ap.parse_args()
 
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return 0
+    if args.summarize_trace:
+        d, k, skip, take = args.summarize_trace
+        summarize_trace(d, k, int(skip), int(take))
         return 0
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -311,15 +360,15 @@ def main():
     if not args.no_extras:
         for bb in (1, 4, 64):
             log(f"[bench] b sweep b={bb}")
-            extras[f"{wl.name}_b{bb}"] = linear_case(wl, bb, max(3, args.steps // 4), 2, x=x)
+            extras[f"{wl.name}_b{bb}"] = linear_case(wl, bb, max(3, args.steps // 4), 10, x=x)
         for wid in (2, 5):
             w2 = inputs.workload(wid)
             log(f"[bench] {w2.name}")
-            extras[w2.name] = linear_case(w2, 16, max(5, args.steps // 2), 2)
+            extras[w2.name] = linear_case(w2, 16, max(5, args.steps // 2), 10)
         w4 = inputs.workload(4)
         log(f"[bench] {w4.name}")
         try:
-            extras[w4.name] = mlp_case(w4, 16, max(5, args.steps // 2), 2)
+            extras[w4.name] = mlp_case(w4, 16, max(5, args.steps // 2), 5)
         except Exception as e:  # reported, never silently replaced
             extras[w4.name] = {"error": str(e)}
         log("[bench] streaming copy reference")
@@ -353,6 +402,8 @@ def main():
                      "alg_bytes_per_launch": head["alg_bytes"],
                      "kernel_us_mean": head["kernel_us_mean"],
                      "kernel_us_median": head["kernel_us_median"],
+                     "kernel_us_p10": head["kernel_us_p10"],
+                     "kernel_us_p90": head["kernel_us_p90"],
                      "mfma_frac": head["mfma_frac"]},
         "cpu_baseline": cpu,
         "extras": extras,
