@@ -44,6 +44,8 @@
 // K row.  K/Q tiles are stored with chunk p of row r at position
 // p ^ (r & 7) (applied by the DMA's source addresses), which makes those
 // 16-row chunk reads bank-conflict free.
+#include <type_traits>
+
 #include "ttt_device.h"
 #include "ttt_launch.h"
 
@@ -118,7 +120,10 @@ __device__ __forceinline__ bf16x8 get8(const char* p, int lane) {
   return *(const bf16x8*)(p + lane * 16);
 }
 
-template <int MODE, int ROWS>
+// TPM: tiles per mini-batch when it is fixed at compile time (b = 32, 64),
+// so a tile's position inside its mini-batch costs nothing; 0 = read from
+// the arguments (other multiples of 16).  Unused below b = 16.
+template <int MODE, int ROWS, int TPM>
 __global__ void __launch_bounds__((Geom<ROWS>::THREADS))
 linear_scan_bf16_kernel(LinearArgs a) {
   using G = Geom<ROWS>;
@@ -329,7 +334,7 @@ linear_scan_bf16_kernel(LinearArgs a) {
 #pragma unroll
   for (int m = 0; m < 4; ++m)
     W[m] = *(const f32x4*)(w0 + (rbase + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1));
-  const int tpm = MODE == MODE_MULTI ? (a.b >> 4) : 1;  // tiles per mini-batch
+  const int tpm = MODE != MODE_MULTI ? 1 : (TPM > 0 ? TPM : (a.b >> 4));  // tiles per mini-batch
   const NegSel ns = make_negsel(c, g);
   // -I on the 16 V columns of this wave: X = -V_block lands in accumulator
   // layout when V's rows are the A-operand (slots 16..31 are unused).
@@ -403,7 +408,10 @@ linear_scan_bf16_kernel(LinearArgs a) {
   // One tile: uses (pc, rc), fills (pn, rn) for the next one.  The loop
   // below alternates two register sets, so nothing is copied between
   // iterations and the reads have a whole tile of work to land.
-  auto tile = [&](const int j, const PrepOps& pc, const RawOps& rc, PrepOps& pn, RawOps& rn) {
+  // POS: the tile's position in its mini-batch when known at compile time
+  // (an std::integral_constant), -1 otherwise.
+  auto tile = [&](const int j, auto POS, const PrepOps& pc, const RawOps& rc, PrepOps& pn,
+                  RawOps& rn) {
     wait_lgkm0();
     wg_barrier_pinned();  // B_j
     // next iteration's operands: prepared tile j+1, raw tile j+2 (stale
@@ -411,8 +419,10 @@ linear_scan_bf16_kernel(LinearArgs a) {
     load_prep(pn, prep + ((j + 1) & 1) * G::PREP);
     load_raw(rn, raw + ((j + 2) % G::NST) * G::RAW);
     __builtin_amdgcn_sched_barrier(0);  // the reads go out first
-    const bool new_mb = MODE != MODE_MULTI || (j % tpm) == 0;
-    const bool next_new_mb = MODE != MODE_MULTI || ((j + 1) % tpm) == 0;
+    constexpr int pos = decltype(POS)::value;
+    const bool new_mb = MODE != MODE_MULTI || (pos >= 0 ? pos == 0 : (j % tpm) == 0);
+    const bool next_new_mb =
+        MODE != MODE_MULTI || (pos >= 0 ? (pos + 1) % (TPM > 0 ? TPM : 1) == 0 : ((j + 1) % tpm) == 0);
 
     // ---- serial chain: X_j = P_j - V_j, then Gn_j = 2 eta (v - p).
     // (gp is zero at j = 0; within a b > 16 mini-batch P keeps its gradient
@@ -469,11 +479,34 @@ linear_scan_bf16_kernel(LinearArgs a) {
     gp = gy;
   };
   int j = 0;
-  for (; j + 1 < ntiles; j += 2) {
-    tile(j, pa, ra, pb, rb);
-    tile(j + 1, pb, rb, pa, ra);
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  using P3 = std::integral_constant<int, 3>;
+  using PN = std::integral_constant<int, -1>;
+  if constexpr (MODE == MODE_MULTI && TPM == 4) {
+    for (; j + 3 < ntiles; j += 4) {
+      tile(j, P0{}, pa, ra, pb, rb);
+      tile(j + 1, P1{}, pb, rb, pa, ra);
+      tile(j + 2, P2{}, pa, ra, pb, rb);
+      tile(j + 3, P3{}, pb, rb, pa, ra);
+    }
+    if (j < ntiles) tile(j, P0{}, pa, ra, pb, rb);
+    if (j + 1 < ntiles) tile(j + 1, P1{}, pb, rb, pa, ra);
+    if (j + 2 < ntiles) tile(j + 2, P2{}, pa, ra, pb, rb);
+  } else if constexpr (MODE == MODE_MULTI && TPM == 2) {
+    for (; j + 1 < ntiles; j += 2) {
+      tile(j, P0{}, pa, ra, pb, rb);
+      tile(j + 1, P1{}, pb, rb, pa, ra);
+    }
+    if (j < ntiles) tile(j, P0{}, pa, ra, pb, rb);
+  } else {
+    for (; j + 1 < ntiles; j += 2) {
+      tile(j, PN{}, pa, ra, pb, rb);
+      tile(j + 1, PN{}, pb, rb, pa, ra);
+    }
+    if (j < ntiles) tile(j, PN{}, pa, ra, pb, rb);
   }
-  if (j < ntiles) tile(j, pa, ra, pb, rb);
 
   float* wo = a.w_out + (size_t)unit * 4096;
 #pragma unroll
@@ -481,30 +514,32 @@ linear_scan_bf16_kernel(LinearArgs a) {
     *(f32x4*)(wo + (rbase + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1)) = W[m];
 }
 
-template <int MODE, int ROWS>
+template <int MODE, int ROWS, int TPM>
 hipError_t launch_one(const LinearArgs& a, hipStream_t s) {
   constexpr int NSPLIT = 64 / ROWS;
   const int blocks = NSPLIT == 1 ? a.units : ((a.units + 7) / 8) * 8 * NSPLIT;
-  hipLaunchKernelGGL((linear_scan_bf16_kernel<MODE, ROWS>), dim3(blocks),
+  hipLaunchKernelGGL((linear_scan_bf16_kernel<MODE, ROWS, TPM>), dim3(blocks),
                      dim3(Geom<ROWS>::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
-template <int MODE>
+template <int MODE, int TPM>
 hipError_t launch_rows(const LinearArgs& a, int rows, hipStream_t s) {
   switch (rows) {
-    case 64: return launch_one<MODE, 64>(a, s);
-    case 32: return launch_one<MODE, 32>(a, s);
-    default: return launch_one<MODE, 16>(a, s);
+    case 64: return launch_one<MODE, 64, TPM>(a, s);
+    case 32: return launch_one<MODE, 32, TPM>(a, s);
+    default: return launch_one<MODE, 16, TPM>(a, s);
   }
 }
 
 }  // namespace
 
 hipError_t launch_linear_bf16(const LinearArgs& a, int rows, hipStream_t s) {
-  if (a.b == 16) return launch_rows<MODE_B16>(a, rows, s);
-  if (a.b < 16) return launch_rows<MODE_SUB>(a, rows, s);
-  return launch_rows<MODE_MULTI>(a, rows, s);
+  if (a.b == 16) return launch_rows<MODE_B16, 1>(a, rows, s);
+  if (a.b < 16) return launch_rows<MODE_SUB, 1>(a, rows, s);
+  if (a.b == 32) return launch_rows<MODE_MULTI, 2>(a, rows, s);
+  if (a.b == 64) return launch_rows<MODE_MULTI, 4>(a, rows, s);
+  return launch_rows<MODE_MULTI, 0>(a, rows, s);
 }
 
 }  // namespace ttt
