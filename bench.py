@@ -97,6 +97,30 @@ def device_inputs(x):
     return d
 
 
+_FLUSH = None
+
+
+def flushed_launches(launch, reps):
+    """Single-launch times (us) with a 512 MiB write before each launch, so
+    that no input is left in the 256 MB MALL or the L2s: median, p10, p90."""
+    import torch
+    global _FLUSH
+    if _FLUSH is None:
+        _FLUSH = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+    ks = []
+    for i in range(reps):
+        _FLUSH.fill_(float(i))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        launch()
+        b.record()
+        torch.cuda.synchronize()
+        ks.append(a.elapsed_time(b) * 1e3)
+    ks = np.array(ks)
+    return {"median": float(np.median(ks)), "p10": float(np.percentile(ks, 10)),
+            "p90": float(np.percentile(ks, 90))}
+
+
 def time_launches(launch, steps, warmup):
     """Times `steps` back-to-back launches after `warmup` untimed ones, with
     device synchronisation around the timed region and one pair of events
@@ -129,7 +153,7 @@ def time_launches(launch, steps, warmup):
                              "p90": float(np.percentile(ks, 90))}
 
 
-def linear_case(wl, b, steps, warmup, x=None, rows=0):
+def linear_case(wl, b, steps, warmup, x=None, rows=0, flush_reps=0):
     import torch
     from test_rnn_layers_head_amd import ttt_linear_fwd
     from test_rnn_layers_head_amd import inputs
@@ -140,12 +164,14 @@ def linear_case(wl, b, steps, warmup, x=None, rows=0):
     launch = lambda: ttt_linear_fwd(d["q"], d["k"], d["v"], d["eta"], d["w0"], b, z=z, w_out=w,
                                     rows_per_workgroup=rows)
     wall, kmean, spread = time_launches(launch, steps, warmup)
+    flushed = flushed_launches(launch, flush_reps) if flush_reps else None
     assert torch.isfinite(z).all().item()
     byts = linear_alg_bytes(wl)
     res = {
         "workload": wl.name, "b": b, "token_heads_per_s": wl.token_heads / (wall * 1e-3),
         "ms_per_step": wall, "kernel_us_mean": kmean, "kernel_us_median": spread["median"],
         "kernel_us_p10": spread["p10"], "kernel_us_p90": spread["p90"],
+        "kernel_us_flushed": flushed,
         "alg_bytes": byts, "hbm_GBps": byts / (kmean * 1e-6) / 1e9,
         "hbm_frac": byts / (kmean * 1e-6) / 1e9 / HBM_PEAK_GBS,
         "mfma_frac": linear_alg_flops(wl, b) / (kmean * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
@@ -194,17 +220,23 @@ def stream_copy_GBps(nbytes=1 << 30, reps=10):
     return 2 * nbytes / (kmean * 1e-6) / 1e9
 
 
-def cpu_baseline(x, b):
-    """The fp64 primal oracle as it stands, on the host cores."""
+def cpu_baseline(x, b, min_seconds=3.0, nthreads=None):
+    """The fp64 primal oracle as it stands, on the host cores: whole calls on
+    the workload, repeated until `min_seconds` of wall time have passed."""
     from oracle import oracle
-    n = oracle.default_threads()
+    n = nthreads or oracle.default_threads()
     q, k, v, eta = (a.astype(np.float64) for a in (x.q, x.k, x.v, x.eta))
+    calls = 0
     t0 = time.perf_counter()
-    oracle.linear(q, k, v, eta, x.w0, b, nthreads=n)
-    dt = time.perf_counter() - t0
-    return {"value": x.wl.token_heads / dt, "unit": UNIT, "cores": n, "kind": "oracle",
+    while True:
+        oracle.linear(q, k, v, eta, x.w0, b, nthreads=n)
+        calls += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": calls * x.wl.token_heads / dt, "unit": UNIT, "cores": n, "kind": "oracle",
             "sample": f"all {x.wl.units} (batch, head) units of {x.wl.name}, b={b}, "
-                      f"fp64 sequential primal form, {dt:.2f} s wall"}
+                      f"fp64 sequential primal form, {calls} calls in {dt:.2f} s wall"}
 
 
 def auto_rows(units: int) -> int:
@@ -346,7 +378,7 @@ def main():
     log(f"[bench] generating {wl.name} inputs")
     x = inputs.make_inputs(wl)
     log(f"[bench] timing ttt_linear_fwd on {wl.name}: {args.warmup} warmup + {args.steps} steps")
-    head = linear_case(wl, b, args.steps, args.warmup, x=x)
+    head = linear_case(wl, b, args.steps, args.warmup, x=x, flush_reps=0 if args.no_extras else 20)
     log(f"[bench] {head['kernel_us_mean']:.1f} us/launch, {head['hbm_frac']:.3f} of HBM peak")
 
     if args.pmc_calibrate:
@@ -373,11 +405,17 @@ def main():
             extras[w4.name] = {"error": str(e)}
         log("[bench] streaming copy reference")
         extras["stream_copy_GBps"] = stream_copy_GBps()
+        extras["headline_frac_of_stream_copy"] = head["hbm_GBps"] / extras["stream_copy_GBps"]
 
     cpu = None
     if not args.no_cpu:
         log("[bench] timing the fp64 oracle on the host (CPU baseline)")
         cpu = cpu_baseline(x, b)
+        if not args.no_extras:
+            for wid in (1, 2):
+                wx = inputs.make_inputs(inputs.workload(wid))
+                log(f"[bench] fp64 oracle, one thread, {wx.wl.name}")
+                extras[f"cpu_oracle_1thread_{wx.wl.name}"] = cpu_baseline(wx, 16, 1.0, nthreads=1)
 
     traffic = traffic_for("linear_scan", SCAN_SOURCES, head["alg_bytes"])
     rec = {
@@ -404,6 +442,7 @@ def main():
                      "kernel_us_median": head["kernel_us_median"],
                      "kernel_us_p10": head["kernel_us_p10"],
                      "kernel_us_p90": head["kernel_us_p90"],
+                     "kernel_us_flushed": head["kernel_us_flushed"],
                      "mfma_frac": head["mfma_frac"]},
         "cpu_baseline": cpu,
         "extras": extras,
