@@ -14,9 +14,9 @@
 //   waves NCW, NCW+1  helpers: build every per-tile operand that depends only
 //                     on K, Q, eta, two tiles ahead, into a double-buffered
 //                     "prepared" LDS area laid out lane-linear (conflict-free
-//                     16-byte reads); helper 0 makes triu(K^T Q), K_{j-1}^T K_j,
-//                     2 eta (and the sub-batch inverse), helper 1 K_{j-1}^T Q_j
-//                     and the update operand;
+//                     16-byte reads); helper 0 makes triu(K^T Q), K_{j-1}^T K_j
+//                     and 2 eta, helper 1 the update operand (and the
+//                     sub-batch inverse);
 //   wave NCW+2        loader: buffer->LDS DMA of 16-token K/Q/V/eta tiles,
 //                     D tiles ahead, into a ring (zero-filled past T).
 // The compute waves read every LDS operand of a tile one iteration before
@@ -27,11 +27,15 @@
 //
 // Serial chain per tile.  Only P_j = W_j K_j feeds the recurrence.  Using
 //   P_{j+1} = W_j K_{j+1} + Gn_j (K_j^T K_{j+1})     (W_{j+1} = W_j + Gn_j K_j^T)
-// the large product W_j K_{j+1} (and W_j Q_{j+1}) is formed one tile early
-// from W_j, so the per-tile critical path is two MFMAs plus the gradient's
-// few VALU ops; the W update, the bf16 hi/lo split of W and the output
-// products overlap with it.  V enters the same accumulator exactly, as
-// (-I) applied to V's rows on MFMA, so the chain yields P - V directly.
+// the large product W_j K_{j+1} is formed one tile early from W_j, so the
+// per-tile critical path is two MFMAs plus the gradient's few VALU ops; the
+// W update, the bf16 hi/lo split of W and the output products overlap with
+// it.  The outputs need no lookahead: R_j = W_j Q_j is formed from the same
+// split of W_j, off the chain.  V enters P's accumulator exactly, as (-I)
+// applied to V's rows on MFMA, so the chain yields P - V directly.
+//
+// The outputs are formed transposed (W Q rather than (W Q)^T), so each lane
+// holds 4 consecutive rows of one token and stores them in one 16-byte write.
 //
 // Precision: fp32 operands enter bf16 MFMA as hi + lo pairs (three products
 // kept, error ~2^-16 relative); K, Q, V are exact bf16; accumulation fp32.
@@ -62,13 +66,12 @@ struct Geom {
   static constexpr int RAW = 2 * KB + VB + 64;   // + eta (16 fp32)
   static constexpr int NI = 4 + (VB + 1023) / 1024 + 1;  // DMA ops per tile
   static constexpr int D = (63 / NI) < 10 ? (63 / NI) : 10;
-  static constexpr int NST = D + 2;
+  static constexpr int NST = D + 3;
   // prepared-operand slot (per tile), byte offsets
   static constexpr int P_E2 = 0;                  // 2 eta_t, 16 fp32
   static constexpr int P_A = 64;                  // triu(K^T Q), hi | lo
   static constexpr int P_MKK = P_A + 1024;        // K_{j-1}^T K_j, hi | lo
-  static constexpr int P_MKQ = P_MKK + 1024;      // K_{j-1}^T Q_j, hi | lo
-  static constexpr int P_KT = P_MKQ + 1024;       // update operand K[t][j], x2
+  static constexpr int P_KT = P_MKK + 1024;       // update operand K[t][j], x4
   static constexpr int P_U = P_KT + 4096;         // sub-batch inverse (b < 16)
   static constexpr int PREP = P_U + 1024;
   static constexpr int LDS = NST * RAW + 2 * PREP;
@@ -116,6 +119,13 @@ __device__ __forceinline__ f32x4 mm_pre(bf16x8 x, const YOps& y, f32x4 acc) {
   acc = mfma_k32(x, y.l0, acc);
   return acc;
 }
+// The same three terms of the transposed product, acc + Y^T X^T, with the
+// operands in swapped roles: accumulator [col][row].
+__device__ __forceinline__ f32x4 mm_pre_t(const YOps& y, bf16x8 x, f32x4 acc) {
+  acc = mfma_k32(y.hh, x, acc);
+  acc = mfma_k32(y.l0, x, acc);
+  return acc;
+}
 __device__ __forceinline__ bf16x8 get8(const char* p, int lane) {
   return *(const bf16x8*)(p + lane * 16);
 }
@@ -155,8 +165,9 @@ linear_scan_bf16_kernel(LinearArgs a) {
   // iteration j (which reads raw tile j+2 for the next iteration) and helper
   // iteration j (which prepares tile j+2 from raw tile j+2); before it the
   // loader makes sure raw tiles <= j+2 have landed.  B_-2 guarantees raw
-  // tiles 0 and 1.  Raw tile t is last read before B_{t-1}, so tile j+D+2
-  // is issued after B_{j-1} into the slot of tile j: NST = D + 2 slots.
+  // tiles 0 and 1.  Raw tile t is last read before B_t (its Q rows, one
+  // iteration ahead of the outputs of tile t), so tile j+D+2 is issued after
+  // B_{j-1} into the slot of tile j-1: NST = D + 3 slots.
   if (wave == G::NCW + 2) {
     const uint32_t ubytes = (uint32_t)T * 128;
     const size_t uoff = (size_t)unit * T * 64;
@@ -252,15 +263,12 @@ linear_scan_bf16_kernel(LinearArgs a) {
         put_split(pp + G::P_MKK, lane, Mkk);
         if (lane < 16) ((float*)(pp + G::P_E2))[lane] = 2.f * Et[lane];
       } else {
-        f32x4 Mkq = {0, 0, 0, 0}, KS[4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) Mkq = mfma_k32(kprev[h], qop[h], Mkq);  // k^{prev}_s . q_t
+        f32x4 KS[4];
         // Update operand kt[m][e] = K[t = 4g+e][sigma(m, c)], formed exactly
         // as K S_m with the one-hot selection S_m[j][c] = [j == sigma(m, c)]
         // (only the 32 columns of block m/2 can be selected).
 #pragma unroll
         for (int m = 0; m < 4; ++m) KS[m] = mfma_k32(kop[m >> 1], sel[m & 1], f32x4{0, 0, 0, 0});
-        put_split(pp + G::P_MKQ, lane, Mkq);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const uint32_t p0 = pack_rne(KS[m][0], KS[m][1]), p1 = pack_rne(KS[m][2], KS[m][3]);
@@ -325,9 +333,9 @@ linear_scan_bf16_kernel(LinearArgs a) {
   // share their SIMDs and must not delay it.
   __builtin_amdgcn_s_setprio(3);
   // Iteration j enters with W = W_j (fp32 accumulators), XB = W_{j-1} K_j - V_j
-  // and RB = W_{j-1} Q_j (formed in iteration j-1), gp = operands of Gn_{j-1},
-  // and in registers the prepared operands of tile j and the raw K/Q/V
-  // operands of tile j+1 (read from LDS during iteration j-1).
+  // (formed in iteration j-1), gp = operands of Gn_{j-1}, and in registers the
+  // prepared operands of tile j, the raw K/V operands of tile j+1 and the Q
+  // operands of tile j (read from LDS during iteration j-1).
   const int rbase = row0 + wave * 16;
   const float* w0 = a.w0 + (size_t)(a.w0_per_batch ? unit : head) * 4096;
   f32x4 W[4];
@@ -347,27 +355,27 @@ linear_scan_bf16_kernel(LinearArgs a) {
   gp.l0 = gp.hh;
   Split8 wg[2];  // gradient point operands (b > 16)
 
-  // raw operands of one tile for this lane: K and Q row chunks, V row chunk
+  // raw operands for this lane: K and V row chunks of one tile and the Q row
+  // chunks of the tile before it
   struct RawOps {
-    bf16x8 k[2], q[2], v;
+    bf16x8 k[2], v, q[2];
   };
-  auto load_raw = [&](RawOps& r, const char* st) {
+  auto load_raw = [&](RawOps& r, const char* st, const char* sq) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       r.k[h] = row_chunk(st, c, h, g);
-      r.q[h] = row_chunk(st + G::KB, c, h, g);
+      r.q[h] = row_chunk(sq + G::KB, c, h, g);
     }
     r.v = *(const bf16x8*)(st + voff);
   };
   // prepared operands of one tile for this lane
   struct PrepOps {
     f32x4 e2;
-    bf16x8 mkk, mkq, att, kt[4], u;
+    bf16x8 mkk, att, kt[4], u;
   };
   auto load_prep = [&](PrepOps& p, const char* pp) {
     p.e2 = *(const f32x4*)(pp + G::P_E2 + 16 * g);
     p.mkk = get8(pp + G::P_MKK, lane);
-    p.mkq = get8(pp + G::P_MKQ, lane);
     p.att = get8(pp + G::P_A, lane);
 #pragma unroll
     for (int m = 0; m < 4; ++m) p.kt[m] = get8(pp + G::P_KT + m * 1024, lane);
@@ -375,35 +383,33 @@ linear_scan_bf16_kernel(LinearArgs a) {
   };
 
   wg_barrier_pinned();  // B_{-2}: raw tiles 0 and 1 are in LDS
-  f32x4 XB = {0, 0, 0, 0}, RB = {0, 0, 0, 0};
-  RawOps ra;  // raw operands of tile j+1
+  f32x4 XB = {0, 0, 0, 0};
+  RawOps ra;  // raw K/V of tile j+1, Q of tile j
   {
     const Split8 ws[2] = {split8_mfma(W[0], W[1], ns), split8_mfma(W[2], W[3], ns)};
     wg[0] = ws[0];
     wg[1] = ws[1];
     RawOps r0;
-    load_raw(r0, raw);
+    load_raw(r0, raw, raw);
     XB = mfma_k32(r0.v, negI, XB);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       XB = mfma_k32(r0.k[h], ws[h].hi, XB);
       XB = mfma_k32(r0.k[h], ws[h].lo, XB);
-      RB = mfma_k32(r0.q[h], ws[h].hi, RB);
-      RB = mfma_k32(r0.q[h], ws[h].lo, RB);
     }
-    load_raw(ra, raw + 1 * G::RAW);
+    load_raw(ra, raw + 1 * G::RAW, raw);
   }
   wait_lgkm0();
   wg_barrier_pinned();  // B_{-1}: prepared tile 0 is in LDS
   PrepOps pa, pb;  // prepared operands of tiles j and j+1 (two register sets)
-  RawOps rb;       // raw operands of tile j+2
+  RawOps rb;       // raw K/V of tile j+2, Q of tile j+1
   load_prep(pa, prep);
 
   // Z through a range-checked buffer: rows past T (padding of the last
   // tile) are dropped by the hardware, so the loop body has no branches and
   // the scheduler can interleave the serial chain with everything else.
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(a.z + (size_t)unit * T * 64, (uint32_t)T * 256);
-  uint32_t zoff = (uint32_t)((4 * g * 64 + rbase + c) * 4);
+  uint32_t zoff = (uint32_t)((c * 64 + rbase + 4 * g) * 4);  // token c, rows 4g..4g+3
 
   // One tile: uses (pc, rc), fills (pn, rn) for the next one.  The loop
   // below alternates two register sets, so nothing is copied between
@@ -414,10 +420,11 @@ linear_scan_bf16_kernel(LinearArgs a) {
                   RawOps& rn) {
     wait_lgkm0();
     wg_barrier_pinned();  // B_j
-    // next iteration's operands: prepared tile j+1, raw tile j+2 (stale
-    // past the end of the sequence, where they are never used)
+    // next iteration's operands: prepared tile j+1, raw K/V of tile j+2 and
+    // Q of tile j+1 (stale past the end of the sequence, where they are never
+    // used)
     load_prep(pn, prep + ((j + 1) & 1) * G::PREP);
-    load_raw(rn, raw + ((j + 2) % G::NST) * G::RAW);
+    load_raw(rn, raw + ((j + 2) % G::NST) * G::RAW, raw + ((j + 1) % G::NST) * G::RAW);
     __builtin_amdgcn_sched_barrier(0);  // the reads go out first
     constexpr int pos = decltype(POS)::value;
     const bool new_mb = MODE != MODE_MULTI || (pos >= 0 ? pos == 0 : (j % tpm) == 0);
@@ -446,7 +453,7 @@ linear_scan_bf16_kernel(LinearArgs a) {
       }
     }
     f32x4 XBn = mfma_k32(rc.v, negI, f32x4{0, 0, 0, 0});
-    f32x4 RBn = {0, 0, 0, 0};
+    f32x4 R = {0, 0, 0, 0};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       bf16x8 whi = ws[h].hi, wlo = ws[h].lo;
@@ -456,18 +463,15 @@ linear_scan_bf16_kernel(LinearArgs a) {
       }
       XBn = mfma_k32(rc.k[h], whi, XBn);
       XBn = mfma_k32(rc.k[h], wlo, XBn);
-      RBn = mfma_k32(rc.q[h], ws[h].hi, RBn);
-      RBn = mfma_k32(rc.q[h], ws[h].lo, RBn);
+      R = mfma_k32(ws[h].hi, rc.q[h], R);
+      R = mfma_k32(ws[h].lo, rc.q[h], R);
     }
 
-    // ---- outputs: Z_j = W_j Q_j + Gn_j triu(K_j^T Q_j)
-    f32x4 Z = mm_pre(pc.mkq, gp, RB);
-    Z = mm_pre(pc.att, gy, Z);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float zr = Z[r];  // element by value (a bit_cast of Z[r] itself reads element 0)
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(zr), rz, zoff + r * 256, 0, 2);
-    }
+    // ---- outputs: Z_j = W_j Q_j + Gn_j triu(K_j^T Q_j); lane (c, g) holds
+    // rows 4g..4g+3 of token c
+    const f32x4 Z = mm_pre_t(gy, pc.att, R);
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Z), rz, zoff, 0, 2);
     zoff += 16 * 64 * 4;
 
     // ---- rank-16 update W_{j+1} = W_j + Gn_j K_j^T
@@ -475,7 +479,6 @@ linear_scan_bf16_kernel(LinearArgs a) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) W[m] = mfma_k32(pc.kt[m], g2, W[m]);
     XB = XBn;
-    RB = RBn;
     gp = gy;
   };
   int j = 0;
