@@ -47,6 +47,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.ttt_oracle_linear.restype = I
     lib.ttt_oracle_mlp.argtypes = [dp, dp, dp, dp, dp, dp, I, L, L, L, L, L, L, dp, dp, dp, I]
     lib.ttt_oracle_mlp.restype = I
+    D = ctypes.c_double
+    lib.ttt_oracle_linear_ln.argtypes = [dp, dp, dp, dp, dp, I, dp, dp, D, L, L, L, L, L, dp, dp, I]
+    lib.ttt_oracle_linear_ln.restype = I
     return lib
 
 
@@ -124,3 +127,29 @@ def mlp(q, k, v, eta, w1_0, w2_0, b: int, nthreads: int | None = None, lib=None)
     if rc != 0:
         raise RuntimeError(f"ttt_oracle_mlp failed with status {rc}")
     return z, w1, w2
+
+
+def linear_ln(q, k, v, eta, w0, gamma, beta, eps: float, b: int, nthreads: int | None = None,
+              lib=None):
+    """TTT-Linear with the LayerNorm + residual inner model, primal forward:
+    f(x) = x + gamma * (Wx - mean) / sqrt(var + eps) + beta over the d output
+    components of each token.
+
+    gamma, beta: [H, d] (per head).  Other arguments as for ``linear``.
+    Returns (z [B, H, T, d], w_T [B, H, d, d]) in float64.
+    """
+    q, k, v, eta, w0, gamma, beta = map(_f64, (q, k, v, eta, w0, gamma, beta))
+    B, H, T, d = q.shape
+    assert k.shape == q.shape and v.shape == q.shape and eta.shape == (B, H, T)
+    assert gamma.shape == (H, d) and beta.shape == (H, d)
+    per_batch = 1 if w0.ndim == 4 else 0
+    assert w0.shape == ((B, H, d, d) if per_batch else (H, d, d))
+    z = np.zeros((B, H, T, d))
+    w_out = np.zeros((B, H, d, d))
+    lib = lib or load()
+    rc = lib.ttt_oracle_linear_ln(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w0), per_batch,
+                                  _ptr(gamma), _ptr(beta), float(eps), B, H, T, d, int(b),
+                                  _ptr(z), _ptr(w_out), nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"ttt_oracle_linear_ln failed with status {rc}")
+    return z, w_out

@@ -24,7 +24,11 @@
  *    is a per-token input that scales token t's own gradient (no 1/b).
  *  - §4.4 Inner models: TTT-Linear f(x) = W x; TTT-MLP f(x) = W2 GELU(W1 x)
  *    with a hidden width that the caller chooses (4x the input on the page).
- *    The LayerNorm + residual wrapper of §4.4 is not part of this oracle.
+ *  - §4.4 LayerNorm + residual wrapper, TTT-Linear only:
+ *    f(x) = x + LN(W x), LN(y) = gamma * (y - mean(y)) / sqrt(var(y) + eps)
+ *    + beta over the d output components of one token (population variance;
+ *    gamma, beta per head and eps are inputs: the page names the wrapper but
+ *    not its parameters).  The gradient goes through the LayerNorm.
  *
  * The loss is the squared L2 norm summed over output components, so its
  * gradient carries the factor 2 (§3.6 linear derivation: G_t = 2(W0 x - x)x^T).
@@ -77,6 +81,70 @@ static void linear_unit(const double *q, const double *k, const double *v,
         for (long j = 0; j < d; ++j) s += W[i * d + j] * qt[j];
         z[t * d + i] = s;
       }
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* TTT-Linear with LayerNorm + residual: f(x) = x + LN(W x).           */
+/* ------------------------------------------------------------------ */
+/* yhat = (y - mean(y)) / sqrt(var(y) + eps) over the d components; returns
+ * 1 / sqrt(var + eps).  Two passes: the mean, then the squared deviations. */
+static double ln_normalise(const double *y, long d, double eps, double *yhat) {
+  double mu = 0.0;
+  for (long i = 0; i < d; ++i) mu += y[i];
+  mu /= (double)d;
+  double var = 0.0;
+  for (long i = 0; i < d; ++i) var += (y[i] - mu) * (y[i] - mu);
+  var /= (double)d;
+  const double rs = 1.0 / sqrt(var + eps);
+  for (long i = 0; i < d; ++i) yhat[i] = (y[i] - mu) * rs;
+  return rs;
+}
+
+static void linear_ln_unit(const double *q, const double *k, const double *v,
+                           const double *eta, const double *w0, const double *gamma,
+                           const double *beta, double eps, long T, long d, long b,
+                           double *z, double *w_out, double *Ws, double *y,
+                           double *yhat, double *gy) {
+  double *W = w_out;
+  memcpy(W, w0, sizeof(double) * (size_t)(d * d));
+  for (long m0 = 0; m0 < T; m0 += b) {
+    long m1 = m0 + b < T ? m0 + b : T;
+    memcpy(Ws, W, sizeof(double) * (size_t)(d * d)); /* gradient point W_{t'} */
+    for (long t = m0; t < m1; ++t) {
+      const double *kt = k + t * d, *vt = v + t * d, *qt = q + t * d;
+      const double et = eta[t];
+      /* forward on the training view at the gradient point */
+      for (long i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (long j = 0; j < d; ++j) acc += Ws[i * d + j] * kt[j];
+        y[i] = acc;
+      }
+      const double rs = ln_normalise(y, d, eps, yhat);
+      /* l = sum_i (k_i + gamma_i yhat_i + beta_i - v_i)^2;
+         dl/dyhat_i = 2 gamma_i (f_i - v_i) */
+      double m1s = 0.0, m2s = 0.0;
+      for (long i = 0; i < d; ++i) {
+        const double f = kt[i] + gamma[i] * yhat[i] + beta[i];
+        gy[i] = 2.0 * gamma[i] * (f - vt[i]);
+        m1s += gy[i];
+        m2s += gy[i] * yhat[i];
+      }
+      m1s /= (double)d;
+      m2s /= (double)d;
+      /* LayerNorm VJP: dl/dy = rs (g - mean(g) - yhat mean(g yhat)) */
+      for (long i = 0; i < d; ++i) gy[i] = rs * (gy[i] - m1s - yhat[i] * m2s);
+      for (long i = 0; i < d; ++i)
+        for (long j = 0; j < d; ++j) W[i * d + j] -= et * gy[i] * kt[j];
+      /* z_t = q_t + LN(W_t q_t) with the updated state */
+      for (long i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (long j = 0; j < d; ++j) acc += W[i * d + j] * qt[j];
+        y[i] = acc;
+      }
+      ln_normalise(y, d, eps, yhat);
+      for (long i = 0; i < d; ++i) z[t * d + i] = qt[i] + gamma[i] * yhat[i] + beta[i];
     }
   }
 }
@@ -151,8 +219,9 @@ static void mlp_unit(const double *q, const double *k, const double *v,
 /* Threading: units (batch, head) are independent; static round robin. */
 /* ------------------------------------------------------------------ */
 typedef struct {
-  int kind; /* 0 linear, 1 mlp */
-  const double *q, *k, *v, *eta, *w0a, *w0b;
+  int kind; /* 0 linear, 1 mlp, 2 linear with LayerNorm + residual */
+  const double *q, *k, *v, *eta, *w0a, *w0b, *gamma, *beta;
+  double eps;
   int w0_per_batch;
   long B, H, T, d, hd, b;
   double *z, *outa, *outb;
@@ -164,8 +233,9 @@ static void *worker(void *arg) {
   const long d = jb->d, hd = jb->hd, T = jb->T;
   const long units = jb->B * jb->H;
   double *buf = NULL;
-  size_t need = jb->kind == 0 ? (size_t)(d * d + d)
-                              : (size_t)(2 * hd * d + 4 * hd + d);
+  size_t need = jb->kind == 0   ? (size_t)(d * d + d)
+                : jb->kind == 2 ? (size_t)(d * d + 3 * d)
+                                : (size_t)(2 * hd * d + 4 * hd + d);
   buf = (double *)malloc(sizeof(double) * need);
   if (!buf) { jb->status = 1; return NULL; }
   for (long u = jb->tid; u < units; u += jb->nthreads) {
@@ -177,6 +247,10 @@ static void *worker(void *arg) {
     if (jb->kind == 0) {
       linear_unit(qu, ku, vu, eu, jb->w0a + wsel * d * d, T, d, jb->b, zu,
                   jb->outa + u * d * d, buf, buf + d * d);
+    } else if (jb->kind == 2) {
+      linear_ln_unit(qu, ku, vu, eu, jb->w0a + wsel * d * d, jb->gamma + hh * d,
+                     jb->beta + hh * d, jb->eps, T, d, jb->b, zu, jb->outa + u * d * d,
+                     buf, buf + d * d, buf + d * d + d, buf + d * d + 2 * d);
     } else {
       mlp_scratch s;
       s.W1s = buf;
@@ -250,5 +324,20 @@ int ttt_oracle_mlp(const double *q, const double *k, const double *v,
   p.kind = 1; p.q = q; p.k = k; p.v = v; p.eta = eta; p.w0a = w1_0; p.w0b = w2_0;
   p.w0_per_batch = w0_per_batch; p.B = B; p.H = H; p.T = T; p.d = d; p.hd = hidden;
   p.b = b; p.z = z; p.outa = w1_out; p.outb = w2_out;
+  return run(p, nthreads);
+}
+
+int ttt_oracle_linear_ln(const double *q, const double *k, const double *v,
+                         const double *eta, const double *w0, int w0_per_batch,
+                         const double *gamma, const double *beta, double eps,
+                         long B, long H, long T, long d, long b, double *z,
+                         double *w_out, int nthreads) {
+  if (!(eps >= 0.0)) return 2;
+  job p;
+  memset(&p, 0, sizeof p);
+  p.kind = 2; p.q = q; p.k = k; p.v = v; p.eta = eta; p.w0a = w0;
+  p.gamma = gamma; p.beta = beta; p.eps = eps;
+  p.w0_per_batch = w0_per_batch; p.B = B; p.H = H; p.T = T; p.d = d; p.hd = 0;
+  p.b = b; p.z = z; p.outa = w_out;
   return run(p, nthreads);
 }

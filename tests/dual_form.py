@@ -41,6 +41,38 @@ def linear_unit(q, k, v, eta, w0, b):
     return Z, W
 
 
+def _ln_columns(Y, eps):
+    """Per-column LayerNorm statistics (columns are tokens): normalised Y and
+    1 / sqrt(var + eps), population variance."""
+    mu = Y.mean(axis=0)
+    var = ((Y - mu) ** 2).mean(axis=0)
+    rs = 1.0 / np.sqrt(var + eps)
+    return (Y - mu) * rs, rs
+
+
+def linear_ln_unit(q, k, v, eta, w0, gamma, beta, eps, b):
+    """One unit of TTT-Linear with the §4.4 LayerNorm + residual wrapper,
+    f(x) = x + gamma * LNhat(W x) + beta, in the dual form: the gradients of
+    a whole mini-batch at its starting W (the LayerNorm VJP column by column),
+    the outputs from W0 Q - G triu(K^T Q) before the output LayerNorm."""
+    T, d = q.shape
+    W = np.array(w0, dtype=np.float64)
+    Z = np.zeros((T, d))
+    gc, bc = gamma[:, None], beta[:, None]
+    for m0 in range(0, T, b):
+        m1 = min(T, m0 + b)
+        XK, XV, XQ = k[m0:m1].T, v[m0:m1].T, q[m0:m1].T
+        e = eta[m0:m1]
+        Yh, rs = _ln_columns(W @ XK, eps)
+        Gh = 2.0 * gc * (XK + gc * Yh + bc - XV)
+        GY = rs[None, :] * (Gh - Gh.mean(axis=0) - Yh * (Gh * Yh).mean(axis=0))
+        G = GY * e[None, :]
+        Oh, _ = _ln_columns(W @ XQ - G @ np.triu(XK.T @ XQ), eps)
+        Z[m0:m1] = (XQ + gc * Oh + bc).T
+        W = W - G @ XK.T
+    return Z, W
+
+
 def mlp_unit(q, k, v, eta, w1, w2, b):
     """One unit of TTT-MLP, f(x) = W2 GELU(W1 x)."""
     T, d = q.shape
@@ -94,3 +126,15 @@ def mlp(q, k, v, eta, w1, w2, b):
             Z[bi, h], W1T[bi, h], W2T[bi, h] = mlp_unit(q[bi, h], k[bi, h], v[bi, h], eta[bi, h],
                                                        a, c, b)
     return Z, W1T, W2T
+
+
+def linear_ln(q, k, v, eta, w0, gamma, beta, eps, b):
+    B, H, T, d = q.shape
+    Z = np.zeros((B, H, T, d))
+    WT = np.zeros((B, H, d, d))
+    for bi in range(B):
+        for h in range(H):
+            w = w0[bi, h] if w0.ndim == 4 else w0[h]
+            Z[bi, h], WT[bi, h] = linear_ln_unit(q[bi, h], k[bi, h], v[bi, h], eta[bi, h], w,
+                                                 gamma[h], beta[h], eps, b)
+    return Z, WT

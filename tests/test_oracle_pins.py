@@ -18,6 +18,12 @@ Time): RNNs with Expressive Hidden States"):
 * hand-worked scalar examples (tests/golden/scalar_worked_examples.json);
 * MLP special cases: zero state stays zero; W2_0 = 0 with b = T is a
   kernelised linear attention with feature map GELU(W1_0 x);
+* LayerNorm + residual wrapper (§4.4) of TTT-Linear: primal == a batched dual
+  form; one mini-batch equals one gradient step through the LayerNorm
+  (central differences); gamma = 0 freezes the state and gives z = q + beta;
+  with eps = 0 the scan is covariant under (W0, eta) -> (a W0, a^2 eta)
+  (LayerNorm is scale-free, its VJP scales as 1/a); with gamma = 1, beta = 0,
+  eps = 0 every output minus its query has mean 0 and variance 1;
 * invariants: homogeneity, superposition, row permutation, state passing,
   thread-count determinism.
 
@@ -238,6 +244,75 @@ def pin_mlp_w2_zero_kernel_attention(lib):
     assert np.array_equal(a[0, 0], w1[0])
 
 
+def rand_ln(rng, H, d, g_scale=0.3, b_scale=0.2):
+    gamma = 1.0 + g_scale * rng.standard_normal((H, d))
+    beta = b_scale * rng.standard_normal((H, d))
+    return gamma, beta
+
+
+def pin_ln_primal_equals_dual(lib):
+    rng = np.random.default_rng(31)
+    for b in (1, 3, 4, 16):
+        q, k, v, eta, w0 = rand_linear(rng, 2, 2, 21, 6, eta_scale=0.3)
+        gamma, beta = rand_ln(rng, 2, 6)
+        zp, wp = oracle.linear_ln(q, k, v, eta, w0, gamma, beta, 1e-5, b, lib=lib)
+        zd, wd = dual_form.linear_ln(q, k, v, eta, w0, gamma, beta, 1e-5, b)
+        assert rel(zp, zd) < 1e-12 and rel(wp, wd) < 1e-12, b
+
+
+def pin_ln_one_step_finite_differences(lib):
+    rng = np.random.default_rng(32)
+    T, d = 3, 5
+    q, k, v, eta, w0 = rand_linear(rng, 1, 1, T, d, eta_scale=0.5, w_scale=0.5)
+    gamma, beta = rand_ln(rng, 1, d)
+    eps = 1e-3
+    _, w1 = oracle.linear_ln(q, k, v, eta, w0, gamma, beta, eps, T, lib=lib)
+    K, V, e, g, bb = k[0, 0], v[0, 0], eta[0, 0], gamma[0], beta[0]
+
+    def L(W):
+        Y = K @ W.T  # tokens as rows
+        mu = Y.mean(axis=1, keepdims=True)
+        var = ((Y - mu) ** 2).mean(axis=1, keepdims=True)
+        r = K + g * (Y - mu) / np.sqrt(var + eps) + bb - V
+        return float(np.sum(e * np.sum(r * r, axis=1)))
+
+    h = 1e-6
+    grad = np.zeros((d, d))
+    for idx in np.ndindex(d, d):
+        E = np.zeros((d, d))
+        E[idx] = h
+        grad[idx] = (L(w0[0] + E) - L(w0[0] - E)) / (2 * h)
+    assert rel(w1[0, 0], w0[0] - grad) < 1e-8
+
+
+def pin_ln_gamma_zero(lib):
+    rng = np.random.default_rng(33)
+    q, k, v, eta, w0 = rand_linear(rng, 2, 2, 13, 6, eta_scale=0.5)
+    _, beta = rand_ln(rng, 2, 6)
+    z, w = oracle.linear_ln(q, k, v, eta, w0, np.zeros((2, 6)), beta, 1e-5, 4, lib=lib)
+    assert np.array_equal(w, np.broadcast_to(w0, w.shape))
+    assert np.array_equal(z, q + beta[None, :, None, :])
+
+
+def pin_ln_scale_covariance(lib):
+    rng = np.random.default_rng(34)
+    q, k, v, eta, w0 = rand_linear(rng, 1, 2, 29, 6, eta_scale=0.2)
+    gamma, beta = rand_ln(rng, 2, 6)
+    a = 3.0
+    z1, w1 = oracle.linear_ln(q, k, v, eta, w0, gamma, beta, 0.0, 4, lib=lib)
+    z2, w2 = oracle.linear_ln(q, k, v, a * a * eta, a * w0, gamma, beta, 0.0, 4, lib=lib)
+    assert rel(z2, z1) < 1e-12 and rel(w2, a * w1) < 1e-12
+
+
+def pin_ln_normalised_outputs(lib):
+    rng = np.random.default_rng(35)
+    q, k, v, eta, w0 = rand_linear(rng, 2, 1, 19, 8, eta_scale=0.3)
+    z, _ = oracle.linear_ln(q, k, v, eta, w0, np.ones((1, 8)), np.zeros((1, 8)), 0.0, 4, lib=lib)
+    y = z - q
+    assert np.abs(y.mean(axis=-1)).max() < 1e-13
+    assert np.abs((y * y).mean(axis=-1) - 1.0).max() < 1e-12
+
+
 PINS = [
     pin_linear_primal_equals_dual,
     pin_mlp_primal_equals_dual,
@@ -251,6 +326,11 @@ PINS = [
     pin_mlp_one_step_finite_differences,
     pin_mlp_zero_state,
     pin_mlp_w2_zero_kernel_attention,
+    pin_ln_primal_equals_dual,
+    pin_ln_one_step_finite_differences,
+    pin_ln_gamma_zero,
+    pin_ln_scale_covariance,
+    pin_ln_normalised_outputs,
 ]
 
 
@@ -334,6 +414,18 @@ MUTATIONS = {
     "mlp_backprop_through_current_w2": ("acc += s->W2s[i * hd + u] * s->e[i];", "acc += W2[i * hd + u] * s->e[i];"),
     "mlp_output_from_start_w1": ("acc += W1[u * d + j] * qt[j];", "acc += s->W1s[u * d + j] * qt[j];"),
     "mlp_gelu_scale": ("return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));", "return 0.5 * x * (1.0 + erf(x));"),
+    "ln_sample_variance": ("  var /= (double)d;", "  var /= (double)(d - 1);"),
+    "ln_eps_outside_sqrt": ("1.0 / sqrt(var + eps);", "1.0 / (sqrt(var) + eps);"),
+    "ln_drop_mean_term": ("rs * (gy[i] - m1s - yhat[i] * m2s);", "rs * (gy[i] - yhat[i] * m2s);"),
+    "ln_drop_projection_term": ("rs * (gy[i] - m1s - yhat[i] * m2s);", "rs * (gy[i] - m1s);"),
+    "ln_drop_rs": ("gy[i] = rs * (gy[i] -", "gy[i] = (gy[i] -"),
+    "ln_no_residual_in_loss": ("const double f = kt[i] + gamma[i] * yhat[i] + beta[i];",
+                               "const double f = gamma[i] * yhat[i] + beta[i];"),
+    "ln_no_residual_in_output": ("z[t * d + i] = qt[i] + gamma[i] * yhat[i] + beta[i];",
+                                 "z[t * d + i] = gamma[i] * yhat[i] + beta[i];"),
+    "ln_no_gamma_in_vjp": ("gy[i] = 2.0 * gamma[i] * (f - vt[i]);", "gy[i] = 2.0 * (f - vt[i]);"),
+    "ln_output_before_update": ("acc += W[i * d + j] * qt[j];", "acc += Ws[i * d + j] * qt[j];"),
+    "ln_grad_at_current_state": ("acc += Ws[i * d + j] * kt[j];", "acc += W[i * d + j] * kt[j];"),
 }
 
 
