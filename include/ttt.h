@@ -46,6 +46,7 @@
  *            TTT-Linear: fp32 or bf16 q/k/v; mini-batch b with b | 16 or
  *            16 | b (1, 2, 4, 8, 16, 32, 48, 64, ...).
  *            TTT-MLP: hidden = 256, bf16 q/k/v, b | 16 (1, 2, 4, 8, 16).
+ *            TTT-Linear with LayerNorm: bf16 q/k/v, 16 | b.
  *            Anything else is TTT_ERR_UNSUPPORTED.
  *            Empty work (B*H == 0) returns TTT_OK without launching; T == 0
  *            copies the initial states to the final-state outputs.
@@ -69,7 +70,8 @@ typedef enum {
   TTT_ERR_UNSUPPORTED = 4, /* d, hidden or b outside the supported set      */
   TTT_ERR_ALIAS = 5,       /* an output overlaps an input (see Aliasing)    */
   TTT_ERR_HIP = 6,         /* the HIP runtime reported an error             */
-  TTT_ERR_ALIGN = 7        /* a tensor pointer is not 16-byte aligned       */
+  TTT_ERR_ALIGN = 7,       /* a tensor pointer is not 16-byte aligned       */
+  TTT_ERR_VALUE = 8        /* a scalar argument is out of range             */
 } ttt_status_t;
 
 typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype_t;
@@ -94,6 +96,37 @@ ttt_status_t ttt_linear_fwd(const void* q, const void* k, const void* v,
                             int32_t T, int32_t d, int32_t b,
                             ttt_dtype_t qkv_dtype, float* z, float* w_out,
                             void* stream);
+
+/*
+ * TTT-Linear with the LayerNorm + residual inner model (§4.4):
+ *   f(x) = x + LN(W x),  LN(y) = gamma * (y - mean(y)) / sqrt(var(y) + eps)
+ *          + beta,
+ * mean and population variance over the d components of one token.  The
+ * inner loss ||f(k_t) - v_t||^2 (§3.3) is differentiated through the
+ * LayerNorm; mini-batches as for ttt_linear_fwd (§3.5, §3.6), outputs
+ * z_t = q_t + LN(W_t q_t) from the updated state (§3.1).
+ *
+ *   q, k, v        : [B][H][T][d] bf16          eta : [B][H][T] fp32
+ *   w0             : [H][d][d] or [B][H][d][d] fp32 (as ttt_linear_fwd)
+ *   ln_gamma, ln_beta : [H][d] fp32, the LayerNorm scale and shift of each
+ *                    head (the page names the wrapper, not its parameters:
+ *                    per head, shared by the batch)
+ *   eps            : LayerNorm epsilon, finite and > 0, else TTT_ERR_VALUE
+ *   z              : out [B][H][T][d] fp32;  w_out : out [B][H][d][d] fp32
+ *
+ * Support: d = 64, bf16 q/k/v, mini-batch b a multiple of 16 (16, 32, 48,
+ * 64, ...); otherwise TTT_ERR_UNSUPPORTED.  Below 16 tokens a mini-batch's
+ * gradients depend non-linearly (through the LayerNorm) on the updates of
+ * the mini-batches before it inside one 16-token tile, which the one-tile
+ * dual form here does not evaluate.  One workgroup per (batch, head).
+ */
+ttt_status_t ttt_linear_ln_fwd(const void* q, const void* k, const void* v,
+                               const float* eta, const float* w0,
+                               int32_t w0_per_batch, const float* ln_gamma,
+                               const float* ln_beta, float eps, int32_t B,
+                               int32_t H, int32_t T, int32_t d, int32_t b,
+                               ttt_dtype_t qkv_dtype, float* z, float* w_out,
+                               void* stream);
 
 /*
  * TTT-MLP forward scan, f(x) = W2 GELU(W1 x) (§3.7 dual form, §4.4).

@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libttt.so")
 STATUS = {
     0: "TTT_OK", 1: "TTT_ERR_NULL", 2: "TTT_ERR_SHAPE", 3: "TTT_ERR_DTYPE",
     4: "TTT_ERR_UNSUPPORTED", 5: "TTT_ERR_ALIAS", 6: "TTT_ERR_HIP", 7: "TTT_ERR_ALIGN",
+    8: "TTT_ERR_VALUE",
 }
 TTT_F32, TTT_BF16 = 0, 1
 
@@ -22,6 +23,8 @@ SIGNATURES = {
                               _vp, _vp, _vp]),
     "ttt_linear_fwd_tuned": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _vp, _vp, _vp, _i32]),
+    "ttt_linear_ln_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, ctypes.c_float, _i32,
+                                 _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "ttt_mlp_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                            _i32, _vp, _vp, _vp, _vp]),
     "ttt_status_str": (ctypes.c_char_p, [_i32]),

@@ -83,6 +83,46 @@ def ttt_linear_fwd(q, k, v, eta, w0, b: int, z=None, w_out=None, stream=None,
     return z, w_out
 
 
+def ttt_linear_ln_fwd(q, k, v, eta, w0, ln_gamma, ln_beta, eps: float, b: int, z=None,
+                      w_out=None, stream=None):
+    """TTT-Linear with the LayerNorm + residual inner model, f(x) = x + LN(W x)
+    (see include/ttt.h).
+
+    q, k, v: [B, H, T, d] bf16; eta: [B, H, T] fp32; w0: [H, d, d] or
+    [B, H, d, d] fp32; ln_gamma, ln_beta: [H, d] fp32; eps > 0.  Returns
+    (z, w_out), allocated when not given.
+    """
+    B, H, T, d = q.shape
+    if z is None:
+        z = torch.empty((B, H, T, d), dtype=torch.float32, device=q.device)
+    if w_out is None:
+        w_out = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+    dev = _check_tensors(dict(q=q, k=k, v=v, eta=eta, w0=w0, ln_gamma=ln_gamma, ln_beta=ln_beta,
+                              z=z, w_out=w_out))
+    for name, t in (("eta", eta), ("w0", w0), ("ln_gamma", ln_gamma), ("ln_beta", ln_beta),
+                    ("z", z), ("w_out", w_out)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if k.shape != q.shape or v.shape != q.shape or tuple(eta.shape) != (B, H, T):
+        raise ValueError("shape mismatch among q, k, v, eta")
+    per_batch = 1 if w0.dim() == 4 else 0
+    if tuple(w0.shape) != ((B, H, d, d) if per_batch else (H, d, d)):
+        raise ValueError(f"w0 has shape {tuple(w0.shape)}")
+    if tuple(ln_gamma.shape) != (H, d) or tuple(ln_beta.shape) != (H, d):
+        raise ValueError("ln_gamma / ln_beta must be [H, d]")
+    if tuple(z.shape) != (B, H, T, d) or tuple(w_out.shape) != (B, H, d, d):
+        raise ValueError("output shape mismatch")
+    L = _lib.lib()
+    with torch.cuda.device(dev):
+        _lib.check(L.ttt_linear_ln_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w0), per_batch,
+                                       _ptr(ln_gamma), _ptr(ln_beta), float(eps), B, H, T, d,
+                                       int(b), _dtype_code(q), _ptr(z), _ptr(w_out),
+                                       _stream(dev, stream)))
+    return z, w_out
+
+
 def ttt_mlp_fwd(q, k, v, eta, w1_0, w2_0, b: int, z=None, w1_out=None, w2_out=None, stream=None):
     """TTT-MLP forward scan, f(x) = W2 GELU(W1 x) (see include/ttt.h).
 

@@ -129,6 +129,44 @@ ttt_status_t linear_impl(const void* q, const void* k, const void* v, const floa
   return TTT_OK;
 }
 
+ttt_status_t linear_ln_impl(const void* q, const void* k, const void* v, const float* eta,
+                            const float* w0, int32_t w0_per_batch, const float* gamma,
+                            const float* beta, float eps, int32_t B, int32_t H, int32_t T,
+                            int32_t d, int32_t b, ttt_dtype_t dt, float* z, float* w_out,
+                            void* stream) {
+  static const char* fn = "ttt_linear_ln_fwd";
+  const int64_t units = (int64_t)B * H;
+  const int64_t es = dt == TTT_F32 ? 4 : 2;
+  const int64_t seq = units * T * d;
+  const Range in[] = {rng("q", q, seq * es), rng("k", k, seq * es), rng("v", v, seq * es),
+                      rng("eta", eta, units * T * 4),
+                      rng("w0", w0, (w0_per_batch ? units : (int64_t)H) * d * d * 4),
+                      rng("ln_gamma", gamma, (int64_t)H * d * 4),
+                      rng("ln_beta", beta, (int64_t)H * d * 4)};
+  const Range out[] = {rng("z", z, seq * 4), rng("w_out", w_out, units * d * d * 4)};
+  const int pairs[][2] = {{4, 1}};
+  ttt_status_t st = check_common(fn, dt, w0_per_batch, B, H, T, d, b, in, 7, out, 2, pairs, 1, T > 0);
+  if (st != TTT_OK) return st;
+  if (!(eps > 0.f) || eps > 3.0e38f)
+    return fail(TTT_ERR_VALUE, "%s: eps=%g must be finite and > 0", fn, (double)eps);
+  if (dt != TTT_BF16) return fail(TTT_ERR_UNSUPPORTED, "%s: only bf16 q/k/v are supported", fn);
+  if (b % 16 != 0)
+    return fail(TTT_ERR_UNSUPPORTED, "%s: mini-batch b=%d unsupported (need 16 | b)", fn, b);
+  if (units == 0) return TTT_OK;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (T == 0) {
+    if (w0_per_batch && w0 == w_out) return TTT_OK;
+    e = ttt::launch_copy_state(w0, w0_per_batch, (int)units, H, d * d, w_out, s);
+  } else {
+    ttt::LinearLnArgs a{{q, k, v, eta, w0, z, w_out, w0_per_batch, (int)units, H, T, b},
+                        gamma, beta, eps};
+    e = ttt::launch_linear_ln(a, s);
+  }
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return TTT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -148,6 +186,15 @@ ttt_status_t ttt_linear_fwd_tuned(const void* q, const void* k, const void* v, c
                                   int32_t rows_per_workgroup) {
   return linear_impl(q, k, v, eta, w0, w0_per_batch, B, H, T, d, b, qkv_dtype, z, w_out, stream,
                      rows_per_workgroup);
+}
+
+ttt_status_t ttt_linear_ln_fwd(const void* q, const void* k, const void* v, const float* eta,
+                               const float* w0, int32_t w0_per_batch, const float* ln_gamma,
+                               const float* ln_beta, float eps, int32_t B, int32_t H, int32_t T,
+                               int32_t d, int32_t b, ttt_dtype_t qkv_dtype, float* z,
+                               float* w_out, void* stream) {
+  return linear_ln_impl(q, k, v, eta, w0, w0_per_batch, ln_gamma, ln_beta, eps, B, H, T, d, b,
+                        qkv_dtype, z, w_out, stream);
 }
 
 ttt_status_t ttt_mlp_fwd(const void* q, const void* k, const void* v, const float* eta,
@@ -202,6 +249,7 @@ const char* ttt_status_str(ttt_status_t s) {
     case TTT_ERR_ALIAS: return "TTT_ERR_ALIAS: an output overlaps an input";
     case TTT_ERR_HIP: return "TTT_ERR_HIP: HIP runtime error";
     case TTT_ERR_ALIGN: return "TTT_ERR_ALIGN: pointer not 16-byte aligned";
+    case TTT_ERR_VALUE: return "TTT_ERR_VALUE: scalar argument out of range";
   }
   return "unknown ttt_status_t";
 }

@@ -21,6 +21,14 @@ struct LinearArgs {
   int b;
 };
 
+// TTT-Linear with the LayerNorm + residual inner model: gamma, beta [H][64].
+struct LinearLnArgs {
+  LinearArgs s;
+  const float* gamma;
+  const float* beta;
+  float eps;
+};
+
 struct MlpArgs {
   const void* q;
   const void* k;
@@ -41,6 +49,7 @@ struct MlpArgs {
 // rows: rows of W per workgroup (64, 32 or 16).
 hipError_t launch_linear(const LinearArgs& a, bool f32in, int rows, hipStream_t s);
 hipError_t launch_linear_bf16(const LinearArgs& a, int rows, hipStream_t s);
+hipError_t launch_linear_ln(const LinearLnArgs& a, hipStream_t s);
 hipError_t launch_mlp(const MlpArgs& a, bool f32in, hipStream_t s);
 hipError_t launch_copy_state(const float* src, int per_unit, int units, int H, int n,
                              float* dst, hipStream_t s);

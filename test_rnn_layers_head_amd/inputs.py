@@ -15,10 +15,18 @@ Recipe (per workload):
   * Q, K, V ~ N(0, 1/d) i.i.d. per element, except the drifting long-context
     workload where K and V follow x_1 = e_1, x_t = 0.9 x_{t-1} + sqrt(0.19) e_t
     with e ~ N(0, 1/d) independent per (batch, head, dim, tensor);
-  * eta_t = 0.1 * sigmoid(N(0, 1)) per (batch, head, token), or U(0, 0.1) for
-    the small fp32 workload;
-  * W0 ~ N(0, 0.02^2) per head ([H, d, d]); TTT-MLP: W1 [H, 4d, d] and
-    W2 [H, d, 4d] from the same distribution;
+  * eta_t = eta_scale * sigmoid(N(0, 1)) per (batch, head, token), or
+    U(0, 0.1) for the small fp32 workload; eta_scale = 0.1 except for the
+    LayerNorm workloads (0.02, see below);
+  * W0 ~ N(0, w_scale^2) per head ([H, d, d]), w_scale = 0.02 except for the
+    LayerNorm workloads; TTT-MLP: W1 [H, 4d, d] and W2 [H, d, 4d] from the
+    same distribution;
+  * LayerNorm + residual inner model (kind "linear_ln"): then
+    ln_gamma = 1 + 0.2 N(0, 1) and ln_beta = 0.1 N(0, 1) per (head, dim),
+    eps = 1e-5.  W0 uses w_scale = 1/sqrt(d) and eta_scale = 0.02: the
+    LayerNorm divides by the spread of W0 k, so the gradient scales like
+    1 / |W0| and the step is stable only for eta |k|^2 / var(W0 k) of order
+    one (with W0 ~ N(0, 0.02^2) it would be ~40 times larger);
   * the drawn float64 values are rounded once, round-to-nearest-even, to the
     storage dtype (bf16 for Q/K/V unless the workload says fp32; eta and the
     states are fp32).  Both sides consume exactly these rounded values.
@@ -34,7 +42,7 @@ import numpy as np
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str  # "linear" | "mlp"
+    kind: str  # "linear" | "linear_ln" | "mlp"
     B: int
     H: int
     T: int
@@ -45,6 +53,9 @@ class Workload:
     eta_dist: str = "sigmoid"  # "sigmoid" | "uniform"
     drift: bool = False
     seed: int = 0
+    eta_scale: float = 0.1
+    w_scale: float = 0.02
+    ln_eps: float = 1e-5
     b_sweep: tuple = field(default_factory=tuple)
 
     @property
@@ -64,6 +75,10 @@ WORKLOADS = {
                 b_sweep=(1, 4, 16, 64)),
     4: Workload("mlp-125M-T2048", "mlp", B=8, H=12, T=2048, hidden=256, seed=4),
     5: Workload("linear-longctx-T32768", "linear", B=1, H=32, T=32768, drift=True, seed=5),
+    6: Workload("linear-ln-1.3B-T8192", "linear_ln", B=4, H=32, T=8192, seed=6, eta_scale=0.02,
+                w_scale=0.125),
+    7: Workload("linear-ln-125M-T2048", "linear_ln", B=8, H=12, T=2048, seed=7, eta_scale=0.02,
+                w_scale=0.125),
 }
 
 
@@ -107,10 +122,13 @@ class Inputs:
     q_raw: np.ndarray | None = None
     k_raw: np.ndarray | None = None
     v_raw: np.ndarray | None = None
+    ln_gamma: np.ndarray | None = None  # [H, d] fp32 (kind "linear_ln")
+    ln_beta: np.ndarray | None = None
 
     def sha256(self) -> str:
         h = hashlib.sha256()
-        for a in (self.q_raw, self.k_raw, self.v_raw, self.eta, self.w0, self.w1, self.w2):
+        for a in (self.q_raw, self.k_raw, self.v_raw, self.eta, self.w0, self.w1, self.w2,
+                  self.ln_gamma, self.ln_beta):
             if a is not None:
                 h.update(np.ascontiguousarray(a).tobytes())
         return h.hexdigest()
@@ -131,7 +149,9 @@ class Inputs:
                       sel(self.eta), st(self.w0), st(self.w1), st(self.w2),
                       None if self.q_raw is None else sel(self.q_raw),
                       None if self.k_raw is None else sel(self.k_raw),
-                      None if self.v_raw is None else sel(self.v_raw))
+                      None if self.v_raw is None else sel(self.v_raw),
+                      None if self.ln_gamma is None else self.ln_gamma[heads],
+                      None if self.ln_beta is None else self.ln_beta[heads])
 
 
 def _ar1(rng: np.random.Generator, shape, rho: float = 0.9) -> np.ndarray:
@@ -162,15 +182,20 @@ def make_inputs(wl: Workload | int, seed: int | None = None) -> Inputs:
     if wl.eta_dist == "uniform":
         eta = rng.uniform(0.0, 0.1, size=(wl.B, wl.H, wl.T))
     else:
-        eta = 0.1 / (1.0 + np.exp(-rng.standard_normal((wl.B, wl.H, wl.T))))
+        eta = wl.eta_scale / (1.0 + np.exp(-rng.standard_normal((wl.B, wl.H, wl.T))))
     eta = eta.astype(np.float32)
-    w0 = w1 = w2 = None
-    if wl.kind == "linear":
-        w0 = (rng.standard_normal((wl.H, wl.d, wl.d)) * 0.02).astype(np.float32)
-    else:
+    w0 = w1 = w2 = gamma = beta = None
+    if wl.kind in ("linear", "linear_ln"):
+        w0 = (rng.standard_normal((wl.H, wl.d, wl.d)) * wl.w_scale).astype(np.float32)
+    elif wl.kind == "mlp":
         hd = wl.hidden or 4 * wl.d
-        w1 = (rng.standard_normal((wl.H, hd, wl.d)) * 0.02).astype(np.float32)
-        w2 = (rng.standard_normal((wl.H, wl.d, hd)) * 0.02).astype(np.float32)
+        w1 = (rng.standard_normal((wl.H, hd, wl.d)) * wl.w_scale).astype(np.float32)
+        w2 = (rng.standard_normal((wl.H, wl.d, hd)) * wl.w_scale).astype(np.float32)
+    else:
+        raise ValueError(wl.kind)
+    if wl.kind == "linear_ln":
+        gamma = (1.0 + 0.2 * rng.standard_normal((wl.H, wl.d))).astype(np.float32)
+        beta = (0.1 * rng.standard_normal((wl.H, wl.d))).astype(np.float32)
     if wl.qkv_dtype == "bf16":
         raws = [bf16_bits(a) for a in (q, k, v)]
         vals = [bf16_to_f32(r) for r in raws]
@@ -179,4 +204,4 @@ def make_inputs(wl: Workload | int, seed: int | None = None) -> Inputs:
         raws = vals
     else:
         raise ValueError(wl.qkv_dtype)
-    return Inputs(wl, *vals, eta, w0, w1, w2, *raws)
+    return Inputs(wl, *vals, eta, w0, w1, w2, *raws, gamma, beta)

@@ -68,3 +68,23 @@ def run_mlp(x, b):
 
 def oracle_mlp(x, b):
     return oracle.mlp(x.q, x.k, x.v, x.eta, x.w1, x.w2, b)
+
+
+def run_linear_ln(x, b, gamma=None, beta=None, eps=None, w0=None):
+    from test_rnn_layers_head_amd import ttt_linear_ln_fwd
+    gamma = x.ln_gamma if gamma is None else gamma
+    beta = x.ln_beta if beta is None else beta
+    eps = x.wl.ln_eps if eps is None else eps
+    w0 = x.w0 if w0 is None else w0
+    z, w = ttt_linear_ln_fwd(dev(x, "q"), dev(x, "k"), dev(x, "v"), f32(x.eta), f32(w0),
+                             f32(gamma), f32(beta), eps, b)
+    torch.cuda.synchronize()
+    return z.cpu().numpy(), w.cpu().numpy()
+
+
+def oracle_linear_ln(x, b, gamma=None, beta=None, eps=None, w0=None):
+    gamma = x.ln_gamma if gamma is None else gamma
+    beta = x.ln_beta if beta is None else beta
+    eps = x.wl.ln_eps if eps is None else eps
+    w0 = x.w0 if w0 is None else w0
+    return oracle.linear_ln(x.q, x.k, x.v, x.eta, w0, gamma, beta, eps, b)

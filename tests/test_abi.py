@@ -1,0 +1,140 @@
+"""The C ABI of libttt.so, host side only (no GPU needed): the library loads,
+exports every function that include/*.h declares with the signature the
+binding uses, and rejects bad arguments before anything reaches the GPU.
+
+Every call below returns from argument validation (or from the empty-work
+shortcut) before the first HIP runtime call; the pointers passed are never
+dereferenced.
+"""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from test_rnn_layers_head_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DECL = re.compile(r"^\s*(?:const\s+)?[A-Za-z_]\w*\s*\*?\s*(ttt_\w+)\s*\(", re.M)
+
+
+def declared():
+    names = {}
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        for m in DECL.finditer(open(h).read()):
+            names[m.group(1)] = os.path.basename(h)
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from test_rnn_layers_head_amd import build
+        build.build()
+    return _lib.lib()
+
+
+def header_value(name):
+    text = open(os.path.join(ROOT, "include", "ttt.h")).read()
+    return int(re.search(rf"#define {name} (\d+)", text).group(1))
+
+
+def test_headers_declare_the_entry_points():
+    names = declared()
+    for fn in ("ttt_linear_fwd", "ttt_linear_ln_fwd", "ttt_mlp_fwd", "ttt_linear_fwd_tuned",
+               "ttt_bench_copy", "ttt_status_str", "ttt_last_error", "ttt_abi_version"):
+        assert fn in names, fn
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    raw = ctypes.CDLL(_lib.LIB_PATH)
+    for name, header in declared().items():
+        assert hasattr(raw, name), f"{name} ({header}) is not exported"
+        assert name in _lib.SIGNATURES, f"{name} ({header}) has no ctypes signature"
+    assert set(_lib.SIGNATURES) <= set(declared())
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ttt_abi_version() == header_value("TTT_ABI_VERSION")
+    for code, name in _lib.STATUS.items():
+        assert lib.ttt_status_str(code).decode().startswith(name)
+    assert b"unknown" in lib.ttt_status_str(99)
+
+
+# fake device addresses: 16-byte aligned, disjoint, never dereferenced
+A = [0x10000000 * (i + 1) for i in range(12)]
+P, M = 0x20000, 0x30000  # unaligned / overlapping variants
+
+
+def linear(lib, **kw):
+    args = dict(q=A[0], k=A[1], v=A[2], eta=A[3], w0=A[4], per_batch=0, B=1, H=1, T=16, d=64,
+                b=16, dt=_lib.TTT_BF16, z=A[5], w=A[6])
+    args.update(kw)
+    return lib.ttt_linear_fwd(args["q"], args["k"], args["v"], args["eta"], args["w0"],
+                              args["per_batch"], args["B"], args["H"], args["T"], args["d"],
+                              args["b"], args["dt"], args["z"], args["w"], None)
+
+
+def linear_ln(lib, **kw):
+    args = dict(q=A[0], k=A[1], v=A[2], eta=A[3], w0=A[4], per_batch=0, gamma=A[7], beta=A[8],
+                eps=1e-5, B=1, H=1, T=16, d=64, b=16, dt=_lib.TTT_BF16, z=A[5], w=A[6])
+    args.update(kw)
+    return lib.ttt_linear_ln_fwd(args["q"], args["k"], args["v"], args["eta"], args["w0"],
+                                 args["per_batch"], args["gamma"], args["beta"], args["eps"],
+                                 args["B"], args["H"], args["T"], args["d"], args["b"],
+                                 args["dt"], args["z"], args["w"], None)
+
+
+def status(code):
+    return {v: k for k, v in _lib.STATUS.items()}[code]
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(d=32), "TTT_ERR_UNSUPPORTED"),
+    (dict(b=24), "TTT_ERR_UNSUPPORTED"),
+    (dict(b=0), "TTT_ERR_UNSUPPORTED"),
+    (dict(B=-1), "TTT_ERR_SHAPE"),
+    (dict(per_batch=2), "TTT_ERR_SHAPE"),
+    (dict(dt=7), "TTT_ERR_DTYPE"),
+    (dict(q=None), "TTT_ERR_NULL"),
+    (dict(eta=A[3] + 4), "TTT_ERR_ALIGN"),
+    (dict(z=A[1]), "TTT_ERR_ALIAS"),
+    (dict(w=A[4]), "TTT_ERR_ALIAS"),            # in place needs w0_per_batch = 1
+    (dict(B=1 << 20, H=1 << 10, T=1 << 10), "TTT_ERR_SHAPE"),
+    (dict(B=0), "TTT_OK"),                      # empty work: nothing launched
+    (dict(H=0), "TTT_OK"),
+])
+def test_linear_argument_checks(lib, kw, expect):
+    assert linear(lib, **kw) == status(expect), lib.ttt_last_error()
+    if expect != "TTT_OK":
+        assert lib.ttt_last_error().startswith(b"ttt_linear_fwd:")
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(eps=0.0), "TTT_ERR_VALUE"),
+    (dict(eps=-1.0), "TTT_ERR_VALUE"),
+    (dict(eps=float("nan")), "TTT_ERR_VALUE"),
+    (dict(eps=float("inf")), "TTT_ERR_VALUE"),
+    (dict(b=8), "TTT_ERR_UNSUPPORTED"),
+    (dict(b=4), "TTT_ERR_UNSUPPORTED"),
+    (dict(dt=_lib.TTT_F32), "TTT_ERR_UNSUPPORTED"),
+    (dict(gamma=None), "TTT_ERR_NULL"),
+    (dict(beta=A[8] + 8), "TTT_ERR_ALIGN"),
+    (dict(z=A[7]), "TTT_ERR_ALIAS"),
+    (dict(B=0), "TTT_OK"),
+])
+def test_linear_ln_argument_checks(lib, kw, expect):
+    assert linear_ln(lib, **kw) == status(expect), lib.ttt_last_error()
+    if expect != "TTT_OK":
+        assert lib.ttt_last_error().startswith(b"ttt_linear_ln_fwd:")
+
+
+def test_mlp_argument_checks(lib):
+    f = lambda **kw: lib.ttt_mlp_fwd(A[0], A[1], A[2], A[3], A[4], A[9], 0, 1, 1, 16, 64,
+                                     kw.get("hidden", 256), kw.get("b", 16),
+                                     kw.get("dt", _lib.TTT_BF16), A[5], A[6], A[10], None)
+    assert f(hidden=128) == status("TTT_ERR_UNSUPPORTED")
+    assert f(b=32) == status("TTT_ERR_UNSUPPORTED")
+    assert f(dt=_lib.TTT_F32) == status("TTT_ERR_UNSUPPORTED")
+    assert f(hidden=-1) == status("TTT_ERR_SHAPE")
