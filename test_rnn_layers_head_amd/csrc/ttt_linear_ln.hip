@@ -51,6 +51,8 @@
 // factors of the lookahead correction Gn (K^T K).  The outputs W Q and
 // Gn triu(K^T Q) use two (~2^-16).  The variance
 // uses the one-pass form E[y^2] - mu^2 (clamped at 0).
+#include <type_traits>
+
 #include "ttt_device.h"
 #include "ttt_launch.h"
 #include "ttt_linear_ops.h"
@@ -65,19 +67,28 @@ struct LnGeom {
   static constexpr int RAW = 2 * KB + VB + 64;  // + eta (16 fp32)
   static constexpr int NI = 4 + 2 + 1;          // DMA ops per tile
   static constexpr int D = 9;                   // loader lookahead (D - 1 tiles in flight)
-  static constexpr int NST = D + 3;
-  static constexpr int P_E2 = 0;                // 2 eta_t, 16 fp32
-  static constexpr int P_A = 64;                // triu(K^T Q), hi | lo
+  static constexpr int NST = D + 3;             // raw ring slots
+  static constexpr int P_NE = 0;                // -eta_t, 16 fp32
+  static constexpr int P_SGU = 64;              // sums of gamma (k + beta - v) over rows 0..31,
+  static constexpr int P_SGU2 = 128;            //   and over rows 32..63, 16 fp32 each
+  static constexpr int P_A = 192;               // triu(K^T Q), hi | lo
   static constexpr int P_MKK = P_A + 1024;      // K_{j-1}^T K_j, hi | mid
   static constexpr int P_MKL = P_MKK + 1024;    // K_{j-1}^T K_j, lo (8 bytes per lane)
   static constexpr int P_KT = P_MKL + 512;      // update operand, x4
-  static constexpr int PREP = P_KT + 4096;
-  static constexpr int NPREP = 3;
+  static constexpr int P_GU = P_KT + 4096;      // 2 gamma (k + beta - v), layout T, x4 waves
+  static constexpr int P_QB = P_GU + 4096;      // q + beta, layout T, x4 waves
+  static constexpr int PREP = P_QB + 4096;
+  static constexpr int NPREP = 4;
   static constexpr int XST = 8 * 16 * 4;        // floats: [stat 8][token 16][wave 4]
   static constexpr int LDS = NST * RAW + NPREP * PREP + 2 * XST * 4;
-  static constexpr int THREADS = (NCW + 3) * 64;
+  // waves 0..3 compute, 4 and 5 helpers, 6 loader, 7 helper: wave i shares
+  // a SIMD with wave i + 4, so every SIMD holds one compute wave and one
+  // wave of preparation work
+  static constexpr int W_H0 = 4, W_H1 = 5, W_LOAD = 6, W_H2 = 7;
+  static constexpr int THREADS = 8 * 64;
 };
 static_assert(63 / LnGeom::NI >= LnGeom::D, "DMA lookahead exceeds the vmcnt range");
+static_assert(LnGeom::NPREP == 4, "prepared slots are indexed with a mask");
 
 __device__ __forceinline__ float bits_f(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t f_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
@@ -154,6 +165,9 @@ __device__ __forceinline__ f32x4 bf4(uint2 u) {
                bits_f(u.y & 0xffff0000u)};
 }
 
+// TPM: tiles per mini-batch when fixed at compile time (b = 16, 32, 64),
+// 0 = read from the arguments (other multiples of 16).
+template <int TPM>
 __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearLnArgs la) {
   using G = LnGeom;
   const LinearArgs& a = la.s;
@@ -176,7 +190,7 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
   // iteration between B_t and B_{t+1}), so after B_{j-1} the loader reuses
   // the slot of tile j-2 for tile j+D+1: NST = D + 3 slots, D - 1 tiles in
   // flight at each barrier.
-  if (wave == G::NCW + 2) {
+  if (wave == G::W_LOAD) {
     const uint32_t ubytes = (uint32_t)T * 128;
     const size_t uoff = (size_t)unit * T * 64;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc((const short*)a.k + uoff, ubytes);
@@ -218,10 +232,24 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
 
   // ================================================================ helper
   // Iteration j (between B_j and B_{j+1}, j = -2 .. ntiles-2) prepares tile
-  // j+2 into prepared slot (j+2) % 3; compute iteration j reads slots j % 3
-  // and (j+1) % 3 in the same interval.
-  if (wave >= G::NCW) {
-    const bool h0 = wave == G::NCW;
+  // j+2 into prepared slot (j+2) % 4; compute iteration j reads the slots of
+  // tiles j and j+1 in the same interval.  Helper 0 forms the products of
+  // the plain scan (triu(K^T Q), K_{j-1}^T K_j, -eta, the update operand);
+  // helpers 1 and 2 the LayerNorm terms that do not depend on W, in layout T
+  // for compute waves 0, 1 and 2, 3 (lane (c, g), wave block w: rows
+  // 16w + 4g .. +3 of token c): 2 gamma (k + beta - v), its sums over their
+  // 32 rows per token, and q + beta.
+  if (wave != G::W_LOAD && wave >= G::NCW) {
+    const int role = wave == G::W_H0 ? 0 : wave == G::W_H1 ? 1 : 2;
+    const float* gm = la.gamma + (size_t)head * 64;
+    const float* bt = la.beta + (size_t)head * 64;
+    const int wb = role == 2 ? 2 : 0;  // first compute-wave block of helpers 1, 2
+    f32x4 hg[2], hb[2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      hg[w] = *(const f32x4*)(gm + 16 * (wb + w) + 4 * g);
+      hb[w] = *(const f32x4*)(bt + 16 * (wb + w) + 4 * g);
+    }
     bf16x8 kprev[2], sel[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -238,22 +266,25 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
       }
       const char* st = raw + (tn % G::NST) * G::RAW;
       const char* Kt = st;
-      const char* Qt = st + G::KB;
-      const float* Et = (const float*)(st + 2 * G::KB + G::VB);
       char* pp = prep + (tn % G::NPREP) * G::PREP;
-      bf16x8 kop[2], qop[2];
+      if (role == 0) {
+        const char* Qt = st + G::KB;
+        const float* Et = (const float*)(st + 2 * G::KB + G::VB);
+        bf16x8 kop[2], qop[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        kop[h] = row_chunk(Kt, c, h, g);
-        qop[h] = row_chunk(Qt, c, h, g);
-      }
-      if (h0) {
-        f32x4 A = {0, 0, 0, 0}, Mkk = {0, 0, 0, 0};
+        for (int h = 0; h < 2; ++h) {
+          kop[h] = row_chunk(Kt, c, h, g);
+          qop[h] = row_chunk(Qt, c, h, g);
+        }
+        f32x4 A = {0, 0, 0, 0}, Mkk = {0, 0, 0, 0}, KS[4];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           A = mfma_k32(kop[h], qop[h], A);        // A[s = 4g+r][t = c] = k_s . q_t
           Mkk = mfma_k32(kprev[h], kop[h], Mkk);  // k^{prev}_s . k_t
         }
+        // update operand kt[m][e] = K[t = 4g+e][sigma(m, c)] (exact selection)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) KS[m] = mfma_k32(kop[m >> 1], sel[m & 1], f32x4{0, 0, 0, 0});
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (4 * g + r > c) A[r] = 0.f;
@@ -262,20 +293,35 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
         const uint2 mh = s4u(m3.hi), mm = s4u(m3.mid);
         *(uint4*)(pp + G::P_MKK + lane * 16) = make_uint4(mh.x, mh.y, mm.x, mm.y);
         *(uint2*)(pp + G::P_MKL + lane * 8) = s4u(m3.lo);
-        if (lane < 16) ((float*)(pp + G::P_E2))[lane] = 2.f * Et[lane];
-      } else {
-        // update operand kt[m][e] = K[t = 4g+e][sigma(m, c)] (exact selection)
-        f32x4 KS[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) KS[m] = mfma_k32(kop[m >> 1], sel[m & 1], f32x4{0, 0, 0, 0});
+        if (lane < 16) ((float*)(pp + G::P_NE))[lane] = -Et[lane];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const uint32_t p0 = pack_rne(KS[m][0], KS[m][1]), p1 = pack_rne(KS[m][2], KS[m][3]);
           *(uint4*)(pp + G::P_KT + m * 1024 + lane * 16) = make_uint4(p0, p1, p0, p1);
         }
+        kprev[0] = kop[0];
+        kprev[1] = kop[1];
+      } else {
+        float su = 0.f;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const int rb = 16 * (wb + w) + 4 * g;
+          const f32x4 kf = bf4(*(const uint2*)(Kt + swz(c, rb)));
+          const f32x4 vf = bf4(*(const uint2*)(st + 2 * G::KB + c * 128 + rb * 2));
+          f32x4 gu;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            gu[r] = hg[w][r] * ((kf[r] + hb[w][r]) - vf[r]);
+            su += gu[r];
+          }
+          *(f32x4*)(pp + G::P_GU + (wb + w) * 1024 + lane * 16) = gu + gu;
+          const f32x4 qf = bf4(*(const uint2*)(st + G::KB + swz(c, rb)));
+          *(f32x4*)(pp + G::P_QB + (wb + w) * 1024 + lane * 16) = qf + hb[w];
+        }
+        const float t = fold32(su, su);
+        su = fold16(t, t);
+        if (lane < 16) ((float*)(pp + (role == 1 ? G::P_SGU : G::P_SGU2)))[lane] = su;
       }
-      kprev[0] = kop[0];
-      kprev[1] = kop[1];
       wait_lgkm0();
       wg_barrier_pinned();  // B_{j+1}
     }
@@ -291,11 +337,9 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
 #pragma unroll
   for (int m = 0; m < 4; ++m)
     W[m] = *(const f32x4*)(w0 + (rbase + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1));
-  // LayerNorm parameters of this lane's rows (layout T: rows rbase + 4g + r)
+  // LayerNorm scale of this lane's rows (layout T: rows rbase + 4g + r)
   const float* gm = la.gamma + (size_t)head * 64;
-  const float* bt = la.beta + (size_t)head * 64;
   const f32x4 gam = *(const f32x4*)(gm + rbase + 4 * g);
-  const f32x4 bet = *(const f32x4*)(bt + rbase + 4 * g);
   f32x4 gsq, tg;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -305,7 +349,7 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
   float G2 = 0.f;  // sum over all 64 rows of gamma^2
   for (int i = 0; i < 64; ++i) G2 = fmaf(gm[i], gm[i], G2);
   const float eps = la.eps;
-  const int tpm = a.b >> 4;  // tiles per mini-batch
+  const int tpm = TPM > 0 ? TPM : (a.b >> 4);  // tiles per mini-batch
 
   const NegSel ns = make_negsel(c, g);
   // one-hot selections that carry the hi (slots 0..3) or lo (4..7) half of a
@@ -316,49 +360,41 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
     selH[e] = (bf16)((e < 4 && 4 * g + e == c) ? 1.f : 0.f);
     selL[e] = (bf16)((e >= 4 && 4 * g + e - 4 == c) ? 1.f : 0.f);
   }
-  // this lane's 4 rows of token c inside a raw tile
-  const int koffT = swz(c, rbase + 4 * g);
-  const int voffT = 2 * G::KB + c * 128 + (rbase + 4 * g) * 2;
   // statistic slots: after the in-wave fold, row g of u0 holds statistic
   // s0[g], of u1 statistic s0[g] + 4
   const int s0g = (g == 0) ? 0 : (g == 1) ? 2 : (g == 2) ? 1 : 3;
+  const int lane16 = lane * 16, wblk = wave * 1024;
+  // per-lane byte offsets inside the exchange buffers and the raw tiles
+  const int xw0 = ((s0g * 16 + c) * 4 + wave) * 4, xw1 = xw0 + 4 * 16 * 4 * 4;
+  const int xr0 = (s0g * 16 + c) * 16, xr1 = xr0 + 4 * 16 * 4 * 4;
+  const int kc0 = c * 128 + (((0 + g) ^ (c & 7)) << 4), kc1 = c * 128 + (((4 + g) ^ (c & 7)) << 4);
 
-  // gamma * (k + beta - v) on this lane's rows of token c
-  auto gamma_u = [&](uint2 kT, uint2 vT) {
-    const f32x4 kf = bf4(kT), vf = bf4(vT);
-    f32x4 r;
+  // Partial sums over this wave's rows of the per-token statistics
+  //   0 sum y, 1 sum y^2, 2 sum gamma^2 y, 3 sum gamma^2 y^2, 4 sum 2 gu y,
+  //   6 sum o, 7 sum o^2   (y = W0 k, gu = gamma (k + beta - v), o = pre-LN
+  // output; slot 5 is unused), folded over the 4 lane rows and written to
+  // exchange buffer xs.
+  auto publish = [&](char* xs, const f32x4& Y, const f32x4& GU2, const f32x4& O) {
+    float p[8];
+    f32x4 gy2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = gam[i] * ((kf[i] + bet[i]) - vf[i]);
-    return r;
-  };
-  // Partial sums over this wave's rows of the 8 per-token statistics
-  //   0 sum y, 1 sum y^2, 2 sum gamma^2 y, 3 sum gamma^2 y^2, 4 sum gu y,
-  //   5 sum gu, 6 sum o, 7 sum o^2   (y = W0 k, gu = gamma u, o = pre-LN output)
-  // folded over the 4 lane rows and written to exchange buffer xs.
-  auto publish = [&](float* xs, const f32x4& Y, const f32x4& GU, const f32x4& O) {
-    float p[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float y = Y[r], gy2 = gsq[r] * y;
-      p[0] += y;
-      p[1] = fmaf(y, y, p[1]);
-      p[2] += gy2;
-      p[3] = fmaf(gy2, y, p[3]);
-      p[4] = fmaf(GU[r], y, p[4]);
-      p[5] += GU[r];
-      p[6] += O[r];
-      p[7] = fmaf(O[r], O[r], p[7]);
-    }
+    for (int r = 0; r < 4; ++r) gy2[r] = gsq[r] * Y[r];
+    p[0] = (Y[0] + Y[1]) + (Y[2] + Y[3]);
+    p[1] = fmaf(Y[3], Y[3], fmaf(Y[2], Y[2], fmaf(Y[1], Y[1], Y[0] * Y[0])));
+    p[2] = (gy2[0] + gy2[1]) + (gy2[2] + gy2[3]);
+    p[3] = fmaf(gy2[3], Y[3], fmaf(gy2[2], Y[2], fmaf(gy2[1], Y[1], gy2[0] * Y[0])));
+    p[4] = fmaf(GU2[3], Y[3], fmaf(GU2[2], Y[2], fmaf(GU2[1], Y[1], GU2[0] * Y[0])));
+    p[5] = 0.f;
+    p[6] = (O[0] + O[1]) + (O[2] + O[3]);
+    p[7] = fmaf(O[3], O[3], fmaf(O[2], O[2], fmaf(O[1], O[1], O[0] * O[0])));
     const float t0 = fold32(p[0], p[1]), t1 = fold32(p[2], p[3]);
     const float t2 = fold32(p[4], p[5]), t3 = fold32(p[6], p[7]);
-    const float u0 = fold16(t0, t1), u1 = fold16(t2, t3);
-    xs[(s0g * 16 + c) * 4 + wave] = u0;
-    xs[((s0g + 4) * 16 + c) * 4 + wave] = u1;
+    *(float*)(xs + xw0) = fold16(t0, t1);
+    *(float*)(xs + xw1) = fold16(t2, t3);
   };
-  // Totals of the 8 statistics for token c, in every lane.
-  auto gather = [&](const float* xs, float S[8]) {
-    const f32x4 v0 = *(const f32x4*)(xs + (s0g * 16 + c) * 4);
-    const f32x4 v1 = *(const f32x4*)(xs + ((s0g + 4) * 16 + c) * 4);
+  // Totals of the 8 statistics for token c, in every lane, from the partial
+  // sums of the four waves.
+  auto gather = [&](const f32x4& v0, const f32x4& v1, float S[8]) {
     const float a0 = (v0[0] + v0[1]) + (v0[2] + v0[3]);
     const float a1 = (v1[0] + v1[1]) + (v1[2] + v1[3]);
     float lo, hi;
@@ -382,14 +418,17 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
     const float ro = rsqrtf(vo + eps);
     f32x4 Z;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Z[r] = fmaf((O[r] - mo) * ro, gam[r], QB[r]);
+    for (int r = 0; r < 4; ++r) {
+      const float rg = ro * gam[r];
+      Z[r] = fmaf(O[r], rg, fmaf(-mo, rg, QB[r]));
+    }
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Z), rz,
                                            zlane + (uint32_t)t * (16 * 64 * 4), 0, 2);
   };
 
   wg_barrier_pinned();  // B_{-2}: raw tiles 0 and 1 are in LDS
   Split8x3 wg[2];       // split of the gradient point (b > 16)
-  f32x4 Y, GU;          // W0 K and gamma U of the current tile (layout T)
+  f32x4 Y;              // W0 K of the current tile (layout T)
   {
     const Split8x3 ws[2] = {split8x3(W[0], W[1], ns), split8x3(W[2], W[3], ns)};
     wg[0] = ws[0];
@@ -402,69 +441,92 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
       Y = mfma_k32(ws[h].mid, k, Y);
       Y = mfma_k32(ws[h].lo, k, Y);
     }
-    GU = gamma_u(*(const uint2*)(raw + koffT), *(const uint2*)(raw + voffT));
-    publish(xst, Y, GU, f32x4{0, 0, 0, 0});
   }
+  wg_barrier_pinned();  // B_{-1}: prepared tile 0 is in LDS
+  f32x4 GU2 = *(const f32x4*)(prep + G::P_GU + wblk + lane16);  // 2 gamma U, tile 0
+  publish((char*)xst, Y, GU2, f32x4{0, 0, 0, 0});
   wait_lgkm0();
-  wg_barrier_pinned();  // B_{-1}
   wg_barrier_pinned();  // B_0: statistics of tile 0 and prepared tiles 0, 1 ready
   f32x4 O = {0, 0, 0, 0}, QB = {0, 0, 0, 0};  // pre-LN outputs of the previous tile, q + beta
 
-  int sj = 0, sj1 = 1;      // prepared slots j % 3, (j+1) % 3
-  int rj = 0, rj1 = 1;      // raw slots j % NST, (j+1) % NST
-  for (int j = 0; j < ntiles; ++j) {
-    const char* pj = prep + sj * G::PREP;
-    const char* pj1 = prep + sj1 * G::PREP;
-    const char* tj = raw + rj * G::RAW;
-    const char* tj1 = raw + rj1 * G::RAW;
-    float* xs = xst + (j & 1) * G::XST;
-    float* xsn = xst + ((j + 1) & 1) * G::XST;
+  // One tile.  POS = the tile's position in its mini-batch when fixed at
+  // compile time (std::integral_constant), -1 otherwise.
+  auto tile = [&](const int j, auto POS) {
+    constexpr int pos = decltype(POS)::value;
+    const bool new_mb = TPM == 1 || (pos >= 0 ? pos == 0 : (j % tpm) == 0);
+    const bool next_new = TPM == 1 || (pos >= 0 ? (pos + 1) % (TPM > 0 ? TPM : 1) == 0
+                                                : ((j + 1) % tpm) == 0);
+    const char* pj = prep + (j & (G::NPREP - 1)) * G::PREP;
+    const char* pj1 = prep + ((j + 1) & (G::NPREP - 1)) * G::PREP;
+    const char* tj = raw + (j % G::NST) * G::RAW;
+    const char* tj1 = raw + ((j + 1) % G::NST) * G::RAW;
+    const char* xs = (const char*)xst + (j & 1) * (G::XST * 4);
+    char* xsn = (char*)xst + ((j + 1) & 1) * (G::XST * 4);
 
-    // statistics of tile j and of the outputs of tile j-1
-    float S[8];
-    gather(xs, S);
-    const float e2 = ((const float*)(pj + G::P_E2))[c];
+    // The body is cut into phases that the compiler may not interleave
+    // (sched_barrier): left to itself it spreads the off-chain products
+    // through the serial chain, which in-order issue then waits behind.
+    //   1. LDS reads, the split of W_j and its products (off the chain);
+    //   2. statistics -> gradient; 3. transposition MFMAs;
+    //   4. outputs of tile j-1, the correction of Y_{j+1}, W_j Q_j's
+    //      correction, the update; then the statistics of tile j+1.
+    // ---- reads: the statistics first (they start the serial chain)
+    const f32x4 v0 = *(const f32x4*)(xs + xr0), v1 = *(const f32x4*)(xs + xr1);
+    const float ne = ((const float*)(pj + G::P_NE))[c];  // -eta_t
+    const float sgu = ((const float*)(pj + G::P_SGU))[c] + ((const float*)(pj + G::P_SGU2))[c];
+    const bf16x8 k1a = *(const bf16x8*)(tj1 + kc0), k1b = *(const bf16x8*)(tj1 + kc1);
+    const bf16x8 q0a = *(const bf16x8*)(tj + G::KB + kc0), q0b = *(const bf16x8*)(tj + G::KB + kc1);
+    const uint4 mkk1 = *(const uint4*)(pj1 + G::P_MKK + lane16);  // [hi | mid]
+    const uint2 mkl1 = *(const uint2*)(pj1 + G::P_MKL + lane * 8);  // lo
     const bf16x8 att = get8(pj + G::P_A, lane);
     bf16x8 kt[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) kt[m] = get8(pj + G::P_KT + m * 1024, lane);
-    const uint4 mkk1 = *(const uint4*)(pj1 + G::P_MKK + lane * 16);  // [hi | mid]
-    const uint2 mkl1 = *(const uint2*)(pj1 + G::P_MKL + lane * 8);   // lo
-    bf16x8 k1[2], q0[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      k1[h] = row_chunk(tj1, c, h, g);
-      q0[h] = row_chunk(tj + G::KB, c, h, g);
-    }
-    const uint2 k1T = *(const uint2*)(tj1 + koffT);
-    const uint2 v1T = *(const uint2*)(tj1 + voffT);
-    const uint2 q0T = *(const uint2*)(tj + G::KB + koffT);
+    const f32x4 qb = *(const f32x4*)(pj + G::P_QB + wblk + lane16);
+    const f32x4 gu2n = *(const f32x4*)(pj1 + G::P_GU + wblk + lane16);
+    const bf16x8 k1[2] = {k1a, k1b}, q0[2] = {q0a, q0b};
 
-    // split of W_j (independent of the statistics)
+    // ---- products with W_j that do not wait for the gradient: its split,
+    // W_j K_{j+1} (or the gradient point's), W_j Q_j
     const Split8x3 ws[2] = {split8x3(W[0], W[1], ns), split8x3(W[2], W[3], ns)};
-    const bool new_mb = (j % tpm) == 0, next_new = ((j + 1) % tpm) == 0;
-    if (new_mb) {
+    if (TPM != 1 && new_mb) {
       wg[0] = ws[0];
       wg[1] = ws[1];
     }
+    f32x4 Yn = {0, 0, 0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const Split8x3& wy = next_new ? ws[h] : wg[h];
+      Yn = mfma_k32(wy.hi, k1[h], Yn);
+      Yn = mfma_k32(wy.mid, k1[h], Yn);
+      Yn = mfma_k32(wy.lo, k1[h], Yn);
+    }
+    f32x4 R = {0, 0, 0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      R = mfma_k32(ws[h].hi, q0[h], R);
+      R = mfma_k32(ws[h].mid, q0[h], R);
+    }
 
-    // ---- gradient of tile j (layout T), token c
+    // ---- gradient of tile j (layout T), token c:
+    //   Gn_r = -eta [rs (2 gu_r - m1) + rs^2 (2 gamma_r^2 - m2)(y_r - mu)]
+    __builtin_amdgcn_sched_barrier(0);
+    float S[8];
+    gather(v0, v1, S);
     const float mu = S[0] * (1.f / 64);
     const float var = fmaxf(fmaf(S[1], 1.f / 64, -mu * mu), 0.f);
     const float rs = rsqrtf(var + eps);
-    const float m1 = (2.f / 64) * fmaf(rs, fmaf(-mu, G2, S[2]), S[5]);
+    const float m1 = (2.f / 64) * fmaf(rs, fmaf(-mu, G2, S[2]), sgu);
     const float c3 = fmaf(mu, fmaf(mu, G2, -2.f * S[2]), S[3]);  // sum gamma^2 (y - mu)^2
-    const float m2 = (2.f / 64) * rs * fmaf(rs, c3, fmaf(-mu, S[5], S[4]));
-    const float a0 = -0.5f * e2 * rs;  // -eta rs
-    const float a1 = a0 * rs;
+    const float m2 = (2.f / 64) * rs * fmaf(rs, c3, fmaf(-mu, sgu, 0.5f * S[4]));  // S4 = sum 2 gu y
+    const float a0 = ne * rs, a1 = a0 * rs;
+    const float na0m1 = -a0 * m1, nm2a1 = -m2 * a1;
     f32x4 GnT;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      GnT[r] = fmaf(a1 * (tg[r] - m2), Y[r] - mu, a0 * fmaf(2.f, GU[r], -m1));
+      GnT[r] = fmaf(fmaf(tg[r], a1, nm2a1), Y[r] - mu, fmaf(a0, GU2[r], na0m1));
 
-    // ---- outputs of tile j-1
-    if (j > 0) store_z(j - 1, S, O, QB);
-
+    __builtin_amdgcn_sched_barrier(0);
     // ---- gradient to layout A: its three bf16 terms moved exactly
     const Split4x3 gT = split4x3(GnT);
     const bf16x8 gat = cat44(gT.hi, gT.mid);
@@ -472,28 +534,22 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
     const f32x4 CH = mfma_k32(gat, selH, f32x4{0, 0, 0, 0});
     const f32x4 CM = mfma_k32(gat, selL, f32x4{0, 0, 0, 0});
     const f32x4 CL = mfma_k32(gal, selH, f32x4{0, 0, 0, 0});
+
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- outputs of tile j-1 (off the chain, while the MFMAs run)
+    if (j > 0) store_z(j - 1, S, O, QB);
+
     Split4 gs;  // hi, mid: the operands of the products with K^T K and K^T Q
     gs.hi = u2s(make_uint2(pack_rne(CH[0], CH[1]), pack_rne(CH[2], CH[3])));
     gs.lo = u2s(make_uint2(pack_rne(CM[0], CM[1]), pack_rne(CM[2], CM[3])));
     const s16x4 glo = u2s(make_uint2(pack_rne(CL[0], CL[1]), pack_rne(CL[2], CL[3])));
     const YOps gy = yops(gs);
 
-    // ---- Y_{j+1}: from W_j (+ the correction) at a new mini-batch, from the
-    // gradient point inside one
-    f32x4 Yn = {0, 0, 0, 0};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const bf16x8 whi = next_new ? ws[h].hi : wg[h].hi;
-      const bf16x8 wmid = next_new ? ws[h].mid : wg[h].mid;
-      const bf16x8 wlo = next_new ? ws[h].lo : wg[h].lo;
-      Yn = mfma_k32(whi, k1[h], Yn);
-      Yn = mfma_k32(wmid, k1[h], Yn);
-      Yn = mfma_k32(wlo, k1[h], Yn);
-    }
-    // Gn (K_j^T K_{j+1}), both factors in three terms; the six products above
-    // 2^-24 in three MFMAs: hi.[hi|mid] + [mid|lo].hi + [hi|mid].[lo|mid]
-    const bf16x8 g2 = cat44(gs.hi, gs.lo);                 // [hi | mid]
-    const bf16x8 g3 = cat44(glo, s16x4{0, 0, 0, 0});       // [lo | 0]
+    // ---- Y_{j+1} += Gn_j (K_j^T K_{j+1}) at a new mini-batch, both factors in
+    // three terms; the six products above 2^-24 in three MFMAs:
+    // hi.[hi|mid] + [mid|lo].hi + [hi|mid].[lo|mid]
+    const bf16x8 g2 = cat44(gs.hi, gs.lo);            // [hi | mid]
+    const bf16x8 g3 = cat44(glo, s16x4{0, 0, 0, 0});  // [lo | 0]
     if (next_new) {
       const bf16x8 x1 = __builtin_bit_cast(bf16x8, mkk1);
       const bf16x8 x2 = __builtin_bit_cast(bf16x8, make_uint4(mkk1.x, mkk1.y, mkk1.x, mkk1.y));
@@ -504,36 +560,54 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
     }
 
     // ---- pre-LN outputs of tile j: W_j Q_j + Gn_j triu(K_j^T Q_j)
-    f32x4 R = {0, 0, 0, 0};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      R = mfma_k32(ws[h].hi, q0[h], R);
-      R = mfma_k32(ws[h].mid, q0[h], R);
-    }
     R = mm_pre_t(gy, att, R);
 
+    __builtin_amdgcn_sched_barrier(0);
     // ---- rank-16 update W_{j+1} = W_j + Gn_j K_j^T
 #pragma unroll
     for (int m = 0; m < 4; ++m) W[m] = mfma_k32(kt[m], g3, mfma_k32(kt[m], g2, W[m]));
 
-    // ---- hand over to tile j+1
-    GU = gamma_u(k1T, v1T);
-    const f32x4 qf = bf4(q0T);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) QB[r] = qf[r] + bet[r];
+    // ---- hand over to tile j+1: publish its statistics
+    publish(xsn, Yn, gu2n, R);
+
+    GU2 = gu2n;
+    QB = qb;
     O = R;
     Y = Yn;
-    publish(xsn, Y, GU, O);
     wait_lgkm0();
     wg_barrier_pinned();  // B_{j+1}
-    sj = sj1;
-    sj1 = sj1 == 2 ? 0 : sj1 + 1;
-    rj = rj1;
-    rj1 = rj1 == G::NST - 1 ? 0 : rj1 + 1;
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  using P3 = std::integral_constant<int, 3>;
+  using PN = std::integral_constant<int, -1>;
+  int j = 0;
+  if constexpr (TPM == 1) {
+    for (; j < ntiles; ++j) tile(j, P0{});
+  } else if constexpr (TPM == 2) {
+    for (; j + 1 < ntiles; j += 2) {
+      tile(j, P0{});
+      tile(j + 1, P1{});
+    }
+    if (j < ntiles) tile(j, P0{});
+  } else if constexpr (TPM == 4) {
+    for (; j + 3 < ntiles; j += 4) {
+      tile(j, P0{});
+      tile(j + 1, P1{});
+      tile(j + 2, P2{});
+      tile(j + 3, P3{});
+    }
+    if (j < ntiles) tile(j, P0{});
+    if (j + 1 < ntiles) tile(j + 1, P1{});
+    if (j + 2 < ntiles) tile(j + 2, P2{});
+  } else {
+    for (; j < ntiles; ++j) tile(j, PN{});
   }
   {
+    const char* xs = (const char*)xst + (ntiles & 1) * (G::XST * 4);
     float S[8];
-    gather(xst + (ntiles & 1) * G::XST, S);
+    gather(*(const f32x4*)(xs + xr0), *(const f32x4*)(xs + xr1), S);
     store_z(ntiles - 1, S, O, QB);
   }
 
@@ -546,7 +620,13 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
 }  // namespace
 
 hipError_t launch_linear_ln(const LinearLnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(linear_ln_scan_kernel, dim3(a.s.units), dim3(LnGeom::THREADS), 0, s, a);
+  const dim3 grid(a.s.units), block(LnGeom::THREADS);
+  switch (a.s.b) {
+    case 16: hipLaunchKernelGGL(linear_ln_scan_kernel<1>, grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL(linear_ln_scan_kernel<2>, grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL(linear_ln_scan_kernel<4>, grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL(linear_ln_scan_kernel<0>, grid, block, 0, s, a); break;
+  }
   return hipGetLastError();
 }
 
