@@ -13,12 +13,13 @@ Prints ONE JSON line: throughput in token*heads/s, the roofline of the scan
 kernel (algorithmic bytes / measured kernel time vs 8 TB/s HBM), the fp64
 oracle timed on the host cores as a baseline, and (unless --no-extras) the
 other workloads: the b sweep, the 125M and long-context TTT-Linear shapes,
+TTT-Linear with the LayerNorm + residual inner model (1.3B and 125M shapes),
 TTT-MLP, and a streaming-copy bandwidth reference.
 
 --pmc-calibrate additionally launches the streaming copy kernel on a known
 byte count, so that a hardware-counter run of this script can scale the
 scans' FETCH_SIZE / WRITE_SIZE readings (see --summarize-pmc), and the
-TTT-MLP scan, so that the same run covers both scan kernels.
+LayerNorm and TTT-MLP scans, so that the same run covers every scan kernel.
 """
 from __future__ import annotations
 
@@ -39,9 +40,13 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, vendor figure
 METRIC = "TTT fwd tokens·heads/s at 1 GPU; % of HBM/MFMA roofline (b=16)"
 UNIT = "tokens·heads/s"
-SCAN_SOURCES = ["ttt_linear_bf16.hip", "ttt_device.h", "ttt_launch.h"]
+SCAN_SOURCES = ["ttt_linear_bf16.hip", "ttt_device.h", "ttt_launch.h", "ttt_linear_ops.h"]
+LN_SOURCES = ["ttt_linear_ln.hip", "ttt_device.h", "ttt_launch.h", "ttt_linear_ops.h"]
 MLP_SOURCES = ["ttt_mlp.hip", "ttt_device.h", "ttt_launch.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+# untimed launches before each extra workload: the cache-flush writes of the
+# headline's cold-start pass leave the clocks low for a few milliseconds
+EXTRA_WARMUP = 50
 
 
 def log(*a):
@@ -68,6 +73,11 @@ def linear_alg_bytes(wl) -> int:
 def linear_alg_flops(wl, b) -> int:
     d = wl.d
     return wl.token_heads * (6 * d * d + 4 * b * d)
+
+
+def ln_alg_bytes(wl) -> int:
+    """The plain scan's bytes plus the LayerNorm scale and shift of each head."""
+    return linear_alg_bytes(wl) + wl.H * wl.d * 2 * 4
 
 
 def mlp_alg_bytes(wl) -> int:
@@ -181,6 +191,34 @@ def linear_case(wl, b, steps, warmup, x=None, rows=0, flush_reps=0):
     return res
 
 
+def ln_case(wl, b, steps, warmup):
+    import torch
+    from test_rnn_layers_head_amd import inputs, ttt_linear_ln_fwd
+    x = inputs.make_inputs(wl)
+    d = device_inputs(x)
+    gam = torch.from_numpy(x.ln_gamma).cuda()
+    bet = torch.from_numpy(x.ln_beta).cuda()
+    z = torch.empty((wl.B, wl.H, wl.T, wl.d), device="cuda")
+    w = torch.empty((wl.B, wl.H, wl.d, wl.d), device="cuda")
+    launch = lambda: ttt_linear_ln_fwd(d["q"], d["k"], d["v"], d["eta"], d["w0"], gam, bet,
+                                       wl.ln_eps, b, z=z, w_out=w)
+    wall, kmean, spread = time_launches(launch, steps, warmup)
+    assert torch.isfinite(z).all().item()
+    byts = ln_alg_bytes(wl)
+    res = {
+        "workload": wl.name, "b": b, "token_heads_per_s": wl.token_heads / (wall * 1e-3),
+        "ms_per_step": wall, "kernel_us_mean": kmean, "kernel_us_median": spread["median"],
+        "kernel_us_p10": spread["p10"], "kernel_us_p90": spread["p90"],
+        "alg_bytes": byts, "hbm_GBps": byts / (kmean * 1e-6) / 1e9,
+        "hbm_frac": byts / (kmean * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "kernel": "linear_ln_scan_kernel (one workgroup per (batch, head))",
+        "traffic": traffic_for("linear_ln_scan", LN_SOURCES, wl.name),
+    }
+    del d, z, w
+    torch.cuda.empty_cache()
+    return res
+
+
 def mlp_case(wl, b, steps, warmup):
     import torch
     from test_rnn_layers_head_amd import inputs, ttt_mlp_fwd
@@ -245,16 +283,17 @@ def auto_rows(units: int) -> int:
     return 64 if units >= 256 else (32 if units > 64 else 16)
 
 
-def traffic_for(kernel_key: str, sources, launch_bytes_alg: int):
+def traffic_for(kernel_key: str, sources, workload: str):
     """HBM bytes per launch from committed counter readings (FETCH_SIZE +
     WRITE_SIZE, scaled by the copy-kernel calibration), or None if the
-    readings are missing or were taken on different kernel sources."""
+    readings are missing, were taken on different kernel sources, or on
+    another workload."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
     e = t.get(kernel_key)
-    if not e or e.get("source_hash") != source_hash(sources):
+    if not e or e.get("source_hash") != source_hash(sources) or e.get("workload") != workload:
         return None
     return e["bytes_per_launch"]
 
@@ -263,26 +302,32 @@ def traffic_for(kernel_key: str, sources, launch_bytes_alg: int):
 # Counter summary: rocprofv3 --pmc output -> profiles/traffic_counters.json
 # --------------------------------------------------------------------------
 def summarize_pmc(fetch_dir, write_dir):
+    """Reads one FETCH_SIZE and one WRITE_SIZE rocprofv3 run of
+    `bench.py --no-extras --no-cpu --pmc-calibrate`, scales both counters by
+    what they read for the 1 GiB streaming copy, writes the per-launch HBM
+    bytes of each scan kernel to profiles/traffic_counters.json and prints a
+    report (per-dispatch readings, calibration, ratio to algorithmic bytes)."""
     import csv
+    from test_rnn_layers_head_amd import inputs
 
     def read(dirname, counter):
-        rows = []
+        agg = {}
         for path in glob.glob(os.path.join(dirname, "**", "*counter_collection.csv"), recursive=True):
             with open(path) as f:
                 for r in csv.DictReader(f):
-                    if r.get("Counter_Name") == counter:
-                        rows.append((r["Kernel_Name"], float(r["Counter_Value"]), int(r["Dispatch_Id"])))
-        agg = {}
-        for name, val, disp in rows:  # sum over hardware instances per dispatch
-            agg.setdefault((name, disp), 0.0)
-            agg[(name, disp)] += val
-        out = {}
-        for (name, disp), val in agg.items():
-            out.setdefault(name, []).append(val)
-        return {k: float(np.median(v)) for k, v in out.items()}
+                    if r.get("Counter_Name") == counter:  # sum over hardware instances
+                        key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+                        agg[key] = agg.get(key, 0.0) + float(r["Counter_Value"])
+        return agg
 
-    fetch = read(fetch_dir, "FETCH_SIZE")
-    write = read(write_dir, "WRITE_SIZE")
+    raw = {"FETCH_SIZE": read(fetch_dir, "FETCH_SIZE"), "WRITE_SIZE": read(write_dir, "WRITE_SIZE")}
+    med = {}
+    for c, agg in raw.items():
+        per = {}
+        for (_, name), val in agg.items():
+            per.setdefault(name, []).append(val)
+        med[c] = {k: float(np.median(v)) for k, v in per.items()}
+    fetch, write = med["FETCH_SIZE"], med["WRITE_SIZE"]
     copy_name = next(k for k in fetch if "stream_copy_kernel" in k)
     copy_bytes = 1 << 30  # --pmc-calibrate copies 1 GiB
     f_scale = copy_bytes / (fetch[copy_name] * 1024.0)
@@ -290,19 +335,36 @@ def summarize_pmc(fetch_dir, write_dir):
     out = {"calibration": {"copy_bytes": copy_bytes, "fetch_kib": fetch[copy_name],
                            "write_kib": write[copy_name], "fetch_scale": f_scale,
                            "write_scale": w_scale}}
-    for key, pat, srcs in (("linear_scan", "linear_scan_bf16_kernel", SCAN_SOURCES),
-                           ("mlp_scan", "mlp_scan_kernel", MLP_SOURCES)):
+    print("Per-dispatch readings of the scan and calibration kernels (KiB, summed over instances):")
+    for c, agg in raw.items():
+        for (disp, name), val in sorted(agg.items()):
+            if "scan" in name or "stream_copy" in name:
+                print(f"  {c:10s} dispatch {disp:>3d}  {val:14.3f}  {name[:60]}")
+    print(f"\nCalibration: stream_copy_kernel over 1 GiB reads {fetch[copy_name]:.0f} KiB by "
+          f"FETCH_SIZE and writes {write[copy_name]:.0f} KiB by WRITE_SIZE;\nscale factors fetch "
+          f"x{f_scale:.4f}, write x{w_scale:.4f} (FETCH_SIZE counts half of the bytes a plain copy "
+          "reads).\n")
+    cases = (("linear_scan", "linear_scan_bf16_kernel", SCAN_SOURCES, linear_alg_bytes, 3),
+             ("linear_ln_scan", "linear_ln_scan_kernel", LN_SOURCES, ln_alg_bytes, 6),
+             ("mlp_scan", "mlp_scan_kernel", MLP_SOURCES, mlp_alg_bytes, 4))
+    for key, pat, srcs, alg_fn, wid in cases:
         names = [k for k in fetch if pat in k]
         if not names:
             continue
         n = names[0]
-        out[key] = {"kernel": n, "fetch_kib": fetch[n], "write_kib": write.get(n, 0.0),
-                    "bytes_per_launch": fetch[n] * 1024 * f_scale + write.get(n, 0.0) * 1024 * w_scale,
-                    "source_hash": source_hash(srcs)}
+        byts = fetch[n] * 1024 * f_scale + write.get(n, 0.0) * 1024 * w_scale
+        wl = inputs.workload(wid)
+        alg = alg_fn(wl)
+        out[key] = {"kernel": n, "workload": wl.name, "fetch_kib": fetch[n],
+                    "write_kib": write.get(n, 0.0), "bytes_per_launch": byts,
+                    "alg_bytes_per_launch": alg, "source_hash": source_hash(srcs)}
+        print(f"{key}: {n}\n  workload {wl.name}: median FETCH {fetch[n]:.1f} KiB, WRITE "
+              f"{write.get(n, 0.0):.1f} KiB -> {byts / 1e6:.1f} MB per launch (scaled)\n"
+              f"  algorithmic bytes per launch {alg / 1e6:.1f} MB -> measured/algorithmic = "
+              f"{byts / alg:.3f}\n  kernel source hash {source_hash(srcs)}")
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
-    print(json.dumps(out, indent=1))
 
 
 # --------------------------------------------------------------------------
@@ -387,20 +449,28 @@ def main():
         w4 = inputs.workload(4)
         log(f"[bench] {w4.name} (counter coverage of the MLP scan)")
         mlp_case(w4, 16, 2, 1)
+        w6 = inputs.workload(6)
+        log(f"[bench] {w6.name} (counter coverage of the LayerNorm scan)")
+        ln_case(w6, 16, 2, 1)
 
     extras = {}
     if not args.no_extras:
         for bb in (1, 4, 64):
             log(f"[bench] b sweep b={bb}")
-            extras[f"{wl.name}_b{bb}"] = linear_case(wl, bb, max(3, args.steps // 4), 10, x=x)
+            extras[f"{wl.name}_b{bb}"] = linear_case(wl, bb, max(3, args.steps // 4), EXTRA_WARMUP,
+                                                     x=x)
         for wid in (2, 5):
             w2 = inputs.workload(wid)
             log(f"[bench] {w2.name}")
-            extras[w2.name] = linear_case(w2, 16, max(5, args.steps // 2), 10)
+            extras[w2.name] = linear_case(w2, 16, max(5, args.steps // 2), EXTRA_WARMUP)
+        for wid in (6, 7):
+            w6 = inputs.workload(wid)
+            log(f"[bench] {w6.name}")
+            extras[w6.name] = ln_case(w6, 16, max(5, args.steps // 2), EXTRA_WARMUP)
         w4 = inputs.workload(4)
         log(f"[bench] {w4.name}")
         try:
-            extras[w4.name] = mlp_case(w4, 16, max(5, args.steps // 2), 5)
+            extras[w4.name] = mlp_case(w4, 16, max(5, args.steps // 2), EXTRA_WARMUP)
         except Exception as e:  # reported, never silently replaced
             extras[w4.name] = {"error": str(e)}
         log("[bench] streaming copy reference")
@@ -417,7 +487,7 @@ def main():
                 log(f"[bench] fp64 oracle, one thread, {wx.wl.name}")
                 extras[f"cpu_oracle_1thread_{wx.wl.name}"] = cpu_baseline(wx, 16, 1.0, nthreads=1)
 
-    traffic = traffic_for("linear_scan", SCAN_SOURCES, head["alg_bytes"])
+    traffic = traffic_for("linear_scan", SCAN_SOURCES, wl.name)
     rec = {
         "metric": METRIC,
         "value": head["token_heads_per_s"],
