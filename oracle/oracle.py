@@ -4,7 +4,8 @@ TEST INFRASTRUCTURE ONLY: imported by the test suite, by the smoke check and
 by the CPU-baseline leg of the benchmark, never by the product path.  It shares
 no code with the HIP kernels.
 
-The C file computes the sequential primal mini-batch TTT forward of
+The C file computes the sequential primal mini-batch TTT forward (and its
+one-token decode step, §6.11) of
 "论文速览 | TTT" (equinox-blog close reading of "Learning to (Learn at Test
 Time)"): §3.1 (update, then output), §3.3 (multi-view loss
 ||f(k;W) - v||^2, output f(q; W_t)), §3.5 (mini-batch gradient point),
@@ -50,6 +51,13 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     D = ctypes.c_double
     lib.ttt_oracle_linear_ln.argtypes = [dp, dp, dp, dp, dp, I, dp, dp, D, L, L, L, L, L, dp, dp, I]
     lib.ttt_oracle_linear_ln.restype = I
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.ttt_oracle_linear_step.argtypes = [dp, dp, dp, dp, dp, dp, ip, L, L, L, L, dp]
+    lib.ttt_oracle_linear_step.restype = I
+    lib.ttt_oracle_linear_ln_step.argtypes = [dp, dp, dp, dp, dp, dp, ip, dp, dp, D, L, L, L, L, dp]
+    lib.ttt_oracle_linear_ln_step.restype = I
+    lib.ttt_oracle_mlp_step.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, ip, L, L, L, L, L, dp]
+    lib.ttt_oracle_mlp_step.restype = I
     return lib
 
 
@@ -153,3 +161,73 @@ def linear_ln(q, k, v, eta, w0, gamma, beta, eps: float, b: int, nthreads: int |
     if rc != 0:
         raise RuntimeError(f"ttt_oracle_linear_ln failed with status {rc}")
     return z, w_out
+
+
+def _ipos(pos, B) -> np.ndarray:
+    p = np.ascontiguousarray(np.asarray(pos, dtype=np.int32))
+    assert p.shape == (B,) and (p >= 0).all()
+    return p
+
+
+def _iptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int))
+
+
+def linear_step(q, k, v, eta, w, wg, pos, b: int, lib=None):
+    """One TTT-Linear decode step (primal form) for every (batch, head) unit.
+
+    q, k, v: [B, H, d] (this token's views); eta: [B, H]; w, wg: [B, H, d, d],
+    the current state and the gradient point (the state at the start of the
+    current mini-batch); pos: [B] token index of this token (the step sets
+    wg = w first when pos % b == 0).  Inputs are not modified.
+    Returns (z [B, H, d], w_new, wg_new) in float64.
+    """
+    q, k, v, eta = map(_f64, (q, k, v, eta))
+    B, H, d = q.shape
+    w, wg = _f64(w).copy(), _f64(wg).copy()
+    assert w.shape == (B, H, d, d) and wg.shape == w.shape and eta.shape == (B, H)
+    p = _ipos(pos, B)
+    z = np.zeros((B, H, d))
+    lib = lib or load()
+    rc = lib.ttt_oracle_linear_step(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w), _ptr(wg),
+                                    _iptr(p), B, H, d, int(b), _ptr(z))
+    if rc != 0:
+        raise RuntimeError(f"ttt_oracle_linear_step failed with status {rc}")
+    return z, w, wg
+
+
+def linear_ln_step(q, k, v, eta, w, wg, pos, gamma, beta, eps: float, b: int, lib=None):
+    """One decode step of TTT-Linear with the LayerNorm + residual inner
+    model; arguments as for ``linear_step`` plus gamma, beta [H, d] and eps."""
+    q, k, v, eta, gamma, beta = map(_f64, (q, k, v, eta, gamma, beta))
+    B, H, d = q.shape
+    w, wg = _f64(w).copy(), _f64(wg).copy()
+    assert w.shape == (B, H, d, d) and wg.shape == w.shape and gamma.shape == (H, d)
+    p = _ipos(pos, B)
+    z = np.zeros((B, H, d))
+    lib = lib or load()
+    rc = lib.ttt_oracle_linear_ln_step(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w), _ptr(wg),
+                                       _iptr(p), _ptr(gamma), _ptr(beta), float(eps), B, H, d,
+                                       int(b), _ptr(z))
+    if rc != 0:
+        raise RuntimeError(f"ttt_oracle_linear_ln_step failed with status {rc}")
+    return z, w, wg
+
+
+def mlp_step(q, k, v, eta, w1, w2, w1g, w2g, pos, b: int, lib=None):
+    """One TTT-MLP decode step: w1, w1g [B, H, hidden, d]; w2, w2g
+    [B, H, d, hidden].  Returns (z, w1_new, w2_new, w1g_new, w2g_new)."""
+    q, k, v, eta = map(_f64, (q, k, v, eta))
+    B, H, d = q.shape
+    w1, w2, w1g, w2g = (_f64(a).copy() for a in (w1, w2, w1g, w2g))
+    hidden = w1.shape[-2]
+    assert w1.shape == (B, H, hidden, d) and w2.shape == (B, H, d, hidden)
+    assert w1g.shape == w1.shape and w2g.shape == w2.shape
+    p = _ipos(pos, B)
+    z = np.zeros((B, H, d))
+    lib = lib or load()
+    rc = lib.ttt_oracle_mlp_step(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w1), _ptr(w2),
+                                 _ptr(w1g), _ptr(w2g), _iptr(p), B, H, d, hidden, int(b), _ptr(z))
+    if rc != 0:
+        raise RuntimeError(f"ttt_oracle_mlp_step failed with status {rc}")
+    return z, w1, w2, w1g, w2g

@@ -30,6 +30,13 @@
  *    gamma, beta per head and eps are inputs: the page names the wrapper but
  *    not its parameters).  The gradient goes through the LayerNorm.
  *
+ * Decode steps (§6.11: token-by-token generation uses the primal form): one
+ * token per (batch, head) unit per call.  A unit carries its current state W
+ * and its gradient point Wg, the state at the start of the current
+ * mini-batch; for a token at position p = pos mod b, p = 0 first sets
+ * Wg = W.  Then the token's gradient is taken at Wg, W takes the step, and the
+ * output is read from the updated W: exactly one iteration of the scans above.
+ *
  * The loss is the squared L2 norm summed over output components, so its
  * gradient carries the factor 2 (§3.6 linear derivation: G_t = 2(W0 x - x)x^T).
  * GELU is the exact erf form x * Phi(x).  Mini-batches start at token 0, b,
@@ -340,4 +347,143 @@ int ttt_oracle_linear_ln(const double *q, const double *k, const double *v,
   p.w0_per_batch = w0_per_batch; p.B = B; p.H = H; p.T = T; p.d = d; p.hd = 0;
   p.b = b; p.z = z; p.outa = w_out;
   return run(p, nthreads);
+}
+
+/* ------------------------------------------------------------------ */
+/* Decode steps: one token per unit, primal form (§6.11).              */
+/* Layouts: q, k, v [B][H][d]; eta [B][H]; pos [B]; states [B][H][...]; */
+/* z [B][H][d].  States are updated in place.                          */
+/* ------------------------------------------------------------------ */
+static int step_args_ok(long B, long H, long d, long b) {
+  return B >= 0 && H >= 0 && d > 0 && b > 0;
+}
+
+int ttt_oracle_linear_step(const double *q, const double *k, const double *v,
+                           const double *eta, double *w, double *wg,
+                           const int *pos, long B, long H, long d, long b,
+                           double *z) {
+  if (!step_args_ok(B, H, d, b)) return 2;
+  double *gr = (double *)malloc(sizeof(double) * (size_t)d);
+  if (!gr) return 1;
+  for (long u = 0; u < B * H; ++u) {
+    const long bi = u / H;
+    const double *ku = k + u * d, *vu = v + u * d, *qu = q + u * d;
+    double *W = w + u * d * d, *Wg = wg + u * d * d;
+    if (pos[bi] % b == 0) memcpy(Wg, W, sizeof(double) * (size_t)(d * d));
+    /* gradient of ||W k - v||^2 at the gradient point: 2 (Wg k - v) k^T */
+    for (long i = 0; i < d; ++i) {
+      double pk = 0.0;
+      for (long j = 0; j < d; ++j) pk += Wg[i * d + j] * ku[j];
+      gr[i] = 2.0 * (pk - vu[i]);
+    }
+    for (long i = 0; i < d; ++i)
+      for (long j = 0; j < d; ++j) W[i * d + j] -= eta[u] * gr[i] * ku[j];
+    for (long i = 0; i < d; ++i) {
+      double zq = 0.0;
+      for (long j = 0; j < d; ++j) zq += W[i * d + j] * qu[j];
+      z[u * d + i] = zq;
+    }
+  }
+  free(gr);
+  return 0;
+}
+
+int ttt_oracle_linear_ln_step(const double *q, const double *k, const double *v,
+                              const double *eta, double *w, double *wg,
+                              const int *pos, const double *gamma,
+                              const double *beta, double eps, long B, long H,
+                              long d, long b, double *z) {
+  if (!step_args_ok(B, H, d, b) || !(eps >= 0.0)) return 2;
+  double *y = (double *)malloc(sizeof(double) * (size_t)(3 * d));
+  if (!y) return 1;
+  double *yh = y + d, *gy = y + 2 * d;
+  for (long u = 0; u < B * H; ++u) {
+    const long bi = u / H, hh = u % H;
+    const double *ku = k + u * d, *vu = v + u * d, *qu = q + u * d;
+    const double *ga = gamma + hh * d, *be = beta + hh * d;
+    double *W = w + u * d * d, *Wg = wg + u * d * d;
+    if (pos[bi] % b == 0) memcpy(Wg, W, sizeof(double) * (size_t)(d * d));
+    for (long i = 0; i < d; ++i) {
+      double pk = 0.0;
+      for (long j = 0; j < d; ++j) pk += Wg[i * d + j] * ku[j];
+      y[i] = pk;
+    }
+    const double rs = ln_normalise(y, d, eps, yh);
+    /* f(k) = k + gamma yhat + beta; dl/dyhat_i = 2 gamma_i (f_i - v_i) */
+    double mg = 0.0, mgy = 0.0;
+    for (long i = 0; i < d; ++i) {
+      gy[i] = 2.0 * ga[i] * (ku[i] + ga[i] * yh[i] + be[i] - vu[i]);
+      mg += gy[i];
+      mgy += gy[i] * yh[i];
+    }
+    mg /= (double)d;
+    mgy /= (double)d;
+    for (long i = 0; i < d; ++i) {
+      const double dy = rs * (gy[i] - mg - yh[i] * mgy); /* LayerNorm VJP */
+      for (long j = 0; j < d; ++j) W[i * d + j] -= eta[u] * dy * ku[j];
+    }
+    for (long i = 0; i < d; ++i) {
+      double zq = 0.0;
+      for (long j = 0; j < d; ++j) zq += W[i * d + j] * qu[j];
+      y[i] = zq;
+    }
+    ln_normalise(y, d, eps, yh);
+    for (long i = 0; i < d; ++i) z[u * d + i] = qu[i] + ga[i] * yh[i] + be[i];
+  }
+  free(y);
+  return 0;
+}
+
+int ttt_oracle_mlp_step(const double *q, const double *k, const double *v,
+                        const double *eta, double *w1, double *w2, double *w1g,
+                        double *w2g, const int *pos, long B, long H, long d,
+                        long hidden, long b, double *z) {
+  if (!step_args_ok(B, H, d, b) || hidden <= 0) return 2;
+  const long hd = hidden;
+  double *sc = (double *)malloc(sizeof(double) * (size_t)(4 * hd + d));
+  if (!sc) return 1;
+  double *a = sc, *x = sc + hd, *dl = sc + 2 * hd, *hq = sc + 3 * hd, *e = sc + 4 * hd;
+  for (long u = 0; u < B * H; ++u) {
+    const long bi = u / H;
+    const double *ku = k + u * d, *vu = v + u * d, *qu = q + u * d;
+    double *W1 = w1 + u * hd * d, *W2 = w2 + u * d * hd;
+    double *W1g = w1g + u * hd * d, *W2g = w2g + u * d * hd;
+    if (pos[bi] % b == 0) {
+      memcpy(W1g, W1, sizeof(double) * (size_t)(hd * d));
+      memcpy(W2g, W2, sizeof(double) * (size_t)(d * hd));
+    }
+    /* forward and backward at the gradient point */
+    for (long h = 0; h < hd; ++h) {
+      double ak = 0.0;
+      for (long j = 0; j < d; ++j) ak += W1g[h * d + j] * ku[j];
+      a[h] = ak;
+      x[h] = gelu(ak);
+    }
+    for (long i = 0; i < d; ++i) {
+      double yo = 0.0;
+      for (long h = 0; h < hd; ++h) yo += W2g[i * hd + h] * x[h];
+      e[i] = 2.0 * (yo - vu[i]);
+    }
+    for (long h = 0; h < hd; ++h) {
+      double bp = 0.0;
+      for (long i = 0; i < d; ++i) bp += W2g[i * hd + h] * e[i];
+      dl[h] = bp * gelu_grad(a[h]);
+    }
+    for (long i = 0; i < d; ++i)
+      for (long h = 0; h < hd; ++h) W2[i * hd + h] -= eta[u] * e[i] * x[h];
+    for (long h = 0; h < hd; ++h)
+      for (long j = 0; j < d; ++j) W1[h * d + j] -= eta[u] * dl[h] * ku[j];
+    for (long h = 0; h < hd; ++h) {
+      double aq = 0.0;
+      for (long j = 0; j < d; ++j) aq += W1[h * d + j] * qu[j];
+      hq[h] = gelu(aq);
+    }
+    for (long i = 0; i < d; ++i) {
+      double zo = 0.0;
+      for (long h = 0; h < hd; ++h) zo += W2[i * hd + h] * hq[h];
+      z[u * d + i] = zo;
+    }
+  }
+  free(sc);
+  return 0;
 }

@@ -313,6 +313,110 @@ def pin_ln_normalised_outputs(lib):
     assert np.abs((y * y).mean(axis=-1) - 1.0).max() < 1e-12
 
 
+# ---- decode steps (§6.11: generation runs the primal form token by token)
+
+def _replay(step_fn, T, B, b, starts):
+    """Runs step_fn(t_index, pos) for t = 0..T-1 with each batch element's
+    positions starting at its own multiple of b (same mini-batch alignment as
+    a scan from token 0)."""
+    for t in range(T):
+        step_fn(t, np.asarray(starts) + t)
+
+
+def pin_linear_step_replays_scan(lib):
+    rng = np.random.default_rng(41)
+    for (T, b) in [(23, 4), (20, 1), (19, 3), (35, 16)]:
+        B, H, d = 2, 2, 6
+        q, k, v, eta, w0 = rand_linear(rng, B, H, T, d)
+        zs, ws = oracle.linear(q, k, v, eta, w0, b, lib=lib)
+        w = np.broadcast_to(w0[None], (B, H, d, d)).copy()
+        wg = rng.standard_normal(w.shape)  # overwritten at the first step (pos % b == 0)
+        z = np.zeros_like(zs)
+        st = {"w": w, "wg": wg}
+
+        def step(t, pos):
+            zt, st["w"], st["wg"] = oracle.linear_step(q[:, :, t], k[:, :, t], v[:, :, t],
+                                                       eta[:, :, t], st["w"], st["wg"], pos, b,
+                                                       lib=lib)
+            z[:, :, t] = zt
+        _replay(step, T, B, b, [0, 2 * b])
+        assert rel(z, zs) < 1e-12 and rel(st["w"], ws) < 1e-12, (T, b)
+
+
+def pin_ln_step_replays_scan(lib):
+    rng = np.random.default_rng(42)
+    for (T, b) in [(21, 4), (18, 1), (33, 16)]:
+        B, H, d = 2, 2, 6
+        q, k, v, eta, w0 = rand_linear(rng, B, H, T, d, eta_scale=0.3)
+        gamma, beta = rand_ln(rng, H, d)
+        zs, ws = oracle.linear_ln(q, k, v, eta, w0, gamma, beta, 1e-5, b, lib=lib)
+        st = {"w": np.broadcast_to(w0[None], (B, H, d, d)).copy(),
+              "wg": rng.standard_normal((B, H, d, d))}
+        z = np.zeros_like(zs)
+
+        def step(t, pos):
+            zt, st["w"], st["wg"] = oracle.linear_ln_step(q[:, :, t], k[:, :, t], v[:, :, t],
+                                                          eta[:, :, t], st["w"], st["wg"], pos,
+                                                          gamma, beta, 1e-5, b, lib=lib)
+            z[:, :, t] = zt
+        _replay(step, T, B, b, [3 * b, 0])
+        assert rel(z, zs) < 1e-12 and rel(st["w"], ws) < 1e-12, (T, b)
+
+
+def pin_mlp_step_replays_scan(lib):
+    rng = np.random.default_rng(43)
+    for (T, b) in [(13, 4), (9, 1)]:
+        B, H, d, hd = 2, 1, 4, 8
+        q, k, v, eta, w1, w2 = rand_mlp(rng, B, H, T, d, hd)
+        zs, w1s, w2s = oracle.mlp(q, k, v, eta, w1, w2, b, lib=lib)
+        st = {"w1": np.broadcast_to(w1[None], (B, H, hd, d)).copy(),
+              "w2": np.broadcast_to(w2[None], (B, H, d, hd)).copy(),
+              "w1g": np.zeros((B, H, hd, d)), "w2g": np.zeros((B, H, d, hd))}
+        z = np.zeros_like(zs)
+
+        def step(t, pos):
+            zt, st["w1"], st["w2"], st["w1g"], st["w2g"] = oracle.mlp_step(
+                q[:, :, t], k[:, :, t], v[:, :, t], eta[:, :, t], st["w1"], st["w2"], st["w1g"],
+                st["w2g"], pos, b, lib=lib)
+            z[:, :, t] = zt
+        _replay(step, T, B, b, [b, 0])
+        assert rel(z, zs) < 1e-12, (T, b)
+        assert rel(st["w1"], w1s) < 1e-12 and rel(st["w2"], w2s) < 1e-12, (T, b)
+
+
+def pin_step_resumes_a_scan_mid_sequence(lib):
+    # A scan over the first m*b tokens ends at the gradient point of the next
+    # mini-batch; decode steps continue from there (also mid-mini-batch).
+    rng = np.random.default_rng(44)
+    B, H, T, d, b, m = 1, 3, 30, 5, 4, 3
+    q, k, v, eta, w0 = rand_linear(rng, B, H, T, d)
+    zs, ws = oracle.linear(q, k, v, eta, w0, b, lib=lib)
+    _, w_mid = oracle.linear(q[:, :, :m * b], k[:, :, :m * b], v[:, :, :m * b],
+                             eta[:, :, :m * b], w0, b, lib=lib)
+    w, wg = w_mid, np.full_like(w_mid, np.nan)  # a NaN gradient point must never be read
+    for t in range(m * b, T):
+        zt, w, wg = oracle.linear_step(q[:, :, t], k[:, :, t], v[:, :, t], eta[:, :, t], w, wg,
+                                       [t], b, lib=lib)
+        assert rel(zt, zs[:, :, t]) < 1e-12, t
+    assert rel(w, ws) < 1e-12
+
+
+def pin_step_golden_scalar_examples(lib):
+    with open(os.path.join(HERE, "golden", "scalar_worked_examples.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        T, d = len(c["eta"]), c["d"]
+        w = np.asarray(c["w0"], dtype=np.float64).reshape(1, 1, d, d)
+        wg = np.zeros_like(w)
+        for t in range(T):
+            vec = lambda key: np.asarray(c[key][t], dtype=np.float64).reshape(1, 1, d)
+            zt, w, wg = oracle.linear_step(vec("q"), vec("k"), vec("v"),
+                                           np.asarray([[c["eta"][t]]]), w, wg, [t], c["b"],
+                                           lib=lib)
+            assert np.array_equal(zt.reshape(d), np.asarray(c["z"][t])), (c["name"], t)
+        assert np.array_equal(w.reshape(d, d), np.asarray(c["w_T"])), c["name"]
+
+
 PINS = [
     pin_linear_primal_equals_dual,
     pin_mlp_primal_equals_dual,
@@ -331,6 +435,11 @@ PINS = [
     pin_ln_gamma_zero,
     pin_ln_scale_covariance,
     pin_ln_normalised_outputs,
+    pin_linear_step_replays_scan,
+    pin_ln_step_replays_scan,
+    pin_mlp_step_replays_scan,
+    pin_step_resumes_a_scan_mid_sequence,
+    pin_step_golden_scalar_examples,
 ]
 
 
@@ -426,6 +535,22 @@ MUTATIONS = {
     "ln_no_gamma_in_vjp": ("gy[i] = 2.0 * gamma[i] * (f - vt[i]);", "gy[i] = 2.0 * (f - vt[i]);"),
     "ln_output_before_update": ("acc += W[i * d + j] * qt[j];", "acc += Ws[i * d + j] * qt[j];"),
     "ln_grad_at_current_state": ("acc += Ws[i * d + j] * kt[j];", "acc += W[i * d + j] * kt[j];"),
+    "step_no_gradient_point_reset": (
+        "if (pos[bi] % b == 0) memcpy(Wg, W, sizeof(double) * (size_t)(d * d));\n    /* gradient of",
+        "/* gradient of"),
+    "step_grad_at_current_state": ("pk += Wg[i * d + j] * ku[j];\n      gr[i]",
+                                   "pk += W[i * d + j] * ku[j];\n      gr[i]"),
+    "step_output_from_gradient_point": ("zq += W[i * d + j] * qu[j];\n      z[u * d + i] = zq;",
+                                        "zq += Wg[i * d + j] * qu[j];\n      z[u * d + i] = zq;"),
+    "step_gradient_point_every_token": ("if (pos[bi] % b == 0) memcpy(Wg, W, sizeof(double) * (size_t)(d * d));\n    /* gradient of",
+                                        "memcpy(Wg, W, sizeof(double) * (size_t)(d * d));\n    /* gradient of"),
+    "ln_step_no_projection_term": ("const double dy = rs * (gy[i] - mg - yh[i] * mgy);",
+                                   "const double dy = rs * (gy[i] - mg);"),
+    "ln_step_no_residual_in_output": ("z[u * d + i] = qu[i] + ga[i] * yh[i] + be[i];",
+                                      "z[u * d + i] = ga[i] * yh[i] + be[i];"),
+    "mlp_step_backprop_through_current_w2": ("bp += W2g[i * hd + h] * e[i];",
+                                             "bp += W2[i * hd + h] * e[i];"),
+    "mlp_step_w1_gradient_point_not_reset": ("memcpy(W1g, W1, sizeof(double) * (size_t)(hd * d));", ""),
 }
 
 
