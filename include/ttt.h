@@ -129,6 +129,44 @@ ttt_status_t ttt_linear_ln_fwd(const void* q, const void* k, const void* v,
                                void* stream);
 
 /*
+ * Decode steps (§6.11: generation runs the primal form, one token at a
+ * time).  One call advances every (batch, head) unit by one token.  A unit
+ * carries two states, both updated in place:
+ *   w     the state after the previous token (W_{t-1});
+ *   w_gp  the gradient point: the state at the start of the current
+ *         mini-batch (§3.5).
+ * With p = pos mod b (mathematical modulo) the token first sets w_gp = w when
+ * p == 0, then takes its gradient at w_gp, updates w, and outputs
+ * z = f(q; w) from the updated state (§3.1).  A scan over a multiple of b
+ * tokens ends exactly at the next gradient point, so a sequence may be
+ * prefilled with the scan and continued with steps; to continue a prefill of
+ * another length, prefill the largest multiple of b and step the rest.
+ *
+ *   q, k, v : [B][H][d] qkv_dtype (this token)     eta : [B][H] fp32
+ *   w, w_gp : [B][H][d][d] fp32, in/out; w_gp may be NULL when b == 1
+ *   pos     : [B] int32 (device), the token's index in its sequence
+ *   z       : out [B][H][d] fp32
+ * Support: d = 64, any b >= 1, fp32 or bf16 q/k/v.  Outputs (z, w, w_gp)
+ * must not overlap each other or an input.  Empty work (B*H == 0) returns
+ * TTT_OK without launching.
+ */
+ttt_status_t ttt_linear_step(const void* q, const void* k, const void* v,
+                             const float* eta, float* w, float* w_gp,
+                             const int32_t* pos, int32_t B, int32_t H,
+                             int32_t d, int32_t b, ttt_dtype_t qkv_dtype,
+                             float* z, void* stream);
+
+/* The same for the LayerNorm + residual inner model of ttt_linear_ln_fwd:
+ * ln_gamma, ln_beta [H][d] fp32, eps finite and > 0 (else TTT_ERR_VALUE);
+ * any b >= 1. */
+ttt_status_t ttt_linear_ln_step(const void* q, const void* k, const void* v,
+                                const float* eta, float* w, float* w_gp,
+                                const int32_t* pos, const float* ln_gamma,
+                                const float* ln_beta, float eps, int32_t B,
+                                int32_t H, int32_t d, int32_t b,
+                                ttt_dtype_t qkv_dtype, float* z, void* stream);
+
+/*
  * TTT-MLP forward scan, f(x) = W2 GELU(W1 x) (§3.7 dual form, §4.4).
  *
  *   w1_0 : [H][hidden][d] fp32 (or [B][H][hidden][d] when w0_per_batch = 1)

@@ -123,6 +123,65 @@ def ttt_linear_ln_fwd(q, k, v, eta, w0, ln_gamma, ln_beta, eps: float, b: int, z
     return z, w_out
 
 
+def _step_common(name, q, k, v, eta, pos, states: dict, z):
+    if q.dim() != 3:
+        raise ValueError(f"{name}: q must be [B, H, d] (one token per unit)")
+    B, H, d = q.shape
+    if z is None:
+        z = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+    dev = _check_tensors(dict(q=q, k=k, v=v, eta=eta, pos=pos, z=z, **states))
+    for nm, t in (("eta", eta), ("z", z), *states.items()):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{nm} must be float32, got {t.dtype}")
+    if pos.dtype != torch.int32 or tuple(pos.shape) != (B,):
+        raise TypeError("pos must be an int32 tensor of shape [B]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if k.shape != q.shape or v.shape != q.shape or tuple(eta.shape) != (B, H):
+        raise ValueError("shape mismatch among q, k, v, eta")
+    if tuple(z.shape) != (B, H, d):
+        raise ValueError("z must be [B, H, d]")
+    return B, H, d, z, dev
+
+
+def ttt_linear_step(q, k, v, eta, w, w_gp, pos, b: int, z=None, stream=None):
+    """One TTT-Linear decode step for every (batch, head) unit (include/ttt.h).
+
+    q, k, v: [B, H, d] (this token); eta: [B, H] fp32; w, w_gp: [B, H, d, d]
+    fp32, the state and the gradient point, updated in place (w_gp may be
+    None when b == 1); pos: [B] int32, the token's index in its sequence.
+    Returns z [B, H, d] fp32.
+    """
+    B, H, d, z, dev = _step_common("ttt_linear_step", q, k, v, eta, pos, dict(w=w, w_gp=w_gp), z)
+    for nm, t in (("w", w), ("w_gp", w_gp)):
+        if t is not None and tuple(t.shape) != (B, H, d, d):
+            raise ValueError(f"{nm} must be [B, H, d, d]")
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib().ttt_linear_step(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w),
+                                              _ptr(w_gp), _ptr(pos), B, H, d, int(b),
+                                              _dtype_code(q), _ptr(z), _stream(dev, stream)))
+    return z
+
+
+def ttt_linear_ln_step(q, k, v, eta, w, w_gp, pos, ln_gamma, ln_beta, eps: float, b: int, z=None,
+                       stream=None):
+    """One decode step of TTT-Linear with the LayerNorm + residual inner
+    model; as ttt_linear_step plus ln_gamma, ln_beta [H, d] fp32 and eps."""
+    B, H, d, z, dev = _step_common("ttt_linear_ln_step", q, k, v, eta, pos,
+                                   dict(w=w, w_gp=w_gp, ln_gamma=ln_gamma, ln_beta=ln_beta), z)
+    for nm, t in (("w", w), ("w_gp", w_gp)):
+        if t is not None and tuple(t.shape) != (B, H, d, d):
+            raise ValueError(f"{nm} must be [B, H, d, d]")
+    if tuple(ln_gamma.shape) != (H, d) or tuple(ln_beta.shape) != (H, d):
+        raise ValueError("ln_gamma / ln_beta must be [H, d]")
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib().ttt_linear_ln_step(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w),
+                                                 _ptr(w_gp), _ptr(pos), _ptr(ln_gamma),
+                                                 _ptr(ln_beta), float(eps), B, H, d, int(b),
+                                                 _dtype_code(q), _ptr(z), _stream(dev, stream)))
+    return z
+
+
 def ttt_mlp_fwd(q, k, v, eta, w1_0, w2_0, b: int, z=None, w1_out=None, w2_out=None, stream=None):
     """TTT-MLP forward scan, f(x) = W2 GELU(W1 x) (see include/ttt.h).
 

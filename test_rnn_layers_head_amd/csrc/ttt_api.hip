@@ -167,9 +167,98 @@ ttt_status_t linear_ln_impl(const void* q, const void* k, const void* v, const f
   return TTT_OK;
 }
 
+// Shared checks of the decode steps.  `in` / `out` list every tensor with its
+// byte extent; states that are updated in place are listed as outputs.
+ttt_status_t check_step(const char* fn, ttt_dtype_t dt, int32_t B, int32_t H, int32_t d, int32_t b,
+                        const Range* in, int nin, const Range* out, int nout,
+                        const bool* optional_out) {
+  if (dt != TTT_F32 && dt != TTT_BF16) return fail(TTT_ERR_DTYPE, "%s: unknown qkv_dtype %d", fn, (int)dt);
+  if (B < 0 || H < 0 || d < 0 || b < 0)
+    return fail(TTT_ERR_SHAPE, "%s: negative size (B=%d H=%d d=%d b=%d)", fn, B, H, d, b);
+  if (d != 64) return fail(TTT_ERR_UNSUPPORTED, "%s: head dim d=%d unsupported (only 64)", fn, d);
+  if (b < 1) return fail(TTT_ERR_UNSUPPORTED, "%s: mini-batch b=%d unsupported (need b >= 1)", fn, b);
+  if ((int64_t)B * H * d * 256 >= ((int64_t)1 << 31))
+    return fail(TTT_ERR_SHAPE, "%s: B*H = %lld units is too many for one call", fn,
+                (long long)B * H);
+  if ((int64_t)B * H == 0) return TTT_OK;
+  for (int i = 0; i < nin; ++i) {
+    if (!in[i].lo) return fail(TTT_ERR_NULL, "%s: %s is NULL", fn, in[i].name);
+    if (in[i].lo & 15) return fail(TTT_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, in[i].name);
+  }
+  for (int o = 0; o < nout; ++o) {
+    if (!out[o].lo) {
+      if (optional_out && optional_out[o]) continue;
+      return fail(TTT_ERR_NULL, "%s: %s is NULL", fn, out[o].name);
+    }
+    if (out[o].lo & 15) return fail(TTT_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, out[o].name);
+    for (int i = 0; i < nin; ++i)
+      if (overlap(out[o], in[i]))
+        return fail(TTT_ERR_ALIAS, "%s: %s overlaps input %s", fn, out[o].name, in[i].name);
+    for (int o2 = o + 1; o2 < nout; ++o2)
+      if (overlap(out[o], out[o2]))
+        return fail(TTT_ERR_ALIAS, "%s: %s and %s overlap", fn, out[o].name, out[o2].name);
+  }
+  return TTT_OK;
+}
+
+ttt_status_t linear_step_impl(const char* fn, const void* q, const void* k, const void* v,
+                              const float* eta, float* w, float* w_gp, const int32_t* pos,
+                              const float* gamma, const float* beta, float eps, bool ln,
+                              int32_t B, int32_t H, int32_t d, int32_t b, ttt_dtype_t dt, float* z,
+                              void* stream) {
+  const int64_t units = (int64_t)B * H;
+  const int64_t es = dt == TTT_F32 ? 4 : 2;
+  const Range in_all[] = {rng("q", q, units * d * es), rng("k", k, units * d * es),
+                          rng("v", v, units * d * es), rng("eta", eta, units * 4),
+                          rng("pos", pos, (int64_t)B * 4),
+                          rng("ln_gamma", gamma, (int64_t)H * d * 4),
+                          rng("ln_beta", beta, (int64_t)H * d * 4)};
+  const Range out[] = {rng("z", z, units * d * 4), rng("w", w, units * d * d * 4),
+                       rng("w_gp", w_gp, units * d * d * 4)};
+  const bool optional[] = {false, false, b == 1};
+  // pos only needs 4-byte alignment; check it apart from the 16-byte rule
+  Range in[7];
+  int nin = 0;
+  for (int i = 0; i < (ln ? 7 : 5); ++i)
+    if (i != 4) in[nin++] = in_all[i];
+  ttt_status_t st = check_step(fn, dt, B, H, d, b, in, nin, out, 3, optional);
+  if (st != TTT_OK || units == 0) return st;
+  if (!w_gp && b != 1)
+    return fail(TTT_ERR_NULL, "%s: w_gp is NULL (allowed only for b = 1)", fn);
+  if (!pos) return fail(TTT_ERR_NULL, "%s: pos is NULL", fn);
+  if ((uintptr_t)pos & 3) return fail(TTT_ERR_ALIGN, "%s: pos is not 4-byte aligned", fn);
+  for (int o = 0; o < 3; ++o)
+    if (overlap(out[o], in_all[4]))
+      return fail(TTT_ERR_ALIAS, "%s: %s overlaps input pos", fn, out[o].name);
+  if (ln && (!(eps > 0.f) || eps > 3.0e38f))
+    return fail(TTT_ERR_VALUE, "%s: eps=%g must be finite and > 0", fn, (double)eps);
+  ttt::StepArgs a{q, k, v, eta, w, w_gp, nullptr, nullptr, pos, z, (int)units, H, b};
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = ln ? ttt::launch_linear_ln_step(a, gamma, beta, eps, dt == TTT_F32, s)
+                    : ttt::launch_linear_step(a, dt == TTT_F32, s);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return TTT_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+ttt_status_t ttt_linear_step(const void* q, const void* k, const void* v, const float* eta,
+                             float* w, float* w_gp, const int32_t* pos, int32_t B, int32_t H,
+                             int32_t d, int32_t b, ttt_dtype_t qkv_dtype, float* z, void* stream) {
+  return linear_step_impl("ttt_linear_step", q, k, v, eta, w, w_gp, pos, nullptr, nullptr, 0.f,
+                          false, B, H, d, b, qkv_dtype, z, stream);
+}
+
+ttt_status_t ttt_linear_ln_step(const void* q, const void* k, const void* v, const float* eta,
+                                float* w, float* w_gp, const int32_t* pos, const float* ln_gamma,
+                                const float* ln_beta, float eps, int32_t B, int32_t H, int32_t d,
+                                int32_t b, ttt_dtype_t qkv_dtype, float* z, void* stream) {
+  return linear_step_impl("ttt_linear_ln_step", q, k, v, eta, w, w_gp, pos, ln_gamma, ln_beta,
+                          eps, true, B, H, d, b, qkv_dtype, z, stream);
+}
+
 
 ttt_status_t ttt_linear_fwd(const void* q, const void* k, const void* v, const float* eta,
                             const float* w0, int32_t w0_per_batch, int32_t B, int32_t H,

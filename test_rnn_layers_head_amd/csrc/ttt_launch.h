@@ -46,11 +46,31 @@ struct MlpArgs {
   int b;
 };
 
+// One decode step for every (batch, head) unit.
+struct StepArgs {
+  const void* q;  // [B][H][d]
+  const void* k;
+  const void* v;
+  const float* eta;  // [B][H]
+  float* w;          // [B][H][...] state, in/out
+  float* w_gp;       // gradient point, in/out (NULL: b == 1)
+  float* w2;         // TTT-MLP second layer, in/out
+  float* w2_gp;
+  const int32_t* pos;  // [B]
+  float* z;            // [B][H][d]
+  int units;
+  int H;
+  int b;
+};
+
 // rows: rows of W per workgroup (64, 32 or 16).
 hipError_t launch_linear(const LinearArgs& a, bool f32in, int rows, hipStream_t s);
 hipError_t launch_linear_bf16(const LinearArgs& a, int rows, hipStream_t s);
 hipError_t launch_linear_ln(const LinearLnArgs& a, hipStream_t s);
 hipError_t launch_mlp(const MlpArgs& a, bool f32in, hipStream_t s);
+hipError_t launch_linear_step(const StepArgs& a, bool f32in, hipStream_t s);
+hipError_t launch_linear_ln_step(const StepArgs& a, const float* gamma, const float* beta,
+                                 float eps, bool f32in, hipStream_t s);
 hipError_t launch_copy_state(const float* src, int per_unit, int units, int H, int n,
                              float* dst, hipStream_t s);
 
