@@ -166,6 +166,17 @@ ttt_status_t ttt_linear_ln_step(const void* q, const void* k, const void* v,
                                 int32_t H, int32_t d, int32_t b,
                                 ttt_dtype_t qkv_dtype, float* z, void* stream);
 
+/* The same for TTT-MLP, f(x) = W2 GELU(W1 x) (as ttt_mlp_fwd):
+ *   w1, w1_gp : [B][H][hidden][d] fp32, in/out
+ *   w2, w2_gp : [B][H][d][hidden] fp32, in/out
+ * Both gradient points may be NULL when b == 1 (pass both or neither).
+ * Support: d = 64, hidden = 256, any b >= 1, fp32 or bf16 q/k/v. */
+ttt_status_t ttt_mlp_step(const void* q, const void* k, const void* v,
+                          const float* eta, float* w1, float* w2, float* w1_gp,
+                          float* w2_gp, const int32_t* pos, int32_t B, int32_t H,
+                          int32_t d, int32_t hidden, int32_t b,
+                          ttt_dtype_t qkv_dtype, float* z, void* stream);
+
 /*
  * TTT-MLP forward scan, f(x) = W2 GELU(W1 x) (§3.7 dual form, §4.4).
  *

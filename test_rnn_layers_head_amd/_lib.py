@@ -29,6 +29,8 @@ SIGNATURES = {
                                _vp, _vp]),
     "ttt_linear_ln_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
                                   _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "ttt_mlp_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                            _i32, _i32, _vp, _vp]),
     "ttt_mlp_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                            _i32, _vp, _vp, _vp, _vp]),
     "ttt_status_str": (ctypes.c_char_p, [_i32]),

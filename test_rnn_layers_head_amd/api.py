@@ -182,6 +182,24 @@ def ttt_linear_ln_step(q, k, v, eta, w, w_gp, pos, ln_gamma, ln_beta, eps: float
     return z
 
 
+def ttt_mlp_step(q, k, v, eta, w1, w2, w1_gp, w2_gp, pos, b: int, z=None, stream=None):
+    """One TTT-MLP decode step (include/ttt.h): w1, w1_gp [B, H, hidden, d],
+    w2, w2_gp [B, H, d, hidden] fp32, updated in place (the gradient points
+    may be None when b == 1).  Returns z [B, H, d] fp32."""
+    B, H, d, z, dev = _step_common("ttt_mlp_step", q, k, v, eta, pos,
+                                   dict(w1=w1, w2=w2, w1_gp=w1_gp, w2_gp=w2_gp), z)
+    hidden = w1.shape[-2]
+    for nm, t, shp in (("w1", w1, (B, H, hidden, d)), ("w2", w2, (B, H, d, hidden)),
+                       ("w1_gp", w1_gp, (B, H, hidden, d)), ("w2_gp", w2_gp, (B, H, d, hidden))):
+        if t is not None and tuple(t.shape) != shp:
+            raise ValueError(f"{nm} must be {list(shp)}")
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib().ttt_mlp_step(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w1), _ptr(w2),
+                                           _ptr(w1_gp), _ptr(w2_gp), _ptr(pos), B, H, d, hidden,
+                                           int(b), _dtype_code(q), _ptr(z), _stream(dev, stream)))
+    return z
+
+
 def ttt_mlp_fwd(q, k, v, eta, w1_0, w2_0, b: int, z=None, w1_out=None, w2_out=None, stream=None):
     """TTT-MLP forward scan, f(x) = W2 GELU(W1 x) (see include/ttt.h).
 

@@ -240,9 +240,51 @@ ttt_status_t linear_step_impl(const char* fn, const void* q, const void* k, cons
   return TTT_OK;
 }
 
+ttt_status_t mlp_step_impl(const void* q, const void* k, const void* v, const float* eta,
+                           float* w1, float* w2, float* w1_gp, float* w2_gp, const int32_t* pos,
+                           int32_t B, int32_t H, int32_t d, int32_t hidden, int32_t b,
+                           ttt_dtype_t dt, float* z, void* stream) {
+  static const char* fn = "ttt_mlp_step";
+  if (hidden < 0) return fail(TTT_ERR_SHAPE, "%s: negative hidden=%d", fn, hidden);
+  const int64_t units = (int64_t)B * H;
+  const int64_t es = dt == TTT_F32 ? 4 : 2;
+  const int64_t sb = units * hidden * d * 4;
+  const Range in[] = {rng("q", q, units * d * es), rng("k", k, units * d * es),
+                      rng("v", v, units * d * es), rng("eta", eta, units * 4)};
+  const Range out[] = {rng("z", z, units * d * 4), rng("w1", w1, sb), rng("w2", w2, sb),
+                       rng("w1_gp", w1_gp, sb), rng("w2_gp", w2_gp, sb)};
+  const bool optional[] = {false, false, false, b == 1, b == 1};
+  ttt_status_t st = check_step(fn, dt, B, H, d, b, in, 4, out, 5, optional);
+  if (st != TTT_OK) return st;
+  if (hidden != 256)
+    return fail(TTT_ERR_UNSUPPORTED, "%s: hidden=%d unsupported (only 256)", fn, hidden);
+  if (units == 0) return TTT_OK;
+  if ((!w1_gp || !w2_gp) && b != 1)
+    return fail(TTT_ERR_NULL, "%s: w1_gp / w2_gp are NULL (allowed only for b = 1)", fn);
+  if ((!w1_gp) != (!w2_gp))
+    return fail(TTT_ERR_NULL, "%s: pass both gradient points or neither", fn);
+  if (!pos) return fail(TTT_ERR_NULL, "%s: pos is NULL", fn);
+  if ((uintptr_t)pos & 3) return fail(TTT_ERR_ALIGN, "%s: pos is not 4-byte aligned", fn);
+  const Range rp = rng("pos", pos, (int64_t)B * 4);
+  for (int o = 0; o < 5; ++o)
+    if (overlap(out[o], rp)) return fail(TTT_ERR_ALIAS, "%s: %s overlaps input pos", fn, out[o].name);
+  ttt::StepArgs a{q, k, v, eta, w1, w1_gp, w2, w2_gp, pos, z, (int)units, H, b};
+  hipError_t e = ttt::launch_mlp_step(a, dt == TTT_F32, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return TTT_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+ttt_status_t ttt_mlp_step(const void* q, const void* k, const void* v, const float* eta,
+                          float* w1, float* w2, float* w1_gp, float* w2_gp, const int32_t* pos,
+                          int32_t B, int32_t H, int32_t d, int32_t hidden, int32_t b,
+                          ttt_dtype_t qkv_dtype, float* z, void* stream) {
+  return mlp_step_impl(q, k, v, eta, w1, w2, w1_gp, w2_gp, pos, B, H, d, hidden, b, qkv_dtype, z,
+                       stream);
+}
 
 ttt_status_t ttt_linear_step(const void* q, const void* k, const void* v, const float* eta,
                              float* w, float* w_gp, const int32_t* pos, int32_t B, int32_t H,

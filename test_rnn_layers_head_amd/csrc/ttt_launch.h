@@ -71,6 +71,8 @@ hipError_t launch_mlp(const MlpArgs& a, bool f32in, hipStream_t s);
 hipError_t launch_linear_step(const StepArgs& a, bool f32in, hipStream_t s);
 hipError_t launch_linear_ln_step(const StepArgs& a, const float* gamma, const float* beta,
                                  float eps, bool f32in, hipStream_t s);
+// TTT-MLP, hidden = 256: w, w_gp = W1 [B][H][256][64]; w2, w2_gp = W2 [B][H][64][256].
+hipError_t launch_mlp_step(const StepArgs& a, bool f32in, hipStream_t s);
 hipError_t launch_copy_state(const float* src, int per_unit, int units, int H, int n,
                              float* dst, hipStream_t s);
 

@@ -62,25 +62,6 @@ __device__ __forceinline__ bf16x8 row_chunk(const char* tile, int r, int h, int 
   return *(const bf16x8*)(tile + swz_chunk(r, 4 * h + g));
 }
 
-// GELU and its derivative.  Phi(x) = 1/2 (1 + erf(x / sqrt 2)); erf from
-// Abramowitz & Stegun 7.1.26: erf(y) = 1 - (a1 t + .. + a5 t^5) exp(-y^2),
-// t = 1 / (1 + p y), y >= 0.  exp(-y^2) = exp(-x^2 / 2) is shared with the
-// normal density phi(x) = exp(-x^2 / 2) / sqrt(2 pi) of GELU' = Phi + x phi.
-struct GeluOut {
-  float g, dg;
-};
-__device__ __forceinline__ GeluOut gelu_and_grad(float x) {
-  const float p = 0.3275911f, a1 = 0.254829592f, a2 = -0.284496736f, a3 = 1.421413741f,
-              a4 = -1.453152027f, a5 = 1.061405429f;
-  const float y = fabsf(x) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(p, y, 1.f));
-  const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, a5, a4), a3), a2), a1);
-  const float e = __builtin_amdgcn_exp2f(x * x * -0.72134752044448170f);  // exp(-x^2/2)
-  const float q = 0.5f * poly * e;                                         // 1 - Phi(|x|)
-  const float phi_cdf = x >= 0.f ? 1.f - q : q;
-  return GeluOut{x * phi_cdf, fmaf(x, e * 0.39894228040143268f, phi_cdf)};
-}
-
 struct YOps {
   bf16x8 hh, l0;
 };

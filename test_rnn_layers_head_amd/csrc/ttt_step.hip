@@ -224,6 +224,138 @@ __global__ void __launch_bounds__(STEP_THREADS) linear_ln_step_kernel(StepArgs a
   if (s == 0) a.z[vo + i] = qi + fmaf(gi, (o - mo) * ro, be);
 }
 
+// ------------------------------------------------------------------ TTT-MLP
+// f(x) = W2 GELU(W1 x), hidden width 256 (§4.4).  At the gradient point:
+//   a = W1g k, x = GELU(a), e = 2 (W2g x - v), delta = (W2g^T e) * GELU'(a);
+// W2 -= eta e x^T, W1 -= eta delta k^T; z = W2 GELU(W1 q).
+// Two thread mappings, one workgroup barrier between phases: "hidden"
+// (thread h = hidden unit h: row h of W1, column h of W2) and "output"
+// (thread t = 4i + s: row i of W2, hidden units 64s .. 64s+63).  A reduction
+// over the hidden units thus becomes an in-thread sum plus a quad sum, and
+// one over the outputs an in-thread sum.  Within a call W1/W2 are read
+// before they are written, by the same thread or across a barrier.
+// GELU(x) = x Phi(x) with erf from Abramowitz & Stegun 7.1.26 (|err| <=
+// 1.5e-7), the same function as the MLP scan's (gelu_and_grad).
+constexpr int MLP_HID = 256;
+
+template <bool F32IN>
+__global__ void __launch_bounds__(STEP_THREADS) mlp_step_kernel(StepArgs a) {
+  __shared__ float sk[64], sq[64], sx[MLP_HID], se[64], sh[MLP_HID];
+  const int unit = blockIdx.x, t = threadIdx.x;
+  const int bi = unit / a.H;
+  const size_t vo = (size_t)unit * 64;
+  const size_t so = (size_t)unit * (MLP_HID * 64);
+  const bool start = minibatch_pos(a.pos[bi], a.b) == 0;  // always when b == 1
+  const bool copy_gp = start && a.w_gp != nullptr;  // gradient points may be NULL for b == 1
+  const float eta = a.eta[unit];
+  if (t < 64) {
+    sk[t] = load1<F32IN>(a.k, vo + t);
+    sq[t] = load1<F32IN>(a.q, vo + t);
+  }
+  __syncthreads();
+
+  // ---- phase 1 (hidden mapping): a_h = W1g[h] . k
+  const int h = t;
+  float4 w1[16];
+  {
+    const float4* src = (const float4*)(a.w + so + (size_t)h * 64);
+    const float4* gsrc = start ? src : (const float4*)(a.w_gp + so + (size_t)h * 64);
+    float4* gdst = copy_gp ? (float4*)(a.w_gp + so + (size_t)h * 64) : nullptr;
+#pragma unroll
+    for (int n = 0; n < 16; ++n) w1[n] = src[n];
+    float ak = 0.f;
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+      const float4 g = start ? w1[n] : gsrc[n];
+      if (copy_gp) gdst[n] = g;
+      ak = fmaf(g.x, sk[4 * n], ak);
+      ak = fmaf(g.y, sk[4 * n + 1], ak);
+      ak = fmaf(g.z, sk[4 * n + 2], ak);
+      ak = fmaf(g.w, sk[4 * n + 3], ak);
+    }
+    const GeluOut ga = gelu_and_grad(ak);
+    sx[h] = ga.g;
+    sh[h] = ga.dg;  // GELU'(a_h), read back by the same thread in phase 3
+  }
+  __syncthreads();
+
+  // ---- phase 2 (output mapping): y_i = W2g[i] . x, e_i = 2 (y_i - v_i)
+  const int i = t >> 2, s = t & 3;
+  const size_t r2 = so + (size_t)i * MLP_HID + 64 * s;  // W2[i][64s ..]
+  {
+    const float4* src = (const float4*)((start ? a.w2 : a.w2_gp) + r2);
+    float4* gdst = copy_gp ? (float4*)(a.w2_gp + r2) : nullptr;
+    float y = 0.f;
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+      const float4 g = src[n];
+      if (copy_gp) gdst[n] = g;
+      const int u = 64 * s + 4 * n;
+      y = fmaf(g.x, sx[u], y);
+      y = fmaf(g.y, sx[u + 1], y);
+      y = fmaf(g.z, sx[u + 2], y);
+      y = fmaf(g.w, sx[u + 3], y);
+    }
+    y = quad_sum(y);
+    if (s == 0) se[i] = 2.f * (y - load1<F32IN>(a.v, vo + i));
+  }
+  __syncthreads();
+
+  // ---- phase 3 (hidden mapping): delta_h = (W2g[:, h] . e) GELU'(a_h);
+  // W1[h] -= eta delta_h k; hq_h = GELU(W1[h] . q)
+  {
+    const float* col = (start ? a.w2 : a.w2_gp) + so + h;
+    float bp = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < 64; ++r) bp = fmaf(col[(size_t)r * MLP_HID], se[r], bp);
+    const float nd = -eta * bp * sh[h];
+    float aq = 0.f;
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+      float4 w = w1[n];
+      w.x = fmaf(nd, sk[4 * n], w.x);
+      w.y = fmaf(nd, sk[4 * n + 1], w.y);
+      w.z = fmaf(nd, sk[4 * n + 2], w.z);
+      w.w = fmaf(nd, sk[4 * n + 3], w.w);
+      w1[n] = w;
+      aq = fmaf(w.x, sq[4 * n], aq);
+      aq = fmaf(w.y, sq[4 * n + 1], aq);
+      aq = fmaf(w.z, sq[4 * n + 2], aq);
+      aq = fmaf(w.w, sq[4 * n + 3], aq);
+    }
+    float4* dst = (float4*)(a.w + so + (size_t)h * 64);
+#pragma unroll
+    for (int n = 0; n < 16; ++n) dst[n] = w1[n];
+    const float hq = gelu_and_grad(aq).g;
+    __syncthreads();  // every thread has read its GELU'(a_h) from sh
+    sh[h] = hq;
+  }
+  __syncthreads();
+
+  // ---- phase 4 (output mapping): W2[i] -= eta e_i x; z_i = W2[i] . hq
+  {
+    float4* row = (float4*)(a.w2 + r2);
+    const float ne = -eta * se[i];
+    float z = 0.f;
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+      float4 w = row[n];
+      const int u = 64 * s + 4 * n;
+      w.x = fmaf(ne, sx[u], w.x);
+      w.y = fmaf(ne, sx[u + 1], w.y);
+      w.z = fmaf(ne, sx[u + 2], w.z);
+      w.w = fmaf(ne, sx[u + 3], w.w);
+      row[n] = w;
+      z = fmaf(w.x, sh[u], z);
+      z = fmaf(w.y, sh[u + 1], z);
+      z = fmaf(w.z, sh[u + 2], z);
+      z = fmaf(w.w, sh[u + 3], z);
+    }
+    z = quad_sum(z);
+    if (s == 0) a.z[vo + i] = z;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_linear_step(const StepArgs& a, bool f32in, hipStream_t s) {
@@ -242,6 +374,14 @@ hipError_t launch_linear_ln_step(const StepArgs& a, const float* gamma, const fl
   else
     hipLaunchKernelGGL(linear_ln_step_kernel<false>, dim3(a.units), dim3(STEP_THREADS), 0, s, a,
                        gamma, beta, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_mlp_step(const StepArgs& a, bool f32in, hipStream_t s) {
+  if (f32in)
+    hipLaunchKernelGGL(mlp_step_kernel<true>, dim3(a.units), dim3(STEP_THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL(mlp_step_kernel<false>, dim3(a.units), dim3(STEP_THREADS), 0, s, a);
   return hipGetLastError();
 }
 

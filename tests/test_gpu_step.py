@@ -179,3 +179,63 @@ def test_step_rejected_arguments():
         ttt_linear_ln_step(dev["q"], dev["k"], dev["v"], dev["eta"], w, wg, pos, g, g, 0.0, 16)
     with pytest.raises(TTTError, match="TTT_ERR_UNSUPPORTED"):
         ttt_linear_step(dev["q"], dev["k"], dev["v"], dev["eta"], w, wg, pos, 0)
+
+
+def mlp_states(B, H, seed, gp=True):
+    rng = np.random.default_rng(seed)
+    # W1 ~ N(0, 1) makes W1 k ~ N(0, 1) for |k| ~ 1, so GELU works away from 0
+    mk = lambda shape, sc: (rng.standard_normal(shape) * sc).astype(np.float32)
+    st = [mk((B, H, 256, 64), 1.0), mk((B, H, 64, 256), 1 / 16)]
+    if gp:
+        st += [mk((B, H, 256, 64), 1.0), mk((B, H, 64, 256), 1 / 16)]
+    return st
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("b", [1, 4, 32])
+def test_mlp_step_parity(dtype, b):
+    from test_rnn_layers_head_amd import ttt_mlp_step
+    B, H = 3, 2
+    host, dev = token_inputs(B, H, dtype, seed=570 + b)
+    w1, w2, w1g, w2g = mlp_states(B, H, seed=571)
+    pos = np.array([0, 9, 32], dtype=np.int32)
+    d = [gu.f32(a) for a in (w1, w2, w1g, w2g)]
+    z = ttt_mlp_step(dev["q"], dev["k"], dev["v"], dev["eta"], *d, torch.from_numpy(pos).cuda(), b)
+    torch.cuda.synchronize()
+    ref = oracle.mlp_step(host["q"], host["k"], host["v"], host["eta"], w1, w2, w1g, w2g, pos, b)
+    close(z.cpu().numpy(), ref[0], "z")
+    for nm, got, want in zip(("w1", "w2", "w1_gp", "w2_gp"), d, ref[1:]):
+        close(got.cpu().numpy(), want, nm)
+
+
+def test_mlp_step_b1_without_gradient_points():
+    from test_rnn_layers_head_amd import ttt_mlp_step
+    B, H = 2, 2
+    host, dev = token_inputs(B, H, "bf16", seed=580)
+    w1, w2 = mlp_states(B, H, seed=581, gp=False)
+    pos = np.array([4, 11], dtype=np.int32)
+    d1, d2 = gu.f32(w1), gu.f32(w2)
+    z = ttt_mlp_step(dev["q"], dev["k"], dev["v"], dev["eta"], d1, d2, None, None,
+                     torch.from_numpy(pos).cuda(), 1)
+    torch.cuda.synchronize()
+    ref = oracle.mlp_step(host["q"], host["k"], host["v"], host["eta"], w1, w2, np.zeros_like(w1),
+                          np.zeros_like(w2), pos, 1)
+    close(z.cpu().numpy(), ref[0], "z")
+    close(d1.cpu().numpy(), ref[1], "w1")
+    close(d2.cpu().numpy(), ref[2], "w2")
+
+
+@pytest.mark.parametrize("b", [4, 16])
+def test_mlp_steps_replay_the_scan(b):
+    from test_rnn_layers_head_amd import ttt_mlp_step
+    x = inputs.make_inputs(inputs.Workload("replay-mlp", "mlp", B=2, H=2, T=24, hidden=256,
+                                           seed=590 + b))
+    w1 = gu.f32(np.broadcast_to(x.w1[None], (2, 2, 256, 64)))
+    w2 = gu.f32(np.broadcast_to(x.w2[None], (2, 2, 64, 256)))
+    w1g, w2g = torch.zeros_like(w1), torch.zeros_like(w2)
+    z = _replay(x, b, lambda q, k, v, e, p: ttt_mlp_step(q, k, v, e, w1, w2, w1g, w2g, p, b), 24)
+    torch.cuda.synchronize()
+    zr, w1r, w2r = oracle.mlp(x.q, x.k, x.v, x.eta, x.w1, x.w2, b)
+    close(z, zr, "z")
+    close(w1.cpu().numpy(), w1r, "w1_T")
+    close(w2.cpu().numpy(), w2r, "w2_T")
