@@ -14,7 +14,8 @@ kernel (algorithmic bytes / measured kernel time vs 8 TB/s HBM), the fp64
 oracle timed on the host cores as a baseline, and (unless --no-extras) the
 other workloads: the b sweep, the 125M and long-context TTT-Linear shapes,
 TTT-Linear with the LayerNorm + residual inner model (1.3B and 125M shapes),
-TTT-MLP, and a streaming-copy bandwidth reference.
+TTT-MLP, the one-token decode steps of the three models, and a
+streaming-copy bandwidth reference.
 
 --pmc-calibrate additionally launches the streaming copy kernel on a known
 byte count, so that a hardware-counter run of this script can scale the
@@ -247,6 +248,86 @@ def mlp_case(wl, b, steps, warmup):
     }
 
 
+# Decode steps: one token for every (batch, head) unit per call, the states
+# resident in HBM.  Shapes: the 1.3B layer (H = 32) and the 125M one
+# (H = 12, TTT-MLP) at a serving batch of 64 sequences, b = 16, each sequence
+# at its own (seeded) position in [0, 8192).
+DECODE_CASES = (("linear", 64, 32), ("linear_ln", 64, 32), ("mlp", 64, 12))
+
+
+def decode_alg_bytes(kind, B, H, pos, b) -> int:
+    """State traffic of one step: read W, write W, and read the gradient
+    point (or write it, at the first token of a mini-batch); plus the
+    token's q, k, v (bf16), eta, pos and z."""
+    st = 4 * 64 * 64 if kind != "mlp" else 2 * 4 * 256 * 64
+    per_unit = 3 * st + 3 * 64 * 2 + 4 + 64 * 4
+    extra = 2 * H * 64 * 4 if kind == "linear_ln" else 0
+    return B * H * per_unit + B * 4 + extra
+
+
+def decode_case(kind, B, H, steps, warmup, b=16, seed=11):
+    import torch
+    from test_rnn_layers_head_amd import ttt_linear_ln_step, ttt_linear_step, ttt_mlp_step
+    g = torch.Generator().manual_seed(seed)
+    bf = lambda *shape: (torch.randn(*shape, generator=g) / 8).to(torch.bfloat16).cuda()
+    q, k, v = bf(B, H, 64), bf(B, H, 64), bf(B, H, 64)
+    eta = (0.02 * torch.sigmoid(torch.randn(B, H, generator=g))).cuda()
+    pos = torch.randint(0, 8192, (B,), generator=g, dtype=torch.int32).cuda()
+    z = torch.empty(B, H, 64, device="cuda")
+    if kind == "mlp":
+        w1 = (torch.randn(B, H, 256, 64, generator=g) * 0.02).cuda()
+        w2 = (torch.randn(B, H, 64, 256, generator=g) * 0.02).cuda()
+        w1g, w2g = w1.clone(), w2.clone()
+        launch = lambda: ttt_mlp_step(q, k, v, eta, w1, w2, w1g, w2g, pos, b, z=z)
+    else:
+        w = (torch.randn(B, H, 64, 64, generator=g) / 8).cuda()
+        wg = w.clone()
+        if kind == "linear":
+            launch = lambda: ttt_linear_step(q, k, v, eta, w, wg, pos, b, z=z)
+        else:
+            gam = (1 + 0.2 * torch.randn(H, 64, generator=g)).cuda()
+            bet = (0.1 * torch.randn(H, 64, generator=g)).cuda()
+            launch = lambda: ttt_linear_ln_step(q, k, v, eta, w, wg, pos, gam, bet, 1e-5, b, z=z)
+    # One launch is a few microseconds of GPU work, less than the host needs
+    # to issue it from Python, so the steps are timed as a captured graph of
+    # GRAPH_STEPS launches (the C ABI enqueues on the capturing stream).
+    GRAPH_STEPS = 20
+    for _ in range(3):
+        launch()  # first launches outside the capture (code load)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(GRAPH_STEPS):
+            launch()
+    one = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(one):
+        launch()
+    for _ in range(max(1, warmup // GRAPH_STEPS)):
+        graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // GRAPH_STEPS)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    kmean = e0.elapsed_time(e1) * 1e3 / (reps * GRAPH_STEPS)
+    # cold: one step after a 512 MiB write that evicts the MALL and the L2s
+    flushed = flushed_launches(one.replay, 10)
+    assert torch.isfinite(z).all().item()
+    byts = decode_alg_bytes(kind, B, H, pos, b)
+    return {"kind": kind, "B": B, "H": H, "b": b, "us_per_step": kmean,
+            "us_per_step_flushed": flushed, "tokens_per_s": B / (kmean * 1e-6),
+            "token_heads_per_s": B * H / (kmean * 1e-6), "alg_bytes": byts,
+            "hbm_GBps": byts / (kmean * 1e-6) / 1e9,
+            "hbm_frac": byts / (kmean * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "hbm_frac_flushed": byts / (flushed["median"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "timing": f"graph of {GRAPH_STEPS} steps replayed {reps} times (states resident "
+                      "in HBM, and in the 256 MB MALL when they fit); flushed: single steps "
+                      "after a 512 MiB cache flush"}
+
+
 def stream_copy_GBps(nbytes=1 << 30, reps=10):
     import torch
     from test_rnn_layers_head_amd import bench_copy
@@ -467,6 +548,9 @@ def main():
             w6 = inputs.workload(wid)
             log(f"[bench] {w6.name}")
             extras[w6.name] = ln_case(w6, 16, max(5, args.steps // 2), EXTRA_WARMUP)
+        for kind, B, H in DECODE_CASES:
+            log(f"[bench] decode step {kind} B={B} H={H}")
+            extras[f"decode-{kind}-B{B}-H{H}"] = decode_case(kind, B, H, 100, 200)
         w4 = inputs.workload(4)
         log(f"[bench] {w4.name}")
         try:
