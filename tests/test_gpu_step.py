@@ -239,3 +239,37 @@ def test_mlp_steps_replay_the_scan(b):
     close(z, zr, "z")
     close(w1.cpu().numpy(), w1r, "w1_T")
     close(w2.cpu().numpy(), w2r, "w2_T")
+
+
+def test_graph_captured_steps_match_eager():
+    # bench.py times the steps as a captured graph: every replay of the
+    # captured step must give exactly what the same step gives eagerly
+    # (eager work and synchronisations between the replays).
+    B, H = 4, 8
+    host, dev = token_inputs(B, H, "bf16", seed=600)
+    w0, wg0 = states(B, H, 0.05, seed=601)
+    pos_g = torch.tensor([0, 3, 16, 21], dtype=torch.int32, device="cuda")
+    w, wg = gu.f32(w0), gu.f32(wg0)          # states advanced by the graph
+    we, wge = gu.f32(w0), gu.f32(wg0)        # the same states advanced eagerly
+    z = torch.empty(B, H, 64, device="cuda")
+    ttt_linear_step(dev["q"], dev["k"], dev["v"], dev["eta"], we.clone(), wge.clone(), pos_g, 16)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            ttt_linear_step(dev["q"], dev["k"], dev["v"], dev["eta"], w, wg, pos_g, 16, z=z)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    w.copy_(gu.f32(w0))
+    wg.copy_(gu.f32(wg0))
+    for rep in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        ze = ttt_linear_step(dev["q"], dev["k"], dev["v"], dev["eta"], we, wge, pos_g, 16)
+        scratch = torch.randn(1 << 16, device="cuda").sum()  # unrelated eager work
+        torch.cuda.synchronize()
+        assert torch.equal(z, ze), rep
+        assert torch.equal(w, we) and torch.equal(wg, wge), rep
+        assert torch.isfinite(scratch)
