@@ -58,6 +58,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.ttt_oracle_linear_ln_step.restype = I
     lib.ttt_oracle_mlp_step.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, ip, L, L, L, L, L, dp]
     lib.ttt_oracle_mlp_step.restype = I
+    lib.ttt_oracle_linear_bwd.argtypes = [dp, dp, dp, dp, dp, I, L, L, L, L, L, dp, dp, dp, dp, dp,
+                                          dp, dp]
+    lib.ttt_oracle_linear_bwd.restype = I
     return lib
 
 
@@ -231,3 +234,27 @@ def mlp_step(q, k, v, eta, w1, w2, w1g, w2g, pos, b: int, lib=None):
     if rc != 0:
         raise RuntimeError(f"ttt_oracle_mlp_step failed with status {rc}")
     return z, w1, w2, w1g, w2g
+
+
+def linear_bwd(q, k, v, eta, w0, b: int, dz, dw_T=None, lib=None):
+    """Backward of the TTT-Linear scan (reverse pass of the primal form):
+    given dz [B, H, T, d] (adjoint of Z) and optionally dw_T [B, H, d, d]
+    (adjoint of the final state), returns (dq, dk, dv, deta, dw0) with dw0
+    per unit [B, H, d, d] (sum over the batch for a shared initial state).
+    """
+    q, k, v, eta, w0, dz = map(_f64, (q, k, v, eta, w0, dz))
+    B, H, T, d = q.shape
+    per_batch = 1 if w0.ndim == 4 else 0
+    assert w0.shape == ((B, H, d, d) if per_batch else (H, d, d)) and dz.shape == q.shape
+    dwT = None if dw_T is None else _f64(dw_T)
+    dq, dk, dv = (np.zeros((B, H, T, d)) for _ in range(3))
+    deta = np.zeros((B, H, T))
+    dw0 = np.zeros((B, H, d, d))
+    lib = lib or load()
+    rc = lib.ttt_oracle_linear_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w0), per_batch,
+                                   B, H, T, d, int(b), _ptr(dz),
+                                   None if dwT is None else _ptr(dwT), _ptr(dq), _ptr(dk),
+                                   _ptr(dv), _ptr(deta), _ptr(dw0))
+    if rc != 0:
+        raise RuntimeError(f"ttt_oracle_linear_bwd failed with status {rc}")
+    return dq, dk, dv, deta, dw0

@@ -37,6 +37,13 @@
  * Wg = W.  Then the token's gradient is taken at Wg, W takes the step, and the
  * output is read from the updated W: exactly one iteration of the scans above.
  *
+ * Backward (§6.12: training differentiates through the inner loop): the
+ * reverse pass of the TTT-Linear primal recurrence above, token by token in
+ * reverse, given the adjoints of Z and of the final state.  It keeps every
+ * intermediate state, which is fine at test sizes (the pages' kernels keep
+ * one per mini-batch and recompute; that is a memory trade, not another
+ * result).
+ *
  * The loss is the squared L2 norm summed over output components, so its
  * gradient carries the factor 2 (§3.6 linear derivation: G_t = 2(W0 x - x)x^T).
  * GELU is the exact erf form x * Phi(x).  Mini-batches start at token 0, b,
@@ -485,5 +492,119 @@ int ttt_oracle_mlp_step(const double *q, const double *k, const double *v,
     }
   }
   free(sc);
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* TTT-Linear backward: reverse pass of the primal recurrence.         */
+/* ------------------------------------------------------------------ */
+/* Forward, one unit (as linear_unit), keeping every state:
+ *   Wst[0] = W0, Wst[t+1] = Wst[t] - eta_t g_t k_t^T,
+ *   g_t = 2 (Wst[m0] k_t - v_t) with m0 the first token of t's mini-batch,
+ *   z_t = Wst[t+1] q_t.
+ * Reverse, with A the adjoint of the state after token t (starting from the
+ * adjoint of W_T) and Ag the adjoint collected for the current mini-batch's
+ * gradient point:
+ *   dq_t = Wst[t+1]^T dz_t,            A += dz_t q_t^T
+ *   gb = -eta_t A k_t                  (adjoint of g_t)
+ *   dk_t = -eta_t A^T g_t + 2 Wst[m0]^T gb,  deta_t = -g_t^T A k_t,
+ *   dv_t = -2 gb,  Ag += 2 gb k_t^T
+ *   at t = m0 the gradient point is Wst[t]: A += Ag, Ag = 0.
+ * A then carries over unchanged to the state before token t. */
+static int linear_bwd_unit(const double *q, const double *k, const double *v,
+                           const double *eta, const double *w0, long T, long d,
+                           long b, const double *dz, const double *dwT, double *dq,
+                           double *dk, double *dv, double *deta, double *dw0) {
+  const size_t dd = (size_t)(d * d);
+  double *Wst = (double *)malloc(sizeof(double) * dd * (size_t)(T + 1));
+  double *Ag = (double *)calloc(dd, sizeof(double));
+  double *g = (double *)malloc(sizeof(double) * (size_t)(3 * d));
+  if (!Wst || !Ag || !g) { free(Wst); free(Ag); free(g); return 1; }
+  double *gb = g + d, *Ak = g + 2 * d;
+  memcpy(Wst, w0, sizeof(double) * dd);
+  for (long t = 0; t < T; ++t) {
+    const long m0 = (t / b) * b;
+    const double *Wg = Wst + (size_t)m0 * dd, *Wp = Wst + (size_t)t * dd;
+    double *Wn = Wst + (size_t)(t + 1) * dd;
+    const double *kt = k + t * d, *vt = v + t * d;
+    for (long i = 0; i < d; ++i) {
+      double pk = 0.0;
+      for (long j = 0; j < d; ++j) pk += Wg[i * d + j] * kt[j];
+      g[i] = 2.0 * (pk - vt[i]);
+    }
+    for (long i = 0; i < d; ++i)
+      for (long j = 0; j < d; ++j) Wn[i * d + j] = Wp[i * d + j] - eta[t] * g[i] * kt[j];
+  }
+  double *A = dw0; /* the running adjoint lives in the output */
+  if (dwT) memcpy(A, dwT, sizeof(double) * dd);
+  else memset(A, 0, sizeof(double) * dd);
+  for (long t = T - 1; t >= 0; --t) {
+    const long m0 = (t / b) * b;
+    const double *Wg = Wst + (size_t)m0 * dd, *Wn = Wst + (size_t)(t + 1) * dd;
+    const double *kt = k + t * d, *vt = v + t * d, *qt = q + t * d, *zt = dz + t * d;
+    /* z_t = W_t q_t */
+    for (long j = 0; j < d; ++j) {
+      double s = 0.0;
+      for (long i = 0; i < d; ++i) s += Wn[i * d + j] * zt[i];
+      dq[t * d + j] = s;
+    }
+    for (long i = 0; i < d; ++i)
+      for (long j = 0; j < d; ++j) A[i * d + j] += zt[i] * qt[j];
+    /* W_t = W_{t-1} - eta_t g_t k_t^T */
+    for (long i = 0; i < d; ++i) {
+      double pk = 0.0;
+      for (long j = 0; j < d; ++j) pk += Wg[i * d + j] * kt[j];
+      g[i] = 2.0 * (pk - vt[i]);
+    }
+    double de = 0.0;
+    for (long i = 0; i < d; ++i) {
+      double s = 0.0;
+      for (long j = 0; j < d; ++j) s += A[i * d + j] * kt[j];
+      Ak[i] = s;
+      gb[i] = -eta[t] * s;
+      de -= g[i] * s;
+    }
+    deta[t] = de;
+    for (long j = 0; j < d; ++j) {
+      double s1 = 0.0, s2 = 0.0;
+      for (long i = 0; i < d; ++i) {
+        s1 += A[i * d + j] * g[i];
+        s2 += Wg[i * d + j] * gb[i];
+      }
+      dk[t * d + j] = -eta[t] * s1 + 2.0 * s2;
+    }
+    /* g_t = 2 (W_{t'} k_t - v_t) */
+    for (long i = 0; i < d; ++i) {
+      dv[t * d + i] = -2.0 * gb[i];
+      for (long j = 0; j < d; ++j) Ag[i * d + j] += 2.0 * gb[i] * kt[j];
+    }
+    if (t == m0) { /* the gradient point of this mini-batch is the state before t */
+      for (size_t e = 0; e < dd; ++e) {
+        A[e] += Ag[e];
+        Ag[e] = 0.0;
+      }
+    }
+  }
+  free(Wst);
+  free(Ag);
+  free(g);
+  return 0;
+}
+
+int ttt_oracle_linear_bwd(const double *q, const double *k, const double *v,
+                          const double *eta, const double *w0, int w0_per_batch,
+                          long B, long H, long T, long d, long b, const double *dz,
+                          const double *dwT, double *dq, double *dk, double *dv,
+                          double *deta, double *dw0) {
+  if (B < 0 || H < 0 || T < 0 || d <= 0 || b <= 0) return 2;
+  for (long u = 0; u < B * H; ++u) {
+    const long wsel = w0_per_batch ? u : u % H;
+    const size_t so = (size_t)u * (size_t)(T * d);
+    int rc = linear_bwd_unit(q + so, k + so, v + so, eta + (size_t)u * (size_t)T,
+                             w0 + (size_t)wsel * (size_t)(d * d), T, d, b, dz + so,
+                             dwT ? dwT + (size_t)u * (size_t)(d * d) : NULL, dq + so, dk + so,
+                             dv + so, deta + (size_t)u * (size_t)T, dw0 + (size_t)u * (size_t)(d * d));
+    if (rc) return rc;
+  }
   return 0;
 }

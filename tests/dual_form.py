@@ -138,3 +138,57 @@ def linear_ln(q, k, v, eta, w0, gamma, beta, eps, b):
             Z[bi, h], WT[bi, h] = linear_ln_unit(q[bi, h], k[bi, h], v[bi, h], eta[bi, h], w,
                                                  gamma[h], beta[h], eps, b)
     return Z, WT
+
+
+def linear_bwd_unit(q, k, v, eta, w0, b, dz, dwT):
+    """Adjoint of the dual-form recurrence, one unit, mini-batch by
+    mini-batch in reverse.  Per mini-batch (columns are tokens, D = diag eta):
+      E = W K - V, G = 2 E D, A = triu(K^T Q), Z = W Q - G A, W' = W - G K^T.
+    Given Zb (adjoint of Z) and Wb' (adjoint of W'):
+      Gb = -Zb A^T - Wb' K, Eb = 2 Gb D, Ab = triu(-G^T Zb),
+      Wb = Wb' + Zb Q^T + Eb K^T, Qb = W^T Zb + K Ab,
+      Kb = W^T Eb + Q Ab^T - Wb'^T G, Vb = -Eb, etab_t = sum_i Gb[i,t] 2 E[i,t].
+    Returns (dq, dk, dv, deta, dw0)."""
+    T, d = q.shape
+    Ws = [np.array(w0, dtype=np.float64)]
+    blocks = list(range(0, T, b))
+    for m0 in blocks:
+        m1 = min(T, m0 + b)
+        XK, XV = k[m0:m1].T, v[m0:m1].T
+        G = 2.0 * (Ws[-1] @ XK - XV) * eta[m0:m1][None, :]
+        Ws.append(Ws[-1] - G @ XK.T)
+    dq, dk, dv = (np.zeros((T, d)) for _ in range(3))
+    deta = np.zeros(T)
+    Wb = np.zeros((d, d)) if dwT is None else np.array(dwT, dtype=np.float64)
+    for jb in reversed(range(len(blocks))):
+        m0 = blocks[jb]
+        m1 = min(T, m0 + b)
+        W = Ws[jb]
+        XK, XV, XQ = k[m0:m1].T, v[m0:m1].T, q[m0:m1].T
+        e = eta[m0:m1]
+        E = W @ XK - XV
+        G = 2.0 * E * e[None, :]
+        A = np.triu(XK.T @ XQ)
+        Zb = dz[m0:m1].T
+        Gb = -Zb @ A.T - Wb @ XK
+        Eb = 2.0 * Gb * e[None, :]
+        Ab = np.triu(-G.T @ Zb)
+        dq[m0:m1] = (W.T @ Zb + XK @ Ab).T
+        dk[m0:m1] = (W.T @ Eb + XQ @ Ab.T - Wb.T @ G).T
+        dv[m0:m1] = (-Eb).T
+        deta[m0:m1] = np.sum(Gb * 2.0 * E, axis=0)
+        Wb = Wb + Zb @ XQ.T + Eb @ XK.T
+    return dq, dk, dv, deta, Wb
+
+
+def linear_bwd(q, k, v, eta, w0, b, dz, dwT=None):
+    B, H, T, d = q.shape
+    out = [np.zeros((B, H, T, d)) for _ in range(3)] + [np.zeros((B, H, T)), np.zeros((B, H, d, d))]
+    for bi in range(B):
+        for h in range(H):
+            w = w0[bi, h] if w0.ndim == 4 else w0[h]
+            r = linear_bwd_unit(q[bi, h], k[bi, h], v[bi, h], eta[bi, h], w, b, dz[bi, h],
+                                None if dwT is None else dwT[bi, h])
+            for o, x in zip(out, r):
+                o[bi, h] = x
+    return tuple(out)

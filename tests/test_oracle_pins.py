@@ -417,6 +417,67 @@ def pin_step_golden_scalar_examples(lib):
         assert np.array_equal(w.reshape(d, d), np.asarray(c["w_T"])), c["name"]
 
 
+# ---- backward of the TTT-Linear scan (§6.12: the outer loop differentiates
+# through the inner one)
+
+def _bwd_case(rng, B, H, T, d, per_batch=False):
+    q, k, v, eta, w0 = rand_linear(rng, B, H, T, d, eta_scale=0.4, w_scale=0.3,
+                                   per_batch=per_batch)
+    dz = rng.standard_normal((B, H, T, d))
+    dwT = rng.standard_normal((B, H, d, d))
+    return q, k, v, eta, w0, dz, dwT
+
+
+def pin_linear_bwd_finite_differences(lib):
+    # L = <dz, Z> + <dwT, W_T>; the backward must give its gradient: compared
+    # with central differences of the forward oracle along random directions
+    rng = np.random.default_rng(61)
+    for (T, b) in [(11, 3), (9, 1), (12, 16), (13, 4)]:
+        B, H, d = 1, 2, 4
+        q, k, v, eta, w0, dz, dwT = _bwd_case(rng, B, H, T, d)
+        grads = oracle.linear_bwd(q, k, v, eta, w0, b, dz, dwT, lib=lib)
+        base = dict(q=q, k=k, v=v, eta=eta, w0=w0)
+
+        def L(**kw):
+            a = dict(base, **kw)
+            z, w = oracle.linear(a["q"], a["k"], a["v"], a["eta"], a["w0"], b, lib=lib)
+            return float(np.sum(dz * z) + np.sum(dwT * w))
+        h = 1e-5
+        for name, g in zip(("q", "k", "v", "eta"), grads[:4]):
+            u = rng.standard_normal(base[name].shape)
+            fd = (L(**{name: base[name] + h * u}) - L(**{name: base[name] - h * u})) / (2 * h)
+            assert abs(fd - np.sum(g * u)) <= 1e-7 * max(1.0, abs(fd)), (name, T, b, fd, np.sum(g * u))
+        u = rng.standard_normal(w0.shape)  # shared initial state: the gradient sums over the batch
+        fd = (L(w0=w0 + h * u) - L(w0=w0 - h * u)) / (2 * h)
+        assert abs(fd - np.sum(grads[4].sum(axis=0) * u)) <= 1e-7 * max(1.0, abs(fd)), ("w0", T, b)
+
+
+def pin_linear_bwd_equals_dual_form_adjoint(lib):
+    rng = np.random.default_rng(62)
+    for (T, b, pb) in [(37, 4, False), (32, 16, True), (20, 1, False), (19, 48, False)]:
+        q, k, v, eta, w0, dz, dwT = _bwd_case(rng, 2, 2, T, 6, per_batch=pb)
+        a = oracle.linear_bwd(q, k, v, eta, w0, b, dz, dwT, lib=lib)
+        r = dual_form.linear_bwd(q, k, v, eta, w0, b, dz, dwT)
+        for name, x, y in zip(("dq", "dk", "dv", "deta", "dw0"), a, r):
+            assert rel(x, y) < 1e-11, (name, T, b, rel(x, y))
+        a0 = oracle.linear_bwd(q, k, v, eta, w0, b, dz, None, lib=lib)
+        r0 = dual_form.linear_bwd(q, k, v, eta, w0, b, dz, None)
+        assert all(rel(x, y) < 1e-11 for x, y in zip(a0, r0)), (T, b)
+
+
+def pin_linear_bwd_eta_zero(lib):
+    # eta = 0: Z = W0 Q, W_T = W0, so dq = W0^T dz, dk = dv = 0 and
+    # dw0 = dwT + sum_t dz_t q_t^T; deta_t is the derivative at eta = 0.
+    rng = np.random.default_rng(63)
+    q, k, v, eta, w0, dz, dwT = _bwd_case(rng, 1, 1, 10, 5)
+    eta = np.zeros_like(eta)
+    dq, dk, dv, deta, dw0 = oracle.linear_bwd(q, k, v, eta, w0, 4, dz, dwT, lib=lib)
+    W = w0[0]
+    assert rel(dq[0, 0], dz[0, 0] @ W) < 1e-13
+    assert np.abs(dk).max() == 0.0 and np.abs(dv).max() == 0.0
+    assert rel(dw0[0, 0], dwT[0, 0] + dz[0, 0].T @ q[0, 0]) < 1e-13
+
+
 PINS = [
     pin_linear_primal_equals_dual,
     pin_mlp_primal_equals_dual,
@@ -440,6 +501,9 @@ PINS = [
     pin_mlp_step_replays_scan,
     pin_step_resumes_a_scan_mid_sequence,
     pin_step_golden_scalar_examples,
+    pin_linear_bwd_finite_differences,
+    pin_linear_bwd_equals_dual_form_adjoint,
+    pin_linear_bwd_eta_zero,
 ]
 
 
@@ -551,6 +615,14 @@ MUTATIONS = {
     "mlp_step_backprop_through_current_w2": ("bp += W2g[i * hd + h] * e[i];",
                                              "bp += W2[i * hd + h] * e[i];"),
     "mlp_step_w1_gradient_point_not_reset": ("memcpy(W1g, W1, sizeof(double) * (size_t)(hd * d));", ""),
+    "bwd_gradient_point_adjoint_dropped": ("        A[e] += Ag[e];\n", ""),
+    "bwd_eta_sign": ("      gb[i] = -eta[t] * s;", "      gb[i] = eta[t] * s;"),
+    "bwd_dq_untransposed": ("for (long i = 0; i < d; ++i) s += Wn[i * d + j] * zt[i];",
+                            "for (long i = 0; i < d; ++i) s += Wn[j * d + i] * zt[i];"),
+    "bwd_dk_drops_gradient_point_term": ("dk[t * d + j] = -eta[t] * s1 + 2.0 * s2;",
+                                         "dk[t * d + j] = -eta[t] * s1;"),
+    "bwd_output_adjoint_dropped": ("A[i * d + j] += zt[i] * qt[j];\n    /* W_t",
+                                   "A[i * d + j] += 0.0 * zt[i] * qt[j];\n    /* W_t"),
 }
 
 
