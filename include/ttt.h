@@ -129,6 +129,42 @@ ttt_status_t ttt_linear_ln_fwd(const void* q, const void* k, const void* v,
                                void* stream);
 
 /*
+ * Training support (§6.12: the outer loop differentiates through the inner
+ * one; the forward keeps the state at the start of every mini-batch, the
+ * kappa = T / b checkpoints, and the backward walks the mini-batches in
+ * reverse).  Support: d = 64, bf16 q/k/v, b = 16; else TTT_ERR_UNSUPPORTED.
+ *
+ * ttt_linear_fwd_ckpt: ttt_linear_fwd plus
+ *   w_ckpt : out [B][H][ceil(T/16)][d][d] fp32, the state before each
+ *            mini-batch (w_ckpt[..][0] = W0).
+ *
+ * ttt_linear_bwd: the gradient of a loss L(Z, W_T) with respect to the
+ * scan's inputs, given
+ *   dz   : [B][H][T][d] fp32, dL/dZ
+ *   dw_T : [B][H][d][d] fp32, dL/dW_T, or NULL for zero
+ *   q, k, v, eta : the forward's inputs; w_ckpt : from ttt_linear_fwd_ckpt
+ * and writing (fp32)
+ *   dq, dk, dv : [B][H][T][d];  deta : [B][H][T]
+ *   dw0 : [B][H][d][d], per unit (sum over the batch for a shared W0)
+ * workspace: caller-owned scratch of the same size as w_ckpt (the adjoint
+ * state at the end of every mini-batch).  Outputs and workspace must not
+ * overlap each other or an input.
+ */
+ttt_status_t ttt_linear_fwd_ckpt(const void* q, const void* k, const void* v,
+                                 const float* eta, const float* w0,
+                                 int32_t w0_per_batch, int32_t B, int32_t H,
+                                 int32_t T, int32_t d, int32_t b,
+                                 ttt_dtype_t qkv_dtype, float* z, float* w_out,
+                                 float* w_ckpt, void* stream);
+ttt_status_t ttt_linear_bwd(const void* q, const void* k, const void* v,
+                            const float* eta, const float* w_ckpt, int32_t B,
+                            int32_t H, int32_t T, int32_t d, int32_t b,
+                            ttt_dtype_t qkv_dtype, const float* dz,
+                            const float* dw_T, float* dq, float* dk, float* dv,
+                            float* deta, float* dw0, float* workspace,
+                            void* stream);
+
+/*
  * Decode steps (§6.11: generation runs the primal form, one token at a
  * time).  One call advances every (batch, head) unit by one token.  A unit
  * carries two states, both updated in place:

@@ -29,6 +29,10 @@ SIGNATURES = {
                                _vp, _vp]),
     "ttt_linear_ln_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
                                   _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "ttt_linear_fwd_ckpt": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                   _vp, _vp, _vp, _vp]),
+    "ttt_linear_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
+                              _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "ttt_mlp_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                             _i32, _i32, _vp, _vp]),
     "ttt_mlp_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,

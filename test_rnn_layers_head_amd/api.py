@@ -123,6 +123,56 @@ def ttt_linear_ln_fwd(q, k, v, eta, w0, ln_gamma, ln_beta, eps: float, b: int, z
     return z, w_out
 
 
+def ttt_linear_fwd_ckpt(q, k, v, eta, w0, b: int, z=None, w_out=None, w_ckpt=None, stream=None):
+    """ttt_linear_fwd that also keeps the state before every mini-batch
+    (include/ttt.h; bf16 q/k/v, b = 16).  Returns (z, w_out, w_ckpt) with
+    w_ckpt [B, H, ceil(T/16), d, d] fp32."""
+    B, H, T, d = q.shape
+    if w_ckpt is None:
+        w_ckpt = torch.empty((B, H, (T + 15) // 16, d, d), dtype=torch.float32, device=q.device)
+    if z is None:
+        z = torch.empty((B, H, T, d), dtype=torch.float32, device=q.device)
+    if w_out is None:
+        w_out = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+    dev = _check_tensors(dict(q=q, k=k, v=v, eta=eta, w0=w0, z=z, w_out=w_out, w_ckpt=w_ckpt))
+    if tuple(w_ckpt.shape) != (B, H, (T + 15) // 16, d, d) or w_ckpt.dtype != torch.float32:
+        raise ValueError("w_ckpt must be float32 [B, H, ceil(T/16), d, d]")
+    per_batch = 1 if w0.dim() == 4 else 0
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib().ttt_linear_fwd_ckpt(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w0),
+                                                  per_batch, B, H, T, d, int(b), _dtype_code(q),
+                                                  _ptr(z), _ptr(w_out), _ptr(w_ckpt),
+                                                  _stream(dev, stream)))
+    return z, w_out, w_ckpt
+
+
+def ttt_linear_bwd(q, k, v, eta, w_ckpt, b: int, dz, dw_T=None, workspace=None, stream=None):
+    """Backward of the TTT-Linear scan (include/ttt.h): given dz = dL/dZ and
+    optionally dw_T = dL/dW_T, returns (dq, dk, dv, deta, dw0), fp32, with
+    dw0 per unit [B, H, d, d].  w_ckpt comes from ttt_linear_fwd_ckpt."""
+    B, H, T, d = q.shape
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=q.device)
+    dq, dk, dv, deta, dw0 = f32(B, H, T, d), f32(B, H, T, d), f32(B, H, T, d), f32(B, H, T), \
+        f32(B, H, d, d)
+    if workspace is None:
+        workspace = f32(*w_ckpt.shape)
+    dev = _check_tensors(dict(q=q, k=k, v=v, eta=eta, w_ckpt=w_ckpt, dz=dz, dw_T=dw_T,
+                              workspace=workspace))
+    for name, t in (("dz", dz), ("dw_T", dw_T), ("w_ckpt", w_ckpt), ("workspace", workspace)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if tuple(dz.shape) != (B, H, T, d):
+        raise ValueError("dz must be [B, H, T, d]")
+    if tuple(w_ckpt.shape) != (B, H, (T + 15) // 16, d, d) or workspace.shape != w_ckpt.shape:
+        raise ValueError("w_ckpt / workspace must be [B, H, ceil(T/16), d, d]")
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib().ttt_linear_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w_ckpt),
+                                             B, H, T, d, int(b), _dtype_code(q), _ptr(dz),
+                                             _ptr(dw_T), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(deta),
+                                             _ptr(dw0), _ptr(workspace), _stream(dev, stream)))
+    return dq, dk, dv, deta, dw0
+
+
 def _step_common(name, q, k, v, eta, pos, states: dict, z):
     if q.dim() != 3:
         raise ValueError(f"{name}: q must be [B, H, d] (one token per unit)")

@@ -102,8 +102,8 @@ int auto_rows(int64_t units) {
 ttt_status_t linear_impl(const void* q, const void* k, const void* v, const float* eta,
                          const float* w0, int32_t w0_per_batch, int32_t B, int32_t H, int32_t T,
                          int32_t d, int32_t b, ttt_dtype_t dt, float* z, float* w_out,
-                         void* stream, int32_t rows) {
-  static const char* fn = "ttt_linear_fwd";
+                         void* stream, int32_t rows, float* w_ckpt = nullptr,
+                         const char* fn = "ttt_linear_fwd") {
   if (rows != 0 && rows != 16 && rows != 32 && rows != 64)
     return fail(TTT_ERR_UNSUPPORTED, "%s: rows_per_workgroup=%d (need 0, 16, 32 or 64)", fn, rows);
   const int64_t units = (int64_t)B * H;
@@ -112,17 +112,22 @@ ttt_status_t linear_impl(const void* q, const void* k, const void* v, const floa
   const Range in[] = {rng("q", q, seq * es), rng("k", k, seq * es), rng("v", v, seq * es),
                       rng("eta", eta, units * T * 4),
                       rng("w0", w0, (w0_per_batch ? units : (int64_t)H) * d * d * 4)};
-  const Range out[] = {rng("z", z, seq * 4), rng("w_out", w_out, units * d * d * 4)};
+  const int64_t nck = units * ((T + 15) / 16) * d * d * 4;
+  const Range out[] = {rng("z", z, seq * 4), rng("w_out", w_out, units * d * d * 4),
+                       rng("w_ckpt", w_ckpt, nck)};
   const int pairs[][2] = {{4, 1}};
-  ttt_status_t st = check_common(fn, dt, w0_per_batch, B, H, T, d, b, in, 5, out, 2, pairs, 1, T > 0);
+  ttt_status_t st = check_common(fn, dt, w0_per_batch, B, H, T, d, b, in, 5, out,
+                                 w_ckpt ? 3 : 2, pairs, 1, T > 0);
   if (st != TTT_OK || units == 0) return st;
+  if (w_ckpt && (dt != TTT_BF16 || b != 16))
+    return fail(TTT_ERR_UNSUPPORTED, "%s: checkpoints need bf16 q/k/v and b = 16", fn);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (T == 0) {
     if (w0_per_batch && w0 == w_out) return TTT_OK;
     e = ttt::launch_copy_state(w0, w0_per_batch, (int)units, H, d * d, w_out, s);
   } else {
-    ttt::LinearArgs a{q, k, v, eta, w0, z, w_out, w0_per_batch, (int)units, H, T, b};
+    ttt::LinearArgs a{q, k, v, eta, w0, z, w_out, w0_per_batch, (int)units, H, T, b, w_ckpt};
     e = ttt::launch_linear(a, dt == TTT_F32, rows ? rows : auto_rows(units), s);
   }
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
@@ -274,9 +279,77 @@ ttt_status_t mlp_step_impl(const void* q, const void* k, const void* v, const fl
   return TTT_OK;
 }
 
+ttt_status_t linear_bwd_impl(const void* q, const void* k, const void* v, const float* eta,
+                            const float* w_ckpt, int32_t B, int32_t H, int32_t T, int32_t d,
+                            int32_t b, ttt_dtype_t dt, const float* dz, const float* dw_T,
+                            float* dq, float* dk, float* dv, float* deta, float* dw0,
+                            float* workspace, void* stream) {
+  static const char* fn = "ttt_linear_bwd";
+  const int64_t units = (int64_t)B * H;
+  const int64_t seq = units * T * d;
+  const int64_t nck = units * ((T + 15) / 16) * d * d * 4;
+  const Range in[] = {rng("q", q, seq * 2), rng("k", k, seq * 2), rng("v", v, seq * 2),
+                      rng("eta", eta, units * T * 4), rng("w_ckpt", w_ckpt, nck),
+                      rng("dz", dz, seq * 4), rng("dw_T", dw_T, units * d * d * 4)};
+  const Range out[] = {rng("dq", dq, seq * 4), rng("dk", dk, seq * 4), rng("dv", dv, seq * 4),
+                       rng("deta", deta, units * T * 4), rng("dw0", dw0, units * d * d * 4),
+                       rng("workspace", workspace, nck)};
+  if (dt != TTT_F32 && dt != TTT_BF16) return fail(TTT_ERR_DTYPE, "%s: unknown qkv_dtype %d", fn, (int)dt);
+  if (B < 0 || H < 0 || T < 0 || d < 0 || b < 0)
+    return fail(TTT_ERR_SHAPE, "%s: negative size (B=%d H=%d T=%d d=%d b=%d)", fn, B, H, T, d, b);
+  if (d != 64) return fail(TTT_ERR_UNSUPPORTED, "%s: head dim d=%d unsupported (only 64)", fn, d);
+  if (b != 16) return fail(TTT_ERR_UNSUPPORTED, "%s: mini-batch b=%d unsupported (only 16)", fn, b);
+  if (dt != TTT_BF16) return fail(TTT_ERR_UNSUPPORTED, "%s: only bf16 q/k/v are supported", fn);
+  if (seq >= ((int64_t)1 << 31))
+    return fail(TTT_ERR_SHAPE, "%s: B*H*T*d = %lld exceeds 2^31 - 1", fn, (long long)seq);
+  if (units == 0) return TTT_OK;
+  for (int i = 0; i < 7; ++i) {
+    const bool seqt = i < 6;  // empty when T == 0
+    if ((seqt && T == 0) || (i == 6 && !dw_T)) continue;
+    if (!in[i].lo) return fail(TTT_ERR_NULL, "%s: %s is NULL", fn, in[i].name);
+    if (in[i].lo & 15) return fail(TTT_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, in[i].name);
+  }
+  if (T > 0 && !w_ckpt) return fail(TTT_ERR_NULL, "%s: w_ckpt is NULL", fn);
+  for (int o = 0; o < 6; ++o) {
+    if ((o != 4 && T == 0)) continue;
+    if (!out[o].lo) return fail(TTT_ERR_NULL, "%s: %s is NULL", fn, out[o].name);
+    if (out[o].lo & 15) return fail(TTT_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, out[o].name);
+    for (int i = 0; i < 7; ++i)
+      if (overlap(out[o], in[i]))
+        return fail(TTT_ERR_ALIAS, "%s: %s overlaps input %s", fn, out[o].name, in[i].name);
+    for (int o2 = o + 1; o2 < 6; ++o2)
+      if (overlap(out[o], out[o2]))
+        return fail(TTT_ERR_ALIAS, "%s: %s and %s overlap", fn, out[o].name, out[o2].name);
+  }
+  ttt::LinearBwdArgs a{q, k, v, eta, w_ckpt, dz, dw_T, dq, dk, dv, deta, dw0, workspace,
+                       (int)units, H, T};
+  hipError_t e = ttt::launch_linear_bwd(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return TTT_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+ttt_status_t ttt_linear_fwd_ckpt(const void* q, const void* k, const void* v, const float* eta,
+                                 const float* w0, int32_t w0_per_batch, int32_t B, int32_t H,
+                                 int32_t T, int32_t d, int32_t b, ttt_dtype_t qkv_dtype, float* z,
+                                 float* w_out, float* w_ckpt, void* stream) {
+  if ((int64_t)B * H > 0 && T > 0 && !w_ckpt)
+    return fail(TTT_ERR_NULL, "ttt_linear_fwd_ckpt: w_ckpt is NULL");
+  return linear_impl(q, k, v, eta, w0, w0_per_batch, B, H, T, d, b, qkv_dtype, z, w_out, stream,
+                     0, w_ckpt, "ttt_linear_fwd_ckpt");
+}
+
+ttt_status_t ttt_linear_bwd(const void* q, const void* k, const void* v, const float* eta,
+                            const float* w_ckpt, int32_t B, int32_t H, int32_t T, int32_t d,
+                            int32_t b, ttt_dtype_t qkv_dtype, const float* dz, const float* dw_T,
+                            float* dq, float* dk, float* dv, float* deta, float* dw0,
+                            float* workspace, void* stream) {
+  return linear_bwd_impl(q, k, v, eta, w_ckpt, B, H, T, d, b, qkv_dtype, dz, dw_T, dq, dk, dv,
+                         deta, dw0, workspace, stream);
+}
 
 ttt_status_t ttt_mlp_step(const void* q, const void* k, const void* v, const float* eta,
                           float* w1, float* w2, float* w1_gp, float* w2_gp, const int32_t* pos,

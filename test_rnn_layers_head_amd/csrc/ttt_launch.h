@@ -19,6 +19,9 @@ struct LinearArgs {
   int H;
   int T;
   int b;
+  // optional: the state at the start of every 16-token mini-batch,
+  // [units][ceil(T / 16)][64][64] (b = 16, bf16 inputs only)
+  float* w_ckpt = nullptr;
 };
 
 // TTT-Linear with the LayerNorm + residual inner model: gamma, beta [H][64].
@@ -45,6 +48,27 @@ struct MlpArgs {
   int T;
   int b;
 };
+
+// Backward of the TTT-Linear scan (b = 16, bf16 q/k/v).
+struct LinearBwdArgs {
+  const void* q;         // [units][T][64] bf16
+  const void* k;
+  const void* v;
+  const float* eta;      // [units][T]
+  const float* w_ckpt;   // [units][ceil(T/16)][64][64]: W at every tile start
+  const float* dz;       // [units][T][64]
+  const float* dw_T;     // [units][64][64] or NULL
+  float* dq;             // [units][T][64]
+  float* dk;
+  float* dv;
+  float* deta;           // [units][T]
+  float* dw0;            // [units][64][64]
+  float* wb_ckpt;        // workspace [units][ceil(T/16)][64][64]
+  int units;
+  int H;
+  int T;
+};
+hipError_t launch_linear_bwd(const LinearBwdArgs& a, hipStream_t s);
 
 // One decode step for every (batch, head) unit.
 struct StepArgs {

@@ -82,7 +82,9 @@ struct Geom {
 // TPM: tiles per mini-batch when it is fixed at compile time (b = 32, 64),
 // so a tile's position inside its mini-batch costs nothing; 0 = read from
 // the arguments (other multiples of 16).  Unused below b = 16.
-template <int MODE, int ROWS, int TPM>
+// CKPT (b = 16 only): also store the state at the start of every tile, the
+// checkpoints the backward pass reads.
+template <int MODE, int ROWS, int TPM, bool CKPT = false>
 __global__ void __launch_bounds__((Geom<ROWS>::THREADS))
 linear_scan_bf16_kernel(LinearArgs a) {
   using G = Geom<ROWS>;
@@ -375,6 +377,12 @@ linear_scan_bf16_kernel(LinearArgs a) {
     load_prep(pn, prep + ((j + 1) & 1) * G::PREP);
     load_raw(rn, raw + ((j + 2) % G::NST) * G::RAW, raw + ((j + 1) % G::NST) * G::RAW);
     __builtin_amdgcn_sched_barrier(0);  // the reads go out first
+    if constexpr (CKPT) {  // W_j, the state before tile j
+      float* ck = a.w_ckpt + ((size_t)unit * ntiles + j) * 4096;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        *(f32x4*)(ck + (rbase + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1)) = W[m];
+    }
     constexpr int pos = decltype(POS)::value;
     const bool new_mb = MODE != MODE_MULTI || (pos >= 0 ? pos == 0 : (j % tpm) == 0);
     const bool next_new_mb =
@@ -466,27 +474,28 @@ linear_scan_bf16_kernel(LinearArgs a) {
     *(f32x4*)(wo + (rbase + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1)) = W[m];
 }
 
-template <int MODE, int ROWS, int TPM>
+template <int MODE, int ROWS, int TPM, bool CKPT = false>
 hipError_t launch_one(const LinearArgs& a, hipStream_t s) {
   constexpr int NSPLIT = 64 / ROWS;
   const int blocks = NSPLIT == 1 ? a.units : ((a.units + 7) / 8) * 8 * NSPLIT;
-  hipLaunchKernelGGL((linear_scan_bf16_kernel<MODE, ROWS, TPM>), dim3(blocks),
+  hipLaunchKernelGGL((linear_scan_bf16_kernel<MODE, ROWS, TPM, CKPT>), dim3(blocks),
                      dim3(Geom<ROWS>::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
-template <int MODE, int TPM>
+template <int MODE, int TPM, bool CKPT = false>
 hipError_t launch_rows(const LinearArgs& a, int rows, hipStream_t s) {
   switch (rows) {
-    case 64: return launch_one<MODE, 64, TPM>(a, s);
-    case 32: return launch_one<MODE, 32, TPM>(a, s);
-    default: return launch_one<MODE, 16, TPM>(a, s);
+    case 64: return launch_one<MODE, 64, TPM, CKPT>(a, s);
+    case 32: return launch_one<MODE, 32, TPM, CKPT>(a, s);
+    default: return launch_one<MODE, 16, TPM, CKPT>(a, s);
   }
 }
 
 }  // namespace
 
 hipError_t launch_linear_bf16(const LinearArgs& a, int rows, hipStream_t s) {
+  if (a.w_ckpt) return a.b == 16 ? launch_rows<MODE_B16, 1, true>(a, rows, s) : hipErrorInvalidValue;
   if (a.b == 16) return launch_rows<MODE_B16, 1>(a, rows, s);
   if (a.b < 16) return launch_rows<MODE_SUB, 1>(a, rows, s);
   if (a.b == 32) return launch_rows<MODE_MULTI, 2>(a, rows, s);

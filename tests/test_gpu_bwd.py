@@ -1,0 +1,110 @@
+"""Backward of the TTT-Linear scan: HIP path (ttt_linear_fwd_ckpt +
+ttt_linear_bwd through the C ABI) against the fp64 backward oracle.
+
+Tolerance: the checkpointed states come from the bf16-input forward (its
+hi/lo operand splits, ~2^-16 relative); the backward's own products are
+fp32 MFMA (exact fp32 products).  The bound is the bf16-input one of the
+forward, rel-L2 <= 2e-3 and max|diff| / RMS <= 1e-2, on every gradient.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as gu
+from oracle import oracle
+from test_rnn_layers_head_amd import (TTTError, inputs, ttt_linear_bwd, ttt_linear_fwd,
+                                      ttt_linear_fwd_ckpt)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd_bwd(x, dz, dwT=None):
+    q, k, v = (gu.dev(x, n) for n in ("q", "k", "v"))
+    eta, w0 = gu.f32(x.eta), gu.f32(x.w0)
+    z, w, ck = ttt_linear_fwd_ckpt(q, k, v, eta, w0, 16)
+    grads = ttt_linear_bwd(q, k, v, eta, ck, 16, gu.f32(dz), None if dwT is None else gu.f32(dwT))
+    torch.cuda.synchronize()
+    return z, w, ck, [t.cpu().numpy() for t in grads]
+
+
+def check(got, ref, what):
+    for name, a, b in zip(("dq", "dk", "dv", "deta", "dw0"), got, ref):
+        gu.assert_close(a, b, "bf16", f"{what} {name}")
+
+
+@pytest.mark.parametrize("T", [1, 16, 37, 130])
+def test_checkpoints_are_the_states_before_each_minibatch(T):
+    x = inputs.make_inputs(inputs.Workload("ck", "linear", B=2, H=3, T=T, seed=700 + T))
+    q, k, v = (gu.dev(x, n) for n in ("q", "k", "v"))
+    eta, w0 = gu.f32(x.eta), gu.f32(x.w0)
+    z, w, ck = ttt_linear_fwd_ckpt(q, k, v, eta, w0, 16)
+    z0, w00 = ttt_linear_fwd(q, k, v, eta, w0, 16)
+    torch.cuda.synchronize()
+    assert torch.equal(z, z0) and torch.equal(w, w00)  # same kernel arithmetic
+    ck = ck.cpu().numpy()
+    for m in range(ck.shape[2]):
+        if m == 0:
+            ref = np.broadcast_to(x.w0[None], ck[:, :, 0].shape)
+        else:
+            sub = inputs.Inputs(x.wl, x.q[:, :, :16 * m], x.k[:, :, :16 * m], x.v[:, :, :16 * m],
+                                x.eta[:, :, :16 * m], x.w0)
+            _, ref = oracle.linear(sub.q, sub.k, sub.v, sub.eta, sub.w0, 16)
+        gu.assert_close(ck[:, :, m], ref, "bf16", f"checkpoint {m}")
+
+
+@pytest.mark.parametrize("T", [16, 37, 130])
+@pytest.mark.parametrize("with_dwT", [False, True])
+def test_backward_parity(T, with_dwT):
+    x = inputs.make_inputs(inputs.Workload("bwd", "linear", B=2, H=3, T=T, seed=710 + T))
+    rng = np.random.default_rng(711 + T)
+    dz = rng.standard_normal(x.q.shape).astype(np.float32)
+    dwT = rng.standard_normal((2, 3, 64, 64)).astype(np.float32) if with_dwT else None
+    _, _, _, got = run_fwd_bwd(x, dz, dwT)
+    ref = oracle.linear_bwd(x.q, x.k, x.v, x.eta, x.w0, 16, dz, dwT)
+    check(got, ref, f"T={T}")
+
+
+def test_backward_per_unit_initial_state_and_eta_zero_tokens():
+    x = inputs.make_inputs(inputs.Workload("bwd2", "linear", B=2, H=2, T=50, seed=720))
+    rng = np.random.default_rng(721)
+    x.w0 = (rng.standard_normal((2, 2, 64, 64)) * 0.02).astype(np.float32)
+    x.eta[:, :, 5:9] = 0.0
+    dz = rng.standard_normal(x.q.shape).astype(np.float32)
+    _, _, _, got = run_fwd_bwd(x, dz)
+    ref = oracle.linear_bwd(x.q, x.k, x.v, x.eta, x.w0, 16, dz)
+    check(got, ref, "per-unit w0")
+
+
+def test_backward_1p3b_workload_sampled_units():
+    x = inputs.make_inputs(3)
+    rng = np.random.default_rng(730)
+    dz = (rng.standard_normal(x.q.shape) * 0.1).astype(np.float32)
+    _, _, _, got = run_fwd_bwd(x, dz)
+    idx = [5, 100]
+    sub = x.units(idx)
+    dzs = dz.reshape(-1, x.wl.T, 64)[idx][None]
+    ref = oracle.linear_bwd(sub.q, sub.k, sub.v, sub.eta, sub.w0, 16, dzs)
+    pick = lambda a: a.reshape(-1, *a.shape[2:])[idx][None]
+    check([pick(a) for a in got], ref, "1.3B")
+    assert all(np.isfinite(a).all() for a in got)
+
+
+def test_backward_empty_sequence_and_rejected_arguments():
+    x = inputs.make_inputs(inputs.Workload("bwd0", "linear", B=1, H=2, T=16, seed=740))
+    q, k, v = (gu.dev(x, n) for n in ("q", "k", "v"))
+    eta, w0 = gu.f32(x.eta), gu.f32(x.w0)
+    dwT = torch.randn(1, 2, 64, 64, device="cuda")
+    e = torch.empty(1, 2, 0, 64, dtype=torch.bfloat16, device="cuda")
+    ck0 = torch.empty(1, 2, 0, 64, 64, device="cuda")
+    grads = ttt_linear_bwd(e, e, e, torch.empty(1, 2, 0, device="cuda"), ck0, 16,
+                           torch.empty(1, 2, 0, 64, device="cuda"), dwT)
+    torch.cuda.synchronize()
+    assert torch.equal(grads[4], dwT)  # no tokens: dL/dW0 = dL/dW_T
+    _, _, ck = ttt_linear_fwd_ckpt(q, k, v, eta, w0, 16)
+    dz = torch.randn(1, 2, 16, 64, device="cuda")
+    with pytest.raises(TTTError, match="TTT_ERR_UNSUPPORTED"):
+        ttt_linear_bwd(q, k, v, eta, ck, 4, dz)
+    with pytest.raises(TTTError, match="TTT_ERR_UNSUPPORTED"):
+        ttt_linear_fwd_ckpt(q, k, v, eta, w0, 32)
+    with pytest.raises(TTTError, match="TTT_ERR_ALIAS"):
+        ttt_linear_bwd(q, k, v, eta, ck, 16, dz, workspace=ck)
