@@ -61,6 +61,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.ttt_oracle_linear_bwd.argtypes = [dp, dp, dp, dp, dp, I, L, L, L, L, L, dp, dp, dp, dp, dp,
                                           dp, dp]
     lib.ttt_oracle_linear_bwd.restype = I
+    lib.ttt_oracle_lr_gate.argtypes = [dp, dp, D, L, L, L, L, dp]
+    lib.ttt_oracle_lr_gate.restype = I
     return lib
 
 
@@ -258,3 +260,28 @@ def linear_bwd(q, k, v, eta, w0, b: int, dz, dw_T=None, lib=None):
     if rc != 0:
         raise RuntimeError(f"ttt_oracle_linear_bwd failed with status {rc}")
     return dq, dk, dv, deta, dw0
+
+
+def lr_gate(x, theta_lr, eta_base: float, lib=None):
+    """Learnable inner learning rate ("论文速览 | TTT", §4.6): x [B, T, dx]
+    layer-input tokens, theta_lr [H, dx] one gate vector per head ->
+    eta [B, H, T] = eta_base * sigmoid(theta_lr[h] . x[b, t])."""
+    x, th = _f64(x), _f64(theta_lr)
+    B, T, dx = x.shape
+    H = th.shape[0]
+    assert th.shape == (H, dx)
+    eta = np.zeros((B, H, T))
+    lib = lib or load()
+    rc = lib.ttt_oracle_lr_gate(_ptr(x), _ptr(th), float(eta_base), B, T, H, dx, _ptr(eta))
+    if rc != 0:
+        raise RuntimeError(f"ttt_oracle_lr_gate failed with status {rc}")
+    return eta
+
+
+def linear_gated(q, k, v, x, theta_lr, eta_base: float, w0, b: int, nthreads: int | None = None,
+                 lib=None):
+    """TTT-Linear scan with the gated learning rate: the gate above, then
+    the scan with that eta.  Returns (z, w_T, eta)."""
+    eta = lr_gate(x, theta_lr, eta_base, lib=lib)
+    z, w = linear(q, k, v, eta, w0, b, nthreads=nthreads, lib=lib)
+    return z, w, eta

@@ -44,6 +44,12 @@
  * one per mini-batch and recompute; that is a memory trade, not another
  * result).
  *
+ * Inner learning-rate gate (§4.6): eta(x) = eta_base * sigmoid(theta_lr . x)
+ * with x the layer's input token and sigmoid(a) = 1 / (1 + exp(-a)).  The
+ * page gives theta_lr as one vector; each head runs its own inner loop, so
+ * here every head h has its own theta_lr[h] (H = 1 is the page's case), and
+ * the gated scan is the scan above fed with eta[b][h][t] from the gate.
+ *
  * The loss is the squared L2 norm summed over output components, so its
  * gradient carries the factor 2 (§3.6 linear derivation: G_t = 2(W0 x - x)x^T).
  * GELU is the exact erf form x * Phi(x).  Mini-batches start at token 0, b,
@@ -55,6 +61,7 @@
  *             W[i][j] with i the output index, f(x)_i = sum_j W[i][j] x_j
  *   MLP     : w1 [.][hidden][d], w2 [.][d][hidden] (same per-batch rule)
  *   z       : [B][H][T][d]        state outputs : [B][H][...]
+ *   gate    : x [B][T][dx], theta_lr [H][dx]  ->  eta [B][H][T]
  *
  * Build: gcc -O2 -ffp-contract=off -fPIC -shared -pthread (no fused
  * multiply-add contraction, so every product is rounded as written).
@@ -606,5 +613,23 @@ int ttt_oracle_linear_bwd(const double *q, const double *k, const double *v,
                              dv + so, deta + (size_t)u * (size_t)T, dw0 + (size_t)u * (size_t)(d * d));
     if (rc) return rc;
   }
+  return 0;
+}
+
+/* §4.6: eta[b][h][t] = eta_base * sigmoid(theta_lr[h] . x[b][t]), the dot
+ * product summed in order in fp64. */
+int ttt_oracle_lr_gate(const double *x, const double *theta, double eta_base, long B, long T,
+                       long H, long dx, double *eta) {
+  if (B < 0 || T < 0 || H < 0 || dx <= 0) return 2;
+  for (long bi = 0; bi < B; ++bi)
+    for (long h = 0; h < H; ++h)
+      for (long t = 0; t < T; ++t) {
+        const double *xt = x + ((size_t)bi * (size_t)T + (size_t)t) * (size_t)dx;
+        const double *th = theta + (size_t)h * (size_t)dx;
+        double a = 0.0;
+        for (long i = 0; i < dx; ++i) a += th[i] * xt[i];
+        eta[((size_t)bi * (size_t)H + (size_t)h) * (size_t)T + (size_t)t] =
+            eta_base / (1.0 + exp(-a));
+      }
   return 0;
 }

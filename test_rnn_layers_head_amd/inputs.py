@@ -27,6 +27,13 @@ Recipe (per workload):
     LayerNorm divides by the spread of W0 k, so the gradient scales like
     1 / |W0| and the step is stable only for eta |k|^2 / var(W0 k) of order
     one (with W0 ~ N(0, 0.02^2) it would be ~40 times larger);
+  * learning-rate gate workloads (gate_dx > 0), drawn last: the layer input
+    x ~ N(0, 1) per element, [B, T, gate_dx], stored bf16, and one gate
+    vector per head theta_lr ~ N(0, 1 / gate_dx), [H, gate_dx], fp32, with
+    eta_base = eta_scale = 0.1: the gate's logit theta_lr . x is then
+    ~N(0, 1), so the gated eta has the distribution 0.1 sigmoid(N(0, 1)) of
+    the other workloads.  gate_dx is the model width H d (2048 for the 1.3B
+    layer, 768 for the 125M one);
   * the drawn float64 values are rounded once, round-to-nearest-even, to the
     storage dtype (bf16 for Q/K/V unless the workload says fp32; eta and the
     states are fp32).  Both sides consume exactly these rounded values.
@@ -56,6 +63,7 @@ class Workload:
     eta_scale: float = 0.1
     w_scale: float = 0.02
     ln_eps: float = 1e-5
+    gate_dx: int = 0  # > 0: draw a gate input x [B, T, gate_dx] and theta_lr [H, gate_dx]
     b_sweep: tuple = field(default_factory=tuple)
 
     @property
@@ -79,6 +87,8 @@ WORKLOADS = {
                 w_scale=0.125),
     7: Workload("linear-ln-125M-T2048", "linear_ln", B=8, H=12, T=2048, seed=7, eta_scale=0.02,
                 w_scale=0.125),
+    8: Workload("linear-gated-1.3B-T8192", "linear", B=4, H=32, T=8192, seed=8, gate_dx=2048),
+    9: Workload("linear-gated-125M-T2048", "linear", B=8, H=12, T=2048, seed=9, gate_dx=768),
 }
 
 
@@ -124,11 +134,18 @@ class Inputs:
     v_raw: np.ndarray | None = None
     ln_gamma: np.ndarray | None = None  # [H, d] fp32 (kind "linear_ln")
     ln_beta: np.ndarray | None = None
+    gate_x: np.ndarray | None = None  # [B, T, dx] float32 holding the bf16 values
+    gate_x_raw: np.ndarray | None = None  # the same as uint16 bf16 patterns
+    theta_lr: np.ndarray | None = None  # [H, dx] fp32
+
+    @property
+    def eta_base(self) -> float:
+        return self.wl.eta_scale
 
     def sha256(self) -> str:
         h = hashlib.sha256()
         for a in (self.q_raw, self.k_raw, self.v_raw, self.eta, self.w0, self.w1, self.w2,
-                  self.ln_gamma, self.ln_beta):
+                  self.ln_gamma, self.ln_beta, self.gate_x_raw, self.theta_lr):
             if a is not None:
                 h.update(np.ascontiguousarray(a).tobytes())
         return h.hexdigest()
@@ -204,4 +221,9 @@ def make_inputs(wl: Workload | int, seed: int | None = None) -> Inputs:
         raws = vals
     else:
         raise ValueError(wl.qkv_dtype)
-    return Inputs(wl, *vals, eta, w0, w1, w2, *raws, gamma, beta)
+    gx = gx_raw = theta = None
+    if wl.gate_dx:
+        gx_raw = bf16_bits(rng.standard_normal((wl.B, wl.T, wl.gate_dx)))
+        gx = bf16_to_f32(gx_raw)
+        theta = (rng.standard_normal((wl.H, wl.gate_dx)) / np.sqrt(wl.gate_dx)).astype(np.float32)
+    return Inputs(wl, *vals, eta, w0, w1, w2, *raws, gamma, beta, gx, gx_raw, theta)

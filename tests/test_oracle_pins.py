@@ -24,6 +24,10 @@ Time): RNNs with Expressive Hidden States"):
   with eps = 0 the scan is covariant under (W0, eta) -> (a W0, a^2 eta)
   (LayerNorm is scale-free, its VJP scales as 1/a); with gamma = 1, beta = 0,
   eps = 0 every output minus its query has mean 0 and variance 1;
+* the inner learning-rate gate (§4.6) eta = eta_base sigmoid(theta_lr . x):
+  logits placed exactly through one-hot gate vectors give the closed values
+  sigmoid(0) = 1/2, sigmoid(+-ln 3) = 3/4, 1/4, sigmoid(+-ln 7) = 7/8, 1/8 and
+  saturation at eta_base, each at its own (batch, head, token);
 * invariants: homogeneity, superposition, row permutation, state passing,
   thread-count determinism.
 
@@ -478,6 +482,43 @@ def pin_linear_bwd_eta_zero(lib):
     assert rel(dw0[0, 0], dwT[0, 0] + dz[0, 0].T @ q[0, 0]) < 1e-13
 
 
+# sigmoid values known in closed form: logit -> sigmoid
+_GATE_LOGITS = {0.0: 0.5, np.log(3.0): 0.75, -np.log(3.0): 0.25, np.log(7.0): 0.875,
+                -np.log(7.0): 0.125, 60.0: 1.0, -60.0: 0.0}
+
+
+def pin_gate_closed_forms(lib):
+    # theta_lr[h] = c_h e_{p(h)} puts the logit c_h x[b, t, p(h)] at every
+    # (b, h, t) on its own; each logit is drawn from the closed-form table, so
+    # a wrong index, sign or scale shows up as a wrong table value.
+    rng = np.random.default_rng(70)
+    B, T, H, dx = 2, 5, 3, 8
+    keys = list(_GATE_LOGITS)
+    pick = rng.integers(0, len(keys), size=(B, H, T))
+    perm = [5, 1, 6]  # p(h): the column of x that head h reads
+    scale = [1.0, -2.0, 0.5]
+    theta = np.zeros((H, dx))
+    x = rng.standard_normal((B, T, dx))
+    want = np.zeros((B, H, T))
+    for h in range(H):
+        theta[h, perm[h]] = scale[h]
+    for bi in range(B):
+        for t in range(T):
+            for h in range(H):
+                a = keys[pick[bi, h, t]]
+                x[bi, t, perm[h]] = a / scale[h]
+                want[bi, h, t] = _GATE_LOGITS[a]
+    eta_base = 0.37
+    got = oracle.lr_gate(x, theta, eta_base, lib=lib)
+    assert np.abs(got - eta_base * want).max() < 1e-15
+    # a gate vector spread over several inputs: the dot product sums them
+    theta2 = np.ones((1, dx)) / dx
+    x2 = np.full((1, 1, dx), np.log(3.0))
+    assert abs(oracle.lr_gate(x2, theta2, 1.0, lib=lib)[0, 0, 0] - 0.75) < 1e-15
+    # theta_lr = 0 gives eta_base / 2 everywhere
+    assert np.all(oracle.lr_gate(x, np.zeros((H, dx)), 2.0, lib=lib) == 1.0)
+
+
 PINS = [
     pin_linear_primal_equals_dual,
     pin_mlp_primal_equals_dual,
@@ -504,6 +545,7 @@ PINS = [
     pin_linear_bwd_finite_differences,
     pin_linear_bwd_equals_dual_form_adjoint,
     pin_linear_bwd_eta_zero,
+    pin_gate_closed_forms,
 ]
 
 
@@ -621,6 +663,12 @@ MUTATIONS = {
                             "for (long i = 0; i < d; ++i) s += Wn[j * d + i] * zt[i];"),
     "bwd_dk_drops_gradient_point_term": ("dk[t * d + j] = -eta[t] * s1 + 2.0 * s2;",
                                          "dk[t * d + j] = -eta[t] * s1;"),
+    "gate_sign": ("eta_base / (1.0 + exp(-a));", "eta_base / (1.0 + exp(a));"),
+    "gate_no_base": ("eta_base / (1.0 + exp(-a));", "1.0 / (1.0 + exp(-a));"),
+    "gate_theta_of_head_0": ("*th = theta + (size_t)h * (size_t)dx;", "*th = theta;"),
+    "gate_token_major_output": ("eta[((size_t)bi * (size_t)H + (size_t)h) * (size_t)T + (size_t)t]",
+                                "eta[((size_t)bi * (size_t)T + (size_t)t) * (size_t)H + (size_t)h]"),
+    "gate_first_token_only": ("+ (size_t)t) * (size_t)dx;", ") * (size_t)dx;"),
     "bwd_output_adjoint_dropped": ("A[i * d + j] += zt[i] * qt[j];\n    /* W_t",
                                    "A[i * d + j] += 0.0 * zt[i] * qt[j];\n    /* W_t"),
 }
