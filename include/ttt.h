@@ -232,6 +232,54 @@ ttt_status_t ttt_mlp_fwd(const void* q, const void* k, const void* v,
                          int32_t b, ttt_dtype_t qkv_dtype, float* z,
                          float* w1_out, float* w2_out, void* stream);
 
+/*
+ * Learnable inner learning rate (§4.6): the step size of token t in head h
+ * depends on the token,
+ *   eta[b][h][t] = eta_base * sigmoid(theta_lr[h] . x[b][t]),
+ * sigmoid(a) = 1 / (1 + exp(-a)), with x the layer's input token.  The page
+ * gives theta_lr as one vector learned by the outer loop; every head runs
+ * its own inner loop, so here each head has its own (H = 1 is the page's
+ * single vector).  The page's eta_base is 1 for TTT-Linear and 0.1 for
+ * TTT-MLP; it is an argument here.
+ *
+ *   x        : [B][T][dx] bf16, the layer input
+ *   theta_lr : [H][dx] fp32
+ *   eta_base : finite, else TTT_ERR_VALUE
+ *   eta      : out [B][H][T] fp32, the scans' eta layout
+ * Support: bf16 x, dx a positive multiple of 32; otherwise
+ * TTT_ERR_UNSUPPORTED.  eta must not overlap x or theta_lr.  The dot
+ * products are fp32 sums of exact products (theta_lr enters as three bf16
+ * terms); sigmoid in fp32.  Empty work (B*T*H == 0) returns TTT_OK.
+ */
+ttt_status_t ttt_lr_gate(const void* x, ttt_dtype_t x_dtype,
+                         const float* theta_lr, float eta_base, int32_t B,
+                         int32_t T, int32_t H, int32_t dx, float* eta,
+                         void* stream);
+
+/*
+ * The gate followed by the forward scan, on one stream: eta is computed from
+ * x into the caller's eta buffer ([B][H][T] fp32, kept as an output for the
+ * backward), then the scan runs with it.  All other arguments, layouts,
+ * support and errors are those of ttt_lr_gate (x bf16) and of
+ * ttt_linear_fwd / ttt_mlp_fwd; every check of both runs before anything is
+ * launched, and eta may not overlap any tensor of the scan.
+ */
+ttt_status_t ttt_linear_gated_fwd(const void* q, const void* k, const void* v,
+                                  const void* x, const float* theta_lr,
+                                  float eta_base, int32_t dx, const float* w0,
+                                  int32_t w0_per_batch, int32_t B, int32_t H,
+                                  int32_t T, int32_t d, int32_t b,
+                                  ttt_dtype_t qkv_dtype, float* eta, float* z,
+                                  float* w_out, void* stream);
+ttt_status_t ttt_mlp_gated_fwd(const void* q, const void* k, const void* v,
+                               const void* x, const float* theta_lr,
+                               float eta_base, int32_t dx, const float* w1_0,
+                               const float* w2_0, int32_t w0_per_batch,
+                               int32_t B, int32_t H, int32_t T, int32_t d,
+                               int32_t hidden, int32_t b,
+                               ttt_dtype_t qkv_dtype, float* eta, float* z,
+                               float* w1_out, float* w2_out, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* ttt_status_str(ttt_status_t status);
 

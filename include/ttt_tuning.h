@@ -34,6 +34,17 @@ ttt_status_t ttt_linear_fwd_tuned(const void* q, const void* k, const void* v,
                                   int32_t rows_per_workgroup);
 
 /*
+ * ttt_lr_gate with an explicit launch shape: tokens_per_workgroup tokens per
+ * workgroup (32 or 64; 0 = automatic).  Each token's sums are the same for
+ * every value.  Other values: TTT_ERR_UNSUPPORTED.
+ */
+ttt_status_t ttt_lr_gate_tuned(const void* x, ttt_dtype_t x_dtype,
+                               const float* theta_lr, float eta_base,
+                               int32_t B, int32_t T, int32_t H, int32_t dx,
+                               float* eta, void* stream,
+                               int32_t tokens_per_workgroup);
+
+/*
  * Plain streaming copy of `bytes` bytes (a multiple of 16, both pointers
  * 16-byte aligned, no overlap) from src to dst on `stream`: the reference
  * kernel whose hardware byte counters calibrate those of the scans.

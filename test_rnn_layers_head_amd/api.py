@@ -284,6 +284,105 @@ def ttt_mlp_fwd(q, k, v, eta, w1_0, w2_0, b: int, z=None, w1_out=None, w2_out=No
     return z, w1_out, w2_out
 
 
+def _gate_common(x, theta_lr, H_expected, eta):
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, dx]")
+    if x.dtype != torch.bfloat16:
+        raise TypeError(f"x must be bfloat16, got {x.dtype}")
+    if theta_lr.dtype != torch.float32:
+        raise TypeError(f"theta_lr must be float32, got {theta_lr.dtype}")
+    B, T, dx = x.shape
+    H = theta_lr.shape[0] if H_expected is None else H_expected
+    if tuple(theta_lr.shape) != (H, dx):
+        raise ValueError(f"theta_lr must be [H, dx] = [{H}, {dx}], got {tuple(theta_lr.shape)}")
+    if eta is None:
+        eta = torch.empty((B, H, T), dtype=torch.float32, device=x.device)
+    if eta.dtype != torch.float32 or tuple(eta.shape) != (B, H, T):
+        raise ValueError("eta must be float32 [B, H, T]")
+    return B, T, H, dx, eta
+
+
+def ttt_lr_gate(x, theta_lr, eta_base: float, eta=None, stream=None, tokens_per_workgroup: int = 0):
+    """Learning-rate gate (include/ttt.h): x [B, T, dx] bf16, theta_lr
+    [H, dx] fp32 -> eta [B, H, T] = eta_base * sigmoid(theta_lr[h] . x[b, t])."""
+    B, T, H, dx, eta = _gate_common(x, theta_lr, None, eta)
+    dev = _check_tensors(dict(x=x, theta_lr=theta_lr, eta=eta))
+    L = _lib.lib()
+    with torch.cuda.device(dev):
+        args = (_ptr(x), _lib.TTT_BF16, _ptr(theta_lr), float(eta_base), B, T, H, dx, _ptr(eta),
+                _stream(dev, stream))
+        if tokens_per_workgroup:
+            _lib.check(L.ttt_lr_gate_tuned(*args, int(tokens_per_workgroup)))
+        else:
+            _lib.check(L.ttt_lr_gate(*args))
+    return eta
+
+
+def ttt_linear_gated_fwd(q, k, v, x, theta_lr, eta_base: float, w0, b: int, eta=None, z=None,
+                         w_out=None, stream=None):
+    """The gate, then the TTT-Linear scan with its eta (include/ttt.h).
+    Returns (z, w_out, eta)."""
+    B, H, T, d = q.shape
+    if tuple(x.shape[:2]) != (B, T):
+        raise ValueError("x must be [B, T, dx] with the scan's B and T")
+    _, _, _, dx, eta = _gate_common(x, theta_lr, H, eta)
+    if z is None:
+        z = torch.empty((B, H, T, d), dtype=torch.float32, device=q.device)
+    if w_out is None:
+        w_out = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+    dev = _check_tensors(dict(q=q, k=k, v=v, x=x, theta_lr=theta_lr, w0=w0, eta=eta, z=z,
+                              w_out=w_out))
+    for name, t in (("w0", w0), ("z", z), ("w_out", w_out)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if k.dtype != q.dtype or v.dtype != q.dtype or k.shape != q.shape or v.shape != q.shape:
+        raise TypeError("q, k, v must share one dtype and shape")
+    per_batch = 1 if w0.dim() == 4 else 0
+    if tuple(w0.shape) != ((B, H, d, d) if per_batch else (H, d, d)):
+        raise ValueError(f"w0 has shape {tuple(w0.shape)}")
+    if tuple(z.shape) != (B, H, T, d) or tuple(w_out.shape) != (B, H, d, d):
+        raise ValueError("output shape mismatch")
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib().ttt_linear_gated_fwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(theta_lr), float(eta_base), dx, _ptr(w0),
+            per_batch, B, H, T, d, int(b), _dtype_code(q), _ptr(eta), _ptr(z), _ptr(w_out),
+            _stream(dev, stream)))
+    return z, w_out, eta
+
+
+def ttt_mlp_gated_fwd(q, k, v, x, theta_lr, eta_base: float, w1_0, w2_0, b: int, eta=None,
+                      z=None, w1_out=None, w2_out=None, stream=None):
+    """The gate, then the TTT-MLP scan with its eta (include/ttt.h).
+    Returns (z, w1_out, w2_out, eta)."""
+    B, H, T, d = q.shape
+    hidden = w1_0.shape[-2]
+    if tuple(x.shape[:2]) != (B, T):
+        raise ValueError("x must be [B, T, dx] with the scan's B and T")
+    _, _, _, dx, eta = _gate_common(x, theta_lr, H, eta)
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=q.device)
+    z = f32(B, H, T, d) if z is None else z
+    w1_out = f32(B, H, hidden, d) if w1_out is None else w1_out
+    w2_out = f32(B, H, d, hidden) if w2_out is None else w2_out
+    dev = _check_tensors(dict(q=q, k=k, v=v, x=x, theta_lr=theta_lr, w1_0=w1_0, w2_0=w2_0,
+                              eta=eta, z=z, w1_out=w1_out, w2_out=w2_out))
+    for name, t in (("w1_0", w1_0), ("w2_0", w2_0), ("z", z), ("w1_out", w1_out),
+                    ("w2_out", w2_out)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if k.dtype != q.dtype or v.dtype != q.dtype or k.shape != q.shape or v.shape != q.shape:
+        raise TypeError("q, k, v must share one dtype and shape")
+    per_batch = 1 if w1_0.dim() == 4 else 0
+    lead = (B, H) if per_batch else (H,)
+    if tuple(w1_0.shape) != (*lead, hidden, d) or tuple(w2_0.shape) != (*lead, d, hidden):
+        raise ValueError("w1_0 / w2_0 shape mismatch")
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib().ttt_mlp_gated_fwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(theta_lr), float(eta_base), dx, _ptr(w1_0),
+            _ptr(w2_0), per_batch, B, H, T, d, hidden, int(b), _dtype_code(q), _ptr(eta), _ptr(z),
+            _ptr(w1_out), _ptr(w2_out), _stream(dev, stream)))
+    return z, w1_out, w2_out, eta
+
+
 def bench_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     """Streaming copy kernel used to calibrate hardware byte counters."""
     dev = _check_tensors(dict(src=src, dst=dst))

@@ -103,7 +103,7 @@ ttt_status_t linear_impl(const void* q, const void* k, const void* v, const floa
                          const float* w0, int32_t w0_per_batch, int32_t B, int32_t H, int32_t T,
                          int32_t d, int32_t b, ttt_dtype_t dt, float* z, float* w_out,
                          void* stream, int32_t rows, float* w_ckpt = nullptr,
-                         const char* fn = "ttt_linear_fwd") {
+                         const char* fn = "ttt_linear_fwd", bool dry = false) {
   if (rows != 0 && rows != 16 && rows != 32 && rows != 64)
     return fail(TTT_ERR_UNSUPPORTED, "%s: rows_per_workgroup=%d (need 0, 16, 32 or 64)", fn, rows);
   const int64_t units = (int64_t)B * H;
@@ -121,6 +121,7 @@ ttt_status_t linear_impl(const void* q, const void* k, const void* v, const floa
   if (st != TTT_OK || units == 0) return st;
   if (w_ckpt && (dt != TTT_BF16 || b != 16))
     return fail(TTT_ERR_UNSUPPORTED, "%s: checkpoints need bf16 q/k/v and b = 16", fn);
+  if (dry) return TTT_OK;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (T == 0) {
@@ -328,6 +329,106 @@ ttt_status_t linear_bwd_impl(const void* q, const void* k, const void* v, const 
   return TTT_OK;
 }
 
+ttt_status_t mlp_impl(const void* q, const void* k, const void* v, const float* eta,
+                      const float* w1_0, const float* w2_0, int32_t w0_per_batch, int32_t B,
+                      int32_t H, int32_t T, int32_t d, int32_t hidden, int32_t b,
+                      ttt_dtype_t qkv_dtype, float* z, float* w1_out, float* w2_out, void* stream,
+                      const char* fn = "ttt_mlp_fwd", bool dry = false) {
+  if (hidden < 0) return fail(TTT_ERR_SHAPE, "%s: negative hidden=%d", fn, hidden);
+  const int64_t units = (int64_t)B * H;
+  const int64_t es = qkv_dtype == TTT_F32 ? 4 : 2;
+  const int64_t seq = units * T * d;
+  const int64_t wn = (w0_per_batch ? units : (int64_t)H) * hidden * d * 4;
+  const Range in[] = {rng("q", q, seq * es), rng("k", k, seq * es), rng("v", v, seq * es),
+                      rng("eta", eta, units * T * 4), rng("w1_0", w1_0, wn),
+                      rng("w2_0", w2_0, wn)};
+  const Range out[] = {rng("z", z, seq * 4), rng("w1_out", w1_out, units * hidden * d * 4),
+                       rng("w2_out", w2_out, units * hidden * d * 4)};
+  const int pairs[][2] = {{4, 1}, {5, 2}};
+  ttt_status_t st =
+      check_common(fn, qkv_dtype, w0_per_batch, B, H, T, d, b, in, 6, out, 3, pairs, 2, T > 0);
+  if (st != TTT_OK) return st;
+  if (hidden != 256)
+    return fail(TTT_ERR_UNSUPPORTED, "%s: hidden=%d unsupported (only 256)", fn, hidden);
+  if (qkv_dtype != TTT_BF16)
+    return fail(TTT_ERR_UNSUPPORTED, "%s: only bf16 q/k/v are supported", fn);
+  if (b > 16)
+    return fail(TTT_ERR_UNSUPPORTED, "%s: mini-batch b=%d unsupported (need b | 16)", fn, b);
+  if (units == 0 || dry) return TTT_OK;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (T == 0) {
+    if (!(w0_per_batch && w1_0 == w1_out))
+      e = ttt::launch_copy_state(w1_0, w0_per_batch, (int)units, H, hidden * d, w1_out, s);
+    if (e == hipSuccess && !(w0_per_batch && w2_0 == w2_out))
+      e = ttt::launch_copy_state(w2_0, w0_per_batch, (int)units, H, hidden * d, w2_out, s);
+  } else {
+    ttt::MlpArgs a{q, k, v, eta, w1_0, w2_0, z, w1_out, w2_out, w0_per_batch, (int)units, H, T, b};
+    e = ttt::launch_mlp(a, qkv_dtype == TTT_F32, s);
+  }
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return TTT_OK;
+}
+
+
+// Checks of the learning-rate gate; `fn` names the entry point in messages.
+ttt_status_t gate_check(const char* fn, const void* x, ttt_dtype_t x_dtype, const float* theta,
+                        float eta_base, int32_t B, int32_t T, int32_t H, int32_t dx,
+                        const float* eta) {
+  if (x_dtype != TTT_F32 && x_dtype != TTT_BF16)
+    return fail(TTT_ERR_DTYPE, "%s: unknown x dtype %d", fn, (int)x_dtype);
+  if (B < 0 || T < 0 || H < 0 || dx < 0)
+    return fail(TTT_ERR_SHAPE, "%s: negative size (B=%d T=%d H=%d dx=%d)", fn, B, T, H, dx);
+  if (dx == 0 || dx % 32 != 0)
+    return fail(TTT_ERR_UNSUPPORTED, "%s: dx=%d unsupported (need a positive multiple of 32)", fn, dx);
+  if (x_dtype != TTT_BF16) return fail(TTT_ERR_UNSUPPORTED, "%s: only bf16 x is supported", fn);
+  if (!(eta_base == eta_base) || eta_base > 3.4e38f || eta_base < -3.4e38f)
+    return fail(TTT_ERR_VALUE, "%s: eta_base=%g must be finite", fn, (double)eta_base);
+  const int64_t ntok = (int64_t)B * T;
+  if (ntok * H >= ((int64_t)1 << 31))
+    return fail(TTT_ERR_SHAPE, "%s: B*H*T = %lld exceeds 2^31 - 1", fn, (long long)(ntok * H));
+  if (ntok * H == 0) return TTT_OK;
+  const Range in[] = {rng("x", x, ntok * dx * 2), rng("theta_lr", theta, (int64_t)H * dx * 4)};
+  const Range out = rng("eta", eta, ntok * H * 4);
+  for (int i = 0; i < 2; ++i) {
+    if (!in[i].lo) return fail(TTT_ERR_NULL, "%s: %s is NULL", fn, in[i].name);
+    if (in[i].lo & 15) return fail(TTT_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, in[i].name);
+  }
+  if (!out.lo) return fail(TTT_ERR_NULL, "%s: eta is NULL", fn);
+  if (out.lo & 15) return fail(TTT_ERR_ALIGN, "%s: eta is not 16-byte aligned", fn);
+  for (int i = 0; i < 2; ++i)
+    if (overlap(out, in[i])) return fail(TTT_ERR_ALIAS, "%s: eta overlaps input %s", fn, in[i].name);
+  return TTT_OK;
+}
+
+ttt_status_t gate_launch(const char* fn, const void* x, const float* theta, float eta_base,
+                         int32_t B, int32_t T, int32_t H, int32_t dx, float* eta, void* stream,
+                         int tokens_per_workgroup = 0) {
+  ttt::GateArgs a{x, theta, eta, eta_base, B, T, H, dx};
+  hipError_t e = ttt::launch_lr_gate(a, tokens_per_workgroup, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return TTT_OK;
+}
+
+// The gate's x, theta and eta against the tensors of the scan that follows:
+// eta may not overlap anything the scan reads or writes, and the scan's
+// outputs may not overlap the gate's inputs.
+ttt_status_t gate_scan_alias(const char* fn, const void* x, const float* theta, const float* eta,
+                             int32_t B, int32_t T, int32_t H, int32_t dx, const Range* scan,
+                             int nscan, int first_out) {
+  const int64_t ntok = (int64_t)B * T;
+  if (ntok * H == 0) return TTT_OK;
+  const Range ge = rng("eta", eta, ntok * H * 4);
+  const Range gi[] = {rng("x", x, ntok * dx * 2), rng("theta_lr", theta, (int64_t)H * dx * 4)};
+  for (int i = 0; i < nscan; ++i) {
+    if (overlap(ge, scan[i])) return fail(TTT_ERR_ALIAS, "%s: eta overlaps %s", fn, scan[i].name);
+    if (i >= first_out)
+      for (int j = 0; j < 2; ++j)
+        if (overlap(scan[i], gi[j]))
+          return fail(TTT_ERR_ALIAS, "%s: %s overlaps input %s", fn, scan[i].name, gi[j].name);
+  }
+  return TTT_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -406,41 +507,78 @@ ttt_status_t ttt_mlp_fwd(const void* q, const void* k, const void* v, const floa
                          int32_t H, int32_t T, int32_t d, int32_t hidden, int32_t b,
                          ttt_dtype_t qkv_dtype, float* z, float* w1_out, float* w2_out,
                          void* stream) {
-  static const char* fn = "ttt_mlp_fwd";
-  if (hidden < 0) return fail(TTT_ERR_SHAPE, "%s: negative hidden=%d", fn, hidden);
-  const int64_t units = (int64_t)B * H;
-  const int64_t es = qkv_dtype == TTT_F32 ? 4 : 2;
-  const int64_t seq = units * T * d;
-  const int64_t wn = (w0_per_batch ? units : (int64_t)H) * hidden * d * 4;
-  const Range in[] = {rng("q", q, seq * es), rng("k", k, seq * es), rng("v", v, seq * es),
-                      rng("eta", eta, units * T * 4), rng("w1_0", w1_0, wn),
-                      rng("w2_0", w2_0, wn)};
-  const Range out[] = {rng("z", z, seq * 4), rng("w1_out", w1_out, units * hidden * d * 4),
-                       rng("w2_out", w2_out, units * hidden * d * 4)};
-  const int pairs[][2] = {{4, 1}, {5, 2}};
-  ttt_status_t st =
-      check_common(fn, qkv_dtype, w0_per_batch, B, H, T, d, b, in, 6, out, 3, pairs, 2, T > 0);
+  return mlp_impl(q, k, v, eta, w1_0, w2_0, w0_per_batch, B, H, T, d, hidden, b, qkv_dtype, z,
+                  w1_out, w2_out, stream);
+}
+
+ttt_status_t ttt_lr_gate(const void* x, ttt_dtype_t x_dtype, const float* theta_lr,
+                         float eta_base, int32_t B, int32_t T, int32_t H, int32_t dx, float* eta,
+                         void* stream) {
+  static const char* fn = "ttt_lr_gate";
+  ttt_status_t st = gate_check(fn, x, x_dtype, theta_lr, eta_base, B, T, H, dx, eta);
   if (st != TTT_OK) return st;
-  if (hidden != 256)
-    return fail(TTT_ERR_UNSUPPORTED, "%s: hidden=%d unsupported (only 256)", fn, hidden);
-  if (qkv_dtype != TTT_BF16)
-    return fail(TTT_ERR_UNSUPPORTED, "%s: only bf16 q/k/v are supported", fn);
-  if (b > 16)
-    return fail(TTT_ERR_UNSUPPORTED, "%s: mini-batch b=%d unsupported (need b | 16)", fn, b);
-  if (units == 0) return TTT_OK;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = hipSuccess;
-  if (T == 0) {
-    if (!(w0_per_batch && w1_0 == w1_out))
-      e = ttt::launch_copy_state(w1_0, w0_per_batch, (int)units, H, hidden * d, w1_out, s);
-    if (e == hipSuccess && !(w0_per_batch && w2_0 == w2_out))
-      e = ttt::launch_copy_state(w2_0, w0_per_batch, (int)units, H, hidden * d, w2_out, s);
-  } else {
-    ttt::MlpArgs a{q, k, v, eta, w1_0, w2_0, z, w1_out, w2_out, w0_per_batch, (int)units, H, T, b};
-    e = ttt::launch_mlp(a, qkv_dtype == TTT_F32, s);
-  }
-  if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
-  return TTT_OK;
+  return gate_launch(fn, x, theta_lr, eta_base, B, T, H, dx, eta, stream);
+}
+
+ttt_status_t ttt_lr_gate_tuned(const void* x, ttt_dtype_t x_dtype, const float* theta_lr,
+                               float eta_base, int32_t B, int32_t T, int32_t H, int32_t dx,
+                               float* eta, void* stream, int32_t tokens_per_workgroup) {
+  static const char* fn = "ttt_lr_gate_tuned";
+  if (tokens_per_workgroup != 0 && tokens_per_workgroup != 32 && tokens_per_workgroup != 64)
+    return fail(TTT_ERR_UNSUPPORTED, "%s: tokens_per_workgroup=%d (need 0, 32 or 64)", fn,
+                tokens_per_workgroup);
+  ttt_status_t st = gate_check(fn, x, x_dtype, theta_lr, eta_base, B, T, H, dx, eta);
+  if (st != TTT_OK) return st;
+  return gate_launch(fn, x, theta_lr, eta_base, B, T, H, dx, eta, stream, tokens_per_workgroup);
+}
+
+ttt_status_t ttt_linear_gated_fwd(const void* q, const void* k, const void* v, const void* x,
+                                  const float* theta_lr, float eta_base, int32_t dx,
+                                  const float* w0, int32_t w0_per_batch, int32_t B, int32_t H,
+                                  int32_t T, int32_t d, int32_t b, ttt_dtype_t qkv_dtype,
+                                  float* eta, float* z, float* w_out, void* stream) {
+  static const char* fn = "ttt_linear_gated_fwd";
+  ttt_status_t st = gate_check(fn, x, TTT_BF16, theta_lr, eta_base, B, T, H, dx, eta);
+  if (st == TTT_OK)
+    st = linear_impl(q, k, v, eta, w0, w0_per_batch, B, H, T, d, b, qkv_dtype, z, w_out, stream,
+                     0, nullptr, fn, true);
+  if (st != TTT_OK) return st;
+  const int64_t units = (int64_t)B * H, es = qkv_dtype == TTT_F32 ? 4 : 2, seq = units * T * d;
+  const Range scan[] = {rng("q", q, seq * es), rng("k", k, seq * es), rng("v", v, seq * es),
+                        rng("w0", w0, (w0_per_batch ? units : (int64_t)H) * d * d * 4),
+                        rng("z", z, seq * 4), rng("w_out", w_out, units * d * d * 4)};
+  st = gate_scan_alias(fn, x, theta_lr, eta, B, T, H, dx, scan, 6, 4);
+  if (st != TTT_OK) return st;
+  st = gate_launch(fn, x, theta_lr, eta_base, B, T, H, dx, eta, stream);
+  if (st != TTT_OK) return st;
+  return linear_impl(q, k, v, eta, w0, w0_per_batch, B, H, T, d, b, qkv_dtype, z, w_out, stream,
+                     0, nullptr, fn);
+}
+
+ttt_status_t ttt_mlp_gated_fwd(const void* q, const void* k, const void* v, const void* x,
+                               const float* theta_lr, float eta_base, int32_t dx,
+                               const float* w1_0, const float* w2_0, int32_t w0_per_batch,
+                               int32_t B, int32_t H, int32_t T, int32_t d, int32_t hidden,
+                               int32_t b, ttt_dtype_t qkv_dtype, float* eta, float* z,
+                               float* w1_out, float* w2_out, void* stream) {
+  static const char* fn = "ttt_mlp_gated_fwd";
+  ttt_status_t st = gate_check(fn, x, TTT_BF16, theta_lr, eta_base, B, T, H, dx, eta);
+  if (st == TTT_OK)
+    st = mlp_impl(q, k, v, eta, w1_0, w2_0, w0_per_batch, B, H, T, d, hidden, b, qkv_dtype, z,
+                  w1_out, w2_out, stream, fn, true);
+  if (st != TTT_OK) return st;
+  const int64_t units = (int64_t)B * H, es = qkv_dtype == TTT_F32 ? 4 : 2, seq = units * T * d;
+  const int64_t wn = (w0_per_batch ? units : (int64_t)H) * hidden * d * 4;
+  const Range scan[] = {rng("q", q, seq * es), rng("k", k, seq * es), rng("v", v, seq * es),
+                        rng("w1_0", w1_0, wn), rng("w2_0", w2_0, wn), rng("z", z, seq * 4),
+                        rng("w1_out", w1_out, units * hidden * d * 4),
+                        rng("w2_out", w2_out, units * hidden * d * 4)};
+  st = gate_scan_alias(fn, x, theta_lr, eta, B, T, H, dx, scan, 8, 5);
+  if (st != TTT_OK) return st;
+  st = gate_launch(fn, x, theta_lr, eta_base, B, T, H, dx, eta, stream);
+  if (st != TTT_OK) return st;
+  return mlp_impl(q, k, v, eta, w1_0, w2_0, w0_per_batch, B, H, T, d, hidden, b, qkv_dtype, z,
+                  w1_out, w2_out, stream, fn);
 }
 
 const char* ttt_status_str(ttt_status_t s) {

@@ -70,6 +70,20 @@ struct LinearBwdArgs {
 };
 hipError_t launch_linear_bwd(const LinearBwdArgs& a, hipStream_t s);
 
+// Learning-rate gate: eta[b][h][t] = eta_base * sigmoid(theta[h] . x[b][t]).
+struct GateArgs {
+  const void* x;       // [B][T][dx] bf16
+  const float* theta;  // [H][dx]
+  float* eta;          // [B][H][T]
+  float eta_base;
+  int B;
+  int T;
+  int H;
+  int dx;  // multiple of 32
+};
+// tokens_per_workgroup: 32, 64 or 0 (chosen from the token count)
+hipError_t launch_lr_gate(const GateArgs& a, int tokens_per_workgroup, hipStream_t s);
+
 // One decode step for every (batch, head) unit.
 struct StepArgs {
   const void* q;  // [B][H][d]

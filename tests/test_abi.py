@@ -138,3 +138,81 @@ def test_mlp_argument_checks(lib):
     assert f(b=32) == status("TTT_ERR_UNSUPPORTED")
     assert f(dt=_lib.TTT_F32) == status("TTT_ERR_UNSUPPORTED")
     assert f(hidden=-1) == status("TTT_ERR_SHAPE")
+
+
+def gate(lib, **kw):
+    args = dict(x=A[0], dt=_lib.TTT_BF16, theta=A[1], eta_base=0.1, B=1, T=16, H=2, dx=64,
+                eta=A[2])
+    args.update(kw)
+    return lib.ttt_lr_gate(args["x"], args["dt"], args["theta"], args["eta_base"], args["B"],
+                           args["T"], args["H"], args["dx"], args["eta"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dx=48), "TTT_ERR_UNSUPPORTED"),
+    (dict(dx=0), "TTT_ERR_UNSUPPORTED"),
+    (dict(dx=-32), "TTT_ERR_SHAPE"),
+    (dict(T=-1), "TTT_ERR_SHAPE"),
+    (dict(dt=_lib.TTT_F32), "TTT_ERR_UNSUPPORTED"),
+    (dict(dt=7), "TTT_ERR_DTYPE"),
+    (dict(eta_base=float("nan")), "TTT_ERR_VALUE"),
+    (dict(eta_base=float("-inf")), "TTT_ERR_VALUE"),
+    (dict(x=None), "TTT_ERR_NULL"),
+    (dict(eta=None), "TTT_ERR_NULL"),
+    (dict(theta=A[1] + 4), "TTT_ERR_ALIGN"),
+    (dict(eta=A[0] + 64), "TTT_ERR_ALIAS"),     # inside x
+    (dict(eta=A[1]), "TTT_ERR_ALIAS"),          # theta_lr
+    (dict(B=1 << 16, T=1 << 12, H=1 << 4), "TTT_ERR_SHAPE"),
+    (dict(B=0), "TTT_OK"),
+    (dict(H=0), "TTT_OK"),
+])
+def test_lr_gate_argument_checks(lib, kw, expect):
+    assert gate(lib, **kw) == status(expect), lib.ttt_last_error()
+    if expect != "TTT_OK":
+        assert lib.ttt_last_error().startswith(b"ttt_lr_gate:")
+
+
+def test_lr_gate_tuned_rejects_launch_shapes(lib):
+    f = lambda tpw: lib.ttt_lr_gate_tuned(A[0], _lib.TTT_BF16, A[1], 0.1, 1, 16, 2, 64, A[2],
+                                          None, tpw)
+    assert f(48) == status("TTT_ERR_UNSUPPORTED")
+    assert f(16) == status("TTT_ERR_UNSUPPORTED")
+
+
+def gated_linear(lib, **kw):
+    args = dict(q=A[0], k=A[1], v=A[2], x=A[7], theta=A[8], eta_base=1.0, dx=64, w0=A[4],
+                per_batch=0, B=1, H=1, T=16, d=64, b=16, dt=_lib.TTT_BF16, eta=A[3], z=A[5],
+                w=A[6])
+    args.update(kw)
+    a = args
+    return lib.ttt_linear_gated_fwd(a["q"], a["k"], a["v"], a["x"], a["theta"], a["eta_base"],
+                                    a["dx"], a["w0"], a["per_batch"], a["B"], a["H"], a["T"],
+                                    a["d"], a["b"], a["dt"], a["eta"], a["z"], a["w"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dx=40), "TTT_ERR_UNSUPPORTED"),       # the gate's checks
+    (dict(theta=None), "TTT_ERR_NULL"),
+    (dict(d=32), "TTT_ERR_UNSUPPORTED"),        # the scan's checks, before any launch
+    (dict(z=A[1]), "TTT_ERR_ALIAS"),
+    (dict(eta=A[0]), "TTT_ERR_ALIAS"),          # eta over q
+    (dict(eta=A[4]), "TTT_ERR_ALIAS"),          # eta over w0
+    (dict(z=A[7]), "TTT_ERR_ALIAS"),            # z over x
+    (dict(w=A[8]), "TTT_ERR_ALIAS"),            # w_out over theta_lr
+    (dict(B=0), "TTT_OK"),
+])
+def test_linear_gated_argument_checks(lib, kw, expect):
+    assert gated_linear(lib, **kw) == status(expect), lib.ttt_last_error()
+    if expect != "TTT_OK":
+        assert lib.ttt_last_error().startswith(b"ttt_linear_gated_fwd:")
+
+
+def test_mlp_gated_argument_checks(lib):
+    f = lambda **kw: lib.ttt_mlp_gated_fwd(A[0], A[1], A[2], A[7], A[8], 0.1, kw.get("dx", 64),
+                                           A[4], A[9], 0, 1, 1, 16, 64, kw.get("hidden", 256),
+                                           16, _lib.TTT_BF16, kw.get("eta", A[3]), A[5], A[6],
+                                           A[10], None)
+    assert f(hidden=128) == status("TTT_ERR_UNSUPPORTED")
+    assert f(dx=33) == status("TTT_ERR_UNSUPPORTED")
+    assert f(eta=A[9]) == status("TTT_ERR_ALIAS")
+    assert lib.ttt_last_error().startswith(b"ttt_mlp_gated_fwd:")
