@@ -14,8 +14,9 @@ kernel (algorithmic bytes / measured kernel time vs 8 TB/s HBM), the fp64
 oracle timed on the host cores as a baseline, and (unless --no-extras) the
 other workloads: the b sweep, the 125M and long-context TTT-Linear shapes,
 TTT-Linear with the LayerNorm + residual inner model (1.3B and 125M shapes),
-TTT-MLP, the one-token decode steps of the three models, and a
-streaming-copy bandwidth reference.
+TTT-MLP, the one-token decode steps of the three models, the forward with
+checkpoints and the backward of TTT-Linear, the learning-rate gate and the
+gated scan, and a streaming-copy bandwidth reference.
 
 --pmc-calibrate additionally launches the streaming copy kernel on a known
 byte count, so that a hardware-counter run of this script can scale the
@@ -328,6 +329,83 @@ def decode_case(kind, B, H, steps, warmup, b=16, seed=11):
                       "after a 512 MiB cache flush"}
 
 
+def bwd_alg_bytes(wl) -> int:
+    """Backward with one state checkpoint per 16-token mini-batch: read q, k,
+    v (bf16), eta, dz and the checkpoints (64 x 64 fp32 per 16 tokens); write
+    dq, dk, dv, deta (fp32) and dW0."""
+    per_tok = 3 * wl.d * 2 + 4 + wl.d * 4 + wl.d * wl.d * 4 // 16 + 3 * wl.d * 4 + 4
+    return wl.token_heads * per_tok + wl.units * wl.d * wl.d * 4
+
+
+def training_case(wl, steps, warmup):
+    """ttt_linear_fwd_ckpt then ttt_linear_bwd on one workload (b = 16), timed
+    separately; dz is a seeded N(0, 0.01) draw."""
+    import torch
+    from test_rnn_layers_head_amd import inputs, ttt_linear_bwd, ttt_linear_fwd_ckpt
+    x = inputs.make_inputs(wl)
+    d = device_inputs(x)
+    g = torch.Generator().manual_seed(17)
+    dz = (torch.randn(wl.B, wl.H, wl.T, wl.d, generator=g) * 0.1).cuda()
+    nt = (wl.T + 15) // 16
+    z = torch.empty((wl.B, wl.H, wl.T, wl.d), device="cuda")
+    w = torch.empty((wl.B, wl.H, wl.d, wl.d), device="cuda")
+    ck = torch.empty((wl.B, wl.H, nt, wl.d, wl.d), device="cuda")
+    ws = torch.empty_like(ck)
+    fwd = lambda: ttt_linear_fwd_ckpt(d["q"], d["k"], d["v"], d["eta"], d["w0"], 16, z=z, w_out=w,
+                                      w_ckpt=ck)
+    fwd()
+    bwd = lambda: ttt_linear_bwd(d["q"], d["k"], d["v"], d["eta"], ck, 16, dz, workspace=ws)
+    _, kf, _ = time_launches(fwd, steps, warmup)
+    _, kb, _ = time_launches(bwd, steps, warmup)
+    grads = bwd()
+    torch.cuda.synchronize()
+    assert all(torch.isfinite(t).all().item() for t in grads)
+    fb = linear_alg_bytes(wl) + wl.units * nt * wl.d * wl.d * 4
+    bb = bwd_alg_bytes(wl)
+    return {"workload": wl.name, "b": 16, "fwd_ckpt_us": kf, "bwd_us": kb,
+            "fwd_alg_bytes": fb, "bwd_alg_bytes": bb,
+            "fwd_hbm_frac": fb / (kf * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "bwd_hbm_frac": bb / (kb * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "train_token_heads_per_s": wl.token_heads / ((kf + kb) * 1e-6)}
+
+
+def gate_alg_bytes(wl) -> int:
+    """Learning-rate gate: read x (bf16) and theta_lr (fp32), write eta."""
+    return wl.B * wl.T * wl.gate_dx * 2 + wl.H * wl.gate_dx * 4 + wl.token_heads * 4
+
+
+def gate_case(wl, steps, warmup):
+    """ttt_lr_gate alone (both launch shapes) and ttt_linear_gated_fwd (gate +
+    scan) on one gated workload."""
+    import torch
+    from test_rnn_layers_head_amd import inputs, ttt_linear_gated_fwd, ttt_lr_gate
+    x = inputs.make_inputs(wl)
+    d = device_inputs(x)
+    gx = torch.from_numpy(x.gate_x_raw.view(np.int16)).cuda().view(torch.bfloat16)
+    th = torch.from_numpy(x.theta_lr).cuda()
+    eta = torch.empty((wl.B, wl.H, wl.T), device="cuda")
+    z = torch.empty((wl.B, wl.H, wl.T, wl.d), device="cuda")
+    w = torch.empty((wl.B, wl.H, wl.d, wl.d), device="cuda")
+    gb = gate_alg_bytes(wl)
+    res = {"workload": wl.name, "dx": wl.gate_dx, "gate_alg_bytes": gb}
+    for tpw in (32, 64):
+        _, k, spread = time_launches(lambda: ttt_lr_gate(gx, th, x.eta_base, eta=eta,
+                                                         tokens_per_workgroup=tpw), steps, warmup)
+        res[f"gate_us_tpw{tpw}"] = k
+        res[f"gate_hbm_frac_tpw{tpw}"] = gb / (k * 1e-6) / 1e9 / HBM_PEAK_GBS
+    launch = lambda: ttt_linear_gated_fwd(d["q"], d["k"], d["v"], gx, th, x.eta_base, d["w0"], 16,
+                                          eta=eta, z=z, w_out=w)
+    wall, k, _ = time_launches(launch, steps, warmup)
+    assert torch.isfinite(z).all().item()
+    res["gated_fwd_us"] = k
+    res["gated_fwd_token_heads_per_s"] = wl.token_heads / (k * 1e-6)
+    res["gated_fwd_alg_bytes"] = gb + linear_alg_bytes(wl)
+    res["gated_fwd_hbm_frac"] = res["gated_fwd_alg_bytes"] / (k * 1e-6) / 1e9 / HBM_PEAK_GBS
+    del d, gx, z, w
+    torch.cuda.empty_cache()
+    return res
+
+
 def stream_copy_GBps(nbytes=1 << 30, reps=10):
     import torch
     from test_rnn_layers_head_amd import bench_copy
@@ -488,6 +566,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="also launch the 1 GiB streaming copy used to scale byte counters")
+    ap.add_argument("--only", choices=("train", "decode", "gate"),
+                    help="run one group of the secondary measurements and print it (for profiling)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "KERNEL", "SKIP", "TAKE"),
                     help="summarise a rocprofv3 --kernel-trace --stats run of this script")
@@ -517,6 +597,18 @@ def main():
     _lib.lib()  # fail loudly if the HIP library is missing
 
     wl = inputs.workload(3)
+    if args.only == "train":
+        print(json.dumps({w.name: training_case(w, max(5, args.steps // 5), 10)
+                          for w in (wl, inputs.workload(2))}))
+        return 0
+    if args.only == "gate":
+        print(json.dumps({inputs.workload(i).name: gate_case(inputs.workload(i), 20, 20)
+                          for i in (8, 9)}))
+        return 0
+    if args.only == "decode":
+        print(json.dumps({f"decode-{k}-B{B}-H{H}": decode_case(k, B, H, 100, 200)
+                          for k, B, H in DECODE_CASES}))
+        return 0
     b = 16
     log(f"[bench] generating {wl.name} inputs")
     x = inputs.make_inputs(wl)
@@ -548,6 +640,12 @@ def main():
             w6 = inputs.workload(wid)
             log(f"[bench] {w6.name}")
             extras[w6.name] = ln_case(w6, 16, max(5, args.steps // 2), EXTRA_WARMUP)
+        for wid in (8, 9):
+            wg = inputs.workload(wid)
+            log(f"[bench] learning-rate gate and gated scan, {wg.name}")
+            extras[f"gate-{wg.name}"] = gate_case(wg, max(5, args.steps // 2), 20)
+        log(f"[bench] forward with checkpoints + backward, {wl.name}")
+        extras[f"train-{wl.name}"] = training_case(wl, max(5, args.steps // 5), 10)
         for kind, B, H in DECODE_CASES:
             log(f"[bench] decode step {kind} B={B} H={H}")
             extras[f"decode-{kind}-B{B}-H{H}"] = decode_case(kind, B, H, 100, 200)
