@@ -350,11 +350,10 @@ def training_case(wl, steps, warmup):
     z = torch.empty((wl.B, wl.H, wl.T, wl.d), device="cuda")
     w = torch.empty((wl.B, wl.H, wl.d, wl.d), device="cuda")
     ck = torch.empty((wl.B, wl.H, nt, wl.d, wl.d), device="cuda")
-    ws = torch.empty_like(ck)
     fwd = lambda: ttt_linear_fwd_ckpt(d["q"], d["k"], d["v"], d["eta"], d["w0"], 16, z=z, w_out=w,
                                       w_ckpt=ck)
     fwd()
-    bwd = lambda: ttt_linear_bwd(d["q"], d["k"], d["v"], d["eta"], ck, 16, dz, workspace=ws)
+    bwd = lambda: ttt_linear_bwd(d["q"], d["k"], d["v"], d["eta"], ck, 16, dz)
     _, kf, _ = time_launches(fwd, steps, warmup)
     _, kb, _ = time_launches(bwd, steps, warmup)
     grads = bwd()

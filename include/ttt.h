@@ -146,9 +146,9 @@ ttt_status_t ttt_linear_ln_fwd(const void* q, const void* k, const void* v,
  * and writing (fp32)
  *   dq, dk, dv : [B][H][T][d];  deta : [B][H][T]
  *   dw0 : [B][H][d][d], per unit (sum over the batch for a shared W0)
- * workspace: caller-owned scratch of the same size as w_ckpt (the adjoint
- * state at the end of every mini-batch).  Outputs and workspace must not
- * overlap each other or an input.
+ * Outputs must not overlap each other or an input.  T = 0 writes
+ * dw0 = dw_T (or zeros).  One workgroup per (batch, head); the adjoint state
+ * stays on chip, nothing beyond the outputs is written.
  */
 ttt_status_t ttt_linear_fwd_ckpt(const void* q, const void* k, const void* v,
                                  const float* eta, const float* w0,
@@ -161,8 +161,7 @@ ttt_status_t ttt_linear_bwd(const void* q, const void* k, const void* v,
                             int32_t H, int32_t T, int32_t d, int32_t b,
                             ttt_dtype_t qkv_dtype, const float* dz,
                             const float* dw_T, float* dq, float* dk, float* dv,
-                            float* deta, float* dw0, float* workspace,
-                            void* stream);
+                            float* deta, float* dw0, void* stream);
 
 /*
  * Decode steps (§6.11: generation runs the primal form, one token at a

@@ -146,7 +146,7 @@ def ttt_linear_fwd_ckpt(q, k, v, eta, w0, b: int, z=None, w_out=None, w_ckpt=Non
     return z, w_out, w_ckpt
 
 
-def ttt_linear_bwd(q, k, v, eta, w_ckpt, b: int, dz, dw_T=None, workspace=None, stream=None):
+def ttt_linear_bwd(q, k, v, eta, w_ckpt, b: int, dz, dw_T=None, stream=None):
     """Backward of the TTT-Linear scan (include/ttt.h): given dz = dL/dZ and
     optionally dw_T = dL/dW_T, returns (dq, dk, dv, deta, dw0), fp32, with
     dw0 per unit [B, H, d, d].  w_ckpt comes from ttt_linear_fwd_ckpt."""
@@ -154,22 +154,19 @@ def ttt_linear_bwd(q, k, v, eta, w_ckpt, b: int, dz, dw_T=None, workspace=None, 
     f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=q.device)
     dq, dk, dv, deta, dw0 = f32(B, H, T, d), f32(B, H, T, d), f32(B, H, T, d), f32(B, H, T), \
         f32(B, H, d, d)
-    if workspace is None:
-        workspace = f32(*w_ckpt.shape)
-    dev = _check_tensors(dict(q=q, k=k, v=v, eta=eta, w_ckpt=w_ckpt, dz=dz, dw_T=dw_T,
-                              workspace=workspace))
-    for name, t in (("dz", dz), ("dw_T", dw_T), ("w_ckpt", w_ckpt), ("workspace", workspace)):
+    dev = _check_tensors(dict(q=q, k=k, v=v, eta=eta, w_ckpt=w_ckpt, dz=dz, dw_T=dw_T))
+    for name, t in (("dz", dz), ("dw_T", dw_T), ("w_ckpt", w_ckpt)):
         if t is not None and t.dtype != torch.float32:
             raise TypeError(f"{name} must be float32")
     if tuple(dz.shape) != (B, H, T, d):
         raise ValueError("dz must be [B, H, T, d]")
-    if tuple(w_ckpt.shape) != (B, H, (T + 15) // 16, d, d) or workspace.shape != w_ckpt.shape:
-        raise ValueError("w_ckpt / workspace must be [B, H, ceil(T/16), d, d]")
+    if tuple(w_ckpt.shape) != (B, H, (T + 15) // 16, d, d):
+        raise ValueError("w_ckpt must be [B, H, ceil(T/16), d, d]")
     with torch.cuda.device(dev):
         _lib.check(_lib.lib().ttt_linear_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w_ckpt),
                                              B, H, T, d, int(b), _dtype_code(q), _ptr(dz),
                                              _ptr(dw_T), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(deta),
-                                             _ptr(dw0), _ptr(workspace), _stream(dev, stream)))
+                                             _ptr(dw0), _stream(dev, stream)))
     return dq, dk, dv, deta, dw0
 
 

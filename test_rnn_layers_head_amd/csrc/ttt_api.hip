@@ -284,7 +284,7 @@ ttt_status_t linear_bwd_impl(const void* q, const void* k, const void* v, const 
                             const float* w_ckpt, int32_t B, int32_t H, int32_t T, int32_t d,
                             int32_t b, ttt_dtype_t dt, const float* dz, const float* dw_T,
                             float* dq, float* dk, float* dv, float* deta, float* dw0,
-                            float* workspace, void* stream) {
+                            void* stream) {
   static const char* fn = "ttt_linear_bwd";
   const int64_t units = (int64_t)B * H;
   const int64_t seq = units * T * d;
@@ -293,8 +293,7 @@ ttt_status_t linear_bwd_impl(const void* q, const void* k, const void* v, const 
                       rng("eta", eta, units * T * 4), rng("w_ckpt", w_ckpt, nck),
                       rng("dz", dz, seq * 4), rng("dw_T", dw_T, units * d * d * 4)};
   const Range out[] = {rng("dq", dq, seq * 4), rng("dk", dk, seq * 4), rng("dv", dv, seq * 4),
-                       rng("deta", deta, units * T * 4), rng("dw0", dw0, units * d * d * 4),
-                       rng("workspace", workspace, nck)};
+                       rng("deta", deta, units * T * 4), rng("dw0", dw0, units * d * d * 4)};
   if (dt != TTT_F32 && dt != TTT_BF16) return fail(TTT_ERR_DTYPE, "%s: unknown qkv_dtype %d", fn, (int)dt);
   if (B < 0 || H < 0 || T < 0 || d < 0 || b < 0)
     return fail(TTT_ERR_SHAPE, "%s: negative size (B=%d H=%d T=%d d=%d b=%d)", fn, B, H, T, d, b);
@@ -311,19 +310,18 @@ ttt_status_t linear_bwd_impl(const void* q, const void* k, const void* v, const 
     if (in[i].lo & 15) return fail(TTT_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, in[i].name);
   }
   if (T > 0 && !w_ckpt) return fail(TTT_ERR_NULL, "%s: w_ckpt is NULL", fn);
-  for (int o = 0; o < 6; ++o) {
+  for (int o = 0; o < 5; ++o) {
     if ((o != 4 && T == 0)) continue;
     if (!out[o].lo) return fail(TTT_ERR_NULL, "%s: %s is NULL", fn, out[o].name);
     if (out[o].lo & 15) return fail(TTT_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, out[o].name);
     for (int i = 0; i < 7; ++i)
       if (overlap(out[o], in[i]))
         return fail(TTT_ERR_ALIAS, "%s: %s overlaps input %s", fn, out[o].name, in[i].name);
-    for (int o2 = o + 1; o2 < 6; ++o2)
+    for (int o2 = o + 1; o2 < 5; ++o2)
       if (overlap(out[o], out[o2]))
         return fail(TTT_ERR_ALIAS, "%s: %s and %s overlap", fn, out[o].name, out[o2].name);
   }
-  ttt::LinearBwdArgs a{q, k, v, eta, w_ckpt, dz, dw_T, dq, dk, dv, deta, dw0, workspace,
-                       (int)units, H, T};
+  ttt::LinearBwdArgs a{q, k, v, eta, w_ckpt, dz, dw_T, dq, dk, dv, deta, dw0, (int)units, H, T};
   hipError_t e = ttt::launch_linear_bwd(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return TTT_OK;
@@ -447,9 +445,9 @@ ttt_status_t ttt_linear_bwd(const void* q, const void* k, const void* v, const f
                             const float* w_ckpt, int32_t B, int32_t H, int32_t T, int32_t d,
                             int32_t b, ttt_dtype_t qkv_dtype, const float* dz, const float* dw_T,
                             float* dq, float* dk, float* dv, float* deta, float* dw0,
-                            float* workspace, void* stream) {
+                            void* stream) {
   return linear_bwd_impl(q, k, v, eta, w_ckpt, B, H, T, d, b, qkv_dtype, dz, dw_T, dq, dk, dv,
-                         deta, dw0, workspace, stream);
+                         deta, dw0, stream);
 }
 
 ttt_status_t ttt_mlp_step(const void* q, const void* k, const void* v, const float* eta,

@@ -63,7 +63,6 @@ struct LinearBwdArgs {
   float* dv;
   float* deta;           // [units][T]
   float* dw0;            // [units][64][64]
-  float* wb_ckpt;        // workspace [units][ceil(T/16)][64][64]
   int units;
   int H;
   int T;

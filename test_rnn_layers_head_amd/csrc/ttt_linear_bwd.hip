@@ -7,80 +7,114 @@
 // in reverse.  Per mini-batch (columns are tokens, D = diag(eta), W the
 // checkpointed state, A = triu(K^T Q) with s <= t, §3.6):
 //   forward   E = W K - V, G = 2 E D, Z = W Q - G A, W' = W - G K^T
-//   backward  (Zb, Wb' the adjoints of Z and W'; the gradient of the loss
-//             with respect to G is Gb = -(Wb' K + Zb A^T))
-//     Gt = 2 (Wb' K + Zb A^T) D        (= dL/dV, and -dL/dE)
+//   backward  (Zb, Wb' the adjoints of Z and W'; Gn = Wb' K + Zb A^T is
+//             minus the adjoint of G)
+//     Gt = 2 Gn D                      (= dL/dV, and -dL/dE)
 //     Wb = Wb' + Zb Q^T - Gt K^T       (the adjoint of W)
 //     Ab = triu(-G^T Zb)
 //     dQ = W^T Zb + K Ab
 //     dK = -W^T Gt + Q Ab^T - Wb'^T G
-//     deta_t = -sum_i (Wb' K + Zb A^T)[i, t] 2 E[i, t]
-// The adjoint recurrence has the forward's form (rows of Wb evolve
-// independently), the other outputs do not feed it.  Two kernels:
-//   1. the reverse scan over 16-row slices of Wb: writes dV = Gt, the
-//      adjoint at the end of every mini-batch (Wb', a checkpoint of its own)
-//      and finally dW0 = Wb_0;
-//   2. one workgroup per (unit, mini-batch), fully parallel: dQ, dK, deta
-//      from W, Wb' and the tile's inputs.
-// All products are fp32 MFMA (16x16x4: exact fp32 products, fp32 sums).
+//     deta_t = -sum_i Gn[i, t] 2 E[i, t]
 //
-// MFMA 16x16x4 f32 operand layouts (wave64, lane (c, g), c = lane % 16,
-// g = lane / 16): A-operand lane holds A[c][g], B-operand lane holds B[g][c],
-// accumulator register r holds C[4g + r][c].  A contraction over 16 tokens
-// whose values a lane holds in registers r (token 4g + r) runs as four MFMAs
-// k = 0..3 taking token 4g + k from each lane group g: the token order in
-// the reduction is permuted, and both operands use the same permutation.
+// One workgroup per (batch, head) unit, five waves.  Wave 4 streams the tiles
+// K, Q, V (bf16), dz (fp32) and eta in reverse order into an LDS ring by
+// buffer->LDS DMA.  Waves 0..3 each own 16 rows of the adjoint state Wb
+// (the rows evolve independently, like the forward's) in MFMA accumulators,
+// read their 16 rows of the tile's checkpoint W from HBM two tiles ahead,
+// and per tile compute their rows' share of everything: the state update,
+// dV, and partial sums over their rows of dQ, dK, Ab and deta.  The partial
+// sums go to a double-buffered LDS area; one tile later (after the next
+// barrier) wave w adds the four partials for 16 columns, applies the K Ab
+// and Q Ab^T terms and writes dQ, dK (wave 0 also deta).  So each tile costs
+// one barrier, and the adjoint state never leaves the chip.
+//
+// Products: 16x16x32 bf16 MFMA with fp32 accumulation.  K, Q, V are exact in
+// bf16; fp32 operands (states, dz, A, G, Gt, Ab) enter as hi + lo bf16 pairs
+// and the three significant products (hi*hi, hi*lo, lo*hi) are kept, about
+// 2^-16 relative per product.  Transposed copies (Q, K and the two states
+// with columns in lanes) come from one-hot selection MFMAs, which are exact.
+//
+// 16x16x32 bf16 layouts (wave64, lane (c, g), c = lane % 16, g = lane / 16):
+// A lane holds A[c][8g .. 8g + 7], B lane holds B[8g .. 8g + 7][c],
+// accumulator register r holds C[4g + r][c].  Contractions over the 16
+// tokens (or 16 rows) of a lane's registers use the slots of lane group g as
+// [4 values hi | the same 4 values lo], both operands alike.
+// The state accumulators hold columns in the permuted order
+// sigma(m, 4g + r) = 32 (m >> 1) + 8g + 4 (m & 1) + r, so that the hi/lo
+// split of blocks 2h, 2h + 1 is operand chunk h in natural column order.
 #include "ttt_device.h"
 #include "ttt_launch.h"
+#include "ttt_linear_ops.h"
 
 namespace ttt {
 namespace {
 
-__device__ __forceinline__ float bf(const uint16_t* p) {
-  return __builtin_bit_cast(float, ((uint32_t)*p) << 16);
-}
-
-// ========================================================= 1. reverse scan
-// Workgroup = (unit, slice of 16 rows): wave 0 computes, wave 1 streams the
-// tiles in reverse order into an LDS ring (buffer->LDS DMA, D tiles ahead).
 struct BwdGeom {
-  static constexpr int KB = 16 * 64 * 2;  // K or Q tile, bf16 [token][col]
-  static constexpr int ZB = 16 * 16 * 4;  // this slice's dz rows, fp32 [token][row]
-  static constexpr int RAW = 2 * KB + ZB + 64;
-  static constexpr int NI = 2 + 2 + 1 + 1;  // DMA ops per tile
-  static constexpr int D = 8;
+  static constexpr int KB = 16 * 64 * 2;          // K, Q or V tile: bf16 [token][col], swizzled
+  static constexpr int ZB = 16 * 64 * 4;          // dz tile: fp32 [token][col], swizzled
+  static constexpr int SLOT = 3 * KB + ZB + 64;   // + eta
+  static constexpr int NI = 2 + 2 + 2 + 4 + 1;    // DMA ops per tile
+  static constexpr int D = 5;                     // tiles in flight
   static constexpr int NST = D + 2;
+  // partial sums of one compute wave: dQ, dK fragments (4 blocks), Ab, deta
+  static constexpr int RQ = 4 * 64 * 16;
+  static constexpr int RA = 64 * 16;
+  static constexpr int RW = 2 * RQ + RA + 64;
+  static constexpr int RING = NST * SLOT;
+  static constexpr int LDS = RING + 2 * 4 * RW;
+  static constexpr int THREADS = 5 * 64;
 };
 
-__global__ void __launch_bounds__(128) linear_bwd_state_kernel(LinearBwdArgs a) {
-  using G = BwdGeom;
-  __shared__ __attribute__((aligned(16))) char smem[G::NST * G::RAW];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int c = lane & 15, g = lane >> 4;
-  const int unit = blockIdx.x >> 2, slice = blockIdx.x & 3;
-  if (unit >= a.units) return;
-  const int T = a.T, ntiles = (T + 15) >> 4;
-  const int rbase = slice * 16;
+// column of block m, position p (0..15) of the state accumulators
+__device__ __forceinline__ int scol(int m, int p) {
+  return 32 * (m >> 1) + 8 * (p >> 2) + 4 * (m & 1) + (p & 3);
+}
 
-  if (wave == 1) {  // ------------------------------------------- loader
-    const size_t uoff = (size_t)unit * T * 64;
+__device__ __forceinline__ uint2 pack4(f32x4 x) {
+  return make_uint2(pack_rne(x[0], x[1]), pack_rne(x[2], x[3]));
+}
+
+__device__ __forceinline__ f32x4 bf4(uint2 u) {
+  return f32x4{__builtin_bit_cast(float, u.x << 16), __builtin_bit_cast(float, u.x & 0xffff0000u),
+               __builtin_bit_cast(float, u.y << 16), __builtin_bit_cast(float, u.y & 0xffff0000u)};
+}
+
+__global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdArgs a) {
+  using G = BwdGeom;
+  __shared__ __attribute__((aligned(16))) char smem[G::LDS];
+  char* const red = smem + G::RING;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int unit = blockIdx.x;
+  const int T = a.T, ntiles = (T + 15) >> 4;
+  const size_t uoff = (size_t)unit * T * 64;
+
+  if (wave == 4) {  // --------------------------------------------- loader
     const __amdgpu_buffer_rsrc_t rk = make_rsrc((const short*)a.k + uoff, (uint32_t)T * 128);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc((const short*)a.q + uoff, (uint32_t)T * 128);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const short*)a.v + uoff, (uint32_t)T * 128);
     const __amdgpu_buffer_rsrc_t rz = make_rsrc(a.dz + uoff, (uint32_t)T * 256);
     const __amdgpu_buffer_rsrc_t re = make_rsrc(a.eta + (size_t)unit * T, (uint32_t)T * 4);
-    // iteration i handles tile ntiles - 1 - i
+    // iteration i handles tile ntiles - 1 - i; 16-byte chunk p of token row r
+    // lands at chunk p ^ (r & 7) (bf16 tiles) or p ^ r (dz)
     auto issue = [&](int i) {
       const int j = ntiles - 1 - i;
-      char* st = smem + (i % G::NST) * G::RAW;
-      const uint32_t tb = (uint32_t)j * 2048;
+      char* st = smem + (i % G::NST) * G::SLOT;
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
-        dma16(rk, st + n * 1024, tb + n * 1024 + lane * 16);
-        dma16(rq, st + G::KB + n * 1024, tb + n * 1024 + lane * 16);
+        const int r = 8 * n + (lane >> 3);
+        const uint32_t vo = (uint32_t)(j * 16 + r) * 128 + (((lane & 7) ^ (r & 7)) << 4);
+        dma16(rk, st + n * 1024, vo);
+        dma16(rq, st + G::KB + n * 1024, vo);
+        dma16(rv, st + 2 * G::KB + n * 1024, vo);
       }
-      // dz[t][rbase .. rbase + 15]: token lane / 4, 16-byte part lane % 4
-      dma16(rz, st + 2 * G::KB, (uint32_t)((j * 16 + (lane >> 2)) * 64 + rbase) * 4 + (lane & 3) * 16);
-      if (lane < 16) dma4(re, st + 2 * G::KB + G::ZB, (uint32_t)(j * 16 + lane) * 4);
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int r = 4 * n + (lane >> 4);
+        dma16(rz, st + 3 * G::KB + n * 1024,
+              (uint32_t)(j * 16 + r) * 256 + (((lane & 15) ^ r) << 4));
+      }
+      if (lane < 16) dma4(re, st + 3 * G::KB + G::ZB, (uint32_t)(j * 16 + lane) * 4);
     };
     const int pro = ntiles < G::D ? ntiles : G::D;
     for (int i = 0; i < pro; ++i) issue(i);
@@ -93,206 +127,244 @@ __global__ void __launch_bounds__(128) linear_bwd_state_kernel(LinearBwdArgs a) 
       }
       wg_barrier();  // B_i
     }
+    wg_barrier();  // B_end
     return;
   }
 
-  // -------------------------------------------------------------- compute
-  // Wb[cb] register r = Wb[row rbase + c][col 16 cb + 4g + r]
-  f32x4 Wb[4];
-  const size_t so = (size_t)unit * 4096 + (size_t)(rbase + c) * 64 + 4 * g;
+  // ---------------------------------------------------------- compute waves
+  const int s = wave;  // rows 16 s .. 16 s + 15
+  // outputs through buffer stores: tokens past T fall outside the descriptor
+  // and are dropped, so every tile issues the same stores (exact wait counts)
+  const __amdgpu_buffer_rsrc_t rdq = make_rsrc(a.dq + uoff, (uint32_t)T * 256);
+  const __amdgpu_buffer_rsrc_t rdk = make_rsrc(a.dk + uoff, (uint32_t)T * 256);
+  const __amdgpu_buffer_rsrc_t rdv = make_rsrc(a.dv + uoff, (uint32_t)T * 256);
+  const __amdgpu_buffer_rsrc_t rde = make_rsrc(a.deta + (size_t)unit * T, (uint32_t)T * 4);
+  auto st32 = [](float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+  };
+  const s16x4 z4 = {0, 0, 0, 0};
+  // one-hot selectors: B operand that picks column scol(m, c) out of a
+  // natural-order chunk, for m even (sel[0]) and odd (sel[1])
+  bf16x8 sel[2];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
-    Wb[cb] = a.dw_T ? *(const f32x4*)(a.dw_T + so + 16 * cb) : f32x4{0, 0, 0, 0};
-  const __amdgpu_buffer_rsrc_t rdv =
-      make_rsrc(a.dv + (size_t)unit * T * 64, (uint32_t)T * 256);
-  for (int i = 0; i < ntiles; ++i) {
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      sel[p][e] = (bf16)((g == (c >> 2) && e == 4 * p + (c & 3)) ? 1.f : 0.f);
+
+  // Wr[m] register r = Wb[row 16 s + c][scol(m, 4g + r)]
+  f32x4 Wr[4];
+  {
+    const float* dwT = a.dw_T ? a.dw_T + (size_t)unit * 4096 + (16 * s + c) * 64 : nullptr;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      Wr[m] = dwT ? *(const f32x4*)(dwT + scol(m, 4 * g)) : f32x4{0, 0, 0, 0};
+  }
+  // this wave's rows of the checkpoint of iteration i, same layout as Wr
+  auto wload = [&](int i, f32x4* w) {
     const int j = ntiles - 1 - i;
-    wg_barrier();  // B_i: tile j is in LDS
-    const char* st = smem + (i % G::NST) * G::RAW;
-    const uint16_t* Kt = (const uint16_t*)st;               // [token][col]
-    const uint16_t* Qt = (const uint16_t*)(st + G::KB);     // [token][col]
-    const float* Zs = (const float*)(st + 2 * G::KB);       // [token][row - rbase]
-    const float* Et = (const float*)(st + 2 * G::KB + G::ZB);
-
-    // Wb' = the adjoint after tile j: the checkpoint kernel 2 reads
-    float* ck = a.wb_ckpt + ((size_t)unit * ntiles + j) * 4096;
+    const float* p = a.w_ckpt + ((size_t)unit * ntiles + j) * 4096 + (16 * s + c) * 64;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-      *(f32x4*)(ck + (size_t)(rbase + c) * 64 + 16 * cb + 4 * g) = Wb[cb];
+    for (int m = 0; m < 4; ++m) w[m] = *(const f32x4*)(p + scol(m, 4 * g));
+  };
+  // three register sets in rotation: tile i uses one while the loads of
+  // tiles i + 1 and i + 2 land in the other two (a register copy of a load
+  // in flight would wait for it, so the sets rotate by unrolling instead)
+  f32x4 wA[4], wB[4], wC[4];
+  if (ntiles > 0) wload(0, wA);
+  if (ntiles > 1) wload(1, wB);
 
-    // A^T: register r = A[s = c][t = 4g + r] = k_s . q_t, kept for s <= t
-    f32x4 At = {0, 0, 0, 0};
-    for (int kk = 0; kk < 16; ++kk)
-      At = mfma_f32(bf(Qt + c * 64 + 4 * kk + g), bf(Kt + c * 64 + 4 * kk + g), At);
+  // Sums the four waves' partials of one tile for column block s and writes
+  // dQ, dK (and deta from wave 0).  q4p, k4p: Q, K of that tile at columns
+  // scol(s, c), tokens 4g .. 4g + 3.
+  auto finalize = [&](int buf, uint2 q4p, uint2 k4p, int t0) {
+    const char* rb = red + buf * 4 * G::RW;
+    f32x4 dq = {0, 0, 0, 0}, dk = {0, 0, 0, 0}, ab1 = {0, 0, 0, 0}, ab2 = {0, 0, 0, 0};
+    float de = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const char* rw = rb + w * G::RW;
+      const f32x4 x = *(const f32x4*)(rw + (s * 64 + lane) * 16);
+      const f32x4 y = *(const f32x4*)(rw + G::RQ + (s * 64 + lane) * 16);
+      const f32x4 z = *(const f32x4*)(rw + 2 * G::RQ + lane * 16);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        dq[r] += x[r];
+        dk[r] += y[r];
+        ab1[r] += z[r];
+        // transposed read: element (s' = c, t = 4g + r)
+        ab2[r] += *(const float*)(rw + 2 * G::RQ + ((4 * g + r + 16 * (c >> 2)) * 16 + (c & 3) * 4));
+      }
+      de += ((const float*)(rw + 2 * G::RQ + G::RA))[c];
+    }
+    // Ab = triu(-sum): ab1 register r = Ab[s' = 4g + r][t = c], ab2 = Ab[s' = c][t = 4g + r]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      ab1[r] = (4 * g + r <= c) ? -ab1[r] : 0.f;
+      ab2[r] = (c <= 4 * g + r) ? -ab2[r] : 0.f;
+    }
+    const Split4 a1 = split4(ab1), a2 = split4(ab2);
+    dq = mfma_k32(cat44(a1.hi, a1.lo), cat8(k4p, k4p), dq);  // + K Ab
+    dk = mfma_k32(cat44(a2.hi, a2.lo), cat8(q4p, q4p), dk);  // + Q Ab^T
+    const int col = scol(s, c);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t off = (uint32_t)((t0 + 4 * g + r) * 64 + col) * 4;
+      const float vq = dq[r], vk = dk[r];  // scalar copies: bit_cast of an element reads element 0
+      st32(vq, rdq, off);
+      st32(vk, rdk, off);
+    }
+    st32(de, rde, (s == 0 && g == 0) ? (uint32_t)(t0 + c) * 4 : 0x80000000u);
+  };
+
+  uint2 q4p = make_uint2(0, 0), k4p = make_uint2(0, 0);
+  int t0p = 0;
+  auto body = [&](int i, const f32x4* wa0, f32x4* wnext) {
+    wload(i + 2 < ntiles ? i + 2 : ntiles - 1, wnext);  // unconditional: exact wait counts
+    wg_barrier();  // B_i: tile i in LDS; the partials of tile i - 1 are complete
+    const int j = ntiles - 1 - i, t0 = j * 16;
+    const char* st = smem + (i % G::NST) * G::SLOT;
+    const char* Kt = st;
+    const char* Qt = st + G::KB;
+    const char* Vt = st + 2 * G::KB;
+    const char* Zt = st + 3 * G::KB;
+    const float* Et = (const float*)(st + 3 * G::KB + G::ZB);
+    if (i > 0) finalize((i - 1) & 1, q4p, k4p, t0p);
+
+    const bf16x8 kc[2] = {row_chunk(Kt, c, 0, g), row_chunk(Kt, c, 1, g)};
+    const bf16x8 qc[2] = {row_chunk(Qt, c, 0, g), row_chunk(Qt, c, 1, g)};
+    // A^T: register r = A[s' = c][t = 4g + r] = k_c . q_{4g+r}, kept for s' <= t
+    f32x4 At = mfma_k32(qc[0], kc[0], f32x4{0, 0, 0, 0});
+    At = mfma_k32(qc[1], kc[1], At);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (c > 4 * g + r) At[r] = 0.f;
-    // M = Zb A^T: register r = M[row c][s = 4g + r]
-    f32x4 M = {0, 0, 0, 0};
+    const Split4 as = split4(At);
+    // Zb with rows in lanes (zr register r = Zb[row 16s + c][t = 4g + r]) and
+    // with tokens in lanes (zt register r = Zb[row 16s + 4g + r][t = c])
+    f32x4 zr;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) M = mfma_f32(At[k], Zs[(4 * g + k) * 16 + c], M);
-    // P = Wb' K: register r = P[row c][s = 4g + r]
-    f32x4 P = {0, 0, 0, 0};
+    for (int r = 0; r < 4; ++r)
+      zr[r] = *(const float*)(Zt + (4 * g + r) * 256 + (((4 * s + (c >> 2)) ^ (4 * g + r)) << 4) +
+                              (c & 3) * 4);
+    const f32x4 zt = *(const f32x4*)(Zt + c * 256 + (((4 * s + g) ^ c) << 4));
+    const Split4 zrs = split4(zr), zts = split4(zt);
+    const f32x4 er = *(const f32x4*)(Et + 4 * g);
+    const float et = Et[c];
+
+    // ---- the chain: Gt with rows in lanes, then the state update
+    const Split8 ws0 = split8(Wr[0], Wr[1]), ws1 = split8(Wr[2], Wr[3]);
+    f32x4 Pr = mfma_k32(kc[0], ws0.hi, f32x4{0, 0, 0, 0});  // register r = (Wb' K)[row c][t = 4g + r]
+    Pr = mfma_k32(kc[0], ws0.lo, Pr);
+    Pr = mfma_k32(kc[1], ws1.hi, Pr);
+    Pr = mfma_k32(kc[1], ws1.lo, Pr);
+    f32x4 Mr = mfma_k32(cat44(as.hi, as.lo), cat44(zrs.hi, zrs.hi), f32x4{0, 0, 0, 0});
+    Mr = mfma_k32(cat44(as.hi, z4), cat44(zrs.lo, zrs.lo), Mr);  // (Zb A^T)[row c][t = 4g + r]
+    f32x4 Gtr;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) P = mfma_f32(bf(Kt + c * 64 + 16 * cb + 4 * g + r), Wb[cb][r], P);
-    // Gt = 2 (P + M) D = dL/dV
-    const f32x4 e4 = *(const f32x4*)(Et + 4 * g);
-    f32x4 Gt;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) Gt[r] = 2.f * e4[r] * (P[r] + M[r]);
+    for (int r = 0; r < 4; ++r) Gtr[r] = 2.f * er[r] * (Pr[r] + Mr[r]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float gv = Gt[r];  // bit_cast of a vector element itself reads element 0
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, gv), rdv,
-                                            (uint32_t)((j * 16 + 4 * g + r) * 64 + rbase + c) * 4, 0, 0);
+      const float gv = Gtr[r];
+      st32(gv, rdv, (uint32_t)((t0 + 4 * g + r) * 64 + 16 * s + c) * 4);
     }
-    // Wb += Zb Q^T - Gt K^T: accumulator cb, register r = [col 16 cb + 4g + r][row c]
+    // Wb' with columns in lanes: BB[m] register r = Wb'[row 16s + 4g + r][scol(m, c)]
+    uint2 BBh[4], BBl[4];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int m = 0; m < 4; ++m) {
+      BBh[m] = pack4(mfma_k32((m >> 1) ? ws1.hi : ws0.hi, sel[m & 1], f32x4{0, 0, 0, 0}));
+      BBl[m] = pack4(mfma_k32((m >> 1) ? ws1.lo : ws0.lo, sel[m & 1], f32x4{0, 0, 0, 0}));
+    }
+    {
+      const Split4 gts = split4(Gtr);
+      const bf16x8 zgh = cat44(zrs.hi, gts.hi), zgl = cat44(zrs.lo, gts.lo);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int t = 4 * g + k;
-        Wb[cb] = mfma_f32(bf(Qt + t * 64 + 16 * cb + c), Zs[t * 16 + c], Wb[cb]);
-        Wb[cb] = mfma_f32(-bf(Kt + t * 64 + 16 * cb + c), Gt[k], Wb[cb]);
+      for (int m = 0; m < 4; ++m) {  // Wb = Wb' + Zb Q^T - Gt K^T
+        // Q, K with columns scol(m, c) in lanes, tokens 4g .. 4g + 3 in registers
+        const uint2 q4 = pack4(mfma_k32(qc[m >> 1], sel[m & 1], f32x4{0, 0, 0, 0}));
+        const uint2 k4 = pack4(mfma_k32(kc[m >> 1], sel[m & 1], f32x4{0, 0, 0, 0}));
+        if (m == s) {  // kept for this wave's column block of the outputs
+          q4p = q4;
+          k4p = k4;
+        }
+        const bf16x8 qk = cat8(q4, make_uint2(k4.x ^ 0x80008000u, k4.y ^ 0x80008000u));
+        Wr[m] = mfma_k32(qk, zgh, Wr[m]);
+        Wr[m] = mfma_k32(qk, zgl, Wr[m]);
       }
-  }
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) *(f32x4*)(a.dw0 + so + 16 * cb) = Wb[cb];
-}
-
-// ==================================================== 2. per-tile outputs
-// Workgroup = (unit, tile j), four waves.  Wave w computes rows 16w .. +15
-// of E, Gb and columns 16w .. +15 of dQ, dK.
-__global__ void __launch_bounds__(256) linear_bwd_out_kernel(LinearBwdArgs a) {
-  __shared__ float sW[64 * 64], sWb[64 * 64];  // W, Wb' [row][col]
-  __shared__ float sK[16 * 64], sQ[16 * 64], sV[16 * 64], sZ[16 * 64];  // [token][col]
-  __shared__ float sG[64 * 16], sGt[64 * 16];  // G, Gt [row][token]
-  __shared__ float sEta[16], sDeta[4][16];
-  const int T = a.T, ntiles = (T + 15) >> 4;
-  const int unit = blockIdx.x / ntiles, j = blockIdx.x % ntiles;
-  if (unit >= a.units) return;
-  const int t0 = j * 16, nt = T - t0 < 16 ? T - t0 : 16;  // valid tokens of the tile
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int c = lane & 15, g = lane >> 4;
-
-  {  // stage the tile (tokens past T read as zero)
-    const float4* w = (const float4*)(a.w_ckpt + ((size_t)unit * ntiles + j) * 4096);
-    const float4* wb = (const float4*)(a.wb_ckpt + ((size_t)unit * ntiles + j) * 4096);
-    for (int e = tid; e < 1024; e += 256) {
-      ((float4*)sW)[e] = w[e];
-      ((float4*)sWb)[e] = wb[e];
     }
-    const size_t vo = ((size_t)unit * T + t0) * 64;
-    for (int e = tid; e < 1024; e += 256) {
-      const int t = e >> 6;
-      const bool ok = t < nt;
-      sK[e] = ok ? bf((const uint16_t*)a.k + vo + e) : 0.f;
-      sQ[e] = ok ? bf((const uint16_t*)a.q + vo + e) : 0.f;
-      sV[e] = ok ? bf((const uint16_t*)a.v + vo + e) : 0.f;
-      sZ[e] = ok ? a.dz[vo + e] : 0.f;
+
+    // ---- tokens in lanes: Gn, Gt, E, G (register r = [row 16s + 4g + r][t = c])
+    f32x4 Pt = mfma_k32(ws0.hi, kc[0], f32x4{0, 0, 0, 0});
+    Pt = mfma_k32(ws0.lo, kc[0], Pt);
+    Pt = mfma_k32(ws1.hi, kc[1], Pt);
+    Pt = mfma_k32(ws1.lo, kc[1], Pt);
+    f32x4 Mt = mfma_k32(cat44(zrs.hi, zrs.lo), cat44(as.hi, as.hi), f32x4{0, 0, 0, 0});
+    Mt = mfma_k32(cat44(zrs.hi, z4), cat44(as.lo, as.lo), Mt);
+    const Split8 wa_0 = split8(wa0[0], wa0[1]), wa_1 = split8(wa0[2], wa0[3]);
+    f32x4 Ew = mfma_k32(wa_0.hi, kc[0], f32x4{0, 0, 0, 0});
+    Ew = mfma_k32(wa_0.lo, kc[0], Ew);
+    Ew = mfma_k32(wa_1.hi, kc[1], Ew);
+    Ew = mfma_k32(wa_1.lo, kc[1], Ew);
+    const f32x4 vv = bf4(*(const uint2*)(Vt + swz(c, 16 * s + 4 * g)));
+    f32x4 Gtt, Gw;
+    float dp = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float gn = Pt[r] + Mt[r];
+      const float e = Ew[r] - vv[r];
+      Gtt[r] = 2.f * et * gn;
+      Gw[r] = 2.f * et * e;
+      dp -= gn * 2.f * e;
     }
-    if (tid < 16) sEta[tid] = tid < nt ? a.eta[(size_t)unit * T + t0 + tid] : 0.f;
-  }
-  __syncthreads();
+    dp += __shfl_xor(dp, 16);
+    dp += __shfl_xor(dp, 32);
+    // W with columns in lanes: WB[m] register r = W[row 16s + 4g + r][scol(m, c)]
+    uint2 WBh[4], WBl[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      WBh[m] = pack4(mfma_k32((m >> 1) ? wa_1.hi : wa_0.hi, sel[m & 1], f32x4{0, 0, 0, 0}));
+      WBl[m] = pack4(mfma_k32((m >> 1) ? wa_1.lo : wa_0.lo, sel[m & 1], f32x4{0, 0, 0, 0}));
+    }
+    // ---- partial sums over this wave's rows
+    char* rw = red + (i & 1) * 4 * G::RW + s * G::RW;
+    const Split4 gts = split4(Gtt), gws = split4(Gw);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      // register r = [t = 4g + r][col scol(m, c)]
+      f32x4 dq = mfma_k32(cat44(zts.hi, zts.lo), cat8(WBh[m], WBh[m]), f32x4{0, 0, 0, 0});
+      dq = mfma_k32(cat44(zts.hi, z4), cat8(WBl[m], WBl[m]), dq);  // W^T Zb
+      f32x4 dk = mfma_k32(cat44(gts.hi, gts.lo), cat8(WBh[m], WBh[m]), f32x4{0, 0, 0, 0});
+      dk = mfma_k32(cat44(gts.hi, z4), cat8(WBl[m], WBl[m]), dk);  // W^T Gt
+      dk = mfma_k32(cat44(gws.hi, gws.lo), cat8(BBh[m], BBh[m]), dk);
+      dk = mfma_k32(cat44(gws.hi, z4), cat8(BBl[m], BBl[m]), dk);  // + Wb'^T G
+      *(f32x4*)(rw + (m * 64 + lane) * 16) = dq;
+      *(f32x4*)(rw + G::RQ + (m * 64 + lane) * 16) = -dk;
+    }
+    // G^T Zb: register r = sum_rows G[row][s' = 4g + r] Zb[row][t = c]
+    f32x4 ab = mfma_k32(cat44(gws.hi, gws.lo), cat44(zts.hi, zts.hi), f32x4{0, 0, 0, 0});
+    ab = mfma_k32(cat44(gws.hi, z4), cat44(zts.lo, zts.lo), ab);
+    *(f32x4*)(rw + 2 * G::RQ + lane * 16) = ab;
+    if (g == 0) ((float*)(rw + 2 * G::RQ + G::RA))[c] = dp;
 
-  // ---- rows 16w + 4g + r, token c (accumulator layout [row][token])
-  const int rw = 16 * wave;
-  f32x4 E = {0, 0, 0, 0}, Pn = {0, 0, 0, 0};  // W K, Wb' K
-  for (int kk = 0; kk < 16; ++kk) {
-    const float kv = sK[c * 64 + 4 * kk + g];
-    E = mfma_f32(sW[(rw + c) * 64 + 4 * kk + g], kv, E);
-    Pn = mfma_f32(sWb[(rw + c) * 64 + 4 * kk + g], kv, Pn);
+    t0p = t0;
+    wait_lgkm0();  // the partials are in LDS before the next barrier
+  };
+  for (int i = 0; i < ntiles; i += 3) {
+    body(i, wA, wC);
+    if (i + 1 < ntiles) body(i + 1, wB, wA);
+    if (i + 2 < ntiles) body(i + 2, wC, wB);
   }
-  // A^T: register r = A[s = c][t = 4g + r] (s <= t)
-  f32x4 At = {0, 0, 0, 0};
-  for (int kk = 0; kk < 16; ++kk)
-    At = mfma_f32(sQ[c * 64 + 4 * kk + g], sK[c * 64 + 4 * kk + g], At);
+  wg_barrier();  // B_end
+  if (ntiles > 0) finalize((ntiles - 1) & 1, q4p, k4p, t0p);
+  float* o = a.dw0 + (size_t)unit * 4096 + (16 * s + c) * 64;
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-    if (c > 4 * g + r) At[r] = 0.f;
-  // Zb A^T [row][s] = sum_t Zb[row][t] A[s][t] needs A with s in the lanes
-  // of the B operand: wave 0 stores A[s][t] to LDS.
-  __shared__ float sA[16 * 16];
-  if (wave == 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sA[c * 16 + 4 * g + r] = At[r];
-  }
-  __syncthreads();
-  f32x4 M = {0, 0, 0, 0};
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    M = mfma_f32(sZ[(4 * k + g) * 64 + rw + c], sA[c * 16 + 4 * k + g], M);
-  // E = W K - V; Gn = Wb' K + Zb A^T (= -Gb); G = 2 E D; Gt = 2 Gn D
-  float dpart = 0.f;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = rw + 4 * g + r;
-    const float e = E[r] - sV[c * 64 + row];
-    const float gn = Pn[r] + M[r];
-    sG[row * 16 + c] = 2.f * sEta[c] * e;
-    sGt[row * 16 + c] = 2.f * sEta[c] * gn;
-    dpart -= gn * 2.f * e;
-  }
-  // deta_t = -sum_rows Gn 2 E: fold the 4 rows of the lane, then the 4 lane
-  // groups and the 4 waves
-  dpart += __shfl_xor(dpart, 16);
-  dpart += __shfl_xor(dpart, 32);
-  if (g == 0) sDeta[wave][c] = dpart;
-  __syncthreads();
-  if (tid < nt)
-    a.deta[(size_t)unit * T + t0 + tid] =
-        (sDeta[0][tid] + sDeta[1][tid]) + (sDeta[2][tid] + sDeta[3][tid]);
-
-  // ---- Ab = triu(-G^T Zb) [s][t]: register r = Ab[s = 4g + r][t = c]; and
-  // its transpose AbT register r = Ab[s = c][t = 4g + r]
-  f32x4 Ab = {0, 0, 0, 0}, AbT = {0, 0, 0, 0};
-  for (int kk = 0; kk < 16; ++kk) {
-    const int row = 4 * kk + g;
-    Ab = mfma_f32(sG[row * 16 + c], sZ[c * 64 + row], Ab);
-    AbT = mfma_f32(sZ[c * 64 + row], sG[row * 16 + c], AbT);
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    Ab[r] = (4 * g + r <= c) ? -Ab[r] : 0.f;
-    AbT[r] = (c <= 4 * g + r) ? -AbT[r] : 0.f;
-  }
-
-  // ---- columns 16w + 4g + r, token c (accumulator layout [col][token])
-  const int cw = 16 * wave;
-  f32x4 dQ = {0, 0, 0, 0}, dK = {0, 0, 0, 0};
-  for (int kk = 0; kk < 16; ++kk) {
-    const int row = 4 * kk + g;
-    const float w = sW[row * 64 + cw + c];
-    dQ = mfma_f32(w, sZ[c * 64 + row], dQ);                 // W^T Zb
-    dK = mfma_f32(-w, sGt[row * 16 + c], dK);                // -W^T Gt
-    dK = mfma_f32(-sWb[row * 64 + cw + c], sG[row * 16 + c], dK);  // -Wb'^T G
-  }
-  // + K Ab (contraction over s = 4g + k, Ab in registers of lane group g)
-  // + Q Ab^T: dK[col][s] += sum_t Q[col][t] Ab[s][t], t = 4g + k
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    dQ = mfma_f32(sK[(4 * g + k) * 64 + cw + c], Ab[k], dQ);
-    dK = mfma_f32(sQ[(4 * g + k) * 64 + cw + c], AbT[k], dK);
-  }
-  // register r = d?[col cw + 4g + r][token c]: one 16-byte store per lane
-  if (c < nt) {
-    const size_t o = ((size_t)unit * T + t0 + c) * 64 + cw + 4 * g;
-    *(f32x4*)(a.dq + o) = dQ;
-    *(f32x4*)(a.dk + o) = dK;
-  }
+  for (int m = 0; m < 4; ++m) *(f32x4*)(o + scol(m, 4 * g)) = Wr[m];
 }
 
 }  // namespace
 
 hipError_t launch_linear_bwd(const LinearBwdArgs& a, hipStream_t s) {
-  const int ntiles = (a.T + 15) / 16;
-  hipLaunchKernelGGL(linear_bwd_state_kernel, dim3(a.units * 4), dim3(128), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (ntiles == 0) return hipSuccess;  // dw0 = dw_T (or 0): nothing per tile
-  hipLaunchKernelGGL(linear_bwd_out_kernel, dim3(a.units * ntiles), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(linear_bwd_kernel, dim3(a.units), dim3(BwdGeom::THREADS), 0, s, a);
   return hipGetLastError();
 }
 

@@ -216,3 +216,42 @@ def test_mlp_gated_argument_checks(lib):
     assert f(dx=33) == status("TTT_ERR_UNSUPPORTED")
     assert f(eta=A[9]) == status("TTT_ERR_ALIAS")
     assert lib.ttt_last_error().startswith(b"ttt_mlp_gated_fwd:")
+
+
+def bwd(lib, **kw):
+    args = dict(q=A[0], k=A[1], v=A[2], eta=A[3], ck=A[4], B=1, H=2, T=37, d=64, b=16,
+                dt=_lib.TTT_BF16, dz=A[5], dwT=None, dq=A[6], dk=A[7], dv=A[8], deta=A[9],
+                dw0=A[10])
+    args.update(kw)
+    a = args
+    return lib.ttt_linear_bwd(a["q"], a["k"], a["v"], a["eta"], a["ck"], a["B"], a["H"], a["T"],
+                              a["d"], a["b"], a["dt"], a["dz"], a["dwT"], a["dq"], a["dk"],
+                              a["dv"], a["deta"], a["dw0"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(b=4), "TTT_ERR_UNSUPPORTED"),
+    (dict(dt=_lib.TTT_F32), "TTT_ERR_UNSUPPORTED"),
+    (dict(d=32), "TTT_ERR_UNSUPPORTED"),
+    (dict(T=-1), "TTT_ERR_SHAPE"),
+    (dict(ck=None), "TTT_ERR_NULL"),
+    (dict(dz=A[5] + 8), "TTT_ERR_ALIGN"),
+    (dict(dq=A[4]), "TTT_ERR_ALIAS"),          # an output over the checkpoints
+    (dict(dw0=A[6] + 256), "TTT_ERR_ALIAS"),    # two outputs
+    (dict(dv=A[11], dwT=A[11] + 64), "TTT_ERR_ALIAS"),
+    (dict(B=0), "TTT_OK"),
+])
+def test_linear_bwd_argument_checks(lib, kw, expect):
+    assert bwd(lib, **kw) == status(expect), lib.ttt_last_error()
+    if expect != "TTT_OK":
+        assert lib.ttt_last_error().startswith(b"ttt_linear_bwd:")
+
+
+def test_linear_fwd_ckpt_argument_checks(lib):
+    f = lambda **kw: lib.ttt_linear_fwd_ckpt(A[0], A[1], A[2], A[3], A[4], 0, 1, 1, 16, 64,
+                                             kw.get("b", 16), kw.get("dt", _lib.TTT_BF16), A[5],
+                                             A[6], kw.get("ck", A[7]), None)
+    assert f(b=4) == status("TTT_ERR_UNSUPPORTED")
+    assert f(dt=_lib.TTT_F32) == status("TTT_ERR_UNSUPPORTED")
+    assert f(ck=None) == status("TTT_ERR_NULL")
+    assert f(ck=A[0]) == status("TTT_ERR_ALIAS")
