@@ -59,7 +59,7 @@ struct BwdGeom {
   // partial sums of one compute wave: dQ, dK fragments (4 blocks), Ab, deta
   static constexpr int RQ = 4 * 64 * 16;
   static constexpr int RA = 64 * 16;
-  static constexpr int RW = 2 * RQ + RA + 64;
+  static constexpr int RW = 2 * RQ + RA + 256;
   static constexpr int RING = NST * SLOT;
   static constexpr int LDS = RING + 2 * 4 * RW;
   static constexpr int THREADS = 5 * 64;
@@ -218,7 +218,9 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
   };
 
   uint2 q4p = make_uint2(0, 0), k4p = make_uint2(0, 0);
-  int t0p = 0;
+  // first token of the previous tile; T (past the end) before the first
+  // tile, so that the first finalize's stores all fall outside the outputs
+  int t0p = T;
   auto body = [&](int i, const f32x4* wa0, f32x4* wnext) {
     wload(i + 2 < ntiles ? i + 2 : ntiles - 1, wnext);  // unconditional: exact wait counts
     wg_barrier();  // B_i: tile i in LDS; the partials of tile i - 1 are complete
@@ -229,7 +231,8 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
     const char* Vt = st + 2 * G::KB;
     const char* Zt = st + 3 * G::KB;
     const float* Et = (const float*)(st + 3 * G::KB + G::ZB);
-    if (i > 0) finalize((i - 1) & 1, q4p, k4p, t0p);
+    // branch-free, so that the scheduler can interleave it with the tile
+    finalize((i - 1) & 1, q4p, k4p, t0p);
 
     const bf16x8 kc[2] = {row_chunk(Kt, c, 0, g), row_chunk(Kt, c, 1, g)};
     const bf16x8 qc[2] = {row_chunk(Qt, c, 0, g), row_chunk(Qt, c, 1, g)};
@@ -283,9 +286,10 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
         // Q, K with columns scol(m, c) in lanes, tokens 4g .. 4g + 3 in registers
         const uint2 q4 = pack4(mfma_k32(qc[m >> 1], sel[m & 1], f32x4{0, 0, 0, 0}));
         const uint2 k4 = pack4(mfma_k32(kc[m >> 1], sel[m & 1], f32x4{0, 0, 0, 0}));
-        if (m == s) {  // kept for this wave's column block of the outputs
-          q4p = q4;
-          k4p = k4;
+        {  // kept for this wave's column block of the outputs (no branch)
+          const uint32_t keep = 0u - (uint32_t)(m == s);
+          q4p = make_uint2((q4.x & keep) | (q4p.x & ~keep), (q4.y & keep) | (q4p.y & ~keep));
+          k4p = make_uint2((k4.x & keep) | (k4p.x & ~keep), (k4.y & keep) | (k4p.y & ~keep));
         }
         const bf16x8 qk = cat8(q4, make_uint2(k4.x ^ 0x80008000u, k4.y ^ 0x80008000u));
         Wr[m] = mfma_k32(qk, zgh, Wr[m]);
@@ -344,7 +348,7 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
     f32x4 ab = mfma_k32(cat44(gws.hi, gws.lo), cat44(zts.hi, zts.hi), f32x4{0, 0, 0, 0});
     ab = mfma_k32(cat44(gws.hi, z4), cat44(zts.lo, zts.lo), ab);
     *(f32x4*)(rw + 2 * G::RQ + lane * 16) = ab;
-    if (g == 0) ((float*)(rw + 2 * G::RQ + G::RA))[c] = dp;
+    ((float*)(rw + 2 * G::RQ + G::RA))[lane] = dp;  // lanes c < 16 hold the sums
 
     t0p = t0;
     wait_lgkm0();  // the partials are in LDS before the next barrier
