@@ -14,17 +14,19 @@
 // own update, §3.1).  The kernel carries Gn = -G.  GELU is x Phi(x) with the
 // error function from Abramowitz & Stegun 7.1.26 (|error| <= 1.5e-7).
 //
-// Work split: one workgroup per (batch, head) unit, NW waves (one per SIMD).
-// Wave w owns the hidden units u in [U w, U w + U), U = 256 / NW, as NB =
-// U / 16 blocks: its rows of W1 and its columns of W2, all in fp32 registers
-// for the whole sequence (NW = 4 leaves each wave the full register file of
-// its SIMD, so nothing spills).  W2 enters
+// Work split: one workgroup per (batch, head) unit, NW waves.  Wave w owns
+// the hidden units u in [U w, U w + U), U = 256 / NW, as NB = U / 16 blocks:
+// its rows of W1 and its columns of W2, all in fp32 registers for the whole
+// sequence.  NW = 8 (two waves per SIMD, 32 hidden units each) for b = 16:
+// the second wave hides the first one's dependency and LDS waits; the b < 16
+// variant keeps more per-pass state and runs NW = 4 (one wave per SIMD with
+// the whole register file, so nothing spills).  W2 enters
 // contractions over u (forward) and over i (backward), so each wave keeps
 // its W2 block in both accumulator layouts (W2T: lane holds i = c and 4
 // consecutive u, in registers; W2N: lane holds u = c and 4 consecutive i,
 // in the wave's own LDS area, read and written block by block) and updates
 // both on MFMA.  The two cross-wave sums per tile (Z2 and Z over hidden units)
-// go through LDS: every wave writes its partial, wave w reduces the
+// go through LDS: every wave writes its partial, wave w < 4 reduces the
 // 16-column block w of d = 64.  Transposes of 16x16 fp32 blocks use an MFMA with the
 // identity as the other operand (exact for hi + lo bf16 halves).
 //
@@ -123,7 +125,7 @@ template <int NW, bool SUB>
 __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
   using G = MlpGeom<NW>;
   constexpr int U = G::U, NB = G::NB, NCH = G::NCH;
-  static_assert(NW == 4, "the cross-wave reductions assign one 16-column block of d per wave");
+  static_assert(NW == 4 || NW == 8, "waves 0..3 each own one 16-column block of d in the reductions");
   __shared__ __attribute__((aligned(16))) char smem[G::L_TOTAL];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
@@ -265,7 +267,8 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
 
     for (int p = 0; p < npass; ++p) {
       // ================= Z of the previous pass, output block mi = w
-      if (prev_tile >= 0) reduce_store_z<NW, SUB>(smem, lane, c, g, w, g2prev, rz, prev_tile, prev_pass, bsub);
+      if (prev_tile >= 0 && w < 4)
+        reduce_store_z<NW, SUB>(smem, lane, c, g, w, g2prev, rz, prev_tile, prev_pass, bsub);
 
       f32x4 e2;  // 2 eta of this pass's sub-batch
 #pragma unroll
@@ -316,7 +319,7 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
       wg_barrier();  // B1: partial Z2 written
 
       // ================= Gn2 = 2 eta (V - Z2) for output block mi = w
-      {
+      if (w < 4) {
         const int mi = w;
         f32x4 Z2 = {0, 0, 0, 0};
 #pragma unroll
@@ -411,7 +414,10 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
           *w2n_at(mi, nu) = mm_pre(cat44(g2s[mi].hi, g2s[mi].lo), xy, *w2n_at(mi, nu));  // += Gn2 X2^T
         }
       }
-      g2prev = g2y[w];
+      if (w == 0) g2prev = g2y[0];
+      if (w == 1) g2prev = g2y[1];
+      if (w == 2) g2prev = g2y[2];
+      if (w == 3) g2prev = g2y[3];
       prev_tile = j;
       prev_pass = p;
 
@@ -421,7 +427,8 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
     fetch(j + 2, pf);
   }
 
-  if (prev_tile >= 0) reduce_store_z<NW, SUB>(smem, lane, c, g, w, g2prev, rz, prev_tile, prev_pass, bsub);
+  if (prev_tile >= 0 && w < 4)
+    reduce_store_z<NW, SUB>(smem, lane, c, g, w, g2prev, rz, prev_tile, prev_pass, bsub);
 
   // final state
   float* w1o = a.w1_out + (size_t)unit * HID * 64;
@@ -444,7 +451,7 @@ hipError_t launch_mlp(const MlpArgs& a, bool f32in, hipStream_t s) {
   constexpr int NW = 4;
   if (f32in || a.b > 16) return hipErrorNotSupported;
   if (a.b == 16)
-    hipLaunchKernelGGL((mlp_scan_kernel<NW, false>), dim3(a.units), dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((mlp_scan_kernel<2 * NW, false>), dim3(a.units), dim3(2 * NW * 64), 0, s, a);
   else
     hipLaunchKernelGGL((mlp_scan_kernel<NW, true>), dim3(a.units), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
