@@ -16,17 +16,29 @@
 //     dK = -W^T Gt + Q Ab^T - Wb'^T G
 //     deta_t = -sum_i Gn[i, t] 2 E[i, t]
 //
-// One workgroup per (batch, head) unit, five waves.  Wave 4 streams the tiles
-// K, Q, V (bf16), dz (fp32) and eta in reverse order into an LDS ring by
-// buffer->LDS DMA.  Waves 0..3 each own 16 rows of the adjoint state Wb
-// (the rows evolve independently, like the forward's) in MFMA accumulators,
-// read their 16 rows of the tile's checkpoint W from HBM two tiles ahead,
-// and per tile compute their rows' share of everything: the state update,
-// dV, and partial sums over their rows of dQ, dK, Ab and deta.  The partial
-// sums go to a double-buffered LDS area; one tile later (after the next
-// barrier) wave w adds the four partials for 16 columns, applies the K Ab
-// and Q Ab^T terms and writes dQ, dK (wave 0 also deta).  So each tile costs
-// one barrier, and the adjoint state never leaves the chip.
+// One workgroup per (batch, head) unit, nine waves.  For each 16-row slice s
+// of the adjoint state Wb (its rows evolve independently, like the
+// forward's) a chain wave (s) and an output wave (s + 4), which share a
+// SIMD, so each hides the other's latencies:
+//   chain wave, tile i:   Wb (MFMA accumulators) -> Wb' K + Zb A^T with rows
+//       in lanes -> Gt -> dV and the update Wb += [Q | -K] [Zb | Gt]^T; the
+//       same with tokens in lanes -> Gn; and Wb' with columns in lanes.  Gn
+//       and that copy of Wb' go to the output wave through LDS.
+//   output wave, tile i-1: E = W K - V from the slice's rows of the
+//       checkpoint (read from HBM two tiles ahead), G, and the partial sums
+//       over the slice's rows of dQ, dK, Ab and deta, into LDS.
+//   chain wave, tile i-2: adds the four slices' partials for 16 columns,
+//       applies K Ab and Q Ab^T, writes dQ, dK (slice 0 also deta).
+// The ninth wave streams K, Q, V and eta in reverse order into an LDS ring
+// by buffer->LDS DMA (a wave that also read LDS would have to wait for its
+// own DMA before every read); dz is read by each wave straight into
+// registers two tiles ahead.  One barrier per tile.  The chain and output
+// waves run the same branch-free body for all ntiles + 2 iterations:
+// iterations outside the sequence see zero inputs (their loads fall outside
+// the buffer descriptors), which leave the state unchanged, and their stores
+// fall outside the outputs; so every iteration issues the same memory
+// operations and the compiler's wait counts stay exact.  The adjoint state
+// never leaves the chip.
 //
 // Products: 16x16x32 bf16 MFMA with fp32 accumulation.  K, Q, V are exact in
 // bf16; fp32 operands (states, dz, A, G, Gt, Ab) enter as hi + lo bf16 pairs
@@ -51,18 +63,21 @@ namespace {
 
 struct BwdGeom {
   static constexpr int KB = 16 * 64 * 2;          // K, Q or V tile: bf16 [token][col], swizzled
-  static constexpr int ZB = 16 * 64 * 4;          // dz tile: fp32 [token][col], swizzled
-  static constexpr int SLOT = 3 * KB + ZB + 64;   // + eta
-  static constexpr int NI = 2 + 2 + 2 + 4 + 1;    // DMA ops per tile
-  static constexpr int D = 5;                     // tiles in flight
-  static constexpr int NST = D + 2;
-  // partial sums of one compute wave: dQ, dK fragments (4 blocks), Ab, deta
+  static constexpr int SLOT = 3 * KB + 64;        // + eta
+  static constexpr int NI = 2 + 2 + 2 + 1;        // DMA ops per tile
+  static constexpr int D = 3;                     // tiles in flight
+  static constexpr int NST = D + 2;               // tile i is read until iteration i + 1
+  // partial sums of one output wave: dQ, dK fragments (4 blocks), Ab, deta
   static constexpr int RQ = 4 * 64 * 16;
   static constexpr int RA = 64 * 16;
   static constexpr int RW = 2 * RQ + RA + 256;
+  // chain -> output hand-over per slice: Gn (16 B) and Wb' hi/lo (64 B) per lane
+  static constexpr int HO = 64 * 80;
   static constexpr int RING = NST * SLOT;
-  static constexpr int LDS = RING + 2 * 4 * RW;
-  static constexpr int THREADS = 5 * 64;
+  static constexpr int RED = RING;                // 2 buffers x 4 slices x RW
+  static constexpr int HOB = RED + 2 * 4 * RW;    // 2 buffers x 4 slices x HO
+  static constexpr int LDS = HOB + 2 * 4 * HO;
+  static constexpr int THREADS = 9 * 64;        // + the DMA wave
 };
 
 // column of block m, position p (0..15) of the state accumulators
@@ -82,67 +97,28 @@ __device__ __forceinline__ f32x4 bf4(uint2 u) {
 __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdArgs a) {
   using G = BwdGeom;
   __shared__ __attribute__((aligned(16))) char smem[G::LDS];
-  char* const red = smem + G::RING;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
+  const int s = wave & 3;  // rows 16 s .. 16 s + 15
   const int unit = blockIdx.x;
   const int T = a.T, ntiles = (T + 15) >> 4;
+  const int niter = ntiles + 2;  // iteration k: chain tile k, outputs of tile k-1, finalize of k-2
   const size_t uoff = (size_t)unit * T * 64;
-
-  if (wave == 4) {  // --------------------------------------------- loader
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc((const short*)a.k + uoff, (uint32_t)T * 128);
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const short*)a.q + uoff, (uint32_t)T * 128);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const short*)a.v + uoff, (uint32_t)T * 128);
-    const __amdgpu_buffer_rsrc_t rz = make_rsrc(a.dz + uoff, (uint32_t)T * 256);
-    const __amdgpu_buffer_rsrc_t re = make_rsrc(a.eta + (size_t)unit * T, (uint32_t)T * 4);
-    // iteration i handles tile ntiles - 1 - i; 16-byte chunk p of token row r
-    // lands at chunk p ^ (r & 7) (bf16 tiles) or p ^ r (dz)
-    auto issue = [&](int i) {
-      const int j = ntiles - 1 - i;
-      char* st = smem + (i % G::NST) * G::SLOT;
+  if (ntiles == 0) {  // no tokens: dW0 = dW_T (or 0); w_ckpt may be NULL
+    if (wave < 4) {
+      const float* dwT = a.dw_T ? a.dw_T + (size_t)unit * 4096 + (16 * wave + c) * 64 : nullptr;
+      float* o = a.dw0 + (size_t)unit * 4096 + (16 * wave + c) * 64;
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const int r = 8 * n + (lane >> 3);
-        const uint32_t vo = (uint32_t)(j * 16 + r) * 128 + (((lane & 7) ^ (r & 7)) << 4);
-        dma16(rk, st + n * 1024, vo);
-        dma16(rq, st + G::KB + n * 1024, vo);
-        dma16(rv, st + 2 * G::KB + n * 1024, vo);
-      }
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const int r = 4 * n + (lane >> 4);
-        dma16(rz, st + 3 * G::KB + n * 1024,
-              (uint32_t)(j * 16 + r) * 256 + (((lane & 15) ^ r) << 4));
-      }
-      if (lane < 16) dma4(re, st + 3 * G::KB + G::ZB, (uint32_t)(j * 16 + lane) * 4);
-    };
-    const int pro = ntiles < G::D ? ntiles : G::D;
-    for (int i = 0; i < pro; ++i) issue(i);
-    for (int i = 0; i < ntiles; ++i) {
-      if (i + G::D < ntiles) {
-        issue(i + G::D);
-        wait_vmcnt<G::NI * G::D>();  // tiles <= i landed
-      } else {
-        wait_vmcnt<0>();
-      }
-      wg_barrier();  // B_i
+      for (int m = 0; m < 4; ++m)
+        *(f32x4*)(o + 16 * m + 4 * g) = dwT ? *(const f32x4*)(dwT + 16 * m + 4 * g) : f32x4{0, 0, 0, 0};
     }
-    wg_barrier();  // B_end
     return;
   }
-
-  // ---------------------------------------------------------- compute waves
-  const int s = wave;  // rows 16 s .. 16 s + 15
-  // outputs through buffer stores: tokens past T fall outside the descriptor
-  // and are dropped, so every tile issues the same stores (exact wait counts)
-  const __amdgpu_buffer_rsrc_t rdq = make_rsrc(a.dq + uoff, (uint32_t)T * 256);
-  const __amdgpu_buffer_rsrc_t rdk = make_rsrc(a.dk + uoff, (uint32_t)T * 256);
-  const __amdgpu_buffer_rsrc_t rdv = make_rsrc(a.dv + uoff, (uint32_t)T * 256);
-  const __amdgpu_buffer_rsrc_t rde = make_rsrc(a.deta + (size_t)unit * T, (uint32_t)T * 4);
-  auto st32 = [](float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
-  };
   const s16x4 z4 = {0, 0, 0, 0};
+  const __amdgpu_buffer_rsrc_t rdz = make_rsrc(a.dz + uoff, (uint32_t)T * 256);
+  // iteration-order tile k covers tokens 16 (ntiles - 1 - k) ..; tiles past
+  // either end read as zeros (their offsets fall outside the descriptors)
+  auto tok0 = [&](int k) { return (ntiles - 1 - k) * 16; };
   // one-hot selectors: B operand that picks column scol(m, c) out of a
   // natural-order chunk, for m even (sel[0]) and odd (sel[1])
   bf16x8 sel[2];
@@ -152,159 +128,229 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
     for (int e = 0; e < 8; ++e)
       sel[p][e] = (bf16)((g == (c >> 2) && e == 4 * p + (c & 3)) ? 1.f : 0.f);
 
-  // Wr[m] register r = Wb[row 16 s + c][scol(m, 4g + r)]
-  f32x4 Wr[4];
-  {
-    const float* dwT = a.dw_T ? a.dw_T + (size_t)unit * 4096 + (16 * s + c) * 64 : nullptr;
+  if (wave < 4) {  // ====================================================== chain
+    const __amdgpu_buffer_rsrc_t rdq = make_rsrc(a.dq + uoff, (uint32_t)T * 256);
+    const __amdgpu_buffer_rsrc_t rdk = make_rsrc(a.dk + uoff, (uint32_t)T * 256);
+    const __amdgpu_buffer_rsrc_t rdv = make_rsrc(a.dv + uoff, (uint32_t)T * 256);
+    const __amdgpu_buffer_rsrc_t rde = make_rsrc(a.deta + (size_t)unit * T, (uint32_t)T * 4);
+    auto st32 = [](float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+    };
+    // Wr[m] register r = Wb[row 16 s + c][scol(m, 4g + r)]
+    f32x4 Wr[4];
+    {
+      const float* dwT = a.dw_T ? a.dw_T + (size_t)unit * 4096 + (16 * s + c) * 64 : nullptr;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-      Wr[m] = dwT ? *(const f32x4*)(dwT + scol(m, 4 * g)) : f32x4{0, 0, 0, 0};
-  }
-  // this wave's rows of the checkpoint of iteration i, same layout as Wr
-  auto wload = [&](int i, f32x4* w) {
-    const int j = ntiles - 1 - i;
-    const float* p = a.w_ckpt + ((size_t)unit * ntiles + j) * 4096 + (16 * s + c) * 64;
+      for (int m = 0; m < 4; ++m)
+        Wr[m] = dwT ? *(const f32x4*)(dwT + scol(m, 4 * g)) : f32x4{0, 0, 0, 0};
+    }
+    // Zb with rows in lanes: register r = Zb[row 16s + c][t = 4g + r] of tile k
+    auto zload = [&](int k, f32x4& z) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) w[m] = *(const f32x4*)(p + scol(m, 4 * g));
-  };
-  // three register sets in rotation: tile i uses one while the loads of
-  // tiles i + 1 and i + 2 land in the other two (a register copy of a load
-  // in flight would wait for it, so the sets rotate by unrolling instead)
-  f32x4 wA[4], wB[4], wC[4];
-  if (ntiles > 0) wload(0, wA);
-  if (ntiles > 1) wload(1, wB);
-
-  // Sums the four waves' partials of one tile for column block s and writes
-  // dQ, dK (and deta from wave 0).  q4p, k4p: Q, K of that tile at columns
-  // scol(s, c), tokens 4g .. 4g + 3.
-  auto finalize = [&](int buf, uint2 q4p, uint2 k4p, int t0) {
-    const char* rb = red + buf * 4 * G::RW;
-    f32x4 dq = {0, 0, 0, 0}, dk = {0, 0, 0, 0}, ab1 = {0, 0, 0, 0}, ab2 = {0, 0, 0, 0};
-    float de = 0.f;
+      for (int r = 0; r < 4; ++r)
+        z[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                   rdz, (uint32_t)((tok0(k) + 4 * g + r) * 64 + 16 * s + c) * 4, 0, 0));
+    };
+    // Sums the four slices' partials of one tile for column block s and
+    // writes dQ, dK (slice 0 also deta).  q4p, k4p: Q, K of that tile at
+    // columns scol(s, c), tokens 4g .. 4g + 3.
+    auto finalize = [&](int buf, uint2 q4p, uint2 k4p, int t0) {
+      const char* rb = smem + G::RED + buf * 4 * G::RW;
+      f32x4 dq = {0, 0, 0, 0}, dk = {0, 0, 0, 0}, ab1 = {0, 0, 0, 0}, ab2 = {0, 0, 0, 0};
+      float de = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const char* rw = rb + w * G::RW;
-      const f32x4 x = *(const f32x4*)(rw + (s * 64 + lane) * 16);
-      const f32x4 y = *(const f32x4*)(rw + G::RQ + (s * 64 + lane) * 16);
-      const f32x4 z = *(const f32x4*)(rw + 2 * G::RQ + lane * 16);
+      for (int w = 0; w < 4; ++w) {
+        const char* rw = rb + w * G::RW;
+        const f32x4 x = *(const f32x4*)(rw + (s * 64 + lane) * 16);
+        const f32x4 y = *(const f32x4*)(rw + G::RQ + (s * 64 + lane) * 16);
+        const f32x4 z = *(const f32x4*)(rw + 2 * G::RQ + lane * 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          dq[r] += x[r];
+          dk[r] += y[r];
+          ab1[r] += z[r];
+          // transposed read: element (s' = c, t = 4g + r)
+          ab2[r] += *(const float*)(rw + 2 * G::RQ + ((4 * g + r + 16 * (c >> 2)) * 16 + (c & 3) * 4));
+        }
+        de += ((const float*)(rw + 2 * G::RQ + G::RA))[c];
+      }
+      // Ab = triu(-sum): ab1 register r = Ab[s' = 4g + r][t = c], ab2 = Ab[s' = c][t = 4g + r]
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        dq[r] += x[r];
-        dk[r] += y[r];
-        ab1[r] += z[r];
-        // transposed read: element (s' = c, t = 4g + r)
-        ab2[r] += *(const float*)(rw + 2 * G::RQ + ((4 * g + r + 16 * (c >> 2)) * 16 + (c & 3) * 4));
+        ab1[r] = (4 * g + r <= c) ? -ab1[r] : 0.f;
+        ab2[r] = (c <= 4 * g + r) ? -ab2[r] : 0.f;
       }
-      de += ((const float*)(rw + 2 * G::RQ + G::RA))[c];
-    }
-    // Ab = triu(-sum): ab1 register r = Ab[s' = 4g + r][t = c], ab2 = Ab[s' = c][t = 4g + r]
+      const Split4 a1 = split4(ab1), a2 = split4(ab2);
+      dq = mfma_k32(cat44(a1.hi, a1.lo), cat8(k4p, k4p), dq);  // + K Ab
+      dk = mfma_k32(cat44(a2.hi, a2.lo), cat8(q4p, q4p), dk);  // + Q Ab^T
+      const int col = scol(s, c);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      ab1[r] = (4 * g + r <= c) ? -ab1[r] : 0.f;
-      ab2[r] = (c <= 4 * g + r) ? -ab2[r] : 0.f;
-    }
-    const Split4 a1 = split4(ab1), a2 = split4(ab2);
-    dq = mfma_k32(cat44(a1.hi, a1.lo), cat8(k4p, k4p), dq);  // + K Ab
-    dk = mfma_k32(cat44(a2.hi, a2.lo), cat8(q4p, q4p), dk);  // + Q Ab^T
-    const int col = scol(s, c);
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t off = (uint32_t)((t0 + 4 * g + r) * 64 + col) * 4;
+        const float vq = dq[r], vk = dk[r];  // scalar copies: bit_cast of an element reads element 0
+        st32(vq, rdq, off);
+        st32(vk, rdk, off);
+      }
+      st32(de, rde, (s == 0 && g == 0) ? (uint32_t)(t0 + c) * 4 : 0x80000000u);
+    };
+
+    // Q, K of the two previous tiles at columns scol(s, c) (for finalize)
+    uint2 q4a = make_uint2(0, 0), k4a = make_uint2(0, 0), q4b = q4a, k4b = k4a;
+    f32x4 zA, zB, zC;  // dz rows of tiles k, k + 1, k + 2 in rotation
+    zload(0, zA);
+    zload(1, zB);
+    auto body = [&](int k, const f32x4& zc, f32x4& zn) {
+      zload(k + 2, zn);
+      wg_barrier();  // B_k: tile k in LDS; partials of tile k - 2 complete
+      finalize((k - 2) & 1, q4b, k4b, tok0(k - 2));
+      q4b = q4a;
+      k4b = k4a;
+      {
+        const char* st = smem + (k % G::NST) * G::SLOT;
+        const char* Kt = st;
+        const char* Qt = st + G::KB;
+        const float* Et = (const float*)(st + 3 * G::KB);
+        const int t0 = tok0(k);
+        const bf16x8 kc[2] = {row_chunk(Kt, c, 0, g), row_chunk(Kt, c, 1, g)};
+        const bf16x8 qc[2] = {row_chunk(Qt, c, 0, g), row_chunk(Qt, c, 1, g)};
+        // A^T: register r = A[s' = c][t = 4g + r] = k_c . q_{4g+r}, kept for s' <= t
+        f32x4 At = mfma_k32(qc[0], kc[0], f32x4{0, 0, 0, 0});
+        At = mfma_k32(qc[1], kc[1], At);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t off = (uint32_t)((t0 + 4 * g + r) * 64 + col) * 4;
-      const float vq = dq[r], vk = dk[r];  // scalar copies: bit_cast of an element reads element 0
-      st32(vq, rdq, off);
-      st32(vk, rdk, off);
+        for (int r = 0; r < 4; ++r)
+          if (c > 4 * g + r) At[r] = 0.f;
+        const Split4 as = split4(At);
+        const Split4 zrs = split4(zc);
+        const f32x4 er = *(const f32x4*)(Et + 4 * g);
+
+        const Split8 ws0 = split8(Wr[0], Wr[1]), ws1 = split8(Wr[2], Wr[3]);
+        f32x4 Pr = mfma_k32(kc[0], ws0.hi, f32x4{0, 0, 0, 0});  // (Wb' K)[row c][t = 4g + r]
+        Pr = mfma_k32(kc[0], ws0.lo, Pr);
+        Pr = mfma_k32(kc[1], ws1.hi, Pr);
+        Pr = mfma_k32(kc[1], ws1.lo, Pr);
+        f32x4 Mr = mfma_k32(cat44(as.hi, as.lo), cat44(zrs.hi, zrs.hi), f32x4{0, 0, 0, 0});
+        Mr = mfma_k32(cat44(as.hi, z4), cat44(zrs.lo, zrs.lo), Mr);  // (Zb A^T)[row c][t = 4g + r]
+        f32x4 Gtr;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Gtr[r] = 2.f * er[r] * (Pr[r] + Mr[r]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float gv = Gtr[r];
+          st32(gv, rdv, (uint32_t)((t0 + 4 * g + r) * 64 + 16 * s + c) * 4);
+        }
+        // tokens in lanes: Gn register r = [row 16s + 4g + r][t = c]
+        f32x4 Pt = mfma_k32(ws0.hi, kc[0], f32x4{0, 0, 0, 0});
+        Pt = mfma_k32(ws0.lo, kc[0], Pt);
+        Pt = mfma_k32(ws1.hi, kc[1], Pt);
+        Pt = mfma_k32(ws1.lo, kc[1], Pt);
+        f32x4 Gn = mfma_k32(cat44(zrs.hi, zrs.lo), cat44(as.hi, as.hi), Pt);
+        Gn = mfma_k32(cat44(zrs.hi, z4), cat44(as.lo, as.lo), Gn);
+        // hand-over: Gn, and Wb' with columns in lanes (register r =
+        // Wb'[row 16s + 4g + r][scol(m, c)]) as hi | lo bf16
+        char* ho = smem + G::HOB + ((k & 1) * 4 + s) * G::HO + lane * 16;
+        *(f32x4*)ho = Gn;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint2 bh = pack4(mfma_k32((m >> 1) ? ws1.hi : ws0.hi, sel[m & 1], f32x4{0, 0, 0, 0}));
+          const uint2 bl = pack4(mfma_k32((m >> 1) ? ws1.lo : ws0.lo, sel[m & 1], f32x4{0, 0, 0, 0}));
+          *(uint4*)(ho + (1 + m) * 1024) = make_uint4(bh.x, bh.y, bl.x, bl.y);
+        }
+        {
+          const Split4 gts = split4(Gtr);
+          const bf16x8 zgh = cat44(zrs.hi, gts.hi), zgl = cat44(zrs.lo, gts.lo);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {  // Wb = Wb' + Zb Q^T - Gt K^T
+            // Q, K with columns scol(m, c) in lanes, tokens 4g .. 4g + 3 in registers
+            const uint2 q4 = pack4(mfma_k32(qc[m >> 1], sel[m & 1], f32x4{0, 0, 0, 0}));
+            const uint2 k4 = pack4(mfma_k32(kc[m >> 1], sel[m & 1], f32x4{0, 0, 0, 0}));
+            {  // kept for this wave's column block of the outputs (no branch)
+              const uint32_t keep = 0u - (uint32_t)(m == s);
+              q4a = make_uint2((q4.x & keep) | (q4a.x & ~keep), (q4.y & keep) | (q4a.y & ~keep));
+              k4a = make_uint2((k4.x & keep) | (k4a.x & ~keep), (k4.y & keep) | (k4a.y & ~keep));
+            }
+            const bf16x8 qk = cat8(q4, make_uint2(k4.x ^ 0x80008000u, k4.y ^ 0x80008000u));
+            Wr[m] = mfma_k32(qk, zgh, Wr[m]);
+            Wr[m] = mfma_k32(qk, zgl, Wr[m]);
+          }
+        }
+      }
+      wait_lgkm0();  // the hand-over is in LDS before the next barrier
+    };
+    for (int k = 0; k < niter; k += 3) {
+      body(k, zA, zC);
+      if (k + 1 < niter) body(k + 1, zB, zA);
+      if (k + 2 < niter) body(k + 2, zC, zB);
     }
-    st32(de, rde, (s == 0 && g == 0) ? (uint32_t)(t0 + c) * 4 : 0x80000000u);
+    float* o = a.dw0 + (size_t)unit * 4096 + (16 * s + c) * 64;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) *(f32x4*)(o + scol(m, 4 * g)) = Wr[m];
+    return;
+  }
+
+  if (wave == 8) {  // ===================================================== DMA
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc((const short*)a.k + uoff, (uint32_t)T * 128);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const short*)a.q + uoff, (uint32_t)T * 128);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const short*)a.v + uoff, (uint32_t)T * 128);
+    const __amdgpu_buffer_rsrc_t re = make_rsrc(a.eta + (size_t)unit * T, (uint32_t)T * 4);
+    // iteration-order tile k (16-byte chunk p of token row r lands at chunk
+    // p ^ (r & 7)); tiles past either end read zeros into a free slot
+    auto issue = [&](int k) {
+      char* st = smem + (k % G::NST) * G::SLOT;
+      const int t0 = tok0(k);
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const int r = 8 * n + (lane >> 3);
+        const uint32_t vo = (uint32_t)(t0 + r) * 128 + (((lane & 7) ^ (r & 7)) << 4);
+        dma16(rk, st + n * 1024, vo);
+        dma16(rq, st + G::KB + n * 1024, vo);
+        dma16(rv, st + 2 * G::KB + n * 1024, vo);
+      }
+      if (lane < 16) dma4(re, st + 3 * G::KB, (uint32_t)(t0 + lane) * 4);
+    };
+    for (int k = 0; k < G::D; ++k) issue(k);
+    wait_vmcnt<G::NI * (G::D - 1)>();  // tile 0 landed
+    for (int k = 0; k < niter; ++k) {
+      wg_barrier();  // B_k
+      issue(k + G::D);  // into the slot of tile k - 2, read last before B_k
+      wait_vmcnt<G::NI * (G::D - 1)>();  // tile k + 1 landed
+    }
+    return;
+  }
+
+  // ========================================================== output waves
+  // the slice's rows of the checkpoint of tile k (Wr's layout) and dz with
+  // tokens in lanes (register r = Zb[row 16s + 4g + r][t = c])
+  struct Pf {
+    f32x4 w[4];
+    f32x4 z;
   };
-
-  uint2 q4p = make_uint2(0, 0), k4p = make_uint2(0, 0);
-  // first token of the previous tile; T (past the end) before the first
-  // tile, so that the first finalize's stores all fall outside the outputs
-  int t0p = T;
-  auto body = [&](int i, const f32x4* wa0, f32x4* wnext) {
-    wload(i + 2 < ntiles ? i + 2 : ntiles - 1, wnext);  // unconditional: exact wait counts
-    wg_barrier();  // B_i: tile i in LDS; the partials of tile i - 1 are complete
-    const int j = ntiles - 1 - i, t0 = j * 16;
-    const char* st = smem + (i % G::NST) * G::SLOT;
+  auto pload = [&](int k, Pf& p) {
+    const int kc = k < 0 ? 0 : (k < ntiles ? k : ntiles - 1);
+    const float* src = a.w_ckpt + ((size_t)unit * ntiles + (ntiles - 1 - kc)) * 4096 + (16 * s + c) * 64;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) p.w[m] = *(const f32x4*)(src + scol(m, 4 * g));
+    p.z = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+              rdz, (uint32_t)((tok0(k) + c) * 64 + 16 * s + 4 * g) * 4, 0, 0));
+  };
+  // partial sums over this slice's rows for tile p (iteration order)
+  auto outputs = [&](int p, const Pf& pf) {
+    const char* st = smem + (p % G::NST) * G::SLOT;
     const char* Kt = st;
-    const char* Qt = st + G::KB;
     const char* Vt = st + 2 * G::KB;
-    const char* Zt = st + 3 * G::KB;
-    const float* Et = (const float*)(st + 3 * G::KB + G::ZB);
-    // branch-free, so that the scheduler can interleave it with the tile
-    finalize((i - 1) & 1, q4p, k4p, t0p);
-
-    const bf16x8 kc[2] = {row_chunk(Kt, c, 0, g), row_chunk(Kt, c, 1, g)};
-    const bf16x8 qc[2] = {row_chunk(Qt, c, 0, g), row_chunk(Qt, c, 1, g)};
-    // A^T: register r = A[s' = c][t = 4g + r] = k_c . q_{4g+r}, kept for s' <= t
-    f32x4 At = mfma_k32(qc[0], kc[0], f32x4{0, 0, 0, 0});
-    At = mfma_k32(qc[1], kc[1], At);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (c > 4 * g + r) At[r] = 0.f;
-    const Split4 as = split4(At);
-    // Zb with rows in lanes (zr register r = Zb[row 16s + c][t = 4g + r]) and
-    // with tokens in lanes (zt register r = Zb[row 16s + 4g + r][t = c])
-    f32x4 zr;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      zr[r] = *(const float*)(Zt + (4 * g + r) * 256 + (((4 * s + (c >> 2)) ^ (4 * g + r)) << 4) +
-                              (c & 3) * 4);
-    const f32x4 zt = *(const f32x4*)(Zt + c * 256 + (((4 * s + g) ^ c) << 4));
-    const Split4 zrs = split4(zr), zts = split4(zt);
-    const f32x4 er = *(const f32x4*)(Et + 4 * g);
-    const float et = Et[c];
-
-    // ---- the chain: Gt with rows in lanes, then the state update
-    const Split8 ws0 = split8(Wr[0], Wr[1]), ws1 = split8(Wr[2], Wr[3]);
-    f32x4 Pr = mfma_k32(kc[0], ws0.hi, f32x4{0, 0, 0, 0});  // register r = (Wb' K)[row c][t = 4g + r]
-    Pr = mfma_k32(kc[0], ws0.lo, Pr);
-    Pr = mfma_k32(kc[1], ws1.hi, Pr);
-    Pr = mfma_k32(kc[1], ws1.lo, Pr);
-    f32x4 Mr = mfma_k32(cat44(as.hi, as.lo), cat44(zrs.hi, zrs.hi), f32x4{0, 0, 0, 0});
-    Mr = mfma_k32(cat44(as.hi, z4), cat44(zrs.lo, zrs.lo), Mr);  // (Zb A^T)[row c][t = 4g + r]
-    f32x4 Gtr;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) Gtr[r] = 2.f * er[r] * (Pr[r] + Mr[r]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float gv = Gtr[r];
-      st32(gv, rdv, (uint32_t)((t0 + 4 * g + r) * 64 + 16 * s + c) * 4);
-    }
-    // Wb' with columns in lanes: BB[m] register r = Wb'[row 16s + 4g + r][scol(m, c)]
+    const float* Et = (const float*)(st + 3 * G::KB);
+    const char* ho = smem + G::HOB + ((p & 1) * 4 + s) * G::HO + lane * 16;
+    const f32x4 Gn = *(const f32x4*)ho;
     uint2 BBh[4], BBl[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      BBh[m] = pack4(mfma_k32((m >> 1) ? ws1.hi : ws0.hi, sel[m & 1], f32x4{0, 0, 0, 0}));
-      BBl[m] = pack4(mfma_k32((m >> 1) ? ws1.lo : ws0.lo, sel[m & 1], f32x4{0, 0, 0, 0}));
+      const uint4 b = *(const uint4*)(ho + (1 + m) * 1024);
+      BBh[m] = make_uint2(b.x, b.y);
+      BBl[m] = make_uint2(b.z, b.w);
     }
-    {
-      const Split4 gts = split4(Gtr);
-      const bf16x8 zgh = cat44(zrs.hi, gts.hi), zgl = cat44(zrs.lo, gts.lo);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {  // Wb = Wb' + Zb Q^T - Gt K^T
-        // Q, K with columns scol(m, c) in lanes, tokens 4g .. 4g + 3 in registers
-        const uint2 q4 = pack4(mfma_k32(qc[m >> 1], sel[m & 1], f32x4{0, 0, 0, 0}));
-        const uint2 k4 = pack4(mfma_k32(kc[m >> 1], sel[m & 1], f32x4{0, 0, 0, 0}));
-        {  // kept for this wave's column block of the outputs (no branch)
-          const uint32_t keep = 0u - (uint32_t)(m == s);
-          q4p = make_uint2((q4.x & keep) | (q4p.x & ~keep), (q4.y & keep) | (q4p.y & ~keep));
-          k4p = make_uint2((k4.x & keep) | (k4p.x & ~keep), (k4.y & keep) | (k4p.y & ~keep));
-        }
-        const bf16x8 qk = cat8(q4, make_uint2(k4.x ^ 0x80008000u, k4.y ^ 0x80008000u));
-        Wr[m] = mfma_k32(qk, zgh, Wr[m]);
-        Wr[m] = mfma_k32(qk, zgl, Wr[m]);
-      }
-    }
-
-    // ---- tokens in lanes: Gn, Gt, E, G (register r = [row 16s + 4g + r][t = c])
-    f32x4 Pt = mfma_k32(ws0.hi, kc[0], f32x4{0, 0, 0, 0});
-    Pt = mfma_k32(ws0.lo, kc[0], Pt);
-    Pt = mfma_k32(ws1.hi, kc[1], Pt);
-    Pt = mfma_k32(ws1.lo, kc[1], Pt);
-    f32x4 Mt = mfma_k32(cat44(zrs.hi, zrs.lo), cat44(as.hi, as.hi), f32x4{0, 0, 0, 0});
-    Mt = mfma_k32(cat44(zrs.hi, z4), cat44(as.lo, as.lo), Mt);
-    const Split8 wa_0 = split8(wa0[0], wa0[1]), wa_1 = split8(wa0[2], wa0[3]);
+    const bf16x8 kc[2] = {row_chunk(Kt, c, 0, g), row_chunk(Kt, c, 1, g)};
+    const float et = Et[c];
+    const Split4 zts = split4(pf.z);
+    const Split8 wa_0 = split8(pf.w[0], pf.w[1]), wa_1 = split8(pf.w[2], pf.w[3]);
     f32x4 Ew = mfma_k32(wa_0.hi, kc[0], f32x4{0, 0, 0, 0});
     Ew = mfma_k32(wa_0.lo, kc[0], Ew);
     Ew = mfma_k32(wa_1.hi, kc[1], Ew);
@@ -314,11 +360,10 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
     float dp = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float gn = Pt[r] + Mt[r];
       const float e = Ew[r] - vv[r];
-      Gtt[r] = 2.f * et * gn;
+      Gtt[r] = 2.f * et * Gn[r];
       Gw[r] = 2.f * et * e;
-      dp -= gn * 2.f * e;
+      dp -= Gn[r] * 2.f * e;
     }
     dp += __shfl_xor(dp, 16);
     dp += __shfl_xor(dp, 32);
@@ -329,8 +374,7 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
       WBh[m] = pack4(mfma_k32((m >> 1) ? wa_1.hi : wa_0.hi, sel[m & 1], f32x4{0, 0, 0, 0}));
       WBl[m] = pack4(mfma_k32((m >> 1) ? wa_1.lo : wa_0.lo, sel[m & 1], f32x4{0, 0, 0, 0}));
     }
-    // ---- partial sums over this wave's rows
-    char* rw = red + (i & 1) * 4 * G::RW + s * G::RW;
+    char* rw = smem + G::RED + ((p & 1) * 4 + s) * G::RW;
     const Split4 gts = split4(Gtt), gws = split4(Gw);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -349,20 +393,23 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
     ab = mfma_k32(cat44(gws.hi, z4), cat44(zts.lo, zts.lo), ab);
     *(f32x4*)(rw + 2 * G::RQ + lane * 16) = ab;
     ((float*)(rw + 2 * G::RQ + G::RA))[lane] = dp;  // lanes c < 16 hold the sums
+  };
 
-    t0p = t0;
+  // Prefetch of tile p happens at iteration p - 1 (p = 0: before the loop),
+  // its use at iteration p + 1; three register sets rotate by unrolling.
+  Pf pA, pB, pC;
+  pload(0, pA);
+  auto body = [&](int k, const Pf& pc, Pf& pn) {
+    pload(k + 1, pn);
+    wg_barrier();  // B_k: tile k in LDS; hand-over of tile k - 1 complete
+    outputs(k - 1, pc);
     wait_lgkm0();  // the partials are in LDS before the next barrier
   };
-  for (int i = 0; i < ntiles; i += 3) {
-    body(i, wA, wC);
-    if (i + 1 < ntiles) body(i + 1, wB, wA);
-    if (i + 2 < ntiles) body(i + 2, wC, wB);
+  for (int k = 0; k < niter; k += 3) {
+    body(k, pC, pB);
+    if (k + 1 < niter) body(k + 1, pA, pC);
+    if (k + 2 < niter) body(k + 2, pB, pA);
   }
-  wg_barrier();  // B_end
-  if (ntiles > 0) finalize((ntiles - 1) & 1, q4p, k4p, t0p);
-  float* o = a.dw0 + (size_t)unit * 4096 + (16 * s + c) * 64;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) *(f32x4*)(o + scol(m, 4 * g)) = Wr[m];
 }
 
 }  // namespace
