@@ -151,6 +151,9 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
     negI[e] = (bf16)((g < 2 && 8 * g + e == c) ? -1.f : 0.f);
   }
 
+  // hi/lo splits of fp32 blocks form the residual on the matrix unit
+  const NegSel ns = make_negsel(c, g);
+
   // ---------------------------------------------------------------- state
   const size_t wsel = a.w0_per_batch ? unit : head;
   const float* w1g = a.w1_0 + wsel * HID * 64;
@@ -278,7 +281,7 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
       f32x4 Z1[NB], ZQ[NB], D[NB], X2t[NB];
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
-        const Split8 s0 = split8(W1[n][0], W1[n][1]), s1 = split8(W1[n][2], W1[n][3]);
+        const Split8 s0 = split8_mfma(W1[n][0], W1[n][1], ns), s1 = split8_mfma(W1[n][2], W1[n][3], ns);
         f32x4 z = {0, 0, 0, 0}, zq = {0, 0, 0, 0};
         z = mfma_k32(kop[0], s0.hi, z);
         z = mfma_k32(kop[0], s0.lo, z);
@@ -307,13 +310,13 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
       for (int ch = 0; ch < NCH; ++ch) {
         const f32x4 t0 = mfma_k32(cat44(x2ts[2 * ch].hi, x2ts[2 * ch].lo), itr, f32x4{0, 0, 0, 0});
         const f32x4 t1 = mfma_k32(cat44(x2ts[2 * ch + 1].hi, x2ts[2 * ch + 1].lo), itr, f32x4{0, 0, 0, 0});
-        x2op[ch] = split8(t0, t1);
+        x2op[ch] = split8_mfma(t0, t1, ns);
       }
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
         f32x4 z2 = {0, 0, 0, 0};
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) z2 = mm3(x2op[ch], split8(W2T[2 * ch][mi], W2T[2 * ch + 1][mi]), z2);
+        for (int ch = 0; ch < NCH; ++ch) z2 = mm3(x2op[ch], split8_mfma(W2T[2 * ch][mi], W2T[2 * ch + 1][mi], ns), z2);
         *(f32x4*)(smem + G::L_Z2P + (w * 4 + mi) * 1024 + lane * 16) = z2;  // partial Z2^T[t][i]
       }
       wg_barrier();  // B1: partial Z2 written
@@ -354,7 +357,7 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
       for (int nu = 0; nu < NB; ++nu) {
         f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) acc = mm3(ga[kb], split8(*w2n_at(2 * kb, nu), *w2n_at(2 * kb + 1, nu)), acc);
+        for (int kb = 0; kb < 2; ++kb) acc = mm3(ga[kb], split8_mfma(*w2n_at(2 * kb, nu), *w2n_at(2 * kb + 1, nu), ns), acc);
         f32x4 g1;
 #pragma unroll
         for (int r = 0; r < 4; ++r) g1[r] = acc[r] * D[nu][r];
@@ -376,13 +379,13 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
       for (int ch = 0; ch < NCH; ++ch) {
         const f32x4 t0 = mfma_k32(cat44(x2qs[2 * ch].hi, x2qs[2 * ch].lo), itr, f32x4{0, 0, 0, 0});
         const f32x4 t1 = mfma_k32(cat44(x2qs[2 * ch + 1].hi, x2qs[2 * ch + 1].lo), itr, f32x4{0, 0, 0, 0});
-        x2qop[ch] = split8(t0, t1);
+        x2qop[ch] = split8_mfma(t0, t1, ns);
       }
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
         f32x4 zp = {0, 0, 0, 0};
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) zp = mm3(x2qop[ch], split8(W2T[2 * ch][mi], W2T[2 * ch + 1][mi]), zp);
+        for (int ch = 0; ch < NCH; ++ch) zp = mm3(x2qop[ch], split8_mfma(W2T[2 * ch][mi], W2T[2 * ch + 1][mi], ns), zp);
         *(f32x4*)(smem + G::L_ZP + (w * 4 + mi) * 1024 + lane * 16) = zp;
       }
       {
