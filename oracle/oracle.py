@@ -63,6 +63,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.ttt_oracle_linear_bwd.restype = I
     lib.ttt_oracle_lr_gate.argtypes = [dp, dp, D, L, L, L, L, dp]
     lib.ttt_oracle_lr_gate.restype = I
+    lib.ttt_oracle_lr_gate_bwd.argtypes = [dp, dp, D, dp, L, L, L, L, dp, dp]
+    lib.ttt_oracle_lr_gate_bwd.restype = I
     return lib
 
 
@@ -285,3 +287,20 @@ def linear_gated(q, k, v, x, theta_lr, eta_base: float, w0, b: int, nthreads: in
     eta = lr_gate(x, theta_lr, eta_base, lib=lib)
     z, w = linear(q, k, v, eta, w0, b, nthreads=nthreads, lib=lib)
     return z, w, eta
+
+
+def lr_gate_bwd(x, theta_lr, eta_base: float, deta, lib=None):
+    """Backward of lr_gate: deta [B, H, T] (dL/deta) -> (dtheta_lr [H, dx],
+    dx [B, T, dx])."""
+    x, th, de = _f64(x), _f64(theta_lr), _f64(deta)
+    B, T, dx = x.shape
+    H = th.shape[0]
+    assert th.shape == (H, dx) and de.shape == (B, H, T)
+    dth = np.zeros((H, dx))
+    dxo = np.zeros((B, T, dx))
+    lib = lib or load()
+    rc = lib.ttt_oracle_lr_gate_bwd(_ptr(x), _ptr(th), float(eta_base), _ptr(de), B, T, H, dx,
+                                    _ptr(dth), _ptr(dxo))
+    if rc != 0:
+        raise RuntimeError(f"ttt_oracle_lr_gate_bwd failed with status {rc}")
+    return dth, dxo

@@ -50,6 +50,11 @@
  * here every head h has its own theta_lr[h] (H = 1 is the page's case), and
  * the gated scan is the scan above fed with eta[b][h][t] from the gate.
  *
+ * Gate backward: given dL/deta, the chain rule through the sigmoid,
+ * d eta / d a = eta_base sigmoid(a) (1 - sigmoid(a)), a = theta_lr[h] . x,
+ * gives dL/dtheta_lr[h] = sum_{b,t} da x[b][t] and dL/dx[b][t] = sum_h da
+ * theta_lr[h].
+ *
  * The loss is the squared L2 norm summed over output components, so its
  * gradient carries the factor 2 (§3.6 linear derivation: G_t = 2(W0 x - x)x^T).
  * GELU is the exact erf form x * Phi(x).  Mini-batches start at token 0, b,
@@ -631,5 +636,34 @@ int ttt_oracle_lr_gate(const double *x, const double *theta, double eta_base, lo
         eta[((size_t)bi * (size_t)H + (size_t)h) * (size_t)T + (size_t)t] =
             eta_base / (1.0 + exp(-a));
       }
+  return 0;
+}
+
+/* Backward of the gate above: deta [B][H][T] -> dtheta [H][dx], dx [B][T][dx]
+ * (both overwritten), recomputing the logits in fp64. */
+int ttt_oracle_lr_gate_bwd(const double *x, const double *theta, double eta_base,
+                           const double *deta, long B, long T, long H, long dx, double *dtheta,
+                           double *dxo) {
+  if (B < 0 || T < 0 || H < 0 || dx <= 0) return 2;
+  memset(dtheta, 0, sizeof(double) * (size_t)(H * dx));
+  memset(dxo, 0, sizeof(double) * (size_t)(B * T * dx));
+  for (long bi = 0; bi < B; ++bi)
+    for (long t = 0; t < T; ++t) {
+      const size_t tok = (size_t)bi * (size_t)T + (size_t)t;
+      const double *xt = x + tok * (size_t)dx;
+      double *gx = dxo + tok * (size_t)dx;
+      for (long h = 0; h < H; ++h) {
+        const double *th = theta + (size_t)(h * dx);
+        double a = 0.0;
+        for (long i = 0; i < dx; ++i) a += th[i] * xt[i];
+        const double sg = 1.0 / (1.0 + exp(-a));
+        const size_t gi = ((size_t)bi * (size_t)H + (size_t)h) * (size_t)T + (size_t)t;
+        const double da = deta[gi] * eta_base * sg * (1.0 - sg);
+        for (long i = 0; i < dx; ++i) {
+          dtheta[(size_t)h * (size_t)dx + (size_t)i] += da * xt[i];
+          gx[i] += da * th[i];
+        }
+      }
+    }
   return 0;
 }

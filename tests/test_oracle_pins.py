@@ -27,7 +27,9 @@ Time): RNNs with Expressive Hidden States"):
 * the inner learning-rate gate (§4.6) eta = eta_base sigmoid(theta_lr . x):
   logits placed exactly through one-hot gate vectors give the closed values
   sigmoid(0) = 1/2, sigmoid(+-ln 3) = 3/4, 1/4, sigmoid(+-ln 7) = 7/8, 1/8 and
-  saturation at eta_base, each at its own (batch, head, token);
+  saturation at eta_base, each at its own (batch, head, token); its
+  backward (dtheta_lr, dx from deta) against central finite differences of
+  sum deta * eta, and the closed form at theta_lr = 0 (sigmoid' = 1/4);
 * invariants: homogeneity, superposition, row permutation, state passing,
   thread-count determinism.
 
@@ -519,6 +521,46 @@ def pin_gate_closed_forms(lib):
     assert np.all(oracle.lr_gate(x, np.zeros((H, dx)), 2.0, lib=lib) == 1.0)
 
 
+def pin_gate_bwd_finite_differences(lib):
+    # L = sum deta * eta(theta, x): the backward must be its gradient
+    rng = np.random.default_rng(71)
+    B, T, H, dx = 2, 3, 3, 5
+    x = rng.standard_normal((B, T, dx))
+    theta = rng.standard_normal((H, dx)) * 0.6
+    deta = rng.standard_normal((B, H, T))
+    eta_base = 0.7
+    dth, dxo = oracle.lr_gate_bwd(x, theta, eta_base, deta, lib=lib)
+    L = lambda xx, tt: float((deta * oracle.lr_gate(xx, tt, eta_base, lib=lib)).sum())
+    h = 1e-6
+    fd_t = np.zeros_like(theta)
+    for i in np.ndindex(theta.shape):
+        e = np.zeros_like(theta)
+        e[i] = h
+        fd_t[i] = (L(x, theta + e) - L(x, theta - e)) / (2 * h)
+    fd_x = np.zeros_like(x)
+    for i in np.ndindex(x.shape):
+        e = np.zeros_like(x)
+        e[i] = h
+        fd_x[i] = (L(x + e, theta) - L(x - e, theta)) / (2 * h)
+    assert rel(dth, fd_t) < 1e-7 and rel(dxo, fd_x) < 1e-7
+
+
+def pin_gate_bwd_zero_vector(lib):
+    # theta_lr = 0: every logit is 0, sigmoid' = 1/4, so
+    # dtheta[h] = eta_base / 4 * sum_{b,t} deta[b,h,t] x[b,t] and dx = 0
+    rng = np.random.default_rng(72)
+    B, T, H, dx = 2, 4, 3, 6
+    x = rng.standard_normal((B, T, dx))
+    deta = rng.standard_normal((B, H, T))
+    dth, dxo = oracle.lr_gate_bwd(x, np.zeros((H, dx)), 2.0, deta, lib=lib)
+    want = np.zeros((H, dx))
+    for h in range(H):
+        for b in range(B):
+            for t in range(T):
+                want[h] += 0.5 * deta[b, h, t] * x[b, t]
+    assert np.abs(dth - want).max() < 1e-14 and np.abs(dxo).max() == 0.0
+
+
 PINS = [
     pin_linear_primal_equals_dual,
     pin_mlp_primal_equals_dual,
@@ -546,6 +588,8 @@ PINS = [
     pin_linear_bwd_equals_dual_form_adjoint,
     pin_linear_bwd_eta_zero,
     pin_gate_closed_forms,
+    pin_gate_bwd_finite_differences,
+    pin_gate_bwd_zero_vector,
 ]
 
 
@@ -669,6 +713,10 @@ MUTATIONS = {
     "gate_token_major_output": ("eta[((size_t)bi * (size_t)H + (size_t)h) * (size_t)T + (size_t)t]",
                                 "eta[((size_t)bi * (size_t)T + (size_t)t) * (size_t)H + (size_t)h]"),
     "gate_first_token_only": ("+ (size_t)t) * (size_t)dx;", ") * (size_t)dx;"),
+    "gate_bwd_no_one_minus_sigmoid": ("eta_base * sg * (1.0 - sg);", "eta_base * sg;"),
+    "gate_bwd_dx_from_head_0": ("gx[i] += da * th[i];", "gx[i] += da * theta[i];"),
+    "gate_bwd_dtheta_from_first_token": ("+= da * xt[i];", "+= da * x[i];"),
+    "gate_bwd_no_base": ("deta[gi] * eta_base * sg", "deta[gi] * sg"),
     "bwd_output_adjoint_dropped": ("A[i * d + j] += zt[i] * qt[j];\n    /* W_t",
                                    "A[i * d + j] += 0.0 * zt[i] * qt[j];\n    /* W_t"),
 }
