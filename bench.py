@@ -374,10 +374,10 @@ def gate_alg_bytes(wl) -> int:
 
 
 def gate_case(wl, steps, warmup):
-    """ttt_lr_gate alone (both launch shapes) and ttt_linear_gated_fwd (gate +
-    scan) on one gated workload."""
+    """ttt_lr_gate alone (both launch shapes), its backward ttt_lr_gate_bwd,
+    and ttt_linear_gated_fwd (gate + scan) on one gated workload."""
     import torch
-    from test_rnn_layers_head_amd import inputs, ttt_linear_gated_fwd, ttt_lr_gate
+    from test_rnn_layers_head_amd import inputs, ttt_linear_gated_fwd, ttt_lr_gate, ttt_lr_gate_bwd
     x = inputs.make_inputs(wl)
     d = device_inputs(x)
     gx = torch.from_numpy(x.gate_x_raw.view(np.int16)).cuda().view(torch.bfloat16)
@@ -392,6 +392,18 @@ def gate_case(wl, steps, warmup):
                                                          tokens_per_workgroup=tpw), steps, warmup)
         res[f"gate_us_tpw{tpw}"] = k
         res[f"gate_hbm_frac_tpw{tpw}"] = gb / (k * 1e-6) / 1e9 / HBM_PEAK_GBS
+    # backward of the gate: read x, theta, eta, deta; write dtheta, dx
+    deta = torch.randn((wl.B, wl.H, wl.T), device="cuda")
+    dth = torch.empty((wl.H, wl.gate_dx), device="cuda")
+    dxo = torch.empty((wl.B, wl.T, wl.gate_dx), device="cuda")
+    ttt_lr_gate(gx, th, x.eta_base, eta=eta)
+    _, k, _ = time_launches(lambda: ttt_lr_gate_bwd(gx, th, x.eta_base, eta, deta, dtheta_lr=dth,
+                                                    dx=dxo), steps, warmup)
+    bb = wl.B * wl.T * wl.gate_dx * 6 + wl.H * wl.gate_dx * 8 + wl.token_heads * 8
+    res["gate_bwd_us"] = k
+    res["gate_bwd_alg_bytes"] = bb
+    res["gate_bwd_hbm_frac"] = bb / (k * 1e-6) / 1e9 / HBM_PEAK_GBS
+    del deta, dth, dxo
     launch = lambda: ttt_linear_gated_fwd(d["q"], d["k"], d["v"], gx, th, x.eta_base, d["w0"], 16,
                                           eta=eta, z=z, w_out=w)
     wall, k, _ = time_launches(launch, steps, warmup)

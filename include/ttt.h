@@ -256,6 +256,27 @@ ttt_status_t ttt_lr_gate(const void* x, ttt_dtype_t x_dtype,
                          void* stream);
 
 /*
+ * Backward of the gate: given deta = dL/deta [B][H][T] fp32 and the gate's
+ * own output eta [B][H][T] (from ttt_lr_gate with the same x, theta_lr and
+ * eta_base), writes
+ *   dtheta_lr [H][dx] fp32:   sum_{b,t} da[b][h][t] x[b][t]
+ *   dx        [B][T][dx] fp32: sum_h da[b][h][t] theta_lr[h]
+ * with da = deta * eta * (1 - eta / eta_base), the derivative of
+ * eta_base * sigmoid(a) at the forward's logit a (eta_base = 0: zero).
+ * dtheta_lr is deterministic (partial sums over token chunks are added in a
+ * fixed order; dx's memory holds them before dx itself is written, so its
+ * prior contents do not matter).  Products: theta_lr and da enter as hi + lo
+ * bf16 pairs against exact bf16 x on the matrix unit (dtheta_lr); dx is fp32
+ * arithmetic.  Support and errors as ttt_lr_gate; outputs must not overlap
+ * each other or an input.
+ */
+ttt_status_t ttt_lr_gate_bwd(const void* x, ttt_dtype_t x_dtype,
+                             const float* theta_lr, float eta_base,
+                             const float* eta, const float* deta, int32_t B,
+                             int32_t T, int32_t H, int32_t dx,
+                             float* dtheta_lr, float* dx_out, void* stream);
+
+/*
  * The gate followed by the forward scan, on one stream: eta is computed from
  * x into the caller's eta buffer ([B][H][T] fp32, kept as an output for the
  * backward), then the scan runs with it.  All other arguments, layouts,

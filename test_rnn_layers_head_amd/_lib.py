@@ -34,6 +34,8 @@ SIGNATURES = {
     "ttt_linear_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                               _vp, _vp, _vp, _vp, _vp, _vp]),
     "ttt_lr_gate": (_i32, [_vp, _i32, _vp, ctypes.c_float, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "ttt_lr_gate_bwd": (_i32, [_vp, _i32, _vp, ctypes.c_float, _vp, _vp, _i32, _i32, _i32, _i32,
+                               _vp, _vp, _vp]),
     "ttt_lr_gate_tuned": (_i32, [_vp, _i32, _vp, ctypes.c_float, _i32, _i32, _i32, _i32, _vp, _vp,
                                  _i32]),
     "ttt_linear_gated_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, _i32, _vp, _i32,

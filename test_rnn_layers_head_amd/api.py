@@ -315,6 +315,31 @@ def ttt_lr_gate(x, theta_lr, eta_base: float, eta=None, stream=None, tokens_per_
     return eta
 
 
+def ttt_lr_gate_bwd(x, theta_lr, eta_base: float, eta, deta, dtheta_lr=None, dx=None, stream=None):
+    """Backward of the learning-rate gate (include/ttt.h): deta = dL/deta
+    [B, H, T] and the gate's output eta -> (dtheta_lr [H, dx], dx [B, T, dx]),
+    fp32."""
+    B, T, H, d_x, _ = _gate_common(x, theta_lr, None, eta)
+    for name, t in (("deta", deta),):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, H, T):
+            raise ValueError(f"{name} must be float32 [B, H, T]")
+    if dtheta_lr is None:
+        dtheta_lr = torch.empty((H, d_x), dtype=torch.float32, device=x.device)
+    if dx is None:
+        dx = torch.empty((B, T, d_x), dtype=torch.float32, device=x.device)
+    if dtheta_lr.dtype != torch.float32 or tuple(dtheta_lr.shape) != (H, d_x):
+        raise ValueError("dtheta_lr must be float32 [H, dx]")
+    if dx.dtype != torch.float32 or tuple(dx.shape) != (B, T, d_x):
+        raise ValueError("dx must be float32 [B, T, dx]")
+    dev = _check_tensors(dict(x=x, theta_lr=theta_lr, eta=eta, deta=deta, dtheta_lr=dtheta_lr,
+                              dx=dx))
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib().ttt_lr_gate_bwd(_ptr(x), _lib.TTT_BF16, _ptr(theta_lr),
+                                              float(eta_base), _ptr(eta), _ptr(deta), B, T, H,
+                                              d_x, _ptr(dtheta_lr), _ptr(dx), _stream(dev, stream)))
+    return dtheta_lr, dx
+
+
 def ttt_linear_gated_fwd(q, k, v, x, theta_lr, eta_base: float, w0, b: int, eta=None, z=None,
                          w_out=None, stream=None):
     """The gate, then the TTT-Linear scan with its eta (include/ttt.h).

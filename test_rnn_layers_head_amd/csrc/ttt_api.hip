@@ -530,6 +530,50 @@ ttt_status_t ttt_lr_gate_tuned(const void* x, ttt_dtype_t x_dtype, const float* 
   return gate_launch(fn, x, theta_lr, eta_base, B, T, H, dx, eta, stream, tokens_per_workgroup);
 }
 
+ttt_status_t ttt_lr_gate_bwd(const void* x, ttt_dtype_t x_dtype, const float* theta_lr,
+                             float eta_base, const float* eta, const float* deta, int32_t B,
+                             int32_t T, int32_t H, int32_t dx, float* dtheta_lr, float* dx_out,
+                             void* stream) {
+  static const char* fn = "ttt_lr_gate_bwd";
+  if (x_dtype != TTT_F32 && x_dtype != TTT_BF16)
+    return fail(TTT_ERR_DTYPE, "%s: unknown x dtype %d", fn, (int)x_dtype);
+  if (B < 0 || T < 0 || H < 0 || dx < 0)
+    return fail(TTT_ERR_SHAPE, "%s: negative size (B=%d T=%d H=%d dx=%d)", fn, B, T, H, dx);
+  if (dx == 0 || dx % 32 != 0)
+    return fail(TTT_ERR_UNSUPPORTED, "%s: dx=%d unsupported (need a positive multiple of 32)", fn, dx);
+  if (x_dtype != TTT_BF16) return fail(TTT_ERR_UNSUPPORTED, "%s: only bf16 x is supported", fn);
+  if (!(eta_base == eta_base) || eta_base > 3.4e38f || eta_base < -3.4e38f)
+    return fail(TTT_ERR_VALUE, "%s: eta_base=%g must be finite", fn, (double)eta_base);
+  const int64_t ntok = (int64_t)B * T;
+  if (ntok * H >= ((int64_t)1 << 31) || ntok * dx >= ((int64_t)1 << 31))
+    return fail(TTT_ERR_SHAPE, "%s: B*T*H or B*T*dx exceeds 2^31 - 1", fn);
+  const Range in[] = {rng("x", x, ntok * dx * 2), rng("theta_lr", theta_lr, (int64_t)H * dx * 4),
+                      rng("eta", eta, ntok * H * 4), rng("deta", deta, ntok * H * 4)};
+  const Range out[] = {rng("dtheta_lr", dtheta_lr, (int64_t)H * dx * 4),
+                       rng("dx", dx_out, ntok * dx * 4)};
+  const bool need[] = {ntok > 0, H > 0, ntok * H > 0, ntok * H > 0};
+  for (int i = 0; i < 4; ++i) {
+    if (!need[i]) continue;
+    if (!in[i].lo) return fail(TTT_ERR_NULL, "%s: %s is NULL", fn, in[i].name);
+    if (in[i].lo & 15) return fail(TTT_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, in[i].name);
+  }
+  const bool needo[] = {H > 0, ntok > 0};
+  for (int o = 0; o < 2; ++o) {
+    if (!needo[o]) continue;
+    if (!out[o].lo) return fail(TTT_ERR_NULL, "%s: %s is NULL", fn, out[o].name);
+    if (out[o].lo & 15) return fail(TTT_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, out[o].name);
+    for (int i = 0; i < 4; ++i)
+      if (overlap(out[o], in[i]))
+        return fail(TTT_ERR_ALIAS, "%s: %s overlaps input %s", fn, out[o].name, in[i].name);
+  }
+  if (overlap(out[0], out[1])) return fail(TTT_ERR_ALIAS, "%s: dtheta_lr and dx overlap", fn);
+  if ((int64_t)H * dx == 0 && ntok * dx == 0) return TTT_OK;
+  ttt::GateBwdArgs a{x, theta_lr, eta, deta, dtheta_lr, dx_out, eta_base, B, T, H, dx};
+  hipError_t e = ttt::launch_lr_gate_bwd(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return TTT_OK;
+}
+
 ttt_status_t ttt_linear_gated_fwd(const void* q, const void* k, const void* v, const void* x,
                                   const float* theta_lr, float eta_base, int32_t dx,
                                   const float* w0, int32_t w0_per_batch, int32_t B, int32_t H,

@@ -172,3 +172,214 @@ hipError_t launch_lr_gate(const GateArgs& a, int tokens_per_workgroup, hipStream
 }
 
 }  // namespace ttt
+
+// ============================================================== backward
+// dL/da = dL/deta * eta (1 - eta / eta_base) (= eta_base sigmoid' (a)), from
+// the forward's eta, so the logits need not be recomputed;
+//   dtheta_lr[h] = sum_{b,t} da[b][h][t] x[b][t],   dx[b][t] = sum_h da[b][h][t] theta_lr[h].
+namespace ttt {
+namespace {
+
+// da at (batch bi, head h, position t); B * H * T < 2^31 (checked by the ABI)
+__device__ __forceinline__ float gate_da_at(const GateBwdArgs& a, int bi, int h, int t,
+                                            float inv_base) {
+  const int i = (bi * a.H + h) * a.T + t;
+  const float e = a.eta[i];
+  return a.deta[i] * e * (1.f - e * inv_base);
+}
+// da of flat token f = bi * T + t (zero past the tokens or the heads)
+__device__ __forceinline__ float gate_da(const GateBwdArgs& a, int f, int h, float inv_base) {
+  if (f >= a.B * a.T || h >= a.H) return 0.f;
+  const int bi = f / a.T;
+  return gate_da_at(a, bi, h, f - bi * a.T, inv_base);
+}
+
+// Partial sums of dtheta over one chunk of tokens, for 16 * NM columns:
+// part[s][h][col].  Products on the matrix unit: x exact in bf16, brought to
+// tokens-in-registers by a one-hot selection MFMA (exact), da as hi + lo.
+// Four waves take interleaved 16-token blocks and meet in LDS.
+template <int NM>
+__global__ void __launch_bounds__(256) lr_gate_bwd_dtheta_kernel(GateBwdArgs a, float* part,
+                                                                 int chunk) {
+  __shared__ f32x4 red[4][2][NM][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int64_t ntok = (int64_t)a.B * a.T;
+  const int col0 = blockIdx.x * 16 * NM;
+  const int64_t f_begin = (int64_t)blockIdx.y * chunk;
+  int64_t f_end = f_begin + chunk;
+  if (f_end > ntok) f_end = ntok;
+  const float inv_base = a.eta_base != 0.f ? 1.f / a.eta_base : 0.f;
+  // one-hot selectors: picks column 16p + c out of a 32-column chunk
+  bf16x8 sel[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sel[p][e] = (bf16)((g == 2 * p + (c >> 3) && e == (c & 7)) ? 1.f : 0.f);
+
+  for (int hp = 0; hp < a.H; hp += 32) {
+    f32x4 acc[2][NM];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) acc[hb][m] = f32x4{0, 0, 0, 0};
+    for (int64_t f0 = f_begin + 16 * wave; f0 < f_end; f0 += 64) {
+      // x rows: token f0 + c, columns col0 + 32 h + 8g .. + 7 (zeros past the chunk)
+      const int64_t f = f0 + c;
+      const bool ok = f < f_end;
+      bf16x8 xr[(NM + 1) / 2];
+#pragma unroll
+      for (int h = 0; h < (NM + 1) / 2; ++h) {
+        xr[h] = bf16x8{};
+        if (ok) xr[h] = *(const bf16x8*)((const uint16_t*)a.x + f * a.dx + col0 + 32 * h + 8 * g);
+      }
+      // tokens in registers: xt[m] register r = x[f0 + 4g + r][col0 + 16 m + c]
+      uint2 xt[NM];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const f32x4 v = mfma_k32(xr[m >> 1], sel[m & 1], f32x4{0, 0, 0, 0});
+        xt[m] = make_uint2(pack_rne(v[0], v[1]), pack_rne(v[2], v[3]));
+      }
+      // batch and position of token f0 + 4g (one division per block), then
+      // of the next three, stepping into the next batch at each sequence end
+      int tb[4], tt[4];
+      {
+        const int fb = (int)(f0 + 4 * g);
+        int bi = fb / a.T, t = fb - bi * a.T;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          tb[r] = bi;
+          tt[r] = t;
+          if (++t == a.T) {
+            t = 0;
+            ++bi;
+          }
+        }
+      }
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const int h = hp + 16 * hb + c;
+        f32x4 d;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          d[r] = (f0 + 4 * g + r < f_end && h < a.H) ? gate_da_at(a, tb[r], h, tt[r], inv_base) : 0.f;
+        const Split4 ds = split4(d);
+        const bf16x8 dop = cat44(ds.hi, ds.lo);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) acc[hb][m] = mfma_k32(dop, cat8(xt[m], xt[m]), acc[hb][m]);
+      }
+    }
+    // register r of acc[hb][m] = sum over this wave's tokens for head
+    // hp + 16 hb + 4g + r, column col0 + 16 m + c
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) red[wave][hb][m][lane] = acc[hb][m];
+    __syncthreads();
+    for (int q = wave; q < 2 * NM; q += 4) {
+      const int hb = q / NM, m = q % NM;
+      const f32x4 s4 = (red[0][hb][m][lane] + red[1][hb][m][lane]) + (red[2][hb][m][lane] + red[3][hb][m][lane]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = hp + 16 * hb + 4 * g + r;
+        if (h < a.H) part[((size_t)blockIdx.y * a.H + h) * a.dx + col0 + 16 * m + c] = s4[r];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// dtheta[h][col] = sum over the chunks, in chunk order
+__global__ void __launch_bounds__(256) lr_gate_bwd_reduce_kernel(GateBwdArgs a, const float* part,
+                                                                 int nchunk) {
+  const int64_t n = (int64_t)a.H * a.dx;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    float s = 0.f;
+    for (int k = 0; k < nchunk; ++k) s += part[k * n + i];
+    a.dtheta[i] = s;
+  }
+}
+
+// dx[f][col .. col + 3] for 32 tokens f per workgroup, 4 columns per thread,
+// 16 heads at a time (their theta rows in registers, da in LDS).
+__global__ void __launch_bounds__(256) lr_gate_bwd_dx_kernel(GateBwdArgs a) {
+  __shared__ float sda[32][17];
+  const int tid = threadIdx.x;
+  const int64_t ntok = (int64_t)a.B * a.T;
+  const int64_t f0 = (int64_t)blockIdx.x * 32;
+  const int col = (blockIdx.y * 256 + tid) * 4;
+  const bool cok = col < a.dx;
+  const float inv_base = a.eta_base != 0.f ? 1.f / a.eta_base : 0.f;
+  float4 acc[32];
+#pragma unroll
+  for (int t = 0; t < 32; ++t) acc[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int hc = 0; hc < a.H; hc += 16) {
+    // stage da of the 32 tokens x 16 heads: thread -> (head tid / 16, tokens (tid % 16) + 16 j)
+    for (int j = 0; j < 2; ++j) {
+      const int hl = tid >> 4, tl = (tid & 15) + 16 * j;
+      sda[tl][hl] = gate_da(a, (int)f0 + tl, hc + hl, inv_base);
+    }
+    float4 th[16];
+#pragma unroll
+    for (int h = 0; h < 16; ++h)
+      th[h] = (cok && hc + h < a.H) ? *(const float4*)(a.theta + (size_t)(hc + h) * a.dx + col)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 32; ++t)
+#pragma unroll
+      for (int h = 0; h < 16; ++h) {
+        const float d = sda[t][h];
+        acc[t].x = fmaf(d, th[h].x, acc[t].x);
+        acc[t].y = fmaf(d, th[h].y, acc[t].y);
+        acc[t].z = fmaf(d, th[h].z, acc[t].z);
+        acc[t].w = fmaf(d, th[h].w, acc[t].w);
+      }
+    __syncthreads();
+  }
+  if (cok)
+#pragma unroll
+    for (int t = 0; t < 32; ++t)
+      if (f0 + t < ntok) *(float4*)(a.dxo + (f0 + t) * a.dx + col) = acc[t];
+}
+
+__global__ void __launch_bounds__(256) fill_zero_kernel(float* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_lr_gate_bwd(const GateBwdArgs& a, hipStream_t s) {
+  const int64_t ntok = (int64_t)a.B * a.T;
+  const int64_t nth = (int64_t)a.H * a.dx;
+  if (ntok == 0 || a.H == 0) {  // dtheta = 0 (no tokens), dx = 0 (no heads)
+    if (nth > 0) hipLaunchKernelGGL(fill_zero_kernel, dim3(256), dim3(256), 0, s, a.dtheta, nth);
+    if (ntok > 0) hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(256), 0, s, a.dxo, ntok * a.dx);
+    return hipGetLastError();
+  }
+  // dtheta: the token range in nchunk chunks whose partial sums go to the
+  // start of dx's memory (nchunk * H <= B * T rows of dx) and are summed in
+  // chunk order, before dx itself is written; one chunk (fewer than 2 H
+  // tokens) writes dtheta directly
+  int64_t nchunk = ntok / a.H;
+  if (nchunk > 16) nchunk = 16;
+  if (nchunk < 1) nchunk = 1;
+  const int chunk = (int)((ntok + nchunk - 1) / nchunk);
+  float* part = nchunk == 1 ? a.dtheta : a.dxo;
+  const dim3 g1(a.dx % 64 == 0 ? a.dx / 64 : a.dx / 32, (unsigned)nchunk);
+  if (a.dx % 64 == 0)
+    hipLaunchKernelGGL(lr_gate_bwd_dtheta_kernel<4>, g1, dim3(256), 0, s, a, part, chunk);
+  else
+    hipLaunchKernelGGL(lr_gate_bwd_dtheta_kernel<2>, g1, dim3(256), 0, s, a, part, chunk);
+  if (nchunk > 1) {
+    const int64_t nb = (nth + 255) / 256;
+    hipLaunchKernelGGL(lr_gate_bwd_reduce_kernel, dim3((unsigned)(nb < 1024 ? nb : 1024)), dim3(256), 0,
+                       s, a, (const float*)a.dxo, (int)nchunk);
+  }
+  hipLaunchKernelGGL(lr_gate_bwd_dx_kernel, dim3((unsigned)((ntok + 31) / 32), (unsigned)((a.dx + 1023) / 1024)),
+                     dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ttt

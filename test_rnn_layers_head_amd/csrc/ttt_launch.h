@@ -83,6 +83,23 @@ struct GateArgs {
 // tokens_per_workgroup: 32, 64 or 0 (chosen from the token count)
 hipError_t launch_lr_gate(const GateArgs& a, int tokens_per_workgroup, hipStream_t s);
 
+// Backward of the gate: dtheta [H][dx] and dxo [B][T][dx] from deta and the
+// forward's eta [B][H][T].
+struct GateBwdArgs {
+  const void* x;       // [B][T][dx] bf16
+  const float* theta;  // [H][dx]
+  const float* eta;    // [B][H][T]
+  const float* deta;   // [B][H][T]
+  float* dtheta;       // [H][dx]
+  float* dxo;          // [B][T][dx]
+  float eta_base;
+  int B;
+  int T;
+  int H;
+  int dx;  // multiple of 32
+};
+hipError_t launch_lr_gate_bwd(const GateBwdArgs& a, hipStream_t s);
+
 // One decode step for every (batch, head) unit.
 struct StepArgs {
   const void* q;  // [B][H][d]

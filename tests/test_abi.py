@@ -255,3 +255,28 @@ def test_linear_fwd_ckpt_argument_checks(lib):
     assert f(dt=_lib.TTT_F32) == status("TTT_ERR_UNSUPPORTED")
     assert f(ck=None) == status("TTT_ERR_NULL")
     assert f(ck=A[0]) == status("TTT_ERR_ALIAS")
+
+
+def gate_bwd(lib, **kw):
+    args = dict(x=A[0], dt=_lib.TTT_BF16, theta=A[1], eta_base=0.1, eta=A[2], deta=A[3], B=1,
+                T=16, H=2, dx=64, dth=A[4], dxo=A[5])
+    args.update(kw)
+    a = args
+    return lib.ttt_lr_gate_bwd(a["x"], a["dt"], a["theta"], a["eta_base"], a["eta"], a["deta"],
+                               a["B"], a["T"], a["H"], a["dx"], a["dth"], a["dxo"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dx=48), "TTT_ERR_UNSUPPORTED"),
+    (dict(dt=_lib.TTT_F32), "TTT_ERR_UNSUPPORTED"),
+    (dict(T=-1), "TTT_ERR_SHAPE"),
+    (dict(eta_base=float("nan")), "TTT_ERR_VALUE"),
+    (dict(deta=None), "TTT_ERR_NULL"),
+    (dict(eta=A[2] + 4), "TTT_ERR_ALIGN"),
+    (dict(dxo=A[0]), "TTT_ERR_ALIAS"),          # dx over x
+    (dict(dth=A[3]), "TTT_ERR_ALIAS"),          # dtheta over deta
+    (dict(dth=A[5] + 256), "TTT_ERR_ALIAS"),    # the two outputs
+])
+def test_lr_gate_bwd_argument_checks(lib, kw, expect):
+    assert gate_bwd(lib, **kw) == status(expect), lib.ttt_last_error()
+    assert lib.ttt_last_error().startswith(b"ttt_lr_gate_bwd:")

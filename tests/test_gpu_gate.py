@@ -1,6 +1,6 @@
 """GPU parity of the inner learning-rate gate ("论文速览 | TTT", §4.6),
-eta = eta_base * sigmoid(theta_lr[h] . x[b, t]), and of the gated scans,
-against the fp64 oracle.
+eta = eta_base * sigmoid(theta_lr[h] . x[b, t]), of its backward, and of the
+gated scans, against the fp64 oracle.
 
 Tolerance of the gate, from its arithmetic: each product theta_i x_i is
 exact on the device except for theta's three-term bf16 split, which drops at
@@ -20,7 +20,7 @@ import torch
 import gpu_util as gu
 from oracle import oracle
 from test_rnn_layers_head_amd import (TTTError, inputs, ttt_linear_gated_fwd, ttt_lr_gate,
-                                      ttt_mlp_gated_fwd)
+                                      ttt_lr_gate_bwd, ttt_mlp_gated_fwd)
 
 pytestmark = pytest.mark.gpu
 
@@ -176,3 +176,59 @@ def test_gated_empty_sequence_and_rejected_arguments():
     raw, _, theta = draw_gate(3, 1, 16, 2, 48)
     with pytest.raises(TTTError, match="TTT_ERR_UNSUPPORTED"):
         ttt_lr_gate(bf16_dev(raw), gu.f32(theta), 1.0)
+
+
+# Backward of the gate.  dtheta_lr sums products of exact bf16 x with da as
+# hi + lo bf16 (~2^-17 relative each) in fp32 over the tokens; dx sums fp32
+# products over the heads; da comes from the forward's fp32 eta rather than
+# the fp64 logit.  The bound is rel-L2 <= 2e-5 on both.
+TOL_GATE_BWD = 2e-5
+
+
+def check_gate_bwd(B, T, H, dx, eta_base, seed):
+    raw, x, theta = draw_gate(seed, B, T, H, dx)
+    deta = np.random.default_rng(seed + 1).standard_normal((B, H, T)).astype(np.float32)
+    xd, td = bf16_dev(raw), gu.f32(theta)
+    eta = ttt_lr_gate(xd, td, eta_base)
+    dth, dxg = ttt_lr_gate_bwd(xd, td, eta_base, eta, gu.f32(deta))
+    torch.cuda.synchronize()
+    rth, rx = oracle.lr_gate_bwd(x, theta, eta_base, deta)
+    m1, m2 = gu.metrics(dth.cpu().numpy(), rth), gu.metrics(dxg.cpu().numpy(), rx)
+    assert m1["rel_l2"] <= TOL_GATE_BWD and m2["rel_l2"] <= TOL_GATE_BWD, (m1, m2)
+
+
+@pytest.mark.parametrize("B,T,H,dx", [
+    (2, 100, 5, 96),     # 32-column groups, ragged token chunks
+    (1, 37, 16, 32),
+    (3, 64, 40, 256),    # two passes of heads
+    (1, 300, 33, 2048),
+    (1, 5, 12, 64),      # fewer tokens than heads: one chunk, no scratch
+    (9, 1, 2, 32),       # one-token sequences: every token starts a batch
+    (6, 3, 3, 64),       # sequences shorter than a four-token group
+])
+def test_gate_bwd_parity(B, T, H, dx):
+    check_gate_bwd(B, T, H, dx, 0.1, 200 + B + T + H + dx)
+
+
+def test_gate_bwd_1p3b_width():
+    # 8192 tokens of the 1.3B layer width: 16 token chunks
+    check_gate_bwd(1, 8192, 32, 2048, 0.1, 300)
+
+
+def test_gate_bwd_is_deterministic_and_handles_empty_dims():
+    raw, x, theta = draw_gate(5, 2, 500, 12, 768)
+    xd, td = bf16_dev(raw), gu.f32(theta)
+    eta = ttt_lr_gate(xd, td, 1.0)
+    deta = torch.randn(2, 12, 500, device="cuda")
+    a1, b1 = ttt_lr_gate_bwd(xd, td, 1.0, eta, deta)
+    a2, b2 = ttt_lr_gate_bwd(xd, td, 1.0, eta, deta)
+    torch.cuda.synchronize()
+    assert torch.equal(a1, a2) and torch.equal(b1, b2)
+    # no tokens: dtheta is zero
+    e0 = torch.empty(1, 0, 64, dtype=torch.bfloat16, device="cuda")
+    th = torch.randn(3, 64, device="cuda")
+    z = torch.empty(1, 3, 0, device="cuda")
+    dth0 = torch.full((3, 64), 7.0, device="cuda")
+    dth, dxg = ttt_lr_gate_bwd(e0, th, 1.0, z, z, dtheta_lr=dth0)
+    torch.cuda.synchronize()
+    assert torch.all(dth == 0) and dxg.numel() == 0
