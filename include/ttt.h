@@ -265,10 +265,11 @@ ttt_status_t ttt_lr_gate(const void* x, ttt_dtype_t x_dtype,
  * eta_base * sigmoid(a) at the forward's logit a (eta_base = 0: zero).
  * dtheta_lr is deterministic (partial sums over token chunks are added in a
  * fixed order; dx's memory holds them before dx itself is written, so its
- * prior contents do not matter).  Products: theta_lr and da enter as hi + lo
- * bf16 pairs against exact bf16 x on the matrix unit (dtheta_lr); dx is fp32
- * arithmetic.  Support and errors as ttt_lr_gate; outputs must not overlap
- * each other or an input.
+ * prior contents do not matter).  Products on the matrix unit: for
+ * dtheta_lr, da as a hi + lo bf16 pair against exact bf16 x; for dx, fp32
+ * products of da and theta_lr; all sums fp32.  Support and errors as
+ * ttt_lr_gate, and B*T*H < 2^30 and B*T*dx < 2^31 (else TTT_ERR_SHAPE);
+ * outputs must not overlap each other or an input.
  */
 ttt_status_t ttt_lr_gate_bwd(const void* x, ttt_dtype_t x_dtype,
                              const float* theta_lr, float eta_base,

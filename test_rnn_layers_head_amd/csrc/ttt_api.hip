@@ -545,8 +545,8 @@ ttt_status_t ttt_lr_gate_bwd(const void* x, ttt_dtype_t x_dtype, const float* th
   if (!(eta_base == eta_base) || eta_base > 3.4e38f || eta_base < -3.4e38f)
     return fail(TTT_ERR_VALUE, "%s: eta_base=%g must be finite", fn, (double)eta_base);
   const int64_t ntok = (int64_t)B * T;
-  if (ntok * H >= ((int64_t)1 << 31) || ntok * dx >= ((int64_t)1 << 31))
-    return fail(TTT_ERR_SHAPE, "%s: B*T*H or B*T*dx exceeds 2^31 - 1", fn);
+  if (ntok * H >= ((int64_t)1 << 30) || ntok * dx >= ((int64_t)1 << 31))
+    return fail(TTT_ERR_SHAPE, "%s: B*T*H exceeds 2^30 - 1 or B*T*dx exceeds 2^31 - 1", fn);
   const Range in[] = {rng("x", x, ntok * dx * 2), rng("theta_lr", theta_lr, (int64_t)H * dx * 4),
                       rng("eta", eta, ntok * H * 4), rng("deta", deta, ntok * H * 4)};
   const Range out[] = {rng("dtheta_lr", dtheta_lr, (int64_t)H * dx * 4),

@@ -17,6 +17,9 @@
 // 16x16x32 bf16 operand layouts (wave64, lane (c, g), c = lane % 16,
 // g = lane / 16): A lane holds A[c][8g .. 8g + 7], B lane holds
 // B[8g .. 8g + 7][c], accumulator register r holds C[4g + r][c].
+#include <algorithm>
+#include <mutex>
+
 #include "ttt_device.h"
 #include "ttt_launch.h"
 
@@ -194,21 +197,75 @@ __device__ __forceinline__ float gate_da(const GateBwdArgs& a, int f, int h, flo
   return gate_da_at(a, bi, h, f - bi * a.T, inv_base);
 }
 
-// Partial sums of dtheta over one chunk of tokens, for 16 * NM columns:
-// part[s][h][col].  Products on the matrix unit: x exact in bf16, brought to
-// tokens-in-registers by a one-hot selection MFMA (exact), da as hi + lo.
-// Four waves take interleaved 16-token blocks and meet in LDS.
-template <int NM>
-__global__ void __launch_bounds__(256) lr_gate_bwd_dtheta_kernel(GateBwdArgs a, float* part,
-                                                                 int chunk) {
-  __shared__ f32x4 red[4][2][NM][64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+// Inputs of da for one 16-token block in the dtheta layout: lane (c, g) holds
+// tokens f0 + 4g .. f0 + 4g + 3 of head hp + 16 hb + c (eta and deta).
+template <int HB>
+struct DaQuad {
+  f32x4 e[HB], de[HB];
+};
+
+// Loads from clamped (always valid) positions; masking happens on use.  eta
+// and deta come through buffer descriptors with 32-bit byte offsets
+// (B * T * H < 2^30).  VEC: T % 4 == 0, so a group of four tokens lies in
+// one sequence and its four values are one aligned 16-byte load.
+template <int HB, bool VEC>
+__device__ __forceinline__ void load_da_quad(const GateBwdArgs& a, __amdgpu_buffer_rsrc_t re,
+                                             __amdgpu_buffer_rsrc_t rd, int f0, int hp, int c, int g,
+                                             DaQuad<HB>& o) {
+  const int ntok = a.B * a.T;
+  if constexpr (VEC) {
+    const int fq = min(f0 + 4 * g, ntok - 4);
+    const int bi = fq / a.T, t = fq - bi * a.T;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const int h = min(hp + 16 * hb + c, a.H - 1);
+      const uint32_t off = (uint32_t)((bi * a.H + h) * a.T + t) * 4u;
+      o.e[hb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(re, off, 0, 0));
+      o.de[hb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0));
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int f = min(f0 + 4 * g + r, ntok - 1);
+      const int bi = f / a.T, t = f - bi * a.T;
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        const int h = min(hp + 16 * hb + c, a.H - 1);
+        const uint32_t off = (uint32_t)((bi * a.H + h) * a.T + t) * 4u;
+        o.e[hb][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, off, 0, 0));
+        o.de[hb][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, off, 0, 0));
+      }
+    }
+  }
+}
+
+// One pipeline stage of the dtheta kernel: the x rows and da inputs of one block.
+template <int NM, int HB>
+struct DthStage {
+  bf16x8 xr[(NM + 1) / 2];
+  DaQuad<HB> da;
+};
+
+// Partial sums of dtheta over one chunk of tokens, for 16 * NM columns and
+// the 16 * HB heads from hp on (one launch per pass): part[chunk][h][col].  Four waves take
+// interleaved 16-token blocks (J each, J a multiple of 3) and meet in LDS.
+// Products on the matrix unit: x exact in bf16, brought to tokens-in-
+// registers by a one-hot selection MFMA (exact), da as hi + lo.  The block
+// loads run two blocks ahead in three rotating register sets (so no copy of
+// a register that a load still writes); x rows come through a buffer
+// descriptor over the block's rows inside the chunk, so rows past the chunk
+// read as zeros without a branch.
+template <int NM, int HB, bool VEC>
+__global__ void __launch_bounds__(256) lr_gate_bwd_dtheta_kernel(GateBwdArgs a, float* part, int J,
+                                                                 int hp) {
+  __shared__ f32x4 red[4][HB][NM][64];
+  // wave index as a scalar: the buffer descriptors built from it stay uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
-  const int64_t ntok = (int64_t)a.B * a.T;
+  const int ntok = a.B * a.T;
   const int col0 = blockIdx.x * 16 * NM;
-  const int64_t f_begin = (int64_t)blockIdx.y * chunk;
-  int64_t f_end = f_begin + chunk;
-  if (f_end > ntok) f_end = ntok;
+  const int f_begin = blockIdx.y * 64 * J;
+  const int f_end = min(ntok, f_begin + 64 * J);
   const float inv_base = a.eta_base != 0.f ? 1.f / a.eta_base : 0.f;
   // one-hot selectors: picks column 16p + c out of a 32-column chunk
   bf16x8 sel[2];
@@ -216,67 +273,84 @@ __global__ void __launch_bounds__(256) lr_gate_bwd_dtheta_kernel(GateBwdArgs a, 
   for (int p = 0; p < 2; ++p)
 #pragma unroll
     for (int e = 0; e < 8; ++e) sel[p][e] = (bf16)((g == 2 * p + (c >> 3) && e == (c & 7)) ? 1.f : 0.f);
+  const uint32_t xoff = (uint32_t)((c * a.dx + col0 + 8 * g) * 2);
+  const uint32_t ebytes = (uint32_t)(ntok * a.H) * 4u;
+  const __amdgpu_buffer_rsrc_t re = make_rsrc(a.eta, ebytes), rd = make_rsrc(a.deta, ebytes);
 
-  for (int hp = 0; hp < a.H; hp += 32) {
-    f32x4 acc[2][NM];
+  {
+    f32x4 acc[HB][NM];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+    for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
       for (int m = 0; m < NM; ++m) acc[hb][m] = f32x4{0, 0, 0, 0};
-    for (int64_t f0 = f_begin + 16 * wave; f0 < f_end; f0 += 64) {
-      // x rows: token f0 + c, columns col0 + 32 h + 8g .. + 7 (zeros past the chunk)
-      const int64_t f = f0 + c;
-      const bool ok = f < f_end;
-      bf16x8 xr[(NM + 1) / 2];
+
+    // block j of this wave starts at token f_begin + 16 (wave + 4 j)
+    auto load = [&](int j, DthStage<NM, HB>& st) {
+      const int f0 = f_begin + 16 * (wave + 4 * j);
+      // (uniform values pinned to scalar registers: a descriptor built from
+      // a vector register would be split into a loop over distinct values)
+      const int rows = __builtin_amdgcn_readfirstlane(min(max(f_end - f0, 0), 16));
+      const int frow = __builtin_amdgcn_readfirstlane(min(f0, ntok));
+      const __amdgpu_buffer_rsrc_t rx =
+          make_rsrc((const uint16_t*)a.x + (int64_t)frow * a.dx, (uint32_t)(rows * a.dx * 2));
 #pragma unroll
-      for (int h = 0; h < (NM + 1) / 2; ++h) {
-        xr[h] = bf16x8{};
-        if (ok) xr[h] = *(const bf16x8*)((const uint16_t*)a.x + f * a.dx + col0 + 32 * h + 8 * g);
-      }
+      for (int h = 0; h < (NM + 1) / 2; ++h)
+        st.xr[h] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff + 64 * h, 0, 0));
+      load_da_quad<HB, VEC>(a, re, rd, min(f0, ntok - 1), hp, c, g, st.da);
+    };
+    auto compute = [&](int j, const DthStage<NM, HB>& st) {
+      const int f0 = f_begin + 16 * (wave + 4 * j);
       // tokens in registers: xt[m] register r = x[f0 + 4g + r][col0 + 16 m + c]
       uint2 xt[NM];
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        const f32x4 v = mfma_k32(xr[m >> 1], sel[m & 1], f32x4{0, 0, 0, 0});
+        const f32x4 v = mfma_k32(st.xr[m >> 1], sel[m & 1], f32x4{0, 0, 0, 0});
         xt[m] = make_uint2(pack_rne(v[0], v[1]), pack_rne(v[2], v[3]));
       }
-      // batch and position of token f0 + 4g (one division per block), then
-      // of the next three, stepping into the next batch at each sequence end
-      int tb[4], tt[4];
-      {
-        const int fb = (int)(f0 + 4 * g);
-        int bi = fb / a.T, t = fb - bi * a.T;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          tb[r] = bi;
-          tt[r] = t;
-          if (++t == a.T) {
-            t = 0;
-            ++bi;
-          }
-        }
-      }
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const int h = hp + 16 * hb + c;
+      for (int hb = 0; hb < HB; ++hb) {
+        const bool hok = hp + 16 * hb + c < a.H;
         f32x4 d;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          d[r] = (f0 + 4 * g + r < f_end && h < a.H) ? gate_da_at(a, tb[r], h, tt[r], inv_base) : 0.f;
+        for (int r = 0; r < 4; ++r) {
+          const float e = st.da.e[hb][r];
+          const float v = st.da.de[hb][r] * e * (1.f - e * inv_base);
+          d[r] = (hok && f0 + 4 * g + r < f_end) ? v : 0.f;
+        }
         const Split4 ds = split4(d);
         const bf16x8 dop = cat44(ds.hi, ds.lo);
 #pragma unroll
         for (int m = 0; m < NM; ++m) acc[hb][m] = mfma_k32(dop, cat8(xt[m], xt[m]), acc[hb][m]);
       }
+    };
+    // scheduling fences keep each set's loads where they stand, so a set is
+    // never reloaded while its previous contents are still being read
+    DthStage<NM, HB> sa, sb, sc;
+    load(0, sa);
+    load(1, sb);
+    for (int j = 0; j < J; j += 3) {
+      __builtin_amdgcn_sched_barrier(0);
+      load(j + 2, sc);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(j, sa);
+      __builtin_amdgcn_sched_barrier(0);
+      load(j + 3, sa);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(j + 1, sb);
+      __builtin_amdgcn_sched_barrier(0);
+      load(j + 4, sb);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(j + 2, sc);
     }
+
     // register r of acc[hb][m] = sum over this wave's tokens for head
     // hp + 16 hb + 4g + r, column col0 + 16 m + c
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+    for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
       for (int m = 0; m < NM; ++m) red[wave][hb][m][lane] = acc[hb][m];
     __syncthreads();
-    for (int q = wave; q < 2 * NM; q += 4) {
+    for (int q = wave; q < HB * NM; q += 4) {
       const int hb = q / NM, m = q % NM;
       const f32x4 s4 = (red[0][hb][m][lane] + red[1][hb][m][lane]) + (red[2][hb][m][lane] + red[3][hb][m][lane]);
 #pragma unroll
@@ -285,7 +359,6 @@ __global__ void __launch_bounds__(256) lr_gate_bwd_dtheta_kernel(GateBwdArgs a, 
         if (h < a.H) part[((size_t)blockIdx.y * a.H + h) * a.dx + col0 + 16 * m + c] = s4[r];
       }
     }
-    __syncthreads();
   }
 }
 
@@ -295,52 +368,118 @@ __global__ void __launch_bounds__(256) lr_gate_bwd_reduce_kernel(GateBwdArgs a, 
   const int64_t n = (int64_t)a.H * a.dx;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     float s = 0.f;
+#pragma unroll 8
     for (int k = 0; k < nchunk; ++k) s += part[k * n + i];
     a.dtheta[i] = s;
   }
 }
 
-// dx[f][col .. col + 3] for 32 tokens f per workgroup, 4 columns per thread,
-// 16 heads at a time (their theta rows in registers, da in LDS).
-__global__ void __launch_bounds__(256) lr_gate_bwd_dx_kernel(GateBwdArgs a) {
-  __shared__ float sda[32][17];
-  const int tid = threadIdx.x;
-  const int64_t ntok = (int64_t)a.B * a.T;
-  const int64_t f0 = (int64_t)blockIdx.x * 32;
-  const int col = (blockIdx.y * 256 + tid) * 4;
-  const bool cok = col < a.dx;
+// da of 16 tokens for the dx kernel: lane (c, g) holds token f0 + c of heads
+// hp + 4j + g, j < KS (eta and deta).
+template <int KS>
+struct DaCol {
+  float e[KS], de[KS];
+};
+
+// dx[f][:] = sum_h da[f][h] theta[h][:] on the fp32 matrix unit (16x16x4
+// f32 MFMA, exact fp32 products): per wave a tile of 16 NE columns, heads in
+// passes of 4 KS.  Product e covers tile columns 16 e .. 16 e + 15 (its
+// 16-row index m is the column 16 e + m): A = theta^T (lane (c, g): head
+// 4j + g, column 16 e + c, loaded once per pass), B = da^T (lane (c, g):
+// token c, head 4j + g); the result lane (c, g) holds token c, columns
+// 16 e + 4g .. 16 e + 4g + 3, so one 16-byte store per product and lane
+// writes 64 contiguous bytes of each of 16 rows.
+// Workgroup = four waves on one column tile, taking interleaved 16-token
+// groups (G each, G a multiple of 3); the da loads run two groups ahead in
+// three rotating register sets; dx goes out through a buffer descriptor over
+// the group's rows, so rows past the chunk are dropped without a branch.
+// One launch per pass of 4 KS heads from hp on; the passes after the first
+// (ADD, H > 4 KS) add to what the earlier ones stored.
+template <int NE, int KS, bool ADD>
+__global__ void __launch_bounds__(256) lr_gate_bwd_dx_kernel(GateBwdArgs a, int G, int hp) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  // wave index as a scalar: the buffer descriptors built from it stay uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int ntok = a.B * a.T;
+  const int col0 = blockIdx.x * 16 * NE;
+  const int f_begin = blockIdx.y * 64 * G;
+  const int f_end = min(ntok, f_begin + 64 * G);
   const float inv_base = a.eta_base != 0.f ? 1.f / a.eta_base : 0.f;
-  float4 acc[32];
+  const uint32_t ooff = (uint32_t)((c * a.dx + col0 + 4 * g) * 4);
+  const uint32_t ebytes = (uint32_t)(ntok * a.H) * 4u;  // B * T * H < 2^30
+  const __amdgpu_buffer_rsrc_t re = make_rsrc(a.eta, ebytes), rd = make_rsrc(a.deta, ebytes);
+
+  {
+    float th[KS][NE];
 #pragma unroll
-  for (int t = 0; t < 32; ++t) acc[t] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int hc = 0; hc < a.H; hc += 16) {
-    // stage da of the 32 tokens x 16 heads: thread -> (head tid / 16, tokens (tid % 16) + 16 j)
-    for (int j = 0; j < 2; ++j) {
-      const int hl = tid >> 4, tl = (tid & 15) + 16 * j;
-      sda[tl][hl] = gate_da(a, (int)f0 + tl, hc + hl, inv_base);
+    for (int j = 0; j < KS; ++j) {
+      const int h = hp + 4 * j + g;
+      const float* p = a.theta + (size_t)min(h, a.H - 1) * a.dx + col0 + c;
+#pragma unroll
+      for (int e = 0; e < NE; ++e) th[j][e] = h < a.H ? p[16 * e] : 0.f;
     }
-    float4 th[16];
+
+    // group i of this wave starts at token f_begin + 16 (wave + 4 i)
+    auto load = [&](int i, DaCol<KS>& st) {
+      const int f = min(f_begin + 16 * (wave + 4 * i) + c, ntok - 1);
+      const int bi = f / a.T, t = f - bi * a.T;
 #pragma unroll
-    for (int h = 0; h < 16; ++h)
-      th[h] = (cok && hc + h < a.H) ? *(const float4*)(a.theta + (size_t)(hc + h) * a.dx + col)
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < 32; ++t)
-#pragma unroll
-      for (int h = 0; h < 16; ++h) {
-        const float d = sda[t][h];
-        acc[t].x = fmaf(d, th[h].x, acc[t].x);
-        acc[t].y = fmaf(d, th[h].y, acc[t].y);
-        acc[t].z = fmaf(d, th[h].z, acc[t].z);
-        acc[t].w = fmaf(d, th[h].w, acc[t].w);
+      for (int j = 0; j < KS; ++j) {
+        const int h = min(hp + 4 * j + g, a.H - 1);
+        const uint32_t off = (uint32_t)((bi * a.H + h) * a.T + t) * 4u;
+        st.e[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(re, off, 0, 0));
+        st.de[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, off, 0, 0));
       }
-    __syncthreads();
-  }
-  if (cok)
+    };
+    auto compute = [&](int i, const DaCol<KS>& st) {
+      const int f0 = f_begin + 16 * (wave + 4 * i);
+      const bool tok = f0 + c < f_end;
+      float bj[KS];
 #pragma unroll
-    for (int t = 0; t < 32; ++t)
-      if (f0 + t < ntok) *(float4*)(a.dxo + (f0 + t) * a.dx + col) = acc[t];
+      for (int j = 0; j < KS; ++j) {
+        const float e = st.e[j];
+        const float v = st.de[j] * e * (1.f - e * inv_base);
+        bj[j] = (tok && hp + 4 * j + g < a.H) ? v : 0.f;
+      }
+      f32x4 acc[NE];
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        acc[e] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < KS; ++j) acc[e] = mfma_f32(th[j][e], bj[j], acc[e]);
+      }
+      const int rows = __builtin_amdgcn_readfirstlane(min(max(f_end - f0, 0), 16));
+      const int frow = __builtin_amdgcn_readfirstlane(min(f0, ntok));
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.dxo + (int64_t)frow * a.dx, (uint32_t)(rows * a.dx * 4));
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const uint32_t off = ooff + (uint32_t)(64 * e);
+        f32x4 o = acc[e];
+        if constexpr (ADD) o += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), ro, off, 0, 0);
+      }
+    };
+    // scheduling fences keep each set's loads where they stand, so a set is
+    // never reloaded while its previous contents are still being read
+    DaCol<KS> sa, sb, sc;
+    load(0, sa);
+    load(1, sb);
+    for (int i = 0; i < G; i += 3) {
+      __builtin_amdgcn_sched_barrier(0);
+      load(i + 2, sc);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(i, sa);
+      __builtin_amdgcn_sched_barrier(0);
+      load(i + 3, sa);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(i + 1, sb);
+      __builtin_amdgcn_sched_barrier(0);
+      load(i + 4, sb);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(i + 2, sc);
+    }
+  }
 }
 
 __global__ void __launch_bounds__(256) fill_zero_kernel(float* p, int64_t n) {
@@ -350,35 +489,95 @@ __global__ void __launch_bounds__(256) fill_zero_kernel(float* p, int64_t n) {
 
 }  // namespace
 
+// Workgroups of `kernel` (256 threads) resident on the whole device at once,
+// cached per kernel and device (the cache is shared by host threads).
+int resident_workgroups(const void* kernel) {
+  struct Entry {
+    const void* k;
+    int dev, n;
+  };
+  static Entry cache[64];
+  static int used = 0;
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < used; ++i)
+    if (cache[i].k == kernel && cache[i].dev == dev) return cache[i].n;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  const int n = per_cu * cus;
+  if (used < 64) cache[used++] = Entry{kernel, dev, n};
+  return n;
+}
+
 hipError_t launch_lr_gate_bwd(const GateBwdArgs& a, hipStream_t s) {
-  const int64_t ntok = (int64_t)a.B * a.T;
+  const int ntok = a.B * a.T;  // B * T * dx < 2^31 (checked by the ABI)
   const int64_t nth = (int64_t)a.H * a.dx;
   if (ntok == 0 || a.H == 0) {  // dtheta = 0 (no tokens), dx = 0 (no heads)
     if (nth > 0) hipLaunchKernelGGL(fill_zero_kernel, dim3(256), dim3(256), 0, s, a.dtheta, nth);
-    if (ntok > 0) hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(256), 0, s, a.dxo, ntok * a.dx);
+    if (ntok > 0)
+      hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(256), 0, s, a.dxo, (int64_t)ntok * a.dx);
     return hipGetLastError();
   }
-  // dtheta: the token range in nchunk chunks whose partial sums go to the
-  // start of dx's memory (nchunk * H <= B * T rows of dx) and are summed in
-  // chunk order, before dx itself is written; one chunk (fewer than 2 H
-  // tokens) writes dtheta directly
-  int64_t nchunk = ntok / a.H;
-  if (nchunk > 16) nchunk = 16;
-  if (nchunk < 1) nchunk = 1;
-  const int chunk = (int)((ntok + nchunk - 1) / nchunk);
-  float* part = nchunk == 1 ? a.dtheta : a.dxo;
-  const dim3 g1(a.dx % 64 == 0 ? a.dx / 64 : a.dx / 32, (unsigned)nchunk);
-  if (a.dx % 64 == 0)
-    hipLaunchKernelGGL(lr_gate_bwd_dtheta_kernel<4>, g1, dim3(256), 0, s, a, part, chunk);
+  const bool small_h = a.H <= 16;
+  // Token chunks are sized so that the whole grid is resident at once (no
+  // second partial round of workgroups): per column tile, at most
+  // resident / tiles chunks, each a multiple of 3 blocks per wave.
+  auto per_wave = [&](const void* k, int tiles, int64_t units) {
+    const int64_t slots = std::max<int64_t>(1, resident_workgroups(k) / tiles);
+    const int64_t u = (units + 4 * slots - 1) / (4 * slots);  // 16-token units per wave
+    return (int)(3 * ((u + 2) / 3));
+  };
+
+  // dtheta: chunks of 64 J tokens (J blocks of 16 per wave) whose partial
+  // sums go to the start of dx's memory (nchunk * H <= B * T rows of dx) and
+  // are summed in chunk order before dx itself is written; a single chunk
+  // writes dtheta directly
+  const int nm = a.dx % 64 == 0 ? 4 : 2;
+  const int ncol1 = a.dx / (16 * nm);
+  const bool vec = a.T % 4 == 0;
+  const void* kd;
+  if (nm == 4)
+    kd = small_h ? (vec ? (const void*)lr_gate_bwd_dtheta_kernel<4, 1, true> : (const void*)lr_gate_bwd_dtheta_kernel<4, 1, false>)
+                 : (vec ? (const void*)lr_gate_bwd_dtheta_kernel<4, 2, true> : (const void*)lr_gate_bwd_dtheta_kernel<4, 2, false>);
   else
-    hipLaunchKernelGGL(lr_gate_bwd_dtheta_kernel<2>, g1, dim3(256), 0, s, a, part, chunk);
+    kd = small_h ? (vec ? (const void*)lr_gate_bwd_dtheta_kernel<2, 1, true> : (const void*)lr_gate_bwd_dtheta_kernel<2, 1, false>)
+                 : (vec ? (const void*)lr_gate_bwd_dtheta_kernel<2, 2, true> : (const void*)lr_gate_bwd_dtheta_kernel<2, 2, false>);
+  int J = per_wave(kd, ncol1, (ntok + 15) / 16);
+  auto chunks = [&](int j) { return (ntok + 64 * j - 1) / (64 * j); };
+  while (chunks(J) > 1 && (int64_t)chunks(J) * a.H > ntok) J += 3;
+  const int nchunk = chunks(J);
+  float* part = nchunk == 1 ? a.dtheta : a.dxo;
+  const dim3 g1((unsigned)ncol1, (unsigned)nchunk);
+  for (int hp = 0; hp < a.H; hp += small_h ? 16 : 32) {
+    void* args[] = {(void*)&a, (void*)&part, (void*)&J, (void*)&hp};
+    const hipError_t e = hipLaunchKernel(kd, g1, dim3(256), args, 0, s);
+    if (e != hipSuccess) return e;
+  }
   if (nchunk > 1) {
     const int64_t nb = (nth + 255) / 256;
     hipLaunchKernelGGL(lr_gate_bwd_reduce_kernel, dim3((unsigned)(nb < 1024 ? nb : 1024)), dim3(256), 0,
-                       s, a, (const float*)a.dxo, (int)nchunk);
+                       s, a, (const float*)a.dxo, nchunk);
   }
-  hipLaunchKernelGGL(lr_gate_bwd_dx_kernel, dim3((unsigned)((ntok + 31) / 32), (unsigned)((a.dx + 1023) / 1024)),
-                     dim3(256), 0, s, a);
+
+  // dx: chunks of 64 G tokens per workgroup (G groups of 16 per wave), tiles
+  // of 128 columns (32 when dx is not a multiple of 128)
+  const int ne = a.dx % 128 == 0 ? 8 : 2;
+  const int ncol2 = a.dx / (16 * ne);
+  const void* kx0 = ne == 8 ? (small_h ? (const void*)lr_gate_bwd_dx_kernel<8, 4, false> : (const void*)lr_gate_bwd_dx_kernel<8, 8, false>)
+                            : (small_h ? (const void*)lr_gate_bwd_dx_kernel<2, 4, false> : (const void*)lr_gate_bwd_dx_kernel<2, 8, false>);
+  const void* kx1 = ne == 8 ? (const void*)lr_gate_bwd_dx_kernel<8, 8, true> : (const void*)lr_gate_bwd_dx_kernel<2, 8, true>;
+  int G = per_wave(kx0, ncol2, (ntok + 15) / 16);
+  const dim3 g2((unsigned)ncol2, (unsigned)((ntok + 64 * G - 1) / (64 * G)));
+  for (int hp = 0; hp < a.H; hp += small_h ? 16 : 32) {
+    void* args[] = {(void*)&a, (void*)&G, (void*)&hp};
+    const hipError_t e = hipLaunchKernel(hp == 0 ? kx0 : kx1, g2, dim3(256), args, 0, s);
+    if (e != hipSuccess) return e;
+  }
   return hipGetLastError();
 }
 

@@ -270,6 +270,7 @@ def gate_bwd(lib, **kw):
     (dict(dx=48), "TTT_ERR_UNSUPPORTED"),
     (dict(dt=_lib.TTT_F32), "TTT_ERR_UNSUPPORTED"),
     (dict(T=-1), "TTT_ERR_SHAPE"),
+    (dict(T=1 << 20, H=1 << 10), "TTT_ERR_SHAPE"),   # B*T*H = 2^30
     (dict(eta_base=float("nan")), "TTT_ERR_VALUE"),
     (dict(deta=None), "TTT_ERR_NULL"),
     (dict(eta=A[2] + 4), "TTT_ERR_ALIGN"),

@@ -205,6 +205,8 @@ def check_gate_bwd(B, T, H, dx, eta_base, seed):
     (1, 5, 12, 64),      # fewer tokens than heads: one chunk, no scratch
     (9, 1, 2, 32),       # one-token sequences: every token starts a batch
     (6, 3, 3, 64),       # sequences shorter than a four-token group
+    (2, 50, 36, 96),     # two head passes on 32-column tiles
+    (2, 33, 20, 160),    # ragged sequences, one 32-head pass, 32-column tiles
 ])
 def test_gate_bwd_parity(B, T, H, dx):
     check_gate_bwd(B, T, H, dx, 0.1, 200 + B + T + H + dx)
