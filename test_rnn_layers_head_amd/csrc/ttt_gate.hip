@@ -394,8 +394,9 @@ struct DaCol {
 // three rotating register sets; dx goes out through a buffer descriptor over
 // the group's rows, so rows past the chunk are dropped without a branch.
 // One launch per pass of 4 KS heads from hp on; the passes after the first
-// (ADD, H > 4 KS) add to what the earlier ones stored.
-template <int NE, int KS, bool ADD>
+// (ADD, H > 4 KS) add to what the earlier ones stored.  NT: nontemporal
+// stores, for outputs too large to stay in the caches.
+template <int NE, int KS, bool ADD, bool NT>
 __global__ void __launch_bounds__(256) lr_gate_bwd_dx_kernel(GateBwdArgs a, int G, int hp) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   // wave index as a scalar: the buffer descriptors built from it stay uniform
@@ -457,7 +458,7 @@ __global__ void __launch_bounds__(256) lr_gate_bwd_dx_kernel(GateBwdArgs a, int 
         const uint32_t off = ooff + (uint32_t)(64 * e);
         f32x4 o = acc[e];
         if constexpr (ADD) o += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0));
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), ro, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), ro, off, 0, NT ? 2 : 0);
       }
     };
     // scheduling fences keep each set's loads where they stand, so a set is
@@ -537,11 +538,14 @@ hipError_t launch_lr_gate_bwd(const GateBwdArgs& a, hipStream_t s) {
   // sums go to the start of dx's memory (nchunk * H <= B * T rows of dx) and
   // are summed in chunk order before dx itself is written; a single chunk
   // writes dtheta directly
-  const int nm = a.dx % 64 == 0 ? 4 : 2;
+  const int nm = a.dx % 128 == 0 ? 8 : a.dx % 64 == 0 ? 4 : 2;
   const int ncol1 = a.dx / (16 * nm);
   const bool vec = a.T % 4 == 0;
   const void* kd;
-  if (nm == 4)
+  if (nm == 8)
+    kd = small_h ? (vec ? (const void*)lr_gate_bwd_dtheta_kernel<8, 1, true> : (const void*)lr_gate_bwd_dtheta_kernel<8, 1, false>)
+                 : (vec ? (const void*)lr_gate_bwd_dtheta_kernel<8, 2, true> : (const void*)lr_gate_bwd_dtheta_kernel<8, 2, false>);
+  else if (nm == 4)
     kd = small_h ? (vec ? (const void*)lr_gate_bwd_dtheta_kernel<4, 1, true> : (const void*)lr_gate_bwd_dtheta_kernel<4, 1, false>)
                  : (vec ? (const void*)lr_gate_bwd_dtheta_kernel<4, 2, true> : (const void*)lr_gate_bwd_dtheta_kernel<4, 2, false>);
   else
@@ -565,12 +569,17 @@ hipError_t launch_lr_gate_bwd(const GateBwdArgs& a, hipStream_t s) {
   }
 
   // dx: chunks of 64 G tokens per workgroup (G groups of 16 per wave), tiles
-  // of 128 columns (32 when dx is not a multiple of 128)
+  // of 128 columns (32 when dx is not a multiple of 128); outputs beyond
+  // 128 MB are stored nontemporally
   const int ne = a.dx % 128 == 0 ? 8 : 2;
   const int ncol2 = a.dx / (16 * ne);
-  const void* kx0 = ne == 8 ? (small_h ? (const void*)lr_gate_bwd_dx_kernel<8, 4, false> : (const void*)lr_gate_bwd_dx_kernel<8, 8, false>)
-                            : (small_h ? (const void*)lr_gate_bwd_dx_kernel<2, 4, false> : (const void*)lr_gate_bwd_dx_kernel<2, 8, false>);
-  const void* kx1 = ne == 8 ? (const void*)lr_gate_bwd_dx_kernel<8, 8, true> : (const void*)lr_gate_bwd_dx_kernel<2, 8, true>;
+  const bool nt = (int64_t)ntok * a.dx * 4 >= ((int64_t)128 << 20);
+#define TTT_DXK(NE, KS, ADD) \
+  (nt ? (const void*)lr_gate_bwd_dx_kernel<NE, KS, ADD, true> : (const void*)lr_gate_bwd_dx_kernel<NE, KS, ADD, false>)
+  const void* kx0 = ne == 8 ? (small_h ? TTT_DXK(8, 4, false) : TTT_DXK(8, 8, false))
+                            : (small_h ? TTT_DXK(2, 4, false) : TTT_DXK(2, 8, false));
+  const void* kx1 = ne == 8 ? TTT_DXK(8, 8, true) : TTT_DXK(2, 8, true);
+#undef TTT_DXK
   int G = per_wave(kx0, ncol2, (ntok + 15) / 16);
   const dim3 g2((unsigned)ncol2, (unsigned)((ntok + 64 * G - 1) / (64 * G)));
   for (int hp = 0; hp < a.H; hp += small_h ? 16 : 32) {
