@@ -387,8 +387,9 @@ struct DaCol {
 // 16-row index m is the column 16 e + m): A = theta^T (lane (c, g): head
 // 4j + g, column 16 e + c, loaded once per pass), B = da^T (lane (c, g):
 // token c, head 4j + g); the result lane (c, g) holds token c, columns
-// 16 e + 4g .. 16 e + 4g + 3, so one 16-byte store per product and lane
-// writes 64 contiguous bytes of each of 16 rows.
+// 16 e + 4g .. 16 e + 4g + 3.  The 16 x 16 NE result tile goes through the
+// wave's own LDS tile (rows padded by four words: conflict-free both ways)
+// and out row by row: 4 NE lanes per row, 16 NE * 4 contiguous bytes.
 // Workgroup = four waves on one column tile, taking interleaved 16-token
 // groups (G each, G a multiple of 3); the da loads run two groups ahead in
 // three rotating register sets; dx goes out through a buffer descriptor over
@@ -399,6 +400,9 @@ struct DaCol {
 template <int NE, int KS, bool ADD, bool NT>
 __global__ void __launch_bounds__(256) lr_gate_bwd_dx_kernel(GateBwdArgs a, int G, int hp) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int PITCH = 16 * NE + 4;  // words per LDS row
+  constexpr int LPR = 4 * NE;         // lanes per output row
+  __shared__ f32x4 tile[4][16 * PITCH / 4];
   // wave index as a scalar: the buffer descriptors built from it stay uniform
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
@@ -407,7 +411,10 @@ __global__ void __launch_bounds__(256) lr_gate_bwd_dx_kernel(GateBwdArgs a, int 
   const int f_begin = blockIdx.y * 64 * G;
   const int f_end = min(ntok, f_begin + 64 * G);
   const float inv_base = a.eta_base != 0.f ? 1.f / a.eta_base : 0.f;
-  const uint32_t ooff = (uint32_t)((c * a.dx + col0 + 4 * g) * 4);
+  // output lane mapping: row lane / LPR (+ 64 / LPR per store), columns 4 (lane % LPR) ..
+  const int orow = lane / LPR, ocol = 4 * (lane % LPR);
+  const uint32_t ooff = (uint32_t)((orow * a.dx + col0 + ocol) * 4);
+  f32x4* const wt = tile[wave];
   const uint32_t ebytes = (uint32_t)(ntok * a.H) * 4u;  // B * T * H < 2^30
   const __amdgpu_buffer_rsrc_t re = make_rsrc(a.eta, ebytes), rd = make_rsrc(a.deta, ebytes);
 
@@ -454,9 +461,12 @@ __global__ void __launch_bounds__(256) lr_gate_bwd_dx_kernel(GateBwdArgs a, int 
       const int frow = __builtin_amdgcn_readfirstlane(min(f0, ntok));
       const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.dxo + (int64_t)frow * a.dx, (uint32_t)(rows * a.dx * 4));
 #pragma unroll
-      for (int e = 0; e < NE; ++e) {
-        const uint32_t off = ooff + (uint32_t)(64 * e);
-        f32x4 o = acc[e];
+      for (int e = 0; e < NE; ++e) wt[(c * PITCH + 16 * e + 4 * g) / 4] = acc[e];
+#pragma unroll
+      for (int k = 0; k < NE; ++k) {  // rows orow + (64 / LPR) k
+        const int r = orow + (64 / LPR) * k;
+        const uint32_t off = ooff + (uint32_t)((64 / LPR) * k * a.dx * 4);
+        f32x4 o = wt[(r * PITCH + ocol) / 4];
         if constexpr (ADD) o += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0));
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), ro, off, 0, NT ? 2 : 0);
       }
