@@ -42,7 +42,7 @@
  *            its initial-state input only when w0_per_batch = 1 and the two
  *            pointers are equal (in-place resume); any other overlap is
  *            TTT_ERR_ALIAS.
- * Support:   d = 64; any T >= 0, B, H >= 0 with B*H*T*d < 2^31.
+ * Support:   d = 64; any 0 <= T < 2^24, B, H >= 0 with B*H*T*d < 2^31.
  *            TTT-Linear: fp32 or bf16 q/k/v; mini-batch b with b | 16 or
  *            16 | b (1, 2, 4, 8, 16, 32, 48, 64, ...).
  *            TTT-MLP: hidden = 256, bf16 q/k/v, b | 16 (1, 2, 4, 8, 16).

@@ -59,6 +59,8 @@ ttt_status_t check_common(const char* fn, ttt_dtype_t dt, int32_t w0_per_batch, 
   const int64_t elems = (int64_t)B * H * T * d;
   if (elems >= ((int64_t)1 << 31))
     return fail(TTT_ERR_SHAPE, "%s: B*H*T*d = %lld exceeds 2^31 - 1", fn, (long long)elems);
+  if (T >= (1 << 24))  // a unit's T x 64 fp32 output stays within 32-bit byte offsets
+    return fail(TTT_ERR_SHAPE, "%s: T = %d exceeds 2^24 - 1", fn, T);
   if ((int64_t)B * H == 0) return TTT_OK;
   for (int i = 0; i < nin; ++i) {
     const bool seq = i < 4;  // q, k, v, eta come first

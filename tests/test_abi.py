@@ -102,6 +102,7 @@ def status(code):
     (dict(z=A[1]), "TTT_ERR_ALIAS"),
     (dict(w=A[4]), "TTT_ERR_ALIAS"),            # in place needs w0_per_batch = 1
     (dict(B=1 << 20, H=1 << 10, T=1 << 10), "TTT_ERR_SHAPE"),
+    (dict(B=1, H=1, T=1 << 24), "TTT_ERR_SHAPE"),   # one unit's z past 32-bit offsets
     (dict(B=0), "TTT_OK"),                      # empty work: nothing launched
     (dict(H=0), "TTT_OK"),
 ])
