@@ -269,7 +269,9 @@ ttt_status_t ttt_lr_gate(const void* x, ttt_dtype_t x_dtype,
  * dtheta_lr, da as a hi + lo bf16 pair against exact bf16 x; for dx, fp32
  * products of da and theta_lr; all sums fp32.  Support and errors as
  * ttt_lr_gate, and B*T*H < 2^30 and B*T*dx < 2^31 (else TTT_ERR_SHAPE);
- * outputs must not overlap each other or an input.
+ * outputs must not overlap each other or an input.  x is taken to be
+ * finite: a non-finite element of x makes dtheta_lr non-finite across its
+ * 32-column group (x is transposed on the matrix unit by one-hot products).
  */
 ttt_status_t ttt_lr_gate_bwd(const void* x, ttt_dtype_t x_dtype,
                              const float* theta_lr, float eta_base,

@@ -183,20 +183,6 @@ hipError_t launch_lr_gate(const GateArgs& a, int tokens_per_workgroup, hipStream
 namespace ttt {
 namespace {
 
-// da at (batch bi, head h, position t); B * H * T < 2^31 (checked by the ABI)
-__device__ __forceinline__ float gate_da_at(const GateBwdArgs& a, int bi, int h, int t,
-                                            float inv_base) {
-  const int i = (bi * a.H + h) * a.T + t;
-  const float e = a.eta[i];
-  return a.deta[i] * e * (1.f - e * inv_base);
-}
-// da of flat token f = bi * T + t (zero past the tokens or the heads)
-__device__ __forceinline__ float gate_da(const GateBwdArgs& a, int f, int h, float inv_base) {
-  if (f >= a.B * a.T || h >= a.H) return 0.f;
-  const int bi = f / a.T;
-  return gate_da_at(a, bi, h, f - bi * a.T, inv_base);
-}
-
 // Inputs of da for one 16-token block in the dtheta layout: lane (c, g) holds
 // tokens f0 + 4g .. f0 + 4g + 3 of head hp + 16 hb + c (eta and deta).
 template <int HB>
@@ -247,8 +233,9 @@ struct DthStage {
 };
 
 // Partial sums of dtheta over one chunk of tokens, for 16 * NM columns and
-// the 16 * HB heads from hp on (one launch per pass): part[chunk][h][col].  Four waves take
-// interleaved 16-token blocks (J each, J a multiple of 3) and meet in LDS.
+// the 16 * HB heads from hp on (one launch per pass): part[chunk][h][col].
+// Four waves take interleaved 16-token blocks (J each, J a multiple of 3) and
+// meet in LDS.
 // Products on the matrix unit: x exact in bf16, brought to tokens-in-
 // registers by a one-hot selection MFMA (exact), da as hi + lo.  The block
 // loads run two blocks ahead in three rotating register sets (so no copy of
