@@ -18,7 +18,6 @@
 // g = lane / 16): A lane holds A[c][8g .. 8g + 7], B lane holds
 // B[8g .. 8g + 7][c], accumulator register r holds C[4g + r][c].
 #include <algorithm>
-#include <mutex>
 
 #include "ttt_device.h"
 #include "ttt_launch.h"
@@ -487,29 +486,18 @@ __global__ void __launch_bounds__(256) fill_zero_kernel(float* p, int64_t n) {
 
 }  // namespace
 
-// Workgroups of `kernel` (256 threads) resident on the whole device at once,
-// cached per kernel and device (the cache is shared by host threads).
+// Workgroups of `kernel` (256 threads) resident on the current device at
+// once, from the runtime's occupancy query (host-side, asked on every call:
+// the library keeps nothing between calls).
+// A failed query falls back to one workgroup per CU of 256 CUs (a sizing
+// choice only) and its error is cleared, so the launches report their own.
 int resident_workgroups(const void* kernel) {
-  struct Entry {
-    const void* k;
-    int dev, n;
-  };
-  static Entry cache[64];
-  static int used = 0;
-  static std::mutex mu;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  std::lock_guard<std::mutex> lock(mu);
-  for (int i = 0; i < used; ++i)
-    if (cache[i].k == kernel && cache[i].dev == dev) return cache[i].n;
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1)
-    per_cu = 1;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    cus = 256;
-  const int n = per_cu * cus;
-  if (used < 64) cache[used++] = Entry{kernel, dev, n};
-  return n;
+  int dev = 0, per_cu = 0, cus = 0;
+  bool ok = hipGetDevice(&dev) == hipSuccess;
+  ok = ok && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) == hipSuccess;
+  ok = ok && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
+  if (!ok) (void)hipGetLastError();
+  return std::max(per_cu, 1) * (cus > 0 ? cus : 256);
 }
 
 hipError_t launch_lr_gate_bwd(const GateBwdArgs& a, hipStream_t s) {
