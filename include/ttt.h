@@ -89,6 +89,18 @@ typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype_t;
  * with W_{j*b} the state before mini-batch j, which is what the dual form
  * W_b = W0 - 2 (W0 K - V) diag(eta) K^T, Z = W0 Q - 2 (W0 K - V) diag(eta)
  * triu(K^T Q) computes per mini-batch.
+ *
+ * Sequence chunks.  Each mini-batch maps the state affinely,
+ * W_b = W0 (I - 2 K diag(eta) K^T) + 2 V diag(eta) K^T, so a run of
+ * mini-batches is one affine map W -> W M + C.  With few (batch, head) units
+ * and long sequences (bf16 q/k/v, b = 16, B*H <= 32 and T >= 8192; then
+ * P = 8 or 16 with B*H*P <= 256 and T / P >= 1024, a multiple of 16) the
+ * scan cuts each sequence into P chunks: it forms every chunk's M (from the
+ * identity with v = 0) and C (from zero), chains the maps to get each
+ * chunk's start state, then runs all chunks at once with outputs.  z's
+ * memory holds the intermediate maps and states before the outputs
+ * overwrite them.  Results agree with the single-pass scan to rounding (not
+ * bit for bit); ttt_linear_fwd_chunked (ttt_tuning.h) sets P explicitly.
  */
 ttt_status_t ttt_linear_fwd(const void* q, const void* k, const void* v,
                             const float* eta, const float* w0,

@@ -20,7 +20,8 @@ extern "C" {
 
 /*
  * ttt_linear_fwd with an explicit launch shape: rows_per_workgroup rows of
- * each head's 64-row state per workgroup (16, 32 or 64; 0 = automatic).
+ * each head's 64-row state per workgroup (16, 32 or 64; 0 = automatic), in
+ * one pass over each sequence (no sequence chunks).
  * The rows of W evolve independently (the reconstruction loss is a sum over
  * output components, "论文速览 | TTT" §3.3), so any split gives the same
  * result bit for bit.  Other values: TTT_ERR_UNSUPPORTED.
@@ -32,6 +33,24 @@ ttt_status_t ttt_linear_fwd_tuned(const void* q, const void* k, const void* v,
                                   ttt_dtype_t qkv_dtype, float* z,
                                   float* w_out, void* stream,
                                   int32_t rows_per_workgroup);
+
+/*
+ * ttt_linear_fwd with explicit sequence chunks (see "Sequence chunks" at
+ * ttt_linear_fwd): seq_chunks = 0 picks as ttt_linear_fwd does, 1 runs one
+ * pass, P >= 2 cuts each sequence into P chunks, which needs bf16 q/k/v,
+ * b = 16 and T / P a multiple of 16 and at least 192 (else
+ * TTT_ERR_UNSUPPORTED; negative values too).  rows_per_workgroup as in
+ * ttt_linear_fwd_tuned, for every pass.
+ */
+ttt_status_t ttt_linear_fwd_chunked(const void* q, const void* k,
+                                    const void* v, const float* eta,
+                                    const float* w0, int32_t w0_per_batch,
+                                    int32_t B, int32_t H, int32_t T,
+                                    int32_t d, int32_t b,
+                                    ttt_dtype_t qkv_dtype, float* z,
+                                    float* w_out, void* stream,
+                                    int32_t rows_per_workgroup,
+                                    int32_t seq_chunks);
 
 /*
  * ttt_lr_gate with an explicit launch shape: tokens_per_workgroup tokens per

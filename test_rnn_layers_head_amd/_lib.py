@@ -23,6 +23,8 @@ SIGNATURES = {
                               _vp, _vp, _vp]),
     "ttt_linear_fwd_tuned": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _vp, _vp, _vp, _i32]),
+    "ttt_linear_fwd_chunked": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                      _i32, _vp, _vp, _vp, _i32, _i32]),
     "ttt_linear_ln_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, ctypes.c_float, _i32,
                                  _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "ttt_linear_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,

@@ -47,12 +47,15 @@ def _stream(dev, stream):
 
 
 def ttt_linear_fwd(q, k, v, eta, w0, b: int, z=None, w_out=None, stream=None,
-                   rows_per_workgroup: int = 0):
+                   rows_per_workgroup: int = 0, seq_chunks=None):
     """TTT-Linear forward scan (see include/ttt.h).
 
     q, k, v: [B, H, T, d] bf16 or fp32; eta: [B, H, T] fp32; w0: [H, d, d] or
     [B, H, d, d] fp32.  Outputs z [B, H, T, d] fp32 and w_out [B, H, d, d]
     fp32 are allocated when not given.  Returns (z, w_out).
+    rows_per_workgroup (ttt_linear_fwd_tuned) and seq_chunks
+    (ttt_linear_fwd_chunked) select the launch shape; by default the library
+    picks both.
     """
     B, H, T, d = q.shape
     if z is None:
@@ -76,7 +79,9 @@ def ttt_linear_fwd(q, k, v, eta, w0, b: int, z=None, w_out=None, stream=None,
     with torch.cuda.device(dev):
         args = (_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w0), per_batch, B, H, T, d, int(b),
                 _dtype_code(q), _ptr(z), _ptr(w_out), _stream(dev, stream))
-        if rows_per_workgroup:
+        if seq_chunks is not None:
+            _lib.check(L.ttt_linear_fwd_chunked(*args, int(rows_per_workgroup), int(seq_chunks)))
+        elif rows_per_workgroup:
             _lib.check(L.ttt_linear_fwd_tuned(*args, int(rows_per_workgroup)))
         else:
             _lib.check(L.ttt_linear_fwd(*args))

@@ -101,13 +101,30 @@ int auto_rows(int64_t units) {
   return 16;
 }
 
+// Sequence chunks for the chunked scan.  With few units the chip idles
+// while each unit's serial chain runs; chunking runs three passes over
+// chunks of T / P tokens (two for the maps, one with outputs) at about twice
+// the single pass's time per 16-token tile (256 sequences of 64 rows keep
+// every CU busy), so it pays from P = 8 on: 8 or 16 chunks with
+// units * P <= 256 and chunks of at least 1024 tokens, else one pass.
+int auto_chunks(int64_t units, int T) {
+  int P = 16;
+  while (P >= 8 && (units * P > 256 || T % (16 * P) != 0 || T / P < 1024)) P /= 2;
+  return P >= 8 ? P : 1;
+}
+
+bool chunks_supported(int P, int T, int b, ttt_dtype_t dt) {
+  return P >= 2 && dt == TTT_BF16 && b == 16 && T % P == 0 && (T / P) % 16 == 0 && T / P >= 192;
+}
+
 ttt_status_t linear_impl(const void* q, const void* k, const void* v, const float* eta,
                          const float* w0, int32_t w0_per_batch, int32_t B, int32_t H, int32_t T,
                          int32_t d, int32_t b, ttt_dtype_t dt, float* z, float* w_out,
                          void* stream, int32_t rows, float* w_ckpt = nullptr,
-                         const char* fn = "ttt_linear_fwd", bool dry = false) {
+                         const char* fn = "ttt_linear_fwd", bool dry = false, int32_t chunks = 0) {
   if (rows != 0 && rows != 16 && rows != 32 && rows != 64)
     return fail(TTT_ERR_UNSUPPORTED, "%s: rows_per_workgroup=%d (need 0, 16, 32 or 64)", fn, rows);
+  if (chunks < 0) return fail(TTT_ERR_UNSUPPORTED, "%s: seq_chunks=%d must be >= 0", fn, chunks);
   const int64_t units = (int64_t)B * H;
   const int64_t es = dt == TTT_F32 ? 4 : 2;
   const int64_t seq = units * T * d;
@@ -123,6 +140,13 @@ ttt_status_t linear_impl(const void* q, const void* k, const void* v, const floa
   if (st != TTT_OK || units == 0) return st;
   if (w_ckpt && (dt != TTT_BF16 || b != 16))
     return fail(TTT_ERR_UNSUPPORTED, "%s: checkpoints need bf16 q/k/v and b = 16", fn);
+  // chunks: 0 = automatic, 1 = one pass, P >= 2 = P sequence chunks
+  int P = chunks;
+  if (P == 0) P = (!w_ckpt && dt == TTT_BF16 && b == 16) ? auto_chunks(units, T) : 1;
+  if (P > 1 && (w_ckpt || !chunks_supported(P, T, b, dt)))
+    return fail(TTT_ERR_UNSUPPORTED,
+                "%s: seq_chunks=%d needs bf16 q/k/v, b = 16, and T / seq_chunks a multiple of 16 "
+                "and >= 192 (T=%d)", fn, P, T);
   if (dry) return TTT_OK;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
@@ -131,7 +155,10 @@ ttt_status_t linear_impl(const void* q, const void* k, const void* v, const floa
     e = ttt::launch_copy_state(w0, w0_per_batch, (int)units, H, d * d, w_out, s);
   } else {
     ttt::LinearArgs a{q, k, v, eta, w0, z, w_out, w0_per_batch, (int)units, H, T, b, w_ckpt};
-    e = ttt::launch_linear(a, dt == TTT_F32, rows ? rows : auto_rows(units), s);
+    if (P > 1)
+      e = ttt::launch_linear_chunked(a, P, rows ? rows : auto_rows(units * P), s);
+    else
+      e = ttt::launch_linear(a, dt == TTT_F32, rows ? rows : auto_rows(units), s);
   }
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return TTT_OK;
@@ -490,7 +517,16 @@ ttt_status_t ttt_linear_fwd_tuned(const void* q, const void* k, const void* v, c
                                   float* z, float* w_out, void* stream,
                                   int32_t rows_per_workgroup) {
   return linear_impl(q, k, v, eta, w0, w0_per_batch, B, H, T, d, b, qkv_dtype, z, w_out, stream,
-                     rows_per_workgroup);
+                     rows_per_workgroup, nullptr, "ttt_linear_fwd_tuned", false, 1);
+}
+
+ttt_status_t ttt_linear_fwd_chunked(const void* q, const void* k, const void* v, const float* eta,
+                                    const float* w0, int32_t w0_per_batch, int32_t B, int32_t H,
+                                    int32_t T, int32_t d, int32_t b, ttt_dtype_t qkv_dtype,
+                                    float* z, float* w_out, void* stream,
+                                    int32_t rows_per_workgroup, int32_t seq_chunks) {
+  return linear_impl(q, k, v, eta, w0, w0_per_batch, B, H, T, d, b, qkv_dtype, z, w_out, stream,
+                     rows_per_workgroup, nullptr, "ttt_linear_fwd_chunked", false, seq_chunks);
 }
 
 ttt_status_t ttt_linear_ln_fwd(const void* q, const void* k, const void* v, const float* eta,

@@ -22,7 +22,28 @@ struct LinearArgs {
   // optional: the state at the start of every 16-token mini-batch,
   // [units][ceil(T / 16)][64][64] (b = 16, bf16 inputs only)
   float* w_ckpt = nullptr;
+  // Passes of the chunked scan (bf16, b = 16; defaults: the plain scan).
+  // z == nullptr: no outputs (Q is not read either).
+  int v_zero = 0;   // V read as zeros
+  int w0_mode = 0;  // start state: W0_ARG (w0, w0_per_batch), W0_IDENTITY, W0_ZERO, or W0_IN_Z
+                    // (unit u's own last 64 tokens of z, layout of chunk_state_in_z)
+  int wout_stride = 4096;  // floats between the final states of consecutive units
+  int wout_every = 1;      // only units u with u % wout_every == wout_every - 1 write their
+                           // final state, to w_out + (u / wout_every) * wout_stride
 };
+
+enum { W0_ARG = 0, W0_IDENTITY = 1, W0_ZERO = 2, W0_IN_Z = 3 };
+
+// Where the chunked scan keeps the start state of a sequence chunk: element
+// (row, col) of the 64 x 64 state of unit u, for a pass with `rows` rows of
+// the state per workgroup, lies in u's own z rows [T - 64, T), at the z
+// position that the workgroup owning that row writes itself (and only after
+// it has read the state): token T - 64 + i * (64 / rows) + col / rows,
+// component row0 + col % rows, with row0 = row - row % rows, i = row % rows.
+__host__ __device__ inline int64_t chunk_state_in_z(int T, int rows, int row, int col) {
+  const int row0 = row - row % rows, i = row % rows;
+  return (int64_t)(T - 64 + i * (64 / rows) + col / rows) * 64 + row0 + col % rows;
+}
 
 // TTT-Linear with the LayerNorm + residual inner model: gamma, beta [H][64].
 struct LinearLnArgs {
@@ -119,6 +140,11 @@ struct StepArgs {
 
 // rows: rows of W per workgroup (64, 32 or 16).
 hipError_t launch_linear(const LinearArgs& a, bool f32in, int rows, hipStream_t s);
+// The chunked (sequence-parallel) TTT-Linear scan for bf16 inputs and b = 16:
+// each unit's sequence in P chunks of T / P tokens (T / P a multiple of 16,
+// at least 192), rows of the state per workgroup as in launch_linear.  z's
+// memory holds the intermediate states, so its prior contents do not matter.
+hipError_t launch_linear_chunked(const LinearArgs& a, int P, int rows, hipStream_t s);
 hipError_t launch_linear_bf16(const LinearArgs& a, int rows, hipStream_t s);
 hipError_t launch_linear_ln(const LinearLnArgs& a, hipStream_t s);
 hipError_t launch_mlp(const MlpArgs& a, bool f32in, hipStream_t s);

@@ -123,8 +123,9 @@ linear_scan_bf16_kernel(LinearArgs a) {
     const uint32_t ubytes = (uint32_t)T * 128;
     const size_t uoff = (size_t)unit * T * 64;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc((const short*)a.k + uoff, ubytes);
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const short*)a.q + uoff, ubytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const short*)a.v + uoff, ubytes);
+    // no outputs: Q is not needed; v_zero: V reads as zeros (no memory access)
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const short*)a.q + uoff, a.z ? ubytes : 0u);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const short*)a.v + uoff, a.v_zero ? 0u : ubytes);
     const __amdgpu_buffer_rsrc_t re = make_rsrc(a.eta + (size_t)unit * T, (uint32_t)T * 4);
     const int krow = lane >> 3, kpos = lane & 7;
     auto issue = [&](int j) {
@@ -288,11 +289,25 @@ linear_scan_bf16_kernel(LinearArgs a) {
   // prepared operands of tile j, the raw K/V operands of tile j+1 and the Q
   // operands of tile j (read from LDS during iteration j-1).
   const int rbase = row0 + wave * 16;
-  const float* w0 = a.w0 + (size_t)(a.w0_per_batch ? unit : head) * 4096;
   f32x4 W[4];
+  if (a.w0_mode == W0_IDENTITY || a.w0_mode == W0_ZERO) {
+    const float one = a.w0_mode == W0_IDENTITY ? 1.f : 0.f;
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-    W[m] = *(const f32x4*)(w0 + (rbase + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1));
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        W[m][r] = rbase + c == 32 * (m >> 1) + 8 * g + 4 * (m & 1) + r ? one : 0.f;
+  } else if (a.w0_mode == W0_IN_Z) {
+    const float* zu = a.z + (size_t)unit * T * 64;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      W[m] = *(const f32x4*)(zu + chunk_state_in_z(T, ROWS, rbase + c, 32 * (m >> 1) + 8 * g + 4 * (m & 1)));
+  } else {
+    const float* w0 = a.w0 + (size_t)(a.w0_per_batch ? unit : head) * 4096;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      W[m] = *(const f32x4*)(w0 + (rbase + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1));
+  }
   const int tpm = MODE != MODE_MULTI ? 1 : (TPM > 0 ? TPM : (a.b >> 4));  // tiles per mini-batch
   const NegSel ns = make_negsel(c, g);
   // -I on the 16 V columns of this wave: X = -V_block lands in accumulator
@@ -359,7 +374,8 @@ linear_scan_bf16_kernel(LinearArgs a) {
   // Z through a range-checked buffer: rows past T (padding of the last
   // tile) are dropped by the hardware, so the loop body has no branches and
   // the scheduler can interleave the serial chain with everything else.
-  const __amdgpu_buffer_rsrc_t rz = make_rsrc(a.z + (size_t)unit * T * 64, (uint32_t)T * 256);
+  const __amdgpu_buffer_rsrc_t rz =
+      make_rsrc(a.z ? a.z + (size_t)unit * T * 64 : a.w_out, a.z ? (uint32_t)T * 256 : 0u);
   uint32_t zoff = (uint32_t)((c * 64 + rbase + 4 * g) * 4);  // token c, rows 4g..4g+3
 
   // One tile: uses (pc, rc), fills (pn, rn) for the next one.  The loop
@@ -468,10 +484,12 @@ linear_scan_bf16_kernel(LinearArgs a) {
     if (j < ntiles) tile(j, PN{}, pa, ra, pb, rb);
   }
 
-  float* wo = a.w_out + (size_t)unit * 4096;
+  if (a.wout_every <= 1 || unit % a.wout_every == a.wout_every - 1) {
+    float* wo = a.w_out + (size_t)(unit / (a.wout_every > 1 ? a.wout_every : 1)) * a.wout_stride;
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-    *(f32x4*)(wo + (rbase + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1)) = W[m];
+    for (int m = 0; m < 4; ++m)
+      *(f32x4*)(wo + (rbase + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1)) = W[m];
+  }
 }
 
 template <int MODE, int ROWS, int TPM, bool CKPT = false>
@@ -493,6 +511,96 @@ hipError_t launch_rows(const LinearArgs& a, int rows, hipStream_t s) {
 }
 
 }  // namespace
+
+// Chunked scan, combination step: for every unit, the start state of each
+// chunk, from w0 and the previous chunks' affine maps W_end = W_start M + C
+// (M: the chunk run from the identity with V = 0; C: run from zero), which
+// the first passes left in z (M at the chunk's tokens 0..63, C at 64..127).
+// The start states go to the chunk's last 64 tokens of z (chunk_state_in_z).
+// Rows of the state are independent (row i of W_start M + C needs row i of
+// W_start only), so a workgroup takes 8 rows of one unit; thread t owns row
+// t / 32, columns 2 (t % 32) and 2 (t % 32) + 1.  The next chunk's M and C
+// are loaded while the current step computes.
+constexpr int COMBINE_ROWS = 8;
+__global__ void __launch_bounds__(256) chunk_combine_kernel(const float* w0, int w0_per_batch, int H,
+                                                            float* z, int Tc, int P, int rows) {
+  __shared__ f32x4 Ms[2][64 * 16];        // M of the current and the next chunk
+  __shared__ float Wr[COMBINE_ROWS][64];  // the rows' current start state
+  const int u = blockIdx.x, row0 = blockIdx.y * COMBINE_ROWS, t = threadIdx.x;
+  const int r = t >> 5, col = 2 * (t & 31);
+  const float* w0u = w0 + (size_t)(w0_per_batch ? u : u % H) * 4096;
+  for (int e = t; e < COMBINE_ROWS * 64; e += 256) Wr[e >> 6][e & 63] = w0u[(row0 + (e >> 6)) * 64 + (e & 63)];
+  auto chunk = [&](int p) { return z + ((size_t)u * P + p) * Tc * 64; };
+  // registers: this thread's quarter-rows of the next M (four float4) and its two C values
+  f32x4 mnext[4];
+  float2 cnext = make_float2(0.f, 0.f);
+  auto fetch = [&](int p) {
+    const float* zc = chunk(p);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mnext[q] = *(const f32x4*)(zc + 4 * (t + 256 * q));
+    cnext = *(const float2*)(zc + 4096 + (row0 + r) * 64 + col);
+  };
+  fetch(0);
+  for (int p = 0; p < P; ++p) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Ms[p & 1][t + 256 * q] = mnext[q];
+    const float2 cc = cnext;
+    if (p + 1 < P - 1) fetch(p + 1);
+    __syncthreads();  // Ms[p & 1] and Wr complete
+    float* zc = chunk(p);
+    for (int e = t; e < COMBINE_ROWS * 64; e += 256)
+      zc[chunk_state_in_z(Tc, rows, row0 + (e >> 6), e & 63)] = Wr[e >> 6][e & 63];
+    if (p == P - 1) break;
+    const float* Mf = (const float*)Ms[p & 1];
+    float a0 = cc.x, a1 = cc.y;
+#pragma unroll 16
+    for (int k = 0; k < 64; ++k) {
+      const float w = Wr[r][k];
+      const float2 m = *(const float2*)(Mf + k * 64 + col);
+      a0 = fmaf(w, m.x, a0);
+      a1 = fmaf(w, m.y, a1);
+    }
+    __syncthreads();  // Wr fully read
+    Wr[r][col] = a0;
+    Wr[r][col + 1] = a1;
+  }
+}
+
+hipError_t launch_linear_chunked(const LinearArgs& a, int P, int rows, hipStream_t s) {
+  const int Tc = a.T / P;
+  if (P < 2 || a.T % P != 0 || Tc % 16 != 0 || Tc < 192 || a.b != 16 || a.w_ckpt)
+    return hipErrorInvalidValue;
+  LinearArgs c = a;
+  c.units = a.units * P;  // chunk p of unit u is sequence u * P + p of length Tc
+  c.T = Tc;
+  c.z = nullptr;
+  // M: from the identity with V = 0, into z's tokens 0..63 of each chunk
+  c.v_zero = 1;
+  c.w0_mode = W0_IDENTITY;
+  c.w_out = a.z;
+  c.wout_stride = Tc * 64;
+  c.wout_every = 1;
+  hipError_t e = launch_rows<MODE_B16, 1>(c, rows, s);
+  if (e != hipSuccess) return e;
+  // C: from zero with V, into tokens 64..127
+  c.v_zero = 0;
+  c.w0_mode = W0_ZERO;
+  c.w_out = a.z + 64 * 64;
+  e = launch_rows<MODE_B16, 1>(c, rows, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(chunk_combine_kernel, dim3(a.units, 64 / COMBINE_ROWS), dim3(256), 0, s, a.w0,
+                     a.w0_per_batch, a.H, a.z, Tc, P, rows);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // every chunk from its start state, with outputs; the last chunk's final
+  // state is the unit's
+  c.z = a.z;
+  c.w0_mode = W0_IN_Z;
+  c.w_out = a.w_out;
+  c.wout_stride = 4096;
+  c.wout_every = P;
+  return launch_rows<MODE_B16, 1>(c, rows, s);
+}
 
 hipError_t launch_linear_bf16(const LinearArgs& a, int rows, hipStream_t s) {
   if (a.w_ckpt) return a.b == 16 ? launch_rows<MODE_B16, 1, true>(a, rows, s) : hipErrorInvalidValue;

@@ -76,6 +76,33 @@ def linear(lib, **kw):
                               args["b"], args["dt"], args["z"], args["w"], None)
 
 
+def linear_chunked(lib, rows=0, chunks=2, **kw):
+    args = dict(q=A[0], k=A[1], v=A[2], eta=A[3], w0=A[4], per_batch=0, B=1, H=1, T=1024, d=64,
+                b=16, dt=_lib.TTT_BF16, z=A[5], w=A[6])
+    args.update(kw)
+    return lib.ttt_linear_fwd_chunked(args["q"], args["k"], args["v"], args["eta"], args["w0"],
+                                      args["per_batch"], args["B"], args["H"], args["T"],
+                                      args["d"], args["b"], args["dt"], args["z"], args["w"], None,
+                                      rows, chunks)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(chunks=-1), "TTT_ERR_UNSUPPORTED"),
+    (dict(chunks=3), "TTT_ERR_UNSUPPORTED"),             # 1024 not a multiple of 3
+    (dict(chunks=8), "TTT_ERR_UNSUPPORTED"),             # 128-token chunks (< 192)
+    (dict(chunks=2, T=1000), "TTT_ERR_UNSUPPORTED"),     # 500-token chunks, not 16 | 500
+    (dict(chunks=2, dt=_lib.TTT_F32), "TTT_ERR_UNSUPPORTED"),
+    (dict(chunks=2, b=4), "TTT_ERR_UNSUPPORTED"),
+    (dict(chunks=2, rows=24), "TTT_ERR_UNSUPPORTED"),
+    (dict(chunks=2, z=A[0]), "TTT_ERR_ALIAS"),
+    (dict(chunks=2, B=0), "TTT_OK"),                      # empty work: nothing launched
+])
+def test_linear_chunked_argument_checks(lib, kw, expect):
+    assert linear_chunked(lib, **kw) == status(expect), lib.ttt_last_error()
+    if expect != "TTT_OK":
+        assert lib.ttt_last_error().startswith(b"ttt_linear_fwd_chunked:")
+
+
 def linear_ln(lib, **kw):
     args = dict(q=A[0], k=A[1], v=A[2], eta=A[3], w0=A[4], per_batch=0, gamma=A[7], beta=A[8],
                 eps=1e-5, B=1, H=1, T=16, d=64, b=16, dt=_lib.TTT_BF16, z=A[5], w=A[6])
