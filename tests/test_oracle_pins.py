@@ -613,6 +613,31 @@ def test_linear_homogeneity_and_superposition():
     assert rel(za + zb, z) < 1e-13 and rel(wa + wb, w) < 1e-13
 
 
+def test_chunked_scan_reading_in_fp64():
+    """The chunked scan's decomposition, on the oracle: with b | chunk length,
+    each chunk's end state is W_start M + C with M its run from the identity
+    with v = 0 and C its run from zero; chaining the maps gives every chunk's
+    start state, and running the chunks from those states reproduces the
+    whole sequence's outputs and end state."""
+    rng = np.random.default_rng(35)
+    B, H, T, d, b, P = 1, 2, 96, 5, 4, 3
+    q, k, v, eta, w0 = rand_linear(rng, B, H, T, d)
+    z, w = oracle.linear(q, k, v, eta, w0, b)
+    Tc = T // P
+    sl = lambda a, p: a[:, :, p * Tc:(p + 1) * Tc]
+    eye = np.broadcast_to(np.eye(d), (H, d, d)).copy()
+    W = np.broadcast_to(w0, (B, H, d, d)).copy()
+    zs = []
+    for p in range(P):
+        _, M = oracle.linear(sl(q, p), sl(k, p), 0 * sl(v, p), sl(eta, p), eye, b)
+        _, C = oracle.linear(sl(q, p), sl(k, p), sl(v, p), sl(eta, p), 0 * eye, b)
+        zp, wp = oracle.linear(sl(q, p), sl(k, p), sl(v, p), sl(eta, p), W, b)
+        zs.append(zp)
+        assert rel(W @ M + C, wp) < 1e-12
+        W = wp
+    assert rel(np.concatenate(zs, axis=2), z) < 1e-12 and rel(W, w) < 1e-12
+
+
 def test_linear_row_permutation():
     rng = np.random.default_rng(31)
     q, k, v, eta, w0 = rand_linear(rng, 1, 2, 21, 7)
