@@ -121,3 +121,32 @@ def test_chunked_rejects_unsupported_splits(kw):
     with pytest.raises(TTTError) as e:
         run(x, kw["P"])
     assert e.value.status == 4
+
+
+def test_chunked_graph_replays_match_eager():
+    """The chunked scan's four launches captured in one HIP graph: every
+    replay gives exactly the eager result (z starts NaN-filled each time)."""
+    x = case(1, 2, 2048, seed=416)
+    q, k, v = (gu.dev(x, n) for n in "qkv")
+    eta, w0 = gu.f32(x.eta), gu.f32(x.w0)
+    ze, we = ttt_linear_fwd(q, k, v, eta, w0, 16, seq_chunks=8)
+    torch.cuda.synchronize()
+    z, w = torch.empty_like(ze), torch.empty_like(we)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            ttt_linear_fwd(q, k, v, eta, w0, 16, z=z, w_out=w, seq_chunks=8)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        z.fill_(float("nan"))
+        w.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        scratch = torch.randn(1 << 16, device="cuda").sum()  # unrelated eager work
+        torch.cuda.synchronize()
+        assert torch.equal(z, ze) and torch.equal(w, we), rep
+        assert torch.isfinite(scratch)

@@ -234,3 +234,39 @@ def test_gate_bwd_is_deterministic_and_handles_empty_dims():
     dth, dxg = ttt_lr_gate_bwd(e0, th, 1.0, z, z, dtheta_lr=dth0)
     torch.cuda.synchronize()
     assert torch.all(dth == 0) and dxg.numel() == 0
+
+
+def test_gate_and_backward_graph_replays_match_eager():
+    """The gate and its backward captured in one HIP graph (the backward
+    sizes its grids with host-side occupancy queries, which capture allows):
+    every replay, with unrelated eager work between replays, gives exactly
+    the eager results."""
+    B, T, H, dx = 2, 256, 12, 768
+    raw, x, theta = draw_gate(77, B, T, H, dx)
+    deta = gu.f32(np.random.default_rng(78).standard_normal((B, H, T)).astype(np.float32))
+    xd, td = bf16_dev(raw), gu.f32(theta)
+    eta_e = ttt_lr_gate(xd, td, 0.1)
+    dth_e, dx_e = ttt_lr_gate_bwd(xd, td, 0.1, eta_e, deta)
+    torch.cuda.synchronize()
+    eta = torch.empty_like(eta_e)
+    dth, dxg = torch.empty_like(dth_e), torch.empty_like(dx_e)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            ttt_lr_gate(xd, td, 0.1, eta=eta)
+            ttt_lr_gate_bwd(xd, td, 0.1, eta, deta, dtheta_lr=dth, dx=dxg)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        eta.fill_(float("nan"))
+        dth.fill_(float("nan"))
+        dxg.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        scratch = torch.randn(1 << 16, device="cuda").sum()  # unrelated eager work
+        torch.cuda.synchronize()
+        assert torch.equal(eta, eta_e) and torch.equal(dth, dth_e) and torch.equal(dxg, dx_e), rep
+        assert torch.isfinite(scratch)
