@@ -228,20 +228,50 @@ __global__ void __launch_bounds__(STEP_THREADS) linear_ln_step_kernel(StepArgs a
 // f(x) = W2 GELU(W1 x), hidden width 256 (§4.4).  At the gradient point:
 //   a = W1g k, x = GELU(a), e = 2 (W2g x - v), delta = (W2g^T e) * GELU'(a);
 // W2 -= eta e x^T, W1 -= eta delta k^T; z = W2 GELU(W1 q).
-// Two thread mappings, one workgroup barrier between phases: "hidden"
-// (thread h = hidden unit h: row h of W1, column h of W2) and "output"
-// (thread t = 4i + s: row i of W2, hidden units 64s .. 64s+63).  A reduction
-// over the hidden units thus becomes an in-thread sum plus a quad sum, and
-// one over the outputs an in-thread sum.  Within a call W1/W2 are read
-// before they are written, by the same thread or across a barrier.
+// Every state access is a whole-row access across lanes, so each wave-wide
+// load or store moves 1 KB of consecutive memory: a W1 row (64 values) is
+// spread over a 16-lane group (4 values per lane; wave w, register n, lane l
+// hold row 64 w + 4 n + l / 16), a W2 row (256 values) over a whole wave
+// (wave w, register n hold row 16 w + n, lane l columns 4 l .. 4 l + 3).
+// Row dot products are in-lane sums plus a 16-lane DPP rotation sum (and,
+// for W2 rows, the four 16-lane sums read out of lanes 0, 16, 32, 48); the
+// sum over W2's rows for delta is in-lane over a wave's 16 rows plus one
+// LDS exchange between the four waves.  Every state element is read before
+// it is written, by the same lane.
 // GELU(x) = x Phi(x) with erf from Abramowitz & Stegun 7.1.26 (|err| <=
 // 1.5e-7), the same function as the MLP scan's (gelu_and_grad).
 constexpr int MLP_HID = 256;
 
+// sum over each group of 16 consecutive lanes, in every lane of the group
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF,
+                                                          0xF, false));  // row_ror:8
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x124, 0xF,
+                                                          0xF, false));  // row_ror:4
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x122, 0xF,
+                                                          0xF, false));  // row_ror:2
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x121, 0xF,
+                                                          0xF, false));  // row_ror:1
+  return x;
+}
+// sum over the whole wave, the same value in every lane
+__device__ __forceinline__ float wave_total(float x) {
+  const int s = __builtin_bit_cast(int, row16_sum(x));
+  return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(s, 0)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(s, 16))) +
+         (__builtin_bit_cast(float, __builtin_amdgcn_readlane(s, 32)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(s, 48)));
+}
+__device__ __forceinline__ float dot4(float4 a, float4 b) {
+  return fmaf(a.w, b.w, fmaf(a.z, b.z, fmaf(a.y, b.y, a.x * b.x)));
+}
+
 template <bool F32IN>
 __global__ void __launch_bounds__(STEP_THREADS) mlp_step_kernel(StepArgs a) {
-  __shared__ float sk[64], sq[64], sx[MLP_HID], se[64], sh[MLP_HID];
+  __shared__ float4 sk[16], sq[16], sx[MLP_HID / 4], shq[MLP_HID / 4];
+  __shared__ float sg[MLP_HID], sd[MLP_HID], pd[4][MLP_HID];
   const int unit = blockIdx.x, t = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63;
   const int bi = unit / a.H;
   const size_t vo = (size_t)unit * 64;
   const size_t so = (size_t)unit * (MLP_HID * 64);
@@ -249,110 +279,111 @@ __global__ void __launch_bounds__(STEP_THREADS) mlp_step_kernel(StepArgs a) {
   const bool copy_gp = start && a.w_gp != nullptr;  // gradient points may be NULL for b == 1
   const float eta = a.eta[unit];
   if (t < 64) {
-    sk[t] = load1<F32IN>(a.k, vo + t);
-    sq[t] = load1<F32IN>(a.q, vo + t);
+    ((float*)sk)[t] = load1<F32IN>(a.k, vo + t);
+    ((float*)sq)[t] = load1<F32IN>(a.q, vo + t);
   }
   __syncthreads();
 
-  // ---- phase 1 (hidden mapping): a_h = W1g[h] . k
-  const int h = t;
+  // ---- phase 1: a_h = W1g[h] . k for this lane group's 16 rows
+  const int c1 = l & 15;                       // W1: columns 4 c1 .. 4 c1 + 3
+  const int h0 = 64 * w + (l >> 4);            // W1: rows h0 + 4 n
+  const float4 k4 = sk[c1], q4 = sq[c1];
   float4 w1[16];
   {
-    const float4* src = (const float4*)(a.w + so + (size_t)h * 64);
-    const float4* gsrc = start ? src : (const float4*)(a.w_gp + so + (size_t)h * 64);
-    float4* gdst = copy_gp ? (float4*)(a.w_gp + so + (size_t)h * 64) : nullptr;
+    const float4* g1 = (const float4*)((start ? a.w : a.w_gp) + so) + c1;
 #pragma unroll
-    for (int n = 0; n < 16; ++n) w1[n] = src[n];
-    float ak = 0.f;
+    for (int n = 0; n < 16; ++n) w1[n] = g1[(h0 + 4 * n) * 16];
+    if (copy_gp) {
+      float4* d1 = (float4*)(a.w_gp + so) + c1;
+#pragma unroll
+      for (int n = 0; n < 16; ++n) d1[(h0 + 4 * n) * 16] = w1[n];
+    }
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
-      const float4 g = start ? w1[n] : gsrc[n];
-      if (copy_gp) gdst[n] = g;
-      ak = fmaf(g.x, sk[4 * n], ak);
-      ak = fmaf(g.y, sk[4 * n + 1], ak);
-      ak = fmaf(g.z, sk[4 * n + 2], ak);
-      ak = fmaf(g.w, sk[4 * n + 3], ak);
+      const float ah = row16_sum(dot4(w1[n], k4));
+      const GeluOut ga = gelu_and_grad(ah);
+      if (c1 == 0) {
+        ((float*)sx)[h0 + 4 * n] = ga.g;
+        sg[h0 + 4 * n] = ga.dg;  // GELU'(a_h)
+      }
     }
-    const GeluOut ga = gelu_and_grad(ak);
-    sx[h] = ga.g;
-    sh[h] = ga.dg;  // GELU'(a_h), read back by the same thread in phase 3
   }
   __syncthreads();
 
-  // ---- phase 2 (output mapping): y_i = W2g[i] . x, e_i = 2 (y_i - v_i)
-  const int i = t >> 2, s = t & 3;
-  const size_t r2 = so + (size_t)i * MLP_HID + 64 * s;  // W2[i][64s ..]
+  // ---- phase 2: y_i = W2g[i] . x, e_i = 2 (y_i - v_i) for this wave's 16 rows,
+  // then this wave's share of W2g^T e
+  const int i0 = 16 * w;
+  float4 w2[16];
+  float ev[16];
   {
-    const float4* src = (const float4*)((start ? a.w2 : a.w2_gp) + r2);
-    float4* gdst = copy_gp ? (float4*)(a.w2_gp + r2) : nullptr;
-    float y = 0.f;
+    const float4* g2 = (const float4*)((start ? a.w2 : a.w2_gp) + so) + l;
+#pragma unroll
+    for (int n = 0; n < 16; ++n) w2[n] = g2[(i0 + n) * 64];
+    if (copy_gp) {
+      float4* d2 = (float4*)(a.w2_gp + so) + l;
+#pragma unroll
+      for (int n = 0; n < 16; ++n) d2[(i0 + n) * 64] = w2[n];
+    }
+    const float4 x4 = sx[l];
+    float4 part = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
-      const float4 g = src[n];
-      if (copy_gp) gdst[n] = g;
-      const int u = 64 * s + 4 * n;
-      y = fmaf(g.x, sx[u], y);
-      y = fmaf(g.y, sx[u + 1], y);
-      y = fmaf(g.z, sx[u + 2], y);
-      y = fmaf(g.w, sx[u + 3], y);
+      const float y = wave_total(dot4(w2[n], x4));
+      ev[n] = 2.f * (y - load1<F32IN>(a.v, vo + i0 + n));
+      part.x = fmaf(w2[n].x, ev[n], part.x);
+      part.y = fmaf(w2[n].y, ev[n], part.y);
+      part.z = fmaf(w2[n].z, ev[n], part.z);
+      part.w = fmaf(w2[n].w, ev[n], part.w);
     }
-    y = quad_sum(y);
-    if (s == 0) se[i] = 2.f * (y - load1<F32IN>(a.v, vo + i));
+    *(float4*)&pd[w][4 * l] = part;
+  }
+  __syncthreads();
+  // delta_h = (W2g^T e)_h GELU'(a_h), thread t -> h = t
+  sd[t] = ((pd[0][t] + pd[1][t]) + (pd[2][t] + pd[3][t])) * sg[t];
+  __syncthreads();
+
+  // ---- phase 3: W1[h] -= eta delta_h k; hq_h = GELU(W1[h] . q)
+  {
+    float4* r1 = (float4*)(a.w + so) + c1;
+    if (!start) {
+#pragma unroll
+      for (int n = 0; n < 16; ++n) w1[n] = r1[(h0 + 4 * n) * 16];
+    }
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+      const float nd = -eta * sd[h0 + 4 * n];
+      float4 v = w1[n];
+      v.x = fmaf(nd, k4.x, v.x);
+      v.y = fmaf(nd, k4.y, v.y);
+      v.z = fmaf(nd, k4.z, v.z);
+      v.w = fmaf(nd, k4.w, v.w);
+      r1[(h0 + 4 * n) * 16] = v;
+      const float aq = row16_sum(dot4(v, q4));
+      if (c1 == 0) ((float*)shq)[h0 + 4 * n] = gelu_and_grad(aq).g;
+    }
   }
   __syncthreads();
 
-  // ---- phase 3 (hidden mapping): delta_h = (W2g[:, h] . e) GELU'(a_h);
-  // W1[h] -= eta delta_h k; hq_h = GELU(W1[h] . q)
+  // ---- phase 4: W2[i] -= eta e_i x; z_i = W2[i] . hq
   {
-    const float* col = (start ? a.w2 : a.w2_gp) + so + h;
-    float bp = 0.f;
-#pragma unroll 8
-    for (int r = 0; r < 64; ++r) bp = fmaf(col[(size_t)r * MLP_HID], se[r], bp);
-    const float nd = -eta * bp * sh[h];
-    float aq = 0.f;
+    float4* r2 = (float4*)(a.w2 + so) + l;
+    if (!start) {
+#pragma unroll
+      for (int n = 0; n < 16; ++n) w2[n] = r2[(i0 + n) * 64];
+    }
+    const float4 x4 = sx[l], hq4 = shq[l];
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
-      float4 w = w1[n];
-      w.x = fmaf(nd, sk[4 * n], w.x);
-      w.y = fmaf(nd, sk[4 * n + 1], w.y);
-      w.z = fmaf(nd, sk[4 * n + 2], w.z);
-      w.w = fmaf(nd, sk[4 * n + 3], w.w);
-      w1[n] = w;
-      aq = fmaf(w.x, sq[4 * n], aq);
-      aq = fmaf(w.y, sq[4 * n + 1], aq);
-      aq = fmaf(w.z, sq[4 * n + 2], aq);
-      aq = fmaf(w.w, sq[4 * n + 3], aq);
+      const float ne = -eta * ev[n];
+      float4 v = w2[n];
+      v.x = fmaf(ne, x4.x, v.x);
+      v.y = fmaf(ne, x4.y, v.y);
+      v.z = fmaf(ne, x4.z, v.z);
+      v.w = fmaf(ne, x4.w, v.w);
+      r2[(i0 + n) * 64] = v;
+      const float z = wave_total(dot4(v, hq4));
+      if (l == 0) a.z[vo + i0 + n] = z;
     }
-    float4* dst = (float4*)(a.w + so + (size_t)h * 64);
-#pragma unroll
-    for (int n = 0; n < 16; ++n) dst[n] = w1[n];
-    const float hq = gelu_and_grad(aq).g;
-    __syncthreads();  // every thread has read its GELU'(a_h) from sh
-    sh[h] = hq;
-  }
-  __syncthreads();
-
-  // ---- phase 4 (output mapping): W2[i] -= eta e_i x; z_i = W2[i] . hq
-  {
-    float4* row = (float4*)(a.w2 + r2);
-    const float ne = -eta * se[i];
-    float z = 0.f;
-#pragma unroll
-    for (int n = 0; n < 16; ++n) {
-      float4 w = row[n];
-      const int u = 64 * s + 4 * n;
-      w.x = fmaf(ne, sx[u], w.x);
-      w.y = fmaf(ne, sx[u + 1], w.y);
-      w.z = fmaf(ne, sx[u + 2], w.z);
-      w.w = fmaf(ne, sx[u + 3], w.w);
-      row[n] = w;
-      z = fmaf(w.x, sh[u], z);
-      z = fmaf(w.y, sh[u + 1], z);
-      z = fmaf(w.z, sh[u + 2], z);
-      z = fmaf(w.w, sh[u + 3], z);
-    }
-    z = quad_sum(z);
-    if (s == 0) a.z[vo + i] = z;
   }
 }
 
