@@ -14,10 +14,9 @@
 // write W (and Wg when a mini-batch starts).  No MFMA: a single token gives
 // no contraction worth a matrix tile.  fp32 throughout.
 //
-// Layout of a linear step: one workgroup of 256 threads per unit; thread
-// t = 4i + s owns row i of W, columns 16s .. 16s+15 (64 contiguous bytes, so
-// a wave moves 4 KB of W per access, coalesced); the four threads of a row
-// are adjacent lanes, so row sums are two quad-permute adds.
+// One workgroup of 256 threads per unit.  Every step lays each state row
+// across consecutive lanes (16 B per lane), so a wave-wide load or store
+// moves 1 KB of consecutive memory; row sums are 16-lane DPP rotation sums.
 #include "ttt_device.h"
 #include "ttt_launch.h"
 
@@ -25,222 +24,6 @@ namespace ttt {
 namespace {
 
 constexpr int STEP_THREADS = 256;
-
-// sum over the 4 adjacent lanes of a quad (row i of W), in every lane
-__device__ __forceinline__ float quad_sum(float x) {
-  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF,
-                                                          0xF, false));  // [1,0,3,2]
-  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF,
-                                                          0xF, false));  // [2,3,0,1]
-  return x;
-}
-
-// 16 consecutive values of a q/k/v row as fp32
-template <bool F32IN>
-__device__ __forceinline__ void load16(const void* base, size_t off, float* out) {
-  if constexpr (F32IN) {
-    const float4* p = (const float4*)((const float*)base + off);
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const float4 x = p[n];
-      out[4 * n] = x.x;
-      out[4 * n + 1] = x.y;
-      out[4 * n + 2] = x.z;
-      out[4 * n + 3] = x.w;
-    }
-  } else {
-    const uint4* p = (const uint4*)((const uint16_t*)base + off);
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const uint4 x = p[n];
-      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        out[8 * n + 2 * e] = __builtin_bit_cast(float, w[e] << 16);
-        out[8 * n + 2 * e + 1] = __builtin_bit_cast(float, w[e] & 0xffff0000u);
-      }
-    }
-  }
-}
-template <bool F32IN>
-__device__ __forceinline__ float load1(const void* base, size_t off) {
-  if constexpr (F32IN) return ((const float*)base)[off];
-  return __builtin_bit_cast(float, ((uint32_t)((const uint16_t*)base)[off]) << 16);
-}
-
-__device__ __forceinline__ int minibatch_pos(int pos, int b) {
-  const int p = pos % b;
-  return p < 0 ? p + b : p;
-}
-
-// ------------------------------------------------------------ TTT-Linear
-// f(x) = W x, l = ||W k - v||^2:  g = 2 (Wg k - v),  W -= eta g k^T,  z = W q.
-template <bool F32IN>
-__global__ void __launch_bounds__(STEP_THREADS) linear_step_kernel(StepArgs a) {
-  const int unit = blockIdx.x;
-  const int t = threadIdx.x, i = t >> 2, s = t & 3;
-  const int bi = unit / a.H;
-  const size_t vo = (size_t)unit * 64;            // this unit's token vectors
-  const size_t wo = (size_t)unit * 4096 + i * 64 + 16 * s;
-  const bool start = minibatch_pos(a.pos[bi], a.b) == 0;
-
-  float kk[16], qq[16], W[16], G[16];
-  load16<F32IN>(a.k, vo + 16 * s, kk);
-  load16<F32IN>(a.q, vo + 16 * s, qq);
-  const float vi = load1<F32IN>(a.v, vo + i);
-  const float eta = a.eta[unit];
-  const float4* wp = (const float4*)(a.w + wo);
-#pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const float4 x = wp[n];
-    W[4 * n] = x.x; W[4 * n + 1] = x.y; W[4 * n + 2] = x.z; W[4 * n + 3] = x.w;
-  }
-  if (start || a.w_gp == nullptr) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) G[e] = W[e];
-  } else {
-    const float4* gp = (const float4*)(a.w_gp + wo);
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const float4 x = gp[n];
-      G[4 * n] = x.x; G[4 * n + 1] = x.y; G[4 * n + 2] = x.z; G[4 * n + 3] = x.w;
-    }
-  }
-  if (start && a.w_gp != nullptr) {  // the gradient point of the new mini-batch
-    float4* gp = (float4*)(a.w_gp + wo);
-#pragma unroll
-    for (int n = 0; n < 4; ++n) gp[n] = make_float4(W[4 * n], W[4 * n + 1], W[4 * n + 2], W[4 * n + 3]);
-  }
-  float y = 0.f;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) y = fmaf(G[e], kk[e], y);
-  y = quad_sum(y);
-  const float ng = -2.f * eta * (y - vi);  // -eta g_i
-  float zq = 0.f;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    W[e] = fmaf(ng, kk[e], W[e]);
-    zq = fmaf(W[e], qq[e], zq);
-  }
-  zq = quad_sum(zq);
-  float4* w_out = (float4*)(a.w + wo);
-#pragma unroll
-  for (int n = 0; n < 4; ++n) w_out[n] = make_float4(W[4 * n], W[4 * n + 1], W[4 * n + 2], W[4 * n + 3]);
-  if (s == 0) a.z[vo + i] = zq;
-}
-
-// ------------------------------------- TTT-Linear with LayerNorm + residual
-// f(x) = x + LN(W x): the LN statistics are sums over the 64 rows, i.e. over
-// the whole workgroup (4 waves x 16 rows): a wave sum of the quad leaders
-// (DPP) and an LDS exchange of the 4 wave partials.
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-  return x;
-}
-// sums over the 64 rows of two per-row values held by the quad leaders;
-// every call site passes its own 4-entry LDS buffer, so one barrier suffices
-__device__ __forceinline__ float2 rows_sum2(float x, float y, float2* red, int s) {
-  x = s == 0 ? x : 0.f;
-  y = s == 0 ? y : 0.f;
-  x = wave_sum(x);
-  y = wave_sum(y);
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = make_float2(x, y);
-  __syncthreads();
-  const float2 r0 = red[0], r1 = red[1], r2 = red[2], r3 = red[3];
-  return make_float2((r0.x + r1.x) + (r2.x + r3.x), (r0.y + r1.y) + (r2.y + r3.y));
-}
-
-template <bool F32IN>
-__global__ void __launch_bounds__(STEP_THREADS) linear_ln_step_kernel(StepArgs a, const float* gamma,
-                                                                      const float* beta, float eps) {
-  __shared__ float2 red[3][4];
-  const int unit = blockIdx.x;
-  const int t = threadIdx.x, i = t >> 2, s = t & 3;
-  const int bi = unit / a.H, head = unit % a.H;
-  const size_t vo = (size_t)unit * 64;
-  const size_t wo = (size_t)unit * 4096 + i * 64 + 16 * s;
-  const bool start = minibatch_pos(a.pos[bi], a.b) == 0;
-  const float gi = gamma[head * 64 + i], be = beta[head * 64 + i];
-
-  float kk[16], qq[16], W[16], G[16];
-  load16<F32IN>(a.k, vo + 16 * s, kk);
-  load16<F32IN>(a.q, vo + 16 * s, qq);
-  const float vi = load1<F32IN>(a.v, vo + i), ki = load1<F32IN>(a.k, vo + i),
-              qi = load1<F32IN>(a.q, vo + i);
-  const float eta = a.eta[unit];
-  const float4* wp = (const float4*)(a.w + wo);
-#pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const float4 x = wp[n];
-    W[4 * n] = x.x; W[4 * n + 1] = x.y; W[4 * n + 2] = x.z; W[4 * n + 3] = x.w;
-  }
-  if (start || a.w_gp == nullptr) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) G[e] = W[e];
-  } else {
-    const float4* gp = (const float4*)(a.w_gp + wo);
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const float4 x = gp[n];
-      G[4 * n] = x.x; G[4 * n + 1] = x.y; G[4 * n + 2] = x.z; G[4 * n + 3] = x.w;
-    }
-  }
-  if (start && a.w_gp != nullptr) {
-    float4* gp = (float4*)(a.w_gp + wo);
-#pragma unroll
-    for (int n = 0; n < 4; ++n) gp[n] = make_float4(W[4 * n], W[4 * n + 1], W[4 * n + 2], W[4 * n + 3]);
-  }
-  // forward on the training view at the gradient point: y = Wg k, mean and
-  // population variance over the 64 rows (one pass: E[y^2] - mu^2, >= 0)
-  float y = 0.f;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) y = fmaf(G[e], kk[e], y);
-  y = quad_sum(y);
-  const float2 sy = rows_sum2(y, y * y, red[0], s);
-  const float mu = sy.x * (1.f / 64);
-  const float rs = rsqrtf(fmaxf(fmaf(sy.y, 1.f / 64, -mu * mu), 0.f) + eps);
-  const float yh = (y - mu) * rs;
-  // dl/dyhat = 2 gamma (k + gamma yhat + beta - v); LayerNorm VJP
-  const float gy = 2.f * gi * ((ki + fmaf(gi, yh, be)) - vi);
-  const float2 m = rows_sum2(gy, gy * yh, red[1], s);
-  const float gr = rs * (gy - m.x * (1.f / 64) - yh * (m.y * (1.f / 64)));
-  const float ng = -eta * gr;
-  float o = 0.f;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    W[e] = fmaf(ng, kk[e], W[e]);
-    o = fmaf(W[e], qq[e], o);
-  }
-  o = quad_sum(o);
-  float4* w_out = (float4*)(a.w + wo);
-#pragma unroll
-  for (int n = 0; n < 4; ++n) w_out[n] = make_float4(W[4 * n], W[4 * n + 1], W[4 * n + 2], W[4 * n + 3]);
-  // z = q + LN(W q)
-  const float2 so = rows_sum2(o, o * o, red[2], s);
-  const float mo = so.x * (1.f / 64);
-  const float ro = rsqrtf(fmaxf(fmaf(so.y, 1.f / 64, -mo * mo), 0.f) + eps);
-  if (s == 0) a.z[vo + i] = qi + fmaf(gi, (o - mo) * ro, be);
-}
-
-// ------------------------------------------------------------------ TTT-MLP
-// f(x) = W2 GELU(W1 x), hidden width 256 (§4.4).  At the gradient point:
-//   a = W1g k, x = GELU(a), e = 2 (W2g x - v), delta = (W2g^T e) * GELU'(a);
-// W2 -= eta e x^T, W1 -= eta delta k^T; z = W2 GELU(W1 q).
-// Every state access is a whole-row access across lanes, so each wave-wide
-// load or store moves 1 KB of consecutive memory: a W1 row (64 values) is
-// spread over a 16-lane group (4 values per lane; wave w, register n, lane l
-// hold row 64 w + 4 n + l / 16), a W2 row (256 values) over a whole wave
-// (wave w, register n hold row 16 w + n, lane l columns 4 l .. 4 l + 3).
-// Row dot products are in-lane sums plus a 16-lane DPP rotation sum (and,
-// for W2 rows, the four 16-lane sums read out of lanes 0, 16, 32, 48); the
-// sum over W2's rows for delta is in-lane over a wave's 16 rows plus one
-// LDS exchange between the four waves.  Every state element is read before
-// it is written, by the same lane.
-// GELU(x) = x Phi(x) with erf from Abramowitz & Stegun 7.1.26 (|err| <=
-// 1.5e-7), the same function as the MLP scan's (gelu_and_grad).
-constexpr int MLP_HID = 256;
 
 // sum over each group of 16 consecutive lanes, in every lane of the group
 __device__ __forceinline__ float row16_sum(float x) {
@@ -265,6 +48,204 @@ __device__ __forceinline__ float wave_total(float x) {
 __device__ __forceinline__ float dot4(float4 a, float4 b) {
   return fmaf(a.w, b.w, fmaf(a.z, b.z, fmaf(a.y, b.y, a.x * b.x)));
 }
+
+template <bool F32IN>
+__device__ __forceinline__ float load1(const void* base, size_t off) {
+  if constexpr (F32IN) return ((const float*)base)[off];
+  return __builtin_bit_cast(float, ((uint32_t)((const uint16_t*)base)[off]) << 16);
+}
+
+__device__ __forceinline__ int minibatch_pos(int pos, int b) {
+  const int p = pos % b;
+  return p < 0 ? p + b : p;
+}
+
+// ------------------------------------------------------------ TTT-Linear
+// f(x) = W x, l = ||W k - v||^2:  g = 2 (Wg k - v),  W -= eta g k^T,  z = W q.
+// A row of W (64 values, 256 bytes) spans a group of 16 lanes, 4 values per
+// lane: wave w, register n, lane l hold row 16 w + 4 n + l / 16, columns
+// 4 (l % 16) .. + 3, so every wave-wide state load or store moves 1 KB of
+// consecutive memory.  Row dot products are in-lane sums plus a 16-lane DPP
+// rotation sum; rows are independent, so no lane exchanges data beyond its
+// group.  Each state element is read before it is written, by the same lane.
+template <bool F32IN>
+__global__ void __launch_bounds__(STEP_THREADS) linear_step_kernel(StepArgs a) {
+  const int unit = blockIdx.x;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, c1 = l & 15;
+  const int r0 = 16 * w + (l >> 4);                 // rows r0 + 4 n
+  const int bi = unit / a.H;
+  const size_t vo = (size_t)unit * 64;              // this unit's token vectors
+  const size_t so = (size_t)unit * 4096;
+  const bool start = minibatch_pos(a.pos[bi], a.b) == 0;
+  const float4 k4 = make_float4(load1<F32IN>(a.k, vo + 4 * c1), load1<F32IN>(a.k, vo + 4 * c1 + 1),
+                                load1<F32IN>(a.k, vo + 4 * c1 + 2), load1<F32IN>(a.k, vo + 4 * c1 + 3));
+  const float4 q4 = make_float4(load1<F32IN>(a.q, vo + 4 * c1), load1<F32IN>(a.q, vo + 4 * c1 + 1),
+                                load1<F32IN>(a.q, vo + 4 * c1 + 2), load1<F32IN>(a.q, vo + 4 * c1 + 3));
+  const float eta = a.eta[unit];
+  float4* wr = (float4*)(a.w + so) + c1;
+  float4 W[4], G[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) W[n] = wr[(r0 + 4 * n) * 16];
+  if (start || a.w_gp == nullptr) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) G[n] = W[n];
+  } else {
+    const float4* gr = (const float4*)(a.w_gp + so) + c1;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) G[n] = gr[(r0 + 4 * n) * 16];
+  }
+  if (start && a.w_gp != nullptr) {  // the gradient point of the new mini-batch
+    float4* gr = (float4*)(a.w_gp + so) + c1;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) gr[(r0 + 4 * n) * 16] = W[n];
+  }
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int i = r0 + 4 * n;
+    const float y = row16_sum(dot4(G[n], k4));
+    const float ng = -2.f * eta * (y - load1<F32IN>(a.v, vo + i));  // -eta g_i
+    float4 v = W[n];
+    v.x = fmaf(ng, k4.x, v.x);
+    v.y = fmaf(ng, k4.y, v.y);
+    v.z = fmaf(ng, k4.z, v.z);
+    v.w = fmaf(ng, k4.w, v.w);
+    wr[i * 16] = v;
+    const float zq = row16_sum(dot4(v, q4));
+    if (c1 == 0) a.z[vo + i] = zq;
+  }
+}
+
+// ------------------------------------- TTT-Linear with LayerNorm + residual
+// f(x) = x + LN(W x), rows laid out as in the TTT-Linear step (16 lanes per
+// row, lane group l / 16 of wave w holding rows 16 w + l / 16 + 4 n).  The
+// LN statistics are sums over the 64 rows: a lane group sums its 4 rows in
+// registers, the wave reads its four groups' sums out of lanes 0, 16, 32,
+// 48, and the 4 wave partials meet in LDS.
+// Sums over the 64 rows of two values already summed over this lane group's
+// rows; every call site passes its own 4-entry LDS buffer, so one barrier
+// suffices.
+__device__ __forceinline__ float2 rows_total2(float x, float y, float2* red, int w, int l) {
+  const int xi = __builtin_bit_cast(int, x), yi = __builtin_bit_cast(int, y);
+  auto groups = [](int v) {
+    return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(v, 0)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(v, 16))) +
+           (__builtin_bit_cast(float, __builtin_amdgcn_readlane(v, 32)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(v, 48)));
+  };
+  const float xw = groups(xi), yw = groups(yi);
+  if (l == 0) red[w] = make_float2(xw, yw);
+  __syncthreads();
+  const float2 r0 = red[0], r1 = red[1], r2 = red[2], r3 = red[3];
+  return make_float2((r0.x + r1.x) + (r2.x + r3.x), (r0.y + r1.y) + (r2.y + r3.y));
+}
+
+template <bool F32IN>
+__global__ void __launch_bounds__(STEP_THREADS) linear_ln_step_kernel(StepArgs a, const float* gamma,
+                                                                      const float* beta, float eps) {
+  __shared__ float2 red[3][4];
+  const int unit = blockIdx.x;
+  const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), l = t & 63, c1 = l & 15;
+  const int r0 = 16 * w + (l >> 4);                 // rows r0 + 4 n
+  const int bi = unit / a.H, head = unit % a.H;
+  const size_t vo = (size_t)unit * 64;
+  const size_t so = (size_t)unit * 4096;
+  const bool start = minibatch_pos(a.pos[bi], a.b) == 0;
+  const float4 k4 = make_float4(load1<F32IN>(a.k, vo + 4 * c1), load1<F32IN>(a.k, vo + 4 * c1 + 1),
+                                load1<F32IN>(a.k, vo + 4 * c1 + 2), load1<F32IN>(a.k, vo + 4 * c1 + 3));
+  const float4 q4 = make_float4(load1<F32IN>(a.q, vo + 4 * c1), load1<F32IN>(a.q, vo + 4 * c1 + 1),
+                                load1<F32IN>(a.q, vo + 4 * c1 + 2), load1<F32IN>(a.q, vo + 4 * c1 + 3));
+  const float eta = a.eta[unit];
+  float gi[4], be[4], ki[4], qi[4], vi[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int i = r0 + 4 * n;
+    gi[n] = gamma[head * 64 + i];
+    be[n] = beta[head * 64 + i];
+    ki[n] = load1<F32IN>(a.k, vo + i);
+    qi[n] = load1<F32IN>(a.q, vo + i);
+    vi[n] = load1<F32IN>(a.v, vo + i);
+  }
+  float4* wr = (float4*)(a.w + so) + c1;
+  float4 W[4], G[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) W[n] = wr[(r0 + 4 * n) * 16];
+  if (start || a.w_gp == nullptr) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) G[n] = W[n];
+  } else {
+    const float4* gr = (const float4*)(a.w_gp + so) + c1;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) G[n] = gr[(r0 + 4 * n) * 16];
+  }
+  if (start && a.w_gp != nullptr) {
+    float4* gr = (float4*)(a.w_gp + so) + c1;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) gr[(r0 + 4 * n) * 16] = W[n];
+  }
+  // forward on the training view at the gradient point: y = Wg k, mean and
+  // population variance over the 64 rows (one pass: E[y^2] - mu^2, >= 0)
+  float y[4], sy1 = 0.f, sy2 = 0.f;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    y[n] = row16_sum(dot4(G[n], k4));
+    sy1 += y[n];
+    sy2 = fmaf(y[n], y[n], sy2);
+  }
+  const float2 sy = rows_total2(sy1, sy2, red[0], w, l);
+  const float mu = sy.x * (1.f / 64);
+  const float rs = rsqrtf(fmaxf(fmaf(sy.y, 1.f / 64, -mu * mu), 0.f) + eps);
+  // dl/dyhat = 2 gamma (k + gamma yhat + beta - v); LayerNorm VJP
+  float yh[4], gy[4], sg1 = 0.f, sg2 = 0.f;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    yh[n] = (y[n] - mu) * rs;
+    gy[n] = 2.f * gi[n] * ((ki[n] + fmaf(gi[n], yh[n], be[n])) - vi[n]);
+    sg1 += gy[n];
+    sg2 = fmaf(gy[n], yh[n], sg2);
+  }
+  const float2 m = rows_total2(sg1, sg2, red[1], w, l);
+  float o[4], so1 = 0.f, so2 = 0.f;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const float gr = rs * (gy[n] - m.x * (1.f / 64) - yh[n] * (m.y * (1.f / 64)));
+    const float ng = -eta * gr;
+    float4 v = W[n];
+    v.x = fmaf(ng, k4.x, v.x);
+    v.y = fmaf(ng, k4.y, v.y);
+    v.z = fmaf(ng, k4.z, v.z);
+    v.w = fmaf(ng, k4.w, v.w);
+    wr[(r0 + 4 * n) * 16] = v;
+    o[n] = row16_sum(dot4(v, q4));
+    so1 += o[n];
+    so2 = fmaf(o[n], o[n], so2);
+  }
+  // z = q + LN(W q)
+  const float2 sz = rows_total2(so1, so2, red[2], w, l);
+  const float mo = sz.x * (1.f / 64);
+  const float ro = rsqrtf(fmaxf(fmaf(sz.y, 1.f / 64, -mo * mo), 0.f) + eps);
+  if (c1 == 0) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) a.z[vo + r0 + 4 * n] = qi[n] + fmaf(gi[n], (o[n] - mo) * ro, be[n]);
+  }
+}
+
+// ------------------------------------------------------------------ TTT-MLP
+// f(x) = W2 GELU(W1 x), hidden width 256 (§4.4).  At the gradient point:
+//   a = W1g k, x = GELU(a), e = 2 (W2g x - v), delta = (W2g^T e) * GELU'(a);
+// W2 -= eta e x^T, W1 -= eta delta k^T; z = W2 GELU(W1 q).
+// Every state access is a whole-row access across lanes, so each wave-wide
+// load or store moves 1 KB of consecutive memory: a W1 row (64 values) is
+// spread over a 16-lane group (4 values per lane; wave w, register n, lane l
+// hold row 64 w + 4 n + l / 16), a W2 row (256 values) over a whole wave
+// (wave w, register n hold row 16 w + n, lane l columns 4 l .. 4 l + 3).
+// Row dot products are in-lane sums plus a 16-lane DPP rotation sum (and,
+// for W2 rows, the four 16-lane sums read out of lanes 0, 16, 32, 48); the
+// sum over W2's rows for delta is in-lane over a wave's 16 rows plus one
+// LDS exchange between the four waves.  Every state element is read before
+// it is written, by the same lane.
+// GELU(x) = x Phi(x) with erf from Abramowitz & Stegun 7.1.26 (|err| <=
+// 1.5e-7), the same function as the MLP scan's (gelu_and_grad).
+constexpr int MLP_HID = 256;
 
 template <bool F32IN>
 __global__ void __launch_bounds__(STEP_THREADS) mlp_step_kernel(StepArgs a) {
