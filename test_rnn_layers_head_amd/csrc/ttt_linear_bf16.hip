@@ -89,7 +89,9 @@ __global__ void __launch_bounds__((Geom<ROWS>::THREADS))
 linear_scan_bf16_kernel(LinearArgs a) {
   using G = Geom<ROWS>;
   constexpr int NSPLIT = 64 / ROWS;
-  __shared__ __attribute__((aligned(16))) char smem[G::LDS];
+  // with checkpoints: per compute wave a 16-row staging tile (rows padded by 4 words)
+  constexpr int CK_TILE = CKPT ? 16 * 68 * 4 : 0;
+  __shared__ __attribute__((aligned(16))) char smem[G::LDS + G::NCW * CK_TILE];
   char* const raw = smem;
   char* const prep = smem + G::NST * G::RAW;
 
@@ -394,10 +396,23 @@ linear_scan_bf16_kernel(LinearArgs a) {
     load_raw(rn, raw + ((j + 2) % G::NST) * G::RAW, raw + ((j + 1) % G::NST) * G::RAW);
     __builtin_amdgcn_sched_barrier(0);  // the reads go out first
     if constexpr (CKPT) {  // W_j, the state before tile j
-      float* ck = a.w_ckpt + ((size_t)unit * ntiles + j) * 4096;
+      // through this wave's LDS tile, so that each store writes 4 whole rows
+      // (1 KB of consecutive memory), nontemporally
+      char* const ct = smem + G::LDS + wave * CK_TILE;
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        *(f32x4*)(ck + (rbase + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1)) = W[m];
+        *(f32x4*)(ct + (c * 68 + 32 * (m >> 1) + 8 * g + 4 * (m & 1)) * 4) = W[m];
+      const __amdgpu_buffer_rsrc_t rc =
+          make_rsrc(a.w_ckpt + ((size_t)unit * ntiles + j) * 4096 + __builtin_amdgcn_readfirstlane(rbase) * 64,
+                    16u * 64u * 4u);  // (rbase pinned to a scalar register: a uniform descriptor)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int row = (lane >> 4) + 4 * kk, col = 4 * (lane & 15);
+        const f32x4 v = *(const f32x4*)(ct + (row * 68 + col) * 4);
+        typedef unsigned int u32x4c __attribute__((ext_vector_type(4)));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4c, v), rc,
+                                               (uint32_t)((row * 64 + col) * 4), 0, 2);
+      }
     }
     constexpr int pos = decltype(POS)::value;
     const bool new_mb = MODE != MODE_MULTI || (pos >= 0 ? pos == 0 : (j % tpm) == 0);
