@@ -259,7 +259,16 @@ __global__ void __launch_bounds__(256) lr_gate_bwd_dtheta_kernel(GateBwdArgs a, 
   for (int p = 0; p < 2; ++p)
 #pragma unroll
     for (int e = 0; e < 8; ++e) sel[p][e] = (bf16)((g == 2 * p + (c >> 3) && e == (c & 7)) ? 1.f : 0.f);
-  const uint32_t xoff = (uint32_t)((c * a.dx + col0 + 8 * g) * 2);
+  // x rows are loaded whole (CPR 16-byte chunks per row, 64 / CPR rows per
+  // load, so each load moves 1 KB of rows of 32 NM bytes) and rearranged into
+  // the matrix unit's layout (lane (c, g): token c, chunk 4h + g) through a
+  // per-wave LDS tile that shares the reduction buffer (used only after the
+  // loop, each wave in its own part)
+  constexpr int CPR = 2 * NM, RPI = 64 / CPR, PITCH = 16 * CPR + 16;
+  const int lrow = lane / CPR, lchunk = lane % CPR;
+  const uint32_t xoff = (uint32_t)((lrow * a.dx + col0) * 2 + 16 * lchunk);
+  char* const xt_lds = (char*)&red[wave][0][0][0];
+  static_assert(16 * PITCH <= (int)sizeof(red[0]), "staging tile fits the wave's reduction slot");
   const uint32_t ebytes = (uint32_t)(ntok * a.H) * 4u;
   const __amdgpu_buffer_rsrc_t re = make_rsrc(a.eta, ebytes), rd = make_rsrc(a.deta, ebytes);
 
@@ -281,16 +290,24 @@ __global__ void __launch_bounds__(256) lr_gate_bwd_dtheta_kernel(GateBwdArgs a, 
           make_rsrc((const uint16_t*)a.x + (int64_t)frow * a.dx, (uint32_t)(rows * a.dx * 2));
 #pragma unroll
       for (int h = 0; h < (NM + 1) / 2; ++h)
-        st.xr[h] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff + 64 * h, 0, 0));
+        st.xr[h] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+            rx, xoff + (uint32_t)(RPI * h * a.dx * 2), 0, 0));  // rows lrow + RPI h
       load_da_quad<HB, VEC>(a, re, rd, min(f0, ntok - 1), hp, c, g, st.da);
     };
     auto compute = [&](int j, const DthStage<NM, HB>& st) {
       const int f0 = f_begin + 16 * (wave + 4 * j);
       // tokens in registers: xt[m] register r = x[f0 + 4g + r][col0 + 16 m + c]
+      // whole rows -> LDS tile -> lane (c, g) gets token c, columns 32 h + 8 g .. + 7
+#pragma unroll
+      for (int h = 0; h < (NM + 1) / 2; ++h)
+        *(bf16x8*)(xt_lds + (lrow + RPI * h) * PITCH + 16 * lchunk) = st.xr[h];
+      bf16x8 xa[(NM + 1) / 2];
+#pragma unroll
+      for (int h = 0; h < (NM + 1) / 2; ++h) xa[h] = *(const bf16x8*)(xt_lds + c * PITCH + 16 * (4 * h + g));
       uint2 xt[NM];
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        const f32x4 v = mfma_k32(st.xr[m >> 1], sel[m & 1], f32x4{0, 0, 0, 0});
+        const f32x4 v = mfma_k32(xa[m >> 1], sel[m & 1], f32x4{0, 0, 0, 0});
         xt[m] = make_uint2(pack_rne(v[0], v[1]), pack_rne(v[2], v[3]));
       }
 #pragma unroll
