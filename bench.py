@@ -626,7 +626,7 @@ def main():
         return 0
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the scan shards over (batch, head) units with no communication, see DESIGN.md)",
+              "(the scan shards over (batch, head) units with no communication)",
               file=sys.stderr)
         return 2
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
