@@ -625,7 +625,7 @@ def main():
         summarize_trace(d, k, int(skip), int(take))
         return 0
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the scan runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the scan shards over (batch, head) units with no communication)",
               file=sys.stderr)
         return 2
