@@ -53,6 +53,17 @@ ttt_status_t ttt_linear_fwd_chunked(const void* q, const void* k,
                                     int32_t seq_chunks);
 
 /*
+ * The launch plan ttt_linear_fwd picks for these sizes: rows of the state
+ * per workgroup and the number of sequence chunks (1 = one pass).  Host-only;
+ * nothing is launched.  NULL outputs: TTT_ERR_NULL; negative sizes or b < 1:
+ * TTT_ERR_SHAPE; unknown dtype: TTT_ERR_DTYPE.
+ */
+ttt_status_t ttt_linear_fwd_plan(int32_t B, int32_t H, int32_t T, int32_t b,
+                                 ttt_dtype_t qkv_dtype,
+                                 int32_t* rows_per_workgroup,
+                                 int32_t* seq_chunks);
+
+/*
  * ttt_lr_gate with an explicit launch shape: tokens_per_workgroup tokens per
  * workgroup (32 or 64; 0 = automatic).  Each token's sums are the same for
  * every value.  Other values: TTT_ERR_UNSUPPORTED.

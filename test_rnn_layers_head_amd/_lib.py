@@ -25,6 +25,7 @@ SIGNATURES = {
                                     _i32, _vp, _vp, _vp, _i32]),
     "ttt_linear_fwd_chunked": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                       _i32, _vp, _vp, _vp, _i32, _i32]),
+    "ttt_linear_fwd_plan": (_i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp]),
     "ttt_linear_ln_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, ctypes.c_float, _i32,
                                  _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "ttt_linear_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,

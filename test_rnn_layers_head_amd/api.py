@@ -46,6 +46,17 @@ def _stream(dev, stream):
     return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
 
 
+def ttt_linear_fwd_plan(B: int, H: int, T: int, b: int, dtype=torch.bfloat16):
+    """(rows_per_workgroup, seq_chunks) that ttt_linear_fwd picks for these
+    sizes (ttt_tuning.h); host-only."""
+    import ctypes
+    rows, chunks = ctypes.c_int32(0), ctypes.c_int32(0)
+    code = _lib.TTT_BF16 if dtype == torch.bfloat16 else _lib.TTT_F32
+    _lib.check(_lib.lib().ttt_linear_fwd_plan(int(B), int(H), int(T), int(b), code,
+                                               ctypes.addressof(rows), ctypes.addressof(chunks)))
+    return rows.value, chunks.value
+
+
 def ttt_linear_fwd(q, k, v, eta, w0, b: int, z=None, w_out=None, stream=None,
                    rows_per_workgroup: int = 0, seq_chunks=None):
     """TTT-Linear forward scan (see include/ttt.h).

@@ -113,6 +113,11 @@ int auto_chunks(int64_t units, int T) {
   return P >= 8 ? P : 1;
 }
 
+// The chunk count ttt_linear_fwd picks when the caller leaves it open.
+int default_chunks(ttt_dtype_t dt, int b, int64_t units, int T) {
+  return (dt == TTT_BF16 && b == 16) ? auto_chunks(units, T) : 1;
+}
+
 bool chunks_supported(int P, int T, int b, ttt_dtype_t dt) {
   return P >= 2 && dt == TTT_BF16 && b == 16 && T % P == 0 && (T / P) % 16 == 0 && T / P >= 192;
 }
@@ -142,7 +147,7 @@ ttt_status_t linear_impl(const void* q, const void* k, const void* v, const floa
     return fail(TTT_ERR_UNSUPPORTED, "%s: checkpoints need bf16 q/k/v and b = 16", fn);
   // chunks: 0 = automatic, 1 = one pass, P >= 2 = P sequence chunks
   int P = chunks;
-  if (P == 0) P = (!w_ckpt && dt == TTT_BF16 && b == 16) ? auto_chunks(units, T) : 1;
+  if (P == 0) P = w_ckpt ? 1 : default_chunks(dt, b, units, T);
   if (P > 1 && (w_ckpt || !chunks_supported(P, T, b, dt)))
     return fail(TTT_ERR_UNSUPPORTED,
                 "%s: seq_chunks=%d needs bf16 q/k/v, b = 16, and T / seq_chunks a multiple of 16 "
@@ -518,6 +523,21 @@ ttt_status_t ttt_linear_fwd_tuned(const void* q, const void* k, const void* v, c
                                   int32_t rows_per_workgroup) {
   return linear_impl(q, k, v, eta, w0, w0_per_batch, B, H, T, d, b, qkv_dtype, z, w_out, stream,
                      rows_per_workgroup, nullptr, "ttt_linear_fwd_tuned", false, 1);
+}
+
+ttt_status_t ttt_linear_fwd_plan(int32_t B, int32_t H, int32_t T, int32_t b, ttt_dtype_t qkv_dtype,
+                                 int32_t* rows_per_workgroup, int32_t* seq_chunks) {
+  static const char* fn = "ttt_linear_fwd_plan";
+  if (!rows_per_workgroup || !seq_chunks) return fail(TTT_ERR_NULL, "%s: output pointer is NULL", fn);
+  if (qkv_dtype != TTT_F32 && qkv_dtype != TTT_BF16)
+    return fail(TTT_ERR_DTYPE, "%s: unknown qkv_dtype %d", fn, (int)qkv_dtype);
+  if (B < 0 || H < 0 || T < 0 || b < 1)
+    return fail(TTT_ERR_SHAPE, "%s: negative size or b < 1 (B=%d H=%d T=%d b=%d)", fn, B, H, T, b);
+  const int64_t units = (int64_t)B * H;
+  const int P = default_chunks(qkv_dtype, b, units, T);
+  *seq_chunks = P;
+  *rows_per_workgroup = auto_rows(units * P);
+  return TTT_OK;
 }
 
 ttt_status_t ttt_linear_fwd_chunked(const void* q, const void* k, const void* v, const float* eta,

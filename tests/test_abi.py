@@ -103,6 +103,33 @@ def test_linear_chunked_argument_checks(lib, kw, expect):
         assert lib.ttt_last_error().startswith(b"ttt_linear_fwd_chunked:")
 
 
+@pytest.mark.parametrize("B,H,T,b,dt,want", [
+    (4, 32, 8192, 16, _lib.TTT_BF16, (32, 1)),      # the 1.3B workload: one pass
+    (1, 32, 32768, 16, _lib.TTT_BF16, (64, 8)),     # long context: 8 chunks of 4096
+    (1, 2, 8192, 16, _lib.TTT_BF16, (16, 8)),       # chunks of at least 1024 tokens
+    (1, 32, 32768, 4, _lib.TTT_BF16, (16, 1)),      # chunking needs b = 16
+    (1, 32, 32768, 16, _lib.TTT_F32, (16, 1)),      # and bf16 inputs
+    (16, 16, 8192, 16, _lib.TTT_BF16, (64, 1)),     # 256 units
+])
+def test_linear_fwd_plan(lib, B, H, T, b, dt, want):
+    import ctypes
+    rows, chunks = ctypes.c_int32(-1), ctypes.c_int32(-1)
+    assert lib.ttt_linear_fwd_plan(B, H, T, b, dt, ctypes.addressof(rows),
+                                   ctypes.addressof(chunks)) == 0
+    assert (rows.value, chunks.value) == want
+
+
+def test_linear_fwd_plan_errors(lib):
+    import ctypes
+    r, c = ctypes.c_int32(0), ctypes.c_int32(0)
+    ra, ca = ctypes.addressof(r), ctypes.addressof(c)
+    assert lib.ttt_linear_fwd_plan(1, 1, 16, 16, _lib.TTT_BF16, None, ca) == status("TTT_ERR_NULL")
+    assert lib.ttt_linear_fwd_plan(-1, 1, 16, 16, _lib.TTT_BF16, ra, ca) == status("TTT_ERR_SHAPE")
+    assert lib.ttt_linear_fwd_plan(1, 1, 16, 0, _lib.TTT_BF16, ra, ca) == status("TTT_ERR_SHAPE")
+    assert lib.ttt_linear_fwd_plan(1, 1, 16, 16, 7, ra, ca) == status("TTT_ERR_DTYPE")
+    assert lib.ttt_last_error().startswith(b"ttt_linear_fwd_plan:")
+
+
 def linear_ln(lib, **kw):
     args = dict(q=A[0], k=A[1], v=A[2], eta=A[3], w0=A[4], per_batch=0, gamma=A[7], beta=A[8],
                 eps=1e-5, B=1, H=1, T=16, d=64, b=16, dt=_lib.TTT_BF16, z=A[5], w=A[6])

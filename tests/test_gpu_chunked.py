@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import gpu_util as gu
-from test_rnn_layers_head_amd import TTTError, inputs, ttt_linear_fwd
+from test_rnn_layers_head_amd import TTTError, inputs, ttt_linear_fwd, ttt_linear_fwd_plan
 
 pytestmark = pytest.mark.gpu
 
@@ -77,6 +77,8 @@ def test_chunked_in_place_resume():
 def test_automatic_choice_chunks_few_long_sequences():
     """ttt_linear_fwd cuts 2 units of 8192 tokens into 8 chunks, and runs one
     pass for 128 units of 2048 tokens and for 32 units of 4096."""
+    assert ttt_linear_fwd_plan(1, 2, 8192, 16) == (16, 8)
+    assert ttt_linear_fwd_plan(8, 16, 2048, 16)[1] == 1 and ttt_linear_fwd_plan(2, 16, 4096, 16)[1] == 1
     x = case(1, 2, 8192, seed=413)
     q, k, v = (gu.dev(x, n) for n in "qkv")
     z, w = ttt_linear_fwd(q, k, v, gu.f32(x.eta), gu.f32(x.w0), 16)
