@@ -149,6 +149,8 @@ ttt_status_t ttt_linear_ln_fwd(const void* q, const void* k, const void* v,
  * ttt_linear_fwd_ckpt: ttt_linear_fwd plus
  *   w_ckpt : out [B][H][ceil(T/16)][d][d] fp32, the state before each
  *            mini-batch (w_ckpt[..][0] = W0).
+ * It takes sequence chunks as ttt_linear_fwd does; the last pass writes the
+ * checkpoints.
  *
  * ttt_linear_bwd: the gradient of a loss L(Z, W_T) with respect to the
  * scan's inputs, given
@@ -161,6 +163,18 @@ ttt_status_t ttt_linear_ln_fwd(const void* q, const void* k, const void* v,
  * Outputs must not overlap each other or an input.  T = 0 writes
  * dw0 = dw_T (or zeros).  One workgroup per (batch, head); the adjoint state
  * stays on chip, nothing beyond the outputs is written.
+ *
+ * Sequence chunks (when ttt_linear_fwd would chunk the same sizes).  The
+ * adjoint of the state also walks affinely, Wb = Wb' (I - 2 K diag(eta) K^T)
+ * + (terms without Wb'), with the forward's symmetric factor: over a chunk
+ * whose forward map is W -> W M + C the end adjoint E maps to E M^T + C',
+ * C' being the chunk's backward from a zero end adjoint.  The backward then
+ * forms every chunk's M and C', chains them from dw_T to get each chunk's
+ * end adjoint (and dw0), and runs all chunks at once with outputs.  dq's
+ * memory holds the intermediate 64 x 64 matrices (its first 192 tokens of
+ * each chunk) before the outputs overwrite them.  Results agree with the
+ * single pass to rounding; ttt_linear_bwd_chunked (ttt_tuning.h) sets the
+ * chunk count explicitly.
  */
 ttt_status_t ttt_linear_fwd_ckpt(const void* q, const void* k, const void* v,
                                  const float* eta, const float* w0,

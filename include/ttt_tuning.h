@@ -53,8 +53,26 @@ ttt_status_t ttt_linear_fwd_chunked(const void* q, const void* k,
                                     int32_t seq_chunks);
 
 /*
+ * ttt_linear_bwd with an explicit sequence-chunk count (see "Sequence
+ * chunks" at ttt_linear_bwd): seq_chunks = 0 picks as ttt_linear_bwd does
+ * (the count ttt_linear_fwd_plan reports), 1 runs one pass, P >= 2 cuts each
+ * sequence into P chunks, which needs T / P a multiple of 16 and at least
+ * 192 (else TTT_ERR_UNSUPPORTED; negative values too).  Arguments, results
+ * and errors otherwise as ttt_linear_bwd.
+ */
+ttt_status_t ttt_linear_bwd_chunked(const void* q, const void* k,
+                                    const void* v, const float* eta,
+                                    const float* w_ckpt, int32_t B, int32_t H,
+                                    int32_t T, int32_t d, int32_t b,
+                                    ttt_dtype_t qkv_dtype, const float* dz,
+                                    const float* dw_T, float* dq, float* dk,
+                                    float* dv, float* deta, float* dw0,
+                                    void* stream, int32_t seq_chunks);
+
+/*
  * The launch plan ttt_linear_fwd picks for these sizes: rows of the state
- * per workgroup and the number of sequence chunks (1 = one pass).  Host-only;
+ * per workgroup and the number of sequence chunks (1 = one pass; the
+ * checkpointing forward and the backward chunk alike).  Host-only;
  * nothing is launched.  NULL outputs: TTT_ERR_NULL; negative sizes or b < 1:
  * TTT_ERR_SHAPE; unknown dtype: TTT_ERR_DTYPE.
  */

@@ -36,6 +36,8 @@ SIGNATURES = {
                                    _vp, _vp, _vp, _vp]),
     "ttt_linear_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                               _vp, _vp, _vp, _vp, _vp, _vp]),
+    "ttt_linear_bwd_chunked": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32]),
     "ttt_lr_gate": (_i32, [_vp, _i32, _vp, ctypes.c_float, _i32, _i32, _i32, _i32, _vp, _vp]),
     "ttt_lr_gate_bwd": (_i32, [_vp, _i32, _vp, ctypes.c_float, _vp, _vp, _i32, _i32, _i32, _i32,
                                _vp, _vp, _vp]),

@@ -162,10 +162,12 @@ def ttt_linear_fwd_ckpt(q, k, v, eta, w0, b: int, z=None, w_out=None, w_ckpt=Non
     return z, w_out, w_ckpt
 
 
-def ttt_linear_bwd(q, k, v, eta, w_ckpt, b: int, dz, dw_T=None, stream=None):
+def ttt_linear_bwd(q, k, v, eta, w_ckpt, b: int, dz, dw_T=None, stream=None, seq_chunks=None):
     """Backward of the TTT-Linear scan (include/ttt.h): given dz = dL/dZ and
     optionally dw_T = dL/dW_T, returns (dq, dk, dv, deta, dw0), fp32, with
-    dw0 per unit [B, H, d, d].  w_ckpt comes from ttt_linear_fwd_ckpt."""
+    dw0 per unit [B, H, d, d].  w_ckpt comes from ttt_linear_fwd_ckpt.
+    seq_chunks: None or 0 = automatic, 1 = one pass, P >= 2 = P sequence
+    chunks (ttt_linear_bwd_chunked, ttt_tuning.h)."""
     B, H, T, d = q.shape
     f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=q.device)
     dq, dk, dv, deta, dw0 = f32(B, H, T, d), f32(B, H, T, d), f32(B, H, T, d), f32(B, H, T), \
@@ -178,11 +180,13 @@ def ttt_linear_bwd(q, k, v, eta, w_ckpt, b: int, dz, dw_T=None, stream=None):
         raise ValueError("dz must be [B, H, T, d]")
     if tuple(w_ckpt.shape) != (B, H, (T + 15) // 16, d, d):
         raise ValueError("w_ckpt must be [B, H, ceil(T/16), d, d]")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w_ckpt), B, H, T, d, int(b), _dtype_code(q),
+            _ptr(dz), _ptr(dw_T), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(deta), _ptr(dw0))
     with torch.cuda.device(dev):
-        _lib.check(_lib.lib().ttt_linear_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w_ckpt),
-                                             B, H, T, d, int(b), _dtype_code(q), _ptr(dz),
-                                             _ptr(dw_T), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(deta),
-                                             _ptr(dw0), _stream(dev, stream)))
+        if seq_chunks is None:
+            _lib.check(_lib.lib().ttt_linear_bwd(*args, _stream(dev, stream)))
+        else:
+            _lib.check(_lib.lib().ttt_linear_bwd_chunked(*args, _stream(dev, stream), int(seq_chunks)))
     return dq, dk, dv, deta, dw0
 
 

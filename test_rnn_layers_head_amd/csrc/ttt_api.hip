@@ -147,8 +147,8 @@ ttt_status_t linear_impl(const void* q, const void* k, const void* v, const floa
     return fail(TTT_ERR_UNSUPPORTED, "%s: checkpoints need bf16 q/k/v and b = 16", fn);
   // chunks: 0 = automatic, 1 = one pass, P >= 2 = P sequence chunks
   int P = chunks;
-  if (P == 0) P = w_ckpt ? 1 : default_chunks(dt, b, units, T);
-  if (P > 1 && (w_ckpt || !chunks_supported(P, T, b, dt)))
+  if (P == 0) P = default_chunks(dt, b, units, T);
+  if (P > 1 && !chunks_supported(P, T, b, dt))
     return fail(TTT_ERR_UNSUPPORTED,
                 "%s: seq_chunks=%d needs bf16 q/k/v, b = 16, and T / seq_chunks a multiple of 16 "
                 "and >= 192 (T=%d)", fn, P, T);
@@ -318,8 +318,7 @@ ttt_status_t linear_bwd_impl(const void* q, const void* k, const void* v, const 
                             const float* w_ckpt, int32_t B, int32_t H, int32_t T, int32_t d,
                             int32_t b, ttt_dtype_t dt, const float* dz, const float* dw_T,
                             float* dq, float* dk, float* dv, float* deta, float* dw0,
-                            void* stream) {
-  static const char* fn = "ttt_linear_bwd";
+                            void* stream, int32_t chunks = 0, const char* fn = "ttt_linear_bwd") {
   const int64_t units = (int64_t)B * H;
   const int64_t seq = units * T * d;
   const int64_t nck = units * ((T + 15) / 16) * d * d * 4;
@@ -336,6 +335,11 @@ ttt_status_t linear_bwd_impl(const void* q, const void* k, const void* v, const 
   if (dt != TTT_BF16) return fail(TTT_ERR_UNSUPPORTED, "%s: only bf16 q/k/v are supported", fn);
   if (seq >= ((int64_t)1 << 31))
     return fail(TTT_ERR_SHAPE, "%s: B*H*T*d = %lld exceeds 2^31 - 1", fn, (long long)seq);
+  if (chunks < 0) return fail(TTT_ERR_UNSUPPORTED, "%s: seq_chunks=%d must be >= 0", fn, chunks);
+  const int P = chunks ? chunks : default_chunks(dt, b, units, T);
+  if (P > 1 && !chunks_supported(P, T, b, dt))
+    return fail(TTT_ERR_UNSUPPORTED,
+                "%s: seq_chunks=%d needs T / seq_chunks a multiple of 16 and >= 192 (T=%d)", fn, P, T);
   if (units == 0) return TTT_OK;
   for (int i = 0; i < 7; ++i) {
     const bool seqt = i < 6;  // empty when T == 0
@@ -356,7 +360,8 @@ ttt_status_t linear_bwd_impl(const void* q, const void* k, const void* v, const 
         return fail(TTT_ERR_ALIAS, "%s: %s and %s overlap", fn, out[o].name, out[o2].name);
   }
   ttt::LinearBwdArgs a{q, k, v, eta, w_ckpt, dz, dw_T, dq, dk, dv, deta, dw0, (int)units, H, T};
-  hipError_t e = ttt::launch_linear_bwd(a, (hipStream_t)stream);
+  hipError_t e = P > 1 ? ttt::launch_linear_bwd_chunked(a, P, auto_rows(units * P), (hipStream_t)stream)
+                       : ttt::launch_linear_bwd(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return TTT_OK;
 }
@@ -482,6 +487,15 @@ ttt_status_t ttt_linear_bwd(const void* q, const void* k, const void* v, const f
                             void* stream) {
   return linear_bwd_impl(q, k, v, eta, w_ckpt, B, H, T, d, b, qkv_dtype, dz, dw_T, dq, dk, dv,
                          deta, dw0, stream);
+}
+
+ttt_status_t ttt_linear_bwd_chunked(const void* q, const void* k, const void* v, const float* eta,
+                                    const float* w_ckpt, int32_t B, int32_t H, int32_t T, int32_t d,
+                                    int32_t b, ttt_dtype_t qkv_dtype, const float* dz,
+                                    const float* dw_T, float* dq, float* dk, float* dv, float* deta,
+                                    float* dw0, void* stream, int32_t seq_chunks) {
+  return linear_bwd_impl(q, k, v, eta, w_ckpt, B, H, T, d, b, qkv_dtype, dz, dw_T, dq, dk, dv,
+                         deta, dw0, stream, seq_chunks, "ttt_linear_bwd_chunked");
 }
 
 ttt_status_t ttt_mlp_step(const void* q, const void* k, const void* v, const float* eta,

@@ -83,12 +83,23 @@ struct LinearBwdArgs {
   float* dk;
   float* dv;
   float* deta;           // [units][T]
-  float* dw0;            // [units][64][64]
+  float* dw0;            // [units][64][64], or NULL: not written
   int units;
   int H;
   int T;
+  // Passes of the chunked backward (defaults: the plain backward).
+  int dw_stride = 4096;   // floats between the dw_T of consecutive units
+  int dw0_stride = 4096;  // floats between the dw0 of consecutive units
+  int tok_out = 1;        // 0: dq, dk, dv, deta are not written
 };
 hipError_t launch_linear_bwd(const LinearBwdArgs& a, hipStream_t s);
+// The backward in P sequence chunks of T / P tokens (a multiple of 16, at
+// least 192): the chunks' forward maps, their backward from a zero end
+// adjoint, a serial combine over the chunks, then every chunk from its end
+// adjoint.  The first passes keep their 64 x 64 results in dq's memory of
+// their chunk (tokens 0..191) before the last pass writes dq.  rows: rows of
+// the state per workgroup of the forward-map pass.
+hipError_t launch_linear_bwd_chunked(const LinearBwdArgs& a, int P, int rows, hipStream_t s);
 
 // Learning-rate gate: eta[b][h][t] = eta_base * sigmoid(theta[h] . x[b][t]).
 struct GateArgs {

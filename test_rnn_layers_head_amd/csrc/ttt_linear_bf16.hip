@@ -583,12 +583,12 @@ __global__ void __launch_bounds__(256) chunk_combine_kernel(const float* w0, int
 
 hipError_t launch_linear_chunked(const LinearArgs& a, int P, int rows, hipStream_t s) {
   const int Tc = a.T / P;
-  if (P < 2 || a.T % P != 0 || Tc % 16 != 0 || Tc < 192 || a.b != 16 || a.w_ckpt)
-    return hipErrorInvalidValue;
+  if (P < 2 || a.T % P != 0 || Tc % 16 != 0 || Tc < 192 || a.b != 16) return hipErrorInvalidValue;
   LinearArgs c = a;
   c.units = a.units * P;  // chunk p of unit u is sequence u * P + p of length Tc
   c.T = Tc;
   c.z = nullptr;
+  c.w_ckpt = nullptr;
   // M: from the identity with V = 0, into z's tokens 0..63 of each chunk
   c.v_zero = 1;
   c.w0_mode = W0_IDENTITY;
@@ -607,13 +607,18 @@ hipError_t launch_linear_chunked(const LinearArgs& a, int P, int rows, hipStream
                      a.w0_per_batch, a.H, a.z, Tc, P, rows);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // every chunk from its start state, with outputs; the last chunk's final
-  // state is the unit's
+  // every chunk from its start state, with outputs (and the checkpoints,
+  // which are laid out per 16-token tile, so chunk u * P + p's are unit u's
+  // tiles of that chunk); the last chunk's final state is the unit's
   c.z = a.z;
   c.w0_mode = W0_IN_Z;
   c.w_out = a.w_out;
   c.wout_stride = 4096;
   c.wout_every = P;
+  if (a.w_ckpt) {
+    c.w_ckpt = a.w_ckpt;
+    return launch_rows<MODE_B16, 1, true>(c, rows, s);
+  }
   return launch_rows<MODE_B16, 1>(c, rows, s);
 }
 

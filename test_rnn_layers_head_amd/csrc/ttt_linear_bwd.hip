@@ -106,11 +106,11 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
   const size_t uoff = (size_t)unit * T * 64;
   if (ntiles == 0) {  // no tokens: dW0 = dW_T (or 0); w_ckpt may be NULL
     if (wave < 4) {
-      const float* dwT = a.dw_T ? a.dw_T + (size_t)unit * 4096 + (16 * wave + c) * 64 : nullptr;
-      float* o = a.dw0 + (size_t)unit * 4096 + (16 * wave + c) * 64;
+      const float* dwT = a.dw_T ? a.dw_T + (size_t)unit * a.dw_stride + (16 * wave + c) * 64 : nullptr;
+      float* o = a.dw0 ? a.dw0 + (size_t)unit * a.dw0_stride + (16 * wave + c) * 64 : nullptr;
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        *(f32x4*)(o + 16 * m + 4 * g) = dwT ? *(const f32x4*)(dwT + 16 * m + 4 * g) : f32x4{0, 0, 0, 0};
+        if (o) *(f32x4*)(o + 16 * m + 4 * g) = dwT ? *(const f32x4*)(dwT + 16 * m + 4 * g) : f32x4{0, 0, 0, 0};
     }
     return;
   }
@@ -129,17 +129,19 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
       sel[p][e] = (bf16)((g == (c >> 2) && e == 4 * p + (c & 3)) ? 1.f : 0.f);
 
   if (wave < 4) {  // ====================================================== chain
-    const __amdgpu_buffer_rsrc_t rdq = make_rsrc(a.dq + uoff, (uint32_t)T * 256);
-    const __amdgpu_buffer_rsrc_t rdk = make_rsrc(a.dk + uoff, (uint32_t)T * 256);
-    const __amdgpu_buffer_rsrc_t rdv = make_rsrc(a.dv + uoff, (uint32_t)T * 256);
-    const __amdgpu_buffer_rsrc_t rde = make_rsrc(a.deta + (size_t)unit * T, (uint32_t)T * 4);
+    // (with tok_out == 0 the descriptors hold no records: the stores are dropped)
+    const uint32_t ot = a.tok_out ? (uint32_t)T : 0u;
+    const __amdgpu_buffer_rsrc_t rdq = make_rsrc(a.dq + uoff, ot * 256);
+    const __amdgpu_buffer_rsrc_t rdk = make_rsrc(a.dk + uoff, ot * 256);
+    const __amdgpu_buffer_rsrc_t rdv = make_rsrc(a.dv + uoff, ot * 256);
+    const __amdgpu_buffer_rsrc_t rde = make_rsrc(a.deta + (size_t)unit * T, ot * 4);
     auto st32 = [](float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
     };
     // Wr[m] register r = Wb[row 16 s + c][scol(m, 4g + r)]
     f32x4 Wr[4];
     {
-      const float* dwT = a.dw_T ? a.dw_T + (size_t)unit * 4096 + (16 * s + c) * 64 : nullptr;
+      const float* dwT = a.dw_T ? a.dw_T + (size_t)unit * a.dw_stride + (16 * s + c) * 64 : nullptr;
 #pragma unroll
       for (int m = 0; m < 4; ++m)
         Wr[m] = dwT ? *(const f32x4*)(dwT + scol(m, 4 * g)) : f32x4{0, 0, 0, 0};
@@ -281,9 +283,11 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
       if (k + 1 < niter) body(k + 1, zB, zA);
       if (k + 2 < niter) body(k + 2, zC, zB);
     }
-    float* o = a.dw0 + (size_t)unit * 4096 + (16 * s + c) * 64;
+    if (a.dw0) {
+      float* o = a.dw0 + (size_t)unit * a.dw0_stride + (16 * s + c) * 64;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) *(f32x4*)(o + scol(m, 4 * g)) = Wr[m];
+      for (int m = 0; m < 4; ++m) *(f32x4*)(o + scol(m, 4 * g)) = Wr[m];
+    }
     return;
   }
 
@@ -412,11 +416,106 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
   }
 }
 
+// Chunked backward, serial part.  Per tile the adjoint of the state walks
+// as Wb = Wb' (I - 2 K D K^T) + (terms without Wb'), the forward's factor,
+// which is symmetric; so over chunk p the end adjoint E_p maps to the start
+// adjoint E_p M_p^T + C_p, with M_p the chunk's forward map (W_end = W_start
+// M_p + ...) and C_p the chunk's backward from a zero end adjoint.  From
+// E_{P-1} = dW_T (or 0), E_{p-1} = E_p M_p^T + C_p; the start adjoint of
+// chunk 0 is dW0.  Chunk p's dq region holds E_p (written here, floats
+// 0..4095), M_p (4096..8191) and C_p (8192..12287), each [64][64].
+// Workgroup = (unit, 8 rows); thread (r, col pair).
+constexpr int ACOMB_ROWS = 8;
+
+__global__ void __launch_bounds__(256) chunk_adjoint_combine_kernel(const float* dw_T, float* dq,
+                                                                    float* dw0, int Tc, int P) {
+  __shared__ float Mp[64 * 65];           // M_p, row pitch 65 (conflict-free column reads)
+  __shared__ float Er[ACOMB_ROWS][64];    // the rows' current adjoint
+  const int u = blockIdx.x, row0 = blockIdx.y * ACOMB_ROWS, t = threadIdx.x;
+  const int r = t >> 5, col = 2 * (t & 31);
+  for (int e = t; e < ACOMB_ROWS * 64; e += 256)
+    Er[e >> 6][e & 63] = dw_T ? dw_T[(size_t)u * 4096 + (row0 + (e >> 6)) * 64 + (e & 63)] : 0.f;
+  for (int p = P - 1; p >= 0; --p) {
+    float* reg = dq + ((size_t)u * P + p) * Tc * 64;
+    __syncthreads();  // Er complete, Mp free
+    for (int e = t; e < 1024; e += 256) {
+      const f32x4 m = *(const f32x4*)(reg + 4096 + 4 * e);
+      float* d = Mp + (e >> 4) * 65 + 4 * (e & 15);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[i] = m[i];
+    }
+    for (int e = t; e < ACOMB_ROWS * 64; e += 256) reg[(row0 + (e >> 6)) * 64 + (e & 63)] = Er[e >> 6][e & 63];
+    const float2 cc = *(const float2*)(reg + 8192 + (row0 + r) * 64 + col);
+    __syncthreads();  // Mp complete
+    float a0 = cc.x, a1 = cc.y;
+#pragma unroll 16
+    for (int k = 0; k < 64; ++k) {
+      const float e = Er[r][k];
+      a0 = fmaf(e, Mp[col * 65 + k], a0);
+      a1 = fmaf(e, Mp[(col + 1) * 65 + k], a1);
+    }
+    __syncthreads();  // Er fully read
+    Er[r][col] = a0;
+    Er[r][col + 1] = a1;
+  }
+  __syncthreads();
+  for (int e = t; e < ACOMB_ROWS * 64; e += 256)
+    dw0[(size_t)u * 4096 + (row0 + (e >> 6)) * 64 + (e & 63)] = Er[e >> 6][e & 63];
+}
+
 }  // namespace
 
 hipError_t launch_linear_bwd(const LinearBwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(linear_bwd_kernel, dim3(a.units), dim3(BwdGeom::THREADS), 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_linear_bwd_chunked(const LinearBwdArgs& a, int P, int rows, hipStream_t s) {
+  const int Tc = a.T / P;
+  if (P < 2 || a.T % P != 0 || Tc % 16 != 0 || Tc < 192 || !a.dw0) return hipErrorInvalidValue;
+  // M_p: each chunk's forward scan from the identity with V = 0 (Q is not
+  // read), into its dq floats 4096..8191; chunk p of unit u is sequence
+  // u * P + p of length Tc
+  LinearArgs f{};
+  f.q = a.q;
+  f.k = a.k;
+  f.v = a.v;
+  f.eta = a.eta;
+  f.w0 = nullptr;
+  f.z = nullptr;
+  f.w_out = a.dq + 4096;
+  f.w0_per_batch = 1;
+  f.units = a.units * P;
+  f.H = a.H;
+  f.T = Tc;
+  f.b = 16;
+  f.v_zero = 1;
+  f.w0_mode = W0_IDENTITY;
+  f.wout_stride = Tc * 64;
+  hipError_t e = launch_linear(f, false, rows, s);
+  if (e != hipSuccess) return e;
+  // C_p: each chunk's backward from a zero end adjoint; only its start
+  // adjoint is kept, in its dq floats 8192..12287
+  LinearBwdArgs c = a;
+  c.units = a.units * P;
+  c.T = Tc;
+  c.dw_T = nullptr;
+  c.tok_out = 0;
+  c.dw0 = a.dq + 8192;
+  c.dw0_stride = Tc * 64;
+  e = launch_linear_bwd(c, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(chunk_adjoint_combine_kernel, dim3(a.units, 64 / ACOMB_ROWS), dim3(256), 0, s,
+                     a.dw_T, a.dq, a.dw0, Tc, P);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // every chunk from its end adjoint (its dq floats 0..4095, read before any
+  // of that memory is written: the first tokens' outputs come last)
+  c.dw_T = a.dq;
+  c.dw_stride = Tc * 64;
+  c.tok_out = 1;
+  c.dw0 = nullptr;
+  return launch_linear_bwd(c, s);
 }
 
 }  // namespace ttt

@@ -336,3 +336,28 @@ def gate_bwd(lib, **kw):
 def test_lr_gate_bwd_argument_checks(lib, kw, expect):
     assert gate_bwd(lib, **kw) == status(expect), lib.ttt_last_error()
     assert lib.ttt_last_error().startswith(b"ttt_lr_gate_bwd:")
+
+
+def bwd_chunked(lib, chunks, **kw):
+    a = dict(q=A[0], k=A[1], v=A[2], eta=A[3], ck=A[4], B=1, H=2, T=768, d=64, b=16,
+             dt=_lib.TTT_BF16, dz=A[5], dwT=None, dq=A[6], dk=A[7], dv=A[8], deta=A[9], dw0=A[10])
+    a.update(kw)
+    return lib.ttt_linear_bwd_chunked(a["q"], a["k"], a["v"], a["eta"], a["ck"], a["B"], a["H"],
+                                      a["T"], a["d"], a["b"], a["dt"], a["dz"], a["dwT"], a["dq"],
+                                      a["dk"], a["dv"], a["deta"], a["dw0"], None, chunks)
+
+
+@pytest.mark.parametrize("chunks,kw,expect", [
+    (-1, {}, "TTT_ERR_UNSUPPORTED"),
+    (5, {}, "TTT_ERR_UNSUPPORTED"),                 # 768 not a multiple of 5
+    (8, {}, "TTT_ERR_UNSUPPORTED"),                 # 96-token chunks (< 192)
+    (2, dict(T=808), "TTT_ERR_UNSUPPORTED"),        # 404-token chunks, not 16 | 404
+    (2, dict(b=4), "TTT_ERR_UNSUPPORTED"),
+    (2, dict(dq=A[4]), "TTT_ERR_ALIAS"),
+    (2, dict(dz=None), "TTT_ERR_NULL"),
+    (4, dict(B=0), "TTT_OK"),                       # empty work: nothing launched
+])
+def test_linear_bwd_chunked_argument_checks(lib, chunks, kw, expect):
+    assert bwd_chunked(lib, chunks, **kw) == status(expect), lib.ttt_last_error()
+    if expect != "TTT_OK":
+        assert lib.ttt_last_error().startswith(b"ttt_linear_bwd_chunked:")

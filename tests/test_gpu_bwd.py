@@ -106,3 +106,77 @@ def test_backward_empty_sequence_and_rejected_arguments():
         ttt_linear_bwd(q, k, v, eta, ck, 4, dz)
     with pytest.raises(TTTError, match="TTT_ERR_UNSUPPORTED"):
         ttt_linear_fwd_ckpt(q, k, v, eta, w0, 32)
+
+
+# ---------------------------------------------------------------- sequence chunks
+@pytest.mark.parametrize("T,P", [(768, 2), (768, 4), (576, 3)])
+@pytest.mark.parametrize("with_dwT", [False, True])
+def test_chunked_backward_parity(T, P, with_dwT):
+    """P chunks of T / P tokens (192 and 384: 12 and 24 tiles per chunk)."""
+    x = inputs.make_inputs(inputs.Workload("bwdc", "linear", B=1, H=2, T=T, seed=750 + P))
+    rng = np.random.default_rng(751 + T + P)
+    dz = rng.standard_normal(x.q.shape).astype(np.float32)
+    dwT = rng.standard_normal((1, 2, 64, 64)).astype(np.float32) if with_dwT else None
+    q, k, v = (gu.dev(x, n) for n in ("q", "k", "v"))
+    eta, w0 = gu.f32(x.eta), gu.f32(x.w0)
+    _, _, ck = ttt_linear_fwd_ckpt(q, k, v, eta, w0, 16)
+    dwT_d = None if dwT is None else gu.f32(dwT)
+    got = ttt_linear_bwd(q, k, v, eta, ck, 16, gu.f32(dz), dwT_d, seq_chunks=P)
+    one = ttt_linear_bwd(q, k, v, eta, ck, 16, gu.f32(dz), dwT_d, seq_chunks=1)
+    torch.cuda.synchronize()
+    got = [t.cpu().numpy() for t in got]
+    ref = oracle.linear_bwd(x.q, x.k, x.v, x.eta, x.w0, 16, dz, dwT)
+    check(got, ref, f"T={T} P={P}")
+    check(got, [t.cpu().numpy() for t in one], f"T={T} P={P} vs one pass")
+
+
+def test_chunked_backward_is_deterministic_and_ignores_prior_output_contents():
+    """dq's memory serves the chunk maps first: NaN there beforehand changes nothing."""
+    x = inputs.make_inputs(inputs.Workload("bwdd", "linear", B=1, H=2, T=768, seed=760))
+    dz = gu.f32(np.random.default_rng(761).standard_normal(x.q.shape).astype(np.float32))
+    q, k, v = (gu.dev(x, n) for n in ("q", "k", "v"))
+    eta, w0 = gu.f32(x.eta), gu.f32(x.w0)
+    _, _, ck = ttt_linear_fwd_ckpt(q, k, v, eta, w0, 16)
+    a = ttt_linear_bwd(q, k, v, eta, ck, 16, dz, seq_chunks=4)
+    outs = [torch.full_like(t, float("nan")) for t in a]
+    from test_rnn_layers_head_amd import _lib
+    from test_rnn_layers_head_amd.api import _ptr
+    _lib.check(_lib.lib().ttt_linear_bwd_chunked(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(ck), 1, 2, 768, 64, 16, _lib.TTT_BF16, _ptr(dz),
+        None, *(_ptr(t) for t in outs), torch.cuda.current_stream().cuda_stream, 4))
+    torch.cuda.synchronize()
+    assert all(torch.equal(u, w) for u, w in zip(a, outs))
+
+
+def test_long_sequence_checkpoints_and_backward_in_chunks():
+    """1 x 2 x 8192: the checkpointing forward and the backward both take 8
+    chunks (units * P <= 256, chunks of 1024 tokens); sampled checkpoints and
+    every gradient against the oracle."""
+    from test_rnn_layers_head_amd import ttt_linear_fwd_plan
+    assert ttt_linear_fwd_plan(1, 2, 8192, 16)[1] == 8
+    x = inputs.make_inputs(inputs.Workload("bwdl", "linear", B=1, H=2, T=8192, seed=770))
+    rng = np.random.default_rng(771)
+    dz = (rng.standard_normal(x.q.shape) * 0.1).astype(np.float32)
+    z, w, ck, got = run_fwd_bwd(x, dz)
+    q, k, v = (gu.dev(x, n) for n in ("q", "k", "v"))
+    z1, w1 = ttt_linear_fwd(q, k, v, gu.f32(x.eta), gu.f32(x.w0), 16)
+    torch.cuda.synchronize()
+    assert torch.equal(z, z1) and torch.equal(w, w1)  # same chunked passes, plus the checkpoints
+    ck = ck.cpu().numpy()
+    for m in (1, 64, 65, 300, 511):  # inside chunks and at chunk starts (every 64 tiles)
+        _, ref = oracle.linear(x.q[:, :, :16 * m], x.k[:, :, :16 * m], x.v[:, :, :16 * m],
+                               x.eta[:, :, :16 * m], x.w0, 16)
+        gu.assert_close(ck[:, :, m], ref, "bf16", f"checkpoint {m}")
+    ref = oracle.linear_bwd(x.q, x.k, x.v, x.eta, x.w0, 16, dz)
+    check(got, ref, "T=8192 chunked")
+
+
+def test_chunked_backward_rejects():
+    x = inputs.make_inputs(inputs.Workload("bwdr", "linear", B=1, H=1, T=768, seed=780))
+    q, k, v = (gu.dev(x, n) for n in ("q", "k", "v"))
+    eta, w0 = gu.f32(x.eta), gu.f32(x.w0)
+    _, _, ck = ttt_linear_fwd_ckpt(q, k, v, eta, w0, 16)
+    dz = torch.zeros(1, 1, 768, 64, device="cuda")
+    for P in (-1, 5, 8):  # negative; T % P != 0; T / P < 192
+        with pytest.raises(TTTError, match="TTT_ERR_UNSUPPORTED"):
+            ttt_linear_bwd(q, k, v, eta, ck, 16, dz, seq_chunks=P)

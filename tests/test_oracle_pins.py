@@ -638,6 +638,40 @@ def test_chunked_scan_reading_in_fp64():
     assert rel(np.concatenate(zs, axis=2), z) < 1e-12 and rel(W, w) < 1e-12
 
 
+def test_chunked_backward_reading_in_fp64():
+    """The chunked backward's decomposition, on the oracle: walking a chunk
+    backward from end adjoint E gives start adjoint E M^T + C', with M the
+    chunk's forward run from the identity with v = 0 (each mini-batch's
+    factor I - 2 K diag(eta) K^T is symmetric) and C' its backward from a zero
+    end adjoint; chaining from dW_T over the chunks in reverse gives each
+    chunk's end adjoint, and the chunks' backward runs from those reproduce
+    the whole sequence's gradients."""
+    rng = np.random.default_rng(36)
+    B, H, T, d, b, P = 1, 2, 96, 5, 4, 3
+    q, k, v, eta, w0 = rand_linear(rng, B, H, T, d)
+    dz = rng.standard_normal(q.shape)
+    dwT = rng.standard_normal((B, H, d, d))
+    full = oracle.linear_bwd(q, k, v, eta, w0, b, dz, dwT)
+    Tc = T // P
+    sl = lambda a, p: a[:, :, p * Tc:(p + 1) * Tc]
+    eye = np.broadcast_to(np.eye(d), (H, d, d)).copy()
+    starts = [np.broadcast_to(w0, (B, H, d, d)).copy()]  # each chunk's start state
+    for p in range(P - 1):
+        starts.append(oracle.linear(sl(q, p), sl(k, p), sl(v, p), sl(eta, p), starts[-1], b)[1])
+    E, parts = dwT, [None] * P
+    for p in reversed(range(P)):
+        a = (sl(q, p), sl(k, p), sl(v, p), sl(eta, p))
+        _, M = oracle.linear(a[0], a[1], 0 * a[2], a[3], eye, b)
+        Cp = oracle.linear_bwd(*a, starts[p], b, sl(dz, p))[4]
+        parts[p] = oracle.linear_bwd(*a, starts[p], b, sl(dz, p), E)
+        S = E @ np.swapaxes(M, -1, -2) + Cp
+        assert rel(S, parts[p][4]) < 1e-12
+        E = S
+    for i in range(4):
+        assert rel(np.concatenate([pp[i] for pp in parts], axis=2), full[i]) < 1e-12
+    assert rel(E, full[4]) < 1e-12
+
+
 def test_linear_row_permutation():
     rng = np.random.default_rng(31)
     q, k, v, eta, w0 = rand_linear(rng, 1, 2, 21, 7)
