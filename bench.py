@@ -339,9 +339,11 @@ def bwd_alg_bytes(wl) -> int:
 
 def training_case(wl, steps, warmup):
     """ttt_linear_fwd_ckpt then ttt_linear_bwd on one workload (b = 16), timed
-    separately; dz is a seeded N(0, 0.01) draw."""
+    separately; dz is a seeded N(0, 0.01) draw.  Where both take sequence
+    chunks, the single-pass backward is timed beside them."""
     import torch
-    from test_rnn_layers_head_amd import inputs, ttt_linear_bwd, ttt_linear_fwd_ckpt
+    from test_rnn_layers_head_amd import (inputs, ttt_linear_bwd, ttt_linear_fwd_ckpt,
+                                          ttt_linear_fwd_plan)
     x = inputs.make_inputs(wl)
     d = device_inputs(x)
     g = torch.Generator().manual_seed(17)
@@ -361,7 +363,13 @@ def training_case(wl, steps, warmup):
     assert all(torch.isfinite(t).all().item() for t in grads)
     fb = linear_alg_bytes(wl) + wl.units * nt * wl.d * wl.d * 4
     bb = bwd_alg_bytes(wl)
-    return {"workload": wl.name, "b": 16, "fwd_ckpt_us": kf, "bwd_us": kb,
+    chunks = ttt_linear_fwd_plan(wl.B, wl.H, wl.T, 16)[1]
+    extra = {"seq_chunks": chunks}
+    if chunks > 1:
+        _, k1, _ = time_launches(lambda: ttt_linear_bwd(d["q"], d["k"], d["v"], d["eta"], ck, 16, dz,
+                                                        seq_chunks=1), steps, warmup)
+        extra["bwd_one_pass_us"] = k1
+    return {"workload": wl.name, "b": 16, **extra, "fwd_ckpt_us": kf, "bwd_us": kb,
             "fwd_alg_bytes": fb, "bwd_alg_bytes": bb,
             "fwd_hbm_frac": fb / (kf * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "bwd_hbm_frac": bb / (kb * 1e-6) / 1e9 / HBM_PEAK_GBS,
@@ -545,8 +553,8 @@ def summarize_pmc(fetch_dir, write_dir):
                 print(f"  {c:10s} dispatch {disp:>3d}  {val:14.3f}  {name[:60]}")
     print(f"\nCalibration: stream_copy_kernel over 1 GiB reads {fetch[copy_name]:.0f} KiB by "
           f"FETCH_SIZE and writes {write[copy_name]:.0f} KiB by WRITE_SIZE;\nscale factors fetch "
-          f"x{f_scale:.4f}, write x{w_scale:.4f} (FETCH_SIZE counts half of the bytes a plain copy "
-          "reads).\n")
+          f"x{f_scale:.4f}, write x{w_scale:.4f} (each factor: the bytes the copy moves over what the "
+          "counter reads for it).\n")
     cases = (("linear_scan", "linear_scan_bf16_kernel", SCAN_SOURCES, linear_alg_bytes, 3),
              ("linear_ln_scan", "linear_ln_scan_kernel", LN_SOURCES, ln_alg_bytes, 6),
              ("mlp_scan", "mlp_scan_kernel", MLP_SOURCES, mlp_alg_bytes, 4))
@@ -610,7 +618,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="also launch the 1 GiB streaming copy used to scale byte counters")
-    ap.add_argument("--only", choices=("train", "decode", "gate"),
+    ap.add_argument("--only", choices=("train", "train-long", "decode", "gate"),
                     help="run one group of the secondary measurements and print it (for profiling)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "KERNEL", "SKIP", "TAKE"),
@@ -644,6 +652,10 @@ def main():
     if args.only == "train":
         print(json.dumps({w.name: training_case(w, max(5, args.steps // 5), 10)
                           for w in (wl, inputs.workload(2))}))
+        return 0
+    if args.only == "train-long":
+        w5 = inputs.workload(5)
+        print(json.dumps({w5.name: training_case(w5, 3, 2)}))
         return 0
     if args.only == "gate":
         print(json.dumps({inputs.workload(i).name: gate_case(inputs.workload(i), 20, 20)
@@ -690,6 +702,9 @@ def main():
             extras[f"gate-{wg.name}"] = gate_case(wg, max(5, args.steps // 2), 20)
         log(f"[bench] forward with checkpoints + backward, {wl.name}")
         extras[f"train-{wl.name}"] = training_case(wl, max(5, args.steps // 5), 10)
+        w5 = inputs.workload(5)
+        log(f"[bench] forward with checkpoints + backward, {w5.name}")
+        extras[f"train-{w5.name}"] = training_case(w5, 3, 2)
         for kind, B, H in DECODE_CASES:
             log(f"[bench] decode step {kind} B={B} H={H}")
             extras[f"decode-{kind}-B{B}-H{H}"] = decode_case(kind, B, H, 100, 200)
