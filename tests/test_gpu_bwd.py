@@ -180,3 +180,34 @@ def test_chunked_backward_rejects():
     for P in (-1, 5, 8):  # negative; T % P != 0; T / P < 192
         with pytest.raises(TTTError, match="TTT_ERR_UNSUPPORTED"):
             ttt_linear_bwd(q, k, v, eta, ck, 16, dz, seq_chunks=P)
+
+
+def test_chunked_backward_graph_replays_match_eager():
+    """The chunked backward's four launches captured in one HIP graph: every
+    replay gives exactly the eager result (outputs NaN-filled before each)."""
+    x = inputs.make_inputs(inputs.Workload("bwdg", "linear", B=1, H=2, T=1536, seed=790))
+    q, k, v = (gu.dev(x, n) for n in ("q", "k", "v"))
+    eta, w0 = gu.f32(x.eta), gu.f32(x.w0)
+    dz = gu.f32(np.random.default_rng(791).standard_normal(x.q.shape).astype(np.float32))
+    dwT = gu.f32(np.random.default_rng(792).standard_normal((1, 2, 64, 64)).astype(np.float32))
+    _, _, ck = ttt_linear_fwd_ckpt(q, k, v, eta, w0, 16)
+    ref = ttt_linear_bwd(q, k, v, eta, ck, 16, dz, dwT, seq_chunks=4)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            outs = ttt_linear_bwd(q, k, v, eta, ck, 16, dz, dwT, stream=s, seq_chunks=4)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        scratch = torch.randn(1 << 16, device="cuda").sum()  # unrelated eager work
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(outs, ref)), rep
+        assert torch.isfinite(scratch)
