@@ -435,17 +435,31 @@ __global__ void __launch_bounds__(256) chunk_adjoint_combine_kernel(const float*
   const int r = t >> 5, col = 2 * (t & 31);
   for (int e = t; e < ACOMB_ROWS * 64; e += 256)
     Er[e >> 6][e & 63] = dw_T ? dw_T[(size_t)u * 4096 + (row0 + (e >> 6)) * 64 + (e & 63)] : 0.f;
+  auto chunk = [&](int p) { return dq + ((size_t)u * P + p) * Tc * 64; };
+  // registers: this thread's four float4 of the next M and its two C' values,
+  // loaded while the current step runs
+  f32x4 mnext[4];
+  float2 cnext;
+  auto fetch = [&](int p) {
+    const float* reg = chunk(p);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mnext[q] = *(const f32x4*)(reg + 4096 + 4 * (t + 256 * q));
+    cnext = *(const float2*)(reg + 8192 + (row0 + r) * 64 + col);
+  };
+  fetch(P - 1);
   for (int p = P - 1; p >= 0; --p) {
-    float* reg = dq + ((size_t)u * P + p) * Tc * 64;
+    float* reg = chunk(p);
     __syncthreads();  // Er complete, Mp free
-    for (int e = t; e < 1024; e += 256) {
-      const f32x4 m = *(const f32x4*)(reg + 4096 + 4 * e);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = t + 256 * q;
       float* d = Mp + (e >> 4) * 65 + 4 * (e & 15);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) d[i] = m[i];
+      for (int i = 0; i < 4; ++i) d[i] = mnext[q][i];
     }
+    const float2 cc = cnext;
+    if (p > 0) fetch(p - 1);
     for (int e = t; e < ACOMB_ROWS * 64; e += 256) reg[(row0 + (e >> 6)) * 64 + (e & 63)] = Er[e >> 6][e & 63];
-    const float2 cc = *(const float2*)(reg + 8192 + (row0 + r) * 64 + col);
     __syncthreads();  // Mp complete
     float a0 = cc.x, a1 = cc.y;
 #pragma unroll 16
