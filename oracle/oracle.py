@@ -11,9 +11,9 @@ Time)"): §3.1 (update, then output), §3.3 (multi-view loss
 ||f(k;W) - v||^2, output f(q; W_t)), §3.5 (mini-batch gradient point),
 §4.4 (TTT-Linear f = Wx, TTT-MLP f = W2 GELU(W1 x)), §4.6 (per-token eta).
 
-Parity pins live in ``tests/test_oracle_pins.py``; the only function here with
-no pin from the pages is the GELU form (exact erf), see the module docstring
-there.
+Parity pins live in ``tests/test_oracle_pins.py``.  The GELU form (exact erf,
+x Phi(x)) is a reading, since the pages name GELU without a form; its values and
+derivative are pinned there to closed normal-distribution values.
 """
 from __future__ import annotations
 

@@ -38,9 +38,15 @@ mistake at a time (dropped factor 2, wrong sign, output before the update,
 gradient at the wrong state, transposed operand, ...) and checks that the pin
 set rejects every one of them.
 
-The GELU form (exact erf) is fixed by no passage of the pages; its parity is
-pinned only through the dual form and the finite-difference check, which use
-the same definition.
+* GELU of the MLP inner model (§4.4 names GELU without a form; read as
+  x Phi(x)): GELU(a) and GELU'(a) at a in {0, +-1, +-2}, and GELU''(0), exposed
+  one per hidden unit through the MLP's output and both layers' updates, against
+  the closed normal-distribution values of
+  tests/golden/normal_distribution_values.json (Phi(1), Phi(2), phi(1), phi(2),
+  sqrt(2/pi)), which ``test_normal_values_fixture`` re-derives from Taylor series
+  in 40-digit decimal arithmetic.  The dual form and the finite-difference check
+  share the oracle's definition; this pin does not, so a mistake common to
+  GELU and GELU' (erf(x) for erf(x/sqrt 2), the tanh approximation) fails it.
 """
 from __future__ import annotations
 
@@ -248,6 +254,74 @@ def pin_mlp_w2_zero_kernel_attention(lib):
         zt[t] = S @ phi(q[0, 0, t])
     assert rel(z[0, 0], zt) < 1e-12 and rel(c[0, 0], S) < 1e-12
     assert np.array_equal(a[0, 0], w1[0])
+
+
+def _normal_table():
+    """Phi, phi at 0, +-1, +-2 and sqrt(2/pi) from tests/golden (closed values)."""
+    with open(os.path.join(HERE, "golden", "normal_distribution_values.json")) as f:
+        g = json.load(f)
+    Phi, phi = {0: 0.5}, {0: float(g["sqrt_2_over_pi"]) / 2.0}
+    for s in ("1", "2"):
+        a = int(s)
+        Phi[a], Phi[-a] = float(g["Phi"][s]), 1.0 - float(g["Phi"][s])
+        phi[a] = phi[-a] = float(g["phi"][s])
+    return Phi, phi, float(g["sqrt_2_over_pi"])
+
+
+GELU_POINTS = (0, 1, -1, 2, -2)
+
+
+def pin_mlp_gelu_closed_values(lib):
+    """GELU and GELU' of the oracle's MLP against closed normal-distribution values.
+
+    d = hidden = 5, W2_0 = I; hidden unit u sees the pre-activation
+    a_u = W1_0[u][0] k_0 with k = e_0, so every quantity of the MLP is exposed
+    per unit:
+      * z = W2 GELU(W1 q) with eta = 0, W1 = I, q = points  -> GELU(points);
+      * one step (T = b = 1, eta = 1/2), v_u = GELU(a_u) - 1/2 so that the
+        output error e = 2 (W2 GELU(a) - v) is 1 in every component:
+        W1_T[u][0] = a_u - GELU'(a_u) / 2 and W2_T[i][u] = [i = u] - GELU(a_u) / 2;
+      * GELU''(0) = sqrt(2/pi) by a central difference of GELU' at +-h.
+    No value of the GELU is computed in this test: the expected values are the
+    closed ones of tests/golden/normal_distribution_values.json.
+    """
+    Phi, phi, s2pi = _normal_table()
+    pts = np.array(GELU_POINTS, dtype=np.float64)
+    gelu = np.array([a * Phi[a] for a in GELU_POINTS])
+    dgelu = np.array([Phi[a] + a * phi[a] for a in GELU_POINTS])
+    n = len(pts)
+    eye = np.eye(n).reshape(1, n, n)
+    zeros = np.zeros((1, 1, 1, n))
+
+    # GELU through the output, eta = 0
+    z, _, _ = oracle.mlp(pts.reshape(1, 1, 1, n), zeros, zeros, np.zeros((1, 1, 1)), eye, eye, 1,
+                         lib=lib)
+    assert np.abs(z[0, 0, 0] - gelu).max() < 1e-15, (z[0, 0, 0], gelu)
+
+    # GELU' through the first layer's update, GELU again through the second's
+    w1 = np.zeros((1, n, n))
+    w1[0, :, 0] = pts
+    k = np.zeros((1, 1, 1, n))
+    k[..., 0] = 1.0
+    v = (gelu - 0.5).reshape(1, 1, 1, n)
+    _, a, c = oracle.mlp(zeros, k, v, np.full((1, 1, 1), 0.5), w1, eye, 1, lib=lib)
+    assert np.abs((pts - a[0, 0, :, 0]) * 2.0 - dgelu).max() < 1e-14, (a[0, 0, :, 0], dgelu)
+    assert np.abs(a[0, 0, :, 1:]).max() == 0.0
+    assert np.abs((np.eye(n) - c[0, 0]) * 2.0 - np.broadcast_to(gelu, (n, n))).max() < 1e-14
+
+    # GELU''(0) = sqrt(2/pi): GELU'(h) - GELU'(-h) over 2h (error ~ (2/3) phi(0) h^2)
+    h = 1e-3
+    w1 = np.zeros((1, 2, 2))
+    w1[0, :, 0] = (h, -h)
+    k2 = np.zeros((1, 1, 1, 2))
+    k2[..., 0] = 1.0
+    eye2 = np.eye(2).reshape(1, 2, 2)
+    # v = GELU(+-h) - 1/2 to first order: e = 1 + O(h^2), its effect cancels in the difference
+    v2 = np.array([h * 0.5, -h * 0.5]).reshape(1, 1, 1, 2) - 0.5
+    _, a2, _ = oracle.mlp(np.zeros((1, 1, 1, 2)), k2, v2, np.full((1, 1, 1), 0.5), w1, eye2, 1,
+                          lib=lib)
+    dg = (np.array([h, -h]) - a2[0, 0, :, 0]) * 2.0
+    assert abs((dg[0] - dg[1]) / (2 * h) - s2pi) < 1e-5 * s2pi, ((dg[0] - dg[1]) / (2 * h), s2pi)
 
 
 def rand_ln(rng, H, d, g_scale=0.3, b_scale=0.2):
@@ -574,6 +648,7 @@ PINS = [
     pin_mlp_one_step_finite_differences,
     pin_mlp_zero_state,
     pin_mlp_w2_zero_kernel_attention,
+    pin_mlp_gelu_closed_values,
     pin_ln_primal_equals_dual,
     pin_ln_one_step_finite_differences,
     pin_ln_gamma_zero,
@@ -596,6 +671,46 @@ PINS = [
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
 def test_pin(pin):
     pin(oracle.load())
+
+
+def test_normal_values_fixture():
+    """The golden normal-distribution values against Taylor series of erf and exp,
+    summed in 40-digit decimal arithmetic (shares nothing with libm or the oracle)."""
+    from decimal import Decimal as D, localcontext
+
+    with localcontext() as ctx:
+        ctx.prec = 45
+        eps = D(10) ** -42
+
+        def series(term0, nxt):
+            s, t, n = D(0), term0, 0
+            while abs(t) > eps:
+                s += t
+                n += 1
+                t = nxt(t, n)
+            return s
+
+        def arctan_inv(m):  # arctan(1/m)
+            x = D(1) / m
+            return series(x, lambda t, n: -t * x * x * (2 * n - 1) / (2 * n + 1))
+
+        pi = 4 * (4 * arctan_inv(5) - arctan_inv(239))  # Machin's formula
+
+        def erf(x):  # 2/sqrt(pi) sum (-1)^n x^(2n+1) / (n! (2n+1))
+            return 2 / pi.sqrt() * series(x, lambda t, n: -t * x * x * (2 * n - 1) / (n * (2 * n + 1)))
+
+        def exp(x):
+            return series(D(1), lambda t, n: t * x / n)
+
+        with open(os.path.join(HERE, "golden", "normal_distribution_values.json")) as f:
+            g = json.load(f)
+        for s in ("1", "2"):
+            a = D(s)
+            Phi = (1 + erf(a / D(2).sqrt())) / 2
+            phi = exp(-a * a / 2) / (2 * pi).sqrt()
+            assert abs(Phi - D(g["Phi"][s])) < D("1e-19"), (s, Phi)
+            assert abs(phi - D(g["phi"][s])) < D("1e-19"), (s, phi)
+        assert abs((2 / pi).sqrt() - D(g["sqrt_2_over_pi"])) < D("1e-19")
 
 
 # ---------------------------------------------------------------------------
@@ -732,6 +847,22 @@ MUTATIONS = {
     "mlp_backprop_through_current_w2": ("acc += s->W2s[i * hd + u] * s->e[i];", "acc += W2[i * hd + u] * s->e[i];"),
     "mlp_output_from_start_w1": ("acc += W1[u * d + j] * qt[j];", "acc += s->W1s[u * d + j] * qt[j];"),
     "mlp_gelu_scale": ("return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));", "return 0.5 * x * (1.0 + erf(x));"),
+    # common-mode GELU mistakes: the value and the derivative carry the same error,
+    # so only closed values (not consistency between the two) can reject them
+    "mlp_gelu_erf_unscaled_both": [
+        ("return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));", "return 0.5 * x * (1.0 + erf(x));"),
+        ("return 0.5 * (1.0 + erf(x / sqrt(2.0))) + x * exp(-0.5 * x * x) / sqrt(2.0 * pi);",
+         "return 0.5 * (1.0 + erf(x)) + x * exp(-x * x) / sqrt(pi);")],
+    "mlp_gelu_tanh_form_both": [
+        ("return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));",
+         "return 0.5 * x * (1.0 + tanh(sqrt(2.0 / 3.14159265358979323846) * (x + 0.044715 * x * x * x)));"),
+        ("return 0.5 * (1.0 + erf(x / sqrt(2.0))) + x * exp(-0.5 * x * x) / sqrt(2.0 * pi);",
+         "const double c = sqrt(2.0 / pi), th = tanh(c * (x + 0.044715 * x * x * x));\n"
+         "  return 0.5 * (1.0 + th) + 0.5 * x * (1.0 - th * th) * c * (1.0 + 3.0 * 0.044715 * x * x);")],
+    "mlp_gelu_grad_density_unnormalised": (
+        "x * exp(-0.5 * x * x) / sqrt(2.0 * pi);", "x * exp(-0.5 * x * x);"),
+    "mlp_gelu_grad_density_wrong_width": (
+        "x * exp(-0.5 * x * x) / sqrt(2.0 * pi);", "x * exp(-x * x) / sqrt(2.0 * pi);"),
     "ln_sample_variance": ("  var /= (double)d;", "  var /= (double)(d - 1);"),
     "ln_eps_outside_sqrt": ("1.0 / sqrt(var + eps);", "1.0 / (sqrt(var) + eps);"),
     "ln_drop_mean_term": ("rs * (gy[i] - m1s - yhat[i] * m2s);", "rs * (gy[i] - yhat[i] * m2s);"),
@@ -785,13 +916,15 @@ MUTATIONS = {
 def test_planted_mistakes_are_caught(name):
     if shutil.which("gcc") is None:
         pytest.skip("gcc not available")
-    old, new = MUTATIONS[name]
+    edits = MUTATIONS[name]
     src = open(os.path.join(os.path.dirname(oracle.__file__), "ttt_oracle.c")).read()
-    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+    for old, new in (edits if isinstance(edits, list) else [edits]):
+        assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+        src = src.replace(old, new)
     with tempfile.TemporaryDirectory() as tmp:
         path = os.path.join(tmp, "mut.c")
         with open(path, "w") as f:
-            f.write(src.replace(old, new))
+            f.write(src)
         lib = oracle.load(oracle.build(path, os.path.join(tmp, "libmut.so")))
         caught = []
         for pin in PINS:
