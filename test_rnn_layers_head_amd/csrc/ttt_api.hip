@@ -335,6 +335,8 @@ ttt_status_t linear_bwd_impl(const void* q, const void* k, const void* v, const 
   if (dt != TTT_BF16) return fail(TTT_ERR_UNSUPPORTED, "%s: only bf16 q/k/v are supported", fn);
   if (seq >= ((int64_t)1 << 31))
     return fail(TTT_ERR_SHAPE, "%s: B*H*T*d = %lld exceeds 2^31 - 1", fn, (long long)seq);
+  if (T >= (1 << 24))  // a unit's T x 64 fp32 gradients stay within 32-bit byte offsets
+    return fail(TTT_ERR_SHAPE, "%s: T = %d exceeds 2^24 - 1", fn, T);
   if (chunks < 0) return fail(TTT_ERR_UNSUPPORTED, "%s: seq_chunks=%d must be >= 0", fn, chunks);
   const int P = chunks ? chunks : default_chunks(dt, b, units, T);
   if (P > 1 && !chunks_supported(P, T, b, dt))

@@ -161,16 +161,10 @@ hipError_t launch_lr_gate(const GateArgs& a, int tokens_per_workgroup, hipStream
   if (ntok == 0 || a.H == 0) return hipSuccess;
   if (tokens_per_workgroup == 0) tokens_per_workgroup = ntok >= 256 * 64 ? 64 : 32;
   switch (tokens_per_workgroup) {
-    case 32:
-      hipLaunchKernelGGL(lr_gate_kernel<2>, dim3((unsigned)((ntok + 31) / 32)), dim3(256), 0, s, a);
-      break;
-    case 64:
-      hipLaunchKernelGGL(lr_gate_kernel<4>, dim3((unsigned)((ntok + 63) / 64)), dim3(256), 0, s, a);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 32: return launch(lr_gate_kernel<2>, dim3((unsigned)((ntok + 31) / 32)), dim3(256), s, a);
+    case 64: return launch(lr_gate_kernel<4>, dim3((unsigned)((ntok + 63) / 64)), dim3(256), s, a);
+    default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace ttt
@@ -507,13 +501,13 @@ __global__ void __launch_bounds__(256) fill_zero_kernel(float* p, int64_t n) {
 // once, from the runtime's occupancy query (host-side, asked on every call:
 // the library keeps nothing between calls).
 // A failed query falls back to one workgroup per CU of 256 CUs (a sizing
-// choice only) and its error is cleared, so the launches report their own.
+// choice only); the launches report their own status (ttt::launch), so an
+// error of the query is neither cleared nor blamed on them.
 int resident_workgroups(const void* kernel) {
   int dev = 0, per_cu = 0, cus = 0;
-  bool ok = hipGetDevice(&dev) == hipSuccess;
-  ok = ok && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) == hipSuccess;
-  ok = ok && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
-  if (!ok) (void)hipGetLastError();
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess) per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
   return std::max(per_cu, 1) * (cus > 0 ? cus : 256);
 }
 
@@ -521,10 +515,11 @@ hipError_t launch_lr_gate_bwd(const GateBwdArgs& a, hipStream_t s) {
   const int ntok = a.B * a.T;  // B * T * dx < 2^31 (checked by the ABI)
   const int64_t nth = (int64_t)a.H * a.dx;
   if (ntok == 0 || a.H == 0) {  // dtheta = 0 (no tokens), dx = 0 (no heads)
-    if (nth > 0) hipLaunchKernelGGL(fill_zero_kernel, dim3(256), dim3(256), 0, s, a.dtheta, nth);
-    if (ntok > 0)
-      hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(256), 0, s, a.dxo, (int64_t)ntok * a.dx);
-    return hipGetLastError();
+    hipError_t e = hipSuccess;
+    if (nth > 0) e = launch(fill_zero_kernel, dim3(256), dim3(256), s, a.dtheta, nth);
+    if (e == hipSuccess && ntok > 0)
+      e = launch(fill_zero_kernel, dim3(1024), dim3(256), s, a.dxo, (int64_t)ntok * a.dx);
+    return e;
   }
   const bool small_h = a.H <= 16;
   // Token chunks are sized so that the whole grid is resident at once (no
@@ -566,8 +561,9 @@ hipError_t launch_lr_gate_bwd(const GateBwdArgs& a, hipStream_t s) {
   }
   if (nchunk > 1) {
     const int64_t nb = (nth + 255) / 256;
-    hipLaunchKernelGGL(lr_gate_bwd_reduce_kernel, dim3((unsigned)(nb < 1024 ? nb : 1024)), dim3(256), 0,
-                       s, a, (const float*)a.dxo, nchunk);
+    const hipError_t e = launch(lr_gate_bwd_reduce_kernel, dim3((unsigned)(nb < 1024 ? nb : 1024)),
+                                dim3(256), s, a, (const float*)a.dxo, nchunk);
+    if (e != hipSuccess) return e;
   }
 
   // dx: chunks of 64 G tokens per workgroup (G groups of 16 per wave), tiles
@@ -589,7 +585,7 @@ hipError_t launch_lr_gate_bwd(const GateBwdArgs& a, hipStream_t s) {
     const hipError_t e = hipLaunchKernel(hp == 0 ? kx0 : kx1, g2, dim3(256), args, 0, s);
     if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace ttt

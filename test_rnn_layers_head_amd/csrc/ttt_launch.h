@@ -4,7 +4,25 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 namespace ttt {
+
+// Enqueue `kernel` on `s` and return the status of this launch alone: an
+// error left pending on the calling thread by earlier HIP calls is neither
+// reported nor cleared.
+template <typename... P, typename... A>
+hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t s, A&&... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  std::tuple<P...> v(std::forward<A>(args)...);
+  return std::apply(
+      [&](auto&... x) {
+        void* argv[] = {(void*)&x...};
+        return hipLaunchKernel((const void*)kernel, grid, block, argv, 0, s);
+      },
+      v);
+}
 
 struct LinearArgs {
   const void* q;

@@ -310,9 +310,7 @@ static hipError_t launch_one(const LinearArgs& a, hipStream_t s) {
   using G = LinearGeom<F32IN, ROWS>;
   constexpr int NSPLIT = 64 / ROWS;
   int blocks = NSPLIT == 1 ? a.units : ((a.units + 7) / 8) * 8 * NSPLIT;
-  hipLaunchKernelGGL((linear_scan_kernel<F32IN, MODE, ROWS>), dim3(blocks), dim3(G::THREADS), 0,
-                     s, a);
-  return hipGetLastError();
+  return launch(linear_scan_kernel<F32IN, MODE, ROWS>, dim3(blocks), dim3(G::THREADS), s, a);
 }
 
 template <bool F32IN, int MODE>

@@ -511,9 +511,8 @@ template <int MODE, int ROWS, int TPM, bool CKPT = false>
 hipError_t launch_one(const LinearArgs& a, hipStream_t s) {
   constexpr int NSPLIT = 64 / ROWS;
   const int blocks = NSPLIT == 1 ? a.units : ((a.units + 7) / 8) * 8 * NSPLIT;
-  hipLaunchKernelGGL((linear_scan_bf16_kernel<MODE, ROWS, TPM, CKPT>), dim3(blocks),
-                     dim3(Geom<ROWS>::THREADS), 0, s, a);
-  return hipGetLastError();
+  return launch(linear_scan_bf16_kernel<MODE, ROWS, TPM, CKPT>, dim3(blocks),
+                dim3(Geom<ROWS>::THREADS), s, a);
 }
 
 template <int MODE, int TPM, bool CKPT = false>
@@ -603,9 +602,8 @@ hipError_t launch_linear_chunked(const LinearArgs& a, int P, int rows, hipStream
   c.w_out = a.z + 64 * 64;
   e = launch_rows<MODE_B16, 1>(c, rows, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(chunk_combine_kernel, dim3(a.units, 64 / COMBINE_ROWS), dim3(256), 0, s, a.w0,
-                     a.w0_per_batch, a.H, a.z, Tc, P, rows);
-  e = hipGetLastError();
+  e = launch(chunk_combine_kernel, dim3(a.units, 64 / COMBINE_ROWS), dim3(256), s, a.w0,
+             a.w0_per_batch, a.H, a.z, Tc, P, rows);
   if (e != hipSuccess) return e;
   // every chunk from its start state, with outputs (and the checkpoints,
   // which are laid out per 16-token tile, so chunk u * P + p's are unit u's

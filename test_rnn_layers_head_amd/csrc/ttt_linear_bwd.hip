@@ -480,8 +480,7 @@ __global__ void __launch_bounds__(256) chunk_adjoint_combine_kernel(const float*
 }  // namespace
 
 hipError_t launch_linear_bwd(const LinearBwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(linear_bwd_kernel, dim3(a.units), dim3(BwdGeom::THREADS), 0, s, a);
-  return hipGetLastError();
+  return launch(linear_bwd_kernel, dim3(a.units), dim3(BwdGeom::THREADS), s, a);
 }
 
 hipError_t launch_linear_bwd_chunked(const LinearBwdArgs& a, int P, int rows, hipStream_t s) {
@@ -519,9 +518,8 @@ hipError_t launch_linear_bwd_chunked(const LinearBwdArgs& a, int P, int rows, hi
   c.dw0_stride = Tc * 64;
   e = launch_linear_bwd(c, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(chunk_adjoint_combine_kernel, dim3(a.units, 64 / ACOMB_ROWS), dim3(256), 0, s,
-                     a.dw_T, a.dq, a.dw0, Tc, P);
-  e = hipGetLastError();
+  e = launch(chunk_adjoint_combine_kernel, dim3(a.units, 64 / ACOMB_ROWS), dim3(256), s, a.dw_T,
+             a.dq, a.dw0, Tc, P);
   if (e != hipSuccess) return e;
   // every chunk from its end adjoint (its dq floats 0..4095, read before any
   // of that memory is written: the first tokens' outputs come last)

@@ -622,12 +622,11 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
 hipError_t launch_linear_ln(const LinearLnArgs& a, hipStream_t s) {
   const dim3 grid(a.s.units), block(LnGeom::THREADS);
   switch (a.s.b) {
-    case 16: hipLaunchKernelGGL(linear_ln_scan_kernel<1>, grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL(linear_ln_scan_kernel<2>, grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL(linear_ln_scan_kernel<4>, grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL(linear_ln_scan_kernel<0>, grid, block, 0, s, a); break;
+    case 16: return launch(linear_ln_scan_kernel<1>, grid, block, s, a);
+    case 32: return launch(linear_ln_scan_kernel<2>, grid, block, s, a);
+    case 64: return launch(linear_ln_scan_kernel<4>, grid, block, s, a);
+    default: return launch(linear_ln_scan_kernel<0>, grid, block, s, a);
   }
-  return hipGetLastError();
 }
 
 }  // namespace ttt

@@ -453,11 +453,8 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
 hipError_t launch_mlp(const MlpArgs& a, bool f32in, hipStream_t s) {
   constexpr int NW = 4;
   if (f32in || a.b > 16) return hipErrorNotSupported;
-  if (a.b == 16)
-    hipLaunchKernelGGL((mlp_scan_kernel<2 * NW, false>), dim3(a.units), dim3(2 * NW * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL((mlp_scan_kernel<NW, true>), dim3(a.units), dim3(NW * 64), 0, s, a);
-  return hipGetLastError();
+  if (a.b == 16) return launch(mlp_scan_kernel<2 * NW, false>, dim3(a.units), dim3(2 * NW * 64), s, a);
+  return launch(mlp_scan_kernel<NW, true>, dim3(a.units), dim3(NW * 64), s, a);
 }
 
 }  // namespace ttt

@@ -371,30 +371,19 @@ __global__ void __launch_bounds__(STEP_THREADS) mlp_step_kernel(StepArgs a) {
 }  // namespace
 
 hipError_t launch_linear_step(const StepArgs& a, bool f32in, hipStream_t s) {
-  if (f32in)
-    hipLaunchKernelGGL(linear_step_kernel<true>, dim3(a.units), dim3(STEP_THREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL(linear_step_kernel<false>, dim3(a.units), dim3(STEP_THREADS), 0, s, a);
-  return hipGetLastError();
+  return launch(f32in ? linear_step_kernel<true> : linear_step_kernel<false>, dim3(a.units),
+                dim3(STEP_THREADS), s, a);
 }
 
 hipError_t launch_linear_ln_step(const StepArgs& a, const float* gamma, const float* beta,
                                  float eps, bool f32in, hipStream_t s) {
-  if (f32in)
-    hipLaunchKernelGGL(linear_ln_step_kernel<true>, dim3(a.units), dim3(STEP_THREADS), 0, s, a,
-                       gamma, beta, eps);
-  else
-    hipLaunchKernelGGL(linear_ln_step_kernel<false>, dim3(a.units), dim3(STEP_THREADS), 0, s, a,
-                       gamma, beta, eps);
-  return hipGetLastError();
+  return launch(f32in ? linear_ln_step_kernel<true> : linear_ln_step_kernel<false>, dim3(a.units),
+                dim3(STEP_THREADS), s, a, gamma, beta, eps);
 }
 
 hipError_t launch_mlp_step(const StepArgs& a, bool f32in, hipStream_t s) {
-  if (f32in)
-    hipLaunchKernelGGL(mlp_step_kernel<true>, dim3(a.units), dim3(STEP_THREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL(mlp_step_kernel<false>, dim3(a.units), dim3(STEP_THREADS), 0, s, a);
-  return hipGetLastError();
+  return launch(f32in ? mlp_step_kernel<true> : mlp_step_kernel<false>, dim3(a.units),
+                dim3(STEP_THREADS), s, a);
 }
 
 }  // namespace ttt

@@ -15,9 +15,8 @@ __global__ void copy_state_kernel(const float* __restrict__ src, int per_unit, i
 
 hipError_t launch_copy_state(const float* src, int per_unit, int units, int H, int n, float* dst,
                              hipStream_t s) {
-  hipLaunchKernelGGL(copy_state_kernel, dim3((n + 255) / 256, units), dim3(256), 0, s, src,
-                     per_unit, H, n, dst);
-  return hipGetLastError();
+  return launch(copy_state_kernel, dim3((n + 255) / 256, units), dim3(256), s, src, per_unit, H, n,
+                dst);
 }
 
 __global__ void __launch_bounds__(256) stream_copy_kernel(const uint4* __restrict__ src,
@@ -38,7 +37,7 @@ extern "C" ttt_status_t ttt_bench_copy(const void* src, void* dst, size_t bytes,
   const size_t n = bytes / 16;
   size_t blocks = (n + 255) / 256;
   if (blocks > 256 * 16) blocks = 256 * 16;
-  hipLaunchKernelGGL(ttt::stream_copy_kernel, dim3((unsigned)blocks), dim3(256), 0,
-                     (hipStream_t)stream, (const uint4*)src, (uint4*)dst, n);
-  return hipGetLastError() == hipSuccess ? TTT_OK : TTT_ERR_HIP;
+  const hipError_t e = ttt::launch(ttt::stream_copy_kernel, dim3((unsigned)blocks), dim3(256),
+                                   (hipStream_t)stream, (const uint4*)src, (uint4*)dst, n);
+  return e == hipSuccess ? TTT_OK : TTT_ERR_HIP;
 }

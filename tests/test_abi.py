@@ -294,6 +294,7 @@ def bwd(lib, **kw):
     (dict(dq=A[4]), "TTT_ERR_ALIAS"),          # an output over the checkpoints
     (dict(dw0=A[6] + 256), "TTT_ERR_ALIAS"),    # two outputs
     (dict(dv=A[11], dwT=A[11] + 64), "TTT_ERR_ALIAS"),
+    (dict(B=1, H=1, T=1 << 24), "TTT_ERR_SHAPE"),   # T x 64 fp32 outputs past 32-bit offsets
     (dict(B=0), "TTT_OK"),
 ])
 def test_linear_bwd_argument_checks(lib, kw, expect):
@@ -355,6 +356,7 @@ def bwd_chunked(lib, chunks, **kw):
     (2, dict(b=4), "TTT_ERR_UNSUPPORTED"),
     (2, dict(dq=A[4]), "TTT_ERR_ALIAS"),
     (2, dict(dz=None), "TTT_ERR_NULL"),
+    (2, dict(B=1, H=1, T=1 << 24), "TTT_ERR_SHAPE"),
     (4, dict(B=0), "TTT_OK"),                       # empty work: nothing launched
 ])
 def test_linear_bwd_chunked_argument_checks(lib, chunks, kw, expect):
