@@ -133,6 +133,22 @@ def flushed_launches(launch, reps):
             "p90": float(np.percentile(ks, 90))}
 
 
+def settle(launch, ms):
+    """Clock settle: the same launch back to back for at least `ms` of wall
+    time (synchronising every 10 launches), before any counted warmup.  The
+    first ~10 ms of work on an idle GPU run ~30% slower while its clocks ramp
+    up.  Returns (wall ms spent, launches)."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(10):
+            launch()
+        n += 10
+        torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3, n
+
+
 def time_launches(launch, steps, warmup):
     """Times `steps` back-to-back launches after `warmup` untimed ones, with
     device synchronisation around the timed region and one pair of events
@@ -165,7 +181,7 @@ def time_launches(launch, steps, warmup):
                              "p90": float(np.percentile(ks, 90))}
 
 
-def linear_case(wl, b, steps, warmup, x=None, rows=0, flush_reps=0):
+def linear_case(wl, b, steps, warmup, x=None, rows=0, flush_reps=0, settle_ms=0.0):
     import torch
     from test_rnn_layers_head_amd import ttt_linear_fwd
     from test_rnn_layers_head_amd import inputs
@@ -175,6 +191,7 @@ def linear_case(wl, b, steps, warmup, x=None, rows=0, flush_reps=0):
     w = torch.empty((wl.B, wl.H, wl.d, wl.d), device="cuda")
     launch = lambda: ttt_linear_fwd(d["q"], d["k"], d["v"], d["eta"], d["w0"], b, z=z, w_out=w,
                                     rows_per_workgroup=rows)
+    settled = settle(launch, settle_ms) if settle_ms > 0 else (0.0, 0)
     wall, kmean, spread = time_launches(launch, steps, warmup)
     flushed = flushed_launches(launch, flush_reps) if flush_reps else None
     assert torch.isfinite(z).all().item()
@@ -183,14 +200,25 @@ def linear_case(wl, b, steps, warmup, x=None, rows=0, flush_reps=0):
         "workload": wl.name, "b": b, "token_heads_per_s": wl.token_heads / (wall * 1e-3),
         "ms_per_step": wall, "kernel_us_mean": kmean, "kernel_us_median": spread["median"],
         "kernel_us_p10": spread["p10"], "kernel_us_p90": spread["p90"],
-        "kernel_us_flushed": flushed,
+        "settle_ms": settled[0], "settle_launches": settled[1],
         "alg_bytes": byts, "hbm_GBps": byts / (kmean * 1e-6) / 1e9,
         "hbm_frac": byts / (kmean * 1e-6) / 1e9 / HBM_PEAK_GBS,
         "mfma_frac": linear_alg_flops(wl, b) / (kmean * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
     }
+    if flushed:
+        res.update(flushed_fields(flushed, byts / 1e9 / HBM_PEAK_GBS))
     del d, z, w
     torch.cuda.empty_cache()
     return res
+
+
+def flushed_fields(flushed, t_roof_s):
+    """Scalar fields of a cold-cache timing (median, p10, p90 of single
+    launches, each after a 512 MiB flush) and the roofline fraction of its
+    median, given the kernel's roofline time in seconds."""
+    return {"kernel_us_flushed_median": flushed["median"], "kernel_us_flushed_p10": flushed["p10"],
+            "kernel_us_flushed_p90": flushed["p90"],
+            "frac_flushed": t_roof_s / (flushed["median"] * 1e-6)}
 
 
 def ln_case(wl, b, steps, warmup):
@@ -221,7 +249,7 @@ def ln_case(wl, b, steps, warmup):
     return res
 
 
-def mlp_case(wl, b, steps, warmup):
+def mlp_case(wl, b, steps, warmup, flush_reps=0):
     import torch
     from test_rnn_layers_head_amd import inputs, ttt_mlp_fwd
     x = inputs.make_inputs(wl)
@@ -232,21 +260,36 @@ def mlp_case(wl, b, steps, warmup):
     launch = lambda: ttt_mlp_fwd(d["q"], d["k"], d["v"], d["eta"], d["w1"], d["w2"], b, z=z,
                                  w1_out=w1, w2_out=w2)
     wall, kmean, spread = time_launches(launch, steps, warmup)
+    flushed = flushed_launches(launch, flush_reps) if flush_reps else None
+    assert torch.isfinite(z).all().item()
     kmed = spread["median"]
     byts = mlp_alg_bytes(wl)
     flops = mlp_alg_flops(wl, b)
-    # designed-traffic reading: the 2 x hidden x d fp32 state read and written
-    # once per mini-batch per unit
+    # the kernel keeps both layers resident on chip: its roofline is the
+    # algorithmic one, max(alg. bytes / HBM peak, alg. FLOPs / bf16 MFMA peak)
+    t_roof = max(byts / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12))
+    # secondary reading only: a design that reads and writes the 2 x hidden x
+    # d fp32 state once per mini-batch (which this kernel does not do) would
+    # move these bytes
     designed = byts + wl.units * ((wl.T + b - 1) // b) * 2 * (2 * wl.hidden * wl.d * 4)
     t = kmean * 1e-6
-    return {
+    res = {
         "workload": wl.name, "b": b, "token_heads_per_s": wl.token_heads / (wall * 1e-3),
         "ms_per_step": wall, "kernel_us_mean": kmean, "kernel_us_median": kmed,
+        "kernel_us_p10": spread["p10"], "kernel_us_p90": spread["p90"],
         "alg_bytes": byts, "alg_flops": flops,
+        "roofline_bound": "mfma (algorithmic)" if t_roof > byts / (HBM_PEAK_GBS * 1e9) else "hbm",
+        "roofline_us": t_roof * 1e6, "roofline_frac": t_roof / t,
         "mfma_frac_algorithmic": flops / t / 1e12 / BF16_PEAK_TFLOPS,
         "hbm_frac_algorithmic": byts / t / 1e9 / HBM_PEAK_GBS,
-        "hbm_frac_designed_traffic": designed / t / 1e9 / HBM_PEAK_GBS,
+        "secondary_state_roundtrip_hbm_frac": designed / t / 1e9 / HBM_PEAK_GBS,
+        "traffic": traffic_for("mlp_scan", MLP_SOURCES, wl.name),
     }
+    if flushed:
+        res.update(flushed_fields(flushed, t_roof))
+    del d, z, w1, w2
+    torch.cuda.empty_cache()
+    return res
 
 
 # Decode steps: one token for every (batch, head) unit per call, the states
@@ -483,9 +526,13 @@ def cpu_baseline(x, b, min_seconds=3.0, nthreads=None):
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
             break
+    visible = oracle.host_cores()
     return {"value": calls * x.wl.token_heads / dt, "unit": UNIT, "cores": n, "kind": "oracle",
+            "host_cores_visible": visible,
             "sample": f"all {x.wl.units} (batch, head) units of {x.wl.name}, b={b}, "
-                      f"fp64 sequential primal form, {calls} calls in {dt:.2f} s wall"}
+                      f"fp64 sequential primal form, {calls} calls in {dt:.2f} s wall, "
+                      f"{n} threads ({visible} cores visible to the process; a GPU's share of "
+                      "the host is 16 cores)"}
 
 
 def auto_rows(units: int) -> int:
@@ -612,8 +659,11 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=300,
-                    help="untimed launches first (the clocks settle within ~0.1 s)")
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed launches after the clock-settle phase")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="wall time of back-to-back headline launches before the warmup "
+                         "(an idle GPU's clocks take ~0.1 s to ramp up)")
     ap.add_argument("--no-extras", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--pmc-calibrate", action="store_true",
@@ -668,8 +718,10 @@ def main():
     b = 16
     log(f"[bench] generating {wl.name} inputs")
     x = inputs.make_inputs(wl)
-    log(f"[bench] timing ttt_linear_fwd on {wl.name}: {args.warmup} warmup + {args.steps} steps")
-    head = linear_case(wl, b, args.steps, args.warmup, x=x, flush_reps=0 if args.no_extras else 20)
+    log(f"[bench] timing ttt_linear_fwd on {wl.name}: {args.settle_ms:.0f} ms clock settle, "
+        f"{args.warmup} warmup + {args.steps} steps")
+    head = linear_case(wl, b, args.steps, args.warmup, x=x, flush_reps=0 if args.no_extras else 20,
+                       settle_ms=args.settle_ms)
     log(f"[bench] {head['kernel_us_mean']:.1f} us/launch, {head['hbm_frac']:.3f} of HBM peak")
 
     if args.pmc_calibrate:
@@ -691,7 +743,9 @@ def main():
         for wid in (2, 5):
             w2 = inputs.workload(wid)
             log(f"[bench] {w2.name}")
-            extras[w2.name] = linear_case(w2, 16, max(5, args.steps // 2), EXTRA_WARMUP)
+            # the 125M inputs (128 MB) fit in the 256 MB MALL: also timed cold
+            extras[w2.name] = linear_case(w2, 16, max(5, args.steps // 2), EXTRA_WARMUP,
+                                          flush_reps=10 if wid == 2 else 0)
         for wid in (6, 7):
             w6 = inputs.workload(wid)
             log(f"[bench] {w6.name}")
@@ -711,7 +765,7 @@ def main():
         w4 = inputs.workload(4)
         log(f"[bench] {w4.name}")
         try:
-            extras[w4.name] = mlp_case(w4, 16, max(5, args.steps // 2), EXTRA_WARMUP)
+            extras[w4.name] = mlp_case(w4, 16, max(5, args.steps // 2), EXTRA_WARMUP, flush_reps=10)
         except Exception as e:  # reported, never silently replaced
             extras[w4.name] = {"error": str(e)}
         log("[bench] streaming copy reference")
@@ -736,6 +790,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": head["settle_ms"],
         "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
@@ -753,7 +808,9 @@ def main():
                      "kernel_us_median": head["kernel_us_median"],
                      "kernel_us_p10": head["kernel_us_p10"],
                      "kernel_us_p90": head["kernel_us_p90"],
-                     "kernel_us_flushed": head["kernel_us_flushed"],
+                     "settle_ms": head["settle_ms"], "settle_launches": head["settle_launches"],
+                     **{k: head[k] for k in ("kernel_us_flushed_median", "kernel_us_flushed_p10",
+                                             "kernel_us_flushed_p90", "frac_flushed") if k in head},
                      "mfma_frac": head["mfma_frac"]},
         "cpu_baseline": cpu,
         "extras": extras,

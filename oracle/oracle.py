@@ -81,12 +81,18 @@ def load(path: str | None = None) -> ctypes.CDLL:
     return _lib
 
 
-def default_threads() -> int:
+def host_cores() -> int:
+    """Cores this process may run on (its CPU affinity set)."""
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
+        return os.cpu_count() or 1
+
+
+def default_threads() -> int:
+    """Threads for the oracle: every core of the affinity set, at most 16 (the
+    host share of one GPU on a shared machine)."""
+    return max(1, min(16, host_cores()))
 
 
 def _f64(a) -> np.ndarray:

@@ -18,10 +18,10 @@
 //    ahead.  Buffer range checks zero-fill tokens past T (eta = 0 there, so a
 //    padded token contributes nothing).
 //  * Per 16-token tile each compute wave runs, on MFMA:
-//      P^T = K^T W^T, R^T = Q^T W^T           (64x16x16, W as bf16 hi + lo)
-//      A   = triu(K^T Q)                       (16x16x64, exact bf16 inputs)
+//      P^T = K^T W^T, R^T = Q^T W^T           (64x16x16, fp32 16x16x4 MFMA)
+//      A   = triu(K^T Q)                       (16x16x64, fp32 MFMA)
 //      Gn  = 2 (V - P) diag(eta)               (VALU; "negative gradient")
-//      Z^T = R^T + A^T Gn^T                    (16x16x16, hi/lo split)
+//      Z^T = R^T + A^T Gn^T                    (16x16x16, fp32 MFMA)
 //      W^T += K Gn^T                           (rank-16 update into the fp32
 //                                               accumulator that holds W)
 //    The update's accumulator layout is reused directly as the next tile's
@@ -40,10 +40,10 @@ namespace ttt {
 
 enum { MODE_B16 = 0, MODE_SUB = 1, MODE_MULTI = 2 };
 
-template <bool F32IN, int ROWS>
+template <int ROWS>
 struct LinearGeom {
   static constexpr int NCW = ROWS / 16;          // compute waves
-  static constexpr int ES = F32IN ? 4 : 2;       // bytes per q/k/v element
+  static constexpr int ES = 4;                   // bytes per q/k/v element (fp32)
   static constexpr int KB = 16 * 64 * ES;        // K (or Q) tile bytes
   static constexpr int VB = 16 * ROWS * ES;      // V tile bytes (this slice)
   static constexpr int EB = 64;                  // eta tile bytes
@@ -54,10 +54,10 @@ struct LinearGeom {
   static constexpr int THREADS = (NCW + 1) * 64;
 };
 
-template <bool F32IN, int MODE, int ROWS>
-__global__ void __launch_bounds__((LinearGeom<F32IN, ROWS>::THREADS))
+template <int MODE, int ROWS>
+__global__ void __launch_bounds__((LinearGeom<ROWS>::THREADS))
 linear_scan_kernel(LinearArgs a) {
-  using G = LinearGeom<F32IN, ROWS>;
+  using G = LinearGeom<ROWS>;
   constexpr int NSPLIT = 64 / ROWS;
   __shared__ __attribute__((aligned(16))) char smem[G::NST * G::STAGE];
 
@@ -138,8 +138,7 @@ linear_scan_kernel(LinearArgs a) {
 
   // SUB mode: index of the sub-batch that token 4g+r / token c belongs to.
   const int bsub = a.b;
-  Split8 gp[2];  // MULTI mode: gradient-point operand, fixed over a mini-batch
-  f32x4 gpf[4];  // same, fp32-input path
+  f32x4 gpf[4];  // MULTI mode: the gradient point, fixed over a mini-batch
   const int tiles_per_mb = MODE == MODE_MULTI ? (a.b >> 4) : 1;
 
   float* zu = a.z + (size_t)unit * T * 64;
@@ -157,62 +156,31 @@ linear_scan_kernel(LinearArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int off = (4 * g + r) * ROWS + wave * 16 + c;
-      vv[r] = F32IN ? ((const float*)Vt)[off] : bf16_val(((const short*)Vt)[off]);
+      vv[r] = ((const float*)Vt)[off];
     }
 
     f32x4 P = {0, 0, 0, 0}, R = {0, 0, 0, 0}, A = {0, 0, 0, 0}, M = {0, 0, 0, 0};
-    if constexpr (!F32IN) {
-      // operands of the d-contractions, reduction slot 8g+e <-> column
-      // 32h + 16(e/4) + 4g + (e%4), matching the accumulator layout of W
-      bf16x8 kop[2], qop[2];
+    f32x4 kop[4], qop[4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int o0 = (c * 64 + 32 * h + 4 * g) * 2, o1 = o0 + 32;
-        kop[h] = cat8(*(const uint2*)(Kt + o0), *(const uint2*)(Kt + o1));
-        qop[h] = cat8(*(const uint2*)(Qt + o0), *(const uint2*)(Qt + o1));
+    for (int m = 0; m < 4; ++m) {
+      kop[m] = *(const f32x4*)(Kt + (c * 64 + 16 * m + 4 * g) * 4);
+      qop[m] = *(const f32x4*)(Qt + (c * 64 + 16 * m + 4 * g) * 4);
+    }
+    if constexpr (MODE == MODE_MULTI) {
+      if (j % tiles_per_mb == 0) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) gpf[m] = W[m];
       }
-      Split8 wcur[2];
+    }
 #pragma unroll
-      for (int h = 0; h < 2; ++h) wcur[h] = split8(W[2 * h], W[2 * h + 1]);
-      if constexpr (MODE == MODE_MULTI) {
-        if (j % tiles_per_mb == 0) {
-          gp[0] = wcur[0];
-          gp[1] = wcur[1];
-        }
-      }
+    for (int m = 0; m < 4; ++m) {
+      const f32x4 wp = MODE == MODE_MULTI ? gpf[m] : W[m];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const Split8& wp = MODE == MODE_MULTI ? gp[h] : wcur[h];
-        P = mfma_k32(kop[h], wp.hi, P);
-        P = mfma_k32(kop[h], wp.lo, P);
-        R = mfma_k32(qop[h], wcur[h].hi, R);
-        R = mfma_k32(qop[h], wcur[h].lo, R);
-        A = mfma_k32(kop[h], qop[h], A);
-        if constexpr (MODE == MODE_SUB) M = mfma_k32(kop[h], kop[h], M);
-      }
-    } else {
-      f32x4 kop[4], qop[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        kop[m] = *(const f32x4*)(Kt + (c * 64 + 16 * m + 4 * g) * 4);
-        qop[m] = *(const f32x4*)(Qt + (c * 64 + 16 * m + 4 * g) * 4);
-      }
-      if constexpr (MODE == MODE_MULTI) {
-        if (j % tiles_per_mb == 0) {
-#pragma unroll
-          for (int m = 0; m < 4; ++m) gpf[m] = W[m];
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const f32x4 wp = MODE == MODE_MULTI ? gpf[m] : W[m];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          P = mfma_f32(kop[m][e], wp[e], P);
-          R = mfma_f32(qop[m][e], W[m][e], R);
-          A = mfma_f32(kop[m][e], qop[m][e], A);
-          if constexpr (MODE == MODE_SUB) M = mfma_f32(kop[m][e], kop[m][e], M);
-        }
+      for (int e = 0; e < 4; ++e) {
+        P = mfma_f32(kop[m][e], wp[e], P);
+        R = mfma_f32(qop[m][e], W[m][e], R);
+        A = mfma_f32(kop[m][e], qop[m][e], A);
+        if constexpr (MODE == MODE_SUB) M = mfma_f32(kop[m][e], kop[m][e], M);
       }
     }
 
@@ -238,10 +206,7 @@ linear_scan_kernel(LinearArgs a) {
         I[r] = (s == c) ? 1.f : 0.f;
       }
       const f32x4 Z0 = {0, 0, 0, 0};
-      auto mm = [&](f32x4 xt, f32x4 y) {
-        if constexpr (F32IN) return mm16_f32(xt, y, Z0);
-        else return mm16_split(xt, y, Z0);
-      };
+      auto mm = [&](f32x4 xt, f32x4 y) { return mm16_f32(xt, y, Z0); };
       // U = (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8), cut at N^nblk = 0
       const int nblk = 16 / bsub;
       f32x4 U;
@@ -266,31 +231,17 @@ linear_scan_kernel(LinearArgs a) {
         U = mm(I - NT, tail);
       }
       // G = E U  <=>  G^T = U^T E^T : A-operand = accumulator layout of U
-      if constexpr (F32IN) Gn = mm16_f32(U, Gn, Z0);
-      else Gn = mm16_split(U, Gn, Z0);
+      Gn = mm16_f32(U, Gn, Z0);
     }
 
     // ---- rank-16 update of the resident state and the outputs
     f32x4 Zt = R;
-    if constexpr (!F32IN) {
-      const Split4 gs = split4(Gn);
-      const bf16x8 g2 = cat44(gs.hi, gs.lo);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        s16x4 kt;  // K[t = 4g+e][j = 16m + c]
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) kt[e] = ((const short*)Kt)[(4 * g + e) * 64 + 16 * m + c];
-        W[m] = mfma_k32(cat44(kt, kt), g2, W[m]);  // K (Ghi + Glo)
-      }
-      Zt = mm16_split(A, Gn, Zt);
-    } else {
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          W[m] = mfma_f32(((const float*)Kt)[(4 * g + e) * 64 + 16 * m + c], Gn[e], W[m]);
-      Zt = mm16_f32(A, Gn, Zt);
-    }
+      for (int e = 0; e < 4; ++e)
+        W[m] = mfma_f32(((const float*)Kt)[(4 * g + e) * 64 + 16 * m + c], Gn[e], W[m]);
+    Zt = mm16_f32(A, Gn, Zt);
 
     // Z[t][i]: lane (c,g) holds tokens 16j + 4g + r of row rbase + c
 #pragma unroll
@@ -305,29 +256,29 @@ linear_scan_kernel(LinearArgs a) {
   for (int m = 0; m < 4; ++m) *(f32x4*)(wo + (rbase + c) * 64 + 16 * m + 4 * g) = W[m];
 }
 
-template <bool F32IN, int MODE, int ROWS>
+template <int MODE, int ROWS>
 static hipError_t launch_one(const LinearArgs& a, hipStream_t s) {
-  using G = LinearGeom<F32IN, ROWS>;
+  using G = LinearGeom<ROWS>;
   constexpr int NSPLIT = 64 / ROWS;
   int blocks = NSPLIT == 1 ? a.units : ((a.units + 7) / 8) * 8 * NSPLIT;
-  return launch(linear_scan_kernel<F32IN, MODE, ROWS>, dim3(blocks), dim3(G::THREADS), s, a);
+  return launch(linear_scan_kernel<MODE, ROWS>, dim3(blocks), dim3(G::THREADS), s, a);
 }
 
-template <bool F32IN, int MODE>
+template <int MODE>
 static hipError_t launch_rows(const LinearArgs& a, int rows, hipStream_t s) {
   switch (rows) {
-    case 64: return launch_one<F32IN, MODE, 64>(a, s);
-    case 32: return launch_one<F32IN, MODE, 32>(a, s);
-    default: return launch_one<F32IN, MODE, 16>(a, s);
+    case 64: return launch_one<MODE, 64>(a, s);
+    case 32: return launch_one<MODE, 32>(a, s);
+    default: return launch_one<MODE, 16>(a, s);
   }
 }
 
 hipError_t launch_linear(const LinearArgs& a, bool f32in, int rows, hipStream_t s) {
   if (!f32in) return launch_linear_bf16(a, rows, s);
   const int mode = a.b == 16 ? MODE_B16 : (a.b < 16 ? MODE_SUB : MODE_MULTI);
-  if (mode == MODE_B16) return launch_rows<true, MODE_B16>(a, rows, s);
-  if (mode == MODE_SUB) return launch_rows<true, MODE_SUB>(a, rows, s);
-  return launch_rows<true, MODE_MULTI>(a, rows, s);
+  if (mode == MODE_B16) return launch_rows<MODE_B16>(a, rows, s);
+  if (mode == MODE_SUB) return launch_rows<MODE_SUB>(a, rows, s);
+  return launch_rows<MODE_MULTI>(a, rows, s);
 }
 
 }  // namespace ttt

@@ -46,6 +46,33 @@ def assert_close(got, ref, qkv_dtype, what=""):
     return m
 
 
+def worst_unit(got, ref):
+    """Diagnostic: the (batch, head) unit with the largest relative L2 error."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    g = got.reshape(got.shape[0] * got.shape[1], -1)
+    r = ref.reshape(g.shape)
+    e = np.linalg.norm(g - r, axis=1) / np.maximum(np.linalg.norm(r, axis=1), 1e-300)
+    u = int(np.argmax(e)) if e.size else -1
+    return {"unit": u, "rel_l2": float(e[u]) if e.size else 0.0}
+
+
+def assert_close_all_units(got, ref, qkv_dtype, what=""):
+    """Whole-tensor tolerance check plus the worst unit's error (printed)."""
+    m = assert_close(got, ref, qkv_dtype, what)
+    m["worst_unit"] = worst_unit(got, ref)
+    return m
+
+
+def oracle_units_parallel(fn, n_units, threads=None):
+    """Runs fn(unit_index) for every unit on a thread pool (the oracle's C
+    calls release the GIL) and returns the results in unit order."""
+    from concurrent.futures import ThreadPoolExecutor
+    threads = threads or oracle.default_threads()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        return list(ex.map(fn, range(n_units)))
+
+
 def run_linear(x, b, rows=0):
     from test_rnn_layers_head_amd import ttt_linear_fwd
     z, w = ttt_linear_fwd(dev(x, "q"), dev(x, "k"), dev(x, "v"), f32(x.eta), f32(x.w0), b,

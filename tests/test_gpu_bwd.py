@@ -75,18 +75,23 @@ def test_backward_per_unit_initial_state_and_eta_zero_tokens():
     check(got, ref, "per-unit w0")
 
 
-def test_backward_1p3b_workload_sampled_units():
+def test_backward_1p3b_workload_all_units():
+    """Every unit of the 1.3B workload: the oracle backward runs one unit per
+    call on a thread pool (it keeps all T states of a unit, 268 MB each)."""
     x = inputs.make_inputs(3)
     rng = np.random.default_rng(730)
     dz = (rng.standard_normal(x.q.shape) * 0.1).astype(np.float32)
     _, _, _, got = run_fwd_bwd(x, dz)
-    idx = [5, 100]
-    sub = x.units(idx)
-    dzs = dz.reshape(-1, x.wl.T, 64)[idx][None]
-    ref = oracle.linear_bwd(sub.q, sub.k, sub.v, sub.eta, sub.w0, 16, dzs)
-    pick = lambda a: a.reshape(-1, *a.shape[2:])[idx][None]
-    check([pick(a) for a in got], ref, "1.3B")
     assert all(np.isfinite(a).all() for a in got)
+    dzu = dz.reshape(-1, x.wl.T, 64)
+
+    def one(u):
+        s = x.units([u])
+        return oracle.linear_bwd(s.q, s.k, s.v, s.eta, s.w0, 16, dzu[u][None, None])
+
+    per = gu.oracle_units_parallel(one, x.wl.units)
+    ref = [np.concatenate([p[i] for p in per], axis=1).reshape(got[i].shape) for i in range(5)]
+    check(got, ref, "1.3B")
 
 
 def test_backward_empty_sequence_and_rejected_arguments():

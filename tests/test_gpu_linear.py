@@ -2,8 +2,10 @@
 
 Sizes: small cases span several 16-token tiles and a ragged tail for every
 supported mini-batch shape; the full workloads run on the GPU at their real
-size and launch shape and are compared on sampled (batch, head) units that
-the oracle recomputes from scratch.
+size and launch shape and are compared with the oracle element by element
+over every (batch, head) unit (the worst unit is printed as a diagnostic).
+Edge cases of the method: Theorem 1 ("论文速览 | TTT" §4.1: W0 = 0, eta = 1/2,
+b = T is causal linear attention) and eta = 0 (Z = W0 Q, W_T = W0).
 """
 import numpy as np
 import pytest
@@ -54,30 +56,55 @@ def big():
 
 
 @pytest.mark.parametrize("b", [1, 4, 16, 64])
-def test_1p3b_workload_sampled_units(big, b):
+def test_1p3b_workload_all_units(big, b):
     x = big
     z, w = gu.run_linear(x, b)
-    idx = [0, 37, 77, 127]
-    sub = x.units(idx)
-    zr, wr = gu.oracle_linear(sub, b)
-    zs = z.reshape(-1, x.wl.T, 64)[idx][None]
-    ws = w.reshape(-1, 64, 64)[idx][None]
-    print(f"1.3B b={b} z:", gu.assert_close(zs, zr, "bf16", "z"),
-          "w:", gu.assert_close(ws, wr, "bf16", "w"))
     assert np.isfinite(z).all()
+    zr, wr = gu.oracle_linear(x, b)
+    print(f"1.3B b={b} z:", gu.assert_close_all_units(z, zr, "bf16", "z"),
+          "w:", gu.assert_close_all_units(w, wr, "bf16", "w"))
 
 
-def test_longctx_workload_sampled_units():
+def test_longctx_workload_all_units():
+    """The long-context workload in one pass (seq_chunks = 1; the automatic
+    choice, chunked, is tested in test_gpu_chunked.py)."""
     x = inputs.make_inputs(5)
-    z, w = gu.run_linear(x, 16)
-    idx = [3, 30]
-    zr, wr = gu.oracle_linear(x.units(idx), 16)
-    zs = z.reshape(-1, x.wl.T, 64)[idx][None]
-    ws = w.reshape(-1, 64, 64)[idx][None]
-    print("long-ctx z:", gu.assert_close(zs, zr, "bf16", "z"),
-          "w:", gu.assert_close(ws, wr, "bf16", "w"))
+    q, k, v = (gu.dev(x, n) for n in "qkv")
+    z, w = ttt_linear_fwd(q, k, v, gu.f32(x.eta), gu.f32(x.w0), 16, seq_chunks=1)
+    torch.cuda.synchronize()
+    z, w = z.cpu().numpy(), w.cpu().numpy()
+    zr, wr = gu.oracle_linear(x, 16)
+    print("long-ctx z:", gu.assert_close_all_units(z, zr, "bf16", "z"),
+          "w:", gu.assert_close_all_units(w, wr, "bf16", "w"))
     # error must not grow along the sequence: compare the last 2k tokens alone
-    gu.assert_close(zs[:, :, -2048:], zr[:, :, -2048:], "bf16", "z tail")
+    gu.assert_close(z[:, :, -2048:], zr[:, :, -2048:], "bf16", "z tail")
+
+
+@pytest.mark.parametrize("b", [16, 64])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_theorem1_causal_linear_attention(dtype, b):
+    """W0 = 0, eta = 1/2, one mini-batch of T = b tokens: z_t = sum_{s<=t}
+    v_s k_s^T q_t and W_T = sum_s v_s k_s^T, evaluated directly in fp64 from
+    the same (rounded) inputs."""
+    x = small(2, 3, b, dtype, seed=60 + b)
+    x.eta[:] = 0.5
+    x.w0[:] = 0.0
+    z, w = gu.run_linear(x, b)
+    S = np.einsum("bhti,bhtj->bhtij", x.v.astype(np.float64), x.k.astype(np.float64)).cumsum(axis=2)
+    zt = np.einsum("bhtij,bhtj->bhti", S, x.q.astype(np.float64))
+    gu.assert_close(z, zt, dtype, "z")
+    gu.assert_close(w, S[:, :, -1], dtype, "w_T")
+
+
+@pytest.mark.parametrize("b", [1, 4, 16, 64])
+def test_eta_zero_leaves_state(b):
+    """eta = 0: every update vanishes, so W_T = W0 exactly and Z = W0 Q."""
+    x = small(2, 3, 77, "bf16", seed=70 + b)
+    x.eta[:] = 0.0
+    z, w = gu.run_linear(x, b)
+    assert np.array_equal(w, np.broadcast_to(x.w0, w.shape))
+    zr = np.einsum("hij,bhtj->bhti", x.w0.astype(np.float64), x.q.astype(np.float64))
+    gu.assert_close(z, zr, "bf16", "z")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
