@@ -9,10 +9,13 @@ terms (~2^-24 relative, i.e. fp32 level) and the output products in two
 (its loss ignores a common shift of W's rows and, up to eps, W's scale, and
 rows with large gamma come to dominate a token's variance), so a plain fp32
 evaluation of the same method, one token at a time, already differs from
-the fp64 oracle by up to ~1e-3 of the RMS after 8k tokens.  Bounds:
+the fp64 oracle after 8k tokens: over all 128 units of the 1.3B workload it
+reaches max|diff| / RMS = 1.9e-2 (units 83 and 51; rel-L2 3.5e-5).  Bounds:
   * up to 2k tokens: rel-L2 <= 1e-4 and max|diff| / RMS <= 1e-3;
-  * the 8k-token workload: the bf16-input bound of the plain scan,
-    rel-L2 <= 2e-3 and max|diff| / RMS <= 1e-2.
+  * the 8k-token workload: rel-L2 <= 2e-3 (the bf16-input bound of the plain
+    scan) and max|diff| / RMS <= max(1e-2, 1.5 x the fp32 floor), the floor
+    being the max|diff| / RMS that ``fp32_reference`` (a plain fp32 numpy
+    evaluation of the method, computed in the test) reaches on the same inputs.
 """
 import numpy as np
 import pytest
@@ -30,6 +33,39 @@ def close(got, ref, what, rel=TOL_REL, mx=TOL_MAX):
     m = gu.metrics(got, ref)
     assert m["rel_l2"] <= rel and m["max_over_rms"] <= mx, (what, m)
     return m
+
+
+def fp32_reference(x, b=16):
+    """The LayerNorm scan evaluated in plain fp32 numpy, token by token, batched
+    over units: each token's gradient at the mini-batch-start state, the LN VJP,
+    the update, then the output from the updated state ("论文速览 | TTT" §3.5,
+    §4.4).  It measures what fp32 arithmetic alone costs on this recurrence; the
+    reference values are still the fp64 oracle's."""
+    B, H, T, d = x.q.shape
+    U, f = B * H, np.float32
+    q, k, v = (a.reshape(U, T, d).astype(f) for a in (x.q, x.k, x.v))
+    eta = x.eta.reshape(U, T).astype(f)
+    gam = np.tile(x.ln_gamma, (B, 1)).astype(f)
+    bet = np.tile(x.ln_beta, (B, 1)).astype(f)
+    eps = f(x.wl.ln_eps)
+    W = np.broadcast_to(x.w0, (B, H, d, d)).reshape(U, d, d).astype(f).copy()
+    z = np.zeros((U, T, d), f)
+
+    def ln(y):
+        yc = y - y.mean(axis=1, keepdims=True)
+        rs = f(1) / np.sqrt((yc * yc).mean(axis=1, keepdims=True) + eps)
+        return yc * rs, rs
+
+    for m0 in range(0, T, b):
+        Ws = W.copy()
+        for t in range(m0, min(T, m0 + b)):
+            kt, vt, qt = k[:, t], v[:, t], q[:, t]
+            yh, rs = ln(np.einsum("uij,uj->ui", Ws, kt))
+            g = f(2) * gam * (kt + gam * yh + bet - vt)
+            dy = rs * (g - g.mean(axis=1, keepdims=True) - yh * (g * yh).mean(axis=1, keepdims=True))
+            W -= (eta[:, t][:, None, None] * dy[:, :, None]) * kt[:, None, :]
+            z[:, t] = qt + gam * ln(np.einsum("uij,uj->ui", W, qt))[0] + bet
+    return z.reshape(B, H, T, d), W.reshape(B, H, d, d)
 
 
 def small(B, H, T, seed):
@@ -99,9 +135,13 @@ def test_1p3b_ln_workload_all_units():
     z, w = gu.run_linear_ln(x, 16)
     assert np.isfinite(z).all() and np.isfinite(w).all()
     zr, wr = gu.oracle_linear_ln(x, 16)
-    loose = dict(rel=gu.TOL_BF16_REL, mx=gu.TOL_BF16_MAX)
-    print("LN 1.3B z:", close(z, zr, "z", **loose), gu.worst_unit(z, zr),
-          "w:", close(w, wr, "w", **loose), gu.worst_unit(w, wr))
+    z32, w32 = fp32_reference(x)
+    fz, fw = gu.metrics(z32, zr), gu.metrics(w32, wr)
+    print("fp32 floor z:", fz, "w:", fw)
+    print("LN 1.3B z:", close(z, zr, "z", rel=gu.TOL_BF16_REL,
+                              mx=max(gu.TOL_BF16_MAX, 1.5 * fz["max_over_rms"])), gu.worst_unit(z, zr),
+          "w:", close(w, wr, "w", rel=gu.TOL_BF16_REL,
+                      mx=max(gu.TOL_BF16_MAX, 1.5 * fw["max_over_rms"])), gu.worst_unit(w, wr))
 
 
 def test_rejected_arguments():
