@@ -45,7 +45,7 @@
  * Support:   d = 64; any 0 <= T < 2^24, B, H >= 0 with B*H*T*d < 2^31.
  *            TTT-Linear: fp32 or bf16 q/k/v; mini-batch b with b | 16 or
  *            16 | b (1, 2, 4, 8, 16, 32, 48, 64, ...).
- *            TTT-MLP: hidden = 256, bf16 q/k/v, b | 16 (1, 2, 4, 8, 16).
+ *            TTT-MLP: hidden = 256, fp32 or bf16 q/k/v, b | 16 or 16 | b.
  *            TTT-Linear with LayerNorm: bf16 q/k/v, 16 | b.
  *            Anything else is TTT_ERR_UNSUPPORTED.
  *            Empty work (B*H == 0) returns TTT_OK without launching; T == 0
@@ -247,8 +247,16 @@ ttt_status_t ttt_mlp_step(const void* q, const void* k, const void* v,
  *   w1_out, w2_out : out [B][H][hidden][d], [B][H][d][hidden] fp32
  *
  * Both layers take their gradient of sum_t eta_t ||f(k_t) - v_t||^2 at the
- * state before the mini-batch.  GELU is x * Phi(x); on the device erf is the
- * Abramowitz & Stegun 7.1.26 approximation (absolute error <= 1.5e-7).
+ * state before the mini-batch (§3.5).  GELU is x * Phi(x).
+ *
+ * Two kernels serve the call.  bf16 q/k/v with b | 16 (1, 2, 4, 8, 16): the
+ * dual form per 16-token tile, state resident in registers, products on
+ * bf16 MFMA with fp32 operands split into bf16 hi + lo, erf from
+ * Abramowitz & Stegun 7.1.26 (absolute error <= 1.5e-7).  fp32 q/k/v, or
+ * b a multiple of 16 above 16: the primal form token by token in fp32
+ * arithmetic (the library's erff), one workgroup of 1024 threads per
+ * (batch, head) with the state and the gradient point in registers; exact
+ * but about 10x slower per token, meant for parity and for long mini-batches.
  */
 ttt_status_t ttt_mlp_fwd(const void* q, const void* k, const void* v,
                          const float* eta, const float* w1_0,

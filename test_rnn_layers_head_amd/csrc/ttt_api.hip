@@ -389,10 +389,6 @@ ttt_status_t mlp_impl(const void* q, const void* k, const void* v, const float* 
   if (st != TTT_OK) return st;
   if (hidden != 256)
     return fail(TTT_ERR_UNSUPPORTED, "%s: hidden=%d unsupported (only 256)", fn, hidden);
-  if (qkv_dtype != TTT_BF16)
-    return fail(TTT_ERR_UNSUPPORTED, "%s: only bf16 q/k/v are supported", fn);
-  if (b > 16)
-    return fail(TTT_ERR_UNSUPPORTED, "%s: mini-batch b=%d unsupported (need b | 16)", fn, b);
   if (units == 0 || dry) return TTT_OK;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;

@@ -177,6 +177,8 @@ hipError_t launch_linear_chunked(const LinearArgs& a, int P, int rows, hipStream
 hipError_t launch_linear_bf16(const LinearArgs& a, int rows, hipStream_t s);
 hipError_t launch_linear_ln(const LinearLnArgs& a, hipStream_t s);
 hipError_t launch_mlp(const MlpArgs& a, bool f32in, hipStream_t s);
+// The TTT-MLP scan token by token in fp32 (any b >= 1, fp32 or bf16 q/k/v).
+hipError_t launch_mlp_primal(const MlpArgs& a, bool f32in, hipStream_t s);
 hipError_t launch_linear_step(const StepArgs& a, bool f32in, hipStream_t s);
 hipError_t launch_linear_ln_step(const StepArgs& a, const float* gamma, const float* beta,
                                  float eps, bool f32in, hipStream_t s);

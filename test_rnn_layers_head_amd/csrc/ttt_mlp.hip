@@ -452,7 +452,8 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
 
 hipError_t launch_mlp(const MlpArgs& a, bool f32in, hipStream_t s) {
   constexpr int NW = 4;
-  if (f32in || a.b > 16) return hipErrorNotSupported;
+  // fp32 inputs and mini-batches spanning several tiles: the primal kernel
+  if (f32in || a.b > 16) return launch_mlp_primal(a, f32in, s);
   if (a.b == 16) return launch(mlp_scan_kernel<2 * NW, false>, dim3(a.units), dim3(2 * NW * 64), s, a);
   return launch(mlp_scan_kernel<NW, true>, dim3(a.units), dim3(NW * 64), s, a);
 }

@@ -190,8 +190,9 @@ def test_mlp_argument_checks(lib):
                                      kw.get("hidden", 256), kw.get("b", 16),
                                      kw.get("dt", _lib.TTT_BF16), A[5], A[6], A[10], None)
     assert f(hidden=128) == status("TTT_ERR_UNSUPPORTED")
-    assert f(b=32) == status("TTT_ERR_UNSUPPORTED")
-    assert f(dt=_lib.TTT_F32) == status("TTT_ERR_UNSUPPORTED")
+    assert f(b=24) == status("TTT_ERR_UNSUPPORTED")  # neither b | 16 nor 16 | b
+    assert f(b=3) == status("TTT_ERR_UNSUPPORTED")
+    assert f(dt=7) == status("TTT_ERR_DTYPE")
     assert f(hidden=-1) == status("TTT_ERR_SHAPE")
 
 
