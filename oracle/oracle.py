@@ -61,6 +61,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.ttt_oracle_linear_bwd.argtypes = [dp, dp, dp, dp, dp, I, L, L, L, L, L, dp, dp, dp, dp, dp,
                                           dp, dp]
     lib.ttt_oracle_linear_bwd.restype = I
+    lib.ttt_oracle_mlp_bwd.argtypes = [dp, dp, dp, dp, dp, dp, I, L, L, L, L, L, L, dp, dp, dp,
+                                       dp, dp, dp, dp, dp, dp]
+    lib.ttt_oracle_mlp_bwd.restype = I
     lib.ttt_oracle_lr_gate.argtypes = [dp, dp, D, L, L, L, L, dp]
     lib.ttt_oracle_lr_gate.restype = I
     lib.ttt_oracle_lr_gate_bwd.argtypes = [dp, dp, D, dp, L, L, L, L, dp, dp]
@@ -268,6 +271,33 @@ def linear_bwd(q, k, v, eta, w0, b: int, dz, dw_T=None, lib=None):
     if rc != 0:
         raise RuntimeError(f"ttt_oracle_linear_bwd failed with status {rc}")
     return dq, dk, dv, deta, dw0
+
+
+def mlp_bwd(q, k, v, eta, w1_0, w2_0, b: int, dz, dw1_T=None, dw2_T=None, lib=None):
+    """Backward of the TTT-MLP scan (reverse pass of the primal form): given
+    dz [B, H, T, d] and optionally the adjoints of the final states dw1_T
+    [B, H, hidden, d], dw2_T [B, H, d, hidden], returns (dq, dk, dv, deta,
+    dw1_0, dw2_0) with the initial-state adjoints per unit."""
+    q, k, v, eta, w1_0, w2_0, dz = map(_f64, (q, k, v, eta, w1_0, w2_0, dz))
+    B, H, T, d = q.shape
+    per_batch = 1 if w1_0.ndim == 4 else 0
+    hidden = w1_0.shape[-2]
+    assert w1_0.shape == ((B, H, hidden, d) if per_batch else (H, hidden, d))
+    assert w2_0.shape == ((B, H, d, hidden) if per_batch else (H, d, hidden)) and dz.shape == q.shape
+    d1 = None if dw1_T is None else _f64(dw1_T)
+    d2 = None if dw2_T is None else _f64(dw2_T)
+    dq, dk, dv = (np.zeros((B, H, T, d)) for _ in range(3))
+    deta = np.zeros((B, H, T))
+    dw1 = np.zeros((B, H, hidden, d))
+    dw2 = np.zeros((B, H, d, hidden))
+    lib = lib or load()
+    rc = lib.ttt_oracle_mlp_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w1_0), _ptr(w2_0),
+                                per_batch, B, H, T, d, hidden, int(b), _ptr(dz),
+                                None if d1 is None else _ptr(d1), None if d2 is None else _ptr(d2),
+                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(deta), _ptr(dw1), _ptr(dw2))
+    if rc != 0:
+        raise RuntimeError(f"ttt_oracle_mlp_bwd failed with status {rc}")
+    return dq, dk, dv, deta, dw1, dw2
 
 
 def lr_gate(x, theta_lr, eta_base: float, lib=None):

@@ -38,8 +38,8 @@
  * output is read from the updated W: exactly one iteration of the scans above.
  *
  * Backward (§6.12: training differentiates through the inner loop): the
- * reverse pass of the TTT-Linear primal recurrence above, token by token in
- * reverse, given the adjoints of Z and of the final state.  It keeps every
+ * reverse pass of the TTT-Linear and TTT-MLP primal recurrences above, token
+ * by token in reverse, given the adjoints of Z and of the final state.  It keeps every
  * intermediate state, which is fine at test sizes (the pages' kernels keep
  * one per mini-batch and recompute; that is a memory trade, not another
  * result).
@@ -616,6 +616,226 @@ int ttt_oracle_linear_bwd(const double *q, const double *k, const double *v,
                              w0 + (size_t)wsel * (size_t)(d * d), T, d, b, dz + so,
                              dwT ? dwT + (size_t)u * (size_t)(d * d) : NULL, dq + so, dk + so,
                              dv + so, deta + (size_t)u * (size_t)T, dw0 + (size_t)u * (size_t)(d * d));
+    if (rc) return rc;
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* TTT-MLP backward: reverse pass of the primal recurrence.            */
+/* ------------------------------------------------------------------ */
+/* d^2/dx^2 [x Phi(x)] = 2 phi(x) + x phi'(x) = phi(x) (2 - x^2) */
+static double gelu_grad2(double x) {
+  const double pi = 3.14159265358979323846;
+  return exp(-0.5 * x * x) / sqrt(2.0 * pi) * (2.0 - x * x);
+}
+
+/* Forward, one unit (as mlp_unit), keeping every state: S1[t], S2[t] are W1,
+ * W2 after t tokens; token t of the mini-batch starting at m0 takes
+ *   a = S1[m0] k_t, x = GELU(a), e = 2 (S2[m0] x - v_t),
+ *   s = S2[m0]^T e, delta = s * GELU'(a),
+ *   S1[t+1] = S1[t] - eta_t delta k_t^T,  S2[t+1] = S2[t] - eta_t e x^T,
+ *   z_t = S2[t+1] GELU(S1[t+1] q_t).
+ * Reverse, with A1, A2 the adjoints of the state after token t (starting
+ * from those of the final state) and G1, G2 the adjoints collected for the
+ * current mini-batch's gradient point (S1[m0], S2[m0]); for token t:
+ *   output:  aq = S1[t+1] q, xq = GELU(aq); A2 += dz xq^T;
+ *            daq = (S2[t+1]^T dz) * GELU'(aq); A1 += daq q^T;
+ *            dq = S1[t+1]^T daq;
+ *   update:  ddelta = -eta A1 k, dk = -eta A1^T delta, de = -eta A2 x,
+ *            dx = -eta A2^T e, deta = -delta^T A1 k - e^T A2 x;
+ *   delta:   ds = ddelta * GELU'(a), da = ddelta * s * GELU''(a);
+ *   s:       G2 += e ds^T, de += S2[m0] ds;
+ *   e:       dv = -2 de;  y = S2[m0] x:  G2 += 2 de x^T, dx += 2 S2[m0]^T de;
+ *   x:       da += dx * GELU'(a);
+ *   a:       G1 += da k^T, dk += S1[m0]^T da;
+ *   at t = m0: A1 += G1, A2 += G2, G1 = G2 = 0.
+ * The adjoints then carry over unchanged to the state before token t. */
+static int mlp_bwd_unit(const double *q, const double *k, const double *v, const double *eta,
+                        const double *w1_0, const double *w2_0, long T, long d, long hd, long b,
+                        const double *dz, const double *dw1T, const double *dw2T, double *dq,
+                        double *dk, double *dv, double *deta, double *dw1_0, double *dw2_0) {
+  const size_t n = (size_t)(hd * d);
+  double *S1 = (double *)malloc(sizeof(double) * n * (size_t)(T + 1));
+  double *S2 = (double *)malloc(sizeof(double) * n * (size_t)(T + 1));
+  double *G1 = (double *)calloc(n, sizeof(double));
+  double *G2 = (double *)calloc(n, sizeof(double));
+  double *vec = (double *)malloc(sizeof(double) * (size_t)(11 * hd + 2 * d));
+  if (!S1 || !S2 || !G1 || !G2 || !vec) {
+    free(S1); free(S2); free(G1); free(G2); free(vec);
+    return 1;
+  }
+  double *a = vec, *x = a + hd, *s = x + hd, *dl = s + hd, *aq = dl + hd, *xq = aq + hd;
+  double *daq = xq + hd, *ddl = daq + hd, *ds = ddl + hd, *da = ds + hd, *dx = da + hd;
+  double *e = dx + hd, *de = e + d;
+  memcpy(S1, w1_0, sizeof(double) * n);
+  memcpy(S2, w2_0, sizeof(double) * n);
+  /* forward, keeping every state */
+  for (long t = 0; t < T; ++t) {
+    const long m0 = (t / b) * b;
+    const double *P1 = S1 + (size_t)m0 * n, *P2 = S2 + (size_t)m0 * n;
+    const double *C1 = S1 + (size_t)t * n, *C2 = S2 + (size_t)t * n;
+    double *N1 = S1 + (size_t)(t + 1) * n, *N2 = S2 + (size_t)(t + 1) * n;
+    const double *kt = k + t * d, *vt = v + t * d;
+    for (long u = 0; u < hd; ++u) {
+      double acc = 0.0;
+      for (long j = 0; j < d; ++j) acc += P1[u * d + j] * kt[j];
+      a[u] = acc;
+      x[u] = gelu(acc);
+    }
+    for (long i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (long u = 0; u < hd; ++u) acc += P2[i * hd + u] * x[u];
+      e[i] = 2.0 * (acc - vt[i]);
+    }
+    for (long u = 0; u < hd; ++u) {
+      double acc = 0.0;
+      for (long i = 0; i < d; ++i) acc += P2[i * hd + u] * e[i];
+      dl[u] = acc * gelu_grad(a[u]);
+    }
+    for (long i = 0; i < d; ++i)
+      for (long u = 0; u < hd; ++u) N2[i * hd + u] = C2[i * hd + u] - eta[t] * e[i] * x[u];
+    for (long u = 0; u < hd; ++u)
+      for (long j = 0; j < d; ++j) N1[u * d + j] = C1[u * d + j] - eta[t] * dl[u] * kt[j];
+  }
+  /* reverse */
+  double *A1 = dw1_0, *A2 = dw2_0; /* the running adjoints live in the outputs */
+  if (dw1T) memcpy(A1, dw1T, sizeof(double) * n);
+  else memset(A1, 0, sizeof(double) * n);
+  if (dw2T) memcpy(A2, dw2T, sizeof(double) * n);
+  else memset(A2, 0, sizeof(double) * n);
+  for (long t = T - 1; t >= 0; --t) {
+    const long m0 = (t / b) * b;
+    const double *P1 = S1 + (size_t)m0 * n, *P2 = S2 + (size_t)m0 * n;
+    const double *N1 = S1 + (size_t)(t + 1) * n, *N2 = S2 + (size_t)(t + 1) * n;
+    const double *kt = k + t * d, *vt = v + t * d, *qt = q + t * d, *zt = dz + t * d;
+    const double et = eta[t];
+    /* forward quantities of token t at the gradient point */
+    for (long u = 0; u < hd; ++u) {
+      double acc = 0.0;
+      for (long j = 0; j < d; ++j) acc += P1[u * d + j] * kt[j];
+      a[u] = acc;
+      x[u] = gelu(acc);
+    }
+    for (long i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (long u = 0; u < hd; ++u) acc += P2[i * hd + u] * x[u];
+      e[i] = 2.0 * (acc - vt[i]);
+    }
+    for (long u = 0; u < hd; ++u) {
+      double acc = 0.0;
+      for (long i = 0; i < d; ++i) acc += P2[i * hd + u] * e[i];
+      s[u] = acc;
+      dl[u] = acc * gelu_grad(a[u]);
+    }
+    /* output z_t = N2 GELU(N1 q_t) */
+    for (long u = 0; u < hd; ++u) {
+      double acc = 0.0;
+      for (long j = 0; j < d; ++j) acc += N1[u * d + j] * qt[j];
+      aq[u] = acc;
+      xq[u] = gelu(acc);
+    }
+    for (long i = 0; i < d; ++i)
+      for (long u = 0; u < hd; ++u) A2[i * hd + u] += zt[i] * xq[u];
+    for (long u = 0; u < hd; ++u) {
+      double acc = 0.0;
+      for (long i = 0; i < d; ++i) acc += N2[i * hd + u] * zt[i];
+      daq[u] = acc * gelu_grad(aq[u]);
+    }
+    for (long u = 0; u < hd; ++u)
+      for (long j = 0; j < d; ++j) A1[u * d + j] += daq[u] * qt[j];
+    for (long j = 0; j < d; ++j) {
+      double acc = 0.0;
+      for (long u = 0; u < hd; ++u) acc += N1[u * d + j] * daq[u];
+      dq[t * d + j] = acc;
+    }
+    /* the updates N1 = S1[t] - eta delta k^T, N2 = S2[t] - eta e x^T */
+    double dsum = 0.0;
+    for (long u = 0; u < hd; ++u) {
+      double acc = 0.0;
+      for (long j = 0; j < d; ++j) acc += A1[u * d + j] * kt[j];
+      ddl[u] = -et * acc;
+      dsum -= dl[u] * acc;
+    }
+    for (long j = 0; j < d; ++j) {
+      double acc = 0.0;
+      for (long u = 0; u < hd; ++u) acc += A1[u * d + j] * dl[u];
+      dk[t * d + j] = -et * acc;
+    }
+    for (long i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (long u = 0; u < hd; ++u) acc += A2[i * hd + u] * x[u];
+      de[i] = -et * acc;
+      dsum -= e[i] * acc;
+    }
+    for (long u = 0; u < hd; ++u) {
+      double acc = 0.0;
+      for (long i = 0; i < d; ++i) acc += A2[i * hd + u] * e[i];
+      dx[u] = -et * acc;
+    }
+    deta[t] = dsum;
+    /* delta = s * GELU'(a) */
+    for (long u = 0; u < hd; ++u) {
+      ds[u] = ddl[u] * gelu_grad(a[u]);
+      da[u] = ddl[u] * s[u] * gelu_grad2(a[u]);
+    }
+    /* s = P2^T e */
+    for (long i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (long u = 0; u < hd; ++u) {
+        G2[i * hd + u] += e[i] * ds[u];
+        acc += P2[i * hd + u] * ds[u];
+      }
+      de[i] += acc;
+    }
+    /* e = 2 (y - v), y = P2 x */
+    for (long i = 0; i < d; ++i) {
+      dv[t * d + i] = -2.0 * de[i];
+      for (long u = 0; u < hd; ++u) G2[i * hd + u] += 2.0 * de[i] * x[u];
+    }
+    for (long u = 0; u < hd; ++u) {
+      double acc = 0.0;
+      for (long i = 0; i < d; ++i) acc += P2[i * hd + u] * de[i];
+      dx[u] += 2.0 * acc;
+    }
+    /* x = GELU(a), a = P1 k */
+    for (long u = 0; u < hd; ++u) {
+      da[u] += dx[u] * gelu_grad(a[u]);
+      for (long j = 0; j < d; ++j) G1[u * d + j] += da[u] * kt[j];
+    }
+    for (long j = 0; j < d; ++j) {
+      double acc = 0.0;
+      for (long u = 0; u < hd; ++u) acc += P1[u * d + j] * da[u];
+      dk[t * d + j] += acc;
+    }
+    if (t == m0) { /* the gradient point of this mini-batch is the state before t */
+      for (size_t i = 0; i < n; ++i) {
+        A1[i] += G1[i];
+        A2[i] += G2[i];
+        G1[i] = 0.0;
+        G2[i] = 0.0;
+      }
+    }
+  }
+  free(S1); free(S2); free(G1); free(G2); free(vec);
+  return 0;
+}
+
+int ttt_oracle_mlp_bwd(const double *q, const double *k, const double *v, const double *eta,
+                       const double *w1_0, const double *w2_0, int w0_per_batch, long B, long H,
+                       long T, long d, long hd, long b, const double *dz, const double *dw1T,
+                       const double *dw2T, double *dq, double *dk, double *dv, double *deta,
+                       double *dw1_0, double *dw2_0) {
+  if (B < 0 || H < 0 || T < 0 || d <= 0 || hd <= 0 || b <= 0) return 2;
+  const size_t n = (size_t)(hd * d);
+  for (long u = 0; u < B * H; ++u) {
+    const long wsel = w0_per_batch ? u : u % H;
+    const size_t so = (size_t)u * (size_t)(T * d);
+    int rc = mlp_bwd_unit(q + so, k + so, v + so, eta + (size_t)u * (size_t)T,
+                          w1_0 + (size_t)wsel * n, w2_0 + (size_t)wsel * n, T, d, hd, b, dz + so,
+                          dw1T ? dw1T + (size_t)u * n : NULL, dw2T ? dw2T + (size_t)u * n : NULL,
+                          dq + so, dk + so, dv + so, deta + (size_t)u * (size_t)T,
+                          dw1_0 + (size_t)u * n, dw2_0 + (size_t)u * n);
     if (rc) return rc;
   }
   return 0;

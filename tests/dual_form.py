@@ -192,3 +192,33 @@ def linear_bwd(q, k, v, eta, w0, b, dz, dwT=None):
             for o, x in zip(out, r):
                 o[bi, h] = x
     return tuple(out)
+
+
+def mlp_unit_torch(q, k, v, eta, w1, w2, b):
+    """The MLP dual form of mlp_unit in float64 torch, differentiable: one
+    unit, q, k, v [T, d], eta [T], w1 [h, d], w2 [d, h] (torch tensors).
+    Per mini-batch (columns are tokens, "论文速览 | TTT" §3.7): Z1 = W1 K,
+    X2 = GELU(Z1), Z2 = W2 X2, G2 = 2 (Z2 - V) diag(eta),
+    G1 = (W2^T G2) * GELU'(Z1), Z1q = W1 Q - G1 triu(K^T Q), X2q = GELU(Z1q),
+    Z = W2 X2q - G2 triu(X2^T X2q), W1 -= G1 K^T, W2 -= G2 X2^T."""
+    import torch
+    c = 1.0 / np.sqrt(2.0)
+    gel = lambda x: 0.5 * x * (1.0 + torch.erf(x * c))
+    gel_d = lambda x: 0.5 * (1.0 + torch.erf(x * c)) + x * torch.exp(-0.5 * x * x) / np.sqrt(2.0 * np.pi)
+    T = q.shape[0]
+    W1, W2 = w1, w2
+    outs = []
+    for m0 in range(0, T, b):
+        m1 = min(T, m0 + b)
+        XK, XV, XQ = k[m0:m1].T, v[m0:m1].T, q[m0:m1].T
+        e = eta[m0:m1]
+        Z1 = W1 @ XK
+        X2 = gel(Z1)
+        G2 = 2.0 * (W2 @ X2 - XV) * e[None, :]
+        G1 = (W2.T @ G2) * gel_d(Z1)
+        Z1q = W1 @ XQ - G1 @ torch.triu(XK.T @ XQ)
+        X2q = gel(Z1q)
+        outs.append((W2 @ X2q - G2 @ torch.triu(X2.T @ X2q)).T)
+        W1 = W1 - G1 @ XK.T
+        W2 = W2 - G2 @ X2.T
+    return torch.cat(outs, dim=0), W1, W2

@@ -30,6 +30,10 @@ Time): RNNs with Expressive Hidden States"):
   saturation at eta_base, each at its own (batch, head, token); its
   backward (dtheta_lr, dx from deta) against central finite differences of
   sum deta * eta, and the closed form at theta_lr = 0 (sigmoid' = 1/4);
+* the TTT-MLP backward (§6.12): central finite differences of
+  <dZ, Z> + <dW1_T, W1_T> + <dW2_T, W2_T> through the forward oracle, torch's
+  float64 autodiff of the independently written dual form, and the eta = 0
+  closed forms (the state never moves);
 * invariants: homogeneity, superposition, row permutation, state passing,
   thread-count determinism.
 
@@ -563,6 +567,78 @@ _GATE_LOGITS = {0.0: 0.5, np.log(3.0): 0.75, -np.log(3.0): 0.25, np.log(7.0): 0.
                 -np.log(7.0): 0.125, 60.0: 1.0, -60.0: 0.0}
 
 
+def _mlp_bwd_case(rng, T, d, hd, with_dwT=True):
+    q, k, v, eta, w1, w2 = rand_mlp(rng, 1, 2, T, d, hd, eta_scale=0.5, w_scale=0.5)
+    dz = rng.standard_normal(q.shape)
+    d1 = rng.standard_normal((1, 2, hd, d)) if with_dwT else None
+    d2 = rng.standard_normal((1, 2, d, hd)) if with_dwT else None
+    return q, k, v, eta, w1, w2, dz, d1, d2
+
+
+def pin_mlp_bwd_finite_differences(lib):
+    """The MLP backward against central finite differences of
+    L = <dZ, Z> + <dW1_T, W1_T> + <dW2_T, W2_T> through the forward oracle,
+    along a random direction of every input ("论文速览 | TTT" §6.12)."""
+    rng = np.random.default_rng(41)
+    for (T, b, with_dwT) in [(7, 3, True), (6, 1, True), (5, 8, False), (9, 9, True)]:
+        q, k, v, eta, w1, w2, dz, d1, d2 = _mlp_bwd_case(rng, T, 3, 5, with_dwT)
+        g = oracle.mlp_bwd(q, k, v, eta, w1, w2, b, dz, d1, d2, lib=lib)
+        base = dict(q=q, k=k, v=v, eta=eta, w1=w1, w2=w2)
+
+        def L(**kw):
+            a = dict(base, **kw)
+            z, s1, s2 = oracle.mlp(a["q"], a["k"], a["v"], a["eta"], a["w1"], a["w2"], b, lib=lib)
+            out = np.sum(dz * z)
+            if with_dwT:
+                out += np.sum(d1 * s1) + np.sum(d2 * s2)
+            return out
+
+        h = 1e-5
+        grads = dict(q=g[0], k=g[1], v=g[2], eta=g[3], w1=g[4].sum(axis=0), w2=g[5].sum(axis=0))
+        for name, arr in base.items():
+            D = rng.standard_normal(arr.shape)
+            fd = (L(**{name: arr + h * D}) - L(**{name: arr - h * D})) / (2 * h)
+            an = float(np.sum(grads[name] * D))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (name, T, b, fd, an)
+
+
+def pin_mlp_bwd_equals_autograd_of_dual_form(lib):
+    """The MLP backward equals torch's reverse-mode autodiff (float64) of the
+    independently written dual form (tests/dual_form.py, §3.7)."""
+    import torch
+    rng = np.random.default_rng(42)
+    for (T, b) in [(9, 4), (8, 8), (5, 1), (11, 16)]:
+        q, k, v, eta, w1, w2, dz, d1, d2 = _mlp_bwd_case(rng, T, 4, 6)
+        g = oracle.mlp_bwd(q, k, v, eta, w1, w2, b, dz, d1, d2, lib=lib)
+        for h in range(2):
+            leaves = [torch.tensor(a, dtype=torch.float64, requires_grad=True)
+                      for a in (q[0, h], k[0, h], v[0, h], eta[0, h], w1[h], w2[h])]
+            z, s1, s2 = dual_form.mlp_unit_torch(*leaves, b)
+            tot = ((z * torch.from_numpy(dz[0, h])).sum() + (s1 * torch.from_numpy(d1[0, h])).sum()
+                   + (s2 * torch.from_numpy(d2[0, h])).sum())
+            tot.backward()
+            for i, leaf in enumerate(leaves):
+                assert rel(g[i][0, h], leaf.grad.numpy()) < 1e-11, (T, b, h, i)
+
+
+def pin_mlp_bwd_eta_zero(lib):
+    """eta = 0: the state never moves, so z_t = W2_0 GELU(W1_0 q_t) and the
+    adjoints are closed forms: dk = dv = 0, dq_t = W1_0^T (GELU'(W1_0 q_t) *
+    W2_0^T dz_t), dW2_0 = dW2_T + sum_t dz_t GELU(W1_0 q_t)^T,
+    dW1_0 = dW1_T + sum_t (GELU'(W1_0 q_t) * W2_0^T dz_t) q_t^T."""
+    rng = np.random.default_rng(43)
+    q, k, v, eta, w1, w2, dz, d1, d2 = _mlp_bwd_case(rng, 13, 4, 6)
+    eta[:] = 0.0
+    g = oracle.mlp_bwd(q, k, v, eta, w1, w2, 4, dz, d1, d2, lib=lib)
+    assert not g[1].any() and not g[2].any()
+    for h in range(2):
+        aq = q[0, h] @ w1[h].T                                   # [T, hd]
+        daq = dual_form.gelu_grad(aq) * (dz[0, h] @ w2[h])       # [T, hd]
+        assert rel(g[0][0, h], daq @ w1[h]) < 1e-13
+        assert rel(g[5][0, h], d2[0, h] + dz[0, h].T @ dual_form.gelu(aq)) < 1e-13
+        assert rel(g[4][0, h], d1[0, h] + daq.T @ q[0, h]) < 1e-13
+
+
 def pin_gate_closed_forms(lib):
     # theta_lr[h] = c_h e_{p(h)} puts the logit c_h x[b, t, p(h)] at every
     # (b, h, t) on its own; each logit is drawn from the closed-form table, so
@@ -662,6 +738,9 @@ PINS = [
     pin_linear_bwd_finite_differences,
     pin_linear_bwd_equals_dual_form_adjoint,
     pin_linear_bwd_eta_zero,
+    pin_mlp_bwd_finite_differences,
+    pin_mlp_bwd_equals_autograd_of_dual_form,
+    pin_mlp_bwd_eta_zero,
     pin_gate_closed_forms,
     pin_gate_bwd_finite_differences,
     pin_gate_bwd_zero_vector,
@@ -907,6 +986,17 @@ MUTATIONS = {
     "gate_bwd_dx_from_head_0": ("gx[i] += da * th[i];", "gx[i] += da * theta[i];"),
     "gate_bwd_dtheta_from_first_token": ("+= da * xt[i];", "+= da * x[i];"),
     "gate_bwd_no_base": ("deta[gi] * eta_base * sg", "deta[gi] * sg"),
+    "mlp_bwd_drop_gelu_second_derivative": ("da[u] = ddl[u] * s[u] * gelu_grad2(a[u]);",
+                                            "da[u] = 0.0;"),
+    "mlp_bwd_gelu_second_derivative_form": ("* (2.0 - x * x);", "* (1.0 - x * x);"),
+    "mlp_bwd_gradient_point_adjoint_dropped": ("        A1[i] += G1[i];\n        A2[i] += G2[i];\n", ""),
+    "mlp_bwd_dk_through_current_state": ("for (long u = 0; u < hd; ++u) acc += P1[u * d + j] * da[u];",
+                                         "for (long u = 0; u < hd; ++u) acc += N1[u * d + j] * da[u];"),
+    "mlp_bwd_dq_through_start_state": ("for (long u = 0; u < hd; ++u) acc += N1[u * d + j] * daq[u];",
+                                       "for (long u = 0; u < hd; ++u) acc += P1[u * d + j] * daq[u];"),
+    "mlp_bwd_eta_sign": ("    deta[t] = dsum;", "    deta[t] = -dsum;"),
+    "mlp_bwd_dv_sign": ("dv[t * d + i] = -2.0 * de[i];", "dv[t * d + i] = 2.0 * de[i];"),
+    "mlp_bwd_y_adjoint_factor": ("G2[i * hd + u] += 2.0 * de[i] * x[u];", "G2[i * hd + u] += de[i] * x[u];"),
     "bwd_output_adjoint_dropped": ("A[i * d + j] += zt[i] * qt[j];\n    /* W_t",
                                    "A[i * d + j] += 0.0 * zt[i] * qt[j];\n    /* W_t"),
 }
