@@ -71,10 +71,15 @@ typedef enum {
   TTT_ERR_ALIAS = 5,       /* an output overlaps an input (see Aliasing)    */
   TTT_ERR_HIP = 6,         /* the HIP runtime reported an error             */
   TTT_ERR_ALIGN = 7,       /* a tensor pointer is not 16-byte aligned       */
-  TTT_ERR_VALUE = 8        /* a scalar argument is out of range             */
+  TTT_ERR_VALUE = 8,       /* a scalar argument is out of range             */
+  /* not a status: makes every int32 a valid value of the type, so that a
+     caller's out-of-range value reaches ttt_status_str well defined */
+  TTT_STATUS_MAX_ENUM = 0x7fffffff
 } ttt_status_t;
 
-typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype_t;
+/* TTT_DTYPE_MAX_ENUM is not a dtype; it widens the type to every int32, so an
+   unknown value from a caller is rejected as TTT_ERR_DTYPE, well defined. */
+typedef enum { TTT_F32 = 0, TTT_BF16 = 1, TTT_DTYPE_MAX_ENUM = 0x7fffffff } ttt_dtype_t;
 
 /*
  * TTT-Linear forward scan, f(x) = W x (§3.6 dual form, §4.4).
@@ -264,6 +269,49 @@ ttt_status_t ttt_mlp_fwd(const void* q, const void* k, const void* v,
                          int32_t H, int32_t T, int32_t d, int32_t hidden,
                          int32_t b, ttt_dtype_t qkv_dtype, float* z,
                          float* w1_out, float* w2_out, void* stream);
+
+/*
+ * Training support for TTT-MLP (§6.12, as for TTT-Linear above; §3.7, §4.4).
+ * Support: d = 64, hidden = 256, fp32 or bf16 q/k/v, b | 16 or 16 | b.
+ *
+ * ttt_mlp_fwd_ckpt: ttt_mlp_fwd plus
+ *   w1_ckpt : out [B][H][ceil(T/b)][hidden][d] fp32, W1 before each
+ *             mini-batch of b tokens (w1_ckpt[..][0] = W1_0);
+ *   w2_ckpt : out [B][H][ceil(T/b)][d][hidden] fp32, the same for W2.
+ * It runs the primal-form kernel (one token at a time, fp32 arithmetic).
+ *
+ * ttt_mlp_bwd: the gradient of a loss L(Z, W1_T, W2_T) with respect to the
+ * scan's inputs, given
+ *   dz             : [B][H][T][d] fp32, dL/dZ
+ *   dw1_T, dw2_T   : [B][H][hidden][d], [B][H][d][hidden] fp32 or NULL (zero)
+ *   q, k, v, eta   : the forward's inputs; w1_ckpt, w2_ckpt from
+ *                    ttt_mlp_fwd_ckpt with the same b
+ * and writing (fp32)
+ *   dq, dk, dv : [B][H][T][d];  deta : [B][H][T]
+ *   dw1_0, dw2_0 : [B][H][hidden][d], [B][H][d][hidden], per unit.
+ * The mini-batches are walked in reverse.  Each is replayed forward from its
+ * checkpoint, then its tokens are taken back one by one; both passes run in
+ * fp32.  The gradient-point adjoints of a mini-batch join the state adjoints
+ * at its first token.  Outputs must not overlap each other or an input.
+ * T = 0 writes dw*_0 = dw*_T (or zeros).  One workgroup of 512 threads per
+ * (batch, head).  Besides the outputs, the kernel uses only its own LDS and
+ * the per-thread register spill space the compiler assigns.
+ */
+ttt_status_t ttt_mlp_fwd_ckpt(const void* q, const void* k, const void* v,
+                              const float* eta, const float* w1_0,
+                              const float* w2_0, int32_t w0_per_batch, int32_t B,
+                              int32_t H, int32_t T, int32_t d, int32_t hidden,
+                              int32_t b, ttt_dtype_t qkv_dtype, float* z,
+                              float* w1_out, float* w2_out, float* w1_ckpt,
+                              float* w2_ckpt, void* stream);
+ttt_status_t ttt_mlp_bwd(const void* q, const void* k, const void* v,
+                         const float* eta, const float* w1_ckpt,
+                         const float* w2_ckpt, int32_t B, int32_t H, int32_t T,
+                         int32_t d, int32_t hidden, int32_t b,
+                         ttt_dtype_t qkv_dtype, const float* dz,
+                         const float* dw1_T, const float* dw2_T, float* dq,
+                         float* dk, float* dv, float* deta, float* dw1_0,
+                         float* dw2_0, void* stream);
 
 /*
  * Learnable inner learning rate (§4.6): the step size of token t in head h

@@ -52,6 +52,10 @@ SIGNATURES = {
                             _i32, _i32, _vp, _vp]),
     "ttt_mlp_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                            _i32, _vp, _vp, _vp, _vp]),
+    "ttt_mlp_fwd_ckpt": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "ttt_mlp_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "ttt_status_str": (ctypes.c_char_p, [_i32]),
     "ttt_last_error": (ctypes.c_char_p, []),
     "ttt_abi_version": (_i32, []),

@@ -301,6 +301,66 @@ def ttt_mlp_fwd(q, k, v, eta, w1_0, w2_0, b: int, z=None, w1_out=None, w2_out=No
     return z, w1_out, w2_out
 
 
+def ttt_mlp_fwd_ckpt(q, k, v, eta, w1_0, w2_0, b: int, z=None, w1_out=None, w2_out=None,
+                     w1_ckpt=None, w2_ckpt=None, stream=None):
+    """ttt_mlp_fwd that also keeps both layers' state before every mini-batch
+    of b tokens (include/ttt.h).  Returns (z, w1_out, w2_out, w1_ckpt,
+    w2_ckpt) with w1_ckpt [B, H, ceil(T/b), hidden, d] and w2_ckpt
+    [B, H, ceil(T/b), d, hidden], fp32."""
+    B, H, T, d = q.shape
+    hidden = w1_0.shape[-2]
+    nmb = (T + b - 1) // b if b > 0 else 0
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=q.device)
+    z = f32(B, H, T, d) if z is None else z
+    w1_out = f32(B, H, hidden, d) if w1_out is None else w1_out
+    w2_out = f32(B, H, d, hidden) if w2_out is None else w2_out
+    w1_ckpt = f32(B, H, nmb, hidden, d) if w1_ckpt is None else w1_ckpt
+    w2_ckpt = f32(B, H, nmb, d, hidden) if w2_ckpt is None else w2_ckpt
+    dev = _check_tensors(dict(q=q, k=k, v=v, eta=eta, w1_0=w1_0, w2_0=w2_0, z=z, w1_out=w1_out,
+                              w2_out=w2_out, w1_ckpt=w1_ckpt, w2_ckpt=w2_ckpt))
+    for name, t in (("eta", eta), ("w1_0", w1_0), ("w2_0", w2_0), ("z", z), ("w1_out", w1_out),
+                    ("w2_out", w2_out), ("w1_ckpt", w1_ckpt), ("w2_ckpt", w2_ckpt)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if tuple(w1_ckpt.shape) != (B, H, nmb, hidden, d) or tuple(w2_ckpt.shape) != (B, H, nmb, d, hidden):
+        raise ValueError("w1_ckpt / w2_ckpt must be [B, H, ceil(T/b), hidden, d] / [.., d, hidden]")
+    per_batch = 1 if w1_0.dim() == 4 else 0
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib().ttt_mlp_fwd_ckpt(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w1_0), _ptr(w2_0), per_batch, B, H, T, d,
+            hidden, int(b), _dtype_code(q), _ptr(z), _ptr(w1_out), _ptr(w2_out), _ptr(w1_ckpt),
+            _ptr(w2_ckpt), _stream(dev, stream)))
+    return z, w1_out, w2_out, w1_ckpt, w2_ckpt
+
+
+def ttt_mlp_bwd(q, k, v, eta, w1_ckpt, w2_ckpt, b: int, dz, dw1_T=None, dw2_T=None, stream=None):
+    """Backward of the TTT-MLP scan (include/ttt.h): given dz = dL/dZ and
+    optionally the adjoints of the final states, returns (dq, dk, dv, deta,
+    dw1_0, dw2_0), fp32, with the initial-state adjoints per unit.  The
+    checkpoints come from ttt_mlp_fwd_ckpt with the same b."""
+    B, H, T, d = q.shape
+    hidden = w1_ckpt.shape[-2]
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=q.device)
+    dq, dk, dv, deta = f32(B, H, T, d), f32(B, H, T, d), f32(B, H, T, d), f32(B, H, T)
+    dw1, dw2 = f32(B, H, hidden, d), f32(B, H, d, hidden)
+    dev = _check_tensors(dict(q=q, k=k, v=v, eta=eta, w1_ckpt=w1_ckpt, w2_ckpt=w2_ckpt, dz=dz,
+                              dw1_T=dw1_T, dw2_T=dw2_T))
+    for name, t in (("dz", dz), ("dw1_T", dw1_T), ("dw2_T", dw2_T), ("w1_ckpt", w1_ckpt),
+                    ("w2_ckpt", w2_ckpt), ("eta", eta)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if tuple(dz.shape) != (B, H, T, d):
+        raise ValueError("dz must be [B, H, T, d]")
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib().ttt_mlp_bwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w1_ckpt), _ptr(w2_ckpt), B, H, T, d, hidden,
+            int(b), _dtype_code(q), _ptr(dz), _ptr(dw1_T), _ptr(dw2_T), _ptr(dq), _ptr(dk), _ptr(dv),
+            _ptr(deta), _ptr(dw1), _ptr(dw2), _stream(dev, stream)))
+    return dq, dk, dv, deta, dw1, dw2
+
+
 def _gate_common(x, theta_lr, H_expected, eta):
     if x.dim() != 3:
         raise ValueError("x must be [B, T, dx]")

@@ -372,7 +372,8 @@ ttt_status_t mlp_impl(const void* q, const void* k, const void* v, const float* 
                       const float* w1_0, const float* w2_0, int32_t w0_per_batch, int32_t B,
                       int32_t H, int32_t T, int32_t d, int32_t hidden, int32_t b,
                       ttt_dtype_t qkv_dtype, float* z, float* w1_out, float* w2_out, void* stream,
-                      const char* fn = "ttt_mlp_fwd", bool dry = false) {
+                      const char* fn = "ttt_mlp_fwd", bool dry = false, float* w1_ckpt = nullptr,
+                      float* w2_ckpt = nullptr) {
   if (hidden < 0) return fail(TTT_ERR_SHAPE, "%s: negative hidden=%d", fn, hidden);
   const int64_t units = (int64_t)B * H;
   const int64_t es = qkv_dtype == TTT_F32 ? 4 : 2;
@@ -381,11 +382,16 @@ ttt_status_t mlp_impl(const void* q, const void* k, const void* v, const float* 
   const Range in[] = {rng("q", q, seq * es), rng("k", k, seq * es), rng("v", v, seq * es),
                       rng("eta", eta, units * T * 4), rng("w1_0", w1_0, wn),
                       rng("w2_0", w2_0, wn)};
+  const int64_t nck = b > 0 ? units * ((T + b - 1) / b) * hidden * d * 4 : 0;
   const Range out[] = {rng("z", z, seq * 4), rng("w1_out", w1_out, units * hidden * d * 4),
-                       rng("w2_out", w2_out, units * hidden * d * 4)};
+                       rng("w2_out", w2_out, units * hidden * d * 4),
+                       rng("w1_ckpt", w1_ckpt, nck), rng("w2_ckpt", w2_ckpt, nck)};
   const int pairs[][2] = {{4, 1}, {5, 2}};
-  ttt_status_t st =
-      check_common(fn, qkv_dtype, w0_per_batch, B, H, T, d, b, in, 6, out, 3, pairs, 2, T > 0);
+  const bool ck = w1_ckpt != nullptr || w2_ckpt != nullptr;
+  if (ck && (!w1_ckpt || !w2_ckpt) && T > 0)
+    return fail(TTT_ERR_NULL, "%s: w1_ckpt and w2_ckpt must both be given", fn);
+  ttt_status_t st = check_common(fn, qkv_dtype, w0_per_batch, B, H, T, d, b, in, 6, out,
+                                 ck && T > 0 ? 5 : 3, pairs, 2, T > 0);
   if (st != TTT_OK) return st;
   if (hidden != 256)
     return fail(TTT_ERR_UNSUPPORTED, "%s: hidden=%d unsupported (only 256)", fn, hidden);
@@ -398,9 +404,66 @@ ttt_status_t mlp_impl(const void* q, const void* k, const void* v, const float* 
     if (e == hipSuccess && !(w0_per_batch && w2_0 == w2_out))
       e = ttt::launch_copy_state(w2_0, w0_per_batch, (int)units, H, hidden * d, w2_out, s);
   } else {
-    ttt::MlpArgs a{q, k, v, eta, w1_0, w2_0, z, w1_out, w2_out, w0_per_batch, (int)units, H, T, b};
-    e = ttt::launch_mlp(a, qkv_dtype == TTT_F32, s);
+    ttt::MlpArgs a{q, k, v, eta, w1_0, w2_0, z, w1_out, w2_out, w0_per_batch, (int)units, H, T, b,
+                   w1_ckpt, w2_ckpt};
+    e = ck ? ttt::launch_mlp_primal(a, qkv_dtype == TTT_F32, s)
+           : ttt::launch_mlp(a, qkv_dtype == TTT_F32, s);
   }
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return TTT_OK;
+}
+
+ttt_status_t mlp_bwd_impl(const void* q, const void* k, const void* v, const float* eta,
+                          const float* w1_ckpt, const float* w2_ckpt, int32_t B, int32_t H,
+                          int32_t T, int32_t d, int32_t hidden, int32_t b, ttt_dtype_t dt,
+                          const float* dz, const float* dw1_T, const float* dw2_T, float* dq,
+                          float* dk, float* dv, float* deta, float* dw1_0, float* dw2_0,
+                          void* stream) {
+  static const char* fn = "ttt_mlp_bwd";
+  if (dt != TTT_F32 && dt != TTT_BF16) return fail(TTT_ERR_DTYPE, "%s: unknown qkv_dtype %d", fn, (int)dt);
+  if (B < 0 || H < 0 || T < 0 || d < 0 || b < 0 || hidden < 0)
+    return fail(TTT_ERR_SHAPE, "%s: negative size (B=%d H=%d T=%d d=%d hidden=%d b=%d)", fn, B, H, T,
+                d, hidden, b);
+  if (d != 64) return fail(TTT_ERR_UNSUPPORTED, "%s: head dim d=%d unsupported (only 64)", fn, d);
+  if (hidden != 256)
+    return fail(TTT_ERR_UNSUPPORTED, "%s: hidden=%d unsupported (only 256)", fn, hidden);
+  if (!supported_b(b))
+    return fail(TTT_ERR_UNSUPPORTED, "%s: mini-batch b=%d unsupported (need b | 16 or 16 | b)", fn, b);
+  const int64_t units = (int64_t)B * H;
+  const int64_t seq = units * T * d;
+  if (seq >= ((int64_t)1 << 31))
+    return fail(TTT_ERR_SHAPE, "%s: B*H*T*d = %lld exceeds 2^31 - 1", fn, (long long)seq);
+  if (T >= (1 << 24)) return fail(TTT_ERR_SHAPE, "%s: T = %d exceeds 2^24 - 1", fn, T);
+  if (units == 0) return TTT_OK;
+  const int64_t es = dt == TTT_F32 ? 4 : 2;
+  const int64_t nst = units * hidden * d * 4;
+  const int64_t nck = units * ((T + b - 1) / b) * hidden * d * 4;
+  const Range in[] = {rng("q", q, seq * es), rng("k", k, seq * es), rng("v", v, seq * es),
+                      rng("eta", eta, units * T * 4), rng("w1_ckpt", w1_ckpt, nck),
+                      rng("w2_ckpt", w2_ckpt, nck), rng("dz", dz, seq * 4),
+                      rng("dw1_T", dw1_T, nst), rng("dw2_T", dw2_T, nst)};
+  const Range out[] = {rng("dq", dq, seq * 4), rng("dk", dk, seq * 4), rng("dv", dv, seq * 4),
+                       rng("deta", deta, units * T * 4), rng("dw1_0", dw1_0, nst),
+                       rng("dw2_0", dw2_0, nst)};
+  for (int i = 0; i < 9; ++i) {
+    if ((i < 7 && T == 0) || (i == 7 && !dw1_T) || (i == 8 && !dw2_T)) continue;
+    if (!in[i].lo) return fail(TTT_ERR_NULL, "%s: %s is NULL", fn, in[i].name);
+    if (in[i].lo & 15) return fail(TTT_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, in[i].name);
+  }
+  for (int o = 0; o < 6; ++o) {
+    if (o < 4 && T == 0) continue;
+    if (!out[o].lo) return fail(TTT_ERR_NULL, "%s: %s is NULL", fn, out[o].name);
+    if (out[o].lo & 15) return fail(TTT_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, out[o].name);
+    for (int i = 0; i < 9; ++i)
+      if (overlap(out[o], in[i]))
+        return fail(TTT_ERR_ALIAS, "%s: %s overlaps input %s", fn, out[o].name, in[i].name);
+    for (int o2 = o + 1; o2 < 6; ++o2)
+      if (overlap(out[o], out[o2]))
+        return fail(TTT_ERR_ALIAS, "%s: %s and %s overlap", fn, out[o].name, out[o2].name);
+  }
+  ttt::MlpBwdArgs a{q,  k,  v,  eta,  w1_ckpt, w2_ckpt, dz, dw1_T, dw2_T, dq, dk, dv, deta, dw1_0,
+                    dw2_0, (int)units, T, b};
+  const hipError_t e = ttt::launch_mlp_bwd(a, dt == TTT_F32, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return TTT_OK;
 }
@@ -570,6 +633,27 @@ ttt_status_t ttt_linear_ln_fwd(const void* q, const void* k, const void* v, cons
                         qkv_dtype, z, w_out, stream);
 }
 
+ttt_status_t ttt_mlp_fwd_ckpt(const void* q, const void* k, const void* v, const float* eta,
+                              const float* w1_0, const float* w2_0, int32_t w0_per_batch,
+                              int32_t B, int32_t H, int32_t T, int32_t d, int32_t hidden,
+                              int32_t b, ttt_dtype_t qkv_dtype, float* z, float* w1_out,
+                              float* w2_out, float* w1_ckpt, float* w2_ckpt, void* stream) {
+  if (T > 0 && (!w1_ckpt || !w2_ckpt))
+    return fail(TTT_ERR_NULL, "ttt_mlp_fwd_ckpt: w1_ckpt and w2_ckpt are required");
+  return mlp_impl(q, k, v, eta, w1_0, w2_0, w0_per_batch, B, H, T, d, hidden, b, qkv_dtype, z,
+                  w1_out, w2_out, stream, "ttt_mlp_fwd_ckpt", false, w1_ckpt, w2_ckpt);
+}
+
+ttt_status_t ttt_mlp_bwd(const void* q, const void* k, const void* v, const float* eta,
+                         const float* w1_ckpt, const float* w2_ckpt, int32_t B, int32_t H,
+                         int32_t T, int32_t d, int32_t hidden, int32_t b, ttt_dtype_t qkv_dtype,
+                         const float* dz, const float* dw1_T, const float* dw2_T, float* dq,
+                         float* dk, float* dv, float* deta, float* dw1_0, float* dw2_0,
+                         void* stream) {
+  return mlp_bwd_impl(q, k, v, eta, w1_ckpt, w2_ckpt, B, H, T, d, hidden, b, qkv_dtype, dz, dw1_T,
+                      dw2_T, dq, dk, dv, deta, dw1_0, dw2_0, stream);
+}
+
 ttt_status_t ttt_mlp_fwd(const void* q, const void* k, const void* v, const float* eta,
                          const float* w1_0, const float* w2_0, int32_t w0_per_batch, int32_t B,
                          int32_t H, int32_t T, int32_t d, int32_t hidden, int32_t b,
@@ -704,6 +788,7 @@ const char* ttt_status_str(ttt_status_t s) {
     case TTT_ERR_HIP: return "TTT_ERR_HIP: HIP runtime error";
     case TTT_ERR_ALIGN: return "TTT_ERR_ALIGN: pointer not 16-byte aligned";
     case TTT_ERR_VALUE: return "TTT_ERR_VALUE: scalar argument out of range";
+    case TTT_STATUS_MAX_ENUM: break;
   }
   return "unknown ttt_status_t";
 }

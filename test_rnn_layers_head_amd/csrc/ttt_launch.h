@@ -86,7 +86,34 @@ struct MlpArgs {
   int H;
   int T;
   int b;
+  // optional: the state at the start of every mini-batch,
+  // [units][ceil(T / b)][256][64] and [units][ceil(T / b)][64][256]
+  float* w1_ckpt = nullptr;
+  float* w2_ckpt = nullptr;
 };
+
+// Backward of the TTT-MLP scan (hidden = 256, any b, fp32 or bf16 q/k/v).
+struct MlpBwdArgs {
+  const void* q;          // [units][T][64]
+  const void* k;
+  const void* v;
+  const float* eta;       // [units][T]
+  const float* w1_ckpt;   // [units][ceil(T/b)][256][64]: W1 at every mini-batch start
+  const float* w2_ckpt;   // [units][ceil(T/b)][64][256]
+  const float* dz;        // [units][T][64]
+  const float* dw1_T;     // [units][256][64] or NULL
+  const float* dw2_T;     // [units][64][256] or NULL
+  float* dq;              // [units][T][64]
+  float* dk;
+  float* dv;
+  float* deta;            // [units][T]
+  float* dw1_0;           // [units][256][64]
+  float* dw2_0;           // [units][64][256]
+  int units;
+  int T;
+  int b;
+};
+hipError_t launch_mlp_bwd(const MlpBwdArgs& a, bool f32in, hipStream_t s);
 
 // Backward of the TTT-Linear scan (b = 16, bf16 q/k/v).
 struct LinearBwdArgs {

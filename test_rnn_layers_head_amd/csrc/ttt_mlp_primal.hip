@@ -124,6 +124,14 @@ __global__ void __launch_bounds__(PTHREADS) mlp_primal_kernel(MlpArgs a) {
           w1g[i] = w1[i];
           w2g[i] = w2[i];
         }
+        if (a.w1_ckpt) {  // the state before mini-batch tt / b
+          const size_t co = ((size_t)unit * ((T + b - 1) / b) + tt / b) * PHID * 64;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            a.w1_ckpt[co + u * 64 + j0 + i] = w1[i];
+            a.w2_ckpt[co + (j0 + i) * PHID + u] = w2[i];
+          }
+        }
       }
       // forward at the gradient point
       float acc = 0.f;
@@ -202,7 +210,294 @@ __global__ void __launch_bounds__(PTHREADS) mlp_primal_kernel(MlpArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Backward ("论文速览 | TTT" §6.12: the outer loop differentiates through the
+// inner loop; the forward keeps the state at every mini-batch start).  The
+// mini-batches are walked in reverse.  For mini-batch m the kernel loads its
+// checkpoint (the gradient point of all its tokens), replays its tokens
+// forward to the state at its end, then walks its tokens backwards; each step
+// takes back its token's update exactly as the forward made it, to recover
+// the state before the token.  Per token t (reverse), with A1, A2 the
+// adjoints of the state after t and G1, G2 those of the gradient point:
+//   output:  aq = W1 q, xq = GELU(aq), A2 += dz xq^T,
+//            daq = (W2^T dz) * GELU'(aq), A1 += daq q^T, dq = W1^T daq;
+//   update:  ddelta = -eta A1 k, dk = -eta A1^T delta, de = -eta A2 x,
+//            dx = -eta A2^T e, deta = -delta^T A1 k - e^T A2 x;
+//   delta = s * GELU'(a): ds = ddelta GELU'(a), da = ddelta s GELU''(a);
+//   s = W2g^T e: G2 += e ds^T, de += W2g ds;
+//   e = 2 (W2g x - v): dv = -2 de, G2 += 2 de x^T, dx += 2 W2g^T de;
+//   x = GELU(a), a = W1g k: da += dx GELU'(a), G1 += da k^T, dk += W1g^T da;
+//   at the mini-batch's first token: A += G, G = 0.
+// Thread layout: 512 threads (8 waves); thread (wave v, lane l) owns hidden
+// unit u = 32 v + (l % 32) and the half j in [32 hf, 32 hf + 32), hf = l / 32,
+// of the 64 components, for the state, its adjoint and the gradient-point
+// adjoint (96 registers); the gradient point sits in LDS, each thread's 64
+// values in a private, bank-conflict-free slot.
+constexpr int BTHREADS = 512;
+constexpr int BSTRIDE = 4 * 64 + 1;  // floats per staged token: k, v, q, dz, eta
+
+// Sum over the 32 lanes of a half wave (two DPP rows).
+__device__ __forceinline__ float half_sum32(float v) { return row_sum16(v) + __shfl_xor(row_sum16(v), 16); }
+
+template <bool F32IN>
+__global__ void __launch_bounds__(BTHREADS) mlp_primal_bwd_kernel(MlpBwdArgs a) {
+  __shared__ f32x4 wg1s[8][8][64];   // gradient point W1g[u][j0 + 4c + r] at [wave][c][lane]
+  __shared__ f32x4 wg2s[8][8][64];   // W2g[j0 + 4c + r][u]
+  __shared__ float tok[2][BSTRIDE];  // the current and the next step's token
+  __shared__ float red_y[8][64], red_q[8][64], red_e[8][64], red_k[8][64];
+  __shared__ float red_eta[8];
+  __shared__ float ebuf[64], debuf[64];
+
+  const int t = threadIdx.x, wv = t >> 6, l = t & 63;
+  const int hf = l >> 5, ul = l & 31;
+  const int u = 32 * wv + ul, j0 = 32 * hf;
+  const int unit = blockIdx.x;
+  const int T = a.T, b = a.b;
+  const int nmb = (T + b - 1) / b;
+  const int nsteps = 2 * T;
+  const int llast = T - (nmb - 1) * b;  // tokens of the last mini-batch
+  const size_t base = (size_t)unit * T * 64;
+  const size_t nst = (size_t)PHID * 64;
+
+  // step n of the walk: mini-batches from the last; in each, its tokens
+  // forward (the replay), then backward
+  auto step_token = [&](int n, bool& fwd, int& m) {
+    int r;
+    if (n < 2 * llast) {
+      m = nmb - 1;
+      r = n;
+    } else {
+      const int n2 = n - 2 * llast;
+      m = nmb - 2 - n2 / (2 * b);
+      r = n2 % (2 * b);
+    }
+    const int len = min(b, T - m * b);
+    fwd = r < len;
+    return m * b + (fwd ? r : 2 * len - 1 - r);
+  };
+  // element e of step n's staged token (threads e < BSTRIDE)
+  auto token_value = [&](int n, int e) {
+    bool fwd;
+    int m;
+    const int tt = step_token(n, fwd, m);
+    const size_t o = base + (size_t)tt * 64;
+    if (e < 64) return load_in<F32IN>(a.k, o + e);
+    if (e < 128) return load_in<F32IN>(a.v, o + e - 64);
+    if (e < 192) return load_in<F32IN>(a.q, o + e - 128);
+    if (e < 256) return a.dz[o + e - 192];
+    return a.eta[(size_t)unit * T + tt];
+  };
+  // the gradient point's values, read from LDS where they are used
+  auto wg1 = [&](int i) { return wg1s[wv][i >> 2][l][i & 3]; };
+  auto wg2 = [&](int i) { return wg2s[wv][i >> 2][l][i & 3]; };
+
+  float w1[32], w2[32], a1[32], a2[32], g1[32], g2[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    a1[i] = a.dw1_T ? a.dw1_T[(size_t)unit * nst + u * 64 + j0 + i] : 0.f;
+    a2[i] = a.dw2_T ? a.dw2_T[(size_t)unit * nst + (j0 + i) * PHID + u] : 0.f;
+    g1[i] = 0.f;
+    g2[i] = 0.f;
+    w1[i] = 0.f;
+    w2[i] = 0.f;
+  }
+  float pre = 0.f;  // step n + 1's staged value, held by thread t < BSTRIDE
+  if (nsteps > 0 && t < BSTRIDE) {
+    tok[0][t] = token_value(0, t);
+    if (nsteps > 1) pre = token_value(1, t);
+  }
+  __syncthreads();
+
+  int pend_t = -1;  // token whose dk partials wait in red_k
+  for (int n = 0; n < nsteps; ++n) {
+    bool fwd;
+    int m;
+    const int tt = step_token(n, fwd, m);
+    const float* kt = tok[n & 1];
+    const float* vt = kt + 64;
+    const float* qt = kt + 128;
+    const float* dzt = kt + 192;
+    const float eta = kt[256];
+    if (fwd && tt == m * b) {  // a mini-batch starts: its checkpoint
+      const size_t co = ((size_t)unit * nmb + m) * nst;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        f32x4 x1, x2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x1[r] = a.w1_ckpt[co + u * 64 + j0 + 4 * c + r];
+          x2[r] = a.w2_ckpt[co + (j0 + 4 * c + r) * PHID + u];
+          w1[4 * c + r] = x1[r];
+          w2[4 * c + r] = x2[r];
+        }
+        wg1s[wv][c][l] = x1;
+        wg2s[wv][c][l] = x2;
+      }
+    }
+    // the token's forward quantities at the gradient point
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc = fmaf(wg1(i), kt[j0 + i], acc);
+    const float av = acc + __shfl_xor(acc, 32);
+    const float ph = gelu_phi(av);
+    const float dens = expf(-0.5f * av * av) * 0.39894228040143268f;  // phi(a)
+    const float x = av * ph;
+    const float gp = fmaf(av, dens, ph);                  // GELU'(a)
+    const float gpp = dens * (2.f - av * av);             // GELU''(a)
+    float mine = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float rs = half_sum32(wg2(i) * x);
+      if (ul == i) mine = rs;
+    }
+    red_y[wv][j0 + ul] = mine;
+    if (!fwd) {
+      // output of token t from the state after it (w1, w2)
+      acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) acc = fmaf(w1[i], qt[j0 + i], acc);
+      const float aq = acc + __shfl_xor(acc, 32);
+      const float phq = gelu_phi(aq);
+      const float xq = aq * phq;
+      const float gq = fmaf(aq, expf(-0.5f * aq * aq) * 0.39894228040143268f, phq);
+      acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) acc = fmaf(w2[i], dzt[j0 + i], acc);
+      const float daq = (acc + __shfl_xor(acc, 32)) * gq;
+      mine = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        a2[i] = fmaf(dzt[j0 + i], xq, a2[i]);
+        a1[i] = fmaf(daq, qt[j0 + i], a1[i]);
+        const float rs = half_sum32(w1[i] * daq);
+        if (ul == i) mine = rs;
+      }
+      red_q[wv][j0 + ul] = mine;
+    }
+    __syncthreads();  // B1
+    if (n + 1 < nsteps && t < BSTRIDE) {
+      tok[(n + 1) & 1][t] = pre;
+      if (n + 2 < nsteps) pre = token_value(n + 2, t);
+    }
+    if (t < 64) {
+      if (pend_t >= 0) {
+        float sm = 0.f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) sm += red_k[w][t];
+        a.dk[base + (size_t)pend_t * 64 + t] = sm;
+      }
+      float y = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) y += red_y[w][t];
+      ebuf[t] = 2.f * (y - vt[t]);
+      if (!fwd) {
+        float sm = 0.f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) sm += red_q[w][t];
+        a.dq[base + (size_t)tt * 64 + t] = sm;
+      }
+    }
+    pend_t = -1;
+    __syncthreads();  // B2
+    acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc = fmaf(wg2(i), ebuf[j0 + i], acc);
+    const float sv = acc + __shfl_xor(acc, 32);
+    const float delta = sv * gp;
+    if (fwd) {  // replay: the token's update
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        w2[i] = fmaf(-eta * ebuf[j0 + i], x, w2[i]);
+        w1[i] = fmaf(-eta * delta, kt[j0 + i], w1[i]);
+      }
+      continue;
+    }
+    // adjoints through the update, then through the gradient
+    float ak = 0.f, ae = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      ak = fmaf(a1[i], kt[j0 + i], ak);
+      ae = fmaf(a2[i], ebuf[j0 + i], ae);
+    }
+    ak += __shfl_xor(ak, 32);
+    ae += __shfl_xor(ae, 32);
+    const float ddl = -eta * ak;
+    float dx = -eta * ae;
+    const float pe = half_sum32(hf == 0 ? -(delta * ak + x * ae) : 0.f);
+    if (l == 0) red_eta[wv] = pe;
+    const float ds = ddl * gp;
+    float da = ddl * sv * gpp;
+    mine = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      g2[i] = fmaf(ebuf[j0 + i], ds, g2[i]);
+      const float rs = half_sum32(fmaf(-eta * a2[i], x, wg2(i) * ds));
+      if (ul == i) mine = rs;
+    }
+    red_e[wv][j0 + ul] = mine;
+    __syncthreads();  // B3
+    if (t < 64) {
+      float de = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) de += red_e[w][t];
+      debuf[t] = de;
+      a.dv[base + (size_t)tt * 64 + t] = -2.f * de;
+      if (t == 0) {
+        float sm = 0.f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) sm += red_eta[w];
+        a.deta[(size_t)unit * T + tt] = sm;
+      }
+    }
+    __syncthreads();  // B4
+    acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc = fmaf(wg2(i), debuf[j0 + i], acc);
+    dx = fmaf(2.f, acc + __shfl_xor(acc, 32), dx);
+    da = fmaf(dx, gp, da);
+    mine = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      g2[i] = fmaf(2.f * debuf[j0 + i], x, g2[i]);
+      g1[i] = fmaf(da, kt[j0 + i], g1[i]);
+      const float rs = half_sum32(fmaf(-eta * a1[i], delta, wg1(i) * da));
+      if (ul == i) mine = rs;
+      // the state before token t
+      w1[i] = fmaf(eta * delta, kt[j0 + i], w1[i]);
+      w2[i] = fmaf(eta * ebuf[j0 + i], x, w2[i]);
+    }
+    red_k[wv][j0 + ul] = mine;
+    pend_t = tt;
+    if (tt == m * b) {  // the gradient point is the state before this token
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        a1[i] += g1[i];
+        a2[i] += g2[i];
+        g1[i] = 0.f;
+        g2[i] = 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  if (t < 64 && pend_t >= 0) {
+    float sm = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) sm += red_k[w][t];
+    a.dk[base + (size_t)pend_t * 64 + t] = sm;
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    a.dw1_0[(size_t)unit * nst + u * 64 + j0 + i] = a1[i];
+    a.dw2_0[(size_t)unit * nst + (j0 + i) * PHID + u] = a2[i];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_mlp_bwd(const MlpBwdArgs& a, bool f32in, hipStream_t s) {
+  if (f32in) return launch(mlp_primal_bwd_kernel<true>, dim3(a.units), dim3(BTHREADS), s, a);
+  return launch(mlp_primal_bwd_kernel<false>, dim3(a.units), dim3(BTHREADS), s, a);
+}
 
 hipError_t launch_mlp_primal(const MlpArgs& a, bool f32in, hipStream_t s) {
   if (f32in) return launch(mlp_primal_kernel<true>, dim3(a.units), dim3(PTHREADS), s, a);

@@ -63,7 +63,7 @@ def test_version_and_status_strings(lib):
 
 
 # fake device addresses: 16-byte aligned, disjoint, never dereferenced
-A = [0x10000000 * (i + 1) for i in range(12)]
+A = [0x10000000 * (i + 1) for i in range(14)]
 P, M = 0x20000, 0x30000  # unaligned / overlapping variants
 
 
@@ -364,3 +364,41 @@ def test_linear_bwd_chunked_argument_checks(lib, chunks, kw, expect):
     assert bwd_chunked(lib, chunks, **kw) == status(expect), lib.ttt_last_error()
     if expect != "TTT_OK":
         assert lib.ttt_last_error().startswith(b"ttt_linear_bwd_chunked:")
+
+
+def mlp_bwd(lib, **kw):
+    a = dict(q=A[0], k=A[1], v=A[2], eta=A[3], c1=A[4], c2=A[5], B=1, H=2, T=37, d=64, hidden=256,
+             b=16, dt=_lib.TTT_BF16, dz=A[6], d1=None, d2=None, dq=A[7], dk=A[8], dv=A[9],
+             deta=A[10], dw1=A[11], dw2=A[12])
+    a.update(kw)
+    return lib.ttt_mlp_bwd(a["q"], a["k"], a["v"], a["eta"], a["c1"], a["c2"], a["B"], a["H"],
+                           a["T"], a["d"], a["hidden"], a["b"], a["dt"], a["dz"], a["d1"], a["d2"],
+                           a["dq"], a["dk"], a["dv"], a["deta"], a["dw1"], a["dw2"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(b=24), "TTT_ERR_UNSUPPORTED"),
+    (dict(hidden=128), "TTT_ERR_UNSUPPORTED"),
+    (dict(d=32), "TTT_ERR_UNSUPPORTED"),
+    (dict(dt=5), "TTT_ERR_DTYPE"),
+    (dict(T=-1), "TTT_ERR_SHAPE"),
+    (dict(B=1, H=1, T=1 << 24), "TTT_ERR_SHAPE"),
+    (dict(c2=None), "TTT_ERR_NULL"),
+    (dict(dz=A[6] + 4), "TTT_ERR_ALIGN"),
+    (dict(dq=A[4]), "TTT_ERR_ALIAS"),            # an output over the checkpoints
+    (dict(dw2=A[11] + 1024), "TTT_ERR_ALIAS"),   # two outputs
+    (dict(B=0), "TTT_OK"),
+])
+def test_mlp_bwd_argument_checks(lib, kw, expect):
+    assert mlp_bwd(lib, **kw) == status(expect), lib.ttt_last_error()
+    if expect != "TTT_OK":
+        assert lib.ttt_last_error().startswith(b"ttt_mlp_bwd:")
+
+
+def test_mlp_fwd_ckpt_argument_checks(lib):
+    f = lambda **kw: lib.ttt_mlp_fwd_ckpt(A[0], A[1], A[2], A[3], A[4], A[9], 0, 1, 1, 16, 64,
+                                          256, kw.get("b", 16), _lib.TTT_BF16, A[5], A[6], A[10],
+                                          kw.get("c1", A[11]), kw.get("c2", A[12]), None)
+    assert f(c1=None) == status("TTT_ERR_NULL")
+    assert f(c2=A[0]) == status("TTT_ERR_ALIAS")     # checkpoints over q
+    assert f(b=24) == status("TTT_ERR_UNSUPPORTED")
