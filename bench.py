@@ -419,6 +419,38 @@ def training_case(wl, steps, warmup):
             "train_token_heads_per_s": wl.token_heads / ((kf + kb) * 1e-6)}
 
 
+def mlp_training_case(wl, b, steps, warmup):
+    """ttt_mlp_fwd_ckpt then ttt_mlp_bwd on one TTT-MLP workload, timed
+    separately; dz is a seeded N(0, 0.01) draw.  Both run the primal-form
+    kernels (fp32 arithmetic, one token at a time)."""
+    import torch
+    from test_rnn_layers_head_amd import inputs, ttt_mlp_bwd, ttt_mlp_fwd_ckpt
+    x = inputs.make_inputs(wl)
+    d = device_inputs(x)
+    g = torch.Generator().manual_seed(19)
+    dz = (torch.randn(wl.B, wl.H, wl.T, wl.d, generator=g) * 0.1).cuda()
+    fwd = lambda: ttt_mlp_fwd_ckpt(d["q"], d["k"], d["v"], d["eta"], d["w1"], d["w2"], b)
+    _, _, _, c1, c2 = fwd()
+    bwd = lambda: ttt_mlp_bwd(d["q"], d["k"], d["v"], d["eta"], c1, c2, b, dz)
+    _, kf, _ = time_launches(fwd, steps, warmup)
+    _, kb, _ = time_launches(bwd, steps, warmup)
+    grads = bwd()
+    torch.cuda.synchronize()
+    assert all(torch.isfinite(t).all().item() for t in grads)
+    nmb = (wl.T + b - 1) // b
+    st = 2 * wl.hidden * wl.d * 4
+    fb = mlp_alg_bytes(wl) + wl.units * nmb * st
+    # backward: q, k, v (bf16), eta, dz and the checkpoints in; dq, dk, dv,
+    # deta and both initial-state adjoints out
+    bb = wl.token_heads * (3 * wl.d * 2 + 4 + wl.d * 4 + 3 * wl.d * 4 + 4) + wl.units * (nmb + 1) * st
+    return {"workload": wl.name, "b": b, "fwd_ckpt_us": kf, "bwd_us": kb,
+            "fwd_alg_bytes": fb, "bwd_alg_bytes": bb,
+            "fwd_hbm_frac": fb / (kf * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "bwd_hbm_frac": bb / (kb * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "train_token_heads_per_s": wl.token_heads / ((kf + kb) * 1e-6),
+            "kernels": "mlp_primal_kernel (checkpoints) / mlp_primal_bwd_kernel"}
+
+
 def gate_alg_bytes(wl) -> int:
     """Learning-rate gate: read x (bf16) and theta_lr (fp32), write eta."""
     return wl.B * wl.T * wl.gate_dx * 2 + wl.H * wl.gate_dx * 4 + wl.token_heads * 4
@@ -668,7 +700,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="also launch the 1 GiB streaming copy used to scale byte counters")
-    ap.add_argument("--only", choices=("train", "train-long", "decode", "gate"),
+    ap.add_argument("--only", choices=("train", "train-long", "train-mlp", "decode", "gate"),
                     help="run one group of the secondary measurements and print it (for profiling)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "KERNEL", "SKIP", "TAKE"),
@@ -702,6 +734,10 @@ def main():
     if args.only == "train":
         print(json.dumps({w.name: training_case(w, max(5, args.steps // 5), 10)
                           for w in (wl, inputs.workload(2))}))
+        return 0
+    if args.only == "train-mlp":
+        w4 = inputs.workload(4)
+        print(json.dumps({w4.name: mlp_training_case(w4, 16, 3, 2)}))
         return 0
     if args.only == "train-long":
         w5 = inputs.workload(5)
@@ -768,6 +804,10 @@ def main():
             extras[w4.name] = mlp_case(w4, 16, max(5, args.steps // 2), EXTRA_WARMUP, flush_reps=10)
         except Exception as e:  # reported, never silently replaced
             extras[w4.name] = {"error": str(e)}
+        log(f"[bench] {w4.name} with b = 64 (the primal kernel)")
+        extras[f"{w4.name}_b64"] = mlp_case(w4, 64, 3, 2)
+        log(f"[bench] forward with checkpoints + backward, {w4.name}")
+        extras[f"train-{w4.name}"] = mlp_training_case(w4, 16, 3, 2)
         log("[bench] streaming copy reference")
         extras["stream_copy_GBps"] = stream_copy_GBps()
         extras["headline_frac_of_stream_copy"] = head["hbm_GBps"] / extras["stream_copy_GBps"]

@@ -35,9 +35,10 @@ CFLAGS = ["-O2", "-ffp-contract=off", "-fPIC", "-shared", "-pthread", "-std=c99"
 
 def build(src: str = _SRC, out: str = _LIB, extra_flags=()) -> str:
     """Compile the oracle C file into a shared library with gcc."""
-    cmd = ["gcc", *CFLAGS, *extra_flags, src, "-o", out + ".tmp", "-lm"]
+    tmp = f"{out}.{os.getpid()}.tmp"  # per process: concurrent builders never share it
+    cmd = ["gcc", *CFLAGS, *extra_flags, src, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True, capture_output=True, text=True)
-    os.replace(out + ".tmp", out)
+    os.replace(tmp, out)
     return out
 
 
@@ -61,6 +62,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.ttt_oracle_linear_bwd.argtypes = [dp, dp, dp, dp, dp, I, L, L, L, L, L, dp, dp, dp, dp, dp,
                                           dp, dp]
     lib.ttt_oracle_linear_bwd.restype = I
+    lib.ttt_oracle_linear_ln_bwd.argtypes = [dp, dp, dp, dp, dp, I, dp, dp, D, L, L, L, L, L, dp,
+                                             dp, dp, dp, dp, dp, dp, dp, dp]
+    lib.ttt_oracle_linear_ln_bwd.restype = I
     lib.ttt_oracle_mlp_bwd.argtypes = [dp, dp, dp, dp, dp, dp, I, L, L, L, L, L, L, dp, dp, dp,
                                        dp, dp, dp, dp, dp, dp]
     lib.ttt_oracle_mlp_bwd.restype = I
@@ -271,6 +275,31 @@ def linear_bwd(q, k, v, eta, w0, b: int, dz, dw_T=None, lib=None):
     if rc != 0:
         raise RuntimeError(f"ttt_oracle_linear_bwd failed with status {rc}")
     return dq, dk, dv, deta, dw0
+
+
+def linear_ln_bwd(q, k, v, eta, w0, gamma, beta, eps: float, b: int, dz, dw_T=None, lib=None):
+    """Backward of TTT-Linear with the LayerNorm + residual inner model:
+    given dz [B, H, T, d] and optionally dw_T [B, H, d, d], returns (dq, dk,
+    dv, deta, dw0, dgamma, dbeta) with dw0 [B, H, d, d] and dgamma, dbeta
+    [B, H, d] per unit (sum over the batch for the shared parameters)."""
+    q, k, v, eta, w0, gamma, beta, dz = map(_f64, (q, k, v, eta, w0, gamma, beta, dz))
+    B, H, T, d = q.shape
+    per_batch = 1 if w0.ndim == 4 else 0
+    assert w0.shape == ((B, H, d, d) if per_batch else (H, d, d)) and dz.shape == q.shape
+    assert gamma.shape == (H, d) and beta.shape == (H, d)
+    dwT = None if dw_T is None else _f64(dw_T)
+    dq, dk, dv = (np.zeros((B, H, T, d)) for _ in range(3))
+    deta = np.zeros((B, H, T))
+    dw0 = np.zeros((B, H, d, d))
+    dg, db = np.zeros((B, H, d)), np.zeros((B, H, d))
+    lib = lib or load()
+    rc = lib.ttt_oracle_linear_ln_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w0), per_batch,
+                                      _ptr(gamma), _ptr(beta), float(eps), B, H, T, d, int(b),
+                                      _ptr(dz), None if dwT is None else _ptr(dwT), _ptr(dq),
+                                      _ptr(dk), _ptr(dv), _ptr(deta), _ptr(dw0), _ptr(dg), _ptr(db))
+    if rc != 0:
+        raise RuntimeError(f"ttt_oracle_linear_ln_bwd failed with status {rc}")
+    return dq, dk, dv, deta, dw0, dg, db
 
 
 def mlp_bwd(q, k, v, eta, w1_0, w2_0, b: int, dz, dw1_T=None, dw2_T=None, lib=None):

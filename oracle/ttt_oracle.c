@@ -622,6 +622,222 @@ int ttt_oracle_linear_bwd(const double *q, const double *k, const double *v,
 }
 
 /* ------------------------------------------------------------------ */
+/* TTT-Linear with LayerNorm + residual: backward (§6.12 with §4.4).   */
+/* ------------------------------------------------------------------ */
+/* Forward, one unit (as linear_ln_unit), keeping every state: S[t+1] =
+ * S[t] - eta_t dy_t k_t^T with, at the gradient point P = S[m0]:
+ *   y = P k, mu = mean(y), c = y - mu, var = mean(c^2), rs = (var+eps)^-1/2,
+ *   yh = c rs, f = k + gamma yh + beta, r = f - v, g = 2 gamma r,
+ *   dy = rs (g - mean(g) - yh mean(g yh));
+ * and the output z = q + gamma LNhat(S[t+1] q) + beta.
+ * Reverse: each forward operation's adjoint, in the opposite order, with A
+ * the adjoint of the state after token t (starting from dW_T), Ag that of
+ * the current mini-batch's gradient point (added to A at its first token),
+ * and dgamma, dbeta summed over the tokens. */
+static void ln_stats(const double *y, long d, double eps, double *c, double *rs) {
+  double mu = 0.0, var = 0.0;
+  for (long i = 0; i < d; ++i) mu += y[i];
+  mu /= (double)d;
+  for (long i = 0; i < d; ++i) {
+    c[i] = y[i] - mu;
+    var += c[i] * c[i];
+  }
+  var = var / (double)d;
+  *rs = 1.0 / sqrt(eps + var);
+}
+
+/* adjoint of yh = LNhat(y) (yh = c rs, c = y - mean(y), rs = (mean(c^2) +
+ * eps)^-1/2) given dyh and the extra adjoint drs0 of rs: returns dy */
+static void ln_hat_adjoint(const double *c, double rs, const double *dyh, double drs0, long d,
+                           double *dc, double *dy) {
+  double drs = drs0;
+  for (long i = 0; i < d; ++i) {
+    dc[i] = rs * dyh[i];
+    drs += c[i] * dyh[i];
+  }
+  const double dvar = -0.5 * rs * rs * rs * drs;
+  double mdc = 0.0;
+  for (long i = 0; i < d; ++i) {
+    dc[i] += 2.0 / (double)d * c[i] * dvar;
+    mdc += dc[i];
+  }
+  mdc /= (double)d;
+  for (long i = 0; i < d; ++i) dy[i] = dc[i] - mdc;
+}
+
+static int linear_ln_bwd_unit(const double *q, const double *k, const double *v,
+                              const double *eta, const double *w0, const double *gamma,
+                              const double *beta, double eps, long T, long d, long b,
+                              const double *dz, const double *dwT, double *dq, double *dk,
+                              double *dv, double *deta, double *dw0, double *dgam, double *dbet) {
+  const size_t dd = (size_t)(d * d);
+  double *S = (double *)malloc(sizeof(double) * dd * (size_t)(T + 1));
+  double *Ag = (double *)calloc(dd, sizeof(double));
+  double *vec = (double *)malloc(sizeof(double) * (size_t)(16 * d));
+  if (!S || !Ag || !vec) { free(S); free(Ag); free(vec); return 1; }
+  double *y = vec, *c = y + d, *yh = c + d, *r = yh + d, *g = r + d, *dy = g + d;
+  double *cq = dy + d, *yhq = cq + d, *dyh = yhq + d, *dc = dyh + d, *dyq = dc + d;
+  double *Ak = dyq + d, *ddy = Ak + d, *dg = ddy + d, *dyv = dg + d, *tmp = dyv + d;
+  (void)tmp;
+  memcpy(S, w0, sizeof(double) * dd);
+  /* forward, keeping every state */
+  for (long t = 0; t < T; ++t) {
+    const long m0 = (t / b) * b;
+    const double *P = S + (size_t)m0 * dd, *C = S + (size_t)t * dd;
+    double *N = S + (size_t)(t + 1) * dd;
+    const double *kt = k + t * d, *vt = v + t * d;
+    double rs;
+    for (long i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (long j = 0; j < d; ++j) acc += P[i * d + j] * kt[j];
+      y[i] = acc;
+    }
+    ln_stats(y, d, eps, c, &rs);
+    double gbar = 0.0, m = 0.0;
+    for (long i = 0; i < d; ++i) {
+      yh[i] = c[i] * rs;
+      g[i] = 2.0 * gamma[i] * (kt[i] + gamma[i] * yh[i] + beta[i] - vt[i]);
+      gbar += g[i];
+      m += g[i] * yh[i];
+    }
+    gbar /= (double)d;
+    m /= (double)d;
+    for (long i = 0; i < d; ++i) dy[i] = rs * (g[i] - gbar - yh[i] * m);
+    for (long i = 0; i < d; ++i)
+      for (long j = 0; j < d; ++j) N[i * d + j] = C[i * d + j] - eta[t] * dy[i] * kt[j];
+  }
+  /* reverse */
+  double *A = dw0;
+  if (dwT) memcpy(A, dwT, sizeof(double) * dd);
+  else memset(A, 0, sizeof(double) * dd);
+  memset(dgam, 0, sizeof(double) * (size_t)d);
+  memset(dbet, 0, sizeof(double) * (size_t)d);
+  for (long t = T - 1; t >= 0; --t) {
+    const long m0 = (t / b) * b;
+    const double *P = S + (size_t)m0 * dd, *N = S + (size_t)(t + 1) * dd;
+    const double *kt = k + t * d, *vt = v + t * d, *qt = q + t * d, *zt = dz + t * d;
+    const double et = eta[t];
+    double rs, rsq;
+    /* the token's forward quantities at the gradient point */
+    for (long i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (long j = 0; j < d; ++j) acc += P[i * d + j] * kt[j];
+      y[i] = acc;
+    }
+    ln_stats(y, d, eps, c, &rs);
+    double gbar = 0.0, m = 0.0;
+    for (long i = 0; i < d; ++i) {
+      yh[i] = c[i] * rs;
+      r[i] = kt[i] + gamma[i] * yh[i] + beta[i] - vt[i];
+      g[i] = 2.0 * gamma[i] * r[i];
+      gbar += g[i];
+      m += g[i] * yh[i];
+    }
+    gbar /= (double)d;
+    m /= (double)d;
+    for (long i = 0; i < d; ++i) dy[i] = rs * (g[i] - gbar - yh[i] * m);
+    /* output z = q + gamma LNhat(N q) + beta */
+    for (long i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (long j = 0; j < d; ++j) acc += N[i * d + j] * qt[j];
+      y[i] = acc;
+    }
+    ln_stats(y, d, eps, cq, &rsq);
+    for (long i = 0; i < d; ++i) {
+      yhq[i] = cq[i] * rsq;
+      dyh[i] = gamma[i] * zt[i];
+      dgam[i] += yhq[i] * zt[i];
+      dbet[i] += zt[i];
+    }
+    ln_hat_adjoint(cq, rsq, dyh, 0.0, d, dc, dyq);
+    for (long i = 0; i < d; ++i)
+      for (long j = 0; j < d; ++j) A[i * d + j] += dyq[i] * qt[j];
+    for (long j = 0; j < d; ++j) {
+      double acc = zt[j]; /* the residual q */
+      for (long i = 0; i < d; ++i) acc += N[i * d + j] * dyq[i];
+      dq[t * d + j] = acc;
+    }
+    /* the update N = S[t] - eta dy k^T */
+    double de = 0.0;
+    for (long i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (long j = 0; j < d; ++j) acc += A[i * d + j] * kt[j];
+      Ak[i] = acc;
+      ddy[i] = -et * acc;
+      de -= dy[i] * acc;
+    }
+    deta[t] = de;
+    for (long j = 0; j < d; ++j) {
+      double acc = 0.0;
+      for (long i = 0; i < d; ++i) acc += A[i * d + j] * dy[i];
+      dk[t * d + j] = -et * acc;
+    }
+    /* dy = rs (g - gbar - yh m) */
+    double drs = 0.0, sdd = 0.0, dm = 0.0;
+    for (long i = 0; i < d; ++i) {
+      drs += ddy[i] * (g[i] - gbar - yh[i] * m);
+      sdd += ddy[i];
+      dm -= rs * ddy[i] * yh[i];
+    }
+    const double dgbar = -rs * sdd;
+    for (long i = 0; i < d; ++i) {
+      dg[i] = rs * ddy[i] + dm / (double)d * yh[i] + dgbar / (double)d; /* m, gbar */
+      dyh[i] = -rs * m * ddy[i] + dm / (double)d * g[i];
+    }
+    /* g = 2 gamma r, r = f - v, f = k + gamma yh + beta */
+    for (long i = 0; i < d; ++i) {
+      const double dr = 2.0 * gamma[i] * dg[i];
+      dgam[i] += 2.0 * r[i] * dg[i] + yh[i] * dr;
+      dbet[i] += dr;
+      dv[t * d + i] = -dr;
+      dk[t * d + i] += dr;
+      dyh[i] += gamma[i] * dr;
+    }
+    /* yh = LNhat(y), y = P k */
+    ln_hat_adjoint(c, rs, dyh, drs, d, dc, dyv);
+    for (long i = 0; i < d; ++i)
+      for (long j = 0; j < d; ++j) Ag[i * d + j] += dyv[i] * kt[j];
+    for (long j = 0; j < d; ++j) {
+      double acc = 0.0;
+      for (long i = 0; i < d; ++i) acc += P[i * d + j] * dyv[i];
+      dk[t * d + j] += acc;
+    }
+    if (t == m0) { /* the gradient point of this mini-batch is the state before t */
+      for (size_t e = 0; e < dd; ++e) {
+        A[e] = A[e] + Ag[e];
+        Ag[e] = 0.0;
+      }
+    }
+  }
+  free(S);
+  free(Ag);
+  free(vec);
+  return 0;
+}
+
+int ttt_oracle_linear_ln_bwd(const double *q, const double *k, const double *v,
+                             const double *eta, const double *w0, int w0_per_batch,
+                             const double *gamma, const double *beta, double eps, long B, long H,
+                             long T, long d, long b, const double *dz, const double *dwT,
+                             double *dq, double *dk, double *dv, double *deta, double *dw0,
+                             double *dgamma, double *dbeta) {
+  if (B < 0 || H < 0 || T < 0 || d <= 0 || b <= 0 || !(eps >= 0.0)) return 2;
+  for (long u = 0; u < B * H; ++u) {
+    const long h = u % H, wsel = w0_per_batch ? u : h;
+    const size_t so = (size_t)u * (size_t)(T * d);
+    int rc = linear_ln_bwd_unit(q + so, k + so, v + so, eta + (size_t)u * (size_t)T,
+                                w0 + (size_t)wsel * (size_t)(d * d), gamma + (size_t)h * (size_t)d,
+                                beta + (size_t)h * (size_t)d, eps, T, d, b, dz + so,
+                                dwT ? dwT + (size_t)u * (size_t)(d * d) : NULL, dq + so, dk + so,
+                                dv + so, deta + (size_t)u * (size_t)T,
+                                dw0 + (size_t)u * (size_t)(d * d), dgamma + (size_t)u * (size_t)d,
+                                dbeta + (size_t)u * (size_t)d);
+    if (rc) return rc;
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* TTT-MLP backward: reverse pass of the primal recurrence.            */
 /* ------------------------------------------------------------------ */
 /* d^2/dx^2 [x Phi(x)] = 2 phi(x) + x phi'(x) = phi(x) (2 - x^2) */

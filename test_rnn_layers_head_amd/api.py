@@ -141,18 +141,19 @@ def ttt_linear_ln_fwd(q, k, v, eta, w0, ln_gamma, ln_beta, eps: float, b: int, z
 
 def ttt_linear_fwd_ckpt(q, k, v, eta, w0, b: int, z=None, w_out=None, w_ckpt=None, stream=None):
     """ttt_linear_fwd that also keeps the state before every mini-batch
-    (include/ttt.h; bf16 q/k/v, b = 16).  Returns (z, w_out, w_ckpt) with
-    w_ckpt [B, H, ceil(T/16), d, d] fp32."""
+    (include/ttt.h).  Returns (z, w_out, w_ckpt) with w_ckpt
+    [B, H, ceil(T/b), d, d] fp32."""
     B, H, T, d = q.shape
+    nmb = (T + b - 1) // b if b > 0 else 0
     if w_ckpt is None:
-        w_ckpt = torch.empty((B, H, (T + 15) // 16, d, d), dtype=torch.float32, device=q.device)
+        w_ckpt = torch.empty((B, H, nmb, d, d), dtype=torch.float32, device=q.device)
     if z is None:
         z = torch.empty((B, H, T, d), dtype=torch.float32, device=q.device)
     if w_out is None:
         w_out = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
     dev = _check_tensors(dict(q=q, k=k, v=v, eta=eta, w0=w0, z=z, w_out=w_out, w_ckpt=w_ckpt))
-    if tuple(w_ckpt.shape) != (B, H, (T + 15) // 16, d, d) or w_ckpt.dtype != torch.float32:
-        raise ValueError("w_ckpt must be float32 [B, H, ceil(T/16), d, d]")
+    if tuple(w_ckpt.shape) != (B, H, nmb, d, d) or w_ckpt.dtype != torch.float32:
+        raise ValueError("w_ckpt must be float32 [B, H, ceil(T/b), d, d]")
     per_batch = 1 if w0.dim() == 4 else 0
     with torch.cuda.device(dev):
         _lib.check(_lib.lib().ttt_linear_fwd_ckpt(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w0),
@@ -178,8 +179,8 @@ def ttt_linear_bwd(q, k, v, eta, w_ckpt, b: int, dz, dw_T=None, stream=None, seq
             raise TypeError(f"{name} must be float32")
     if tuple(dz.shape) != (B, H, T, d):
         raise ValueError("dz must be [B, H, T, d]")
-    if tuple(w_ckpt.shape) != (B, H, (T + 15) // 16, d, d):
-        raise ValueError("w_ckpt must be [B, H, ceil(T/16), d, d]")
+    if b > 0 and tuple(w_ckpt.shape) != (B, H, (T + b - 1) // b, d, d):
+        raise ValueError("w_ckpt must be [B, H, ceil(T/b), d, d]")
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w_ckpt), B, H, T, d, int(b), _dtype_code(q),
             _ptr(dz), _ptr(dw_T), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(deta), _ptr(dw0))
     with torch.cuda.device(dev):

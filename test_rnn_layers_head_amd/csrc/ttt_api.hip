@@ -136,15 +136,15 @@ ttt_status_t linear_impl(const void* q, const void* k, const void* v, const floa
   const Range in[] = {rng("q", q, seq * es), rng("k", k, seq * es), rng("v", v, seq * es),
                       rng("eta", eta, units * T * 4),
                       rng("w0", w0, (w0_per_batch ? units : (int64_t)H) * d * d * 4)};
-  const int64_t nck = units * ((T + 15) / 16) * d * d * 4;
+  const int64_t nck = b > 0 ? units * ((T + b - 1) / b) * d * d * 4 : 0;
   const Range out[] = {rng("z", z, seq * 4), rng("w_out", w_out, units * d * d * 4),
                        rng("w_ckpt", w_ckpt, nck)};
   const int pairs[][2] = {{4, 1}};
   ttt_status_t st = check_common(fn, dt, w0_per_batch, B, H, T, d, b, in, 5, out,
                                  w_ckpt ? 3 : 2, pairs, 1, T > 0);
   if (st != TTT_OK || units == 0) return st;
-  if (w_ckpt && (dt != TTT_BF16 || b != 16))
-    return fail(TTT_ERR_UNSUPPORTED, "%s: checkpoints need bf16 q/k/v and b = 16", fn);
+  // checkpoints for b != 16 or fp32 inputs: the primal-form kernel
+  const bool ck_primal = w_ckpt && (dt != TTT_BF16 || b != 16);
   // chunks: 0 = automatic, 1 = one pass, P >= 2 = P sequence chunks
   int P = chunks;
   if (P == 0) P = default_chunks(dt, b, units, T);
@@ -160,7 +160,9 @@ ttt_status_t linear_impl(const void* q, const void* k, const void* v, const floa
     e = ttt::launch_copy_state(w0, w0_per_batch, (int)units, H, d * d, w_out, s);
   } else {
     ttt::LinearArgs a{q, k, v, eta, w0, z, w_out, w0_per_batch, (int)units, H, T, b, w_ckpt};
-    if (P > 1)
+    if (ck_primal)
+      e = ttt::launch_linear_primal_ckpt(a, dt == TTT_F32, s);
+    else if (P > 1)
       e = ttt::launch_linear_chunked(a, P, rows ? rows : auto_rows(units * P), s);
     else
       e = ttt::launch_linear(a, dt == TTT_F32, rows ? rows : auto_rows(units), s);
@@ -321,8 +323,9 @@ ttt_status_t linear_bwd_impl(const void* q, const void* k, const void* v, const 
                             void* stream, int32_t chunks = 0, const char* fn = "ttt_linear_bwd") {
   const int64_t units = (int64_t)B * H;
   const int64_t seq = units * T * d;
-  const int64_t nck = units * ((T + 15) / 16) * d * d * 4;
-  const Range in[] = {rng("q", q, seq * 2), rng("k", k, seq * 2), rng("v", v, seq * 2),
+  const int64_t es = dt == TTT_F32 ? 4 : 2;
+  const int64_t nck = b > 0 ? units * ((T + b - 1) / b) * d * d * 4 : 0;
+  const Range in[] = {rng("q", q, seq * es), rng("k", k, seq * es), rng("v", v, seq * es),
                       rng("eta", eta, units * T * 4), rng("w_ckpt", w_ckpt, nck),
                       rng("dz", dz, seq * 4), rng("dw_T", dw_T, units * d * d * 4)};
   const Range out[] = {rng("dq", dq, seq * 4), rng("dk", dk, seq * 4), rng("dv", dv, seq * 4),
@@ -331,14 +334,19 @@ ttt_status_t linear_bwd_impl(const void* q, const void* k, const void* v, const 
   if (B < 0 || H < 0 || T < 0 || d < 0 || b < 0)
     return fail(TTT_ERR_SHAPE, "%s: negative size (B=%d H=%d T=%d d=%d b=%d)", fn, B, H, T, d, b);
   if (d != 64) return fail(TTT_ERR_UNSUPPORTED, "%s: head dim d=%d unsupported (only 64)", fn, d);
-  if (b != 16) return fail(TTT_ERR_UNSUPPORTED, "%s: mini-batch b=%d unsupported (only 16)", fn, b);
-  if (dt != TTT_BF16) return fail(TTT_ERR_UNSUPPORTED, "%s: only bf16 q/k/v are supported", fn);
+  if (!supported_b(b))
+    return fail(TTT_ERR_UNSUPPORTED, "%s: mini-batch b=%d unsupported (need b | 16 or 16 | b)", fn, b);
+  // bf16 with b = 16: the dual-form kernel (and its sequence chunks); any
+  // other b or fp32 inputs: the primal-form kernel, one pass
+  const bool primal = dt != TTT_BF16 || b != 16;
+  if (primal && chunks > 1)
+    return fail(TTT_ERR_UNSUPPORTED, "%s: seq_chunks=%d needs bf16 q/k/v and b = 16", fn, chunks);
   if (seq >= ((int64_t)1 << 31))
     return fail(TTT_ERR_SHAPE, "%s: B*H*T*d = %lld exceeds 2^31 - 1", fn, (long long)seq);
   if (T >= (1 << 24))  // a unit's T x 64 fp32 gradients stay within 32-bit byte offsets
     return fail(TTT_ERR_SHAPE, "%s: T = %d exceeds 2^24 - 1", fn, T);
   if (chunks < 0) return fail(TTT_ERR_UNSUPPORTED, "%s: seq_chunks=%d must be >= 0", fn, chunks);
-  const int P = chunks ? chunks : default_chunks(dt, b, units, T);
+  const int P = primal ? 1 : (chunks ? chunks : default_chunks(dt, b, units, T));
   if (P > 1 && !chunks_supported(P, T, b, dt))
     return fail(TTT_ERR_UNSUPPORTED,
                 "%s: seq_chunks=%d needs T / seq_chunks a multiple of 16 and >= 192 (T=%d)", fn, P, T);
@@ -361,9 +369,15 @@ ttt_status_t linear_bwd_impl(const void* q, const void* k, const void* v, const 
       if (overlap(out[o], out[o2]))
         return fail(TTT_ERR_ALIAS, "%s: %s and %s overlap", fn, out[o].name, out[o2].name);
   }
-  ttt::LinearBwdArgs a{q, k, v, eta, w_ckpt, dz, dw_T, dq, dk, dv, deta, dw0, (int)units, H, T};
-  hipError_t e = P > 1 ? ttt::launch_linear_bwd_chunked(a, P, auto_rows(units * P), (hipStream_t)stream)
-                       : ttt::launch_linear_bwd(a, (hipStream_t)stream);
+  hipError_t e;
+  if (primal) {
+    ttt::LinearPrimalBwdArgs a{q, k, v, eta, w_ckpt, dz, dw_T, dq, dk, dv, deta, dw0, (int)units, T, b};
+    e = ttt::launch_linear_primal_bwd(a, dt == TTT_F32, (hipStream_t)stream);
+  } else {
+    ttt::LinearBwdArgs a{q, k, v, eta, w_ckpt, dz, dw_T, dq, dk, dv, deta, dw0, (int)units, H, T};
+    e = P > 1 ? ttt::launch_linear_bwd_chunked(a, P, auto_rows(units * P), (hipStream_t)stream)
+              : ttt::launch_linear_bwd(a, (hipStream_t)stream);
+  }
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return TTT_OK;
 }

@@ -138,6 +138,29 @@ struct LinearBwdArgs {
   int tok_out = 1;        // 0: dq, dk, dv, deta are not written
 };
 hipError_t launch_linear_bwd(const LinearBwdArgs& a, hipStream_t s);
+
+// TTT-Linear training support in the primal form (any b, fp32 or bf16 q/k/v):
+// the checkpointing forward (a.w_ckpt [units][ceil(T/b)][64][64]) and the
+// backward from those checkpoints.
+struct LinearPrimalBwdArgs {
+  const void* q;          // [units][T][64]
+  const void* k;
+  const void* v;
+  const float* eta;       // [units][T]
+  const float* w_ckpt;    // [units][ceil(T/b)][64][64]
+  const float* dz;        // [units][T][64]
+  const float* dw_T;      // [units][64][64] or NULL
+  float* dq;              // [units][T][64]
+  float* dk;
+  float* dv;
+  float* deta;            // [units][T]
+  float* dw0;             // [units][64][64]
+  int units;
+  int T;
+  int b;
+};
+hipError_t launch_linear_primal_ckpt(const LinearArgs& a, bool f32in, hipStream_t s);
+hipError_t launch_linear_primal_bwd(const LinearPrimalBwdArgs& a, bool f32in, hipStream_t s);
 // The backward in P sequence chunks of T / P tokens (a multiple of 16, at
 // least 192): the chunks' forward maps, their backward from a zero end
 // adjoint, a serial combine over the chunks, then every chunk from its end

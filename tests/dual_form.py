@@ -222,3 +222,36 @@ def mlp_unit_torch(q, k, v, eta, w1, w2, b):
         W1 = W1 - G1 @ XK.T
         W2 = W2 - G2 @ X2.T
     return torch.cat(outs, dim=0), W1, W2
+
+
+def linear_ln_unit_torch(q, k, v, eta, w0, gamma, beta, eps, b):
+    """linear_ln_unit in float64 torch, differentiable (one unit; q, k, v
+    [T, d], eta [T], w0 [d, d], gamma, beta [d]).  Per mini-batch at its
+    starting W (columns are tokens): Y = W K, the LayerNorm VJP of
+    2 gamma (K + gamma LNhat(Y) + beta - V) column by column gives G,
+    W_b = W - G diag(eta) K^T, and the outputs are
+    Q + gamma LNhat(W Q - G diag(eta) triu(K^T Q)) + beta ("论文速览 | TTT"
+    §3.6 with the §4.4 wrapper)."""
+    import torch
+
+    def lnhat(Y):
+        mu = Y.mean(dim=0, keepdim=True)
+        var = ((Y - mu) ** 2).mean(dim=0, keepdim=True)
+        rs = 1.0 / torch.sqrt(var + eps)
+        return (Y - mu) * rs, rs
+
+    T = q.shape[0]
+    W = w0
+    g_, b_ = gamma[:, None], beta[:, None]
+    outs = []
+    for m0 in range(0, T, b):
+        m1 = min(T, m0 + b)
+        XK, XV, XQ = k[m0:m1].T, v[m0:m1].T, q[m0:m1].T
+        e = eta[m0:m1]
+        Yh, rs = lnhat(W @ XK)
+        g = 2.0 * g_ * (XK + g_ * Yh + b_ - XV)
+        G = rs * (g - g.mean(dim=0, keepdim=True) - Yh * (g * Yh).mean(dim=0, keepdim=True))
+        Ge = G * e[None, :]
+        outs.append((XQ + g_ * lnhat(W @ XQ - Ge @ torch.triu(XK.T @ XQ))[0] + b_).T)
+        W = W - Ge @ XK.T
+    return torch.cat(outs, dim=0), W

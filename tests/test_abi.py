@@ -286,8 +286,9 @@ def bwd(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,expect", [
-    (dict(b=4), "TTT_ERR_UNSUPPORTED"),
-    (dict(dt=_lib.TTT_F32), "TTT_ERR_UNSUPPORTED"),
+    (dict(b=24), "TTT_ERR_UNSUPPORTED"),        # neither b | 16 nor 16 | b
+    (dict(b=0), "TTT_ERR_UNSUPPORTED"),
+    (dict(dt=9), "TTT_ERR_DTYPE"),
     (dict(d=32), "TTT_ERR_UNSUPPORTED"),
     (dict(T=-1), "TTT_ERR_SHAPE"),
     (dict(ck=None), "TTT_ERR_NULL"),
@@ -308,8 +309,8 @@ def test_linear_fwd_ckpt_argument_checks(lib):
     f = lambda **kw: lib.ttt_linear_fwd_ckpt(A[0], A[1], A[2], A[3], A[4], 0, 1, 1, 16, 64,
                                              kw.get("b", 16), kw.get("dt", _lib.TTT_BF16), A[5],
                                              A[6], kw.get("ck", A[7]), None)
-    assert f(b=4) == status("TTT_ERR_UNSUPPORTED")
-    assert f(dt=_lib.TTT_F32) == status("TTT_ERR_UNSUPPORTED")
+    assert f(b=24) == status("TTT_ERR_UNSUPPORTED")
+    assert f(dt=9) == status("TTT_ERR_DTYPE")
     assert f(ck=None) == status("TTT_ERR_NULL")
     assert f(ck=A[0]) == status("TTT_ERR_ALIAS")
 

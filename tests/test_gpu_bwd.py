@@ -108,9 +108,72 @@ def test_backward_empty_sequence_and_rejected_arguments():
     _, _, ck = ttt_linear_fwd_ckpt(q, k, v, eta, w0, 16)
     dz = torch.randn(1, 2, 16, 64, device="cuda")
     with pytest.raises(TTTError, match="TTT_ERR_UNSUPPORTED"):
-        ttt_linear_bwd(q, k, v, eta, ck, 4, dz)
-    with pytest.raises(TTTError, match="TTT_ERR_UNSUPPORTED"):
-        ttt_linear_fwd_ckpt(q, k, v, eta, w0, 32)
+        ttt_linear_bwd(q, k, v, eta, ck, 24, dz)
+    ck4 = ttt_linear_fwd_ckpt(q, k, v, eta, w0, 4)[2]
+    with pytest.raises(TTTError, match="TTT_ERR_UNSUPPORTED"):  # chunks need bf16, b = 16
+        ttt_linear_bwd(q, k, v, eta, ck4, 4, dz, seq_chunks=2)
+
+
+# ------------------------------------------------ any b, fp32 inputs (primal form)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("b", [1, 4, 16, 32, 64])
+@pytest.mark.parametrize("T", [1, 37, 130])
+def test_any_minibatch_checkpoints_and_backward(dtype, b, T):
+    """b != 16 or fp32 q/k/v: the primal-form kernels.  Checkpoints (one per
+    mini-batch) against the oracle's states, then every gradient against the
+    oracle backward, with dW_T given."""
+    if dtype == "bf16" and b == 16:
+        pytest.skip("the dual-form kernels, tested above")
+    x = inputs.make_inputs(inputs.Workload("bwdb", "linear", B=2, H=2, T=T, qkv_dtype=dtype,
+                                           seed=760 + T + b))
+    rng = np.random.default_rng(761 + T + b)
+    dz = rng.standard_normal(x.q.shape).astype(np.float32)
+    dwT = rng.standard_normal((2, 2, 64, 64)).astype(np.float32)
+    q, k, v = (gu.dev(x, n) for n in ("q", "k", "v"))
+    eta, w0 = gu.f32(x.eta), gu.f32(x.w0)
+    z, w, ck = ttt_linear_fwd_ckpt(q, k, v, eta, w0, b)
+    grads = ttt_linear_bwd(q, k, v, eta, ck, b, gu.f32(dz), gu.f32(dwT))
+    torch.cuda.synchronize()
+    zr, wr = oracle.linear(x.q, x.k, x.v, x.eta, x.w0, b)
+    gu.assert_close(z.cpu().numpy(), zr, dtype, "z")
+    gu.assert_close(w.cpu().numpy(), wr, dtype, "w_T")
+    ck = ck.cpu().numpy()
+    assert ck.shape[2] == (T + b - 1) // b
+    for m in range(1, ck.shape[2]):
+        _, ref = oracle.linear(x.q[:, :, :b * m], x.k[:, :, :b * m], x.v[:, :, :b * m],
+                               x.eta[:, :, :b * m], x.w0, b)
+        gu.assert_close(ck[:, :, m], ref, dtype, f"checkpoint {m}")
+    ref = oracle.linear_bwd(x.q, x.k, x.v, x.eta, x.w0, b, dz, dwT)
+    got = [t.cpu().numpy() for t in grads]
+    for name, a, r in zip(("dq", "dk", "dv", "deta", "dw0"), got, ref):
+        m_ = gu.assert_close(a, r, dtype, f"T={T} b={b} {name}")
+    print(f"{dtype} T={T} b={b} last:", m_)
+
+
+@pytest.mark.parametrize("b", [1, 4, 64])
+def test_backward_1p3b_workload_any_minibatch_sampled_units(b):
+    """The 1.3B workload with b in {1, 4, 64} (primal backward): 16 units
+    spread over the batch and heads against the oracle backward."""
+    x = inputs.make_inputs(3)
+    rng = np.random.default_rng(770 + b)
+    dz = (rng.standard_normal(x.q.shape) * 0.1).astype(np.float32)
+    q, k, v = (gu.dev(x, n) for n in ("q", "k", "v"))
+    eta, w0 = gu.f32(x.eta), gu.f32(x.w0)
+    _, _, ck = ttt_linear_fwd_ckpt(q, k, v, eta, w0, b)
+    got = [t.cpu().numpy() for t in ttt_linear_bwd(q, k, v, eta, ck, b, gu.f32(dz))]
+    torch.cuda.synchronize()
+    idx = list(range(0, 128, 8))
+    dzu = dz.reshape(-1, x.wl.T, 64)
+
+    def one(u):
+        s_ = x.units([u])
+        return oracle.linear_bwd(s_.q, s_.k, s_.v, s_.eta, s_.w0, b, dzu[u][None, None])
+
+    per = gu.oracle_units_parallel(lambda i: one(idx[i]), len(idx))
+    for i, name in enumerate(("dq", "dk", "dv", "deta", "dw0")):
+        ref = np.concatenate([p[i] for p in per], axis=1)
+        sub = got[i].reshape(-1, *got[i].shape[2:])[idx][None]
+        gu.assert_close(sub, ref, "bf16", f"1.3B b={b} {name}")
 
 
 # ---------------------------------------------------------------- sequence chunks

@@ -30,6 +30,10 @@ Time): RNNs with Expressive Hidden States"):
   saturation at eta_base, each at its own (batch, head, token); its
   backward (dtheta_lr, dx from deta) against central finite differences of
   sum deta * eta, and the closed form at theta_lr = 0 (sigmoid' = 1/4);
+* the LayerNorm scan's backward (§6.12 with §4.4), gamma and beta included:
+  central finite differences through the forward oracle, torch's float64
+  autodiff of the independently written dual form, and the eta = 0 closed
+  forms;
 * the TTT-MLP backward (§6.12): central finite differences of
   <dZ, Z> + <dW1_T, W1_T> + <dW2_T, W2_T> through the forward oracle, torch's
   float64 autodiff of the independently written dual form, and the eta = 0
@@ -639,6 +643,84 @@ def pin_mlp_bwd_eta_zero(lib):
         assert rel(g[4][0, h], d1[0, h] + daq.T @ q[0, h]) < 1e-13
 
 
+def _ln_bwd_case(rng, T, d, with_dwT=True):
+    q, k, v, eta, w0 = rand_linear(rng, 1, 2, T, d, eta_scale=0.3, w_scale=0.5)
+    gamma, beta = rand_ln(rng, 2, d)
+    dz = rng.standard_normal(q.shape)
+    dwT = rng.standard_normal((1, 2, d, d)) if with_dwT else None
+    return q, k, v, eta, w0, gamma, beta, dz, dwT
+
+
+def pin_ln_bwd_finite_differences(lib):
+    """The LayerNorm scan's backward against central finite differences of
+    L = <dZ, Z> + <dW_T, W_T> through the forward oracle along a random
+    direction of every input, gamma and beta included (§6.12, §4.4)."""
+    rng = np.random.default_rng(44)
+    eps = 1e-3
+    for (T, b, with_dwT) in [(7, 3, True), (6, 1, True), (5, 8, False), (9, 9, True)]:
+        q, k, v, eta, w0, gamma, beta, dz, dwT = _ln_bwd_case(rng, T, 4, with_dwT)
+        g = oracle.linear_ln_bwd(q, k, v, eta, w0, gamma, beta, eps, b, dz, dwT, lib=lib)
+        base = dict(q=q, k=k, v=v, eta=eta, w0=w0, gamma=gamma, beta=beta)
+
+        def L(**kw):
+            a = dict(base, **kw)
+            z, w = oracle.linear_ln(a["q"], a["k"], a["v"], a["eta"], a["w0"], a["gamma"],
+                                    a["beta"], eps, b, lib=lib)
+            return np.sum(dz * z) + (np.sum(dwT * w) if with_dwT else 0.0)
+
+        h = 1e-4
+        grads = dict(q=g[0], k=g[1], v=g[2], eta=g[3], w0=g[4].sum(axis=0),
+                     gamma=g[5].sum(axis=0), beta=g[6].sum(axis=0))
+        for name, arr in base.items():
+            D = rng.standard_normal(arr.shape)
+            cd = lambda s: (L(**{name: arr + s * D}) - L(**{name: arr - s * D})) / (2 * s)
+            fd = (4.0 * cd(h / 2) - cd(h)) / 3.0  # Richardson: the h^2 term cancels
+            an = float(np.sum(grads[name] * D))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (name, T, b, fd, an)
+
+
+def pin_ln_bwd_equals_autograd_of_dual_form(lib):
+    """The LayerNorm scan's backward equals torch's float64 reverse-mode
+    autodiff of the independently written dual form (tests/dual_form.py)."""
+    import torch
+    rng = np.random.default_rng(45)
+    eps = 1e-3
+    for (T, b) in [(9, 4), (8, 8), (5, 1), (11, 16)]:
+        q, k, v, eta, w0, gamma, beta, dz, dwT = _ln_bwd_case(rng, T, 5)
+        g = oracle.linear_ln_bwd(q, k, v, eta, w0, gamma, beta, eps, b, dz, dwT, lib=lib)
+        for h in range(2):
+            leaves = [torch.tensor(a, dtype=torch.float64, requires_grad=True)
+                      for a in (q[0, h], k[0, h], v[0, h], eta[0, h], w0[h], gamma[h], beta[h])]
+            z, w = dual_form.linear_ln_unit_torch(*leaves, eps, b)
+            ((z * torch.from_numpy(dz[0, h])).sum() + (w * torch.from_numpy(dwT[0, h])).sum()).backward()
+            for i, leaf in enumerate(leaves):
+                assert rel(g[i][0, h], leaf.grad.numpy()) < 1e-11, (T, b, h, i)
+
+
+def pin_ln_bwd_eta_zero(lib):
+    """eta = 0: the state never moves, z_t = q_t + gamma LNhat(W0 q_t) + beta,
+    so dk = dv = 0, dbeta = sum_t dz_t, dgamma = sum_t LNhat(W0 q_t) dz_t and
+    dq_t = dz_t + W0^T J_t (gamma dz_t), with J_t the LayerNorm Jacobian's
+    transpose applied column by column (rs (x - mean x - yh mean(x yh)))."""
+    rng = np.random.default_rng(46)
+    eps = 1e-3
+    q, k, v, eta, w0, gamma, beta, dz, dwT = _ln_bwd_case(rng, 11, 5)
+    eta[:] = 0.0
+    g = oracle.linear_ln_bwd(q, k, v, eta, w0, gamma, beta, eps, 4, dz, dwT, lib=lib)
+    assert not g[1].any() and not g[2].any()
+    for h in range(2):
+        Y = q[0, h] @ w0[h].T                                         # [T, d]
+        mu = Y.mean(axis=1, keepdims=True)
+        rs = 1.0 / np.sqrt(((Y - mu) ** 2).mean(axis=1, keepdims=True) + eps)
+        Yh = (Y - mu) * rs
+        x = gamma[h] * dz[0, h]
+        dY = rs * (x - x.mean(axis=1, keepdims=True) - Yh * (x * Yh).mean(axis=1, keepdims=True))
+        assert rel(g[0][0, h], dz[0, h] + dY @ w0[h]) < 1e-13
+        assert rel(g[6][0, h], dz[0, h].sum(axis=0)) < 1e-13
+        assert rel(g[5][0, h], (Yh * dz[0, h]).sum(axis=0)) < 1e-13
+        assert rel(g[4][0, h], dwT[0, h] + dY.T @ q[0, h]) < 1e-13
+
+
 def pin_gate_closed_forms(lib):
     # theta_lr[h] = c_h e_{p(h)} puts the logit c_h x[b, t, p(h)] at every
     # (b, h, t) on its own; each logit is drawn from the closed-form table, so
@@ -738,6 +820,9 @@ PINS = [
     pin_linear_bwd_finite_differences,
     pin_linear_bwd_equals_dual_form_adjoint,
     pin_linear_bwd_eta_zero,
+    pin_ln_bwd_finite_differences,
+    pin_ln_bwd_equals_autograd_of_dual_form,
+    pin_ln_bwd_eta_zero,
     pin_mlp_bwd_finite_differences,
     pin_mlp_bwd_equals_autograd_of_dual_form,
     pin_mlp_bwd_eta_zero,
@@ -986,6 +1071,17 @@ MUTATIONS = {
     "gate_bwd_dx_from_head_0": ("gx[i] += da * th[i];", "gx[i] += da * theta[i];"),
     "gate_bwd_dtheta_from_first_token": ("+= da * xt[i];", "+= da * x[i];"),
     "gate_bwd_no_base": ("deta[gi] * eta_base * sg", "deta[gi] * sg"),
+    "ln_bwd_drop_rs_adjoint": ("drs += ddy[i] * (g[i] - gbar - yh[i] * m);", ""),
+    "ln_bwd_drop_mean_adjoint": ("+ dm / (double)d * yh[i] + dgbar / (double)d; /* m, gbar */",
+                                 "+ dm / (double)d * yh[i]; /* m, gbar */"),
+    "ln_bwd_variance_factor": ("dc[i] += 2.0 / (double)d * c[i] * dvar;",
+                               "dc[i] += 1.0 / (double)d * c[i] * dvar;"),
+    "ln_bwd_no_residual_in_dq": ("double acc = zt[j]; /* the residual q */",
+                                 "double acc = 0.0; /* the residual q */"),
+    "ln_bwd_gamma_from_f_only": ("dgam[i] += 2.0 * r[i] * dg[i] + yh[i] * dr;",
+                                 "dgam[i] += yh[i] * dr;"),
+    "ln_bwd_dk_through_current_state": ("for (long i = 0; i < d; ++i) acc += P[i * d + j] * dyv[i];",
+                                        "for (long i = 0; i < d; ++i) acc += N[i * d + j] * dyv[i];"),
     "mlp_bwd_drop_gelu_second_derivative": ("da[u] = ddl[u] * s[u] * gelu_grad2(a[u]);",
                                             "da[u] = 0.0;"),
     "mlp_bwd_gelu_second_derivative_form": ("* (2.0 - x * x);", "* (1.0 - x * x);"),
