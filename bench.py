@@ -243,6 +243,7 @@ def ln_case(wl, b, steps, warmup):
         "hbm_frac": byts / (kmean * 1e-6) / 1e9 / HBM_PEAK_GBS,
         "kernel": "linear_ln_scan_kernel (one workgroup per (batch, head))",
         "traffic": traffic_for("linear_ln_scan", LN_SOURCES, wl.name),
+        "sq": sq_for("linear_ln_scan", LN_SOURCES),
     }
     del d, z, w
     torch.cuda.empty_cache()
@@ -284,6 +285,7 @@ def mlp_case(wl, b, steps, warmup, flush_reps=0):
         "hbm_frac_algorithmic": byts / t / 1e9 / HBM_PEAK_GBS,
         "secondary_state_roundtrip_hbm_frac": designed / t / 1e9 / HBM_PEAK_GBS,
         "traffic": traffic_for("mlp_scan", MLP_SOURCES, wl.name),
+        "sq": sq_for("mlp_scan", MLP_SOURCES),
     }
     if flushed:
         res.update(flushed_fields(flushed, t_roof))
@@ -658,6 +660,79 @@ def summarize_pmc(fetch_dir, write_dir):
 
 
 # --------------------------------------------------------------------------
+# SQ counter summary: rocprofv3 --pmc (MFMA / VALU activity) -> JSON + text
+# --------------------------------------------------------------------------
+SQ_FILE = os.path.join(ROOT, "profiles", "sq_counters.json")
+SQ_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
+               "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY")
+SIMDS, CUS = 1024, 256  # MI355X: 256 CUs x 4 SIMDs
+
+
+def summarize_sq(sq_dir):
+    """Reads one rocprofv3 --pmc run of `bench.py --no-extras --no-cpu
+    --pmc-calibrate` with SQ_COUNTERS and reports, per scan kernel (median
+    over its dispatches):
+      mfma_busy  = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMDs): the
+                   fraction of the chip's SIMD-cycles the matrix unit is busy;
+      valu_busy  = SQ_ACTIVE_INST_VALU / (GRBM_GUI_ACTIVE * CUs) (per-CU
+                   cycles with a VALU instruction issued);
+      wait_frac  = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (wave-cycles waiting);
+    plus instruction counts per dispatch.  Writes profiles/sq_counters.json
+    (source-hashed per kernel, as the traffic counters are)."""
+    import csv
+    vals = {}
+    for path in glob.glob(os.path.join(sq_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                c = r.get("Counter_Name")
+                if c in SQ_COUNTERS:
+                    key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+                    d = vals.setdefault(key, {})
+                    if c == "GRBM_GUI_ACTIVE":  # the same clock on every instance
+                        d[c] = max(d.get(c, 0.0), float(r["Counter_Value"]))
+                    else:
+                        d[c] = d.get(c, 0.0) + float(r["Counter_Value"])
+    cases = (("linear_scan", "linear_scan_bf16_kernel", SCAN_SOURCES),
+             ("linear_ln_scan", "linear_ln_scan_kernel", LN_SOURCES),
+             ("mlp_scan", "mlp_scan_kernel", MLP_SOURCES))
+    out = {"counters": list(SQ_COUNTERS), "simds": SIMDS, "cus": CUS}
+    print("SQ counters per dispatch (medians over each kernel's dispatches):")
+    for key, pat, srcs in cases:
+        rows = [d for (disp, name), d in sorted(vals.items()) if pat in name and
+                all(c in d for c in SQ_COUNTERS)]
+        if not rows:
+            continue
+        med = {c: float(np.median([d[c] for d in rows])) for c in SQ_COUNTERS}
+        g = med["GRBM_GUI_ACTIVE"]
+        e = {"dispatches": len(rows), **med,
+             "mfma_busy": med["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * SIMDS),
+             "valu_busy": med["SQ_ACTIVE_INST_VALU"] / (g * CUS),
+             "wait_frac": med["SQ_WAIT_INST_ANY"] / med["SQ_WAVE_CYCLES"],
+             "source_hash": source_hash(srcs)}
+        out[key] = e
+        print(f"{key} ({pat}, {len(rows)} dispatches): GRBM_GUI_ACTIVE {g:.0f} cycles, "
+              f"MFMA busy {e['mfma_busy']:.3f} of all SIMD-cycles, VALU busy {e['valu_busy']:.3f}, "
+              f"waves waiting {e['wait_frac']:.3f} of wave-cycles;\n  per dispatch: "
+              f"{med['SQ_INSTS_MFMA']:.4g} MFMA and {med['SQ_INSTS_VALU']:.4g} VALU instructions "
+              f"(summed over instances), source hash {e['source_hash']}")
+    os.makedirs(os.path.dirname(SQ_FILE), exist_ok=True)
+    with open(SQ_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+
+
+def sq_for(kernel_key: str, sources):
+    """MFMA-busy fraction from committed SQ counters, or None when missing or
+    taken on other kernel sources."""
+    if not os.path.exists(SQ_FILE):
+        return None
+    with open(SQ_FILE) as f:
+        e = json.load(f).get(kernel_key)
+    if not e or e.get("source_hash") != source_hash(sources):
+        return None
+    return {"mfma_busy": e["mfma_busy"], "valu_busy": e["valu_busy"], "wait_frac": e["wait_frac"]}
+
+
+# --------------------------------------------------------------------------
 # Kernel-trace summary: rocprofv3 --kernel-trace --stats output -> text
 # --------------------------------------------------------------------------
 def summarize_trace(trace_dir, pattern, skip, take):
@@ -703,12 +778,17 @@ def main():
     ap.add_argument("--only", choices=("train", "train-long", "train-mlp", "decode", "gate"),
                     help="run one group of the secondary measurements and print it (for profiling)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-sq", metavar="SQ_DIR",
+                    help="summarise a rocprofv3 --pmc run with the SQ counters (MFMA / VALU busy)")
     ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "KERNEL", "SKIP", "TAKE"),
                     help="summarise a rocprofv3 --kernel-trace --stats run of this script")
     args = ap.parse_args()
 
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return 0
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq)
         return 0
     if args.summarize_trace:
         d, k, skip, take = args.summarize_trace
@@ -764,8 +844,8 @@ def main():
         log("[bench] streaming copy calibration (1 GiB)")
         stream_copy_GBps(1 << 30, reps=3)
         w4 = inputs.workload(4)
-        log(f"[bench] {w4.name} (counter coverage of the MLP scan)")
-        mlp_case(w4, 16, 2, 1)
+        log(f"[bench] {w4.name} (counter coverage of the MLP scan, launches after cache flushes)")
+        mlp_case(w4, 16, 2, 1, flush_reps=2)
         w6 = inputs.workload(6)
         log(f"[bench] {w6.name} (counter coverage of the LayerNorm scan)")
         ln_case(w6, 16, 2, 1)
@@ -851,7 +931,8 @@ def main():
                      "settle_ms": head["settle_ms"], "settle_launches": head["settle_launches"],
                      **{k: head[k] for k in ("kernel_us_flushed_median", "kernel_us_flushed_p10",
                                              "kernel_us_flushed_p90", "frac_flushed") if k in head},
-                     "mfma_frac": head["mfma_frac"]},
+                     "mfma_frac": head["mfma_frac"],
+                     "mfma_busy": sq_for("linear_scan", SCAN_SOURCES)},
         "cpu_baseline": cpu,
         "extras": extras,
     }

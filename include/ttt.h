@@ -46,7 +46,7 @@
  *            TTT-Linear: fp32 or bf16 q/k/v; mini-batch b with b | 16 or
  *            16 | b (1, 2, 4, 8, 16, 32, 48, 64, ...).
  *            TTT-MLP: hidden = 256, fp32 or bf16 q/k/v, b | 16 or 16 | b.
- *            TTT-Linear with LayerNorm: bf16 q/k/v, 16 | b.
+ *            TTT-Linear with LayerNorm: fp32 or bf16 q/k/v, b | 16 or 16 | b.
  *            Anything else is TTT_ERR_UNSUPPORTED.
  *            Empty work (B*H == 0) returns TTT_OK without launching; T == 0
  *            copies the initial states to the final-state outputs.
@@ -131,11 +131,13 @@ ttt_status_t ttt_linear_fwd(const void* q, const void* k, const void* v,
  *   eps            : LayerNorm epsilon, finite and > 0, else TTT_ERR_VALUE
  *   z              : out [B][H][T][d] fp32;  w_out : out [B][H][d][d] fp32
  *
- * Support: d = 64, bf16 q/k/v, mini-batch b a multiple of 16 (16, 32, 48,
- * 64, ...); otherwise TTT_ERR_UNSUPPORTED.  Below 16 tokens a mini-batch's
- * gradients depend non-linearly (through the LayerNorm) on the updates of
- * the mini-batches before it inside one 16-token tile, which the one-tile
- * dual form here does not evaluate.  One workgroup per (batch, head).
+ * Support: d = 64, fp32 or bf16 q/k/v, b | 16 or 16 | b.  bf16 with 16 | b
+ * runs the dual form per 16-token tile (one workgroup per (batch, head)).
+ * Below 16 tokens a mini-batch's gradients depend non-linearly, through the
+ * LayerNorm, on the updates of earlier mini-batches in the same tile, which
+ * a one-tile dual form cannot evaluate.  So b < 16 and fp32 inputs run the
+ * primal form token by token in fp32 arithmetic (256 threads per
+ * (batch, head)): exact, and slower per token.
  */
 ttt_status_t ttt_linear_ln_fwd(const void* q, const void* k, const void* v,
                                const float* eta, const float* w0,
@@ -269,6 +271,44 @@ ttt_status_t ttt_mlp_fwd(const void* q, const void* k, const void* v,
                          int32_t H, int32_t T, int32_t d, int32_t hidden,
                          int32_t b, ttt_dtype_t qkv_dtype, float* z,
                          float* w1_out, float* w2_out, void* stream);
+
+/*
+ * Training support for TTT-Linear with the LayerNorm + residual inner model
+ * (§6.12 with §4.4).  Support: d = 64, fp32 or bf16 q/k/v, b | 16 or 16 | b.
+ *
+ * ttt_linear_ln_fwd_ckpt: ttt_linear_ln_fwd plus
+ *   w_ckpt : out [B][H][ceil(T/b)][d][d] fp32, the state before each
+ *            mini-batch of b tokens.
+ * ttt_linear_ln_bwd: the gradient of a loss L(Z, W_T) given
+ *   dz : [B][H][T][d] fp32;  dw_T : [B][H][d][d] fp32 or NULL (zero);
+ *   the forward's q, k, v, eta, ln_gamma, ln_beta, eps; w_ckpt from
+ *   ttt_linear_ln_fwd_ckpt with the same b;
+ * writing (fp32) dq, dk, dv [B][H][T][d], deta [B][H][T], dw0 [B][H][d][d]
+ * and the LayerNorm parameters' adjoints dgamma, dbeta [B][H][d], per unit
+ * (sum over the batch for the shared per-head parameters).
+ * Both run the primal form token by token in fp32 arithmetic, one workgroup
+ * of 256 threads per (batch, head).  The backward replays each mini-batch
+ * from its checkpoint, then takes its tokens back; it applies the adjoint of
+ * every forward operation (the LayerNorm statistics, the LayerNorm VJP of
+ * the inner gradient, the update, the output) in reverse order.  Outputs
+ * must not overlap each other or an input; T = 0 writes dw0 = dw_T (or
+ * zeros) and zero dgamma, dbeta.
+ */
+ttt_status_t ttt_linear_ln_fwd_ckpt(const void* q, const void* k, const void* v,
+                                   const float* eta, const float* w0,
+                                   int32_t w0_per_batch, const float* ln_gamma,
+                                   const float* ln_beta, float eps, int32_t B,
+                                   int32_t H, int32_t T, int32_t d, int32_t b,
+                                   ttt_dtype_t qkv_dtype, float* z, float* w_out,
+                                   float* w_ckpt, void* stream);
+ttt_status_t ttt_linear_ln_bwd(const void* q, const void* k, const void* v,
+                               const float* eta, const float* w_ckpt,
+                               const float* ln_gamma, const float* ln_beta,
+                               float eps, int32_t B, int32_t H, int32_t T,
+                               int32_t d, int32_t b, ttt_dtype_t qkv_dtype,
+                               const float* dz, const float* dw_T, float* dq,
+                               float* dk, float* dv, float* deta, float* dw0,
+                               float* dgamma, float* dbeta, void* stream);
 
 /*
  * Training support for TTT-MLP (§6.12, as for TTT-Linear above; §3.7, §4.4).

@@ -35,6 +35,25 @@ ttt_status_t ttt_linear_fwd_tuned(const void* q, const void* k, const void* v,
                                   int32_t rows_per_workgroup);
 
 /*
+ * ttt_linear_fwd_tuned with the depth of the LDS prefetch ring of the bf16
+ * scan set: ring_depth = 0 is the default (about ten 16-token tiles in flight
+ * ahead of the two being worked on), 1 keeps a single one.  The ring only
+ * changes when tiles land, never what is computed, so results are
+ * bit-identical for every depth; it exists to check that (a shallow ring
+ * would expose a missing wait as a wrong result).  ring_depth = 1 needs bf16
+ * q/k/v and b = 16 (one pass); other values are TTT_ERR_UNSUPPORTED.
+ */
+ttt_status_t ttt_linear_fwd_ring_depth(const void* q, const void* k,
+                                       const void* v, const float* eta,
+                                       const float* w0, int32_t w0_per_batch,
+                                       int32_t B, int32_t H, int32_t T,
+                                       int32_t d, int32_t b,
+                                       ttt_dtype_t qkv_dtype, float* z,
+                                       float* w_out, void* stream,
+                                       int32_t rows_per_workgroup,
+                                       int32_t ring_depth);
+
+/*
  * ttt_linear_fwd with explicit sequence chunks (see "Sequence chunks" at
  * ttt_linear_fwd): seq_chunks = 0 picks as ttt_linear_fwd does, 1 runs one
  * pass, P >= 2 cuts each sequence into P chunks, which needs bf16 q/k/v,

@@ -23,6 +23,8 @@ SIGNATURES = {
                               _vp, _vp, _vp]),
     "ttt_linear_fwd_tuned": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _vp, _vp, _vp, _i32]),
+    "ttt_linear_fwd_ring_depth": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                         _i32, _i32, _vp, _vp, _vp, _i32, _i32]),
     "ttt_linear_fwd_chunked": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                       _i32, _vp, _vp, _vp, _i32, _i32]),
     "ttt_linear_fwd_plan": (_i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp]),
@@ -52,6 +54,11 @@ SIGNATURES = {
                             _i32, _i32, _vp, _vp]),
     "ttt_mlp_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                            _i32, _vp, _vp, _vp, _vp]),
+    "ttt_linear_ln_fwd_ckpt": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, ctypes.c_float,
+                                      _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "ttt_linear_ln_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _i32, _i32,
+                                 _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _vp]),
     "ttt_mlp_fwd_ckpt": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                 _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "ttt_mlp_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,

@@ -58,7 +58,7 @@ def ttt_linear_fwd_plan(B: int, H: int, T: int, b: int, dtype=torch.bfloat16):
 
 
 def ttt_linear_fwd(q, k, v, eta, w0, b: int, z=None, w_out=None, stream=None,
-                   rows_per_workgroup: int = 0, seq_chunks=None):
+                   rows_per_workgroup: int = 0, seq_chunks=None, ring_depth=None):
     """TTT-Linear forward scan (see include/ttt.h).
 
     q, k, v: [B, H, T, d] bf16 or fp32; eta: [B, H, T] fp32; w0: [H, d, d] or
@@ -66,7 +66,8 @@ def ttt_linear_fwd(q, k, v, eta, w0, b: int, z=None, w_out=None, stream=None,
     fp32 are allocated when not given.  Returns (z, w_out).
     rows_per_workgroup (ttt_linear_fwd_tuned) and seq_chunks
     (ttt_linear_fwd_chunked) select the launch shape; by default the library
-    picks both.
+    picks both.  ring_depth (ttt_linear_fwd_ring_depth: 0 default, 1 one tile
+    in flight) sets the bf16 scan's LDS prefetch depth.
     """
     B, H, T, d = q.shape
     if z is None:
@@ -90,7 +91,10 @@ def ttt_linear_fwd(q, k, v, eta, w0, b: int, z=None, w_out=None, stream=None,
     with torch.cuda.device(dev):
         args = (_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w0), per_batch, B, H, T, d, int(b),
                 _dtype_code(q), _ptr(z), _ptr(w_out), _stream(dev, stream))
-        if seq_chunks is not None:
+        if ring_depth is not None:
+            _lib.check(L.ttt_linear_fwd_ring_depth(*args, int(rows_per_workgroup),
+                                                   int(ring_depth)))
+        elif seq_chunks is not None:
             _lib.check(L.ttt_linear_fwd_chunked(*args, int(rows_per_workgroup), int(seq_chunks)))
         elif rows_per_workgroup:
             _lib.check(L.ttt_linear_fwd_tuned(*args, int(rows_per_workgroup)))
@@ -104,7 +108,7 @@ def ttt_linear_ln_fwd(q, k, v, eta, w0, ln_gamma, ln_beta, eps: float, b: int, z
     """TTT-Linear with the LayerNorm + residual inner model, f(x) = x + LN(W x)
     (see include/ttt.h).
 
-    q, k, v: [B, H, T, d] bf16; eta: [B, H, T] fp32; w0: [H, d, d] or
+    q, k, v: [B, H, T, d] bf16 or fp32; eta: [B, H, T] fp32; w0: [H, d, d] or
     [B, H, d, d] fp32; ln_gamma, ln_beta: [H, d] fp32; eps > 0.  Returns
     (z, w_out), allocated when not given.
     """
@@ -137,6 +141,52 @@ def ttt_linear_ln_fwd(q, k, v, eta, w0, ln_gamma, ln_beta, eps: float, b: int, z
                                        int(b), _dtype_code(q), _ptr(z), _ptr(w_out),
                                        _stream(dev, stream)))
     return z, w_out
+
+
+def ttt_linear_ln_fwd_ckpt(q, k, v, eta, w0, ln_gamma, ln_beta, eps: float, b: int, stream=None):
+    """ttt_linear_ln_fwd that also keeps the state before every mini-batch
+    (include/ttt.h).  Returns (z, w_out, w_ckpt), w_ckpt [B, H, ceil(T/b), d, d]."""
+    B, H, T, d = q.shape
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=q.device)
+    z, w_out = f32(B, H, T, d), f32(B, H, d, d)
+    w_ckpt = f32(B, H, (T + b - 1) // b if b > 0 else 0, d, d)
+    dev = _check_tensors(dict(q=q, k=k, v=v, eta=eta, w0=w0, ln_gamma=ln_gamma, ln_beta=ln_beta))
+    for name, t in (("eta", eta), ("w0", w0), ("ln_gamma", ln_gamma), ("ln_beta", ln_beta)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    per_batch = 1 if w0.dim() == 4 else 0
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib().ttt_linear_ln_fwd_ckpt(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w0), per_batch, _ptr(ln_gamma),
+            _ptr(ln_beta), float(eps), B, H, T, d, int(b), _dtype_code(q), _ptr(z), _ptr(w_out),
+            _ptr(w_ckpt), _stream(dev, stream)))
+    return z, w_out, w_ckpt
+
+
+def ttt_linear_ln_bwd(q, k, v, eta, w_ckpt, ln_gamma, ln_beta, eps: float, b: int, dz, dw_T=None,
+                      stream=None):
+    """Backward of TTT-Linear with the LayerNorm + residual inner model
+    (include/ttt.h): returns (dq, dk, dv, deta, dw0, dgamma, dbeta), fp32,
+    with dw0 [B, H, d, d] and dgamma, dbeta [B, H, d] per unit."""
+    B, H, T, d = q.shape
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=q.device)
+    dq, dk, dv, deta = f32(B, H, T, d), f32(B, H, T, d), f32(B, H, T, d), f32(B, H, T)
+    dw0, dg, db = f32(B, H, d, d), f32(B, H, d), f32(B, H, d)
+    dev = _check_tensors(dict(q=q, k=k, v=v, eta=eta, w_ckpt=w_ckpt, ln_gamma=ln_gamma,
+                              ln_beta=ln_beta, dz=dz, dw_T=dw_T))
+    for name, t in (("dz", dz), ("dw_T", dw_T), ("w_ckpt", w_ckpt), ("eta", eta)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if tuple(dz.shape) != (B, H, T, d):
+        raise ValueError("dz must be [B, H, T, d]")
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib().ttt_linear_ln_bwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w_ckpt), _ptr(ln_gamma), _ptr(ln_beta),
+            float(eps), B, H, T, d, int(b), _dtype_code(q), _ptr(dz), _ptr(dw_T), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(deta), _ptr(dw0), _ptr(dg), _ptr(db), _stream(dev, stream)))
+    return dq, dk, dv, deta, dw0, dg, db
 
 
 def ttt_linear_fwd_ckpt(q, k, v, eta, w0, b: int, z=None, w_out=None, w_ckpt=None, stream=None):

@@ -126,7 +126,8 @@ ttt_status_t linear_impl(const void* q, const void* k, const void* v, const floa
                          const float* w0, int32_t w0_per_batch, int32_t B, int32_t H, int32_t T,
                          int32_t d, int32_t b, ttt_dtype_t dt, float* z, float* w_out,
                          void* stream, int32_t rows, float* w_ckpt = nullptr,
-                         const char* fn = "ttt_linear_fwd", bool dry = false, int32_t chunks = 0) {
+                         const char* fn = "ttt_linear_fwd", bool dry = false, int32_t chunks = 0,
+                         int32_t ring_depth = 0) {
   if (rows != 0 && rows != 16 && rows != 32 && rows != 64)
     return fail(TTT_ERR_UNSUPPORTED, "%s: rows_per_workgroup=%d (need 0, 16, 32 or 64)", fn, rows);
   if (chunks < 0) return fail(TTT_ERR_UNSUPPORTED, "%s: seq_chunks=%d must be >= 0", fn, chunks);
@@ -160,6 +161,7 @@ ttt_status_t linear_impl(const void* q, const void* k, const void* v, const floa
     e = ttt::launch_copy_state(w0, w0_per_batch, (int)units, H, d * d, w_out, s);
   } else {
     ttt::LinearArgs a{q, k, v, eta, w0, z, w_out, w0_per_batch, (int)units, H, T, b, w_ckpt};
+    a.ring_depth = ring_depth;
     if (ck_primal)
       e = ttt::launch_linear_primal_ckpt(a, dt == TTT_F32, s);
     else if (P > 1)
@@ -175,8 +177,8 @@ ttt_status_t linear_ln_impl(const void* q, const void* k, const void* v, const f
                             const float* w0, int32_t w0_per_batch, const float* gamma,
                             const float* beta, float eps, int32_t B, int32_t H, int32_t T,
                             int32_t d, int32_t b, ttt_dtype_t dt, float* z, float* w_out,
-                            void* stream) {
-  static const char* fn = "ttt_linear_ln_fwd";
+                            void* stream, float* w_ckpt = nullptr,
+                            const char* fn = "ttt_linear_ln_fwd") {
   const int64_t units = (int64_t)B * H;
   const int64_t es = dt == TTT_F32 ? 4 : 2;
   const int64_t seq = units * T * d;
@@ -185,26 +187,83 @@ ttt_status_t linear_ln_impl(const void* q, const void* k, const void* v, const f
                       rng("w0", w0, (w0_per_batch ? units : (int64_t)H) * d * d * 4),
                       rng("ln_gamma", gamma, (int64_t)H * d * 4),
                       rng("ln_beta", beta, (int64_t)H * d * 4)};
-  const Range out[] = {rng("z", z, seq * 4), rng("w_out", w_out, units * d * d * 4)};
+  const int64_t nck = b > 0 ? units * ((T + b - 1) / b) * d * d * 4 : 0;
+  const Range out[] = {rng("z", z, seq * 4), rng("w_out", w_out, units * d * d * 4),
+                       rng("w_ckpt", w_ckpt, nck)};
   const int pairs[][2] = {{4, 1}};
-  ttt_status_t st = check_common(fn, dt, w0_per_batch, B, H, T, d, b, in, 7, out, 2, pairs, 1, T > 0);
+  ttt_status_t st = check_common(fn, dt, w0_per_batch, B, H, T, d, b, in, 7, out,
+                                 w_ckpt && T > 0 ? 3 : 2, pairs, 1, T > 0);
   if (st != TTT_OK) return st;
   if (!(eps > 0.f) || eps > 3.0e38f)
     return fail(TTT_ERR_VALUE, "%s: eps=%g must be finite and > 0", fn, (double)eps);
-  if (dt != TTT_BF16) return fail(TTT_ERR_UNSUPPORTED, "%s: only bf16 q/k/v are supported", fn);
-  if (b % 16 != 0)
-    return fail(TTT_ERR_UNSUPPORTED, "%s: mini-batch b=%d unsupported (need 16 | b)", fn, b);
   if (units == 0) return TTT_OK;
+  // bf16 with 16 | b and no checkpoints: the dual-form kernel; otherwise the
+  // primal-form kernel
+  const bool primal = dt != TTT_BF16 || b % 16 != 0 || w_ckpt != nullptr;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (T == 0) {
     if (w0_per_batch && w0 == w_out) return TTT_OK;
     e = ttt::launch_copy_state(w0, w0_per_batch, (int)units, H, d * d, w_out, s);
   } else {
-    ttt::LinearLnArgs a{{q, k, v, eta, w0, z, w_out, w0_per_batch, (int)units, H, T, b},
+    ttt::LinearLnArgs a{{q, k, v, eta, w0, z, w_out, w0_per_batch, (int)units, H, T, b, w_ckpt},
                         gamma, beta, eps};
-    e = ttt::launch_linear_ln(a, s);
+    e = primal ? ttt::launch_linear_ln_primal(a, dt == TTT_F32, s) : ttt::launch_linear_ln(a, s);
   }
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return TTT_OK;
+}
+
+ttt_status_t linear_ln_bwd_impl(const void* q, const void* k, const void* v, const float* eta,
+                                const float* w_ckpt, const float* gamma, const float* beta,
+                                float eps, int32_t B, int32_t H, int32_t T, int32_t d, int32_t b,
+                                ttt_dtype_t dt, const float* dz, const float* dw_T, float* dq,
+                                float* dk, float* dv, float* deta, float* dw0, float* dgamma,
+                                float* dbeta, void* stream) {
+  static const char* fn = "ttt_linear_ln_bwd";
+  if (dt != TTT_F32 && dt != TTT_BF16) return fail(TTT_ERR_DTYPE, "%s: unknown qkv_dtype %d", fn, (int)dt);
+  if (B < 0 || H < 0 || T < 0 || d < 0 || b < 0)
+    return fail(TTT_ERR_SHAPE, "%s: negative size (B=%d H=%d T=%d d=%d b=%d)", fn, B, H, T, d, b);
+  if (d != 64) return fail(TTT_ERR_UNSUPPORTED, "%s: head dim d=%d unsupported (only 64)", fn, d);
+  if (!supported_b(b))
+    return fail(TTT_ERR_UNSUPPORTED, "%s: mini-batch b=%d unsupported (need b | 16 or 16 | b)", fn, b);
+  if (!(eps > 0.f) || eps > 3.0e38f)
+    return fail(TTT_ERR_VALUE, "%s: eps=%g must be finite and > 0", fn, (double)eps);
+  const int64_t units = (int64_t)B * H;
+  const int64_t seq = units * T * d;
+  if (seq >= ((int64_t)1 << 31))
+    return fail(TTT_ERR_SHAPE, "%s: B*H*T*d = %lld exceeds 2^31 - 1", fn, (long long)seq);
+  if (T >= (1 << 24)) return fail(TTT_ERR_SHAPE, "%s: T = %d exceeds 2^24 - 1", fn, T);
+  if (units == 0) return TTT_OK;
+  const int64_t es = dt == TTT_F32 ? 4 : 2;
+  const int64_t nck = units * ((T + b - 1) / b) * d * d * 4;
+  const Range in[] = {rng("q", q, seq * es), rng("k", k, seq * es), rng("v", v, seq * es),
+                      rng("eta", eta, units * T * 4), rng("w_ckpt", w_ckpt, nck),
+                      rng("dz", dz, seq * 4), rng("ln_gamma", gamma, (int64_t)H * d * 4),
+                      rng("ln_beta", beta, (int64_t)H * d * 4),
+                      rng("dw_T", dw_T, units * d * d * 4)};
+  const Range out[] = {rng("dq", dq, seq * 4), rng("dk", dk, seq * 4), rng("dv", dv, seq * 4),
+                       rng("deta", deta, units * T * 4), rng("dw0", dw0, units * d * d * 4),
+                       rng("dgamma", dgamma, units * d * 4), rng("dbeta", dbeta, units * d * 4)};
+  for (int i = 0; i < 9; ++i) {
+    if ((i < 6 && T == 0) || (i == 8 && !dw_T)) continue;  // gamma, beta always
+    if (!in[i].lo) return fail(TTT_ERR_NULL, "%s: %s is NULL", fn, in[i].name);
+    if (in[i].lo & 15) return fail(TTT_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, in[i].name);
+  }
+  for (int o = 0; o < 7; ++o) {
+    if (o < 4 && T == 0) continue;
+    if (!out[o].lo) return fail(TTT_ERR_NULL, "%s: %s is NULL", fn, out[o].name);
+    if (out[o].lo & 15) return fail(TTT_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, out[o].name);
+    for (int i = 0; i < 9; ++i)
+      if (overlap(out[o], in[i]))
+        return fail(TTT_ERR_ALIAS, "%s: %s overlaps input %s", fn, out[o].name, in[i].name);
+    for (int o2 = o + 1; o2 < 7; ++o2)
+      if (overlap(out[o], out[o2]))
+        return fail(TTT_ERR_ALIAS, "%s: %s and %s overlap", fn, out[o].name, out[o2].name);
+  }
+  ttt::LinearLnBwdArgs a{q,  k,  v,  eta, w_ckpt, gamma, beta,  eps,        dz,    dw_T, dq,
+                         dk, dv, deta, dw0, dgamma, dbeta, (int)units, H, T,  b};
+  const hipError_t e = ttt::launch_linear_ln_primal_bwd(a, dt == TTT_F32, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return TTT_OK;
 }
@@ -614,6 +673,20 @@ ttt_status_t ttt_linear_fwd_tuned(const void* q, const void* k, const void* v, c
                      rows_per_workgroup, nullptr, "ttt_linear_fwd_tuned", false, 1);
 }
 
+ttt_status_t ttt_linear_fwd_ring_depth(const void* q, const void* k, const void* v,
+                                       const float* eta, const float* w0, int32_t w0_per_batch,
+                                       int32_t B, int32_t H, int32_t T, int32_t d, int32_t b,
+                                       ttt_dtype_t qkv_dtype, float* z, float* w_out, void* stream,
+                                       int32_t rows_per_workgroup, int32_t ring_depth) {
+  static const char* fn = "ttt_linear_fwd_ring_depth";
+  if (ring_depth != 0 && ring_depth != 1)
+    return fail(TTT_ERR_UNSUPPORTED, "%s: ring_depth=%d (need 0 or 1)", fn, ring_depth);
+  if (ring_depth == 1 && (qkv_dtype != TTT_BF16 || b != 16))
+    return fail(TTT_ERR_UNSUPPORTED, "%s: ring_depth = 1 needs bf16 q/k/v and b = 16", fn);
+  return linear_impl(q, k, v, eta, w0, w0_per_batch, B, H, T, d, b, qkv_dtype, z, w_out, stream,
+                     rows_per_workgroup, nullptr, fn, false, 1, ring_depth);
+}
+
 ttt_status_t ttt_linear_fwd_plan(int32_t B, int32_t H, int32_t T, int32_t b, ttt_dtype_t qkv_dtype,
                                  int32_t* rows_per_workgroup, int32_t* seq_chunks) {
   static const char* fn = "ttt_linear_fwd_plan";
@@ -645,6 +718,27 @@ ttt_status_t ttt_linear_ln_fwd(const void* q, const void* k, const void* v, cons
                                float* w_out, void* stream) {
   return linear_ln_impl(q, k, v, eta, w0, w0_per_batch, ln_gamma, ln_beta, eps, B, H, T, d, b,
                         qkv_dtype, z, w_out, stream);
+}
+
+ttt_status_t ttt_linear_ln_fwd_ckpt(const void* q, const void* k, const void* v,
+                                   const float* eta, const float* w0, int32_t w0_per_batch,
+                                   const float* ln_gamma, const float* ln_beta, float eps,
+                                   int32_t B, int32_t H, int32_t T, int32_t d, int32_t b,
+                                   ttt_dtype_t qkv_dtype, float* z, float* w_out, float* w_ckpt,
+                                   void* stream) {
+  if (T > 0 && !w_ckpt) return fail(TTT_ERR_NULL, "ttt_linear_ln_fwd_ckpt: w_ckpt is NULL");
+  return linear_ln_impl(q, k, v, eta, w0, w0_per_batch, ln_gamma, ln_beta, eps, B, H, T, d, b,
+                        qkv_dtype, z, w_out, stream, w_ckpt, "ttt_linear_ln_fwd_ckpt");
+}
+
+ttt_status_t ttt_linear_ln_bwd(const void* q, const void* k, const void* v, const float* eta,
+                               const float* w_ckpt, const float* ln_gamma, const float* ln_beta,
+                               float eps, int32_t B, int32_t H, int32_t T, int32_t d, int32_t b,
+                               ttt_dtype_t qkv_dtype, const float* dz, const float* dw_T,
+                               float* dq, float* dk, float* dv, float* deta, float* dw0,
+                               float* dgamma, float* dbeta, void* stream) {
+  return linear_ln_bwd_impl(q, k, v, eta, w_ckpt, ln_gamma, ln_beta, eps, B, H, T, d, b, qkv_dtype,
+                            dz, dw_T, dq, dk, dv, deta, dw0, dgamma, dbeta, stream);
 }
 
 ttt_status_t ttt_mlp_fwd_ckpt(const void* q, const void* k, const void* v, const float* eta,

@@ -48,6 +48,7 @@ struct LinearArgs {
   int wout_stride = 4096;  // floats between the final states of consecutive units
   int wout_every = 1;      // only units u with u % wout_every == wout_every - 1 write their
                            // final state, to w_out + (u / wout_every) * wout_stride
+  int ring_depth = 0;      // bf16, b = 16: 0 = the default LDS ring depth, 1 = one tile in flight
 };
 
 enum { W0_ARG = 0, W0_IDENTITY = 1, W0_ZERO = 2, W0_IN_Z = 3 };
@@ -70,6 +71,35 @@ struct LinearLnArgs {
   const float* beta;
   float eps;
 };
+
+// TTT-Linear with the LayerNorm + residual inner model, primal form (any b,
+// fp32 or bf16 q/k/v): the forward (s.w_ckpt non-NULL: also the state before
+// every mini-batch, [units][ceil(T/b)][64][64]) and the backward.
+hipError_t launch_linear_ln_primal(const LinearLnArgs& a, bool f32in, hipStream_t s);
+struct LinearLnBwdArgs {
+  const void* q;          // [units][T][64]
+  const void* k;
+  const void* v;
+  const float* eta;       // [units][T]
+  const float* w_ckpt;    // [units][ceil(T/b)][64][64]
+  const float* gamma;     // [H][64]
+  const float* beta;
+  float eps;
+  const float* dz;        // [units][T][64]
+  const float* dw_T;      // [units][64][64] or NULL
+  float* dq;              // [units][T][64]
+  float* dk;
+  float* dv;
+  float* deta;            // [units][T]
+  float* dw0;             // [units][64][64]
+  float* dgamma;          // [units][64]
+  float* dbeta;
+  int units;
+  int H;
+  int T;
+  int b;
+};
+hipError_t launch_linear_ln_primal_bwd(const LinearLnBwdArgs& a, bool f32in, hipStream_t s);
 
 struct MlpArgs {
   const void* q;

@@ -59,14 +59,19 @@ namespace {
 
 enum { MODE_B16 = 0, MODE_SUB = 1, MODE_MULTI = 2 };
 
-template <int ROWS>
+// DEPTH: tiles the loader keeps in flight beyond the two the compute waves
+// are working on (0 = the default, as many as the vmcnt field can count, at
+// most 10).  Any depth >= 1 gives bit-identical results: the ring only
+// changes when tiles land, never what is computed.
+template <int ROWS, int DEPTH = 0>
 struct Geom {
   static constexpr int NCW = ROWS / 16;
   static constexpr int KB = 16 * 64 * 2;         // K or Q tile (bf16)
   static constexpr int VB = 16 * ROWS * 2;       // V tile, this slice's columns
   static constexpr int RAW = 2 * KB + VB + 64;   // + eta (16 fp32)
   static constexpr int NI = 4 + (VB + 1023) / 1024 + 1;  // DMA ops per tile
-  static constexpr int D = (63 / NI) < 10 ? (63 / NI) : 10;
+  static constexpr int D = DEPTH > 0 ? DEPTH : ((63 / NI) < 10 ? (63 / NI) : 10);
+  static_assert(D >= 1 && NI * D < 64, "in-flight DMA count must fit vmcnt");
   static constexpr int NST = D + 3;
   // prepared-operand slot (per tile), byte offsets
   static constexpr int P_E2 = 0;                  // 2 eta_t, 16 fp32
@@ -84,10 +89,10 @@ struct Geom {
 // the arguments (other multiples of 16).  Unused below b = 16.
 // CKPT (b = 16 only): also store the state at the start of every tile, the
 // checkpoints the backward pass reads.
-template <int MODE, int ROWS, int TPM, bool CKPT = false>
+template <int MODE, int ROWS, int TPM, bool CKPT = false, int DEPTH = 0>
 __global__ void __launch_bounds__((Geom<ROWS>::THREADS))
 linear_scan_bf16_kernel(LinearArgs a) {
-  using G = Geom<ROWS>;
+  using G = Geom<ROWS, DEPTH>;
   constexpr int NSPLIT = 64 / ROWS;
   // with checkpoints: per compute wave a 16-row staging tile (rows padded by 4 words)
   constexpr int CK_TILE = CKPT ? 16 * 68 * 4 : 0;
@@ -507,20 +512,20 @@ linear_scan_bf16_kernel(LinearArgs a) {
   }
 }
 
-template <int MODE, int ROWS, int TPM, bool CKPT = false>
+template <int MODE, int ROWS, int TPM, bool CKPT = false, int DEPTH = 0>
 hipError_t launch_one(const LinearArgs& a, hipStream_t s) {
   constexpr int NSPLIT = 64 / ROWS;
   const int blocks = NSPLIT == 1 ? a.units : ((a.units + 7) / 8) * 8 * NSPLIT;
-  return launch(linear_scan_bf16_kernel<MODE, ROWS, TPM, CKPT>, dim3(blocks),
+  return launch(linear_scan_bf16_kernel<MODE, ROWS, TPM, CKPT, DEPTH>, dim3(blocks),
                 dim3(Geom<ROWS>::THREADS), s, a);
 }
 
-template <int MODE, int TPM, bool CKPT = false>
+template <int MODE, int TPM, bool CKPT = false, int DEPTH = 0>
 hipError_t launch_rows(const LinearArgs& a, int rows, hipStream_t s) {
   switch (rows) {
-    case 64: return launch_one<MODE, 64, TPM, CKPT>(a, s);
-    case 32: return launch_one<MODE, 32, TPM, CKPT>(a, s);
-    default: return launch_one<MODE, 16, TPM, CKPT>(a, s);
+    case 64: return launch_one<MODE, 64, TPM, CKPT, DEPTH>(a, s);
+    case 32: return launch_one<MODE, 32, TPM, CKPT, DEPTH>(a, s);
+    default: return launch_one<MODE, 16, TPM, CKPT, DEPTH>(a, s);
   }
 }
 
@@ -622,6 +627,8 @@ hipError_t launch_linear_chunked(const LinearArgs& a, int P, int rows, hipStream
 
 hipError_t launch_linear_bf16(const LinearArgs& a, int rows, hipStream_t s) {
   if (a.w_ckpt) return a.b == 16 ? launch_rows<MODE_B16, 1, true>(a, rows, s) : hipErrorInvalidValue;
+  if (a.ring_depth == 1) return a.b == 16 ? launch_rows<MODE_B16, 1, false, 1>(a, rows, s)
+                                          : hipErrorInvalidValue;
   if (a.b == 16) return launch_rows<MODE_B16, 1>(a, rows, s);
   if (a.b < 16) return launch_rows<MODE_SUB, 1>(a, rows, s);
   if (a.b == 32) return launch_rows<MODE_MULTI, 2>(a, rows, s);

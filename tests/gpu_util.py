@@ -73,10 +73,10 @@ def oracle_units_parallel(fn, n_units, threads=None):
         return list(ex.map(fn, range(n_units)))
 
 
-def run_linear(x, b, rows=0):
+def run_linear(x, b, rows=0, ring_depth=None):
     from test_rnn_layers_head_amd import ttt_linear_fwd
     z, w = ttt_linear_fwd(dev(x, "q"), dev(x, "k"), dev(x, "v"), f32(x.eta), f32(x.w0), b,
-                          rows_per_workgroup=rows)
+                          rows_per_workgroup=rows, ring_depth=ring_depth)
     torch.cuda.synchronize()
     return z.cpu().numpy(), w.cpu().numpy()
 

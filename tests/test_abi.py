@@ -103,6 +103,25 @@ def test_linear_chunked_argument_checks(lib, kw, expect):
         assert lib.ttt_last_error().startswith(b"ttt_linear_fwd_chunked:")
 
 
+@pytest.mark.parametrize("depth,b,dt,kw,expect", [
+    (2, 16, _lib.TTT_BF16, {}, "TTT_ERR_UNSUPPORTED"),
+    (-1, 16, _lib.TTT_BF16, {}, "TTT_ERR_UNSUPPORTED"),
+    (1, 8, _lib.TTT_BF16, {}, "TTT_ERR_UNSUPPORTED"),
+    (1, 16, _lib.TTT_F32, {}, "TTT_ERR_UNSUPPORTED"),
+    (1, 16, _lib.TTT_BF16, dict(z=A[0]), "TTT_ERR_ALIAS"),
+    (1, 16, _lib.TTT_BF16, dict(B=0), "TTT_OK"),
+])
+def test_linear_ring_depth_argument_checks(lib, depth, b, dt, kw, expect):
+    args = dict(q=A[0], k=A[1], v=A[2], eta=A[3], w0=A[4], B=1, H=1, T=64, z=A[5], w=A[6])
+    args.update(kw)
+    r = lib.ttt_linear_fwd_ring_depth(args["q"], args["k"], args["v"], args["eta"], args["w0"], 0,
+                                      args["B"], args["H"], args["T"], 64, b, dt, args["z"],
+                                      args["w"], None, 0, depth)
+    assert r == status(expect), lib.ttt_last_error()
+    if expect != "TTT_OK":
+        assert lib.ttt_last_error().startswith(b"ttt_linear_fwd_ring_depth:")
+
+
 @pytest.mark.parametrize("B,H,T,b,dt,want", [
     (4, 32, 8192, 16, _lib.TTT_BF16, (32, 1)),      # the 1.3B workload: one pass
     (1, 32, 32768, 16, _lib.TTT_BF16, (64, 8)),     # long context: 8 chunks of 4096
@@ -171,9 +190,9 @@ def test_linear_argument_checks(lib, kw, expect):
     (dict(eps=-1.0), "TTT_ERR_VALUE"),
     (dict(eps=float("nan")), "TTT_ERR_VALUE"),
     (dict(eps=float("inf")), "TTT_ERR_VALUE"),
-    (dict(b=8), "TTT_ERR_UNSUPPORTED"),
-    (dict(b=4), "TTT_ERR_UNSUPPORTED"),
-    (dict(dt=_lib.TTT_F32), "TTT_ERR_UNSUPPORTED"),
+    (dict(b=24), "TTT_ERR_UNSUPPORTED"),
+    (dict(b=3), "TTT_ERR_UNSUPPORTED"),
+    (dict(dt=6), "TTT_ERR_DTYPE"),
     (dict(gamma=None), "TTT_ERR_NULL"),
     (dict(beta=A[8] + 8), "TTT_ERR_ALIGN"),
     (dict(z=A[7]), "TTT_ERR_ALIAS"),
@@ -403,3 +422,44 @@ def test_mlp_fwd_ckpt_argument_checks(lib):
     assert f(c1=None) == status("TTT_ERR_NULL")
     assert f(c2=A[0]) == status("TTT_ERR_ALIAS")     # checkpoints over q
     assert f(b=24) == status("TTT_ERR_UNSUPPORTED")
+
+
+def ln_bwd(lib, **kw):
+    a = dict(q=A[0], k=A[1], v=A[2], eta=A[3], ck=A[4], gamma=A[5], beta=A[6], eps=1e-5, B=1, H=2,
+             T=37, d=64, b=16, dt=_lib.TTT_BF16, dz=A[7], dwT=None, dq=A[8], dk=A[9], dv=A[10],
+             deta=A[11], dw0=A[12], dg=A[13], db=A[13] + 4096)
+    a.update(kw)
+    return lib.ttt_linear_ln_bwd(a["q"], a["k"], a["v"], a["eta"], a["ck"], a["gamma"], a["beta"],
+                                 a["eps"], a["B"], a["H"], a["T"], a["d"], a["b"], a["dt"], a["dz"],
+                                 a["dwT"], a["dq"], a["dk"], a["dv"], a["deta"], a["dw0"], a["dg"],
+                                 a["db"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(b=24), "TTT_ERR_UNSUPPORTED"),
+    (dict(d=32), "TTT_ERR_UNSUPPORTED"),
+    (dict(dt=4), "TTT_ERR_DTYPE"),
+    (dict(eps=0.0), "TTT_ERR_VALUE"),
+    (dict(T=-1), "TTT_ERR_SHAPE"),
+    (dict(B=1, H=1, T=1 << 24), "TTT_ERR_SHAPE"),
+    (dict(ck=None), "TTT_ERR_NULL"),
+    (dict(gamma=None, T=0), "TTT_ERR_NULL"),     # gamma, beta needed even without tokens
+    (dict(dz=A[7] + 4), "TTT_ERR_ALIGN"),
+    (dict(dq=A[4]), "TTT_ERR_ALIAS"),            # an output over the checkpoints
+    (dict(db=A[13] + 256), "TTT_ERR_ALIAS"),     # dgamma and dbeta overlap
+    (dict(B=0), "TTT_OK"),
+])
+def test_linear_ln_bwd_argument_checks(lib, kw, expect):
+    assert ln_bwd(lib, **kw) == status(expect), lib.ttt_last_error()
+    if expect != "TTT_OK":
+        assert lib.ttt_last_error().startswith(b"ttt_linear_ln_bwd:")
+
+
+def test_linear_ln_fwd_ckpt_argument_checks(lib):
+    f = lambda **kw: lib.ttt_linear_ln_fwd_ckpt(A[0], A[1], A[2], A[3], A[4], 0, A[7], A[8], 1e-5,
+                                                1, 1, 16, 64, kw.get("b", 16), _lib.TTT_BF16, A[5],
+                                                A[6], kw.get("ck", A[9]), None)
+    assert f(ck=None) == status("TTT_ERR_NULL")
+    assert f(ck=A[0]) == status("TTT_ERR_ALIAS")
+    assert f(b=24) == status("TTT_ERR_UNSUPPORTED")
+    assert lib.ttt_last_error().startswith(b"ttt_linear_ln_fwd_ckpt:")

@@ -117,6 +117,25 @@ def test_row_split_is_bit_identical(dtype, b):
         assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]), rows
 
 
+@pytest.mark.parametrize("rows", [16, 32, 64])
+@pytest.mark.parametrize("T", [1, 16, 37, 300, 2048])
+def test_ring_depth_one_is_bit_identical(rows, T):
+    """The bf16 scan's LDS prefetch ring only decides when tiles land: one
+    tile in flight must give the same bits as the default depth (a missing
+    wait would show here as a difference)."""
+    x = small(3, 5, T, "bf16", seed=70 + T)
+    ref = gu.run_linear(x, 16, rows=rows)
+    got = gu.run_linear(x, 16, rows=rows, ring_depth=1)
+    assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]), (rows, T)
+    assert np.array_equal(gu.run_linear(x, 16, rows=rows, ring_depth=0)[0], ref[0])
+
+
+@pytest.mark.parametrize("b, dtype, depth", [(16, "bf16", 2), (8, "bf16", 1), (16, "f32", 1)])
+def test_ring_depth_rejections(b, dtype, depth):
+    with pytest.raises(TTTError, match="TTT_ERR_UNSUPPORTED"):
+        gu.run_linear(small(1, 2, 32, dtype, seed=71), b, ring_depth=depth)
+
+
 def test_deterministic_reruns():
     x = small(4, 8, 300, "bf16", seed=8)
     a = gu.run_linear(x, 16)
