@@ -423,8 +423,9 @@ def training_case(wl, steps, warmup):
 
 def mlp_training_case(wl, b, steps, warmup):
     """ttt_mlp_fwd_ckpt then ttt_mlp_bwd on one TTT-MLP workload, timed
-    separately; dz is a seeded N(0, 0.01) draw.  Both run the primal-form
-    kernels (fp32 arithmetic, one token at a time)."""
+    separately; dz is a seeded N(0, 0.01) draw.  The forward is the bf16
+    dual-form scan with checkpoint stores (b | 16), the backward the primal
+    form (fp32 arithmetic, one token at a time)."""
     import torch
     from test_rnn_layers_head_amd import inputs, ttt_mlp_bwd, ttt_mlp_fwd_ckpt
     x = inputs.make_inputs(wl)
@@ -450,7 +451,8 @@ def mlp_training_case(wl, b, steps, warmup):
             "fwd_hbm_frac": fb / (kf * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "bwd_hbm_frac": bb / (kb * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "train_token_heads_per_s": wl.token_heads / ((kf + kb) * 1e-6),
-            "kernels": "mlp_primal_kernel (checkpoints) / mlp_primal_bwd_kernel"}
+            "kernels": ("mlp_scan_kernel with checkpoint stores" if b <= 16 and 16 % b == 0
+                        else "mlp_primal_kernel (checkpoints)") + " / mlp_primal_bwd_kernel"}
 
 
 def gate_alg_bytes(wl) -> int:
@@ -665,56 +667,85 @@ def summarize_pmc(fetch_dir, write_dir):
 SQ_FILE = os.path.join(ROOT, "profiles", "sq_counters.json")
 SQ_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
                "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY")
-SIMDS, CUS = 1024, 256  # MI355X: 256 CUs x 4 SIMDs
+SIMDS, CUS, XCDS = 1024, 256, 8  # MI355X: 8 XCDs x 32 CUs x 4 SIMDs
+
+
+def sq_derive(med, active_cus):
+    """Per-kernel readings from the dispatch's counter values (rocprofv3
+    reports each counter summed over its hardware instances):
+      clock      = GRBM_GUI_ACTIVE / XCDs: the kernel's duration in GPU
+                   cycles (the counter runs once per XCD);
+      mfma_busy  = SQ_VALU_MFMA_BUSY_CYCLES / (clock * SIMDs): the fraction
+                   of the chip's SIMD-cycles the matrix unit is busy (the
+                   counter sums busy cycles over SIMDs; one 16x16x32 bf16
+                   MFMA reads 16);
+      valu_busy  = 4 SQ_ACTIVE_INST_VALU / (clock * SIMDs): the same for VALU
+                   issue (the counter is in quad-cycles: one per wave64 VALU
+                   instruction, as SQ_INSTS_VALU shows);
+      *_active   = the same over the SIMDs of the CUs that have work
+                   (one workgroup per CU: min(workgroups, CUs));
+      wait_frac  = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (wave-cycles waiting)."""
+    clock = med["GRBM_GUI_ACTIVE"] / XCDS
+    mfma = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (clock * SIMDS)
+    valu = 4.0 * med["SQ_ACTIVE_INST_VALU"] / (clock * SIMDS)
+    share = CUS / active_cus
+    return {"clock_cycles": clock, "mfma_busy": mfma, "valu_busy": valu,
+            "mfma_busy_active": mfma * share, "valu_busy_active": valu * share,
+            "mfma_cycles_per_inst": med["SQ_VALU_MFMA_BUSY_CYCLES"] / med["SQ_INSTS_MFMA"],
+            "wait_frac": med["SQ_WAIT_INST_ANY"] / med["SQ_WAVE_CYCLES"]}
+
+
+SQ_CASES = (("linear_scan", "linear_scan_bf16_kernel", "SCAN_SOURCES", 256),   # 2 workgroups x 128 units
+            ("linear_ln_scan", "linear_ln_scan_kernel", "LN_SOURCES", 128),   # 128 units
+            ("mlp_scan", "mlp_scan_kernel", "MLP_SOURCES", 96))               # 96 units
 
 
 def summarize_sq(sq_dir):
     """Reads one rocprofv3 --pmc run of `bench.py --no-extras --no-cpu
     --pmc-calibrate` with SQ_COUNTERS and reports, per scan kernel (median
-    over its dispatches):
-      mfma_busy  = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMDs): the
-                   fraction of the chip's SIMD-cycles the matrix unit is busy;
-      valu_busy  = SQ_ACTIVE_INST_VALU / (GRBM_GUI_ACTIVE * CUs) (per-CU
-                   cycles with a VALU instruction issued);
-      wait_frac  = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (wave-cycles waiting);
-    plus instruction counts per dispatch.  Writes profiles/sq_counters.json
-    (source-hashed per kernel, as the traffic counters are)."""
+    over its dispatches), the readings of sq_derive plus instruction counts.
+    Writes profiles/sq_counters.json (source-hashed per kernel, as the
+    traffic counters are).  A JSON file written earlier can be given instead
+    of the run's directory: the readings are then derived again from its
+    medians (same sources required)."""
     import csv
     vals = {}
-    for path in glob.glob(os.path.join(sq_dir, "**", "*counter_collection.csv"), recursive=True):
-        with open(path) as f:
-            for r in csv.DictReader(f):
-                c = r.get("Counter_Name")
-                if c in SQ_COUNTERS:
-                    key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
-                    d = vals.setdefault(key, {})
-                    if c == "GRBM_GUI_ACTIVE":  # the same clock on every instance
-                        d[c] = max(d.get(c, 0.0), float(r["Counter_Value"]))
-                    else:
+    meds = {}
+    if sq_dir.endswith(".json"):
+        with open(sq_dir) as f:
+            old = json.load(f)
+        meds = {k: {c: old[k][c] for c in SQ_COUNTERS} | {"dispatches": old[k]["dispatches"]}
+                for k, _, _, _ in SQ_CASES if k in old}
+    else:
+        for path in glob.glob(os.path.join(sq_dir, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    c = r.get("Counter_Name")
+                    if c in SQ_COUNTERS:
+                        key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+                        d = vals.setdefault(key, {})
                         d[c] = d.get(c, 0.0) + float(r["Counter_Value"])
-    cases = (("linear_scan", "linear_scan_bf16_kernel", SCAN_SOURCES),
-             ("linear_ln_scan", "linear_ln_scan_kernel", LN_SOURCES),
-             ("mlp_scan", "mlp_scan_kernel", MLP_SOURCES))
-    out = {"counters": list(SQ_COUNTERS), "simds": SIMDS, "cus": CUS}
+        for key, pat, _, _ in SQ_CASES:
+            rows = [d for (disp, name), d in sorted(vals.items()) if pat in name and
+                    all(c in d for c in SQ_COUNTERS)]
+            if rows:
+                meds[key] = {c: float(np.median([d[c] for d in rows])) for c in SQ_COUNTERS}
+                meds[key]["dispatches"] = len(rows)
+    out = {"counters": list(SQ_COUNTERS), "simds": SIMDS, "cus": CUS, "xcds": XCDS}
     print("SQ counters per dispatch (medians over each kernel's dispatches):")
-    for key, pat, srcs in cases:
-        rows = [d for (disp, name), d in sorted(vals.items()) if pat in name and
-                all(c in d for c in SQ_COUNTERS)]
-        if not rows:
+    for key, pat, srcs, active in SQ_CASES:
+        if key not in meds:
             continue
-        med = {c: float(np.median([d[c] for d in rows])) for c in SQ_COUNTERS}
-        g = med["GRBM_GUI_ACTIVE"]
-        e = {"dispatches": len(rows), **med,
-             "mfma_busy": med["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * SIMDS),
-             "valu_busy": med["SQ_ACTIVE_INST_VALU"] / (g * CUS),
-             "wait_frac": med["SQ_WAIT_INST_ANY"] / med["SQ_WAVE_CYCLES"],
-             "source_hash": source_hash(srcs)}
+        med = meds[key]
+        e = {**med, **sq_derive(med, active), "active_cus": active,
+             "source_hash": source_hash(globals()[srcs])}
         out[key] = e
-        print(f"{key} ({pat}, {len(rows)} dispatches): GRBM_GUI_ACTIVE {g:.0f} cycles, "
-              f"MFMA busy {e['mfma_busy']:.3f} of all SIMD-cycles, VALU busy {e['valu_busy']:.3f}, "
-              f"waves waiting {e['wait_frac']:.3f} of wave-cycles;\n  per dispatch: "
-              f"{med['SQ_INSTS_MFMA']:.4g} MFMA and {med['SQ_INSTS_VALU']:.4g} VALU instructions "
-              f"(summed over instances), source hash {e['source_hash']}")
+        print(f"{key} ({pat}, {med['dispatches']} dispatches): {e['clock_cycles']:.0f} GPU cycles; "
+              f"MFMA busy {e['mfma_busy']:.3f} of all SIMD-cycles ({e['mfma_busy_active']:.3f} on the "
+              f"{active} CUs with work; {e['mfma_cycles_per_inst']:.1f} cycles per MFMA), VALU busy "
+              f"{e['valu_busy']:.3f} ({e['valu_busy_active']:.3f}), waves waiting "
+              f"{e['wait_frac']:.3f} of wave-cycles;\n  per dispatch: {med['SQ_INSTS_MFMA']:.4g} MFMA "
+              f"and {med['SQ_INSTS_VALU']:.4g} VALU instructions, source hash {e['source_hash']}")
     os.makedirs(os.path.dirname(SQ_FILE), exist_ok=True)
     with open(SQ_FILE, "w") as f:
         json.dump(out, f, indent=1)
@@ -729,7 +760,8 @@ def sq_for(kernel_key: str, sources):
         e = json.load(f).get(kernel_key)
     if not e or e.get("source_hash") != source_hash(sources):
         return None
-    return {"mfma_busy": e["mfma_busy"], "valu_busy": e["valu_busy"], "wait_frac": e["wait_frac"]}
+    return {k: e[k] for k in ("mfma_busy", "valu_busy", "mfma_busy_active", "valu_busy_active",
+                              "wait_frac")}
 
 
 # --------------------------------------------------------------------------
@@ -738,8 +770,9 @@ def sq_for(kernel_key: str, sources):
 def summarize_trace(trace_dir, pattern, skip, take):
     """Prints the per-kernel statistics of a rocprofv3 kernel-trace run and
     the mean duration of dispatches [skip, skip + take) of the kernels whose
-    name contains `pattern` (in dispatch order): with skip = warmup and take
-    = steps of the bench run this is the timed region of the headline."""
+    name contains `pattern` (in dispatch order; skip < 0: the last `take`).
+    With skip = -1 and take = steps of a `--no-extras` run this is the timed
+    region of the headline."""
     import csv
     stats = glob.glob(os.path.join(trace_dir, "**", "*_kernel_stats.csv"), recursive=True)
     trace = glob.glob(os.path.join(trace_dir, "**", "*_kernel_trace.csv"), recursive=True)
@@ -755,6 +788,8 @@ def summarize_trace(trace_dir, pattern, skip, take):
             if pattern in r["Kernel_Name"]:
                 rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
     rows.sort()
+    if skip < 0:  # the last `take` dispatches of the run
+        skip = max(0, len(rows) - take)
     sel = rows[skip:skip + take]
     if sel:
         d = np.array([(e - b) / 1e3 for b, e, _ in sel])

@@ -318,7 +318,9 @@ ttt_status_t ttt_linear_ln_bwd(const void* q, const void* k, const void* v,
  *   w1_ckpt : out [B][H][ceil(T/b)][hidden][d] fp32, W1 before each
  *             mini-batch of b tokens (w1_ckpt[..][0] = W1_0);
  *   w2_ckpt : out [B][H][ceil(T/b)][d][hidden] fp32, the same for W2.
- * It runs the primal-form kernel (one token at a time, fp32 arithmetic).
+ * It runs the kernel ttt_mlp_fwd picks for the same arguments (the bf16
+ * dual-form scan for bf16 q/k/v with b | 16, else the primal form), which
+ * also stores each mini-batch's starting state.
  *
  * ttt_mlp_bwd: the gradient of a loss L(Z, W1_T, W2_T) with respect to the
  * scan's inputs, given

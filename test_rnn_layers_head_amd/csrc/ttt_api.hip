@@ -479,8 +479,7 @@ ttt_status_t mlp_impl(const void* q, const void* k, const void* v, const float* 
   } else {
     ttt::MlpArgs a{q, k, v, eta, w1_0, w2_0, z, w1_out, w2_out, w0_per_batch, (int)units, H, T, b,
                    w1_ckpt, w2_ckpt};
-    e = ck ? ttt::launch_mlp_primal(a, qkv_dtype == TTT_F32, s)
-           : ttt::launch_mlp(a, qkv_dtype == TTT_F32, s);
+    e = ttt::launch_mlp(a, qkv_dtype == TTT_F32, s);
   }
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return TTT_OK;

@@ -30,6 +30,9 @@
 // 16-column block w of d = 64.  Transposes of 16x16 fp32 blocks use an MFMA with the
 // identity as the other operand (exact for hi + lo bf16 halves).
 //
+// For training, a variant also stores the state before every mini-batch
+// (the checkpoints of §6.12), straight from the registers.
+//
 // Inputs are register-staged one tile ahead by the waves themselves (each
 // lane moves 16-byte chunks of K, Q, V or one eta), so no wave issues
 // LDS-DMA and no wave is idle.  Mini-batches b < 16 (b | 16) run each
@@ -121,7 +124,10 @@ __device__ __forceinline__ void reduce_store_z(const char* smem, int lane, int c
   }
 }
 
-template <int NW, bool SUB>
+// CKPT: also store the state before every mini-batch (W1 [256][64] and W2
+// [64][256] per unit and mini-batch, the layouts of the final state) for the
+// backward; the stores are fire-and-forget and leave the recurrence alone.
+template <int NW, bool SUB, bool CKPT = false>
 __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
   using G = MlpGeom<NW>;
   constexpr int U = G::U, NB = G::NB, NCH = G::NCH;
@@ -244,6 +250,20 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
 
   YOps g2prev;  // Gn2 operands (block mi = w) of the previous pass
   int prev_tile = -1, prev_pass = 0;
+  const int nmb = (T + bsub - 1) / bsub;  // mini-batches (checkpoints)
+  // this wave's rows of W1 and columns of W2 in the final-state layouts
+  auto store_state = [&](float* w1o, float* w2o) {
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        *(f32x4*)(w1o + (u0 + 16 * n + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1)) = W1[n][m];
+#pragma unroll
+    for (int nu = 0; nu < NB; ++nu)
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+        *(f32x4*)(w2o + (16 * mi + c) * HID + u0 + 16 * nu + 4 * g) = W2T[nu][mi];
+  };
 
   for (int j = 0; j < ntiles; ++j) {
     const char* raw = smem + G::L_RAW + (j & 1) * RAWB;
@@ -269,6 +289,13 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
     const f32x4 eta4 = *(const f32x4*)(Et + 4 * g);
 
     for (int p = 0; p < npass; ++p) {
+      if constexpr (CKPT) {
+        const int mb = j * npass + p;  // mini-batch starting at token 16 j + bsub p
+        if (mb < nmb) {
+          const size_t co = ((size_t)unit * nmb + mb) * HID * 64;
+          store_state(a.w1_ckpt + co, a.w2_ckpt + co);
+        }
+      }
       // ================= Z of the previous pass, output block mi = w
       if (prev_tile >= 0 && w < 4)
         reduce_store_z<NW, SUB>(smem, lane, c, g, w, g2prev, rz, prev_tile, prev_pass, bsub);
@@ -433,19 +460,7 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
   if (prev_tile >= 0 && w < 4)
     reduce_store_z<NW, SUB>(smem, lane, c, g, w, g2prev, rz, prev_tile, prev_pass, bsub);
 
-  // final state
-  float* w1o = a.w1_out + (size_t)unit * HID * 64;
-  float* w2o = a.w2_out + (size_t)unit * 64 * HID;
-#pragma unroll
-  for (int n = 0; n < NB; ++n)
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      *(f32x4*)(w1o + (u0 + 16 * n + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1)) = W1[n][m];
-#pragma unroll
-  for (int nu = 0; nu < NB; ++nu)
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-      *(f32x4*)(w2o + (16 * mi + c) * HID + u0 + 16 * nu + 4 * g) = W2T[nu][mi];
+  store_state(a.w1_out + (size_t)unit * HID * 64, a.w2_out + (size_t)unit * 64 * HID);  // final state
 }
 
 }  // namespace
@@ -454,6 +469,10 @@ hipError_t launch_mlp(const MlpArgs& a, bool f32in, hipStream_t s) {
   constexpr int NW = 4;
   // fp32 inputs and mini-batches spanning several tiles: the primal kernel
   if (f32in || a.b > 16) return launch_mlp_primal(a, f32in, s);
+  if (a.w1_ckpt) {
+    if (a.b == 16) return launch(mlp_scan_kernel<2 * NW, false, true>, dim3(a.units), dim3(2 * NW * 64), s, a);
+    return launch(mlp_scan_kernel<NW, true, true>, dim3(a.units), dim3(NW * 64), s, a);
+  }
   if (a.b == 16) return launch(mlp_scan_kernel<2 * NW, false>, dim3(a.units), dim3(2 * NW * 64), s, a);
   return launch(mlp_scan_kernel<NW, true>, dim3(a.units), dim3(NW * 64), s, a);
 }
