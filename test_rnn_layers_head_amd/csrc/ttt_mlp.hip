@@ -339,11 +339,16 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
         const f32x4 t1 = mfma_k32(cat44(x2ts[2 * ch + 1].hi, x2ts[2 * ch + 1].lo), itr, f32x4{0, 0, 0, 0});
         x2op[ch] = split8_mfma(t0, t1, ns);
       }
+      Split8 w2s[4][NCH];  // hi/lo of W2 at the gradient point: Z2 and the outputs
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) w2s[mi][ch] = split8_mfma(W2T[2 * ch][mi], W2T[2 * ch + 1][mi], ns);
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
         f32x4 z2 = {0, 0, 0, 0};
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) z2 = mm3(x2op[ch], split8_mfma(W2T[2 * ch][mi], W2T[2 * ch + 1][mi], ns), z2);
+        for (int ch = 0; ch < NCH; ++ch) z2 = mm3(x2op[ch], w2s[mi][ch], z2);
         *(f32x4*)(smem + G::L_Z2P + (w * 4 + mi) * 1024 + lane * 16) = z2;  // partial Z2^T[t][i]
       }
       wg_barrier();  // B1: partial Z2 written
@@ -412,7 +417,7 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
       for (int mi = 0; mi < 4; ++mi) {
         f32x4 zp = {0, 0, 0, 0};
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) zp = mm3(x2qop[ch], split8_mfma(W2T[2 * ch][mi], W2T[2 * ch + 1][mi], ns), zp);
+        for (int ch = 0; ch < NCH; ++ch) zp = mm3(x2qop[ch], w2s[mi][ch], zp);
         *(f32x4*)(smem + G::L_ZP + (w * 4 + mi) * 1024 + lane * 16) = zp;
       }
       {
