@@ -26,7 +26,9 @@
 // j+1 (of Y_{j+1} = W0 K_{j+1}) and of the outputs of tile j; after it, every
 // wave finishes the reduction and computes the gradient of tile j+1 and the
 // outputs of tile j.  The output normalisation thus runs one tile behind the
-// recurrence and off its serial chain.
+// recurrence and off its serial chain; the normalised outputs pass through
+// an LDS staging tile, from which helpers 1 and 2 store whole 256-byte rows
+// one tile later.
 //
 // Layouts.  The statistics and the gradient are formed transposed ("layout
 // T": lane (c, g) register r holds row 4g+r of the wave's 16 rows for token
@@ -80,7 +82,9 @@ struct LnGeom {
   static constexpr int PREP = P_QB + 4096;
   static constexpr int NPREP = 4;
   static constexpr int XST = 8 * 16 * 4;        // floats: [stat 8][token 16][wave 4]
-  static constexpr int LDS = NST * RAW + NPREP * PREP + 2 * XST * 4;
+  static constexpr int ZROW = 68 * 4;           // bytes per token of a Z staging tile (64 + 4 pad)
+  static constexpr int ZT = 16 * ZROW;          // one Z staging tile (16 tokens)
+  static constexpr int LDS = NST * RAW + NPREP * PREP + 2 * XST * 4 + 2 * ZT;
   // waves 0..3 compute, 4 and 5 helpers, 6 loader, 7 helper: wave i shares
   // a SIMD with wave i + 4, so every SIMD holds one compute wave and one
   // wave of preparation work
@@ -175,6 +179,7 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
   char* const raw = smem;
   char* const prep = smem + G::NST * G::RAW;
   float* const xst = (float*)(smem + G::NST * G::RAW + G::NPREP * G::PREP);
+  char* const zst = smem + G::NST * G::RAW + G::NPREP * G::PREP + 2 * G::XST * 4;  // 2 Z tiles
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
@@ -183,6 +188,23 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
   const int head = unit % a.H;
   const int T = a.T;
   const int ntiles = (T + 15) >> 4;
+
+  // Z through a range-checked buffer (rows past T are dropped).  A token's
+  // 256-byte row spans the four compute waves (16 rows each), so they stage
+  // their parts in an LDS tile (two, alternating) and helpers 1 and 2 store
+  // whole rows from it one tile later: 1 KB of consecutive memory per store.
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(a.z + (size_t)unit * T * 64, (uint32_t)T * 256);
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  // tokens tok0 + 4 k + g (k = 0, 1) of staged tile t to HBM, lane chunk c
+  auto flush_z = [&](int t, int tok0) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int tk = tok0 + 4 * k + g;
+      const f32x4 Z = *(const f32x4*)(zst + (t & 1) * G::ZT + tk * G::ZROW + c * 16);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Z), rz,
+                                             (uint32_t)((t * 16 + tk) * 256 + c * 16), 0, 2);
+    }
+  };
 
   // ================================================================ loader
   // Barriers B_-2, B_-1, B_0 .. B_ntiles.  At B_j raw tiles <= j+2 have
@@ -257,10 +279,14 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
         kprev[h][e] = (bf16)0.f;
         sel[h][e] = (bf16)((g == (c >> 2) && e == 4 * h + (c & 3)) ? 1.f : 0.f);
       }
+    const int ztok0 = role == 1 ? 0 : 8;  // the staged tokens this helper stores
     wg_barrier_pinned();  // B_{-2}
     for (int j = -2; j < ntiles - 1; ++j) {
       const int tn = j + 2;
+      // tile j-2's outputs, staged by the compute waves before B_j
+      if (role != 0 && j >= 2) flush_z(j - 2, ztok0);
       if (tn >= ntiles) {
+        wait_lgkm0();
         wg_barrier_pinned();  // B_{j+1}
         continue;
       }
@@ -326,6 +352,11 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
       wg_barrier_pinned();  // B_{j+1}
     }
     wg_barrier_pinned();  // B_ntiles
+    // the last two staged tiles (tile ntiles-1 goes out from the compute waves)
+    if (role != 0) {
+      if (ntiles >= 3) flush_z(ntiles - 3, ztok0);
+      if (ntiles >= 2) flush_z(ntiles - 2, ztok0);
+    }
     return;
   }
 
@@ -406,13 +437,10 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
     bcast16(hi, S[5], S[7]);
   };
 
-  // Z through a range-checked buffer (rows past T are dropped); lane (c, g)
-  // stores rows rbase + 4g .. +3 of token c.
-  const __amdgpu_buffer_rsrc_t rz = make_rsrc(a.z + (size_t)unit * T * 64, (uint32_t)T * 256);
+  // Lane (c, g) of a compute wave holds rows rbase + 4g .. +3 of token c.
   const uint32_t zlane = (uint32_t)((c * 64 + rbase + 4 * g) * 4);
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   // z = q + beta + gamma (o - mu_o) rs_o, from the output statistics S6, S7
-  auto store_z = [&](int t, const float S[8], const f32x4& O, const f32x4& QB) {
+  auto z_of = [&](const float S[8], const f32x4& O, const f32x4& QB) {
     const float mo = S[6] * (1.f / 64);
     const float vo = fmaxf(fmaf(S[7], 1.f / 64, -mo * mo), 0.f);
     const float ro = rsqrtf(vo + eps);
@@ -422,7 +450,15 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
       const float rg = ro * gam[r];
       Z[r] = fmaf(O[r], rg, fmaf(-mo, rg, QB[r]));
     }
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Z), rz,
+    return Z;
+  };
+  // tile t's part of this lane into the staging tile of t's parity
+  auto stage_z = [&](int t, const float S[8], const f32x4& O, const f32x4& QB) {
+    *(f32x4*)(zst + (t & 1) * G::ZT + c * G::ZROW + (rbase + 4 * g) * 4) = z_of(S, O, QB);
+  };
+  // the last tile directly (no barrier follows it)
+  auto store_z = [&](int t, const float S[8], const f32x4& O, const f32x4& QB) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, z_of(S, O, QB)), rz,
                                            zlane + (uint32_t)t * (16 * 64 * 4), 0, 2);
   };
 
@@ -536,8 +572,9 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
     const f32x4 CL = mfma_k32(gal, selH, f32x4{0, 0, 0, 0});
 
     __builtin_amdgcn_sched_barrier(0);
-    // ---- outputs of tile j-1 (off the chain, while the MFMAs run)
-    if (j > 0) store_z(j - 1, S, O, QB);
+    // ---- outputs of tile j-1 (off the chain, while the MFMAs run), staged
+    // in LDS for the helpers
+    if (j > 0) stage_z(j - 1, S, O, QB);
 
     Split4 gs;  // hi, mid: the operands of the products with K^T K and K^T Q
     gs.hi = u2s(make_uint2(pack_rne(CH[0], CH[1]), pack_rne(CH[2], CH[3])));
