@@ -52,6 +52,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     D = ctypes.c_double
     lib.ttt_oracle_linear_ln.argtypes = [dp, dp, dp, dp, dp, I, dp, dp, D, L, L, L, L, L, dp, dp, I]
     lib.ttt_oracle_linear_ln.restype = I
+    lib.ttt_oracle_mlp_ln.argtypes = [dp, dp, dp, dp, dp, dp, I, dp, dp, D, L, L, L, L, L, L, dp, dp,
+                                      dp, I]
+    lib.ttt_oracle_mlp_ln.restype = I
     ip = ctypes.POINTER(ctypes.c_int)
     lib.ttt_oracle_linear_step.argtypes = [dp, dp, dp, dp, dp, dp, ip, L, L, L, L, dp]
     lib.ttt_oracle_linear_step.restype = I
@@ -181,6 +184,34 @@ def linear_ln(q, k, v, eta, w0, gamma, beta, eps: float, b: int, nthreads: int |
     if rc != 0:
         raise RuntimeError(f"ttt_oracle_linear_ln failed with status {rc}")
     return z, w_out
+
+
+def mlp_ln(q, k, v, eta, w1_0, w2_0, gamma, beta, eps: float, b: int,
+           nthreads: int | None = None, lib=None):
+    """TTT-MLP with the LayerNorm + residual wrapper, primal forward:
+    f(x) = x + gamma * (y - mean) / sqrt(var + eps) + beta with
+    y = W2 GELU(W1 x), over the d output components of each token.
+
+    gamma, beta: [H, d] (per head).  Other arguments as for ``mlp``.
+    Returns (z, w1_T, w2_T) in float64.
+    """
+    q, k, v, eta, w1_0, w2_0, gamma, beta = map(_f64, (q, k, v, eta, w1_0, w2_0, gamma, beta))
+    B, H, T, d = q.shape
+    per_batch = 1 if w1_0.ndim == 4 else 0
+    hidden = w1_0.shape[-2]
+    assert w1_0.shape == ((B, H, hidden, d) if per_batch else (H, hidden, d))
+    assert w2_0.shape == ((B, H, d, hidden) if per_batch else (H, d, hidden))
+    assert gamma.shape == (H, d) and beta.shape == (H, d)
+    z = np.zeros((B, H, T, d))
+    w1 = np.zeros((B, H, hidden, d))
+    w2 = np.zeros((B, H, d, hidden))
+    lib = lib or load()
+    rc = lib.ttt_oracle_mlp_ln(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w1_0), _ptr(w2_0),
+                               per_batch, _ptr(gamma), _ptr(beta), float(eps), B, H, T, d, hidden,
+                               int(b), _ptr(z), _ptr(w1), _ptr(w2), nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"ttt_oracle_mlp_ln failed with status {rc}")
+    return z, w1, w2
 
 
 def _ipos(pos, B) -> np.ndarray:

@@ -24,11 +24,12 @@
  *    is a per-token input that scales token t's own gradient (no 1/b).
  *  - §4.4 Inner models: TTT-Linear f(x) = W x; TTT-MLP f(x) = W2 GELU(W1 x)
  *    with a hidden width that the caller chooses (4x the input on the page).
- *  - §4.4 LayerNorm + residual wrapper, TTT-Linear only:
- *    f(x) = x + LN(W x), LN(y) = gamma * (y - mean(y)) / sqrt(var(y) + eps)
- *    + beta over the d output components of one token (population variance;
- *    gamma, beta per head and eps are inputs: the page names the wrapper but
- *    not its parameters).  The gradient goes through the LayerNorm.
+ *  - §4.4 LayerNorm + residual wrapper around either inner model:
+ *    f(x) = x + LN(W x) or x + LN(W2 GELU(W1 x)), LN(y) = gamma * (y -
+ *    mean(y)) / sqrt(var(y) + eps) + beta over the d output components of one
+ *    token (population variance; gamma, beta per head and eps are inputs: the
+ *    page names the wrapper but not its parameters).  The gradient goes
+ *    through the LayerNorm.
  *
  * Decode steps (§6.11: token-by-token generation uses the primal form): one
  * token per (batch, head) unit per call.  A unit carries its current state W
@@ -242,10 +243,86 @@ static void mlp_unit(const double *q, const double *k, const double *v,
 }
 
 /* ------------------------------------------------------------------ */
+/* TTT-MLP with LayerNorm + residual: f(x) = x + LN(W2 GELU(W1 x)).    */
+/* ------------------------------------------------------------------ */
+/* The MLP's output y = W2 GELU(W1 x) takes the place of W x in the linear
+ * wrapper above: the loss sum_i (k_i + LN(y)_i - v_i)^2 sends
+ * g_i = 2 gamma_i (f_i - v_i) into the LayerNorm's VJP, which gives dl/dy;
+ * from there the MLP's own backpropagation (as in mlp_unit) gives the two
+ * layers' gradients, all at the mini-batch's gradient point. */
+static void mlp_ln_unit(const double *q, const double *k, const double *v,
+                        const double *eta, const double *w1_0, const double *w2_0,
+                        const double *gamma, const double *beta, double eps, long T,
+                        long d, long hd, long b, double *z, double *W1, double *W2,
+                        mlp_scratch *s, double *y, double *yhat) {
+  memcpy(W1, w1_0, sizeof(double) * (size_t)(hd * d));
+  memcpy(W2, w2_0, sizeof(double) * (size_t)(d * hd));
+  for (long m0 = 0; m0 < T; m0 += b) {
+    long m1 = m0 + b < T ? m0 + b : T;
+    memcpy(s->W1s, W1, sizeof(double) * (size_t)(hd * d));
+    memcpy(s->W2s, W2, sizeof(double) * (size_t)(d * hd));
+    for (long t = m0; t < m1; ++t) {
+      const double *kt = k + t * d, *vt = v + t * d, *qt = q + t * d;
+      const double et = eta[t];
+      /* forward at the gradient point */
+      for (long u = 0; u < hd; ++u) {
+        double acc = 0.0;
+        for (long j = 0; j < d; ++j) acc += s->W1s[u * d + j] * kt[j];
+        s->a[u] = acc;
+        s->x[u] = gelu(acc);
+      }
+      for (long i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (long u = 0; u < hd; ++u) acc += s->W2s[i * hd + u] * s->x[u];
+        y[i] = acc;
+      }
+      const double rs = ln_normalise(y, d, eps, yhat);
+      /* dl/dyhat_i = 2 gamma_i (k_i + gamma_i yhat_i + beta_i - v_i), then the
+         LayerNorm VJP: e = dl/dy = rs (g - mean(g) - yhat mean(g yhat)) */
+      double m1s = 0.0, m2s = 0.0;
+      for (long i = 0; i < d; ++i) {
+        const double resid = kt[i] + beta[i] - vt[i] + gamma[i] * yhat[i]; /* f_i - v_i */
+        s->e[i] = 2.0 * gamma[i] * resid;
+        m1s += s->e[i];
+        m2s += s->e[i] * yhat[i];
+      }
+      m1s /= (double)d;
+      m2s /= (double)d;
+      for (long i = 0; i < d; ++i) s->e[i] = rs * (s->e[i] - m1s - yhat[i] * m2s);
+      /* the MLP below the LayerNorm: dl/dW2 = e x^T, delta = (W2s^T e) * GELU'(a) */
+      for (long u = 0; u < hd; ++u) {
+        double back = 0.0;
+        for (long i = 0; i < d; ++i) back += s->e[i] * s->W2s[i * hd + u];
+        s->delta[u] = gelu_grad(s->a[u]) * back;
+      }
+      for (long i = 0; i < d; ++i) {
+        const double step = et * s->e[i];
+        for (long u = 0; u < hd; ++u) W2[i * hd + u] -= step * s->x[u];
+      }
+      for (long u = 0; u < hd; ++u)
+        for (long j = 0; j < d; ++j) W1[u * d + j] -= et * s->delta[u] * kt[j];
+      /* z_t = q_t + LN(W2_t GELU(W1_t q_t)) with the updated state */
+      for (long u = 0; u < hd; ++u) {
+        double pre = 0.0;
+        for (long j = 0; j < d; ++j) pre += qt[j] * W1[u * d + j];
+        s->hq[u] = gelu(pre);
+      }
+      for (long i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (long u = 0; u < hd; ++u) acc += W2[i * hd + u] * s->hq[u];
+        y[i] = acc;
+      }
+      ln_normalise(y, d, eps, yhat);
+      for (long i = 0; i < d; ++i) z[t * d + i] = gamma[i] * yhat[i] + beta[i] + qt[i];
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ */
 /* Threading: units (batch, head) are independent; static round robin. */
 /* ------------------------------------------------------------------ */
 typedef struct {
-  int kind; /* 0 linear, 1 mlp, 2 linear with LayerNorm + residual */
+  int kind; /* 0 linear, 1 mlp, 2 linear with LayerNorm + residual, 3 mlp with it */
   const double *q, *k, *v, *eta, *w0a, *w0b, *gamma, *beta;
   double eps;
   int w0_per_batch;
@@ -261,7 +338,7 @@ static void *worker(void *arg) {
   double *buf = NULL;
   size_t need = jb->kind == 0   ? (size_t)(d * d + d)
                 : jb->kind == 2 ? (size_t)(d * d + 3 * d)
-                                : (size_t)(2 * hd * d + 4 * hd + d);
+                                : (size_t)(2 * hd * d + 4 * hd + 3 * d);
   buf = (double *)malloc(sizeof(double) * need);
   if (!buf) { jb->status = 1; return NULL; }
   for (long u = jb->tid; u < units; u += jb->nthreads) {
@@ -286,9 +363,14 @@ static void *worker(void *arg) {
       s.delta = s.x + hd;
       s.hq = s.delta + hd;
       s.e = s.hq + hd;
-      mlp_unit(qu, ku, vu, eu, jb->w0a + wsel * hd * d, jb->w0b + wsel * d * hd,
-               T, d, hd, jb->b, zu, jb->outa + u * hd * d, jb->outb + u * d * hd,
-               &s);
+      if (jb->kind == 1)
+        mlp_unit(qu, ku, vu, eu, jb->w0a + wsel * hd * d, jb->w0b + wsel * d * hd,
+                 T, d, hd, jb->b, zu, jb->outa + u * hd * d, jb->outb + u * d * hd,
+                 &s);
+      else
+        mlp_ln_unit(qu, ku, vu, eu, jb->w0a + wsel * hd * d, jb->w0b + wsel * d * hd,
+                    jb->gamma + hh * d, jb->beta + hh * d, jb->eps, T, d, hd, jb->b, zu,
+                    jb->outa + u * hd * d, jb->outb + u * d * hd, &s, s.e + d, s.e + 2 * d);
     }
   }
   free(buf);
@@ -365,6 +447,21 @@ int ttt_oracle_linear_ln(const double *q, const double *k, const double *v,
   p.gamma = gamma; p.beta = beta; p.eps = eps;
   p.w0_per_batch = w0_per_batch; p.B = B; p.H = H; p.T = T; p.d = d; p.hd = 0;
   p.b = b; p.z = z; p.outa = w_out;
+  return run(p, nthreads);
+}
+
+int ttt_oracle_mlp_ln(const double *q, const double *k, const double *v,
+                      const double *eta, const double *w1_0, const double *w2_0,
+                      int w0_per_batch, const double *gamma, const double *beta, double eps,
+                      long B, long H, long T, long d, long hidden, long b, double *z,
+                      double *w1_out, double *w2_out, int nthreads) {
+  if (hidden <= 0 || !(eps >= 0.0)) return 2;
+  job p;
+  memset(&p, 0, sizeof p);
+  p.kind = 3; p.q = q; p.k = k; p.v = v; p.eta = eta; p.w0a = w1_0; p.w0b = w2_0;
+  p.gamma = gamma; p.beta = beta; p.eps = eps;
+  p.w0_per_batch = w0_per_batch; p.B = B; p.H = H; p.T = T; p.d = d; p.hd = hidden;
+  p.b = b; p.z = z; p.outa = w1_out; p.outb = w2_out;
   return run(p, nthreads);
 }
 

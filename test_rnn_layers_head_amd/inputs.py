@@ -27,6 +27,10 @@ Recipe (per workload):
     LayerNorm divides by the spread of W0 k, so the gradient scales like
     1 / |W0| and the step is stable only for eta |k|^2 / var(W0 k) of order
     one (with W0 ~ N(0, 0.02^2) it would be ~40 times larger);
+  * TTT-MLP with the same wrapper (kind "mlp_ln"): W1, W2 as for TTT-MLP with
+    w_scale = 1/sqrt(d) and eta_scale = 0.02, then ln_gamma, ln_beta as
+    above, for the same reason (with the plain MLP's 0.02 and 0.1 the states
+    grow ~30 times over 2k tokens; with these, ~1.2 times);
   * learning-rate gate workloads (gate_dx > 0), drawn last: the layer input
     x ~ N(0, 1) per element, [B, T, gate_dx], stored bf16, and one gate
     vector per head theta_lr ~ N(0, 1 / gate_dx), [H, gate_dx], fp32, with
@@ -49,7 +53,7 @@ import numpy as np
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str  # "linear" | "linear_ln" | "mlp"
+    kind: str  # "linear" | "linear_ln" | "mlp" | "mlp_ln"
     B: int
     H: int
     T: int
@@ -89,6 +93,8 @@ WORKLOADS = {
                 w_scale=0.125),
     8: Workload("linear-gated-1.3B-T8192", "linear", B=4, H=32, T=8192, seed=8, gate_dx=2048),
     9: Workload("linear-gated-125M-T2048", "linear", B=8, H=12, T=2048, seed=9, gate_dx=768),
+    10: Workload("mlp-ln-125M-T2048", "mlp_ln", B=8, H=12, T=2048, hidden=256, seed=10,
+                 eta_scale=0.02, w_scale=0.125),
 }
 
 
@@ -132,7 +138,7 @@ class Inputs:
     q_raw: np.ndarray | None = None
     k_raw: np.ndarray | None = None
     v_raw: np.ndarray | None = None
-    ln_gamma: np.ndarray | None = None  # [H, d] fp32 (kind "linear_ln")
+    ln_gamma: np.ndarray | None = None  # [H, d] fp32 (kinds "linear_ln", "mlp_ln")
     ln_beta: np.ndarray | None = None
     gate_x: np.ndarray | None = None  # [B, T, dx] float32 holding the bf16 values
     gate_x_raw: np.ndarray | None = None  # the same as uint16 bf16 patterns
@@ -204,13 +210,13 @@ def make_inputs(wl: Workload | int, seed: int | None = None) -> Inputs:
     w0 = w1 = w2 = gamma = beta = None
     if wl.kind in ("linear", "linear_ln"):
         w0 = (rng.standard_normal((wl.H, wl.d, wl.d)) * wl.w_scale).astype(np.float32)
-    elif wl.kind == "mlp":
+    elif wl.kind in ("mlp", "mlp_ln"):
         hd = wl.hidden or 4 * wl.d
         w1 = (rng.standard_normal((wl.H, hd, wl.d)) * wl.w_scale).astype(np.float32)
         w2 = (rng.standard_normal((wl.H, wl.d, hd)) * wl.w_scale).astype(np.float32)
     else:
         raise ValueError(wl.kind)
-    if wl.kind == "linear_ln":
+    if wl.kind in ("linear_ln", "mlp_ln"):
         gamma = (1.0 + 0.2 * rng.standard_normal((wl.H, wl.d))).astype(np.float32)
         beta = (0.1 * rng.standard_normal((wl.H, wl.d))).astype(np.float32)
     if wl.qkv_dtype == "bf16":

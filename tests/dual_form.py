@@ -98,6 +98,51 @@ def mlp_unit(q, k, v, eta, w1, w2, b):
     return Z, W1, W2
 
 
+def mlp_ln_unit(q, k, v, eta, w1, w2, gamma, beta, eps, b):
+    """One unit of TTT-MLP with the §4.4 LayerNorm + residual wrapper,
+    f(x) = x + gamma * LNhat(W2 GELU(W1 x)) + beta, in the §3.7 dual form:
+    the whole mini-batch's gradients at its starting weights, with the
+    LayerNorm VJP (column by column) between the loss and the second layer;
+    the outputs from the two masked products, then the output LayerNorm."""
+    T, d = q.shape
+    W1 = np.array(w1, dtype=np.float64)
+    W2 = np.array(w2, dtype=np.float64)
+    Z = np.zeros((T, d))
+    gc, bc = gamma[:, None], beta[:, None]
+    for m0 in range(0, T, b):
+        m1 = min(T, m0 + b)
+        XK, XV, XQ = k[m0:m1].T, v[m0:m1].T, q[m0:m1].T
+        e = eta[m0:m1]
+        Z1 = W1 @ XK
+        X2 = gelu(Z1)
+        Yh, rs = _ln_columns(W2 @ X2, eps)
+        Gh = 2.0 * gc * (XK + gc * Yh + bc - XV)
+        G2 = rs[None, :] * (Gh - Gh.mean(axis=0) - Yh * (Gh * Yh).mean(axis=0)) * e[None, :]
+        G1 = (W2.T @ G2) * gelu_grad(Z1)
+        X2q = gelu(W1 @ XQ - G1 @ np.triu(XK.T @ XQ))
+        Oh, _ = _ln_columns(W2 @ X2q - G2 @ np.triu(X2.T @ X2q), eps)
+        Z[m0:m1] = (XQ + gc * Oh + bc).T
+        W1 = W1 - G1 @ XK.T
+        W2 = W2 - G2 @ X2.T
+    return Z, W1, W2
+
+
+def mlp_ln(q, k, v, eta, w1, w2, gamma, beta, eps, b):
+    B, H, T, d = q.shape
+    hd = w1.shape[-2]
+    Z = np.zeros((B, H, T, d))
+    W1T = np.zeros((B, H, hd, d))
+    W2T = np.zeros((B, H, d, hd))
+    for bi in range(B):
+        for h in range(H):
+            a = w1[bi, h] if w1.ndim == 4 else w1[h]
+            c = w2[bi, h] if w2.ndim == 4 else w2[h]
+            Z[bi, h], W1T[bi, h], W2T[bi, h] = mlp_ln_unit(q[bi, h], k[bi, h], v[bi, h],
+                                                          eta[bi, h], a, c, gamma[h], beta[h],
+                                                          eps, b)
+    return Z, W1T, W2T
+
+
 def _units(a, lead):
     return a.reshape(lead, *a.shape[2:])
 

@@ -373,6 +373,78 @@ def pin_ln_one_step_finite_differences(lib):
     assert rel(w1[0, 0], w0[0] - grad) < 1e-8
 
 
+def pin_mlp_ln_primal_equals_dual(lib):
+    """TTT-MLP with the LayerNorm + residual wrapper: the primal oracle against
+    the dual form of tests/dual_form.py ("论文速览 | TTT" §3.7 with §4.4)."""
+    rng = np.random.default_rng(131)
+    for b in (1, 3, 4, 16):
+        q, k, v, eta, w1, w2 = rand_mlp(rng, 2, 2, 21, 6, 10, eta_scale=0.3)
+        gamma, beta = rand_ln(rng, 2, 6)
+        zp, ap, cp = oracle.mlp_ln(q, k, v, eta, w1, w2, gamma, beta, 1e-5, b, lib=lib)
+        zd, ad, cd = dual_form.mlp_ln(q, k, v, eta, w1, w2, gamma, beta, 1e-5, b)
+        assert rel(zp, zd) < 1e-12 and rel(ap, ad) < 1e-12 and rel(cp, cd) < 1e-12, b
+
+
+def pin_mlp_ln_one_step_finite_differences(lib):
+    """One mini-batch (b = T) is one gradient step of sum_s eta_s l_s on both
+    layers, l_s = ||k_s + LN(W2 GELU(W1 k_s)) - v_s||^2, checked by central
+    differences (Richardson-extrapolated) of that loss written out here."""
+    from scipy.special import erf
+    rng = np.random.default_rng(132)
+    T, d, hd = 3, 4, 5
+    q, k, v, eta, w1, w2 = rand_mlp(rng, 1, 1, T, d, hd, eta_scale=0.5, w_scale=0.6)
+    gamma, beta = rand_ln(rng, 1, d)
+    eps = 1e-3
+    _, a1, a2 = oracle.mlp_ln(q, k, v, eta, w1, w2, gamma, beta, eps, T, lib=lib)
+    K, V, e, g, bb = k[0, 0], v[0, 0], eta[0, 0], gamma[0], beta[0]
+
+    def L(W1, W2):
+        A = K @ W1.T
+        Y = (0.5 * A * (1.0 + erf(A / np.sqrt(2.0)))) @ W2.T  # tokens as rows
+        mu = Y.mean(axis=1, keepdims=True)
+        var = ((Y - mu) ** 2).mean(axis=1, keepdims=True)
+        r = K + g * (Y - mu) / np.sqrt(var + eps) + bb - V
+        return float(np.sum(e * np.sum(r * r, axis=1)))
+
+    def grad(f, X):
+        out = np.zeros_like(X)
+        for idx in np.ndindex(*X.shape):
+            def c(h):
+                E = np.zeros_like(X)
+                E[idx] = h
+                return (f(X + E) - f(X - E)) / (2 * h)
+            h = 1e-4
+            out[idx] = (4.0 * c(h / 2) - c(h)) / 3.0
+        return out
+
+    g1 = grad(lambda W: L(W, w2[0]), w1[0])
+    g2 = grad(lambda W: L(w1[0], W), w2[0])
+    assert rel(a1[0, 0], w1[0] - g1) < 1e-7 and rel(a2[0, 0], w2[0] - g2) < 1e-7
+
+
+def pin_mlp_ln_gamma_zero(lib):
+    """gamma = 0: the LayerNorm passes no gradient, both layers stay put and
+    z = q + beta exactly."""
+    rng = np.random.default_rng(133)
+    q, k, v, eta, w1, w2 = rand_mlp(rng, 2, 2, 13, 6, 8, eta_scale=0.5)
+    _, beta = rand_ln(rng, 2, 6)
+    z, a, c = oracle.mlp_ln(q, k, v, eta, w1, w2, np.zeros((2, 6)), beta, 1e-5, 4, lib=lib)
+    assert np.array_equal(a, np.broadcast_to(w1, a.shape))
+    assert np.array_equal(c, np.broadcast_to(w2, c.shape))
+    assert np.array_equal(z, q + beta[None, :, None, :])
+
+
+def pin_mlp_ln_normalised_outputs(lib):
+    """gamma = 1, beta = 0, eps = 0: z - q is a normalised vector per token
+    (zero mean, unit population variance over the d components)."""
+    rng = np.random.default_rng(134)
+    q, k, v, eta, w1, w2 = rand_mlp(rng, 2, 2, 17, 6, 8, eta_scale=0.3)
+    z, _, _ = oracle.mlp_ln(q, k, v, eta, w1, w2, np.ones((2, 6)), np.zeros((2, 6)), 0.0, 4, lib=lib)
+    r = z - q
+    assert np.abs(r.mean(axis=-1)).max() < 1e-12
+    assert np.abs((r * r).mean(axis=-1) - 1.0).max() < 1e-10
+
+
 def pin_ln_gamma_zero(lib):
     rng = np.random.default_rng(33)
     q, k, v, eta, w0 = rand_linear(rng, 2, 2, 13, 6, eta_scale=0.5)
@@ -810,6 +882,10 @@ PINS = [
     pin_ln_primal_equals_dual,
     pin_ln_one_step_finite_differences,
     pin_ln_gamma_zero,
+    pin_mlp_ln_primal_equals_dual,
+    pin_mlp_ln_one_step_finite_differences,
+    pin_mlp_ln_gamma_zero,
+    pin_mlp_ln_normalised_outputs,
     pin_ln_scale_covariance,
     pin_ln_normalised_outputs,
     pin_linear_step_replays_scan,
@@ -1027,6 +1103,14 @@ MUTATIONS = {
         "x * exp(-0.5 * x * x) / sqrt(2.0 * pi);", "x * exp(-0.5 * x * x);"),
     "mlp_gelu_grad_density_wrong_width": (
         "x * exp(-0.5 * x * x) / sqrt(2.0 * pi);", "x * exp(-x * x) / sqrt(2.0 * pi);"),
+    "mlp_ln_no_residual_in_loss": ("const double resid = kt[i] + beta[i] - vt[i] + gamma[i] * yhat[i];",
+                                   "const double resid = beta[i] - vt[i] + gamma[i] * yhat[i];"),
+    "mlp_ln_vjp_drops_mean": ("s->e[i] = rs * (s->e[i] - m1s - yhat[i] * m2s);",
+                              "s->e[i] = rs * (s->e[i] - yhat[i] * m2s);"),
+    "mlp_ln_drop_gelu_grad": ("s->delta[u] = gelu_grad(s->a[u]) * back;", "s->delta[u] = back;"),
+    "mlp_ln_output_before_update": ("pre += qt[j] * W1[u * d + j];", "pre += qt[j] * s->W1s[u * d + j];"),
+    "mlp_ln_no_residual_in_output": ("z[t * d + i] = gamma[i] * yhat[i] + beta[i] + qt[i];",
+                                     "z[t * d + i] = gamma[i] * yhat[i] + beta[i];"),
     "ln_sample_variance": ("  var /= (double)d;", "  var /= (double)(d - 1);"),
     "ln_eps_outside_sqrt": ("1.0 / sqrt(var + eps);", "1.0 / (sqrt(var) + eps);"),
     "ln_drop_mean_term": ("rs * (gy[i] - m1s - yhat[i] * m2s);", "rs * (gy[i] - yhat[i] * m2s);"),
