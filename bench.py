@@ -374,18 +374,20 @@ def decode_case(kind, B, H, steps, warmup, b=16, seed=11):
                       "after a 512 MiB cache flush"}
 
 
-def bwd_alg_bytes(wl) -> int:
-    """Backward with one state checkpoint per 16-token mini-batch: read q, k,
-    v (bf16), eta, dz and the checkpoints (64 x 64 fp32 per 16 tokens); write
-    dq, dk, dv, deta (fp32) and dW0."""
-    per_tok = 3 * wl.d * 2 + 4 + wl.d * 4 + wl.d * wl.d * 4 // 16 + 3 * wl.d * 4 + 4
-    return wl.token_heads * per_tok + wl.units * wl.d * wl.d * 4
+def bwd_alg_bytes(wl, b=16) -> int:
+    """Backward with one state checkpoint per b-token mini-batch: read q, k,
+    v (bf16), eta, dz and the checkpoints (64 x 64 fp32 per mini-batch);
+    write dq, dk, dv, deta (fp32) and dW0."""
+    per_tok = 3 * wl.d * 2 + 4 + wl.d * 4 + 3 * wl.d * 4 + 4
+    nmb = (wl.T + b - 1) // b
+    return wl.token_heads * per_tok + wl.units * (nmb + 1) * wl.d * wl.d * 4
 
 
-def training_case(wl, steps, warmup):
-    """ttt_linear_fwd_ckpt then ttt_linear_bwd on one workload (b = 16), timed
+def training_case(wl, steps, warmup, b=16):
+    """ttt_linear_fwd_ckpt then ttt_linear_bwd on one workload, timed
     separately; dz is a seeded N(0, 0.01) draw.  Where both take sequence
-    chunks, the single-pass backward is timed beside them."""
+    chunks, the single-pass backward is timed beside them.  b = 16 runs the
+    dual-form kernels, other b the primal-form ones."""
     import torch
     from test_rnn_layers_head_amd import (inputs, ttt_linear_bwd, ttt_linear_fwd_ckpt,
                                           ttt_linear_fwd_plan)
@@ -393,28 +395,30 @@ def training_case(wl, steps, warmup):
     d = device_inputs(x)
     g = torch.Generator().manual_seed(17)
     dz = (torch.randn(wl.B, wl.H, wl.T, wl.d, generator=g) * 0.1).cuda()
-    nt = (wl.T + 15) // 16
+    nt = (wl.T + b - 1) // b
     z = torch.empty((wl.B, wl.H, wl.T, wl.d), device="cuda")
     w = torch.empty((wl.B, wl.H, wl.d, wl.d), device="cuda")
     ck = torch.empty((wl.B, wl.H, nt, wl.d, wl.d), device="cuda")
-    fwd = lambda: ttt_linear_fwd_ckpt(d["q"], d["k"], d["v"], d["eta"], d["w0"], 16, z=z, w_out=w,
+    fwd = lambda: ttt_linear_fwd_ckpt(d["q"], d["k"], d["v"], d["eta"], d["w0"], b, z=z, w_out=w,
                                       w_ckpt=ck)
     fwd()
-    bwd = lambda: ttt_linear_bwd(d["q"], d["k"], d["v"], d["eta"], ck, 16, dz)
+    bwd = lambda: ttt_linear_bwd(d["q"], d["k"], d["v"], d["eta"], ck, b, dz)
     _, kf, _ = time_launches(fwd, steps, warmup)
     _, kb, _ = time_launches(bwd, steps, warmup)
     grads = bwd()
     torch.cuda.synchronize()
     assert all(torch.isfinite(t).all().item() for t in grads)
     fb = linear_alg_bytes(wl) + wl.units * nt * wl.d * wl.d * 4
-    bb = bwd_alg_bytes(wl)
-    chunks = ttt_linear_fwd_plan(wl.B, wl.H, wl.T, 16)[1]
+    bb = bwd_alg_bytes(wl, b)
+    chunks = ttt_linear_fwd_plan(wl.B, wl.H, wl.T, b)[1]
     extra = {"seq_chunks": chunks}
+    if b != 16 or x.q.dtype != np.uint16:
+        extra["kernels"] = "linear_primal_ckpt_kernel / linear_primal_bwd_kernel"
     if chunks > 1:
         _, k1, _ = time_launches(lambda: ttt_linear_bwd(d["q"], d["k"], d["v"], d["eta"], ck, 16, dz,
                                                         seq_chunks=1), steps, warmup)
         extra["bwd_one_pass_us"] = k1
-    return {"workload": wl.name, "b": 16, **extra, "fwd_ckpt_us": kf, "bwd_us": kb,
+    return {"workload": wl.name, "b": b, **extra, "fwd_ckpt_us": kf, "bwd_us": kb,
             "fwd_alg_bytes": fb, "bwd_alg_bytes": bb,
             "fwd_hbm_frac": fb / (kf * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "bwd_hbm_frac": bb / (kb * 1e-6) / 1e9 / HBM_PEAK_GBS,
@@ -453,6 +457,59 @@ def mlp_training_case(wl, b, steps, warmup):
             "train_token_heads_per_s": wl.token_heads / ((kf + kb) * 1e-6),
             "kernels": ("mlp_scan_kernel with checkpoint stores" if b <= 16 and 16 % b == 0
                         else "mlp_primal_kernel (checkpoints)") + " / mlp_primal_bwd_kernel"}
+
+
+def ln_training_case(wl, b, steps, warmup):
+    """ttt_linear_ln_fwd_ckpt then ttt_linear_ln_bwd on one LayerNorm
+    workload, timed separately (the primal-form kernels, fp32 arithmetic);
+    dz is a seeded N(0, 0.01) draw."""
+    import torch
+    from test_rnn_layers_head_amd import inputs, ttt_linear_ln_bwd, ttt_linear_ln_fwd_ckpt
+    x = inputs.make_inputs(wl)
+    d = device_inputs(x)
+    gam = torch.from_numpy(x.ln_gamma).cuda()
+    bet = torch.from_numpy(x.ln_beta).cuda()
+    g = torch.Generator().manual_seed(23)
+    dz = (torch.randn(wl.B, wl.H, wl.T, wl.d, generator=g) * 0.1).cuda()
+    fwd = lambda: ttt_linear_ln_fwd_ckpt(d["q"], d["k"], d["v"], d["eta"], d["w0"], gam, bet,
+                                         wl.ln_eps, b)
+    _, _, ck = fwd()
+    bwd = lambda: ttt_linear_ln_bwd(d["q"], d["k"], d["v"], d["eta"], ck, gam, bet, wl.ln_eps, b, dz)
+    _, kf, _ = time_launches(fwd, steps, warmup)
+    _, kb, _ = time_launches(bwd, steps, warmup)
+    grads = bwd()
+    torch.cuda.synchronize()
+    assert all(torch.isfinite(t).all().item() for t in grads)
+    nmb = (wl.T + b - 1) // b
+    fb = ln_alg_bytes(wl) + wl.units * nmb * wl.d * wl.d * 4
+    bb = bwd_alg_bytes(wl, b) + 2 * wl.units * wl.d * 4  # + dgamma, dbeta
+    return {"workload": wl.name, "b": b, "fwd_ckpt_us": kf, "bwd_us": kb,
+            "fwd_alg_bytes": fb, "bwd_alg_bytes": bb,
+            "fwd_hbm_frac": fb / (kf * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "bwd_hbm_frac": bb / (kb * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "train_token_heads_per_s": wl.token_heads / ((kf + kb) * 1e-6),
+            "kernels": "linear_ln_primal_kernel (checkpoints) / linear_ln_primal_bwd_kernel"}
+
+
+def mlp_ln_case(wl, b, steps, warmup):
+    """ttt_mlp_ln_fwd (TTT-MLP with the LayerNorm + residual wrapper, the
+    primal-form kernel) on one workload."""
+    import torch
+    from test_rnn_layers_head_amd import inputs, ttt_mlp_ln_fwd
+    x = inputs.make_inputs(wl)
+    d = device_inputs(x)
+    gam = torch.from_numpy(x.ln_gamma).cuda()
+    bet = torch.from_numpy(x.ln_beta).cuda()
+    launch = lambda: ttt_mlp_ln_fwd(d["q"], d["k"], d["v"], d["eta"], d["w1"], d["w2"], gam, bet,
+                                    wl.ln_eps, b)
+    wall, kmean, spread = time_launches(launch, steps, warmup)
+    byts = mlp_alg_bytes(wl) + wl.H * wl.d * 2 * 4
+    flops = mlp_alg_flops(wl, b)
+    return {"workload": wl.name, "b": b, "token_heads_per_s": wl.token_heads / (wall * 1e-3),
+            "kernel_us_mean": kmean, "kernel_us_median": spread["median"],
+            "alg_bytes": byts, "alg_flops": flops,
+            "hbm_frac_algorithmic": byts / (kmean * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "kernel": "mlp_primal_kernel with the LayerNorm wrapper (fp32, one token at a time)"}
 
 
 def gate_alg_bytes(wl) -> int:
@@ -910,6 +967,11 @@ def main():
         w5 = inputs.workload(5)
         log(f"[bench] forward with checkpoints + backward, {w5.name}")
         extras[f"train-{w5.name}"] = training_case(w5, 3, 2)
+        log(f"[bench] forward with checkpoints + backward, {wl.name}, b = 4 (primal kernels)")
+        extras[f"train-{wl.name}_b4"] = training_case(wl, 2, 1, b=4)
+        w7 = inputs.workload(7)
+        log(f"[bench] forward with checkpoints + backward, {w7.name}")
+        extras[f"train-{w7.name}"] = ln_training_case(w7, 16, 2, 1)
         for kind, B, H in DECODE_CASES:
             log(f"[bench] decode step {kind} B={B} H={H}")
             extras[f"decode-{kind}-B{B}-H{H}"] = decode_case(kind, B, H, 100, 200)
@@ -923,6 +985,9 @@ def main():
         extras[f"{w4.name}_b64"] = mlp_case(w4, 64, 3, 2)
         log(f"[bench] forward with checkpoints + backward, {w4.name}")
         extras[f"train-{w4.name}"] = mlp_training_case(w4, 16, 3, 2)
+        w10 = inputs.workload(10)
+        log(f"[bench] {w10.name} (MLP with the LayerNorm wrapper)")
+        extras[w10.name] = mlp_ln_case(w10, 16, 3, 2)
         log("[bench] streaming copy reference")
         extras["stream_copy_GBps"] = stream_copy_GBps()
         extras["headline_frac_of_stream_copy"] = head["hbm_GBps"] / extras["stream_copy_GBps"]

@@ -148,6 +148,31 @@ ttt_status_t ttt_linear_ln_fwd(const void* q, const void* k, const void* v,
                                void* stream);
 
 /*
+ * TTT-MLP with the same LayerNorm + residual wrapper (§4.4 applies it to
+ * both inner models):
+ *   f(x) = x + LN(W2 GELU(W1 x)),  LN as for ttt_linear_ln_fwd.
+ * The inner loss ||f(k_t) - v_t||^2 is differentiated through the LayerNorm
+ * and then through both layers, every gradient of a mini-batch at the state
+ * before it (§3.5, §3.7); outputs z_t = q_t + LN(W2_t GELU(W1_t q_t)) from
+ * the updated state (§3.1).  Arguments as for ttt_mlp_fwd, plus ln_gamma,
+ * ln_beta ([H][d] fp32, per head) and eps (finite and > 0, else
+ * TTT_ERR_VALUE).
+ *
+ * Support: d = 64, hidden = 256, fp32 or bf16 q/k/v, b | 16 or 16 | b.  It
+ * runs the primal form token by token in fp32 arithmetic (1024 threads per
+ * (batch, head)); the LayerNorm's sums over the 64 components are wave
+ * reductions.
+ */
+ttt_status_t ttt_mlp_ln_fwd(const void* q, const void* k, const void* v,
+                            const float* eta, const float* w1_0,
+                            const float* w2_0, int32_t w0_per_batch,
+                            const float* ln_gamma, const float* ln_beta,
+                            float eps, int32_t B, int32_t H, int32_t T,
+                            int32_t d, int32_t hidden, int32_t b,
+                            ttt_dtype_t qkv_dtype, float* z, float* w1_out,
+                            float* w2_out, void* stream);
+
+/*
  * Training support (§6.12: the outer loop differentiates through the inner
  * one; the forward keeps the state at the start of every mini-batch, the
  * kappa = T / b checkpoints, and the backward walks the mini-batches in

@@ -30,6 +30,8 @@ SIGNATURES = {
     "ttt_linear_fwd_plan": (_i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp]),
     "ttt_linear_ln_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, ctypes.c_float, _i32,
                                  _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "ttt_mlp_ln_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, ctypes.c_float, _i32,
+                              _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "ttt_linear_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                _vp, _vp]),
     "ttt_linear_ln_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,

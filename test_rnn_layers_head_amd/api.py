@@ -352,6 +352,43 @@ def ttt_mlp_fwd(q, k, v, eta, w1_0, w2_0, b: int, z=None, w1_out=None, w2_out=No
     return z, w1_out, w2_out
 
 
+def ttt_mlp_ln_fwd(q, k, v, eta, w1_0, w2_0, ln_gamma, ln_beta, eps: float, b: int, z=None,
+                   w1_out=None, w2_out=None, stream=None):
+    """TTT-MLP with the LayerNorm + residual wrapper,
+    f(x) = x + LN(W2 GELU(W1 x)) (see include/ttt.h).
+
+    Arguments as for ttt_mlp_fwd, plus ln_gamma, ln_beta: [H, d] fp32 and
+    eps > 0.  Returns (z, w1_out, w2_out), allocated when not given.
+    """
+    B, H, T, d = q.shape
+    hidden = w1_0.shape[-2]
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=q.device)
+    z = f32(B, H, T, d) if z is None else z
+    w1_out = f32(B, H, hidden, d) if w1_out is None else w1_out
+    w2_out = f32(B, H, d, hidden) if w2_out is None else w2_out
+    dev = _check_tensors(dict(q=q, k=k, v=v, eta=eta, w1_0=w1_0, w2_0=w2_0, ln_gamma=ln_gamma,
+                              ln_beta=ln_beta, z=z, w1_out=w1_out, w2_out=w2_out))
+    for name, t in (("eta", eta), ("w1_0", w1_0), ("w2_0", w2_0), ("ln_gamma", ln_gamma),
+                    ("ln_beta", ln_beta), ("z", z), ("w1_out", w1_out), ("w2_out", w2_out)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if tuple(ln_gamma.shape) != (H, d) or tuple(ln_beta.shape) != (H, d):
+        raise ValueError("ln_gamma / ln_beta must be [H, d]")
+    per_batch = 1 if w1_0.dim() == 4 else 0
+    lead = (B, H) if per_batch else (H,)
+    if tuple(w1_0.shape) != (*lead, hidden, d) or tuple(w2_0.shape) != (*lead, d, hidden):
+        raise ValueError("w1_0 / w2_0 shape mismatch")
+    L = _lib.lib()
+    with torch.cuda.device(dev):
+        _lib.check(L.ttt_mlp_ln_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w1_0), _ptr(w2_0),
+                                    per_batch, _ptr(ln_gamma), _ptr(ln_beta), float(eps), B, H, T,
+                                    d, hidden, int(b), _dtype_code(q), _ptr(z), _ptr(w1_out),
+                                    _ptr(w2_out), _stream(dev, stream)))
+    return z, w1_out, w2_out
+
+
 def ttt_mlp_fwd_ckpt(q, k, v, eta, w1_0, w2_0, b: int, z=None, w1_out=None, w2_out=None,
                      w1_ckpt=None, w2_ckpt=None, stream=None):
     """ttt_mlp_fwd that also keeps both layers' state before every mini-batch

@@ -485,6 +485,49 @@ ttt_status_t mlp_impl(const void* q, const void* k, const void* v, const float* 
   return TTT_OK;
 }
 
+ttt_status_t mlp_ln_impl(const void* q, const void* k, const void* v, const float* eta,
+                         const float* w1_0, const float* w2_0, int32_t w0_per_batch,
+                         const float* gamma, const float* beta, float eps, int32_t B, int32_t H,
+                         int32_t T, int32_t d, int32_t hidden, int32_t b, ttt_dtype_t dt,
+                         float* z, float* w1_out, float* w2_out, void* stream) {
+  static const char* fn = "ttt_mlp_ln_fwd";
+  if (hidden < 0) return fail(TTT_ERR_SHAPE, "%s: negative hidden=%d", fn, hidden);
+  const int64_t units = (int64_t)B * H;
+  const int64_t es = dt == TTT_F32 ? 4 : 2;
+  const int64_t seq = units * T * d;
+  const int64_t wn = (w0_per_batch ? units : (int64_t)H) * hidden * d * 4;
+  const Range in[] = {rng("q", q, seq * es), rng("k", k, seq * es), rng("v", v, seq * es),
+                      rng("eta", eta, units * T * 4), rng("w1_0", w1_0, wn),
+                      rng("w2_0", w2_0, wn), rng("ln_gamma", gamma, (int64_t)H * d * 4),
+                      rng("ln_beta", beta, (int64_t)H * d * 4)};
+  const Range out[] = {rng("z", z, seq * 4), rng("w1_out", w1_out, units * hidden * d * 4),
+                       rng("w2_out", w2_out, units * hidden * d * 4)};
+  const int pairs[][2] = {{4, 1}, {5, 2}};
+  ttt_status_t st = check_common(fn, dt, w0_per_batch, B, H, T, d, b, in, 8, out, 3, pairs, 2,
+                                 T > 0);
+  if (st != TTT_OK) return st;
+  if (hidden != 256)
+    return fail(TTT_ERR_UNSUPPORTED, "%s: hidden=%d unsupported (only 256)", fn, hidden);
+  if (!(eps > 0.f) || eps > 3.0e38f)
+    return fail(TTT_ERR_VALUE, "%s: eps=%g must be finite and > 0", fn, (double)eps);
+  if (units == 0) return TTT_OK;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (T == 0) {
+    if (!(w0_per_batch && w1_0 == w1_out))
+      e = ttt::launch_copy_state(w1_0, w0_per_batch, (int)units, H, hidden * d, w1_out, s);
+    if (e == hipSuccess && !(w0_per_batch && w2_0 == w2_out))
+      e = ttt::launch_copy_state(w2_0, w0_per_batch, (int)units, H, hidden * d, w2_out, s);
+  } else {
+    const ttt::MlpLnArgs a{{q, k, v, eta, w1_0, w2_0, z, w1_out, w2_out, w0_per_batch, (int)units,
+                            H, T, b},
+                           gamma, beta, eps};
+    e = ttt::launch_mlp_ln(a, dt == TTT_F32, s);
+  }
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return TTT_OK;
+}
+
 ttt_status_t mlp_bwd_impl(const void* q, const void* k, const void* v, const float* eta,
                           const float* w1_ckpt, const float* w2_ckpt, int32_t B, int32_t H,
                           int32_t T, int32_t d, int32_t hidden, int32_t b, ttt_dtype_t dt,
@@ -768,6 +811,16 @@ ttt_status_t ttt_mlp_fwd(const void* q, const void* k, const void* v, const floa
                          void* stream) {
   return mlp_impl(q, k, v, eta, w1_0, w2_0, w0_per_batch, B, H, T, d, hidden, b, qkv_dtype, z,
                   w1_out, w2_out, stream);
+}
+
+ttt_status_t ttt_mlp_ln_fwd(const void* q, const void* k, const void* v, const float* eta,
+                            const float* w1_0, const float* w2_0, int32_t w0_per_batch,
+                            const float* ln_gamma, const float* ln_beta, float eps, int32_t B,
+                            int32_t H, int32_t T, int32_t d, int32_t hidden, int32_t b,
+                            ttt_dtype_t qkv_dtype, float* z, float* w1_out, float* w2_out,
+                            void* stream) {
+  return mlp_ln_impl(q, k, v, eta, w1_0, w2_0, w0_per_batch, ln_gamma, ln_beta, eps, B, H, T, d,
+                     hidden, b, qkv_dtype, z, w1_out, w2_out, stream);
 }
 
 ttt_status_t ttt_lr_gate(const void* x, ttt_dtype_t x_dtype, const float* theta_lr,

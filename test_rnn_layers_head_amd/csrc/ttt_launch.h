@@ -122,6 +122,16 @@ struct MlpArgs {
   float* w2_ckpt = nullptr;
 };
 
+// TTT-MLP with the LayerNorm + residual wrapper, f(x) = x + LN(W2 GELU(W1 x))
+// (primal form, any b, fp32 or bf16 q/k/v; gamma, beta [H][64]).
+struct MlpLnArgs {
+  MlpArgs s;
+  const float* gamma;
+  const float* beta;
+  float eps;
+};
+hipError_t launch_mlp_ln(const MlpLnArgs& a, bool f32in, hipStream_t s);
+
 // Backward of the TTT-MLP scan (hidden = 256, any b, fp32 or bf16 q/k/v).
 struct MlpBwdArgs {
   const void* q;          // [units][T][64]

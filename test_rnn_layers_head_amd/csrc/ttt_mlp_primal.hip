@@ -19,6 +19,13 @@
 // exactly in real arithmetic; it is the per-token recurrence the dual form
 // reorganises.
 //
+// With the LayerNorm + residual wrapper (§4.4), f(x) = x + LN(y) with
+// y = W2 GELU(W1 x) and LN(y) = gamma (y - mean y) / sqrt(var y + eps) + beta
+// over the 64 components: e = 2 (y - v) becomes the LayerNorm's VJP of
+// g = 2 gamma (k + LN(y) - v), and the output is q + LN(W2_t GELU(W1_t q)).
+// The 64 components of y live in wave 0, one per lane, so the LayerNorm's
+// sums are wave reductions.
+//
 // Work split: one workgroup of 1024 threads (16 waves) per (batch, head) unit.
 // Thread (wave v, lane l) owns hidden unit u = 16 v + (l % 16) and the quarter
 // j in [16 qd, 16 qd + 16), qd = l / 16, of the 64 input / output components:
@@ -50,6 +57,14 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v;
 }
 
+// Sum over the 64 lanes of a wave; every lane gets the total.
+__device__ __forceinline__ float wave_total(float v) {
+  v = row_sum16(v);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
 // Sum over the four quarters (lanes l, l ^ 16, l ^ 32, l ^ 48).
 __device__ __forceinline__ float quarter_sum(float v) {
   v += __shfl_xor(v, 16);
@@ -63,8 +78,9 @@ __device__ __forceinline__ float load_in(const void* p, size_t i) {
   else return bf16_val(((const short*)p)[i]);
 }
 
-template <bool F32IN>
-__global__ void __launch_bounds__(PTHREADS) mlp_primal_kernel(MlpArgs a) {
+template <bool F32IN, bool LN>
+__global__ void __launch_bounds__(PTHREADS) mlp_primal_kernel(MlpLnArgs la) {
+  const MlpArgs& a = la.s;
   __shared__ float tok[2][PCH * PSTRIDE];  // staged tokens: k[64] v[64] q[64] eta
   __shared__ float red[2][16][64];         // per-wave partial sums over u (y, z)
   __shared__ float ebuf[64];               // e of the current token
@@ -89,6 +105,19 @@ __global__ void __launch_bounds__(PTHREADS) mlp_primal_kernel(MlpArgs a) {
   }
 
   const size_t base = (size_t)unit * T * 64;
+  // LayerNorm (wave 0, lane = component): scale, shift, and the previous
+  // token's q for its output
+  float lg = 0.f, lb = 0.f, qprev = 0.f;
+  if (LN && t < 64) {
+    lg = la.gamma[(size_t)head * 64 + t];
+    lb = la.beta[(size_t)head * 64 + t];
+  }
+  // (y - mean) / sqrt(var + eps) over the wave's 64 lanes (two passes); rs out
+  auto lnhat = [&](float y, float& rs) {
+    const float dev = y - wave_total(y) * (1.f / 64);
+    rs = 1.f / sqrtf(wave_total(dev * dev) * (1.f / 64) + la.eps);
+    return dev * rs;
+  };
   // stage tokens [c * PCH, c * PCH + PCH) into buffer c & 1 (zeros past T)
   auto stage = [&](int c) {
     float* dst = tok[c & 1];
@@ -156,13 +185,27 @@ __global__ void __launch_bounds__(PTHREADS) mlp_primal_kernel(MlpArgs a) {
         float y = 0.f;
 #pragma unroll
         for (int w = 0; w < 16; ++w) y += red[0][w][t];
-        ebuf[t] = 2.f * (y - vt[t]);
+        if constexpr (LN) {
+          // g = 2 gamma (k + gamma yhat + beta - v), then the LayerNorm VJP
+          float rs;
+          const float yh = lnhat(y, rs);
+          const float gv = 2.f * lg * (kt[t] + lg * yh + lb - vt[t]);
+          const float m1 = wave_total(gv) * (1.f / 64), m2 = wave_total(gv * yh) * (1.f / 64);
+          ebuf[t] = rs * (gv - m1 - yh * m2);
+        } else {
+          ebuf[t] = 2.f * (y - vt[t]);
+        }
         if (tt > 0) {
           float zs = 0.f;
 #pragma unroll
           for (int w = 0; w < 16; ++w) zs += red[1][w][t];
+          if constexpr (LN) {
+            float rs;
+            zs = qprev + lg * lnhat(zs, rs) + lb;
+          }
           zu[(size_t)(tt - 1) * 64 + t] = zs;
         }
+        if constexpr (LN) qprev = qt[t];
       }
       __syncthreads();  // B2
       // backward to the first layer, then both updates
@@ -199,6 +242,10 @@ __global__ void __launch_bounds__(PTHREADS) mlp_primal_kernel(MlpArgs a) {
     float zs = 0.f;
 #pragma unroll
     for (int w = 0; w < 16; ++w) zs += red[1][w][t];
+    if constexpr (LN) {
+      float rs;
+      zs = qprev + lg * lnhat(zs, rs) + lb;
+    }
     zu[(size_t)(T - 1) * 64 + t] = zs;
   }
   float* w1o = a.w1_out + (size_t)unit * PHID * 64;
@@ -500,8 +547,14 @@ hipError_t launch_mlp_bwd(const MlpBwdArgs& a, bool f32in, hipStream_t s) {
 }
 
 hipError_t launch_mlp_primal(const MlpArgs& a, bool f32in, hipStream_t s) {
-  if (f32in) return launch(mlp_primal_kernel<true>, dim3(a.units), dim3(PTHREADS), s, a);
-  return launch(mlp_primal_kernel<false>, dim3(a.units), dim3(PTHREADS), s, a);
+  const MlpLnArgs la{a, nullptr, nullptr, 0.f};
+  if (f32in) return launch(mlp_primal_kernel<true, false>, dim3(a.units), dim3(PTHREADS), s, la);
+  return launch(mlp_primal_kernel<false, false>, dim3(a.units), dim3(PTHREADS), s, la);
+}
+
+hipError_t launch_mlp_ln(const MlpLnArgs& a, bool f32in, hipStream_t s) {
+  if (f32in) return launch(mlp_primal_kernel<true, true>, dim3(a.s.units), dim3(PTHREADS), s, a);
+  return launch(mlp_primal_kernel<false, true>, dim3(a.s.units), dim3(PTHREADS), s, a);
 }
 
 }  // namespace ttt

@@ -204,6 +204,39 @@ def test_linear_ln_argument_checks(lib, kw, expect):
         assert lib.ttt_last_error().startswith(b"ttt_linear_ln_fwd:")
 
 
+def mlp_ln(lib, **kw):
+    args = dict(q=A[0], k=A[1], v=A[2], eta=A[3], w1=A[4], w2=A[9], per_batch=0, gamma=A[7],
+                beta=A[8], eps=1e-5, B=1, H=1, T=16, d=64, hidden=256, b=16, dt=_lib.TTT_BF16,
+                z=A[5], w1o=A[6], w2o=A[10])
+    args.update(kw)
+    return lib.ttt_mlp_ln_fwd(args["q"], args["k"], args["v"], args["eta"], args["w1"],
+                              args["w2"], args["per_batch"], args["gamma"], args["beta"],
+                              args["eps"], args["B"], args["H"], args["T"], args["d"],
+                              args["hidden"], args["b"], args["dt"], args["z"], args["w1o"],
+                              args["w2o"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(eps=0.0), "TTT_ERR_VALUE"),
+    (dict(eps=float("nan")), "TTT_ERR_VALUE"),
+    (dict(b=24), "TTT_ERR_UNSUPPORTED"),
+    (dict(hidden=128), "TTT_ERR_UNSUPPORTED"),
+    (dict(d=32), "TTT_ERR_UNSUPPORTED"),
+    (dict(dt=6), "TTT_ERR_DTYPE"),
+    (dict(gamma=None), "TTT_ERR_NULL"),
+    (dict(w2=None), "TTT_ERR_NULL"),
+    (dict(beta=A[8] + 8), "TTT_ERR_ALIGN"),
+    (dict(z=A[7]), "TTT_ERR_ALIAS"),
+    (dict(w1o=A[9]), "TTT_ERR_ALIAS"),
+    (dict(T=1 << 24), "TTT_ERR_SHAPE"),
+    (dict(B=0), "TTT_OK"),
+])
+def test_mlp_ln_argument_checks(lib, kw, expect):
+    assert mlp_ln(lib, **kw) == status(expect), lib.ttt_last_error()
+    if expect != "TTT_OK":
+        assert lib.ttt_last_error().startswith(b"ttt_mlp_ln_fwd:")
+
+
 def test_mlp_argument_checks(lib):
     f = lambda **kw: lib.ttt_mlp_fwd(A[0], A[1], A[2], A[3], A[4], A[9], 0, 1, 1, 16, 64,
                                      kw.get("hidden", 256), kw.get("b", 16),
