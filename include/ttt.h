@@ -176,10 +176,13 @@ ttt_status_t ttt_mlp_ln_fwd(const void* q, const void* k, const void* v,
  * Training support (§6.12: the outer loop differentiates through the inner
  * one; the forward keeps the state at the start of every mini-batch, the
  * kappa = T / b checkpoints, and the backward walks the mini-batches in
- * reverse).  Support: d = 64, bf16 q/k/v, b = 16; else TTT_ERR_UNSUPPORTED.
+ * reverse).  Support: d = 64, bf16 or fp32 q/k/v, b dividing 16 or a
+ * multiple of 16; else TTT_ERR_UNSUPPORTED.  bf16 with b = 16 runs the
+ * dual-form kernels; every other case runs the primal-form kernels (one
+ * token at a time, fp32 arithmetic, no sequence chunks).
  *
  * ttt_linear_fwd_ckpt: ttt_linear_fwd plus
- *   w_ckpt : out [B][H][ceil(T/16)][d][d] fp32, the state before each
+ *   w_ckpt : out [B][H][ceil(T/b)][d][d] fp32, the state before each
  *            mini-batch (w_ckpt[..][0] = W0).
  * It takes sequence chunks as ttt_linear_fwd does; the last pass writes the
  * checkpoints.
