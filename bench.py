@@ -412,8 +412,10 @@ def training_case(wl, steps, warmup, b=16):
     bb = bwd_alg_bytes(wl, b)
     chunks = ttt_linear_fwd_plan(wl.B, wl.H, wl.T, b)[1]
     extra = {"seq_chunks": chunks}
-    if b != 16 or x.q.dtype != np.uint16:
+    if b != 16 or wl.qkv_dtype != "bf16":
         extra["kernels"] = "linear_primal_ckpt_kernel / linear_primal_bwd_kernel"
+    else:
+        extra["kernels"] = "linear_scan_bf16_kernel with checkpoint stores / linear_bwd_kernel"
     if chunks > 1:
         _, k1, _ = time_launches(lambda: ttt_linear_bwd(d["q"], d["k"], d["v"], d["eta"], ck, 16, dz,
                                                         seq_chunks=1), steps, warmup)
