@@ -494,8 +494,9 @@ def ln_training_case(wl, b, steps, warmup):
 
 
 def mlp_ln_case(wl, b, steps, warmup):
-    """ttt_mlp_ln_fwd (TTT-MLP with the LayerNorm + residual wrapper, the
-    primal-form kernel) on one workload."""
+    """ttt_mlp_ln_fwd (TTT-MLP with the LayerNorm + residual wrapper) on one
+    workload: the dual-form scan for bf16 inputs with b | 16, else the
+    primal-form kernel."""
     import torch
     from test_rnn_layers_head_amd import inputs, ttt_mlp_ln_fwd
     x = inputs.make_inputs(wl)
@@ -511,7 +512,10 @@ def mlp_ln_case(wl, b, steps, warmup):
             "kernel_us_mean": kmean, "kernel_us_median": spread["median"],
             "alg_bytes": byts, "alg_flops": flops,
             "hbm_frac_algorithmic": byts / (kmean * 1e-6) / 1e9 / HBM_PEAK_GBS,
-            "kernel": "mlp_primal_kernel with the LayerNorm wrapper (fp32, one token at a time)"}
+            "mfma_frac_algorithmic": flops / (kmean * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+            "kernel": ("mlp_scan_kernel with the LayerNorm wrapper (dual form)"
+                       if wl.qkv_dtype == "bf16" and b <= 16 and 16 % b == 0 else
+                       "mlp_primal_kernel with the LayerNorm wrapper (fp32, one token at a time)")}
 
 
 def gate_alg_bytes(wl) -> int:

@@ -158,10 +158,12 @@ ttt_status_t ttt_linear_ln_fwd(const void* q, const void* k, const void* v,
  * ln_beta ([H][d] fp32, per head) and eps (finite and > 0, else
  * TTT_ERR_VALUE).
  *
- * Support: d = 64, hidden = 256, fp32 or bf16 q/k/v, b | 16 or 16 | b.  It
- * runs the primal form token by token in fp32 arithmetic (1024 threads per
- * (batch, head)); the LayerNorm's sums over the 64 components are wave
- * reductions.
+ * Support: d = 64, hidden = 256, fp32 or bf16 q/k/v, b | 16 or 16 | b.
+ * bf16 q/k/v with b | 16 runs the dual-form scan of ttt_mlp_fwd (same
+ * work split and precision), the LayerNorm's per-token sums over the 64
+ * components crossing the reducing waves through LDS; fp32 inputs and b > 16
+ * run the primal form token by token in fp32 arithmetic (1024 threads per
+ * (batch, head)).
  */
 ttt_status_t ttt_mlp_ln_fwd(const void* q, const void* k, const void* v,
                             const float* eta, const float* w1_0,

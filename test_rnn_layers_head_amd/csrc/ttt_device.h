@@ -166,6 +166,16 @@ __device__ __forceinline__ GeluOut gelu_and_grad(float x) {
   return GeluOut{x * phi_cdf, fmaf(x, e * 0.39894228040143268f, phi_cdf)};
 }
 
+// Sum over the 16 lanes of a DPP row (row rotations by 8, 4, 2, 1); every
+// lane of the row gets the total.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xf, 0xf, false));
+  return v;
+}
+
 // Compiler-level ordering around the hardware barrier.  No cache or counter
 // wait is implied: producers that write LDS with DMA wait on their own
 // vector-memory counter before arriving.

@@ -123,7 +123,8 @@ struct MlpArgs {
 };
 
 // TTT-MLP with the LayerNorm + residual wrapper, f(x) = x + LN(W2 GELU(W1 x))
-// (primal form, any b, fp32 or bf16 q/k/v; gamma, beta [H][64]).
+// (gamma, beta [H][64]).  launch_mlp_ln runs the dual-form scan for bf16
+// q/k/v with b | 16 and the primal form (any b, fp32 or bf16) otherwise.
 struct MlpLnArgs {
   MlpArgs s;
   const float* gamma;
@@ -131,6 +132,7 @@ struct MlpLnArgs {
   float eps;
 };
 hipError_t launch_mlp_ln(const MlpLnArgs& a, bool f32in, hipStream_t s);
+hipError_t launch_mlp_ln_primal(const MlpLnArgs& a, bool f32in, hipStream_t s);
 
 // Backward of the TTT-MLP scan (hidden = 256, any b, fp32 or bf16 q/k/v).
 struct MlpBwdArgs {

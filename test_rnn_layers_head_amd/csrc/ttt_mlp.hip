@@ -33,6 +33,19 @@
 // For training, a variant also stores the state before every mini-batch
 // (the checkpoints of §6.12), straight from the registers.
 //
+// LayerNorm + residual variant (§4.4 wrapper, f(x) = x + LN(W2 GELU(W1 x)),
+// LN over the d = 64 outputs of one token with gamma, beta per head): with
+// Y = Z2 at the gradient point, rs = 1 / sqrt(var_i Y + eps), Yh = (Y - mean) rs
+// and g = 2 gamma (K + gamma Yh + beta - V) (the loss gradient at Yh),
+//   Gn2 = -rs (g - mean_i g - Yh mean_i (g Yh)) diag(eta)
+// replaces the plain -2 (Z2 - V) diag(eta), and every output is
+// z = q + gamma LN-hat(Z) + beta.  The per-token sums over i cross the four
+// reducing waves through LDS: (sum Y, sum Y^2), then (sum g, sum g Yh), each
+// behind a workgroup barrier, and the output's (sum Z, sum Z^2) behind the
+// next tile's first barrier, off the recurrence.  The variance is the
+// one-pass E[Y^2] - mean^2, clamped at 0.  K - V and q enter the
+// accumulator layout exactly, as one-hot MFMA selections of the bf16 tiles.
+//
 // Inputs are register-staged one tile ahead by the waves themselves (each
 // lane moves 16-byte chunks of K, Q, V or one eta), so no wave issues
 // LDS-DMA and no wave is idle.  Mini-batches b < 16 (b | 16) run each
@@ -58,7 +71,9 @@ struct MlpGeom {
   static constexpr int L_G2A = L_A2P + NW * 1024;      // [mi][lane] hi|lo of Gn2^T (t x i)
   static constexpr int L_G2B = L_G2A + 4 * 1024;       // [mi][lane] hi|lo of Gn2 (i x t)
   static constexpr int L_W2N = L_G2B + 4 * 1024;       // [wave][mi][nu][lane] f32x4: W2 (i x u)
-  static constexpr int L_TOTAL = L_W2N + NW * 4 * NB * 1024;
+  // LayerNorm sums: 3 areas (Y, the VJP, the outputs) x 2 values x [mi][t]
+  static constexpr int L_ST = L_W2N + NW * 4 * NB * 1024;
+  static constexpr int L_TOTAL = L_ST + 3 * 512;
   static constexpr int LOADS = (400 + NW * 64 - 1) / (NW * 64);  // staged chunks per lane
 };
 
@@ -96,12 +111,12 @@ __device__ __forceinline__ Split4 unpack_split(uint4 v) {
                 __builtin_bit_cast(s16x4, make_uint2(v.z, v.w))};
 }
 
-// Sum of the NW partial blocks of a cross-wave reduction, and the final Z of
-// one pass for output block mi: Z^T = sum partials + triu(sum A2)^T Gn2^T.
-template <int NW, bool SUB>
-__device__ __forceinline__ void reduce_store_z(const char* smem, int lane, int c, int g, int mi,
-                                               const YOps& g2, __amdgpu_buffer_rsrc_t rz,
-                                               int tile, int pass, int bsub) {
+// Sum of the NW partial blocks of a cross-wave reduction: the Z of one pass
+// for output block mi (before the LayerNorm of the wrapped variant),
+// Z^T = sum partials + triu(sum A2)^T Gn2^T.
+template <int NW>
+__device__ __forceinline__ f32x4 reduce_z(const char* smem, int lane, int c, int g, int mi,
+                                          const YOps& g2) {
   using G = MlpGeom<NW>;
   f32x4 Zt = {0, 0, 0, 0}, A2 = {0, 0, 0, 0};
 #pragma unroll
@@ -113,7 +128,12 @@ __device__ __forceinline__ void reduce_store_z(const char* smem, int lane, int c
   for (int r = 0; r < 4; ++r)
     if (4 * g + r > c) A2[r] = 0.f;
   const Split4 a2s = split4(A2);
-  Zt = mm_pre(cat44(a2s.hi, a2s.lo), g2, Zt);
+  return mm_pre(cat44(a2s.hi, a2s.lo), g2, Zt);
+}
+// Store output block mi of one pass: lane (c, g) holds Z[t = 4g + r][16 mi + c]
+template <bool SUB>
+__device__ __forceinline__ void store_z(f32x4 Zt, int c, int g, int mi, __amdgpu_buffer_rsrc_t rz,
+                                        int tile, int pass, int bsub) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int tl = 4 * g + r;
@@ -124,12 +144,40 @@ __device__ __forceinline__ void reduce_store_z(const char* smem, int lane, int c
   }
 }
 
+// LayerNorm sums over i of one output block: lane (c, g) holds x[t = 4g + r]
+// at i = 16 mi + c; the row of 16 lanes sums to the block's total for its 4
+// tokens, which lane c = 0 leaves in LDS (area [2][mi][16 t] floats).
+__device__ __forceinline__ void ln_put(char* area, int mi, int c, int g, f32x4 x, f32x4 y) {
+  f32x4 sx, sy;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    sx[r] = row_sum16(x[r]);
+    sy[r] = row_sum16(y[r]);
+  }
+  if (c == 0) {
+    *(f32x4*)(area + (mi * 16 + 4 * g) * 4) = sx;
+    *(f32x4*)(area + 256 + (mi * 16 + 4 * g) * 4) = sy;
+  }
+}
+// Totals over the four blocks (fixed order) for tokens 4g .. 4g + 3.
+__device__ __forceinline__ void ln_get(const char* area, int g, f32x4& sx, f32x4& sy) {
+  sx = f32x4{0, 0, 0, 0};
+  sy = f32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    sx += *(const f32x4*)(area + (mi * 16 + 4 * g) * 4);
+    sy += *(const f32x4*)(area + 256 + (mi * 16 + 4 * g) * 4);
+  }
+}
+
 // CKPT: also store the state before every mini-batch (W1 [256][64] and W2
 // [64][256] per unit and mini-batch, the layouts of the final state) for the
 // backward; the stores are fire-and-forget and leave the recurrence alone.
-template <int NW, bool SUB, bool CKPT = false>
-__global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
+// LN: the LayerNorm + residual wrapper (gamma, beta, eps from the arguments).
+template <int NW, bool SUB, bool CKPT = false, bool LN = false>
+__global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
   using G = MlpGeom<NW>;
+  const MlpArgs& a = la.s;
   constexpr int U = G::U, NB = G::NB, NCH = G::NCH;
   static_assert(NW == 4 || NW == 8, "waves 0..3 each own one 16-column block of d in the reductions");
   __shared__ __attribute__((aligned(16))) char smem[G::L_TOTAL];
@@ -155,6 +203,12 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
     itr[e] = (bf16)((4 * g + (e & 3) == c) ? 1.f : 0.f);
     // -I on 16 V columns (slots 16..31 unused)
     negI[e] = (bf16)((g < 2 && 8 * g + e == c) ? -1.f : 0.f);
+  }
+  // LayerNorm wrapper: gamma, beta of output i = 16 (w % 4) + c
+  float lg = 0.f, lb = 0.f;
+  if constexpr (LN) {
+    lg = la.gamma[head * 64 + 16 * (w & 3) + c];
+    lb = la.beta[head * 64 + 16 * (w & 3) + c];
   }
 
   // hi/lo splits of fp32 blocks form the residual on the matrix unit
@@ -248,8 +302,48 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
   fetch(1, pf);
   wg_barrier();
 
-  YOps g2prev;  // Gn2 operands (block mi = w) of the previous pass
+  // Outputs.  Block mi = w % 4 of the previous pass's Z goes out from waves
+  // OUT0 .. OUT0 + 3 at the start of the next pass; in the wrapped variant
+  // with 8 waves (LATE) from waves 4..7 between its first two barriers,
+  // where they would otherwise wait for the gradient, taking the Gn2
+  // operands from LDS rather than holding them through the forward.
+  constexpr bool LATE = LN && NW == 8;
+  constexpr int OUT0 = LATE ? 4 : 0;
+  const bool outw = w >= OUT0 && w < OUT0 + 4;
+  const int omi = w & 3;
+  YOps g2prev;  // Gn2 operands (block omi) of the previous pass
   int prev_tile = -1, prev_pass = 0;
+  // first stage: the plain variant stores the block; the wrapped one leaves
+  // its LayerNorm sums in LDS and reads -q while the tile is in the ring
+  auto out_first = [&](int tile, int pass, f32x4& zo, f32x4& qn) {
+    if constexpr (LATE)
+      zo = reduce_z<NW>(smem, lane, c, g, omi,
+                        yops(unpack_split(*(const uint4*)(smem + G::L_G2A + omi * 1024 + lane * 16))));
+    else
+      zo = reduce_z<NW>(smem, lane, c, g, omi, g2prev);
+    if constexpr (LN) {
+      const char* Qp = smem + G::L_RAW + (tile & 1) * RAWB + 2048;
+      qn = mfma_k32(*(const bf16x8*)(Qp + swz_chunk(c, 2 * omi + (g & 1))), negI, f32x4{0, 0, 0, 0});
+      f32x4 z2;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) z2[r] = zo[r] * zo[r];
+      ln_put(smem + G::L_ST + 2 * 512, omi, c, g, zo, z2);
+    } else {
+      store_z<SUB>(zo, c, g, omi, rz, tile, pass, bsub);
+    }
+  };
+  // second stage (wrapped, after a barrier): z = q + gamma LN-hat(Z) + beta
+  auto out_second = [&](int tile, int pass, f32x4 zo, f32x4 qn) {
+    f32x4 s1, s2, zr;
+    ln_get(smem + G::L_ST + 2 * 512, g, s1, s2);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float mu = s1[r] * (1.f / 64);
+      const float ro = rsqrtf(fmaxf(fmaf(s2[r], 1.f / 64, -mu * mu), 0.f) + la.eps);
+      zr[r] = fmaf(lg, (zo[r] - mu) * ro, lb) - qn[r];
+    }
+    store_z<SUB>(zr, c, g, omi, rz, tile, pass, bsub);
+  };
   const int nmb = (T + bsub - 1) / bsub;  // mini-batches (checkpoints)
   // this wave's rows of W1 and columns of W2 in the final-state layouts
   auto store_state = [&](float* w1o, float* w2o) {
@@ -296,9 +390,12 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
           store_state(a.w1_ckpt + co, a.w2_ckpt + co);
         }
       }
-      // ================= Z of the previous pass, output block mi = w
-      if (prev_tile >= 0 && w < 4)
-        reduce_store_z<NW, SUB>(smem, lane, c, g, w, g2prev, rz, prev_tile, prev_pass, bsub);
+      // ================= Z of the previous pass (4 waves: now; the wrapped
+      // variant normalises after B2, holding Z and q)
+      f32x4 zo = {0, 0, 0, 0}, qn = {0, 0, 0, 0};
+      const int out_tile = prev_tile, out_pass = prev_pass;
+      if constexpr (!LATE)
+        if (out_tile >= 0 && outw) out_first(out_tile, out_pass, zo, qn);
 
       f32x4 e2;  // 2 eta of this pass's sub-batch
 #pragma unroll
@@ -353,22 +450,78 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
       }
       wg_barrier();  // B1: partial Z2 written
 
+      // ================= LATE: the previous pass's Z from waves 4..7
+      if constexpr (LATE)
+        if (out_tile >= 0 && outw) out_first(out_tile, out_pass, zo, qn);
+
       // ================= Gn2 = 2 eta (V - Z2) for output block mi = w
+      // (wrapped variant: the LayerNorm VJP, two rounds of sums over i)
+      // (LATE: waves 0..3 keep Y and K - V in the registers that waves 4..7
+      // use for the previous Z and -q, so the two roles share them)
+      f32x4 Z2v = {0, 0, 0, 0}, KVv = {0, 0, 0, 0};
+      f32x4& Z2 = LATE ? zo : Z2v;
+      f32x4& KV = LATE ? qn : KVv;
       if (w < 4) {
         const int mi = w;
-        f32x4 Z2 = {0, 0, 0, 0};
 #pragma unroll
         for (int v = 0; v < NW; ++v) Z2 += *(const f32x4*)(smem + G::L_Z2P + (v * 4 + mi) * 1024 + lane * 16);
-        Z2 = mfma_k32(*(const bf16x8*)(Vt + c * 128 + (16 * mi + 8 * (g & 1)) * 2), negI, Z2);  // Z2 - V
-        f32x4 Gv;
+        const bf16x8 vch = *(const bf16x8*)(Vt + c * 128 + (16 * mi + 8 * (g & 1)) * 2);
+        if constexpr (LN) {
+          KV = mfma_k32(*(const bf16x8*)(Kt + swz_chunk(c, 2 * mi + (g & 1))), negI, KV);  // -K
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Gv[r] = -e2[r] * Z2[r];
+          for (int r = 0; r < 4; ++r) KV[r] = -KV[r];
+          KV = mfma_k32(vch, negI, KV);  // K - V
+          f32x4 y2;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) y2[r] = Z2[r] * Z2[r];
+          ln_put(smem + G::L_ST, mi, c, g, Z2, y2);
+        } else {
+          Z2 = mfma_k32(vch, negI, Z2);  // Z2 - V
+        }
+      }
+      f32x4 rs, yh, gv;
+      if constexpr (LN) {
+        wg_barrier();  // sums of Y (and of the previous pass's Z)
+        if constexpr (LATE)
+          if (out_tile >= 0 && outw) out_second(out_tile, out_pass, zo, qn);
+        if (w < 4) {
+          f32x4 s1, s2;
+          ln_get(smem + G::L_ST, g, s1, s2);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float mu = s1[r] * (1.f / 64);
+            rs[r] = rsqrtf(fmaxf(fmaf(s2[r], 1.f / 64, -mu * mu), 0.f) + la.eps);
+            yh[r] = (Z2[r] - mu) * rs[r];
+            gv[r] = 2.f * lg * (KV[r] + fmaf(lg, yh[r], lb));
+          }
+          f32x4 gy;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) gy[r] = gv[r] * yh[r];
+          ln_put(smem + G::L_ST + 512, w, c, g, gv, gy);
+        }
+        wg_barrier();  // sums of the VJP
+      }
+      if (w < 4) {
+        const int mi = w;
+        f32x4 Gv;
+        if constexpr (LN) {
+          f32x4 m1, m2;
+          ln_get(smem + G::L_ST + 512, g, m1, m2);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            Gv[r] = -0.5f * e2[r] * rs[r] * (gv[r] - m1[r] * (1.f / 64) - yh[r] * m2[r] * (1.f / 64));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Gv[r] = -e2[r] * Z2[r];
+        }
         const Split4 gs = split4(Gv);
         *(uint4*)(smem + G::L_G2A + mi * 1024 + lane * 16) = pack_split(gs);
         const f32x4 GT = mfma_k32(cat44(gs.hi, gs.lo), itr, f32x4{0, 0, 0, 0});  // Gn2[i][t]
         *(uint4*)(smem + G::L_G2B + mi * 1024 + lane * 16) = pack_split(split4(GT));
       }
       wg_barrier();  // B2: Gn2 ready
+      if constexpr (LN && !LATE)
+        if (out_tile >= 0 && outw) out_second(out_tile, out_pass, zo, qn);
 
       // ================= backward to layer 1: Gn1^T = (Gn2^T W2) * GELU'(Z1)
       Split4 g2s[4];
@@ -417,7 +570,12 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
       for (int mi = 0; mi < 4; ++mi) {
         f32x4 zp = {0, 0, 0, 0};
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) zp = mm3(x2qop[ch], w2s[mi][ch], zp);
+        for (int ch = 0; ch < NCH; ++ch) {
+          if constexpr (LN)  // split again: not held through the LayerNorm rounds
+            zp = mm3(x2qop[ch], split8_mfma(W2T[2 * ch][mi], W2T[2 * ch + 1][mi], ns), zp);
+          else
+            zp = mm3(x2qop[ch], w2s[mi][ch], zp);
+        }
         *(f32x4*)(smem + G::L_ZP + (w * 4 + mi) * 1024 + lane * 16) = zp;
       }
       {
@@ -449,10 +607,12 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
           *w2n_at(mi, nu) = mm_pre(cat44(g2s[mi].hi, g2s[mi].lo), xy, *w2n_at(mi, nu));  // += Gn2 X2^T
         }
       }
-      if (w == 0) g2prev = g2y[0];
-      if (w == 1) g2prev = g2y[1];
-      if (w == 2) g2prev = g2y[2];
-      if (w == 3) g2prev = g2y[3];
+      if constexpr (!LATE) {  // the output waves are 0..3
+        if (w == 0) g2prev = g2y[0];
+        if (w == 1) g2prev = g2y[1];
+        if (w == 2) g2prev = g2y[2];
+        if (w == 3) g2prev = g2y[3];
+      }
       prev_tile = j;
       prev_pass = p;
 
@@ -462,8 +622,13 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpArgs a) {
     fetch(j + 2, pf);
   }
 
-  if (prev_tile >= 0 && w < 4)
-    reduce_store_z<NW, SUB>(smem, lane, c, g, w, g2prev, rz, prev_tile, prev_pass, bsub);
+  // the last pass's outputs (prev_tile is the same in every wave)
+  f32x4 zo = {0, 0, 0, 0}, qn = {0, 0, 0, 0};
+  if (prev_tile >= 0 && outw) out_first(prev_tile, prev_pass, zo, qn);
+  if constexpr (LN) {
+    wg_barrier();  // the output sums
+    if (prev_tile >= 0 && outw) out_second(prev_tile, prev_pass, zo, qn);
+  }
 
   store_state(a.w1_out + (size_t)unit * HID * 64, a.w2_out + (size_t)unit * 64 * HID);  // final state
 }
@@ -474,12 +639,21 @@ hipError_t launch_mlp(const MlpArgs& a, bool f32in, hipStream_t s) {
   constexpr int NW = 4;
   // fp32 inputs and mini-batches spanning several tiles: the primal kernel
   if (f32in || a.b > 16) return launch_mlp_primal(a, f32in, s);
+  const MlpLnArgs la{a, nullptr, nullptr, 0.f};
   if (a.w1_ckpt) {
-    if (a.b == 16) return launch(mlp_scan_kernel<2 * NW, false, true>, dim3(a.units), dim3(2 * NW * 64), s, a);
-    return launch(mlp_scan_kernel<NW, true, true>, dim3(a.units), dim3(NW * 64), s, a);
+    if (a.b == 16) return launch(mlp_scan_kernel<2 * NW, false, true>, dim3(a.units), dim3(2 * NW * 64), s, la);
+    return launch(mlp_scan_kernel<NW, true, true>, dim3(a.units), dim3(NW * 64), s, la);
   }
-  if (a.b == 16) return launch(mlp_scan_kernel<2 * NW, false>, dim3(a.units), dim3(2 * NW * 64), s, a);
-  return launch(mlp_scan_kernel<NW, true>, dim3(a.units), dim3(NW * 64), s, a);
+  if (a.b == 16) return launch(mlp_scan_kernel<2 * NW, false>, dim3(a.units), dim3(2 * NW * 64), s, la);
+  return launch(mlp_scan_kernel<NW, true>, dim3(a.units), dim3(NW * 64), s, la);
+}
+
+hipError_t launch_mlp_ln(const MlpLnArgs& a, bool f32in, hipStream_t s) {
+  constexpr int NW = 4;
+  if (f32in || a.s.b > 16) return launch_mlp_ln_primal(a, f32in, s);
+  if (a.s.b == 16)
+    return launch(mlp_scan_kernel<2 * NW, false, false, true>, dim3(a.s.units), dim3(2 * NW * 64), s, a);
+  return launch(mlp_scan_kernel<NW, true, false, true>, dim3(a.s.units), dim3(NW * 64), s, a);
 }
 
 }  // namespace ttt

@@ -48,15 +48,6 @@ __device__ __forceinline__ float gelu_phi(float x) {
   return 0.5f * (1.f + erff(x * 0.70710678118654752f));
 }
 
-// Sum over the 16 lanes of a DPP row; every lane of the row gets the total.
-__device__ __forceinline__ float row_sum16(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xf, 0xf, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xf, 0xf, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xf, 0xf, false));
-  return v;
-}
-
 // Sum over the 64 lanes of a wave; every lane gets the total.
 __device__ __forceinline__ float wave_total(float v) {
   v = row_sum16(v);
@@ -552,7 +543,7 @@ hipError_t launch_mlp_primal(const MlpArgs& a, bool f32in, hipStream_t s) {
   return launch(mlp_primal_kernel<false, false>, dim3(a.units), dim3(PTHREADS), s, la);
 }
 
-hipError_t launch_mlp_ln(const MlpLnArgs& a, bool f32in, hipStream_t s) {
+hipError_t launch_mlp_ln_primal(const MlpLnArgs& a, bool f32in, hipStream_t s) {
   if (f32in) return launch(mlp_primal_kernel<true, true>, dim3(a.s.units), dim3(PTHREADS), s, a);
   return launch(mlp_primal_kernel<false, true>, dim3(a.s.units), dim3(PTHREADS), s, a);
 }
