@@ -226,6 +226,86 @@ def linear_bwd_unit(q, k, v, eta, w0, b, dz, dwT):
     return dq, dk, dv, deta, Wb
 
 
+def gelu_grad2(x):
+    return np.exp(-0.5 * x * x) / np.sqrt(2.0 * np.pi) * (2.0 - x * x)
+
+
+def mlp_bwd_unit(q, k, v, eta, w1, w2, b, dz, dw1T=None, dw2T=None):
+    """Adjoint of the TTT-MLP dual-form recurrence (mlp_unit), one unit,
+    mini-batch by mini-batch in reverse.  Per mini-batch (D = diag eta,
+    Phi' = GELU', Phi'' = GELU''):
+      Z1 = W1 K, X2 = GELU(Z1), Z2 = W2 X2, G2 = 2 (Z2 - V) D,
+      S = W2^T G2, G1 = S * Phi'(Z1), A = triu(K^T Q),
+      Z1q = W1 Q - G1 A, X2q = GELU(Z1q), B2 = triu(X2^T X2q),
+      Z = W2 X2q - G2 B2, W1' = W1 - G1 K^T, W2' = W2 - G2 X2^T.
+    Given Zb and W1b', W2b' it takes every product back in reverse order.
+    Returns (dq, dk, dv, deta, dw1_0, dw2_0)."""
+    T, d = q.shape
+    W1s, W2s = [np.array(w1, dtype=np.float64)], [np.array(w2, dtype=np.float64)]
+    blocks = list(range(0, T, b))
+    for m0 in blocks:
+        m1 = min(T, m0 + b)
+        XK, XV = k[m0:m1].T, v[m0:m1].T
+        Z1 = W1s[-1] @ XK
+        X2 = gelu(Z1)
+        G2 = 2.0 * (W2s[-1] @ X2 - XV) * eta[m0:m1][None, :]
+        G1 = (W2s[-1].T @ G2) * gelu_grad(Z1)
+        W1s.append(W1s[-1] - G1 @ XK.T)
+        W2s.append(W2s[-1] - G2 @ X2.T)
+    dq, dk, dv = (np.zeros((T, d)) for _ in range(3))
+    deta = np.zeros(T)
+    W1b = np.zeros_like(W1s[0]) if dw1T is None else np.array(dw1T, dtype=np.float64)
+    W2b = np.zeros_like(W2s[0]) if dw2T is None else np.array(dw2T, dtype=np.float64)
+    for jb in reversed(range(len(blocks))):
+        m0 = blocks[jb]
+        m1 = min(T, m0 + b)
+        W1, W2 = W1s[jb], W2s[jb]
+        XK, XV, XQ = k[m0:m1].T, v[m0:m1].T, q[m0:m1].T
+        e = eta[m0:m1][None, :]
+        # forward of the mini-batch
+        Z1 = W1 @ XK
+        X2, D = gelu(Z1), gelu_grad(Z1)
+        E = W2 @ X2 - XV
+        G2 = 2.0 * E * e
+        S = W2.T @ G2
+        G1 = S * D
+        A = np.triu(XK.T @ XQ)
+        Z1q = W1 @ XQ - G1 @ A
+        X2q, Dq = gelu(Z1q), gelu_grad(Z1q)
+        B2 = np.triu(X2.T @ X2q)
+        # adjoints
+        Zb = dz[m0:m1].T
+        W1n, W2n = W1b.copy(), W2b.copy()  # the state's adjoint passes through
+        W2n += Zb @ X2q.T
+        Mb = np.triu(-G2.T @ Zb)
+        X2b = X2q @ Mb.T - W2b.T @ G2
+        X2qb = W2.T @ Zb + X2 @ Mb
+        G2b = -Zb @ B2.T - W2b @ X2
+        G1b = -W1b @ XK
+        Kb = -W1b.T @ G1
+        Z1qb = X2qb * Dq
+        W1n += Z1qb @ XQ.T
+        Qb = W1.T @ Z1qb
+        G1b += -Z1qb @ A.T
+        Ab = np.triu(-G1.T @ Z1qb)
+        Kb += XQ @ Ab.T
+        Qb += XK @ Ab
+        Sb = G1b * D
+        Z1b = G1b * S * gelu_grad2(Z1)
+        W2n += G2 @ Sb.T
+        G2b += W2 @ Sb
+        Eb = 2.0 * G2b * e
+        deta[m0:m1] = np.sum(G2b * 2.0 * E, axis=0)
+        W2n += Eb @ X2.T
+        X2b += W2.T @ Eb
+        Z1b += X2b * D
+        W1n += Z1b @ XK.T
+        Kb += W1.T @ Z1b
+        dq[m0:m1], dk[m0:m1], dv[m0:m1] = Qb.T, Kb.T, -Eb.T
+        W1b, W2b = W1n, W2n
+    return dq, dk, dv, deta, W1b, W2b
+
+
 def linear_bwd(q, k, v, eta, w0, b, dz, dwT=None):
     B, H, T, d = q.shape
     out = [np.zeros((B, H, T, d)) for _ in range(3)] + [np.zeros((B, H, T)), np.zeros((B, H, d, d))]

@@ -697,6 +697,21 @@ def pin_mlp_bwd_equals_autograd_of_dual_form(lib):
                 assert rel(g[i][0, h], leaf.grad.numpy()) < 1e-11, (T, b, h, i)
 
 
+def pin_mlp_bwd_equals_dual_form_adjoint(lib):
+    """The MLP backward equals the hand-written adjoint of the dual form
+    (tests/dual_form.py: every product of one mini-batch taken back in
+    reverse, the form a dual-form backward kernel evaluates), float64."""
+    rng = np.random.default_rng(44)
+    for (T, b) in [(16, 16), (21, 16), (10, 4), (7, 1), (13, 8)]:
+        q, k, v, eta, w1, w2, dz, d1, d2 = _mlp_bwd_case(rng, T, 4, 6)
+        g = oracle.mlp_bwd(q, k, v, eta, w1, w2, b, dz, d1, d2, lib=lib)
+        for h in range(2):
+            r = dual_form.mlp_bwd_unit(q[0, h], k[0, h], v[0, h], eta[0, h], w1[h], w2[h], b,
+                                       dz[0, h], d1[0, h], d2[0, h])
+            for i in range(6):
+                assert rel(g[i][0, h], r[i]) < 1e-12, (T, b, h, i)
+
+
 def pin_mlp_bwd_eta_zero(lib):
     """eta = 0: the state never moves, so z_t = W2_0 GELU(W1_0 q_t) and the
     adjoints are closed forms: dk = dv = 0, dq_t = W1_0^T (GELU'(W1_0 q_t) *
@@ -901,6 +916,7 @@ PINS = [
     pin_ln_bwd_eta_zero,
     pin_mlp_bwd_finite_differences,
     pin_mlp_bwd_equals_autograd_of_dual_form,
+    pin_mlp_bwd_equals_dual_form_adjoint,
     pin_mlp_bwd_eta_zero,
     pin_gate_closed_forms,
     pin_gate_bwd_finite_differences,
