@@ -44,7 +44,7 @@ METRIC = "TTT fwd tokens·heads/s at 1 GPU; % of HBM/MFMA roofline (b=16)"
 UNIT = "tokens·heads/s"
 SCAN_SOURCES = ["ttt_linear_bf16.hip", "ttt_device.h", "ttt_launch.h", "ttt_linear_ops.h"]
 LN_SOURCES = ["ttt_linear_ln.hip", "ttt_device.h", "ttt_launch.h", "ttt_linear_ops.h"]
-MLP_SOURCES = ["ttt_mlp.hip", "ttt_device.h", "ttt_launch.h"]
+MLP_SOURCES = ["ttt_mlp.hip", "ttt_mlp_ops.h", "ttt_device.h", "ttt_launch.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # untimed launches before each extra workload: the cache-flush writes of the
 # headline's cold-start pass leave the clocks low for a few milliseconds
@@ -429,9 +429,10 @@ def training_case(wl, steps, warmup, b=16):
 
 def mlp_training_case(wl, b, steps, warmup):
     """ttt_mlp_fwd_ckpt then ttt_mlp_bwd on one TTT-MLP workload, timed
-    separately; dz is a seeded N(0, 0.01) draw.  The forward is the bf16
-    dual-form scan with checkpoint stores (b | 16), the backward the primal
-    form (fp32 arithmetic, one token at a time)."""
+    separately; dz is a seeded N(0, 0.01) draw.  bf16 inputs: the forward is
+    the dual-form scan with checkpoint stores (b | 16), the backward the
+    dual-form backward at b = 16 and the primal form (fp32 arithmetic, one
+    token at a time) otherwise."""
     import torch
     from test_rnn_layers_head_amd import inputs, ttt_mlp_bwd, ttt_mlp_fwd_ckpt
     x = inputs.make_inputs(wl)
@@ -452,13 +453,15 @@ def mlp_training_case(wl, b, steps, warmup):
     # backward: q, k, v (bf16), eta, dz and the checkpoints in; dq, dk, dv,
     # deta and both initial-state adjoints out
     bb = wl.token_heads * (3 * wl.d * 2 + 4 + wl.d * 4 + 3 * wl.d * 4 + 4) + wl.units * (nmb + 1) * st
+    dual_bwd = wl.qkv_dtype == "bf16" and b == 16
     return {"workload": wl.name, "b": b, "fwd_ckpt_us": kf, "bwd_us": kb,
             "fwd_alg_bytes": fb, "bwd_alg_bytes": bb,
             "fwd_hbm_frac": fb / (kf * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "bwd_hbm_frac": bb / (kb * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "train_token_heads_per_s": wl.token_heads / ((kf + kb) * 1e-6),
             "kernels": ("mlp_scan_kernel with checkpoint stores" if b <= 16 and 16 % b == 0
-                        else "mlp_primal_kernel (checkpoints)") + " / mlp_primal_bwd_kernel"}
+                        else "mlp_primal_kernel (checkpoints)")
+                       + (" / mlp_bwd_kernel (dual form)" if dual_bwd else " / mlp_primal_bwd_kernel")}
 
 
 def ln_training_case(wl, b, steps, warmup):

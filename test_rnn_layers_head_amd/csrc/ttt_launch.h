@@ -155,7 +155,10 @@ struct MlpBwdArgs {
   int T;
   int b;
 };
+// bf16 q/k/v with b = 16: the dual-form backward (one workgroup of 8 waves
+// per unit); otherwise the primal form token by token.
 hipError_t launch_mlp_bwd(const MlpBwdArgs& a, bool f32in, hipStream_t s);
+hipError_t launch_mlp_bwd_primal(const MlpBwdArgs& a, bool f32in, hipStream_t s);
 
 // Backward of the TTT-Linear scan (b = 16, bf16 q/k/v).
 struct LinearBwdArgs {

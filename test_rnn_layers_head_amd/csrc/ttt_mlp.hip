@@ -52,6 +52,7 @@
 // sub-batch of a tile as its own pass with eta masked to that sub-batch.
 #include "ttt_device.h"
 #include "ttt_launch.h"
+#include "ttt_mlp_ops.h"
 
 namespace ttt {
 namespace {
@@ -76,40 +77,6 @@ struct MlpGeom {
   static constexpr int L_TOTAL = L_ST + 3 * 512;
   static constexpr int LOADS = (400 + NW * 64 - 1) / (NW * 64);  // staged chunks per lane
 };
-
-__device__ __forceinline__ int swz_chunk(int r, int p) { return r * 128 + ((p ^ (r & 7)) << 4); }
-__device__ __forceinline__ bf16x8 row_chunk(const char* tile, int r, int h, int g) {
-  return *(const bf16x8*)(tile + swz_chunk(r, 4 * h + g));
-}
-
-struct YOps {
-  bf16x8 hh, l0;
-};
-__device__ __forceinline__ YOps yops(const Split4& y) {
-  const s16x4 z = {0, 0, 0, 0};
-  return YOps{cat44(y.hi, y.hi), cat44(y.lo, z)};
-}
-// acc + X*Y, X as [Xhi | Xlo] of the accumulator layout of X^T (three terms)
-__device__ __forceinline__ f32x4 mm_pre(bf16x8 x, const YOps& y, f32x4 acc) {
-  acc = mfma_k32(x, y.hh, acc);
-  acc = mfma_k32(x, y.l0, acc);
-  return acc;
-}
-// acc + A*B for 8-slot operands split into hi/lo (three terms)
-__device__ __forceinline__ f32x4 mm3(const Split8& a, const Split8& b, f32x4 acc) {
-  acc = mfma_k32(a.hi, b.hi, acc);
-  acc = mfma_k32(a.hi, b.lo, acc);
-  acc = mfma_k32(a.lo, b.hi, acc);
-  return acc;
-}
-__device__ __forceinline__ uint4 pack_split(const Split4& s) {
-  const uint2 h = __builtin_bit_cast(uint2, s.hi), l = __builtin_bit_cast(uint2, s.lo);
-  return make_uint4(h.x, h.y, l.x, l.y);
-}
-__device__ __forceinline__ Split4 unpack_split(uint4 v) {
-  return Split4{__builtin_bit_cast(s16x4, make_uint2(v.x, v.y)),
-                __builtin_bit_cast(s16x4, make_uint2(v.z, v.w))};
-}
 
 // Sum of the NW partial blocks of a cross-wave reduction: the Z of one pass
 // for output block mi (before the LayerNorm of the wrapped variant),

@@ -532,7 +532,7 @@ __global__ void __launch_bounds__(BTHREADS) mlp_primal_bwd_kernel(MlpBwdArgs a) 
 
 }  // namespace
 
-hipError_t launch_mlp_bwd(const MlpBwdArgs& a, bool f32in, hipStream_t s) {
+hipError_t launch_mlp_bwd_primal(const MlpBwdArgs& a, bool f32in, hipStream_t s) {
   if (f32in) return launch(mlp_primal_bwd_kernel<true>, dim3(a.units), dim3(BTHREADS), s, a);
   return launch(mlp_primal_bwd_kernel<false>, dim3(a.units), dim3(BTHREADS), s, a);
 }
