@@ -70,10 +70,6 @@ constexpr int L_W2N = L_ETA + 256;                // [wave][mi][nu][lane] f32x4
 constexpr int L_TOTAL = L_W2N + BWV * 8 * 1024;
 static_assert(L_TOTAL <= 160 * 1024, "LDS budget");
 
-// staged items per lane: 384 K/Q/V chunks, 256 dZ chunks, 16 eta values
-constexpr int NITEM = 384 + 256 + 16;
-constexpr int LOADS = (NITEM + BWV * 64 - 1) / (BWV * 64);
-
 // transpose of an accumulator tile (exact for its hi + lo halves)
 __device__ __forceinline__ f32x4 transpose16(f32x4 x, bf16x8 itr) {
   const Split4 s = split4(x);
@@ -153,59 +149,33 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
   }
 
   // ------------------------------------------------------- input staging
-  // Item q (lane-flat index + 512 * round): q < 128 a K chunk, < 256 a Q
-  // chunk, < 384 a V chunk, < 640 a dZ chunk, < 656 one eta; zero past T.
-  // Every 64-item block lies in one tensor, so descriptors are wave-uniform.
+  // Tile j goes into slot j & 1 by LDS DMA, one 1 KiB block per wave and
+  // instruction: waves 0..5 the two halves of K, Q, V (K, Q with chunk p of
+  // row r at position p ^ (r & 7), set by the source addresses), waves 6, 7
+  // two blocks of dZ each, wave 0 also eta.  Loads past T return zeros.
   const size_t uoff = (size_t)unit * T * 64;
-  __amdgpu_buffer_rsrc_t rsrc[LOADS];
-  int ldst[LOADS];
-  uint32_t gsrc[LOADS], gstep[LOADS];
   const int wu = __builtin_amdgcn_readfirstlane(w);
+  const __amdgpu_buffer_rsrc_t rin =
+      wu < 2 ? make_rsrc((const short*)a.k + uoff, (uint32_t)T * 128)
+             : (wu < 4 ? make_rsrc((const short*)a.q + uoff, (uint32_t)T * 128)
+                       : (wu < 6 ? make_rsrc((const short*)a.v + uoff, (uint32_t)T * 128)
+                                 : make_rsrc(a.dz + uoff, (uint32_t)T * 256)));
+  const __amdgpu_buffer_rsrc_t reta = make_rsrc(a.eta + (size_t)unit * T, (uint32_t)T * 4);
+  auto issue = [&](int j) {
+    char* slot = smem + L_RAW + (j & 1) * RAWB;
+    if (wu < 6) {
+      const int n = wu & 1, r = 8 * n + (lane >> 3), kp = lane & 7;
+      const uint32_t tb = (uint32_t)j * 2048;
+      const uint32_t off = wu < 4 ? tb + r * 128 + ((kp ^ (r & 7)) << 4) : tb + n * 1024 + lane * 16;
+      dma16(rin, slot + (wu >> 1) * 2048 + n * 1024, off);
+    } else {
 #pragma unroll
-  for (int l = 0; l < LOADS; ++l) {
-    const int q0 = wu * 64 + l * BWV * 64, q = q0 + lane;
-    ldst[l] = -1;
-    gsrc[l] = 0;
-    gstep[l] = 2048;
-    rsrc[l] = make_rsrc(a.eta + (size_t)unit * T, (uint32_t)T * 4);
-    if (q0 < 384) {
-      const int part = q0 >> 7, ch = q & 127, r = ch >> 3, p = ch & 7;
-      const void* base = part == 0 ? a.k : (part == 1 ? a.q : a.v);
-      rsrc[l] = make_rsrc((const short*)base + uoff, (uint32_t)T * 128);
-      gsrc[l] = r * 128 + p * 16;
-      ldst[l] = part * 2048 + (part < 2 ? swz_chunk(r, p) : (int)gsrc[l]);
-    } else if (q0 < 640) {
-      const int ch = q - 384, r = ch >> 4, p = ch & 15;
-      rsrc[l] = make_rsrc(a.dz + uoff, (uint32_t)T * 256);
-      gsrc[l] = r * 256 + p * 16;
-      gstep[l] = 4096;
-      ldst[l] = T_DZ + (int)gsrc[l];
-    } else if (q < 656) {
-      gsrc[l] = (q - 640) * 4;
-      gstep[l] = 64;
-      ldst[l] = T_ETA + (q - 640) * 4;
-    }
-  }
-  auto fetch = [&](int j, uint4* v) {
-#pragma unroll
-    for (int l = 0; l < LOADS; ++l) {
-      v[l] = make_uint4(0, 0, 0, 0);
-      if (ldst[l] >= 0 && j >= 0) {
-        const uint32_t off = gsrc[l] + (uint32_t)j * gstep[l];
-        if (gstep[l] == 64) v[l].x = __builtin_amdgcn_raw_buffer_load_b32(rsrc[l], off, 0, 0);
-        else v[l] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc[l], off, 0, 0));
+      for (int n = 0; n < 2; ++n) {
+        const int blk = 2 * (wu - 6) + n;
+        dma16(rin, slot + T_DZ + blk * 1024, (uint32_t)j * 4096 + blk * 1024 + lane * 16);
       }
     }
-  };
-  auto stash = [&](int j, const uint4* v) {
-#pragma unroll
-    for (int l = 0; l < LOADS; ++l) {
-      if (ldst[l] >= 0 && j >= 0) {
-        char* dst = smem + L_RAW + (j & 1) * RAWB + ldst[l];
-        if (gstep[l] == 64) *(uint32_t*)dst = v[l].x;
-        else *(uint4*)dst = v[l];
-      }
-    }
+    if (wu == 0 && lane < 16) dma4(reta, slot + T_ETA, (uint32_t)(j * 16 + lane) * 4);
   };
 
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.dq + uoff, (uint32_t)T * 256);
@@ -223,10 +193,8 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
   auto w2n_at = [&](int mi, int nu) { return (f32x4*)(w2n + (mi * 2 + nu) * 1024); };
   auto part_at = [&](int v, int blk) { return (f32x4*)(smem + L_P + (v * 4 + blk) * 1024 + lane * 16); };
 
-  uint4 pf[LOADS];
-  fetch(ntiles - 1, pf);
-  stash(ntiles - 1, pf);
-  fetch(ntiles - 2, pf);
+  if (ntiles > 0) issue(ntiles - 1);
+  wait_vmcnt<0>();
   wg_barrier();
 
   for (int j = ntiles - 1; j >= 0; --j) {
@@ -236,28 +204,34 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
     const char* Vt = raw + T_V;
     const float* dZt = (const float*)(raw + T_DZ);
     const float* Et = (const float*)(raw + T_ETA);
+    if (j > 0) issue(j - 1);  // into the slot tile j + 1 used
 
     // ------------------------------------------------ checkpoint of tile j
     const size_t co = ((size_t)unit * ntiles + j) * nst;
     const float* w1c = a.w1_ckpt + co;
     const float* w2c = a.w2_ckpt + co;
-    f32x4 W1[2][4], W2T[2][4];
+    // W2 with u on the rows, block (nu, mi), and W1 with u on the rows and
+    // columns sigma(m, c), block (nu, m): read where they are used
+    auto w2t = [&](int nu, int mi) { return *(const f32x4*)(w2c + (16 * mi + c) * BHID + u0 + 16 * nu + 4 * g); };
+    auto w2t_op = [&](int mi) { return split8_mfma(w2t(0, mi), w2t(1, mi), ns); };
+    auto w1t_op = [&](int m) {
+      f32x4 x0, x1;
 #pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        W1[n][m] = *(const f32x4*)(w1c + (u0 + 16 * n + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1));
-        W2T[n][m] = *(const f32x4*)(w2c + (16 * m + c) * BHID + u0 + 16 * n + 4 * g);
+      for (int r = 0; r < 4; ++r) {
+        x0[r] = w1c[(u0 + 4 * g + r) * 64 + sigc(m)];
+        x1[r] = w1c[(u0 + 16 + 4 * g + r) * 64 + sigc(m)];
       }
+      return split8_mfma(x0, x1, ns);
+    };
+    auto w1blk = [&](int n, int m) {
+      return *(const f32x4*)(w1c + (u0 + 16 * n + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1));
+    };
+    // W2N = the transposes of the W2^T blocks (their hi + lo halves, which
+    // split again into the same halves as W2 itself)
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int nu = 0; nu < 2; ++nu) {
-        f32x4 x;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = w2c[(16 * mi + 4 * g + r) * BHID + u0 + 16 * nu + c];
-        *w2n_at(mi, nu) = x;  // read back only by this wave
-      }
+      for (int nu = 0; nu < 2; ++nu) *w2n_at(mi, nu) = transpose16(w2t(nu, mi), itr);  // this wave only
     auto w2n_op = [&](int kb, int nu) { return split8_mfma(*w2n_at(2 * kb, nu), *w2n_at(2 * kb + 1, nu), ns); };
 
     // ------------------------------------------- per-tile K, Q operands
@@ -293,7 +267,7 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
       f32x4 X2t[2], D2[2];
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
-        const Split8 s0 = split8_mfma(W1[n][0], W1[n][1], ns), s1 = split8_mfma(W1[n][2], W1[n][3], ns);
+        const Split8 s0 = split8_mfma(w1blk(n, 0), w1blk(n, 1), ns), s1 = split8_mfma(w1blk(n, 2), w1blk(n, 3), ns);
         f32x4 z = {0, 0, 0, 0}, zq = {0, 0, 0, 0};
         z = mfma_k32(kop[0], s0.hi, z);
         z = mfma_k32(kop[0], s0.lo, z);
@@ -320,7 +294,7 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
     // Y partial over this wave's units: [t][i] per block mi
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
-      *part_at(w, mi) = mm3(x2o, split8_mfma(W2T[0][mi], W2T[1][mi], ns), f32x4{0, 0, 0, 0});
+      *part_at(w, mi) = mm3(x2o, w2t_op(mi), f32x4{0, 0, 0, 0});
     wg_barrier();  // B1: Y partials
 
     // ================================== E, Gn2 (block mi = w)
@@ -436,7 +410,7 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
       }
     }
     // Snb = Gn1b * P1, Z1b (part) = Gn1b * Sn * P2
-    Split8 g1o, z1qbo;
+    Split8 g1o;
     {
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
@@ -449,7 +423,7 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
         snbs[n] = split4(snb);
       }
       g1o = u_operand(g1s[0], g1s[1], itr, ns);
-      z1qbo = u_operand(z1qbs[0], z1qbs[1], itr, ns);
+      const Split8 z1qbo = u_operand(z1qbs[0], z1qbs[1], itr, ns);
       const Split8 snbo = u_operand(snbs[0], snbs[1], itr, ns);
       // Ab partial: [s][t] = sum_u Gn1[u][s] Z1qb[u][t]
       *(f32x4*)(smem + L_SA + w * 1024 + lane * 16) = mm3(g1o, z1qbo, f32x4{0, 0, 0, 0});
@@ -457,7 +431,7 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
         f32x4 acc = mm3(x2o, split8_mfma(A2[0][mi], A2[1][mi], ns), f32x4{0, 0, 0, 0});
-        *part_at(w, mi) = mm3(snbo, split8_mfma(W2T[0][mi], W2T[1][mi], ns), acc);
+        *part_at(w, mi) = mm3(snbo, w2t_op(mi), acc);
       }
     }
     wg_barrier();  // B3: Gn2b, B2^T and Ab partials
@@ -512,19 +486,14 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
       Split8 ga[2], yba[2];
       load_ga(L_G2B, ga);
       load_ga(L_YBB, yba);
-      // A2 with i on the rows (W2N layout), from the resident W2^T layout
-      f32x4 A2N[4][2];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int nu = 0; nu < 2; ++nu) A2N[mi][nu] = transpose16(A2[nu][mi], itr);
       Split4 z1bs[2];
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
         f32x4 acc = mm_pre(mbtop, yops(x2qs[n]), f32x4{0, 0, 0, 0});  // X2q Mb^T
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          acc = mm3(ga[kb], split8_mfma(A2N[2 * kb][n], A2N[2 * kb + 1][n], ns), acc);
+          // A2 with i on the rows (the W2N layout), transposed from the resident layout
+          acc = mm3(ga[kb], split8_mfma(transpose16(A2[n][2 * kb], itr), transpose16(A2[n][2 * kb + 1], itr), ns), acc);
           acc = mm3(yba[kb], w2n_op(kb, n), acc);
         }
         f32x4 z1b;
@@ -534,16 +503,11 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
       }
       z1bo = u_operand(z1bs[0], z1bs[1], itr, ns);
       // dQ partial: [t][sigma(m, c)] = sum_u Z1qb^T[t][u] W1[u][sigma]
-      f32x4 W1T[2][4];
-      const float* w1c2 = a.w1_ckpt + co;
+      {
+        const Split8 z1qbo = u_operand(z1qbs[0], z1qbs[1], itr, ns);
 #pragma unroll
-      for (int nu = 0; nu < 2; ++nu)
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) W1T[nu][m][r] = w1c2[(u0 + 16 * nu + 4 * g + r) * 64 + sigc(m)];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) *part_at(w, m) = mm3(z1qbo, split8_mfma(W1T[0][m], W1T[1][m], ns), f32x4{0, 0, 0, 0});
+        for (int m = 0; m < 4; ++m) *part_at(w, m) = mm3(z1qbo, w1t_op(m), f32x4{0, 0, 0, 0});
+      }
       wg_barrier();  // B5: dQ partials
       if (w < 4) {
         const int m = w;
@@ -560,7 +524,7 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
       for (int m = 0; m < 4; ++m) {
         const f32x4 a1t0 = transpose16(A1[0][m], itr), a1t1 = transpose16(A1[1][m], itr);
         f32x4 acc = mm3(g1o, split8_mfma(a1t0, a1t1, ns), f32x4{0, 0, 0, 0});
-        *part_at(w, m) = mm3(z1bo, split8_mfma(W1T[0][m], W1T[1][m], ns), acc);
+        *part_at(w, m) = mm3(z1bo, w1t_op(m), acc);
       }
       wg_barrier();  // B7: dK partials
       if (w < 4) {
@@ -576,8 +540,8 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
       // A1 += Z1qb Q^T + Z1b K^T (accumulator [sigma][u])
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const f32x4 xq = mfma_k32(qop[m >> 1], sel[m & 1], f32x4{0, 0, 0, 0});  // Q[t][sigma(m, c)]
-        const f32x4 xk = mfma_k32(kop[m >> 1], sel[m & 1], f32x4{0, 0, 0, 0});
+        const f32x4 xq = mfma_k32(row_chunk(Qt, c, m >> 1, g), sel[m & 1], f32x4{0, 0, 0, 0});  // Q[t][sigma(m, c)]
+        const f32x4 xk = mfma_k32(row_chunk(Kt, c, m >> 1, g), sel[m & 1], f32x4{0, 0, 0, 0});
         const uint32_t q0 = pack_rne(xq[0], xq[1]), q1 = pack_rne(xq[2], xq[3]);
         const uint32_t k0 = pack_rne(xk[0], xk[1]), k1 = pack_rne(xk[2], xk[3]);
         const bf16x8 qt2 = __builtin_bit_cast(bf16x8, make_uint4(q0, q1, q0, q1));
@@ -605,9 +569,8 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
       }
     }
 
-    if (j > 0) stash(j - 1, pf);  // next tile's inputs into the other slot
-    wg_barrier();                 // B0: the next tile's inputs; partial areas free
-    fetch(j - 2, pf);
+    wait_vmcnt<0>();  // the next tile's inputs have landed
+    wg_barrier();     // B0: the next tile's inputs; partial areas free
   }
 
   // the adjoint of the initial state
