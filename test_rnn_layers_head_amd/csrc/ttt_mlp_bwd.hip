@@ -214,17 +214,13 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
     // columns sigma(m, c), block (nu, m): read where they are used
     auto w2t = [&](int nu, int mi) { return *(const f32x4*)(w2c + (16 * mi + c) * BHID + u0 + 16 * nu + 4 * g); };
     auto w2t_op = [&](int mi) { return split8_mfma(w2t(0, mi), w2t(1, mi), ns); };
-    auto w1t_op = [&](int m) {
-      f32x4 x0, x1;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        x0[r] = w1c[(u0 + 4 * g + r) * 64 + sigc(m)];
-        x1[r] = w1c[(u0 + 16 + 4 * g + r) * 64 + sigc(m)];
-      }
-      return split8_mfma(x0, x1, ns);
-    };
+    // W1^T block (nu, m) = the transpose of W1's block (nu, m): rows u, columns
+    // sigma(m, c) - the hi + lo halves of W1, which split again into the same halves
     auto w1blk = [&](int n, int m) {
       return *(const f32x4*)(w1c + (u0 + 16 * n + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1));
+    };
+    auto w1t_op = [&](int m) {
+      return split8_mfma(transpose16(w1blk(0, m), itr), transpose16(w1blk(1, m), itr), ns);
     };
     // W2N = the transposes of the W2^T blocks (their hi + lo halves, which
     // split again into the same halves as W2 itself)
@@ -402,10 +398,11 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
         // Gn1b^T[s][u] = sum_i K[s][i] A1[u][i] + sum_t Am[s][t] Z1qb^T[t][u]
         const Split8 s0 = split8_mfma(A1[n][0], A1[n][1], ns), s1 = split8_mfma(A1[n][2], A1[n][3], ns);
         f32x4 gb = {0, 0, 0, 0};
-        gb = mfma_k32(kop[0], s0.hi, gb);
-        gb = mfma_k32(kop[0], s0.lo, gb);
-        gb = mfma_k32(kop[1], s1.hi, gb);
-        gb = mfma_k32(kop[1], s1.lo, gb);
+        const bf16x8 k0 = row_chunk(Kt, c, 0, g), k1 = row_chunk(Kt, c, 1, g);  // re-read
+        gb = mfma_k32(k0, s0.hi, gb);
+        gb = mfma_k32(k0, s0.lo, gb);
+        gb = mfma_k32(k1, s1.hi, gb);
+        gb = mfma_k32(k1, s1.lo, gb);
         Gn1b[n] = mm_pre(aTop, yops(z1qbs[n]), gb);
       }
     }
