@@ -361,13 +361,17 @@ ttt_status_t ttt_linear_ln_bwd(const void* q, const void* k, const void* v,
  * and writing (fp32)
  *   dq, dk, dv : [B][H][T][d];  deta : [B][H][T]
  *   dw1_0, dw2_0 : [B][H][hidden][d], [B][H][d][hidden], per unit.
- * The mini-batches are walked in reverse.  Each is replayed forward from its
- * checkpoint, then its tokens are taken back one by one; both passes run in
- * fp32.  The gradient-point adjoints of a mini-batch join the state adjoints
- * at its first token.  Outputs must not overlap each other or an input.
- * T = 0 writes dw*_0 = dw*_T (or zeros).  One workgroup of 512 threads per
- * (batch, head).  Besides the outputs, the kernel uses only its own LDS and
- * the per-thread register spill space the compiler assigns.
+ * The mini-batches are walked in reverse, each from its checkpoint.  bf16
+ * q/k/v with b = 16 run the dual form: the mini-batch's forward is recomputed
+ * on MFMA and every product taken back in reverse (the adjoints of W1, W2
+ * resident in registers; fp32 factors as bf16 hi + lo halves, ~2^-16
+ * relative per product).  Other cases replay the mini-batch forward and take
+ * its tokens back one by one in fp32, the gradient-point adjoints joining
+ * the state adjoints at its first token.  Outputs must not overlap each
+ * other or an input.  T = 0 writes dw*_0 = dw*_T (or zeros).  One workgroup
+ * of 512 threads per (batch, head).  Besides the outputs, the kernels use
+ * only their own LDS and the per-thread register spill space the compiler
+ * assigns.
  */
 ttt_status_t ttt_mlp_fwd_ckpt(const void* q, const void* k, const void* v,
                               const float* eta, const float* w1_0,

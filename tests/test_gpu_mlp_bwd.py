@@ -3,10 +3,11 @@ the scan (through the C ABI) against the fp64 oracle ("论文速览 | TTT" §6.1
 
 Tolerance: for fp32 inputs the fp32 bound (rel-L2 <= 1e-5) on every
 gradient; for bf16 inputs the bf16-input bound of the forward (rel-L2 <= 2e-3,
-max|diff| / RMS <= 1e-2), as for the TTT-Linear backward.  The backward runs
-in fp32 arithmetic; for bf16 q/k/v with b | 16 its checkpoints come from the
-bf16 dual-form forward (~2^-16 relative per product), for fp32 from the
-primal fp32 kernel.  The errors are printed.
+max|diff| / RMS <= 1e-2), as for the TTT-Linear backward.  bf16 q/k/v with
+b = 16 run the dual-form backward (bf16 MFMA on hi + lo splits, ~2^-16
+relative per product); other cases the primal backward in fp32 arithmetic.
+For bf16 q/k/v with b | 16 the checkpoints come from the bf16 dual-form
+forward, for fp32 from the primal fp32 kernel.  The errors are printed.
 """
 import numpy as np
 import pytest
