@@ -45,6 +45,11 @@ UNIT = "tokens·heads/s"
 SCAN_SOURCES = ["ttt_linear_bf16.hip", "ttt_device.h", "ttt_launch.h", "ttt_linear_ops.h"]
 LN_SOURCES = ["ttt_linear_ln.hip", "ttt_device.h", "ttt_launch.h", "ttt_linear_ops.h"]
 MLP_SOURCES = ["ttt_mlp.hip", "ttt_mlp_ops.h", "ttt_device.h", "ttt_launch.h"]
+MLP_BWD_SOURCES = ["ttt_mlp_bwd.hip", "ttt_mlp_ops.h", "ttt_device.h", "ttt_launch.h"]
+# kernel names as rocprofv3 reports them (template arguments: waves,
+# sub-batches, checkpoint stores, LayerNorm wrapper)
+MLP_SCAN_NAME = "mlp_scan_kernel<8, false, false, false>"
+MLP_LN_SCAN_NAME = "mlp_scan_kernel<8, false, false, true>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # untimed launches before each extra workload: the cache-flush writes of the
 # headline's cold-start pass leave the clocks low for a few milliseconds
@@ -87,6 +92,19 @@ def mlp_alg_bytes(wl) -> int:
     per_tok = 3 * wl.d * es + 4 + wl.d * 4
     st = 2 * wl.hidden * wl.d * 4
     return wl.token_heads * per_tok + wl.H * st + wl.units * st
+
+
+def mlp_ln_alg_bytes(wl) -> int:
+    """The plain MLP scan's bytes plus the LayerNorm scale and shift of each head."""
+    return mlp_alg_bytes(wl) + wl.H * wl.d * 2 * 4
+
+
+def mlp_bwd_alg_bytes(wl, b=16) -> int:
+    """TTT-MLP backward: q, k, v (bf16), eta, dz and the checkpoints in; dq,
+    dk, dv, deta and both initial-state adjoints out."""
+    nmb = (wl.T + b - 1) // b
+    st = 2 * wl.hidden * wl.d * 4
+    return wl.token_heads * (3 * wl.d * 2 + 4 + wl.d * 4 + 3 * wl.d * 4 + 4) + wl.units * (nmb + 1) * st
 
 
 def mlp_alg_flops(wl, b) -> int:
@@ -450,15 +468,15 @@ def mlp_training_case(wl, b, steps, warmup):
     nmb = (wl.T + b - 1) // b
     st = 2 * wl.hidden * wl.d * 4
     fb = mlp_alg_bytes(wl) + wl.units * nmb * st
-    # backward: q, k, v (bf16), eta, dz and the checkpoints in; dq, dk, dv,
-    # deta and both initial-state adjoints out
-    bb = wl.token_heads * (3 * wl.d * 2 + 4 + wl.d * 4 + 3 * wl.d * 4 + 4) + wl.units * (nmb + 1) * st
+    bb = mlp_bwd_alg_bytes(wl, b)
     dual_bwd = wl.qkv_dtype == "bf16" and b == 16
     return {"workload": wl.name, "b": b, "fwd_ckpt_us": kf, "bwd_us": kb,
             "fwd_alg_bytes": fb, "bwd_alg_bytes": bb,
             "fwd_hbm_frac": fb / (kf * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "bwd_hbm_frac": bb / (kb * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "train_token_heads_per_s": wl.token_heads / ((kf + kb) * 1e-6),
+            **({"bwd_traffic": traffic_for("mlp_bwd", MLP_BWD_SOURCES, wl.name),
+                "bwd_sq": sq_for("mlp_bwd", MLP_BWD_SOURCES)} if dual_bwd else {}),
             "kernels": ("mlp_scan_kernel with checkpoint stores" if b <= 16 and 16 % b == 0
                         else "mlp_primal_kernel (checkpoints)")
                        + (" / mlp_bwd_kernel (dual form)" if dual_bwd else " / mlp_primal_bwd_kernel")}
@@ -509,15 +527,18 @@ def mlp_ln_case(wl, b, steps, warmup):
     launch = lambda: ttt_mlp_ln_fwd(d["q"], d["k"], d["v"], d["eta"], d["w1"], d["w2"], gam, bet,
                                     wl.ln_eps, b)
     wall, kmean, spread = time_launches(launch, steps, warmup)
-    byts = mlp_alg_bytes(wl) + wl.H * wl.d * 2 * 4
+    byts = mlp_ln_alg_bytes(wl)
     flops = mlp_alg_flops(wl, b)
+    dual = wl.qkv_dtype == "bf16" and b <= 16 and 16 % b == 0
     return {"workload": wl.name, "b": b, "token_heads_per_s": wl.token_heads / (wall * 1e-3),
             "kernel_us_mean": kmean, "kernel_us_median": spread["median"],
             "alg_bytes": byts, "alg_flops": flops,
             "hbm_frac_algorithmic": byts / (kmean * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "mfma_frac_algorithmic": flops / (kmean * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+            **({"traffic": traffic_for("mlp_ln_scan", MLP_SOURCES, wl.name),
+                "sq": sq_for("mlp_ln_scan", MLP_SOURCES)} if dual and b == 16 else {}),
             "kernel": ("mlp_scan_kernel with the LayerNorm wrapper (dual form)"
-                       if wl.qkv_dtype == "bf16" and b <= 16 and 16 % b == 0 else
+                       if dual else
                        "mlp_primal_kernel with the LayerNorm wrapper (fp32, one token at a time)")}
 
 
@@ -706,7 +727,9 @@ def summarize_pmc(fetch_dir, write_dir):
           "counter reads for it).\n")
     cases = (("linear_scan", "linear_scan_bf16_kernel", SCAN_SOURCES, linear_alg_bytes, 3),
              ("linear_ln_scan", "linear_ln_scan_kernel", LN_SOURCES, ln_alg_bytes, 6),
-             ("mlp_scan", "mlp_scan_kernel", MLP_SOURCES, mlp_alg_bytes, 4))
+             ("mlp_scan", MLP_SCAN_NAME, MLP_SOURCES, mlp_alg_bytes, 4),
+             ("mlp_ln_scan", MLP_LN_SCAN_NAME, MLP_SOURCES, mlp_ln_alg_bytes, 10),
+             ("mlp_bwd", "mlp_bwd_kernel", MLP_BWD_SOURCES, mlp_bwd_alg_bytes, 4))
     for key, pat, srcs, alg_fn, wid in cases:
         names = [k for k in fetch if pat in k]
         if not names:
@@ -763,7 +786,9 @@ def sq_derive(med, active_cus):
 
 SQ_CASES = (("linear_scan", "linear_scan_bf16_kernel", "SCAN_SOURCES", 256),   # 2 workgroups x 128 units
             ("linear_ln_scan", "linear_ln_scan_kernel", "LN_SOURCES", 128),   # 128 units
-            ("mlp_scan", "mlp_scan_kernel", "MLP_SOURCES", 96))               # 96 units
+            ("mlp_scan", MLP_SCAN_NAME, "MLP_SOURCES", 96),                     # 96 units
+            ("mlp_ln_scan", MLP_LN_SCAN_NAME, "MLP_SOURCES", 96),
+            ("mlp_bwd", "mlp_bwd_kernel", "MLP_BWD_SOURCES", 96))
 
 
 def summarize_sq(sq_dir):
@@ -950,6 +975,11 @@ def main():
         w6 = inputs.workload(6)
         log(f"[bench] {w6.name} (counter coverage of the LayerNorm scan)")
         ln_case(w6, 16, 2, 1)
+        w10 = inputs.workload(10)
+        log(f"[bench] {w10.name} (counter coverage of the MLP scan with the LayerNorm wrapper)")
+        mlp_ln_case(w10, 16, 2, 1)
+        log(f"[bench] {w4.name} training (counter coverage of the MLP backward)")
+        mlp_training_case(w4, 16, 2, 1)
 
     extras = {}
     if not args.no_extras:
@@ -993,10 +1023,10 @@ def main():
         log(f"[bench] {w4.name} with b = 64 (the primal kernel)")
         extras[f"{w4.name}_b64"] = mlp_case(w4, 64, 3, 2)
         log(f"[bench] forward with checkpoints + backward, {w4.name}")
-        extras[f"train-{w4.name}"] = mlp_training_case(w4, 16, 3, 2)
+        extras[f"train-{w4.name}"] = mlp_training_case(w4, 16, 5, 2)
         w10 = inputs.workload(10)
         log(f"[bench] {w10.name} (MLP with the LayerNorm wrapper)")
-        extras[w10.name] = mlp_ln_case(w10, 16, 3, 2)
+        extras[w10.name] = mlp_ln_case(w10, 16, max(5, args.steps // 2), EXTRA_WARMUP)
         log("[bench] streaming copy reference")
         extras["stream_copy_GBps"] = stream_copy_GBps()
         extras["headline_frac_of_stream_copy"] = head["hbm_GBps"] / extras["stream_copy_GBps"]
