@@ -27,7 +27,8 @@
 // the whole sequence.  Products over the hidden units (Y, the Gn2 adjoint,
 // dQ, dK, B2, Ab) leave per-wave partials in LDS that the first four waves
 // (one 16-column block of d each) or every wave (16 x 16) sum in a fixed
-// order.  Tokens sit on the accumulator rows ("transposed" tiles, X^T[t][.]).
+// order; dK's partials reuse each wave's W2N area once its last read of the
+// tile is done.  Tokens sit on the accumulator rows ("transposed" tiles, X^T[t][.]).
 //
 // Layouts per wave (lane c + 16 g, register r; u0 = 32 w):
 //   W1, A1   [n][m]: [u0 + 16 n + c][sigma(m, 4g + r)], sigma(m, 4g + r) =
@@ -192,6 +193,8 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
   char* const w2n = smem + L_W2N + w * 8192 + lane * 16;
   auto w2n_at = [&](int mi, int nu) { return (f32x4*)(w2n + (mi * 2 + nu) * 1024); };
   auto part_at = [&](int v, int blk) { return (f32x4*)(smem + L_P + (v * 4 + blk) * 1024 + lane * 16); };
+  // dK partials of wave v, block m: the first 4 KiB of the wave's W2N area
+  auto dk_at = [&](int v, int m) { return (f32x4*)(smem + L_W2N + v * 8192 + m * 1024 + lane * 16); };
 
   if (ntiles > 0) issue(ntiles - 1);
   wait_vmcnt<0>();
@@ -505,33 +508,30 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) *part_at(w, m) = mm3(z1qbo, w1t_op(m), f32x4{0, 0, 0, 0});
       }
-      wg_barrier();  // B5: dQ partials
-      if (w < 4) {
-        const int m = w;
-        f32x4 dq = {0, 0, 0, 0};
-#pragma unroll
-        for (int v = 0; v < BWV; ++v) dq += *part_at(v, m);
-        const Split4 abs_ = split4(Ab);
-        dq = mfma_k32(cat44(abs_.hi, abs_.lo), rows_twice(Kt, g, sigc(m)), dq);  // + K Ab
-        if (16 * j + 4 * g < T) store_tile(rq, j, sigc(m), dq);
-      }
-      wg_barrier();  // B6: dQ partials read
-      // dK partial: [s][sigma] = sum_u Gn1^T[s][u] A1[u][sigma] + Z1b^T[s][u] W1[u][sigma]
+      // dK partial: [s][sigma] = sum_u Gn1^T[s][u] A1[u][sigma] + Z1b^T[s][u] W1[u][sigma],
+      // into this wave's W2N area (its last read was X2b above)
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const f32x4 a1t0 = transpose16(A1[0][m], itr), a1t1 = transpose16(A1[1][m], itr);
         f32x4 acc = mm3(g1o, split8_mfma(a1t0, a1t1, ns), f32x4{0, 0, 0, 0});
-        *part_at(w, m) = mm3(z1bo, w1t_op(m), acc);
+        *dk_at(w, m) = mm3(z1bo, w1t_op(m), acc);
       }
-      wg_barrier();  // B7: dK partials
+      wg_barrier();  // B5: dQ and dK partials
       if (w < 4) {
         const int m = w;
-        f32x4 dk = {0, 0, 0, 0};
+        f32x4 dq = {0, 0, 0, 0}, dk = {0, 0, 0, 0};
 #pragma unroll
-        for (int v = 0; v < BWV; ++v) dk += *part_at(v, m);
-        const Split4 abts = split4(AbT);
+        for (int v = 0; v < BWV; ++v) {
+          dq += *part_at(v, m);
+          dk += *dk_at(v, m);
+        }
+        const Split4 abs_ = split4(Ab), abts = split4(AbT);
+        dq = mfma_k32(cat44(abs_.hi, abs_.lo), rows_twice(Kt, g, sigc(m)), dq);   // + K Ab
         dk = mfma_k32(cat44(abts.hi, abts.lo), rows_twice(Qt, g, sigc(m)), dk);  // + Q Ab^T
-        if (16 * j + 4 * g < T) store_tile(rk, j, sigc(m), dk);
+        if (16 * j + 4 * g < T) {
+          store_tile(rq, j, sigc(m), dq);
+          store_tile(rk, j, sigc(m), dk);
+        }
       }
       // ============================== adjoint updates
       // A1 += Z1qb Q^T + Z1b K^T (accumulator [sigma][u])
