@@ -316,13 +316,16 @@ ttt_status_t ttt_mlp_fwd(const void* q, const void* k, const void* v,
  * writing (fp32) dq, dk, dv [B][H][T][d], deta [B][H][T], dw0 [B][H][d][d]
  * and the LayerNorm parameters' adjoints dgamma, dbeta [B][H][d], per unit
  * (sum over the batch for the shared per-head parameters).
- * Both run the primal form token by token in fp32 arithmetic, one workgroup
- * of 256 threads per (batch, head).  The backward replays each mini-batch
- * from its checkpoint, then takes its tokens back; it applies the adjoint of
- * every forward operation (the LayerNorm statistics, the LayerNorm VJP of
- * the inner gradient, the update, the output) in reverse order.  Outputs
- * must not overlap each other or an input; T = 0 writes dw0 = dw_T (or
- * zeros) and zero dgamma, dbeta.
+ * ttt_linear_ln_fwd_ckpt runs the kernel ttt_linear_ln_fwd picks (the
+ * dual-form scan for bf16 q/k/v with 16 | b, else the primal form), which
+ * also stores each mini-batch's starting state; z and w_out equal
+ * ttt_linear_ln_fwd's bit for bit.  The backward runs the primal form token
+ * by token in fp32 arithmetic, one workgroup of 256 threads per (batch,
+ * head): it replays each mini-batch from its checkpoint, then takes its
+ * tokens back, applying the adjoint of every forward operation (the
+ * LayerNorm statistics, the LayerNorm VJP of the inner gradient, the update,
+ * the output) in reverse order.  Outputs must not overlap each other or an
+ * input; T = 0 writes dw0 = dw_T (or zeros) and zero dgamma, dbeta.
  */
 ttt_status_t ttt_linear_ln_fwd_ckpt(const void* q, const void* k, const void* v,
                                    const float* eta, const float* w0,

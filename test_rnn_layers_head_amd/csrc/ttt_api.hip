@@ -199,7 +199,8 @@ ttt_status_t linear_ln_impl(const void* q, const void* k, const void* v, const f
   if (units == 0) return TTT_OK;
   // bf16 with 16 | b and no checkpoints: the dual-form kernel; otherwise the
   // primal-form kernel
-  const bool primal = dt != TTT_BF16 || b % 16 != 0 || w_ckpt != nullptr;
+  // bf16 with 16 | b: the dual-form scan (with checkpoint stores when asked)
+  const bool primal = dt != TTT_BF16 || b % 16 != 0;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (T == 0) {

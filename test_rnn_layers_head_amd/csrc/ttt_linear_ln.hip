@@ -170,8 +170,10 @@ __device__ __forceinline__ f32x4 bf4(uint2 u) {
 }
 
 // TPM: tiles per mini-batch when fixed at compile time (b = 16, 32, 64),
-// 0 = read from the arguments (other multiples of 16).
-template <int TPM>
+// 0 = read from the arguments (other multiples of 16).  CKPT: also store
+// the state before every mini-batch (the checkpoints the backward reads),
+// straight from the compute waves' accumulators.
+template <int TPM, bool CKPT = false>
 __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearLnArgs la) {
   using G = LnGeom;
   const LinearArgs& a = la.s;
@@ -381,6 +383,7 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
   for (int i = 0; i < 64; ++i) G2 = fmaf(gm[i], gm[i], G2);
   const float eps = la.eps;
   const int tpm = TPM > 0 ? TPM : (a.b >> 4);  // tiles per mini-batch
+  const int nmb = (T + a.b - 1) / a.b;           // mini-batches (checkpoints)
 
   const NegSel ns = make_negsel(c, g);
   // one-hot selections that carry the hi (slots 0..3) or lo (4..7) half of a
@@ -522,6 +525,14 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
     const f32x4 gu2n = *(const f32x4*)(pj1 + G::P_GU + wblk + lane16);
     const bf16x8 k1[2] = {k1a, k1b}, q0[2] = {q0a, q0b};
 
+    if constexpr (CKPT) {  // W_j is the state before mini-batch j / tpm
+      if (new_mb) {
+        float* ck = a.w_ckpt + ((size_t)unit * nmb + j / tpm) * 4096;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          *(f32x4*)(ck + (rbase + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1)) = W[m];
+      }
+    }
     // ---- products with W_j that do not wait for the gradient: its split,
     // W_j K_{j+1} (or the gradient point's), W_j Q_j
     const Split8x3 ws[2] = {split8x3(W[0], W[1], ns), split8x3(W[2], W[3], ns)};
@@ -658,6 +669,14 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
 
 hipError_t launch_linear_ln(const LinearLnArgs& a, hipStream_t s) {
   const dim3 grid(a.s.units), block(LnGeom::THREADS);
+  if (a.s.w_ckpt) {
+    switch (a.s.b) {
+      case 16: return launch(linear_ln_scan_kernel<1, true>, grid, block, s, a);
+      case 32: return launch(linear_ln_scan_kernel<2, true>, grid, block, s, a);
+      case 64: return launch(linear_ln_scan_kernel<4, true>, grid, block, s, a);
+      default: return launch(linear_ln_scan_kernel<0, true>, grid, block, s, a);
+    }
+  }
   switch (a.s.b) {
     case 16: return launch(linear_ln_scan_kernel<1>, grid, block, s, a);
     case 32: return launch(linear_ln_scan_kernel<2>, grid, block, s, a);

@@ -1,6 +1,8 @@
 """TTT-Linear with the LayerNorm + residual inner model: the primal-form
-forward (b < 16, fp32 q/k/v, checkpoints) and the backward through the scan,
-through the C ABI, against the fp64 oracle ("论文速览 | TTT" §4.4, §6.12).
+forward (b < 16, fp32 q/k/v), the forward with checkpoints (the dual-form
+scan with checkpoint stores for bf16 with 16 | b, else the primal form) and
+the backward through the scan, through the C ABI, against the fp64 oracle
+("论文速览 | TTT" §4.4, §6.12).
 
 Tolerance: these kernels run in fp32 arithmetic with exact products, so up to
 a few hundred tokens the LayerNorm forward bound (rel-L2 <= 1e-4, max|diff| /
@@ -8,7 +10,8 @@ RMS <= 1e-3) applies to outputs, checkpoints and every gradient.  Over the
 2k-token workload the LayerNorm recurrence amplifies rounding in the adjoint
 as it does in the forward: float32 autodiff of the dual form
 (``fp32_floor``, computed in the test) reaches max|diff| / RMS = 1.04e-2 on dv
-against the fp64 oracle (the kernel: 1.10e-2).  The bound there is rel-L2 <= 2e-3 and max|diff| /
+against the fp64 oracle (the kernel, from the dual-form forward's
+checkpoints: 1.39e-2).  The bound there is rel-L2 <= 2e-3 and max|diff| /
 RMS <= max(1e-2, 1.5 x that floor), gradient by gradient.
 """
 import numpy as np
@@ -81,6 +84,22 @@ def test_backward_parity(with_dwT, dtype, b, T):
     got = [t.cpu().numpy() for t in g]
     out = {name: close(a, r, f"T={T} b={b} {name}")["rel_l2"] for name, a, r in zip(NAMES, got, ref)}
     print(f"{dtype} T={T} b={b} dW_T={with_dwT}:", out)
+
+
+@pytest.mark.parametrize("b", [16, 32, 64])
+def test_forward_with_checkpoints_matches_plain_forward(b):
+    """bf16 with 16 | b: ttt_linear_ln_fwd_ckpt runs the dual-form scan of
+    ttt_linear_ln_fwd with checkpoint stores added, so z and the final state
+    are bit-identical, and checkpoint 0 is W0 itself."""
+    x = case(1, 3, 100, "bf16", seed=930 + b)
+    (q, k, v), eta, w0, gam, bet = dev_all(x)
+    eps = x.wl.ln_eps
+    z0, w1 = ttt_linear_ln_fwd(q, k, v, eta, w0, gam, bet, eps, b)
+    z, w, ck = ttt_linear_ln_fwd_ckpt(q, k, v, eta, w0, gam, bet, eps, b)
+    torch.cuda.synchronize()
+    assert torch.equal(z0, z) and torch.equal(w1, w)
+    assert ck.shape[2] == (100 + b - 1) // b
+    assert np.array_equal(ck[:, :, 0].cpu().numpy(), np.broadcast_to(x.w0, (1, 3, 64, 64)))
 
 
 def fp32_floor(x, dz, b=16):
