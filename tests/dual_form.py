@@ -306,6 +306,93 @@ def mlp_bwd_unit(q, k, v, eta, w1, w2, b, dz, dw1T=None, dw2T=None):
     return dq, dk, dv, deta, W1b, W2b
 
 
+def _ln_hat_adjoint(C, rs, Hb, rsb0=0.0):
+    """Adjoint of Yh = C rs, C = Y - mean Y, rs = (mean C^2 + eps)^-1/2 per
+    column, given Yh's adjoint Hb (and an extra adjoint rsb0 of rs): Y's."""
+    d = C.shape[0]
+    rsb = rsb0 + np.sum(C * Hb, axis=0)
+    varb = -0.5 * rs ** 3 * rsb
+    Cb = rs[None, :] * Hb + (2.0 / d) * C * varb[None, :]
+    return Cb - Cb.mean(axis=0)
+
+
+def linear_ln_bwd_unit(q, k, v, eta, w0, gamma, beta, eps, b, dz, dwT=None):
+    """Adjoint of linear_ln_unit, one unit, mini-batch by mini-batch in
+    reverse, every product of the dual form taken back (columns are tokens,
+    D = diag eta, A = triu(K^T Q)):
+      Y = W K, Yh = LNhat(Y), R = K + gamma Yh + beta - V, Gh = 2 gamma R,
+      P = Gh - mean Gh - Yh mean(Gh Yh), GY = rs P, G = GY D,
+      Zp = W Q - G A, Z = Q + gamma LNhat(Zp) + beta, W' = W - G K^T.
+    Returns (dq, dk, dv, deta, dw0, dgamma, dbeta)."""
+    T, d = q.shape
+    gc, bc = gamma[:, None], beta[:, None]
+    Ws = [np.array(w0, dtype=np.float64)]
+    blocks = list(range(0, T, b))
+    for m0 in blocks:
+        m1 = min(T, m0 + b)
+        XK, XV = k[m0:m1].T, v[m0:m1].T
+        Yh, rs = _ln_columns(Ws[-1] @ XK, eps)
+        Gh = 2.0 * gc * (XK + gc * Yh + bc - XV)
+        G = rs[None, :] * (Gh - Gh.mean(axis=0) - Yh * (Gh * Yh).mean(axis=0)) * eta[m0:m1][None, :]
+        Ws.append(Ws[-1] - G @ XK.T)
+    dq, dk, dv = (np.zeros((T, d)) for _ in range(3))
+    deta = np.zeros(T)
+    dgam, dbet = np.zeros(d), np.zeros(d)
+    Wb = np.zeros((d, d)) if dwT is None else np.array(dwT, dtype=np.float64)
+    for jb in reversed(range(len(blocks))):
+        m0 = blocks[jb]
+        m1 = min(T, m0 + b)
+        W = Ws[jb]
+        XK, XV, XQ = k[m0:m1].T, v[m0:m1].T, q[m0:m1].T
+        e = eta[m0:m1][None, :]
+        # forward of the mini-batch
+        Y = W @ XK
+        C = Y - Y.mean(axis=0)
+        Yh, rs = _ln_columns(Y, eps)
+        R = XK + gc * Yh + bc - XV
+        Gh = 2.0 * gc * R
+        gbar, m = Gh.mean(axis=0), (Gh * Yh).mean(axis=0)
+        P = Gh - gbar - Yh * m
+        GY = rs[None, :] * P
+        G = GY * e
+        A = np.triu(XK.T @ XQ)
+        Zp = W @ XQ - G @ A
+        Cq = Zp - Zp.mean(axis=0)
+        Zh, rsq = _ln_columns(Zp, eps)
+        # the output
+        Zb = dz[m0:m1].T
+        Qb = Zb.copy()
+        dgam += np.sum(Zb * Zh, axis=1)
+        dbet += np.sum(Zb, axis=1)
+        Zpb = _ln_hat_adjoint(Cq, rsq, gc * Zb)
+        Wn = Wb + Zpb @ XQ.T
+        Qb += W.T @ Zpb
+        Gb = -Zpb @ A.T - Wb @ XK       # W' = W - G K^T passes Wb through
+        Ab = np.triu(-G.T @ Zpb)
+        Kb = XQ @ Ab.T - Wb.T @ G
+        Qb += XK @ Ab
+        # G = GY D
+        GYb = Gb * e
+        deta[m0:m1] = np.sum(Gb * GY, axis=0)
+        # GY = rs P, P = Gh - gbar - Yh m
+        rsb = np.sum(GYb * P, axis=0)
+        Pb = rs[None, :] * GYb
+        Ghb = Pb + (-Pb.sum(axis=0) / d)[None, :] + Yh * (-(Pb * Yh).sum(axis=0) / d)[None, :]
+        Yhb = -Pb * m[None, :] + Gh * (-(Pb * Yh).sum(axis=0) / d)[None, :]
+        # Gh = 2 gamma R, R = K + gamma Yh + beta - V
+        Rb = 2.0 * gc * Ghb
+        dgam += np.sum(2.0 * R * Ghb + Yh * Rb, axis=1)
+        dbet += np.sum(Rb, axis=1)
+        Kb += Rb
+        Yhb += gc * Rb
+        Yb = _ln_hat_adjoint(C, rs, Yhb, rsb)
+        Wn += Yb @ XK.T
+        Kb += W.T @ Yb
+        dq[m0:m1], dk[m0:m1], dv[m0:m1] = Qb.T, Kb.T, -Rb.T
+        Wb = Wn
+    return dq, dk, dv, deta, Wb, dgam, dbet
+
+
 def linear_bwd(q, k, v, eta, w0, b, dz, dwT=None):
     B, H, T, d = q.shape
     out = [np.zeros((B, H, T, d)) for _ in range(3)] + [np.zeros((B, H, T)), np.zeros((B, H, d, d))]

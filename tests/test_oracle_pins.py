@@ -784,6 +784,21 @@ def pin_ln_bwd_equals_autograd_of_dual_form(lib):
                 assert rel(g[i][0, h], leaf.grad.numpy()) < 1e-11, (T, b, h, i)
 
 
+def pin_ln_bwd_equals_dual_form_adjoint(lib):
+    """The LayerNorm backward equals the hand-written adjoint of the dual form
+    (tests/dual_form.py: every product of one mini-batch taken back in reverse,
+    with the LayerNorm VJP's own adjoint), float64."""
+    rng = np.random.default_rng(46)
+    for (T, b) in [(16, 16), (21, 16), (10, 4), (7, 1), (13, 8)]:
+        q, k, v, eta, w0, gamma, beta, dz, dwT = _ln_bwd_case(rng, T, 6)
+        g = oracle.linear_ln_bwd(q, k, v, eta, w0, gamma, beta, 1e-3, b, dz, dwT, lib=lib)
+        for h in range(2):
+            r = dual_form.linear_ln_bwd_unit(q[0, h], k[0, h], v[0, h], eta[0, h], w0[h], gamma[h],
+                                             beta[h], 1e-3, b, dz[0, h], dwT[0, h])
+            for i in range(7):
+                assert rel(g[i][0, h], r[i]) < 1e-12, (T, b, h, i)
+
+
 def pin_ln_bwd_eta_zero(lib):
     """eta = 0: the state never moves, z_t = q_t + gamma LNhat(W0 q_t) + beta,
     so dk = dv = 0, dbeta = sum_t dz_t, dgamma = sum_t LNhat(W0 q_t) dz_t and
@@ -913,6 +928,7 @@ PINS = [
     pin_linear_bwd_eta_zero,
     pin_ln_bwd_finite_differences,
     pin_ln_bwd_equals_autograd_of_dual_form,
+    pin_ln_bwd_equals_dual_form_adjoint,
     pin_ln_bwd_eta_zero,
     pin_mlp_bwd_finite_differences,
     pin_mlp_bwd_equals_autograd_of_dual_form,
