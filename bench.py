@@ -485,8 +485,9 @@ def mlp_training_case(wl, b, steps, warmup):
 def ln_training_case(wl, b, steps, warmup):
     """ttt_linear_ln_fwd_ckpt then ttt_linear_ln_bwd on one LayerNorm
     workload, timed separately; dz is a seeded N(0, 0.01) draw.  bf16 with
-    16 | b: the forward is the dual-form scan with checkpoint stores; the
-    backward is the primal form (fp32 arithmetic, one token at a time)."""
+    16 | b: the forward is the dual-form scan with checkpoint stores; bf16
+    with b = 16: the backward is the dual form (one wave per unit), else the
+    primal form (fp32 arithmetic, one token at a time)."""
     import torch
     from test_rnn_layers_head_amd import inputs, ttt_linear_ln_bwd, ttt_linear_ln_fwd_ckpt
     x = inputs.make_inputs(wl)
@@ -513,7 +514,9 @@ def ln_training_case(wl, b, steps, warmup):
             "bwd_hbm_frac": bb / (kb * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "train_token_heads_per_s": wl.token_heads / ((kf + kb) * 1e-6),
             "kernels": ("linear_ln_scan_kernel with checkpoint stores" if wl.qkv_dtype == "bf16" and b % 16 == 0
-                        else "linear_ln_primal_kernel (checkpoints)") + " / linear_ln_primal_bwd_kernel"}
+                        else "linear_ln_primal_kernel (checkpoints)")
+                       + (" / linear_ln_bwd_kernel (dual form)" if wl.qkv_dtype == "bf16" and b == 16
+                          else " / linear_ln_primal_bwd_kernel")}
 
 
 def mlp_ln_case(wl, b, steps, warmup):

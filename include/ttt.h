@@ -319,12 +319,14 @@ ttt_status_t ttt_mlp_fwd(const void* q, const void* k, const void* v,
  * ttt_linear_ln_fwd_ckpt runs the kernel ttt_linear_ln_fwd picks (the
  * dual-form scan for bf16 q/k/v with 16 | b, else the primal form), which
  * also stores each mini-batch's starting state; z and w_out equal
- * ttt_linear_ln_fwd's bit for bit.  The backward runs the primal form token
- * by token in fp32 arithmetic, one workgroup of 256 threads per (batch,
- * head): it replays each mini-batch from its checkpoint, then takes its
- * tokens back, applying the adjoint of every forward operation (the
- * LayerNorm statistics, the LayerNorm VJP of the inner gradient, the update,
- * the output) in reverse order.  Outputs must not overlap each other or an
+ * ttt_linear_ln_fwd's bit for bit.  The backward applies the adjoint of
+ * every forward operation (the LayerNorm statistics, the LayerNorm VJP of
+ * the inner gradient, the update, the output) in reverse order, mini-batch
+ * by mini-batch from the checkpoints: for bf16 q/k/v with b = 16 in dual
+ * form on the matrix unit, one wave per (batch, head) holding all 64 rows
+ * (fp32 factors as bf16 hi + lo halves, ~2^-16 relative per product);
+ * otherwise token by token in fp32 arithmetic, one workgroup of 256
+ * threads per (batch, head).  Outputs must not overlap each other or an
  * input; T = 0 writes dw0 = dw_T (or zeros) and zero dgamma, dbeta.
  */
 ttt_status_t ttt_linear_ln_fwd_ckpt(const void* q, const void* k, const void* v,

@@ -264,7 +264,7 @@ ttt_status_t linear_ln_bwd_impl(const void* q, const void* k, const void* v, con
   }
   ttt::LinearLnBwdArgs a{q,  k,  v,  eta, w_ckpt, gamma, beta,  eps,        dz,    dw_T, dq,
                          dk, dv, deta, dw0, dgamma, dbeta, (int)units, H, T,  b};
-  const hipError_t e = ttt::launch_linear_ln_primal_bwd(a, dt == TTT_F32, (hipStream_t)stream);
+  const hipError_t e = ttt::launch_linear_ln_bwd(a, dt == TTT_F32, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return TTT_OK;
 }

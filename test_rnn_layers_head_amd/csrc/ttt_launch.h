@@ -100,6 +100,9 @@ struct LinearLnBwdArgs {
   int b;
 };
 hipError_t launch_linear_ln_primal_bwd(const LinearLnBwdArgs& a, bool f32in, hipStream_t s);
+// bf16 q/k/v with b = 16: the dual-form backward (one wave per unit);
+// otherwise the primal form.
+hipError_t launch_linear_ln_bwd(const LinearLnBwdArgs& a, bool f32in, hipStream_t s);
 
 struct MlpArgs {
   const void* q;

@@ -71,11 +71,6 @@ constexpr int L_W2N = L_ETA + 256;                // [wave][mi][nu][lane] f32x4
 constexpr int L_TOTAL = L_W2N + BWV * 8 * 1024;
 static_assert(L_TOTAL <= 160 * 1024, "LDS budget");
 
-// transpose of an accumulator tile (exact for its hi + lo halves)
-__device__ __forceinline__ f32x4 transpose16(f32x4 x, bf16x8 itr) {
-  const Split4 s = split4(x);
-  return mfma_k32(cat44(s.hi, s.lo), itr, f32x4{0, 0, 0, 0});
-}
 // Operand over the wave's 32 hidden units from the splits of two
 // accumulator tiles X[n] (rows tokens, columns u0 + 16 n + c): lane (c, g)
 // slot 8g + e holds X[token c][u0 + 16 (e/4) + 4g + e%4], an A operand over

@@ -47,4 +47,12 @@ __device__ __forceinline__ Split4 unpack_split(uint4 v) {
                 __builtin_bit_cast(s16x4, make_uint2(v.z, v.w))};
 }
 
+// Transpose of an accumulator tile: [hi | lo] as A operand (X^T) against
+// itr = [I; I] (slots 8g + e with 4g + e % 4 == c), exact for the hi + lo
+// halves, which split again into the same halves.
+__device__ __forceinline__ f32x4 transpose16(f32x4 x, bf16x8 itr) {
+  const Split4 s = split4(x);
+  return mfma_k32(cat44(s.hi, s.lo), itr, f32x4{0, 0, 0, 0});
+}
+
 }  // namespace ttt

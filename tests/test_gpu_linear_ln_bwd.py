@@ -4,14 +4,16 @@ scan with checkpoint stores for bf16 with 16 | b, else the primal form) and
 the backward through the scan, through the C ABI, against the fp64 oracle
 ("论文速览 | TTT" §4.4, §6.12).
 
-Tolerance: these kernels run in fp32 arithmetic with exact products, so up to
-a few hundred tokens the LayerNorm forward bound (rel-L2 <= 1e-4, max|diff| /
-RMS <= 1e-3) applies to outputs, checkpoints and every gradient.  Over the
+bf16 q/k/v with b = 16 run the dual-form backward (hi + lo splits, ~2^-16
+relative per product), every other case the primal form in fp32 arithmetic.
+Tolerance: up to a few hundred tokens the LayerNorm forward bound (rel-L2 <=
+1e-4, max|diff| / RMS <= 1e-3) applies to outputs, checkpoints and every
+gradient.  Over the
 2k-token workload the LayerNorm recurrence amplifies rounding in the adjoint
 as it does in the forward: float32 autodiff of the dual form
 (``fp32_floor``, computed in the test) reaches max|diff| / RMS = 1.04e-2 on dv
-against the fp64 oracle (the kernel, from the dual-form forward's
-checkpoints: 1.39e-2).  The bound there is rel-L2 <= 2e-3 and max|diff| /
+against the fp64 oracle (the dual-form backward from the dual-form
+forward's checkpoints: 1.24e-2).  The bound there is rel-L2 <= 2e-3 and max|diff| /
 RMS <= max(1e-2, 1.5 x that floor), gradient by gradient.
 """
 import numpy as np
