@@ -176,17 +176,21 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v;
 }
 
-// Compiler-level ordering around the hardware barrier.  No cache or counter
-// wait is implied: producers that write LDS with DMA wait on their own
-// vector-memory counter before arriving.
+// Workgroup barrier for LDS traffic: this wave's LDS reads and writes are
+// complete before it arrives (the LDS may reorder requests of different
+// waves, and the barrier instruction waits on no counter); no cache or
+// vector-memory wait is implied: producers that write LDS with DMA wait on
+// their own vector-memory counter before arriving.
 __device__ __forceinline__ void wg_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), gfx9 encoding
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
-// The same, and no instruction of any kind is scheduled across it: keeps a
-// software pipeline's stages (reads issued right after the barrier, their
-// use one iteration later) in the order they were written.
+// A barrier with no counter wait at all (the caller waits on what it needs)
+// and no instruction of any kind scheduled across it: keeps a software
+// pipeline's stages (reads issued right after the barrier, their use one
+// iteration later) in the order they were written.
 __device__ __forceinline__ void wg_barrier_pinned() {
   __builtin_amdgcn_sched_barrier(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);

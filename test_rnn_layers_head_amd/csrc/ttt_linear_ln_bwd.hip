@@ -24,16 +24,19 @@
 // where LNhat'(H) = C' - mean C', C' = rs H + (2/64) C varb,
 // varb = -rs^3 (rsb0 + sum_i C H) / 2 is LNhat's adjoint.
 //
-// Work split: one wave per (batch, head) unit holds all 64 rows, so every
-// sum over the rows is four in-lane adds and a DPP row sum, with no barrier.
+// Work split: one workgroup of four waves per (batch, head) unit; wave w
+// owns column block j in [16 w, 16 w + 16) of the state and of its adjoint,
+// kept as W[i][j] at [16 w + 4g + r][16 ib + c] (rows j; all 64 rows i).
 // Tiles are "transposed" (tokens on the accumulator rows): lane (c, g)
-// register r holds X[token 4g + r][16 ib + c] for the four column blocks ib.
-// The state and its adjoint are kept as W[i][j] at [16 jb + 4g + r][16 ib + c]
-// (rows j): split, two j-blocks form the B operand of a contraction over j,
-// whose A operand (K or Q rows) is two 8-byte reads per lane; contractions
-// over i take the transposed blocks (an MFMA against the identity, exact
-// for the hi + lo halves).  The checkpoint of each tile is read from HBM;
-// K, Q, V, dZ and eta arrive by LDS DMA one tile ahead.
+// register r holds X[token 4g + r][16 ib + c] for the four row blocks ib.
+// The three contractions over j (Y = W K, W Q and Wb' K) leave per-wave
+// partials in LDS, summed in a fixed order after one barrier; everything
+// else over the 64 rows is repeated in every wave, so each LayerNorm sum is
+// four in-lane adds and a DPP row sum; the contractions over i (dQ, dK's
+// terms) and the adjoint's update need only the wave's own column block, from
+// the transposed blocks (an MFMA against the identity, exact for the hi + lo
+// halves).  The checkpoint's column block of each tile is read from HBM; K,
+// Q, V, dZ and eta arrive by LDS DMA one tile ahead.  Two barriers per tile.
 //
 // Precision: fp32 factors enter the bf16 MFMA as hi + lo halves, three
 // products kept (~2^-16 relative per product); K, Q, V are exact bf16; the
@@ -46,9 +49,15 @@
 namespace ttt {
 namespace {
 
+typedef unsigned int uint4v __attribute__((ext_vector_type(4)));
+
 // one staged tile: K, Q (swizzled), V, dZ (fp32), eta
 constexpr int T_K = 0, T_Q = 2048, T_V = 4096, T_DZ = 6144, T_ETA = 10240;
 constexpr int RAWB = T_ETA + 64;
+// per-wave partials of the contractions over j: [set][wave][ib][lane] f32x4,
+// sets Y = W K, W Q, Wb' K
+constexpr int L_PART = 2 * RAWB;
+constexpr int L_TOTAL = L_PART + 3 * 4 * 4 * 1024;
 
 // [x0 x1 x2 x3 x0 x1 x2 x3]: the bf16 rows 4g .. 4g + 3 of column col of a
 // swizzled tile, seen by both the hi and the lo slots of the other operand
@@ -67,9 +76,9 @@ __device__ __forceinline__ Split8 i_operand(f32x4 x0, f32x4 x1, bf16x8 itr, cons
   return split8_mfma(transpose16(x0, itr), transpose16(x1, itr), ns);
 }
 
-__global__ void __launch_bounds__(64) linear_ln_bwd_kernel(LinearLnBwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * RAWB];
-  const int lane = threadIdx.x;
+__global__ void __launch_bounds__(256) linear_ln_bwd_kernel(LinearLnBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[L_TOTAL];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
   const int unit = blockIdx.x;
   if (unit >= a.units) return;
@@ -108,40 +117,56 @@ __global__ void __launch_bounds__(64) linear_ln_bwd_kernel(LinearLnBwdArgs a) {
     return s;
   };
 
-  // the adjoint of the state, W[i][j] at [16 jb + 4g + r][16 ib + c]
-  f32x4 Wb[4][4];
+  // this wave's column block of the state's adjoint, W[i][j] at [16 w + 4g + r][16 ib + c]
+  f32x4 Wb[4];
   {
     const float* d0 = a.dw_T ? a.dw_T + (size_t)unit * 4096 : nullptr;
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-      for (int ib = 0; ib < 4; ++ib)
-        Wb[jb][ib] = d0 ? *(const f32x4*)(d0 + (16 * ib + c) * 64 + 16 * jb + 4 * g) : f32x4{0, 0, 0, 0};
+    for (int ib = 0; ib < 4; ++ib)
+      Wb[ib] = d0 ? *(const f32x4*)(d0 + (16 * ib + c) * 64 + 16 * w + 4 * g) : f32x4{0, 0, 0, 0};
   }
+  auto part_at = [&](int set, int v, int ib) {
+    return (f32x4*)(smem + L_PART + ((set * 4 + v) * 4 + ib) * 1024 + lane * 16);
+  };
   f32x4 dgam = {0, 0, 0, 0}, dbet = {0, 0, 0, 0};  // [ib]: partial sums over this lane's tokens
 
   // ------------------------------------------------------- input staging
   const size_t uoff = (size_t)unit * T * 64;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const short*)a.k + uoff, (uint32_t)T * 128);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const short*)a.q + uoff, (uint32_t)T * 128);
-  const __amdgpu_buffer_rsrc_t rvv = make_rsrc((const short*)a.v + uoff, (uint32_t)T * 128);
-  const __amdgpu_buffer_rsrc_t rdz = make_rsrc(a.dz + uoff, (uint32_t)T * 256);
-  const __amdgpu_buffer_rsrc_t reta = make_rsrc(a.eta + (size_t)unit * T, (uint32_t)T * 4);
-  // tile j into slot j & 1: K, Q with chunk p of row r at position p ^ (r & 7)
-  auto issue = [&](int j) {
-    char* slot = smem + (j & 1) * RAWB;
-    const uint32_t tb = (uint32_t)j * 2048;
+  // Tile j is loaded into registers one tile ahead and written to slot
+  // j & 1 at the end of the tile before it (register staging: the compiler
+  // then waits for exactly these loads, and only where they are written).
+  // Wave 0 loads K (and eta), wave 1 Q, wave 2 V, wave 3 dZ, with the same
+  // instructions: four 1 KB pieces, those a wave does not need aimed past its
+  // buffer's end (the hardware returns zeros without a memory access), so no
+  // loaded register is merged across branches.  K and Q rows get chunk p of
+  // row r at position p ^ (r & 7), linear in the staged tile.
+  const char* const src = w == 0 ? (const char*)a.k : w == 1 ? (const char*)a.q
+                        : w == 2 ? (const char*)a.v : (const char*)a.dz;
+  const uint32_t srow = w == 3 ? 256u : 128u;  // bytes per token
+  const __amdgpu_buffer_rsrc_t rin = make_rsrc(src + uoff / 64 * srow, (uint32_t)T * srow);
+  const __amdgpu_buffer_rsrc_t reta = make_rsrc(a.eta + (size_t)unit * T, w == 0 ? (uint32_t)T * 4 : 0u);
+  const int npiece = w == 3 ? 4 : 2;
+  uint32_t pofs[4];  // piece n's offset within the tile
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int r = 8 * n + (lane >> 3), kp = lane & 7;
-      const uint32_t off = tb + r * 128 + ((kp ^ (r & 7)) << 4);
-      dma16(rk, slot + T_K + n * 1024, off);
-      dma16(rq, slot + T_Q + n * 1024, off);
-      dma16(rvv, slot + T_V + n * 1024, tb + n * 1024 + lane * 16);
-    }
+  for (int n = 0; n < 4; ++n) {
+    const int r = 8 * n + (lane >> 3), kp = lane & 7;
+    pofs[n] = w < 2 ? (uint32_t)(r * 128 + ((kp ^ (r & 7)) << 4)) : (uint32_t)(n * 1024 + lane * 16);
+  }
+  uint4v pf[4];
+  float pfe;
+  auto fetch = [&](int j) {
+    const uint32_t tb = (uint32_t)j * 16 * srow;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) dma16(rdz, slot + T_DZ + n * 1024, (uint32_t)j * 4096 + n * 1024 + lane * 16);
-    if (lane < 16) dma4(reta, slot + T_ETA, (uint32_t)(j * 16 + lane) * 4);
+    for (int n = 0; n < 4; ++n)
+      pf[n] = __builtin_amdgcn_raw_buffer_load_b128(rin, n < npiece ? tb + pofs[n] : 0x80000000u, 0, 0);
+    pfe = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(reta, (uint32_t)(j * 16 + (lane & 15)) * 4, 0, 0));
+  };
+  auto stash = [&](int j) {
+    char* dst = smem + (j & 1) * RAWB + w * 2048 + lane * 16;  // T_K, T_Q, T_V, T_DZ = 2048 w
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+      if (n < npiece) *(uint4v*)(dst + n * 1024) = pf[n];
+    if (w == 0 && lane < 16) *(float*)(smem + (j & 1) * RAWB + T_ETA + lane * 4) = pfe;
   };
   const __amdgpu_buffer_rsrc_t oq = make_rsrc(a.dq + uoff, (uint32_t)T * 256);
   const __amdgpu_buffer_rsrc_t ok = make_rsrc(a.dk + uoff, (uint32_t)T * 256);
@@ -155,8 +180,19 @@ __global__ void __launch_bounds__(64) linear_ln_bwd_kernel(LinearLnBwdArgs a) {
                                             (uint32_t)(((16 * j + 4 * g + k) * 64 + col) * 4), 0, 0);
   };
 
-  if (ntiles > 0) issue(ntiles - 1);
-  wait_vmcnt<0>();
+  // this wave's column block of the checkpoint of tile t
+  auto load_w = [&](int t, f32x4* x) {
+    const float* wc = a.w_ckpt + ((size_t)unit * ntiles + t) * 4096;
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) x[ib] = *(const f32x4*)(wc + (16 * ib + c) * 64 + 16 * w + 4 * g);
+  };
+  f32x4 W[4], Wn[4];
+  if (ntiles > 0) {
+    load_w(ntiles - 1, W);
+    fetch(ntiles - 1);
+    stash(ntiles - 1);
+  }
+  wg_barrier();
 
   for (int j = ntiles - 1; j >= 0; --j) {
     const char* raw = smem + (j & 1) * RAWB;
@@ -166,14 +202,11 @@ __global__ void __launch_bounds__(64) linear_ln_bwd_kernel(LinearLnBwdArgs a) {
     const float* dZt = (const float*)(raw + T_DZ);
     const f32x4 eta4 = *(const f32x4*)(raw + T_ETA + 16 * g);
 
-    // ------------------------------------------------ checkpoint of tile j
-    const float* wc = a.w_ckpt + ((size_t)unit * ntiles + j) * 4096;
-    f32x4 W[4][4];
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-      for (int ib = 0; ib < 4; ++ib) W[jb][ib] = *(const f32x4*)(wc + (16 * ib + c) * 64 + 16 * jb + 4 * g);
-    if (j > 0) issue(j - 1);  // into the slot tile j + 1 used
+    // the next tile's checkpoint block and inputs, into registers
+    if (j > 0) {
+      load_w(j - 1, Wn);
+      fetch(j - 1);
+    }
 
     // K, Q rows as A operands over j: slots 8g + e of half h are columns
     // 32 h + 16 (e/4) + 4g + e % 4 (two 8-byte reads)
@@ -204,17 +237,30 @@ __global__ void __launch_bounds__(64) linear_ln_bwd_kernel(LinearLnBwdArgs a) {
     const bf16x8 aTop = cat44(amts.hi, amts.lo); // A = Am: rows s, slots t
 
     // ============================================== forward of the tile
+    // partials over this wave's 16 columns j of W K, W Q and Wb' K: A = the
+    // K / Q row's 4 columns 16 w + 4g .. + 3 twice, B = [hi | lo] of the block
+    {
+      const int kcol = swz_chunk(c, 2 * w + (g >> 1)) + (g & 1) * 8;
+      const uint2 kx = *(const uint2*)(Kt + kcol), qx = *(const uint2*)(Qt + kcol);
+      const bf16x8 kw = cat8(kx, kx), qw = cat8(qx, qx);
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+        const Split4 ws = split4(W[ib]), bs = split4(Wb[ib]);
+        const bf16x8 wop = cat44(ws.hi, ws.lo), bop = cat44(bs.hi, bs.lo);
+        *part_at(0, w, ib) = mfma_k32(kw, wop, f32x4{0, 0, 0, 0});
+        *part_at(1, w, ib) = mfma_k32(qw, wop, f32x4{0, 0, 0, 0});
+        *part_at(2, w, ib) = mfma_k32(kw, bop, f32x4{0, 0, 0, 0});
+      }
+    }
+    wg_barrier();  // the partials of the three contractions over j
     f32x4 Y[4], Zp[4];
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) {
       f32x4 y = {0, 0, 0, 0}, zq = {0, 0, 0, 0};
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const Split8 s = split8_mfma(W[2 * h][ib], W[2 * h + 1][ib], ns);
-        y = mfma_k32(kop[h], s.hi, y);
-        y = mfma_k32(kop[h], s.lo, y);
-        zq = mfma_k32(qop[h], s.hi, zq);
-        zq = mfma_k32(qop[h], s.lo, zq);
+      for (int v = 0; v < 4; ++v) {
+        y += *part_at(0, v, ib);
+        zq += *part_at(1, v, ib);
       }
       Y[ib] = y;
       Zp[ib] = zq;  // W Q; the Gn A term is added below
@@ -310,18 +356,14 @@ __global__ void __launch_bounds__(64) linear_ln_bwd_kernel(LinearLnBwdArgs a) {
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) zpbs[ib] = split4(Zpb[ib]);
 
-    // Gnb^T[s][i] = sum_t Am[s][t] Zpb^T[t][i] + sum_j K[s][j] Wb'[i][j]
+    // Gnb^T[s][i] = sum_t Am[s][t] Zpb^T[t][i] + sum_j K[s][j] Wb'[i][j] (the partials)
     f32x4 Gnb[4];
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) {
-      f32x4 acc = mm_pre(aTop, yops(zpbs[ib]), f32x4{0, 0, 0, 0});
+      f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const Split8 s = split8_mfma(Wb[2 * h][ib], Wb[2 * h + 1][ib], ns);
-        acc = mfma_k32(kop[h], s.hi, acc);
-        acc = mfma_k32(kop[h], s.lo, acc);
-      }
-      Gnb[ib] = acc;
+      for (int v = 0; v < 4; ++v) acc += *part_at(2, v, ib);
+      Gnb[ib] = mm_pre(aTop, yops(zpbs[ib]), acc);
     }
 
     // ============================================== the gradient's adjoint
@@ -345,7 +387,7 @@ __global__ void __launch_bounds__(64) linear_ln_bwd_kernel(LinearLnBwdArgs a) {
         spb = tsum(Pb);
         spy = tdot(Pb, Yh);
       }
-      if (c == 0) {  // tokens past T fall outside the descriptor
+      if (w == 0 && c == 0) {  // tokens past T fall outside the descriptor
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-de[r]), odeta,
@@ -399,51 +441,57 @@ __global__ void __launch_bounds__(64) linear_ln_bwd_kernel(LinearLnBwdArgs a) {
     const bf16x8 abop = cat44(abs_.hi, abs_.lo);     // A = Ab^T: rows t, slots s
     const bf16x8 abTop = cat44(abts.hi, abts.lo);   // A = Ab: rows s, slots t
 
-    // ============================================== dQ, dK, dV by column block
+    // ============================================== dQ, dK, dV of column block w
+    {
+      // the residual's dz and dk's direct Rb of column block w (selects, no indexing)
+      f32x4 dq = Zb[0], dk = Rb[0];
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      f32x4 dq = Zb[jb], dk = Rb[jb];  // the residual's dz; dk's direct Rb
+      for (int jb = 1; jb < 4; ++jb)
+        if (w == jb) {
+          dq = Zb[jb];
+          dk = Rb[jb];
+        }
+      f32x4 dv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dv[r] = -dk[r];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        // W and Wb' with i on the rows (transposed blocks), column block jb
-        const Split8 w2 = split8_mfma(transpose16(W[jb][2 * kb], itr), transpose16(W[jb][2 * kb + 1], itr), ns);
-        const Split8 b2 = split8_mfma(transpose16(Wb[jb][2 * kb], itr), transpose16(Wb[jb][2 * kb + 1], itr), ns);
+        // W and Wb' with i on the rows (transposed blocks)
+        const Split8 w2 = split8_mfma(transpose16(W[2 * kb], itr), transpose16(W[2 * kb + 1], itr), ns);
+        const Split8 b2 = split8_mfma(transpose16(Wb[2 * kb], itr), transpose16(Wb[2 * kb + 1], itr), ns);
         dq = mm3(zpbo[kb], w2, dq);  // W^T Zpb
         dk = mm3(ybo[kb], w2, dk);   // W^T Yb
         dk = mm3(gno[kb], b2, dk);   // Wb'^T Gn
       }
-      dq = mfma_k32(abop, rows_twice(Kt, g, 16 * jb + c), dq);   // + K Ab
-      dk = mfma_k32(abTop, rows_twice(Qt, g, 16 * jb + c), dk);  // + Q Ab^T
-      f32x4 dv;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dv[r] = -Rb[jb][r];
-      store_tile(oq, j, 16 * jb + c, dq);
-      store_tile(ok, j, 16 * jb + c, dk);
-      store_tile(ov, j, 16 * jb + c, dv);
+      dq = mfma_k32(abop, rows_twice(Kt, g, 16 * w + c), dq);   // + K Ab
+      dk = mfma_k32(abTop, rows_twice(Qt, g, 16 * w + c), dk);  // + Q Ab^T
+      store_tile(oq, j, 16 * w + c, dq);
+      store_tile(ok, j, 16 * w + c, dk);
+      store_tile(ov, j, 16 * w + c, dv);
     }
 
     // ============================================== Wb = Wb' + Zpb Q^T + Yb K^T
     Split4 ybs[4];
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) ybs[ib] = split4(Yb[ib]);
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      const bf16x8 qj = rows_twice(Qt, g, 16 * jb + c), kj = rows_twice(Kt, g, 16 * jb + c);
+    {
+      const bf16x8 qj = rows_twice(Qt, g, 16 * w + c), kj = rows_twice(Kt, g, 16 * w + c);
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib) {
-        Wb[jb][ib] = mfma_k32(qj, cat44(zpbs[ib].hi, zpbs[ib].lo), Wb[jb][ib]);
-        Wb[jb][ib] = mfma_k32(kj, cat44(ybs[ib].hi, ybs[ib].lo), Wb[jb][ib]);
+        Wb[ib] = mfma_k32(qj, cat44(zpbs[ib].hi, zpbs[ib].lo), Wb[ib]);
+        Wb[ib] = mfma_k32(kj, cat44(ybs[ib].hi, ybs[ib].lo), Wb[ib]);
       }
     }
-    wait_vmcnt<0>();  // the next tile's inputs have landed
+    if (j > 0) stash(j - 1);  // into the slot tile j + 1 used
+    wg_barrier();             // the next tile's inputs; the partial areas free again
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) W[ib] = Wn[ib];
   }
 
   // the adjoint of the initial state and of the LayerNorm parameters
   float* d0 = a.dw0 + (size_t)unit * 4096;
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-    for (int ib = 0; ib < 4; ++ib) *(f32x4*)(d0 + (16 * ib + c) * 64 + 16 * jb + 4 * g) = Wb[jb][ib];
+  for (int ib = 0; ib < 4; ++ib) *(f32x4*)(d0 + (16 * ib + c) * 64 + 16 * w + 4 * g) = Wb[ib];
 #pragma unroll
   for (int ib = 0; ib < 4; ++ib) {
     float sg = dgam[ib], sb = dbet[ib];
@@ -451,7 +499,7 @@ __global__ void __launch_bounds__(64) linear_ln_bwd_kernel(LinearLnBwdArgs a) {
     sg += __shfl_xor(sg, 32);
     sb += __shfl_xor(sb, 16);
     sb += __shfl_xor(sb, 32);
-    if (g == 0) {
+    if (w == 0 && g == 0) {
       a.dgamma[(size_t)unit * 64 + 16 * ib + c] = sg;
       a.dbeta[(size_t)unit * 64 + 16 * ib + c] = sb;
     }
@@ -462,7 +510,7 @@ __global__ void __launch_bounds__(64) linear_ln_bwd_kernel(LinearLnBwdArgs a) {
 
 hipError_t launch_linear_ln_bwd(const LinearLnBwdArgs& a, bool f32in, hipStream_t s) {
   if (f32in || a.b != 16) return launch_linear_ln_primal_bwd(a, f32in, s);
-  return launch(linear_ln_bwd_kernel, dim3(a.units), dim3(64), s, a);
+  return launch(linear_ln_bwd_kernel, dim3(a.units), dim3(256), s, a);
 }
 
 }  // namespace ttt
