@@ -46,8 +46,10 @@ SCAN_SOURCES = ["ttt_linear_bf16.hip", "ttt_device.h", "ttt_launch.h", "ttt_line
 LN_SOURCES = ["ttt_linear_ln.hip", "ttt_device.h", "ttt_launch.h", "ttt_linear_ops.h"]
 MLP_SOURCES = ["ttt_mlp.hip", "ttt_mlp_ops.h", "ttt_device.h", "ttt_launch.h"]
 MLP_BWD_SOURCES = ["ttt_mlp_bwd.hip", "ttt_mlp_ops.h", "ttt_device.h", "ttt_launch.h"]
+LN_BWD_SOURCES = ["ttt_linear_ln_bwd.hip", "ttt_mlp_ops.h", "ttt_device.h", "ttt_launch.h"]
 # kernel names as rocprofv3 reports them (template arguments: waves,
 # sub-batches, checkpoint stores, LayerNorm wrapper)
+LN_SCAN_NAME = "linear_ln_scan_kernel<1, false>"  # one unit per workgroup, no checkpoint stores
 MLP_SCAN_NAME = "mlp_scan_kernel<8, false, false, false>"
 MLP_LN_SCAN_NAME = "mlp_scan_kernel<8, false, false, true>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
@@ -105,6 +107,13 @@ def mlp_bwd_alg_bytes(wl, b=16) -> int:
     nmb = (wl.T + b - 1) // b
     st = 2 * wl.hidden * wl.d * 4
     return wl.token_heads * (3 * wl.d * 2 + 4 + wl.d * 4 + 3 * wl.d * 4 + 4) + wl.units * (nmb + 1) * st
+
+
+def ln_bwd_alg_bytes(wl, b=16) -> int:
+    """TTT-Linear + LayerNorm backward: the plain backward's traffic (q, k,
+    v, eta, dz and the checkpoints in; dq, dk, dv, deta and dW0 out) plus
+    dgamma and dbeta per unit."""
+    return bwd_alg_bytes(wl, b) + 2 * wl.units * wl.d * 4
 
 
 def mlp_alg_flops(wl, b) -> int:
@@ -486,7 +495,7 @@ def ln_training_case(wl, b, steps, warmup):
     """ttt_linear_ln_fwd_ckpt then ttt_linear_ln_bwd on one LayerNorm
     workload, timed separately; dz is a seeded N(0, 0.01) draw.  bf16 with
     16 | b: the forward is the dual-form scan with checkpoint stores; bf16
-    with b = 16: the backward is the dual form (one wave per unit), else the
+    with b = 16: the backward is the dual form (four waves per unit), else the
     primal form (fp32 arithmetic, one token at a time)."""
     import torch
     from test_rnn_layers_head_amd import inputs, ttt_linear_ln_bwd, ttt_linear_ln_fwd_ckpt
@@ -507,12 +516,15 @@ def ln_training_case(wl, b, steps, warmup):
     assert all(torch.isfinite(t).all().item() for t in grads)
     nmb = (wl.T + b - 1) // b
     fb = ln_alg_bytes(wl) + wl.units * nmb * wl.d * wl.d * 4
-    bb = bwd_alg_bytes(wl, b) + 2 * wl.units * wl.d * 4  # + dgamma, dbeta
+    bb = ln_bwd_alg_bytes(wl, b)
+    dual_bwd = wl.qkv_dtype == "bf16" and b == 16
     return {"workload": wl.name, "b": b, "fwd_ckpt_us": kf, "bwd_us": kb,
             "fwd_alg_bytes": fb, "bwd_alg_bytes": bb,
             "fwd_hbm_frac": fb / (kf * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "bwd_hbm_frac": bb / (kb * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "train_token_heads_per_s": wl.token_heads / ((kf + kb) * 1e-6),
+            **({"bwd_traffic": traffic_for("linear_ln_bwd", LN_BWD_SOURCES, wl.name),
+                "bwd_sq": sq_for("linear_ln_bwd", LN_BWD_SOURCES)} if dual_bwd else {}),
             "kernels": ("linear_ln_scan_kernel with checkpoint stores" if wl.qkv_dtype == "bf16" and b % 16 == 0
                         else "linear_ln_primal_kernel (checkpoints)")
                        + (" / linear_ln_bwd_kernel (dual form)" if wl.qkv_dtype == "bf16" and b == 16
@@ -731,10 +743,11 @@ def summarize_pmc(fetch_dir, write_dir):
           f"x{f_scale:.4f}, write x{w_scale:.4f} (each factor: the bytes the copy moves over what the "
           "counter reads for it).\n")
     cases = (("linear_scan", "linear_scan_bf16_kernel", SCAN_SOURCES, linear_alg_bytes, 3),
-             ("linear_ln_scan", "linear_ln_scan_kernel", LN_SOURCES, ln_alg_bytes, 6),
+             ("linear_ln_scan", LN_SCAN_NAME, LN_SOURCES, ln_alg_bytes, 6),
              ("mlp_scan", MLP_SCAN_NAME, MLP_SOURCES, mlp_alg_bytes, 4),
              ("mlp_ln_scan", MLP_LN_SCAN_NAME, MLP_SOURCES, mlp_ln_alg_bytes, 10),
-             ("mlp_bwd", "mlp_bwd_kernel", MLP_BWD_SOURCES, mlp_bwd_alg_bytes, 4))
+             ("mlp_bwd", "mlp_bwd_kernel", MLP_BWD_SOURCES, mlp_bwd_alg_bytes, 4),
+             ("linear_ln_bwd", "linear_ln_bwd_kernel", LN_BWD_SOURCES, ln_bwd_alg_bytes, 7))
     for key, pat, srcs, alg_fn, wid in cases:
         names = [k for k in fetch if pat in k]
         if not names:
@@ -790,10 +803,11 @@ def sq_derive(med, active_cus):
 
 
 SQ_CASES = (("linear_scan", "linear_scan_bf16_kernel", "SCAN_SOURCES", 256),   # 2 workgroups x 128 units
-            ("linear_ln_scan", "linear_ln_scan_kernel", "LN_SOURCES", 128),   # 128 units
+            ("linear_ln_scan", LN_SCAN_NAME, "LN_SOURCES", 128),   # 128 units
             ("mlp_scan", MLP_SCAN_NAME, "MLP_SOURCES", 96),                     # 96 units
             ("mlp_ln_scan", MLP_LN_SCAN_NAME, "MLP_SOURCES", 96),
-            ("mlp_bwd", "mlp_bwd_kernel", "MLP_BWD_SOURCES", 96))
+            ("mlp_bwd", "mlp_bwd_kernel", "MLP_BWD_SOURCES", 96),
+            ("linear_ln_bwd", "linear_ln_bwd_kernel", "LN_BWD_SOURCES", 96))
 
 
 def summarize_sq(sq_dir):
@@ -985,6 +999,9 @@ def main():
         mlp_ln_case(w10, 16, 2, 1)
         log(f"[bench] {w4.name} training (counter coverage of the MLP backward)")
         mlp_training_case(w4, 16, 2, 1)
+        w7 = inputs.workload(7)
+        log(f"[bench] {w7.name} training (counter coverage of the LayerNorm backward)")
+        ln_training_case(w7, 16, 2, 1)
 
     extras = {}
     if not args.no_extras:

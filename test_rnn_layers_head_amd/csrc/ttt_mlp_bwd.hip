@@ -202,7 +202,6 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
     const char* Vt = raw + T_V;
     const float* dZt = (const float*)(raw + T_DZ);
     const float* Et = (const float*)(raw + T_ETA);
-    if (j > 0) issue(j - 1);  // into the slot tile j + 1 used
 
     // ------------------------------------------------ checkpoint of tile j
     const size_t co = ((size_t)unit * ntiles + j) * nst;
@@ -250,6 +249,11 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
     const bf16x8 aop = cat44(ams.hi, ams.lo);    // A = Am^T (rows t, slots s)
     const bf16x8 aTop = cat44(amts.hi, amts.lo); // A = Am (rows s, slots t)
     const f32x4 eta4 = *(const f32x4*)(Et + 4 * g);
+    // the next tile's inputs, into the slot tile j + 1 used: issued after the
+    // tile's first LDS reads, since the compiler makes the next LDS read wait
+    // for every DMA in flight
+    __builtin_amdgcn_sched_barrier(0);
+    if (j > 0) issue(j - 1);
     f32x4 e2;
 #pragma unroll
     for (int r = 0; r < 4; ++r) e2[r] = 2.f * eta4[r];
