@@ -313,6 +313,7 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
   };
   const int nmb = (T + bsub - 1) / bsub;  // mini-batches (checkpoints)
   // this wave's rows of W1 and columns of W2 in the final-state layouts
+  // the state (W1 [256][64], W2 [64][256], the layouts of the final state)
   auto store_state = [&](float* w1o, float* w2o) {
 #pragma unroll
     for (int n = 0; n < NB; ++n)
@@ -324,6 +325,43 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
         *(f32x4*)(w2o + (16 * mi + c) * HID + u0 + 16 * nu + 4 * g) = W2T[nu][mi];
+  };
+  // the same for the checkpoint of mini-batch mb: nontemporal buffer stores
+  // through descriptors built in scalar registers, the lane's part of the
+  // offsets loop-invariant, so that a burst of them needs no vector
+  // registers beyond the state (an address spilled around the burst would be
+  // reloaded behind all of its stores: the memory counter is in order).  The
+  // stores are issued for every pass, those past the last mini-batch through
+  // an empty descriptor (dropped by the hardware): with the same instruction
+  // count on every path the compiler's wait for the next tile's inputs leaves
+  // them in flight, instead of waiting for them all.  A pass issues them in
+  // four quarters (every other block of W1, then of W2) at four points
+  // before the update: a burst of all of them at once stalls the issuing
+  // waves on the memory unit's queue.
+  const uint32_t w1off = CKPT ? (uint32_t)(((u0 + c) * 64 + 8 * g) * 4) : 0u;
+  const uint32_t w2off = CKPT ? (uint32_t)((c * HID + u0 + 4 * g) * 4) : 0u;
+  auto store_ckpt = [&](int mb, int quarter) {
+    typedef unsigned int u32x4s __attribute__((ext_vector_type(4)));
+    const bool in = mb < nmb;
+    const size_t co = ((size_t)unit * nmb + (in ? mb : 0)) * HID * 64;
+    if (quarter < 2) {  // W1 blocks n = quarter, quarter + 2, ...
+      const __amdgpu_buffer_rsrc_t r1 = make_rsrc(a.w1_ckpt + co, in ? HID * 64 * 4 : 0u);
+#pragma unroll
+      for (int n = quarter; n < NB; n += 2)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4s, W1[n][m]), r1,
+                                                 w1off + (uint32_t)((16 * n * 64 + 32 * (m >> 1) + 4 * (m & 1)) * 4),
+                                                 0, 2);
+    } else {  // W2 blocks nu = quarter - 2, quarter, ...
+      const __amdgpu_buffer_rsrc_t r2 = make_rsrc(a.w2_ckpt + co, in ? HID * 64 * 4 : 0u);
+#pragma unroll
+      for (int nu = quarter - 2; nu < NB; nu += 2)
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4s, W2T[nu][mi]), r2,
+                                                 w2off + (uint32_t)((16 * mi * HID + 16 * nu) * 4), 0, 2);
+    }
   };
 
   for (int j = 0; j < ntiles; ++j) {
@@ -350,13 +388,8 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
     const f32x4 eta4 = *(const f32x4*)(Et + 4 * g);
 
     for (int p = 0; p < npass; ++p) {
-      if constexpr (CKPT) {
-        const int mb = j * npass + p;  // mini-batch starting at token 16 j + bsub p
-        if (mb < nmb) {
-          const size_t co = ((size_t)unit * nmb + mb) * HID * 64;
-          store_state(a.w1_ckpt + co, a.w2_ckpt + co);
-        }
-      }
+      const int mb = j * npass + p;  // mini-batch starting at token 16 j + bsub p
+      if constexpr (CKPT) store_ckpt(mb, 0);
       // ================= Z of the previous pass (4 waves: now; the wrapped
       // variant normalises after B2, holding Z and q)
       f32x4 zo = {0, 0, 0, 0}, qn = {0, 0, 0, 0};
@@ -416,6 +449,7 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
         *(f32x4*)(smem + G::L_Z2P + (w * 4 + mi) * 1024 + lane * 16) = z2;  // partial Z2^T[t][i]
       }
       wg_barrier();  // B1: partial Z2 written
+      if constexpr (CKPT) store_ckpt(mb, 1);
 
       // ================= LATE: the previous pass's Z from waves 4..7
       if constexpr (LATE)
@@ -487,6 +521,7 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
         *(uint4*)(smem + G::L_G2B + mi * 1024 + lane * 16) = pack_split(split4(GT));
       }
       wg_barrier();  // B2: Gn2 ready
+      if constexpr (CKPT) store_ckpt(mb, 2);
       if constexpr (LN && !LATE)
         if (out_tile >= 0 && outw) out_second(out_tile, out_pass, zo, qn);
 
@@ -553,6 +588,7 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
       }
 
       // ================= rank-16 updates of both layers
+      if constexpr (CKPT) store_ckpt(mb, 3);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const f32x4 x = mfma_k32(kop[m >> 1], sel[m & 1], f32x4{0, 0, 0, 0});  // K[t][sigma(m,c)]
