@@ -526,11 +526,14 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
     const bf16x8 k1[2] = {k1a, k1b}, q0[2] = {q0a, q0b};
 
     if constexpr (CKPT) {  // W_j is the state before mini-batch j / tpm
-      if (new_mb) {
-        float* ck = a.w_ckpt + ((size_t)unit * nmb + j / tpm) * 4096;
+      if (new_mb) {  // nontemporal: read back only by the backward
+        typedef unsigned int u32x4c __attribute__((ext_vector_type(4)));
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.w_ckpt + ((size_t)unit * nmb + j / tpm) * 4096, 4096u * 4u);
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-          *(f32x4*)(ck + (rbase + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1)) = W[m];
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4c, W[m]), rc,
+                                                 (uint32_t)(((rbase + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1)) * 4),
+                                                 0, 2);
       }
     }
     // ---- products with W_j that do not wait for the gradient: its split,

@@ -378,9 +378,9 @@ __global__ void __launch_bounds__(256) linear_ln_bwd_kernel(LinearLnBwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             gyb[ib][r] = -eta4[r] * Gnb[ib][r];
-            P[ib][r] = GY[ib][r] / rs[r];
-            Pb[ib][r] = rs[r] * gyb[ib][r];
             Yh[ib][r] = C[ib][r] * rs[r];
+            P[ib][r] = fmaf(-Yh[ib][r], m[r], fmaf(2.f * gam[ib], R[ib][r], -gbar[r]));  // GY = rs P
+            Pb[ib][r] = rs[r] * gyb[ib][r];
           }
         de = tdot(Gnb, GY);
         rsb = tdot(gyb, P);
