@@ -141,12 +141,21 @@ __device__ __forceinline__ void ln_get(const char* area, int g, f32x4& sx, f32x4
 // [64][256] per unit and mini-batch, the layouts of the final state) for the
 // backward; the stores are fire-and-forget and leave the recurrence alone.
 // LN: the LayerNorm + residual wrapper (gamma, beta, eps from the arguments).
-template <int NW, bool SUB, bool CKPT = false, bool LN = false>
+// HOLD: mini-batches of b = 16 tpm tokens (tpm > 1): the gradients of all
+// tpm tiles of a mini-batch are taken at the state W0 of its start, the
+// outputs and updates use the running state (in the dual form the output of
+// token t is W_cur q_t plus the in-tile triangular term, W_cur holding the
+// earlier tiles' updates).  W0 is written at each mini-batch start into the
+// final-state outputs (this wave's part, in their layouts; they are written
+// with the final state at the end) and read back where its products need it;
+// W2 with i on the rows comes from MFMA transposes of the same blocks.
+template <int NW, bool SUB, bool CKPT = false, bool LN = false, bool HOLD = false>
 __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
   using G = MlpGeom<NW>;
   const MlpArgs& a = la.s;
   constexpr int U = G::U, NB = G::NB, NCH = G::NCH;
   static_assert(NW == 4 || NW == 8, "waves 0..3 each own one 16-column block of d in the reductions");
+  static_assert(!HOLD || (NW == 8 && !SUB && !LN), "held gradient point: the plain 8-wave variant");
   __shared__ __attribute__((aligned(16))) char smem[G::L_TOTAL];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
@@ -157,6 +166,7 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
   const int ntiles = (T + 15) >> 4;
   const int bsub = SUB ? a.b : 16;
   const int npass = 16 / bsub;
+  const int tpm = HOLD ? a.b / 16 : 1;  // tiles per mini-batch
   const int u0 = U * w;  // first hidden unit of this wave
 
   // ------------------------------------------------------------ constants
@@ -200,11 +210,22 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       W2T[nu][mi] = *(const f32x4*)(w2g + (16 * mi + c) * HID + u0 + 16 * nu + 4 * g);
-      f32x4 x;
+      if constexpr (!HOLD) {
+        f32x4 x;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = w2g[(16 * mi + 4 * g + r) * HID + u0 + 16 * nu + c];
-      *w2n_at(mi, nu) = x;  // read back only by this wave
+        for (int r = 0; r < 4; ++r) x[r] = w2g[(16 * mi + 4 * g + r) * HID + u0 + 16 * nu + c];
+        *w2n_at(mi, nu) = x;  // read back only by this wave
+      }
     }
+  // HOLD: the gradient point's blocks, read back by the lane that wrote them
+  float* const h1 = a.w1_out + (size_t)unit * HID * 64;
+  float* const h2 = a.w2_out + (size_t)unit * 64 * HID;
+  auto w1_held = [&](int n, int m) {
+    return *(const f32x4*)(h1 + (u0 + 16 * n + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1));
+  };
+  auto w2_held = [&](int nu, int mi) {  // W2[16 mi + c][u0 + 16 nu + 4g + r]
+    return *(const f32x4*)(h2 + (16 * mi + c) * HID + u0 + 16 * nu + 4 * g);
+  };
 
   // ------------------------------------------------------- input staging
   // Chunk q of a tile (q = lane-flat index + NW*64*round): q < 128 a K chunk,
@@ -311,9 +332,9 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
     }
     store_z<SUB>(zr, c, g, omi, rz, tile, pass, bsub);
   };
-  const int nmb = (T + bsub - 1) / bsub;  // mini-batches (checkpoints)
-  // this wave's rows of W1 and columns of W2 in the final-state layouts
-  // the state (W1 [256][64], W2 [64][256], the layouts of the final state)
+  const int nmb = HOLD ? (T + a.b - 1) / a.b : (T + bsub - 1) / bsub;  // mini-batches (checkpoints)
+  // this wave's rows of W1 and columns of W2 (W1 [256][64], W2 [64][256], the
+  // layouts of the final state)
   auto store_state = [&](float* w1o, float* w2o) {
 #pragma unroll
     for (int n = 0; n < NB; ++n)
@@ -388,7 +409,11 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
     const f32x4 eta4 = *(const f32x4*)(Et + 4 * g);
 
     for (int p = 0; p < npass; ++p) {
-      const int mb = j * npass + p;  // mini-batch starting at token 16 j + bsub p
+      // mini-batch starting at token 16 j + bsub p (HOLD: at tile j, if any;
+      // nmb, an empty checkpoint, otherwise)
+      const int mb = HOLD ? (j % tpm == 0 ? j / tpm : nmb) : j * npass + p;
+      if constexpr (HOLD)
+        if (j % tpm == 0) store_state(h1, h2);  // the gradient point
       if constexpr (CKPT) store_ckpt(mb, 0);
       // ================= Z of the previous pass (4 waves: now; the wrapped
       // variant normalises after B2, holding Z and q)
@@ -407,10 +432,19 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
       for (int n = 0; n < NB; ++n) {
         const Split8 s0 = split8_mfma(W1[n][0], W1[n][1], ns), s1 = split8_mfma(W1[n][2], W1[n][3], ns);
         f32x4 z = {0, 0, 0, 0}, zq = {0, 0, 0, 0};
-        z = mfma_k32(kop[0], s0.hi, z);
-        z = mfma_k32(kop[0], s0.lo, z);
-        z = mfma_k32(kop[1], s1.hi, z);
-        z = mfma_k32(kop[1], s1.lo, z);
+        if constexpr (HOLD) {
+          const Split8 t0 = split8_mfma(w1_held(n, 0), w1_held(n, 1), ns);
+          const Split8 t1 = split8_mfma(w1_held(n, 2), w1_held(n, 3), ns);
+          z = mfma_k32(kop[0], t0.hi, z);
+          z = mfma_k32(kop[0], t0.lo, z);
+          z = mfma_k32(kop[1], t1.hi, z);
+          z = mfma_k32(kop[1], t1.lo, z);
+        } else {
+          z = mfma_k32(kop[0], s0.hi, z);
+          z = mfma_k32(kop[0], s0.lo, z);
+          z = mfma_k32(kop[1], s1.hi, z);
+          z = mfma_k32(kop[1], s1.lo, z);
+        }
         zq = mfma_k32(qop[0], s0.hi, zq);
         zq = mfma_k32(qop[0], s0.lo, zq);
         zq = mfma_k32(qop[1], s1.hi, zq);
@@ -437,15 +471,22 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
         x2op[ch] = split8_mfma(t0, t1, ns);
       }
       Split8 w2s[4][NCH];  // hi/lo of W2 at the gradient point: Z2 and the outputs
+      if constexpr (!HOLD) {
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) w2s[mi][ch] = split8_mfma(W2T[2 * ch][mi], W2T[2 * ch + 1][mi], ns);
+          for (int ch = 0; ch < NCH; ++ch) w2s[mi][ch] = split8_mfma(W2T[2 * ch][mi], W2T[2 * ch + 1][mi], ns);
+      }
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
         f32x4 z2 = {0, 0, 0, 0};
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) z2 = mm3(x2op[ch], w2s[mi][ch], z2);
+        for (int ch = 0; ch < NCH; ++ch) {
+          if constexpr (HOLD)
+            z2 = mm3(x2op[ch], split8_mfma(w2_held(2 * ch, mi), w2_held(2 * ch + 1, mi), ns), z2);
+          else
+            z2 = mm3(x2op[ch], w2s[mi][ch], z2);
+        }
         *(f32x4*)(smem + G::L_Z2P + (w * 4 + mi) * 1024 + lane * 16) = z2;  // partial Z2^T[t][i]
       }
       wg_barrier();  // B1: partial Z2 written
@@ -544,7 +585,14 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
       for (int nu = 0; nu < NB; ++nu) {
         f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) acc = mm3(ga[kb], split8_mfma(*w2n_at(2 * kb, nu), *w2n_at(2 * kb + 1, nu), ns), acc);
+        for (int kb = 0; kb < 2; ++kb) {
+          if constexpr (HOLD)  // W2 with i on the rows: transposes of the held blocks
+            acc = mm3(ga[kb],
+                      split8_mfma(transpose16(w2_held(nu, 2 * kb), itr), transpose16(w2_held(nu, 2 * kb + 1), itr), ns),
+                      acc);
+          else
+            acc = mm3(ga[kb], split8_mfma(*w2n_at(2 * kb, nu), *w2n_at(2 * kb + 1, nu), ns), acc);
+        }
         f32x4 g1;
 #pragma unroll
         for (int r = 0; r < 4; ++r) g1[r] = acc[r] * D[nu][r];
@@ -573,7 +621,8 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
         f32x4 zp = {0, 0, 0, 0};
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch) {
-          if constexpr (LN)  // split again: not held through the LayerNorm rounds
+          if constexpr (LN || HOLD)  // split again: not held through the LayerNorm rounds; HOLD:
+            // the running state, not the gradient point
             zp = mm3(x2qop[ch], split8_mfma(W2T[2 * ch][mi], W2T[2 * ch + 1][mi], ns), zp);
           else
             zp = mm3(x2qop[ch], w2s[mi][ch], zp);
@@ -606,8 +655,9 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
         const YOps xy = yops(x2ts[nu]);
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
-          W2T[nu][mi] = mm_pre(xa, g2y[mi], W2T[nu][mi]);                          // += X2 Gn2^T
-          *w2n_at(mi, nu) = mm_pre(cat44(g2s[mi].hi, g2s[mi].lo), xy, *w2n_at(mi, nu));  // += Gn2 X2^T
+          W2T[nu][mi] = mm_pre(xa, g2y[mi], W2T[nu][mi]);  // += X2 Gn2^T
+          if constexpr (!HOLD)
+            *w2n_at(mi, nu) = mm_pre(cat44(g2s[mi].hi, g2s[mi].lo), xy, *w2n_at(mi, nu));  // += Gn2 X2^T
         }
       }
       if constexpr (!LATE) {  // the output waves are 0..3
@@ -640,9 +690,14 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
 
 hipError_t launch_mlp(const MlpArgs& a, bool f32in, hipStream_t s) {
   constexpr int NW = 4;
-  // fp32 inputs and mini-batches spanning several tiles: the primal kernel
-  if (f32in || a.b > 16) return launch_mlp_primal(a, f32in, s);
+  // fp32 inputs: the primal kernel
+  if (f32in || (a.b > 16 && a.b % 16 != 0)) return launch_mlp_primal(a, f32in, s);
   const MlpLnArgs la{a, nullptr, nullptr, 0.f};
+  if (a.b > 16) {  // mini-batches of several tiles: the gradient point held in memory
+    if (a.w1_ckpt)
+      return launch(mlp_scan_kernel<2 * NW, false, true, false, true>, dim3(a.units), dim3(2 * NW * 64), s, la);
+    return launch(mlp_scan_kernel<2 * NW, false, false, false, true>, dim3(a.units), dim3(2 * NW * 64), s, la);
+  }
   if (a.w1_ckpt) {
     if (a.b == 16) return launch(mlp_scan_kernel<2 * NW, false, true>, dim3(a.units), dim3(2 * NW * 64), s, la);
     return launch(mlp_scan_kernel<NW, true, true>, dim3(a.units), dim3(NW * 64), s, la);
