@@ -145,10 +145,12 @@ __device__ __forceinline__ void ln_get(const char* area, int g, f32x4& sx, f32x4
 // tpm tiles of a mini-batch are taken at the state W0 of its start, the
 // outputs and updates use the running state (in the dual form the output of
 // token t is W_cur q_t plus the in-tile triangular term, W_cur holding the
-// earlier tiles' updates).  W0 is written at each mini-batch start into the
-// final-state outputs (this wave's part, in their layouts; they are written
-// with the final state at the end) and read back where its products need it;
-// W2 with i on the rows comes from MFMA transposes of the same blocks.
+// earlier tiles' updates).  At each mini-batch start the bf16 hi/lo operands
+// of W1 go into this wave's LDS area (the W2 copy with i on the rows is not
+// kept: nothing else needs it), and W2 into the final-state output (this
+// wave's columns, in its layout; the final state overwrites it at the end),
+// read back where its products need it, by the lane that wrote it; W2 with i
+// on the rows comes from MFMA transposes of those blocks.
 template <int NW, bool SUB, bool CKPT = false, bool LN = false, bool HOLD = false>
 __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
   using G = MlpGeom<NW>;
@@ -217,12 +219,8 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
         *w2n_at(mi, nu) = x;  // read back only by this wave
       }
     }
-  // HOLD: the gradient point's blocks, read back by the lane that wrote them
-  float* const h1 = a.w1_out + (size_t)unit * HID * 64;
+  // HOLD: the gradient point's W2 blocks, read back by the lane that wrote them
   float* const h2 = a.w2_out + (size_t)unit * 64 * HID;
-  auto w1_held = [&](int n, int m) {
-    return *(const f32x4*)(h1 + (u0 + 16 * n + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1));
-  };
   auto w2_held = [&](int nu, int mi) {  // W2[16 mi + c][u0 + 16 nu + 4g + r]
     return *(const f32x4*)(h2 + (16 * mi + c) * HID + u0 + 16 * nu + 4 * g);
   };
@@ -413,7 +411,13 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
       // nmb, an empty checkpoint, otherwise)
       const int mb = HOLD ? (j % tpm == 0 ? j / tpm : nmb) : j * npass + p;
       if constexpr (HOLD)
-        if (j % tpm == 0) store_state(h1, h2);  // the gradient point
+        if (j % tpm == 0) {  // the gradient point's W2
+#pragma unroll
+          for (int nu = 0; nu < NB; ++nu)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+              *(f32x4*)(h2 + (16 * mi + c) * HID + u0 + 16 * nu + 4 * g) = W2T[nu][mi];
+        }
       if constexpr (CKPT) store_ckpt(mb, 0);
       // ================= Z of the previous pass (4 waves: now; the wrapped
       // variant normalises after B2, holding Z and q)
@@ -432,9 +436,16 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
       for (int n = 0; n < NB; ++n) {
         const Split8 s0 = split8_mfma(W1[n][0], W1[n][1], ns), s1 = split8_mfma(W1[n][2], W1[n][3], ns);
         f32x4 z = {0, 0, 0, 0}, zq = {0, 0, 0, 0};
-        if constexpr (HOLD) {
-          const Split8 t0 = split8_mfma(w1_held(n, 0), w1_held(n, 1), ns);
-          const Split8 t1 = split8_mfma(w1_held(n, 2), w1_held(n, 3), ns);
+        if constexpr (HOLD) {  // W1's operands at the gradient point, [n][s0 hi, lo, s1 hi, lo][lane]
+          char* const hb = w2n + n * 4096;
+          if (j % tpm == 0) {
+            *(bf16x8*)hb = s0.hi;
+            *(bf16x8*)(hb + 1024) = s0.lo;
+            *(bf16x8*)(hb + 2048) = s1.hi;
+            *(bf16x8*)(hb + 3072) = s1.lo;
+          }
+          const Split8 t0{*(const bf16x8*)hb, *(const bf16x8*)(hb + 1024)};
+          const Split8 t1{*(const bf16x8*)(hb + 2048), *(const bf16x8*)(hb + 3072)};
           z = mfma_k32(kop[0], t0.hi, z);
           z = mfma_k32(kop[0], t0.lo, z);
           z = mfma_k32(kop[1], t1.hi, z);
