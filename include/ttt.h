@@ -286,14 +286,17 @@ ttt_status_t ttt_mlp_step(const void* q, const void* k, const void* v,
  * Both layers take their gradient of sum_t eta_t ||f(k_t) - v_t||^2 at the
  * state before the mini-batch (§3.5).  GELU is x * Phi(x).
  *
- * Two kernels serve the call.  bf16 q/k/v with b | 16 (1, 2, 4, 8, 16): the
- * dual form per 16-token tile, state resident in registers, products on
- * bf16 MFMA with fp32 operands split into bf16 hi + lo, erf from
- * Abramowitz & Stegun 7.1.26 (absolute error <= 1.5e-7).  fp32 q/k/v, or
- * b a multiple of 16 above 16: the primal form token by token in fp32
- * arithmetic (the library's erff), one workgroup of 1024 threads per
- * (batch, head) with the state and the gradient point in registers; exact
- * but about 10x slower per token, meant for parity and for long mini-batches.
+ * Two kernels serve the call.  bf16 q/k/v with b | 16 or 16 | b: the dual
+ * form per 16-token tile, state resident in registers, products on bf16
+ * MFMA with fp32 operands split into bf16 hi + lo, erf from Abramowitz &
+ * Stegun 7.1.26 (absolute error <= 1.5e-7); for b > 16 the state at the
+ * mini-batch start (the gradient point) is kept in LDS and in w2_out, which
+ * is therefore written during the call and holds the final W2 only at its
+ * end (in-place resume, w2_out == w2_0 with w0_per_batch = 1, stays valid).
+ * fp32 q/k/v: the primal form token by token in fp32 arithmetic (the
+ * library's erff), one workgroup of 1024 threads per (batch, head) with the
+ * state and the gradient point in registers; exact but about 10x slower per
+ * token, meant for parity.
  */
 ttt_status_t ttt_mlp_fwd(const void* q, const void* k, const void* v,
                          const float* eta, const float* w1_0,
@@ -354,8 +357,8 @@ ttt_status_t ttt_linear_ln_bwd(const void* q, const void* k, const void* v,
  *             mini-batch of b tokens (w1_ckpt[..][0] = W1_0);
  *   w2_ckpt : out [B][H][ceil(T/b)][d][hidden] fp32, the same for W2.
  * It runs the kernel ttt_mlp_fwd picks for the same arguments (the bf16
- * dual-form scan for bf16 q/k/v with b | 16, else the primal form), which
- * also stores each mini-batch's starting state.
+ * dual-form scan for bf16 q/k/v, else the primal form), which also stores
+ * each mini-batch's starting state.
  *
  * ttt_mlp_bwd: the gradient of a loss L(Z, W1_T, W2_T) with respect to the
  * scan's inputs, given
