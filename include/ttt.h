@@ -159,11 +159,12 @@ ttt_status_t ttt_linear_ln_fwd(const void* q, const void* k, const void* v,
  * TTT_ERR_VALUE).
  *
  * Support: d = 64, hidden = 256, fp32 or bf16 q/k/v, b | 16 or 16 | b.
- * bf16 q/k/v with b | 16 runs the dual-form scan of ttt_mlp_fwd (same
- * work split and precision), the LayerNorm's per-token sums over the 64
- * components crossing the reducing waves through LDS; fp32 inputs and b > 16
- * run the primal form token by token in fp32 arithmetic (1024 threads per
- * (batch, head)).
+ * bf16 q/k/v with b | 16 or 16 | b runs the dual-form scan of ttt_mlp_fwd
+ * (same work split and precision, and for b > 16 the same use of w2_out as
+ * the held state during the call), the LayerNorm's per-token sums over the
+ * 64 components crossing the reducing waves through LDS; fp32 inputs run the
+ * primal form token by token in fp32 arithmetic (1024 threads per (batch,
+ * head)).
  */
 ttt_status_t ttt_mlp_ln_fwd(const void* q, const void* k, const void* v,
                             const float* eta, const float* w1_0,

@@ -157,7 +157,7 @@ __global__ void __launch_bounds__(NW * 64) mlp_scan_kernel(MlpLnArgs la) {
   const MlpArgs& a = la.s;
   constexpr int U = G::U, NB = G::NB, NCH = G::NCH;
   static_assert(NW == 4 || NW == 8, "waves 0..3 each own one 16-column block of d in the reductions");
-  static_assert(!HOLD || (NW == 8 && !SUB && !LN), "held gradient point: the plain 8-wave variant");
+  static_assert(!HOLD || (NW == 8 && !SUB), "held gradient point: the 8-wave variant");
   __shared__ __attribute__((aligned(16))) char smem[G::L_TOTAL];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
@@ -719,7 +719,9 @@ hipError_t launch_mlp(const MlpArgs& a, bool f32in, hipStream_t s) {
 
 hipError_t launch_mlp_ln(const MlpLnArgs& a, bool f32in, hipStream_t s) {
   constexpr int NW = 4;
-  if (f32in || a.s.b > 16) return launch_mlp_ln_primal(a, f32in, s);
+  if (f32in || (a.s.b > 16 && a.s.b % 16 != 0)) return launch_mlp_ln_primal(a, f32in, s);
+  if (a.s.b > 16)  // mini-batches of several tiles: the gradient point held in memory
+    return launch(mlp_scan_kernel<2 * NW, false, false, true, true>, dim3(a.s.units), dim3(2 * NW * 64), s, a);
   if (a.s.b == 16)
     return launch(mlp_scan_kernel<2 * NW, false, false, true>, dim3(a.s.units), dim3(2 * NW * 64), s, a);
   return launch(mlp_scan_kernel<NW, true, false, true>, dim3(a.s.units), dim3(NW * 64), s, a);

@@ -2,8 +2,9 @@
 ("论文速览 | TTT" §4.4 with §3.7), through the C ABI against the fp64 oracle.
 
 bf16 inputs with b | 16 run the dual-form scan (bf16 MFMA on hi + lo
-splits, ~2^-16 relative per product); fp32 inputs and b = 64 the primal form
-in fp32 arithmetic.  The bound is the LayerNorm bound of the linear wrapper,
+splits, ~2^-16 relative per product), with 16 | b the same scan with the
+gradient point held across the mini-batch's tiles; fp32 inputs the primal
+form in fp32 arithmetic.  The bound is the LayerNorm bound of the linear wrapper,
 rel-L2 <= 1e-4 and max|diff| / RMS <= 1e-3, on z and both final states.  On the 2k-token workload the max bound is
 max(1e-3, 1.5 x the fp32 floor).  The floor is what a plain float32
 evaluation of the same method (torch on the CPU, the dual form, batched over
@@ -56,7 +57,19 @@ def test_small_parity(dtype, b, T):
     print(f"{dtype} T={T} b={b}:", out)
 
 
-@pytest.mark.parametrize("dtype, b", [("bf16", 16), ("bf16", 4), ("f32", 16)])
+@pytest.mark.parametrize("b", [32, 48, 64])
+@pytest.mark.parametrize("T", [16, 130, 200])
+def test_held_gradient_point(b, T):
+    """Mini-batches of several tiles (bf16): ragged last mini-batch, tile
+    counts that are and are not multiples of b / 16."""
+    x = case(1, 3, T, "bf16", seed=1100 + T + b)
+    got = run(x, b)
+    ref = oracle.mlp_ln(x.q, x.k, x.v, x.eta, x.w1, x.w2, x.ln_gamma, x.ln_beta, x.wl.ln_eps, b)
+    out = {n: close(g, r, n)["rel_l2"] for n, g, r in zip(("z", "w1", "w2"), got, ref)}
+    print(f"bf16 T={T} b={b}:", out)
+
+
+@pytest.mark.parametrize("dtype, b", [("bf16", 16), ("bf16", 4), ("bf16", 32), ("f32", 16)])
 def test_gamma_zero_freezes_the_state(dtype, b):
     """gamma = 0: no gradient passes the LayerNorm, z = q + beta exactly and
     the state is unchanged (both kernels' arithmetic on this path is exact)."""
