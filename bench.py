@@ -489,8 +489,8 @@ def mlp_training_case(wl, b, steps, warmup):
             "train_token_heads_per_s": wl.token_heads / ((kf + kb) * 1e-6),
             **({"bwd_traffic": traffic_for("mlp_bwd", MLP_BWD_SOURCES, wl.name),
                 "bwd_sq": sq_for("mlp_bwd", MLP_BWD_SOURCES)} if dual_bwd else {}),
-            "kernels": ("mlp_scan_kernel with checkpoint stores" if b <= 16 and 16 % b == 0
-                        else "mlp_primal_kernel (checkpoints)")
+            "kernels": ("mlp_scan_kernel with checkpoint stores" if wl.qkv_dtype == "bf16" and
+                        (16 % b == 0 or b % 16 == 0) else "mlp_primal_kernel (checkpoints)")
                        + (" / mlp_bwd_kernel (dual form)" if dual_bwd else " / mlp_primal_bwd_kernel")}
 
 
@@ -536,8 +536,9 @@ def ln_training_case(wl, b, steps, warmup):
 
 def mlp_ln_case(wl, b, steps, warmup):
     """ttt_mlp_ln_fwd (TTT-MLP with the LayerNorm + residual wrapper) on one
-    workload: the dual-form scan for bf16 inputs with b | 16, else the
-    primal-form kernel."""
+    workload: the dual-form scan for bf16 inputs with b | 16 or 16 | b (the
+    gradient point held across tiles for b > 16), else the primal-form
+    kernel."""
     import torch
     from test_rnn_layers_head_amd import inputs, ttt_mlp_ln_fwd
     x = inputs.make_inputs(wl)
@@ -548,7 +549,7 @@ def mlp_ln_case(wl, b, steps, warmup):
                                     wl.ln_eps, b)
     wall, kmean, spread = time_launches(launch, steps, warmup)
     byts = mlp_ln_alg_bytes(wl)
-    flops = mlp_alg_flops(wl, b)
+    dual = wl.qkv_dtype == "bf16" and (16 % b == 0 or b % 16 == 0)
     dual = wl.qkv_dtype == "bf16" and b <= 16 and 16 % b == 0
     return {"workload": wl.name, "b": b, "token_heads_per_s": wl.token_heads / (wall * 1e-3),
             "kernel_us_mean": kmean, "kernel_us_median": spread["median"],
