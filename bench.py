@@ -549,8 +549,8 @@ def mlp_ln_case(wl, b, steps, warmup):
                                     wl.ln_eps, b)
     wall, kmean, spread = time_launches(launch, steps, warmup)
     byts = mlp_ln_alg_bytes(wl)
+    flops = mlp_alg_flops(wl, b)
     dual = wl.qkv_dtype == "bf16" and (16 % b == 0 or b % 16 == 0)
-    dual = wl.qkv_dtype == "bf16" and b <= 16 and 16 % b == 0
     return {"workload": wl.name, "b": b, "token_heads_per_s": wl.token_heads / (wall * 1e-3),
             "kernel_us_mean": kmean, "kernel_us_median": spread["median"],
             "alg_bytes": byts, "alg_flops": flops,
