@@ -1082,6 +1082,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
+        "inputs_sha256": x.sha256(),  # the seeded headline inputs, as both sides consume them
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "d": wl.d, "b": b,
                    "qkv_dtype": "bf16", "state_dtype": "f32", "global_batch": wl.B,
                    "seq_len": wl.T, "parallelism": "none (1 GPU)"},
