@@ -47,11 +47,11 @@ LN_SOURCES = ["ttt_linear_ln.hip", "ttt_device.h", "ttt_launch.h", "ttt_linear_o
 MLP_SOURCES = ["ttt_mlp.hip", "ttt_mlp_ops.h", "ttt_device.h", "ttt_launch.h"]
 MLP_BWD_SOURCES = ["ttt_mlp_bwd.hip", "ttt_mlp_ops.h", "ttt_device.h", "ttt_launch.h"]
 LN_BWD_SOURCES = ["ttt_linear_ln_bwd.hip", "ttt_mlp_ops.h", "ttt_device.h", "ttt_launch.h"]
-# kernel names as rocprofv3 reports them (template arguments: waves,
-# sub-batches, checkpoint stores, LayerNorm wrapper)
+# kernel names as rocprofv3 reports them (the MLP scan's template arguments:
+# waves, sub-batches, checkpoint stores, LayerNorm wrapper, held gradient point)
 LN_SCAN_NAME = "linear_ln_scan_kernel<1, false>"  # one unit per workgroup, no checkpoint stores
-MLP_SCAN_NAME = "mlp_scan_kernel<8, false, false, false>"
-MLP_LN_SCAN_NAME = "mlp_scan_kernel<8, false, false, true>"
+MLP_SCAN_NAME = "mlp_scan_kernel<8, false, false, false, false>"
+MLP_LN_SCAN_NAME = "mlp_scan_kernel<8, false, false, true, false>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # untimed launches before each extra workload: the cache-flush writes of the
 # headline's cold-start pass leave the clocks low for a few milliseconds
