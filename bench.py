@@ -416,8 +416,9 @@ def bwd_alg_bytes(wl, b=16) -> int:
 def training_case(wl, steps, warmup, b=16):
     """ttt_linear_fwd_ckpt then ttt_linear_bwd on one workload, timed
     separately; dz is a seeded N(0, 0.01) draw.  Where both take sequence
-    chunks, the single-pass backward is timed beside them.  b = 16 runs the
-    dual-form kernels, other b the primal-form ones."""
+    chunks, the single-pass backward is timed beside them.  bf16 with b = 16
+    runs the dual-form kernels, with b < 16 the same kernels with one
+    mini-batch per zero-padded tile, other cases the primal-form ones."""
     import torch
     from test_rnn_layers_head_amd import (inputs, ttt_linear_bwd, ttt_linear_fwd_ckpt,
                                           ttt_linear_fwd_plan)
@@ -442,10 +443,11 @@ def training_case(wl, steps, warmup, b=16):
     bb = bwd_alg_bytes(wl, b)
     chunks = ttt_linear_fwd_plan(wl.B, wl.H, wl.T, b)[1]
     extra = {"seq_chunks": chunks}
-    if b != 16 or wl.qkv_dtype != "bf16":
+    if b > 16 or wl.qkv_dtype != "bf16":
         extra["kernels"] = "linear_primal_ckpt_kernel / linear_primal_bwd_kernel"
     else:
-        extra["kernels"] = "linear_scan_bf16_kernel with checkpoint stores / linear_bwd_kernel"
+        extra["kernels"] = ("linear_scan_bf16_kernel with checkpoint stores / linear_bwd_kernel"
+                            + (" (one mini-batch per zero-padded tile)" if b < 16 else ""))
     if chunks > 1:
         _, k1, _ = time_launches(lambda: ttt_linear_bwd(d["q"], d["k"], d["v"], d["eta"], ck, 16, dz,
                                                         seq_chunks=1), steps, warmup)
@@ -1032,7 +1034,7 @@ def main():
         w5 = inputs.workload(5)
         log(f"[bench] forward with checkpoints + backward, {w5.name}")
         extras[f"train-{w5.name}"] = training_case(w5, 3, 2)
-        log(f"[bench] forward with checkpoints + backward, {wl.name}, b = 4 (primal kernels)")
+        log(f"[bench] forward with checkpoints + backward, {wl.name}, b = 4 (padded tiles)")
         extras[f"train-{wl.name}_b4"] = training_case(wl, 2, 1, b=4)
         w7 = inputs.workload(7)
         log(f"[bench] forward with checkpoints + backward, {w7.name}")

@@ -144,8 +144,9 @@ ttt_status_t linear_impl(const void* q, const void* k, const void* v, const floa
   ttt_status_t st = check_common(fn, dt, w0_per_batch, B, H, T, d, b, in, 5, out,
                                  w_ckpt ? 3 : 2, pairs, 1, T > 0);
   if (st != TTT_OK || units == 0) return st;
-  // checkpoints for b != 16 or fp32 inputs: the primal-form kernel
-  const bool ck_primal = w_ckpt && (dt != TTT_BF16 || b != 16);
+  // checkpoints for b > 16 or fp32 inputs: the primal-form kernel (bf16
+  // with b < 16: the b = 16 kernel, one mini-batch per zero-padded tile)
+  const bool ck_primal = w_ckpt && (dt != TTT_BF16 || b > 16);
   // chunks: 0 = automatic, 1 = one pass, P >= 2 = P sequence chunks
   int P = chunks;
   if (P == 0) P = default_chunks(dt, b, units, T);
@@ -162,6 +163,7 @@ ttt_status_t linear_impl(const void* q, const void* k, const void* v, const floa
   } else {
     ttt::LinearArgs a{q, k, v, eta, w0, z, w_out, w0_per_batch, (int)units, H, T, b, w_ckpt};
     a.ring_depth = ring_depth;
+    if (w_ckpt && b < 16) a.bt = b;
     if (ck_primal)
       e = ttt::launch_linear_primal_ckpt(a, dt == TTT_F32, s);
     else if (P > 1)
@@ -396,10 +398,11 @@ ttt_status_t linear_bwd_impl(const void* q, const void* k, const void* v, const 
   if (d != 64) return fail(TTT_ERR_UNSUPPORTED, "%s: head dim d=%d unsupported (only 64)", fn, d);
   if (!supported_b(b))
     return fail(TTT_ERR_UNSUPPORTED, "%s: mini-batch b=%d unsupported (need b | 16 or 16 | b)", fn, b);
-  // bf16 with b = 16: the dual-form kernel (and its sequence chunks); any
-  // other b or fp32 inputs: the primal-form kernel, one pass
-  const bool primal = dt != TTT_BF16 || b != 16;
-  if (primal && chunks > 1)
+  // bf16 with b = 16: the dual-form kernel (and its sequence chunks); bf16
+  // with b < 16: the same kernel, one mini-batch per zero-padded tile; b > 16
+  // or fp32 inputs: the primal-form kernel, one pass
+  const bool primal = dt != TTT_BF16 || b > 16;
+  if ((primal || b != 16) && chunks > 1)
     return fail(TTT_ERR_UNSUPPORTED, "%s: seq_chunks=%d needs bf16 q/k/v and b = 16", fn, chunks);
   if (seq >= ((int64_t)1 << 31))
     return fail(TTT_ERR_SHAPE, "%s: B*H*T*d = %lld exceeds 2^31 - 1", fn, (long long)seq);
@@ -435,6 +438,7 @@ ttt_status_t linear_bwd_impl(const void* q, const void* k, const void* v, const 
     e = ttt::launch_linear_primal_bwd(a, dt == TTT_F32, (hipStream_t)stream);
   } else {
     ttt::LinearBwdArgs a{q, k, v, eta, w_ckpt, dz, dw_T, dq, dk, dv, deta, dw0, (int)units, H, T};
+    a.bt = b < 16 ? b : 16;
     e = P > 1 ? ttt::launch_linear_bwd_chunked(a, P, auto_rows(units * P), (hipStream_t)stream)
               : ttt::launch_linear_bwd(a, (hipStream_t)stream);
   }

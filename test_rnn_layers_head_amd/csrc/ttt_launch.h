@@ -37,8 +37,8 @@ struct LinearArgs {
   int H;
   int T;
   int b;
-  // optional: the state at the start of every 16-token mini-batch,
-  // [units][ceil(T / 16)][64][64] (b = 16, bf16 inputs only)
+  // optional: the state at the start of every mini-batch,
+  // [units][ceil(T / b)][64][64] (bf16 inputs, b | 16)
   float* w_ckpt = nullptr;
   // Passes of the chunked scan (bf16, b = 16; defaults: the plain scan).
   // z == nullptr: no outputs (Q is not read either).
@@ -49,6 +49,10 @@ struct LinearArgs {
   int wout_every = 1;      // only units u with u % wout_every == wout_every - 1 write their
                            // final state, to w_out + (u / wout_every) * wout_stride
   int ring_depth = 0;      // bf16, b = 16: 0 = the default LDS ring depth, 1 = one tile in flight
+  // With w_ckpt: tokens per tile, 16 or b < 16 (b | 16), each b-token
+  // mini-batch then alone in a tile whose other rows read as zero tokens
+  // (eta = 0: no contribution) and drop their outputs.
+  int bt = 16;
 };
 
 enum { W0_ARG = 0, W0_IDENTITY = 1, W0_ZERO = 2, W0_IN_Z = 3 };
@@ -169,7 +173,7 @@ struct LinearBwdArgs {
   const void* k;
   const void* v;
   const float* eta;      // [units][T]
-  const float* w_ckpt;   // [units][ceil(T/16)][64][64]: W at every tile start
+  const float* w_ckpt;   // [units][ceil(T/bt)][64][64]: W at every tile start
   const float* dz;       // [units][T][64]
   const float* dw_T;     // [units][64][64] or NULL
   float* dq;             // [units][T][64]
@@ -184,6 +188,10 @@ struct LinearBwdArgs {
   int dw_stride = 4096;   // floats between the dw_T of consecutive units
   int dw0_stride = 4096;  // floats between the dw0 of consecutive units
   int tok_out = 1;        // 0: dq, dk, dv, deta are not written
+  // Tokens per tile: 16, or b < 16 (b | 16) with each b-token mini-batch
+  // alone in a tile whose other rows read as zero tokens (eta = 0: no
+  // contribution to the state) and whose outputs there are dropped.
+  int bt = 16;
 };
 hipError_t launch_linear_bwd(const LinearBwdArgs& a, hipStream_t s);
 

@@ -87,8 +87,11 @@ struct Geom {
 // TPM: tiles per mini-batch when it is fixed at compile time (b = 32, 64),
 // so a tile's position inside its mini-batch costs nothing; 0 = read from
 // the arguments (other multiples of 16).  Unused below b = 16.
-// CKPT (b = 16 only): also store the state at the start of every tile, the
-// checkpoints the backward pass reads.
+// CKPT (b | 16): also store the state at the start of every tile, the
+// checkpoints the backward pass reads; for b < 16 each b-token mini-batch
+// takes a tile of its own (a.bt = b), rows b..15 reading as zero tokens
+// (eta = 0 leaves the state and the other tokens' outputs unchanged) and
+// dropping their outputs: the b = 16 arithmetic on padded tiles.
 template <int MODE, int ROWS, int TPM, bool CKPT = false, int DEPTH = 0>
 __global__ void __launch_bounds__((Geom<ROWS>::THREADS))
 linear_scan_bf16_kernel(LinearArgs a) {
@@ -115,8 +118,16 @@ linear_scan_bf16_kernel(LinearArgs a) {
   if (unit >= a.units) return;
   const int head = unit % a.H;
   const int T = a.T;
-  const int ntiles = (T + 15) >> 4;
+  const int bt = CKPT ? a.bt : 16;  // tokens per tile
+  const int ntiles = CKPT ? (T + bt - 1) / bt : (T + 15) >> 4;
   const int row0 = slice * ROWS;
+  // token of row r of tile j (T, just past every descriptor, for rows >= bt)
+  auto tokrow = [&](int j, int r) {
+    if constexpr (CKPT)
+      return r < bt ? j * bt + r : T;
+    else
+      return j * 16 + r;
+  };
 
   // ================================================================ loader
   // Barriers B_-2, B_-1, B_0 .. B_{ntiles-1}.  B_j (j >= 0) releases compute
@@ -137,11 +148,10 @@ linear_scan_bf16_kernel(LinearArgs a) {
     const int krow = lane >> 3, kpos = lane & 7;
     auto issue = [&](int j) {
       char* st = raw + (j % G::NST) * G::RAW;
-      const uint32_t tb = (uint32_t)j * 2048;
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
         const int r = 8 * n + krow;
-        const uint32_t off = tb + r * 128 + ((kpos ^ (r & 7)) << 4);
+        const uint32_t off = (uint32_t)tokrow(j, r) * 128 + ((kpos ^ (r & 7)) << 4);
         dma16(rk, st + n * 1024, off);
         dma16(rq, st + G::KB + n * 1024, off);
       }
@@ -150,10 +160,10 @@ linear_scan_bf16_kernel(LinearArgs a) {
         const int byte = n * 1024 + lane * 16;
         if (G::VB % 1024 == 0 || byte < G::VB) {
           const int tok = byte / (ROWS * 2), cb = byte % (ROWS * 2);
-          dma16(rv, st + 2 * G::KB + n * 1024, (uint32_t)(j * 16 + tok) * 128 + row0 * 2 + cb);
+          dma16(rv, st + 2 * G::KB + n * 1024, (uint32_t)tokrow(j, tok) * 128 + row0 * 2 + cb);
         }
       }
-      if (lane < 16) dma4(re, st + 2 * G::KB + G::VB, (uint32_t)(j * 16 + lane) * 4);
+      if (lane < 16) dma4(re, st + 2 * G::KB + G::VB, (uint32_t)tokrow(j, lane) * 4);
     };
     const int pro = ntiles < G::D + 2 ? ntiles : G::D + 2;
     for (int j = 0; j < pro; ++j) issue(j);
@@ -464,7 +474,8 @@ linear_scan_bf16_kernel(LinearArgs a) {
     // rows 4g..4g+3 of token c
     const f32x4 Z = mm_pre_t(gy, pc.att, R);
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Z), rz, zoff, 0, 2);
+    __builtin_amdgcn_raw_buffer_store_b128(
+        __builtin_bit_cast(u32x4, Z), rz, CKPT ? (uint32_t)((tokrow(j, c) * 64 + rbase + 4 * g) * 4) : zoff, 0, 2);
     zoff += 16 * 64 * 4;
 
     // ---- rank-16 update W_{j+1} = W_j + Gn_j K_j^T
@@ -626,7 +637,9 @@ hipError_t launch_linear_chunked(const LinearArgs& a, int P, int rows, hipStream
 }
 
 hipError_t launch_linear_bf16(const LinearArgs& a, int rows, hipStream_t s) {
-  if (a.w_ckpt) return a.b == 16 ? launch_rows<MODE_B16, 1, true>(a, rows, s) : hipErrorInvalidValue;
+  if (a.w_ckpt)
+    return a.b == 16 || (a.b < 16 && a.bt == a.b) ? launch_rows<MODE_B16, 1, true>(a, rows, s)
+                                                   : hipErrorInvalidValue;
   if (a.ring_depth == 1) return a.b == 16 ? launch_rows<MODE_B16, 1, false, 1>(a, rows, s)
                                           : hipErrorInvalidValue;
   if (a.b == 16) return launch_rows<MODE_B16, 1>(a, rows, s);

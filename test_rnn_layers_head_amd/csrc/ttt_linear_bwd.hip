@@ -1,4 +1,4 @@
-// Backward of the TTT-Linear scan (b = 16), gfx950.
+// Backward of the TTT-Linear scan (b | 16), gfx950.
 //
 // Method ("论文速览 | TTT", equinox-blog close reading of "Learning to
 // (Learn at Test Time)"): training differentiates through the inner loop;
@@ -37,7 +37,10 @@
 // iterations outside the sequence see zero inputs (their loads fall outside
 // the buffer descriptors), which leave the state unchanged, and their stores
 // fall outside the outputs; so every iteration issues the same memory
-// operations and the compiler's wait counts stay exact.  The adjoint state
+// operations and the compiler's wait counts stay exact.  Mini-batches of
+// b < 16 tokens each take a tile of their own, rows b..15 of which read as
+// zero tokens (eta = 0, so they leave the state and every other token's
+// outputs unchanged) and drop their outputs the same way.  The adjoint state
 // never leaves the chip.
 //
 // Products: 16x16x32 bf16 MFMA with fp32 accumulation.  K, Q, V are exact in
@@ -101,7 +104,7 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
   const int c = lane & 15, g = lane >> 4;
   const int s = wave & 3;  // rows 16 s .. 16 s + 15
   const int unit = blockIdx.x;
-  const int T = a.T, ntiles = (T + 15) >> 4;
+  const int T = a.T, bt = a.bt, ntiles = (T + bt - 1) / bt;
   const int niter = ntiles + 2;  // iteration k: chain tile k, outputs of tile k-1, finalize of k-2
   const size_t uoff = (size_t)unit * T * 64;
   if (ntiles == 0) {  // no tokens: dW0 = dW_T (or 0); w_ckpt may be NULL
@@ -116,9 +119,11 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
   }
   const s16x4 z4 = {0, 0, 0, 0};
   const __amdgpu_buffer_rsrc_t rdz = make_rsrc(a.dz + uoff, (uint32_t)T * 256);
-  // iteration-order tile k covers tokens 16 (ntiles - 1 - k) ..; tiles past
-  // either end read as zeros (their offsets fall outside the descriptors)
-  auto tok0 = [&](int k) { return (ntiles - 1 - k) * 16; };
+  // iteration-order tile k covers tokens bt (ntiles - 1 - k) ..; tiles past
+  // either end read as zeros (their offsets fall outside the descriptors),
+  // and so do rows r >= bt (token T: just past every descriptor)
+  auto tok0 = [&](int k) { return (ntiles - 1 - k) * bt; };
+  auto tk = [&](int t0, int r) { return r < bt ? t0 + r : T; };
   // one-hot selectors: B operand that picks column scol(m, c) out of a
   // natural-order chunk, for m even (sel[0]) and odd (sel[1])
   bf16x8 sel[2];
@@ -151,7 +156,7 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         z[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                   rdz, (uint32_t)((tok0(k) + 4 * g + r) * 64 + 16 * s + c) * 4, 0, 0));
+                   rdz, (uint32_t)(tk(tok0(k), 4 * g + r) * 64 + 16 * s + c) * 4, 0, 0));
     };
     // Sums the four slices' partials of one tile for column block s and
     // writes dQ, dK (slice 0 also deta).  q4p, k4p: Q, K of that tile at
@@ -188,12 +193,12 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
       const int col = scol(s, c);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const uint32_t off = (uint32_t)((t0 + 4 * g + r) * 64 + col) * 4;
+        const uint32_t off = (uint32_t)(tk(t0, 4 * g + r) * 64 + col) * 4;
         const float vq = dq[r], vk = dk[r];  // scalar copies: bit_cast of an element reads element 0
         st32(vq, rdq, off);
         st32(vk, rdk, off);
       }
-      st32(de, rde, (s == 0 && g == 0) ? (uint32_t)(t0 + c) * 4 : 0x80000000u);
+      st32(de, rde, (s == 0 && g == 0) ? (uint32_t)tk(t0, c) * 4 : 0x80000000u);
     };
 
     // Q, K of the two previous tiles at columns scol(s, c) (for finalize)
@@ -238,7 +243,7 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float gv = Gtr[r];
-          st32(gv, rdv, (uint32_t)((t0 + 4 * g + r) * 64 + 16 * s + c) * 4);
+          st32(gv, rdv, (uint32_t)(tk(t0, 4 * g + r) * 64 + 16 * s + c) * 4);
         }
         // tokens in lanes: Gn register r = [row 16s + 4g + r][t = c]
         f32x4 Pt = mfma_k32(ws0.hi, kc[0], f32x4{0, 0, 0, 0});
@@ -304,12 +309,12 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
         const int r = 8 * n + (lane >> 3);
-        const uint32_t vo = (uint32_t)(t0 + r) * 128 + (((lane & 7) ^ (r & 7)) << 4);
+        const uint32_t vo = (uint32_t)tk(t0, r) * 128 + (((lane & 7) ^ (r & 7)) << 4);
         dma16(rk, st + n * 1024, vo);
         dma16(rq, st + G::KB + n * 1024, vo);
         dma16(rv, st + 2 * G::KB + n * 1024, vo);
       }
-      if (lane < 16) dma4(re, st + 3 * G::KB, (uint32_t)(t0 + lane) * 4);
+      if (lane < 16) dma4(re, st + 3 * G::KB, (uint32_t)tk(t0, lane) * 4);
     };
     for (int k = 0; k < G::D; ++k) issue(k);
     wait_vmcnt<G::NI * (G::D - 1)>();  // tile 0 landed
@@ -334,7 +339,7 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
 #pragma unroll
     for (int m = 0; m < 4; ++m) p.w[m] = *(const f32x4*)(src + scol(m, 4 * g));
     p.z = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-              rdz, (uint32_t)((tok0(k) + c) * 64 + 16 * s + 4 * g) * 4, 0, 0));
+              rdz, (uint32_t)(tk(tok0(k), c) * 64 + 16 * s + 4 * g) * 4, 0, 0));
   };
   // partial sums over this slice's rows for tile p (iteration order)
   auto outputs = [&](int p, const Pf& pf) {
