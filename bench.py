@@ -462,9 +462,9 @@ def training_case(wl, steps, warmup, b=16):
 def mlp_training_case(wl, b, steps, warmup):
     """ttt_mlp_fwd_ckpt then ttt_mlp_bwd on one TTT-MLP workload, timed
     separately; dz is a seeded N(0, 0.01) draw.  bf16 inputs: the forward is
-    the dual-form scan with checkpoint stores (b | 16), the backward the
-    dual-form backward at b = 16 and the primal form (fp32 arithmetic, one
-    token at a time) otherwise."""
+    the dual-form scan with checkpoint stores, the backward the dual-form
+    backward for b | 16 (b < 16: one mini-batch per zero-padded tile) and the
+    primal form (fp32 arithmetic, one token at a time) otherwise."""
     import torch
     from test_rnn_layers_head_amd import inputs, ttt_mlp_bwd, ttt_mlp_fwd_ckpt
     x = inputs.make_inputs(wl)
@@ -483,17 +483,19 @@ def mlp_training_case(wl, b, steps, warmup):
     st = 2 * wl.hidden * wl.d * 4
     fb = mlp_alg_bytes(wl) + wl.units * nmb * st
     bb = mlp_bwd_alg_bytes(wl, b)
-    dual_bwd = wl.qkv_dtype == "bf16" and b == 16
+    dual_bwd = wl.qkv_dtype == "bf16" and 16 % b == 0
     return {"workload": wl.name, "b": b, "fwd_ckpt_us": kf, "bwd_us": kb,
             "fwd_alg_bytes": fb, "bwd_alg_bytes": bb,
             "fwd_hbm_frac": fb / (kf * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "bwd_hbm_frac": bb / (kb * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "train_token_heads_per_s": wl.token_heads / ((kf + kb) * 1e-6),
             **({"bwd_traffic": traffic_for("mlp_bwd", MLP_BWD_SOURCES, wl.name),
-                "bwd_sq": sq_for("mlp_bwd", MLP_BWD_SOURCES)} if dual_bwd else {}),
+                "bwd_sq": sq_for("mlp_bwd", MLP_BWD_SOURCES)} if dual_bwd and b == 16 else {}),
             "kernels": ("mlp_scan_kernel with checkpoint stores" if wl.qkv_dtype == "bf16" and
                         (16 % b == 0 or b % 16 == 0) else "mlp_primal_kernel (checkpoints)")
-                       + (" / mlp_bwd_kernel (dual form)" if dual_bwd else " / mlp_primal_bwd_kernel")}
+                       + (" / mlp_bwd_kernel (dual form" + (", one mini-batch per zero-padded tile)"
+                                                             if b < 16 else ")")
+                          if dual_bwd else " / mlp_primal_bwd_kernel")}
 
 
 def ln_training_case(wl, b, steps, warmup):

@@ -180,9 +180,13 @@ ttt_status_t ttt_mlp_ln_fwd(const void* q, const void* k, const void* v,
  * one; the forward keeps the state at the start of every mini-batch, the
  * kappa = T / b checkpoints, and the backward walks the mini-batches in
  * reverse).  Support: d = 64, bf16 or fp32 q/k/v, b dividing 16 or a
- * multiple of 16; else TTT_ERR_UNSUPPORTED.  bf16 with b = 16 runs the
- * dual-form kernels; every other case runs the primal-form kernels (one
- * token at a time, fp32 arithmetic, no sequence chunks).
+ * multiple of 16; else TTT_ERR_UNSUPPORTED.  bf16 with b | 16 runs the
+ * dual-form kernels of b = 16; for b < 16 each mini-batch takes a 16-token
+ * tile of its own whose other rows are zero tokens (eta = 0: they change
+ * neither the state nor the other tokens' outputs, and their own outputs are
+ * dropped), so the cost per token is 16 / b times that of b = 16.  b > 16 and
+ * fp32 q/k/v run the primal-form kernels (one token at a time, fp32
+ * arithmetic, no sequence chunks).  Sequence chunks: b = 16 only.
  *
  * ttt_linear_fwd_ckpt: ttt_linear_fwd plus
  *   w_ckpt : out [B][H][ceil(T/b)][d][d] fp32, the state before each
@@ -327,7 +331,7 @@ ttt_status_t ttt_mlp_fwd(const void* q, const void* k, const void* v,
  * every forward operation (the LayerNorm statistics, the LayerNorm VJP of
  * the inner gradient, the update, the output) in reverse order, mini-batch
  * by mini-batch from the checkpoints: for bf16 q/k/v with b = 16 in dual
- * form on the matrix unit, one wave per (batch, head) holding all 64 rows
+ * form on the matrix unit, one workgroup of four waves per (batch, head)
  * (fp32 factors as bf16 hi + lo halves, ~2^-16 relative per product);
  * otherwise token by token in fp32 arithmetic, one workgroup of 256
  * threads per (batch, head).  Outputs must not overlap each other or an
@@ -371,10 +375,12 @@ ttt_status_t ttt_linear_ln_bwd(const void* q, const void* k, const void* v,
  *   dq, dk, dv : [B][H][T][d];  deta : [B][H][T]
  *   dw1_0, dw2_0 : [B][H][hidden][d], [B][H][d][hidden], per unit.
  * The mini-batches are walked in reverse, each from its checkpoint.  bf16
- * q/k/v with b = 16 run the dual form: the mini-batch's forward is recomputed
+ * q/k/v with b | 16 run the dual form: the mini-batch's forward is recomputed
  * on MFMA and every product taken back in reverse (the adjoints of W1, W2
  * resident in registers; fp32 factors as bf16 hi + lo halves, ~2^-16
- * relative per product).  Other cases replay the mini-batch forward and take
+ * relative per product); for b < 16 each mini-batch takes a 16-token tile of
+ * its own, the other rows zero tokens (eta = 0: no effect on the state or
+ * the other tokens).  Other cases replay the mini-batch forward and take
  * its tokens back one by one in fp32, the gradient-point adjoints joining
  * the state adjoints at its first token.  Outputs must not overlap each
  * other or an input.  T = 0 writes dw*_0 = dw*_T (or zeros).  One workgroup

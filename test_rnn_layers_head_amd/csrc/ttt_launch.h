@@ -162,8 +162,9 @@ struct MlpBwdArgs {
   int T;
   int b;
 };
-// bf16 q/k/v with b = 16: the dual-form backward (one workgroup of 8 waves
-// per unit); otherwise the primal form token by token.
+// bf16 q/k/v with b | 16: the dual-form backward (one workgroup of 8 waves
+// per unit; for b < 16 one mini-batch per 16-token tile, its other rows
+// zero tokens); otherwise the primal form token by token.
 hipError_t launch_mlp_bwd(const MlpBwdArgs& a, bool f32in, hipStream_t s);
 hipError_t launch_mlp_bwd_primal(const MlpBwdArgs& a, bool f32in, hipStream_t s);
 

@@ -1,4 +1,4 @@
-// Backward of the TTT-MLP scan in dual form, bf16 Q/K/V, b = 16, gfx950.
+// Backward of the TTT-MLP scan in dual form, bf16 Q/K/V, b | 16, gfx950.
 //
 // Method ("论文速览 | TTT", equinox-blog close reading of "Learning to
 // (Learn at Test Time)"): the outer loop differentiates through the inner
@@ -20,6 +20,9 @@
 //   X2b = X2q Mb^T + A2'^T Gn2 + W2^T Yb,  Z1b += X2b * P1,
 //   dQ = W1^T Z1qb + K Ab,  dK = A1'^T Gn1 + Q Ab^T + W1^T Z1b,
 //   A1 = A1' + Z1qb Q^T + Z1b K^T,  A2 = A2' + Zb X2q^T + Gn2 Snb^T + Yb X2^T.
+// A mini-batch of b < 16 tokens takes a tile of its own whose rows b..15
+// read as zero tokens (eta = 0: they change neither the state nor the other
+// tokens' outputs) and drop their outputs.
 //
 // Work split: one workgroup of 8 waves per (batch, head) unit; wave w owns
 // the hidden units u in [32 w, 32 w + 32) (two 16-blocks): its rows of W1 and
@@ -104,6 +107,7 @@ __device__ __forceinline__ bf16x8 rows_twice(const char* tile, int g, int col) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+template <bool PAD>  // PAD: b < 16, one mini-batch per tile
 __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[L_TOTAL];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -111,7 +115,17 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
   const int unit = blockIdx.x;
   if (unit >= a.units) return;
   const int T = a.T;
-  const int ntiles = (T + 15) >> 4;
+  // tokens per tile: 16, or b < 16 with each mini-batch alone in a tile
+  // whose rows b..15 read as zero tokens (eta = 0: they change nothing) and
+  // drop their outputs (token T: just past every descriptor)
+  const int bt = PAD ? a.b : 16;
+  const int ntiles = PAD ? (T + bt - 1) / bt : (T + 15) >> 4;
+  auto tk = [&](int j, int r) {
+    if constexpr (PAD)
+      return r < bt ? j * bt + r : T;
+    else
+      return 16 * j + r;
+  };
   const int u0 = 32 * w;
   const size_t nst = (size_t)BHID * 64;
 
@@ -162,16 +176,19 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
     if (wu < 6) {
       const int n = wu & 1, r = 8 * n + (lane >> 3), kp = lane & 7;
       const uint32_t tb = (uint32_t)j * 2048;
-      const uint32_t off = wu < 4 ? tb + r * 128 + ((kp ^ (r & 7)) << 4) : tb + n * 1024 + lane * 16;
+      const uint32_t off = PAD ? (uint32_t)tk(j, r) * 128 + ((wu < 4 ? kp ^ (r & 7) : kp) << 4)
+                               : (wu < 4 ? tb + r * 128 + ((kp ^ (r & 7)) << 4) : tb + n * 1024 + lane * 16);
       dma16(rin, slot + (wu >> 1) * 2048 + n * 1024, off);
     } else {
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
         const int blk = 2 * (wu - 6) + n;
-        dma16(rin, slot + T_DZ + blk * 1024, (uint32_t)j * 4096 + blk * 1024 + lane * 16);
+        dma16(rin, slot + T_DZ + blk * 1024,
+              PAD ? (uint32_t)tk(j, 4 * blk + (lane >> 4)) * 256 + (lane & 15) * 16
+                  : (uint32_t)j * 4096 + blk * 1024 + lane * 16);
       }
     }
-    if (wu == 0 && lane < 16) dma4(reta, slot + T_ETA, (uint32_t)(j * 16 + lane) * 4);
+    if (wu == 0 && lane < 16) dma4(reta, slot + T_ETA, (uint32_t)tk(j, lane) * 4);
   };
 
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.dq + uoff, (uint32_t)T * 256);
@@ -182,7 +199,7 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x[k]), r,
-                                            (uint32_t)(((16 * j + 4 * g + k) * 64 + col) * 4), 0, 0);
+                                            (uint32_t)((tk(j, 4 * g + k) * 64 + col) * 4), 0, 0);
   };
 
   char* const w2n = smem + L_W2N + w * 8192 + lane * 16;
@@ -464,7 +481,7 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
         dv[r] = -Yb[r];
         ep[r] = row_sum16(G2b[r] * Eb[r]);
       }
-      if (16 * j + 4 * g < T) store_tile(rv, j, 16 * mi + c, dv);
+      if (tk(j, 4 * g) < T) store_tile(rv, j, 16 * mi + c, dv);
       if (c == 0) *(f32x4*)(smem + L_ETA + (mi * 16 + 4 * g) * 4) = ep;
       const Split4 ys = split4(Yb);
       *(uint4*)(smem + L_YBA + mi * 1024 + lane * 16) = pack_split(ys);
@@ -473,11 +490,11 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
     }
     wg_barrier();  // B4: Yb
 
-    if (w == 4 && lane < 16 && 16 * j + lane < T) {
+    if (w == 4 && lane < 16 && tk(j, lane) < T) {
       float s = 0.f;
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) s += *(const float*)(smem + L_ETA + (mi * 16 + lane) * 4);
-      a.deta[(size_t)unit * T + 16 * j + lane] = -2.f * s;
+      a.deta[(size_t)unit * T + tk(j, lane)] = -2.f * s;
     }
     // ================================== X2b, Z1b
     {
@@ -527,7 +544,7 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
         const Split4 abs_ = split4(Ab), abts = split4(AbT);
         dq = mfma_k32(cat44(abs_.hi, abs_.lo), rows_twice(Kt, g, sigc(m)), dq);   // + K Ab
         dk = mfma_k32(cat44(abts.hi, abts.lo), rows_twice(Qt, g, sigc(m)), dk);  // + Q Ab^T
-        if (16 * j + 4 * g < T) {
+        if (tk(j, 4 * g) < T) {
           store_tile(rq, j, sigc(m), dq);
           store_tile(rk, j, sigc(m), dk);
         }
@@ -584,8 +601,9 @@ __global__ void __launch_bounds__(BWV * 64) mlp_bwd_kernel(MlpBwdArgs a) {
 }  // namespace
 
 hipError_t launch_mlp_bwd(const MlpBwdArgs& a, bool f32in, hipStream_t s) {
-  if (f32in || a.b != 16) return launch_mlp_bwd_primal(a, f32in, s);
-  return launch(mlp_bwd_kernel, dim3(a.units), dim3(BWV * 64), s, a);
+  if (f32in || a.b > 16) return launch_mlp_bwd_primal(a, f32in, s);
+  if (a.b < 16) return launch(mlp_bwd_kernel<true>, dim3(a.units), dim3(BWV * 64), s, a);
+  return launch(mlp_bwd_kernel<false>, dim3(a.units), dim3(BWV * 64), s, a);
 }
 
 }  // namespace ttt
