@@ -49,7 +49,7 @@ MLP_BWD_SOURCES = ["ttt_mlp_bwd.hip", "ttt_mlp_ops.h", "ttt_device.h", "ttt_laun
 LN_BWD_SOURCES = ["ttt_linear_ln_bwd.hip", "ttt_mlp_ops.h", "ttt_device.h", "ttt_launch.h"]
 # kernel names as rocprofv3 reports them (the MLP scan's template arguments:
 # waves, sub-batches, checkpoint stores, LayerNorm wrapper, held gradient point)
-LN_SCAN_NAME = "linear_ln_scan_kernel<1, false>"  # one unit per workgroup, no checkpoint stores
+LN_SCAN_NAME = "linear_ln_scan_kernel<1, false, false>"  # one unit per workgroup, no checkpoint stores
 MLP_SCAN_NAME = "mlp_scan_kernel<8, false, false, false, false>"
 MLP_LN_SCAN_NAME = "mlp_scan_kernel<8, false, false, true, false>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")

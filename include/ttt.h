@@ -135,9 +135,12 @@ ttt_status_t ttt_linear_fwd(const void* q, const void* k, const void* v,
  * runs the dual form per 16-token tile (one workgroup per (batch, head)).
  * Below 16 tokens a mini-batch's gradients depend non-linearly, through the
  * LayerNorm, on the updates of earlier mini-batches in the same tile, which
- * a one-tile dual form cannot evaluate.  So b < 16 and fp32 inputs run the
- * primal form token by token in fp32 arithmetic (256 threads per
- * (batch, head)): exact, and slower per token.
+ * a one-tile dual form cannot evaluate; so bf16 with b < 16 gives each
+ * mini-batch a 16-token tile of its own, its other rows zero tokens (eta = 0:
+ * they change neither the state nor the other tokens' outputs, and their own
+ * outputs are dropped), at 16 / b times the cost per token.  fp32 inputs run
+ * the primal form token by token in fp32 arithmetic (256 threads per
+ * (batch, head)).
  */
 ttt_status_t ttt_linear_ln_fwd(const void* q, const void* k, const void* v,
                                const float* eta, const float* w0,
@@ -325,13 +328,14 @@ ttt_status_t ttt_mlp_fwd(const void* q, const void* k, const void* v,
  * and the LayerNorm parameters' adjoints dgamma, dbeta [B][H][d], per unit
  * (sum over the batch for the shared per-head parameters).
  * ttt_linear_ln_fwd_ckpt runs the kernel ttt_linear_ln_fwd picks (the
- * dual-form scan for bf16 q/k/v with 16 | b, else the primal form), which
+ * dual-form scan for bf16 q/k/v, else the primal form), which
  * also stores each mini-batch's starting state; z and w_out equal
  * ttt_linear_ln_fwd's bit for bit.  The backward applies the adjoint of
  * every forward operation (the LayerNorm statistics, the LayerNorm VJP of
  * the inner gradient, the update, the output) in reverse order, mini-batch
- * by mini-batch from the checkpoints: for bf16 q/k/v with b = 16 in dual
- * form on the matrix unit, one workgroup of four waves per (batch, head)
+ * by mini-batch from the checkpoints: for bf16 q/k/v with b | 16 in dual
+ * form on the matrix unit (b < 16: one mini-batch per zero-padded tile, as
+ * above), one workgroup of four waves per (batch, head)
  * (fp32 factors as bf16 hi + lo halves, ~2^-16 relative per product);
  * otherwise token by token in fp32 arithmetic, one workgroup of 256
  * threads per (batch, head).  Outputs must not overlap each other or an

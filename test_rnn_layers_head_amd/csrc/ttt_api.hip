@@ -199,10 +199,10 @@ ttt_status_t linear_ln_impl(const void* q, const void* k, const void* v, const f
   if (!(eps > 0.f) || eps > 3.0e38f)
     return fail(TTT_ERR_VALUE, "%s: eps=%g must be finite and > 0", fn, (double)eps);
   if (units == 0) return TTT_OK;
-  // bf16 with 16 | b and no checkpoints: the dual-form kernel; otherwise the
+  // bf16 with b | 16 or 16 | b: the dual-form scan (with checkpoint stores
+  // when asked; b < 16: one mini-batch per zero-padded tile); fp32: the
   // primal-form kernel
-  // bf16 with 16 | b: the dual-form scan (with checkpoint stores when asked)
-  const bool primal = dt != TTT_BF16 || b % 16 != 0;
+  const bool primal = dt != TTT_BF16 || (b > 16 && b % 16 != 0);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (T == 0) {

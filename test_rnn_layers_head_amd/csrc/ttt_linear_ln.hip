@@ -173,7 +173,11 @@ __device__ __forceinline__ f32x4 bf4(uint2 u) {
 // 0 = read from the arguments (other multiples of 16).  CKPT: also store
 // the state before every mini-batch (the checkpoints the backward reads),
 // straight from the compute waves' accumulators.
-template <int TPM, bool CKPT = false>
+// PAD (b < 16, TPM = 1): each b-token mini-batch takes a tile of its own whose
+// rows b..15 read as zero tokens (eta = 0: they change neither the state nor
+// the other tokens' outputs) and drop their outputs (token T: past every
+// descriptor): the b = 16 arithmetic at 16 / b times the tiles.
+template <int TPM, bool CKPT = false, bool PAD = false>
 __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearLnArgs la) {
   using G = LnGeom;
   const LinearArgs& a = la.s;
@@ -189,7 +193,15 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
   if (unit >= a.units) return;
   const int head = unit % a.H;
   const int T = a.T;
-  const int ntiles = (T + 15) >> 4;
+  const int bt = PAD ? a.b : 16;  // tokens per tile
+  const int ntiles = PAD ? (T + bt - 1) / bt : (T + 15) >> 4;
+  // token of row r of tile t
+  auto tokrow = [&](int t, int r) {
+    if constexpr (PAD)
+      return r < bt ? t * bt + r : T;
+    else
+      return t * 16 + r;
+  };
 
   // Z through a range-checked buffer (rows past T are dropped).  A token's
   // 256-byte row spans the four compute waves (16 rows each), so they stage
@@ -204,7 +216,7 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
       const int tk = tok0 + 4 * k + g;
       const f32x4 Z = *(const f32x4*)(zst + (t & 1) * G::ZT + tk * G::ZROW + c * 16);
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Z), rz,
-                                             (uint32_t)((t * 16 + tk) * 256 + c * 16), 0, 2);
+                                             (uint32_t)(tokrow(t, tk) * 256 + c * 16), 0, 2);
     }
   };
 
@@ -228,12 +240,14 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
         const int r = 8 * n + krow;
-        const uint32_t off = tb + r * 128 + ((kpos ^ (r & 7)) << 4);
+        const uint32_t off = PAD ? (uint32_t)tokrow(j, r) * 128 + ((kpos ^ (r & 7)) << 4)
+                                 : tb + r * 128 + ((kpos ^ (r & 7)) << 4);
         dma16(rk, st + n * 1024, off);
         dma16(rq, st + G::KB + n * 1024, off);
-        dma16(rv, st + 2 * G::KB + n * 1024, tb + n * 1024 + lane * 16);  // V unswizzled
+        dma16(rv, st + 2 * G::KB + n * 1024,  // V unswizzled
+              PAD ? (uint32_t)tokrow(j, r) * 128 + kpos * 16 : tb + n * 1024 + lane * 16);
       }
-      if (lane < 16) dma4(re, st + 2 * G::KB + G::VB, (uint32_t)(j * 16 + lane) * 4);
+      if (lane < 16) dma4(re, st + 2 * G::KB + G::VB, (uint32_t)tokrow(j, lane) * 4);
     };
     const int pro = ntiles < G::D + 1 ? ntiles : G::D + 1;
     for (int j = 0; j < pro; ++j) issue(j);
@@ -461,8 +475,9 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
   };
   // the last tile directly (no barrier follows it)
   auto store_z = [&](int t, const float S[8], const f32x4& O, const f32x4& QB) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, z_of(S, O, QB)), rz,
-                                           zlane + (uint32_t)t * (16 * 64 * 4), 0, 2);
+    __builtin_amdgcn_raw_buffer_store_b128(
+        __builtin_bit_cast(u32x4, z_of(S, O, QB)), rz,
+        PAD ? (uint32_t)((tokrow(t, c) * 64 + rbase + 4 * g) * 4) : zlane + (uint32_t)t * (16 * 64 * 4), 0, 2);
   };
 
   wg_barrier_pinned();  // B_{-2}: raw tiles 0 and 1 are in LDS
@@ -672,6 +687,9 @@ __global__ void __launch_bounds__(LnGeom::THREADS) linear_ln_scan_kernel(LinearL
 
 hipError_t launch_linear_ln(const LinearLnArgs& a, hipStream_t s) {
   const dim3 grid(a.s.units), block(LnGeom::THREADS);
+  if (a.s.b < 16)  // one mini-batch per zero-padded tile
+    return a.s.w_ckpt ? launch(linear_ln_scan_kernel<1, true, true>, grid, block, s, a)
+                      : launch(linear_ln_scan_kernel<1, false, true>, grid, block, s, a);
   if (a.s.w_ckpt) {
     switch (a.s.b) {
       case 16: return launch(linear_ln_scan_kernel<1, true>, grid, block, s, a);

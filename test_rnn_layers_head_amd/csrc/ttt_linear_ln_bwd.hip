@@ -76,6 +76,10 @@ __device__ __forceinline__ Split8 i_operand(f32x4 x0, f32x4 x1, bf16x8 itr, cons
   return split8_mfma(transpose16(x0, itr), transpose16(x1, itr), ns);
 }
 
+// PAD: b < 16, each b-token mini-batch alone in a tile whose rows b..15 read
+// as zero tokens (eta = 0: they change neither the state nor the other
+// tokens' outputs) and drop their outputs (token T: past every descriptor).
+template <bool PAD>
 __global__ void __launch_bounds__(256) linear_ln_bwd_kernel(LinearLnBwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[L_TOTAL];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -84,7 +88,14 @@ __global__ void __launch_bounds__(256) linear_ln_bwd_kernel(LinearLnBwdArgs a) {
   if (unit >= a.units) return;
   const int head = unit % a.H;
   const int T = a.T;
-  const int ntiles = (T + 15) >> 4;
+  const int bt = PAD ? a.b : 16;  // tokens per tile
+  const int ntiles = PAD ? (T + bt - 1) / bt : (T + 15) >> 4;
+  auto tk = [&](int j, int r) {
+    if constexpr (PAD)
+      return r < bt ? j * bt + r : T;
+    else
+      return 16 * j + r;
+  };
   const float eps = a.eps;
 
   bf16x8 itr, negI;
@@ -146,20 +157,25 @@ __global__ void __launch_bounds__(256) linear_ln_bwd_kernel(LinearLnBwdArgs a) {
   const __amdgpu_buffer_rsrc_t rin = make_rsrc(src + uoff / 64 * srow, (uint32_t)T * srow);
   const __amdgpu_buffer_rsrc_t reta = make_rsrc(a.eta + (size_t)unit * T, w == 0 ? (uint32_t)T * 4 : 0u);
   const int npiece = w == 3 ? 4 : 2;
-  uint32_t pofs[4];  // piece n's offset within the tile
+  uint32_t pofs[4];  // piece n's offset within the tile (PAD: within its token row)
+  int prow[4];       // PAD: the token row of piece n
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const int r = 8 * n + (lane >> 3), kp = lane & 7;
     pofs[n] = w < 2 ? (uint32_t)(r * 128 + ((kp ^ (r & 7)) << 4)) : (uint32_t)(n * 1024 + lane * 16);
+    prow[n] = w == 3 ? 4 * n + (lane >> 4) : r;
+    if constexpr (PAD) pofs[n] = w < 2 ? (uint32_t)((kp ^ (r & 7)) << 4) : (uint32_t)((lane * 16) % srow);
   }
   uint4v pf[4];
   float pfe;
   auto fetch = [&](int j) {
     const uint32_t tb = (uint32_t)j * 16 * srow;
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
-      pf[n] = __builtin_amdgcn_raw_buffer_load_b128(rin, n < npiece ? tb + pofs[n] : 0x80000000u, 0, 0);
-    pfe = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(reta, (uint32_t)(j * 16 + (lane & 15)) * 4, 0, 0));
+    for (int n = 0; n < 4; ++n) {
+      const uint32_t off = PAD ? (uint32_t)tk(j, prow[n]) * srow + pofs[n] : tb + pofs[n];
+      pf[n] = __builtin_amdgcn_raw_buffer_load_b128(rin, n < npiece ? off : 0x80000000u, 0, 0);
+    }
+    pfe = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(reta, (uint32_t)tk(j, lane & 15) * 4, 0, 0));
   };
   auto stash = [&](int j) {
     char* dst = smem + (j & 1) * RAWB + w * 2048 + lane * 16;  // T_K, T_Q, T_V, T_DZ = 2048 w
@@ -172,12 +188,12 @@ __global__ void __launch_bounds__(256) linear_ln_bwd_kernel(LinearLnBwdArgs a) {
   const __amdgpu_buffer_rsrc_t ok = make_rsrc(a.dk + uoff, (uint32_t)T * 256);
   const __amdgpu_buffer_rsrc_t ov = make_rsrc(a.dv + uoff, (uint32_t)T * 256);
   const __amdgpu_buffer_rsrc_t odeta = make_rsrc(a.deta + (size_t)unit * T, (uint32_t)T * 4);
-  // lane (c, g) stores [token 16 j + 4g + r][col]; stores past T fall outside
+  // lane (c, g) stores [row 4g + r of tile j][col]; stores past T fall outside
   auto store_tile = [&](__amdgpu_buffer_rsrc_t r, int j, int col, f32x4 x) {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x[k]), r,
-                                            (uint32_t)(((16 * j + 4 * g + k) * 64 + col) * 4), 0, 0);
+                                            (uint32_t)((tk(j, 4 * g + k) * 64 + col) * 4), 0, 0);
   };
 
   // this wave's column block of the checkpoint of tile t
@@ -391,7 +407,7 @@ __global__ void __launch_bounds__(256) linear_ln_bwd_kernel(LinearLnBwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-de[r]), odeta,
-                                                (uint32_t)(16 * j + 4 * g + r) * 4, 0, 0);
+                                                (uint32_t)tk(j, 4 * g + r) * 4, 0, 0);
       }
       f32x4 Yhb[4];
 #pragma unroll
@@ -509,8 +525,9 @@ __global__ void __launch_bounds__(256) linear_ln_bwd_kernel(LinearLnBwdArgs a) {
 }  // namespace
 
 hipError_t launch_linear_ln_bwd(const LinearLnBwdArgs& a, bool f32in, hipStream_t s) {
-  if (f32in || a.b != 16) return launch_linear_ln_primal_bwd(a, f32in, s);
-  return launch(linear_ln_bwd_kernel, dim3(a.units), dim3(256), s, a);
+  if (f32in || a.b > 16) return launch_linear_ln_primal_bwd(a, f32in, s);
+  if (a.b < 16) return launch(linear_ln_bwd_kernel<true>, dim3(a.units), dim3(256), s, a);
+  return launch(linear_ln_bwd_kernel<false>, dim3(a.units), dim3(256), s, a);
 }
 
 }  // namespace ttt

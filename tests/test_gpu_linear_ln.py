@@ -74,9 +74,11 @@ def small(B, H, T, seed):
     return inputs.make_inputs(wl)
 
 
-@pytest.mark.parametrize("b", [16, 32, 48, 64])
+@pytest.mark.parametrize("b", [1, 4, 8, 16, 32, 48, 64])
 @pytest.mark.parametrize("T", [1, 15, 16, 37, 130])
 def test_small_parity(b, T):
+    """bf16 with 16 | b: the dual-form scan; with b < 16 the same scan, one
+    mini-batch per 16-token tile whose other rows are zero tokens."""
     x = small(2, 3, T, seed=300 + T + b)
     z, w = gu.run_linear_ln(x, b)
     zr, wr = gu.oracle_linear_ln(x, b)
