@@ -418,7 +418,8 @@ def training_case(wl, steps, warmup, b=16):
     separately; dz is a seeded N(0, 0.01) draw.  Where both take sequence
     chunks, the single-pass backward is timed beside them.  bf16 with b = 16
     runs the dual-form kernels, with b < 16 the same kernels with one
-    mini-batch per zero-padded tile, other cases the primal-form ones."""
+    mini-batch per zero-padded tile, with b > 16 the dual-form forward and
+    the primal-form backward; fp32 inputs the primal-form kernels."""
     import torch
     from test_rnn_layers_head_amd import (inputs, ttt_linear_bwd, ttt_linear_fwd_ckpt,
                                           ttt_linear_fwd_plan)
@@ -443,8 +444,10 @@ def training_case(wl, steps, warmup, b=16):
     bb = bwd_alg_bytes(wl, b)
     chunks = ttt_linear_fwd_plan(wl.B, wl.H, wl.T, b)[1]
     extra = {"seq_chunks": chunks}
-    if b > 16 or wl.qkv_dtype != "bf16":
+    if wl.qkv_dtype != "bf16":
         extra["kernels"] = "linear_primal_ckpt_kernel / linear_primal_bwd_kernel"
+    elif b > 16:
+        extra["kernels"] = "linear_scan_bf16_kernel with checkpoint stores / linear_primal_bwd_kernel"
     else:
         extra["kernels"] = ("linear_scan_bf16_kernel with checkpoint stores / linear_bwd_kernel"
                             + (" (one mini-batch per zero-padded tile)" if b < 16 else ""))

@@ -187,9 +187,11 @@ ttt_status_t ttt_mlp_ln_fwd(const void* q, const void* k, const void* v,
  * dual-form kernels of b = 16; for b < 16 each mini-batch takes a 16-token
  * tile of its own whose other rows are zero tokens (eta = 0: they change
  * neither the state nor the other tokens' outputs, and their own outputs are
- * dropped), so the cost per token is 16 / b times that of b = 16.  b > 16 and
- * fp32 q/k/v run the primal-form kernels (one token at a time, fp32
- * arithmetic, no sequence chunks).  Sequence chunks: b = 16 only.
+ * dropped), so the cost per token is 16 / b times that of b = 16.  With
+ * b > 16 the checkpointing forwards are the dual-form scans and the backward
+ * kernels the primal form; fp32 q/k/v run the primal-form kernels (one token
+ * at a time, fp32 arithmetic, no sequence chunks).  Sequence chunks: b = 16
+ * only.
  *
  * ttt_linear_fwd_ckpt: ttt_linear_fwd plus
  *   w_ckpt : out [B][H][ceil(T/b)][d][d] fp32, the state before each

@@ -144,9 +144,9 @@ ttt_status_t linear_impl(const void* q, const void* k, const void* v, const floa
   ttt_status_t st = check_common(fn, dt, w0_per_batch, B, H, T, d, b, in, 5, out,
                                  w_ckpt ? 3 : 2, pairs, 1, T > 0);
   if (st != TTT_OK || units == 0) return st;
-  // checkpoints for b > 16 or fp32 inputs: the primal-form kernel (bf16
-  // with b < 16: the b = 16 kernel, one mini-batch per zero-padded tile)
-  const bool ck_primal = w_ckpt && (dt != TTT_BF16 || b > 16);
+  // checkpoints for fp32 inputs: the primal-form kernel (bf16 with b < 16:
+  // the b = 16 kernel, one mini-batch per zero-padded tile)
+  const bool ck_primal = w_ckpt && dt != TTT_BF16;
   // chunks: 0 = automatic, 1 = one pass, P >= 2 = P sequence chunks
   int P = chunks;
   if (P == 0) P = default_chunks(dt, b, units, T);

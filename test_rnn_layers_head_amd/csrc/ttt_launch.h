@@ -38,7 +38,7 @@ struct LinearArgs {
   int T;
   int b;
   // optional: the state at the start of every mini-batch,
-  // [units][ceil(T / b)][64][64] (bf16 inputs, b | 16)
+  // [units][ceil(T / b)][64][64] (bf16 inputs)
   float* w_ckpt = nullptr;
   // Passes of the chunked scan (bf16, b = 16; defaults: the plain scan).
   // z == nullptr: no outputs (Q is not read either).

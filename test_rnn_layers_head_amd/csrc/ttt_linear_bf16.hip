@@ -87,8 +87,9 @@ struct Geom {
 // TPM: tiles per mini-batch when it is fixed at compile time (b = 32, 64),
 // so a tile's position inside its mini-batch costs nothing; 0 = read from
 // the arguments (other multiples of 16).  Unused below b = 16.
-// CKPT (b | 16): also store the state at the start of every tile, the
-// checkpoints the backward pass reads; for b < 16 each b-token mini-batch
+// CKPT: also store the state at the start of every mini-batch, the
+// checkpoints the backward pass reads (b = 16: every tile; 16 | b: every
+// b / 16 tiles); for b < 16 each b-token mini-batch
 // takes a tile of its own (a.bt = b), rows b..15 reading as zero tokens
 // (eta = 0 leaves the state and the other tokens' outputs unchanged) and
 // dropping their outputs: the b = 16 arithmetic on padded tiles.
@@ -326,6 +327,7 @@ linear_scan_bf16_kernel(LinearArgs a) {
       W[m] = *(const f32x4*)(w0 + (rbase + c) * 64 + 32 * (m >> 1) + 8 * g + 4 * (m & 1));
   }
   const int tpm = MODE != MODE_MULTI ? 1 : (TPM > 0 ? TPM : (a.b >> 4));  // tiles per mini-batch
+  const int nmb = MODE == MODE_MULTI ? (T + a.b - 1) / a.b : ntiles;        // mini-batches (checkpoints)
   const NegSel ns = make_negsel(c, g);
   // -I on the 16 V columns of this wave: X = -V_block lands in accumulator
   // layout when V's rows are the A-operand (slots 16..31 are unused).
@@ -410,29 +412,32 @@ linear_scan_bf16_kernel(LinearArgs a) {
     load_prep(pn, prep + ((j + 1) & 1) * G::PREP);
     load_raw(rn, raw + ((j + 2) % G::NST) * G::RAW, raw + ((j + 1) % G::NST) * G::RAW);
     __builtin_amdgcn_sched_barrier(0);  // the reads go out first
-    if constexpr (CKPT) {  // W_j, the state before tile j
-      // through this wave's LDS tile, so that each store writes 4 whole rows
-      // (1 KB of consecutive memory), nontemporally
-      char* const ct = smem + G::LDS + wave * CK_TILE;
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        *(f32x4*)(ct + (c * 68 + 32 * (m >> 1) + 8 * g + 4 * (m & 1)) * 4) = W[m];
-      const __amdgpu_buffer_rsrc_t rc =
-          make_rsrc(a.w_ckpt + ((size_t)unit * ntiles + j) * 4096 + __builtin_amdgcn_readfirstlane(rbase) * 64,
-                    16u * 64u * 4u);  // (rbase pinned to a scalar register: a uniform descriptor)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int row = (lane >> 4) + 4 * kk, col = 4 * (lane & 15);
-        const f32x4 v = *(const f32x4*)(ct + (row * 68 + col) * 4);
-        typedef unsigned int u32x4c __attribute__((ext_vector_type(4)));
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4c, v), rc,
-                                               (uint32_t)((row * 64 + col) * 4), 0, 2);
-      }
-    }
     constexpr int pos = decltype(POS)::value;
     const bool new_mb = MODE != MODE_MULTI || (pos >= 0 ? pos == 0 : (j % tpm) == 0);
     const bool next_new_mb =
         MODE != MODE_MULTI || (pos >= 0 ? (pos + 1) % (TPM > 0 ? TPM : 1) == 0 : ((j + 1) % tpm) == 0);
+    if constexpr (CKPT) {  // W_j, the state before mini-batch j / tpm, when one starts
+      if (new_mb) {
+        // through this wave's LDS tile, so that each store writes 4 whole rows
+        // (1 KB of consecutive memory), nontemporally
+        char* const ct = smem + G::LDS + wave * CK_TILE;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          *(f32x4*)(ct + (c * 68 + 32 * (m >> 1) + 8 * g + 4 * (m & 1)) * 4) = W[m];
+        const int mb = MODE == MODE_MULTI ? j / tpm : j;
+        const __amdgpu_buffer_rsrc_t rc =
+            make_rsrc(a.w_ckpt + ((size_t)unit * nmb + mb) * 4096 + __builtin_amdgcn_readfirstlane(rbase) * 64,
+                      16u * 64u * 4u);  // (rbase pinned to a scalar register: a uniform descriptor)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int row = (lane >> 4) + 4 * kk, col = 4 * (lane & 15);
+          const f32x4 v = *(const f32x4*)(ct + (row * 68 + col) * 4);
+          typedef unsigned int u32x4c __attribute__((ext_vector_type(4)));
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4c, v), rc,
+                                                 (uint32_t)((row * 64 + col) * 4), 0, 2);
+        }
+      }
+    }
 
     // ---- serial chain: X_j = P_j - V_j, then Gn_j = 2 eta (v - p).
     // (gp is zero at j = 0; within a b > 16 mini-batch P keeps its gradient
@@ -637,9 +642,13 @@ hipError_t launch_linear_chunked(const LinearArgs& a, int P, int rows, hipStream
 }
 
 hipError_t launch_linear_bf16(const LinearArgs& a, int rows, hipStream_t s) {
-  if (a.w_ckpt)
-    return a.b == 16 || (a.b < 16 && a.bt == a.b) ? launch_rows<MODE_B16, 1, true>(a, rows, s)
-                                                   : hipErrorInvalidValue;
+  if (a.w_ckpt) {
+    if (a.b == 16 || (a.b < 16 && a.bt == a.b)) return launch_rows<MODE_B16, 1, true>(a, rows, s);
+    if (a.b == 32) return launch_rows<MODE_MULTI, 2, true>(a, rows, s);
+    if (a.b == 64) return launch_rows<MODE_MULTI, 4, true>(a, rows, s);
+    if (a.b > 16 && a.b % 16 == 0) return launch_rows<MODE_MULTI, 0, true>(a, rows, s);
+    return hipErrorInvalidValue;
+  }
   if (a.ring_depth == 1) return a.b == 16 ? launch_rows<MODE_B16, 1, false, 1>(a, rows, s)
                                           : hipErrorInvalidValue;
   if (a.b == 16) return launch_rows<MODE_B16, 1>(a, rows, s);
