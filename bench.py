@@ -447,7 +447,8 @@ def training_case(wl, steps, warmup, b=16):
     if wl.qkv_dtype != "bf16":
         extra["kernels"] = "linear_primal_ckpt_kernel / linear_primal_bwd_kernel"
     elif b > 16:
-        extra["kernels"] = "linear_scan_bf16_kernel with checkpoint stores / linear_primal_bwd_kernel"
+        extra["kernels"] = ("linear_scan_bf16_kernel with checkpoint stores / linear_bwd_kernel<true> "
+                            "(gradient point held across b / 16 tiles)")
     else:
         extra["kernels"] = ("linear_scan_bf16_kernel with checkpoint stores / linear_bwd_kernel"
                             + (" (one mini-batch per zero-padded tile)" if b < 16 else ""))
@@ -1041,6 +1042,8 @@ def main():
         extras[f"train-{w5.name}"] = training_case(w5, 3, 2)
         log(f"[bench] forward with checkpoints + backward, {wl.name}, b = 4 (padded tiles)")
         extras[f"train-{wl.name}_b4"] = training_case(wl, 2, 1, b=4)
+        log(f"[bench] forward with checkpoints + backward, {wl.name}, b = 64 (gradient point held)")
+        extras[f"train-{wl.name}_b64"] = training_case(wl, 5, 2, b=64)
         w7 = inputs.workload(7)
         log(f"[bench] forward with checkpoints + backward, {w7.name}")
         extras[f"train-{w7.name}"] = ln_training_case(w7, 16, 2, 1)

@@ -188,7 +188,11 @@ ttt_status_t ttt_mlp_ln_fwd(const void* q, const void* k, const void* v,
  * tile of its own whose other rows are zero tokens (eta = 0: they change
  * neither the state nor the other tokens' outputs, and their own outputs are
  * dropped), so the cost per token is 16 / b times that of b = 16.  With
- * b > 16 the checkpointing forwards are the dual-form scans and the backward
+ * b > 16 the checkpointing forwards are the dual-form scans; the TTT-Linear
+ * backward is the b = 16 kernel with the gradient point held across b / 16
+ * tiles (its adjoint kept apart and added at each mini-batch start, and the
+ * running state of each tile rebuilt in reverse from the checkpoints, the
+ * last mini-batch's end state first), the LayerNorm and TTT-MLP backward
  * kernels the primal form; fp32 q/k/v run the primal-form kernels (one token
  * at a time, fp32 arithmetic, no sequence chunks).  Sequence chunks: b = 16
  * only.

@@ -165,7 +165,7 @@ ttt_status_t linear_impl(const void* q, const void* k, const void* v, const floa
     a.ring_depth = ring_depth;
     if (w_ckpt && b < 16) a.bt = b;
     if (ck_primal)
-      e = ttt::launch_linear_primal_ckpt(a, dt == TTT_F32, s);
+      e = ttt::launch_linear_primal_ckpt(a, s);
     else if (P > 1)
       e = ttt::launch_linear_chunked(a, P, rows ? rows : auto_rows(units * P), s);
     else
@@ -399,9 +399,10 @@ ttt_status_t linear_bwd_impl(const void* q, const void* k, const void* v, const 
   if (!supported_b(b))
     return fail(TTT_ERR_UNSUPPORTED, "%s: mini-batch b=%d unsupported (need b | 16 or 16 | b)", fn, b);
   // bf16 with b = 16: the dual-form kernel (and its sequence chunks); bf16
-  // with b < 16: the same kernel, one mini-batch per zero-padded tile; b > 16
-  // or fp32 inputs: the primal-form kernel, one pass
-  const bool primal = dt != TTT_BF16 || b > 16;
+  // with b < 16: the same kernel, one mini-batch per zero-padded tile; bf16
+  // with b > 16: the same kernel with the gradient point held across b / 16
+  // tiles; fp32 inputs: the primal-form kernel, one pass
+  const bool primal = dt != TTT_BF16;
   if ((primal || b != 16) && chunks > 1)
     return fail(TTT_ERR_UNSUPPORTED, "%s: seq_chunks=%d needs bf16 q/k/v and b = 16", fn, chunks);
   if (seq >= ((int64_t)1 << 31))
@@ -435,10 +436,11 @@ ttt_status_t linear_bwd_impl(const void* q, const void* k, const void* v, const 
   hipError_t e;
   if (primal) {
     ttt::LinearPrimalBwdArgs a{q, k, v, eta, w_ckpt, dz, dw_T, dq, dk, dv, deta, dw0, (int)units, T, b};
-    e = ttt::launch_linear_primal_bwd(a, dt == TTT_F32, (hipStream_t)stream);
+    e = ttt::launch_linear_primal_bwd(a, (hipStream_t)stream);
   } else {
     ttt::LinearBwdArgs a{q, k, v, eta, w_ckpt, dz, dw_T, dq, dk, dv, deta, dw0, (int)units, H, T};
     a.bt = b < 16 ? b : 16;
+    a.tpm = b > 16 ? b / 16 : 1;
     e = P > 1 ? ttt::launch_linear_bwd_chunked(a, P, auto_rows(units * P), (hipStream_t)stream)
               : ttt::launch_linear_bwd(a, (hipStream_t)stream);
   }

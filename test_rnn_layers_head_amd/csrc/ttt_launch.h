@@ -174,7 +174,7 @@ struct LinearBwdArgs {
   const void* k;
   const void* v;
   const float* eta;      // [units][T]
-  const float* w_ckpt;   // [units][ceil(T/bt)][64][64]: W at every tile start
+  const float* w_ckpt;   // [units][ceil(T/bt)][64][64]: W at every tile start (tpm = 1)
   const float* dz;       // [units][T][64]
   const float* dw_T;     // [units][64][64] or NULL
   float* dq;             // [units][T][64]
@@ -193,6 +193,10 @@ struct LinearBwdArgs {
   // alone in a tile whose other rows read as zero tokens (eta = 0: no
   // contribution to the state) and whose outputs there are dropped.
   int bt = 16;
+  // Mini-batches of 16 tpm tokens (tpm > 1): the gradient point is held
+  // across tpm tiles; w_ckpt then holds one state per mini-batch,
+  // [units][ceil(T / (16 tpm))][64][64].
+  int tpm = 1;
 };
 hipError_t launch_linear_bwd(const LinearBwdArgs& a, hipStream_t s);
 
@@ -216,8 +220,8 @@ struct LinearPrimalBwdArgs {
   int T;
   int b;
 };
-hipError_t launch_linear_primal_ckpt(const LinearArgs& a, bool f32in, hipStream_t s);
-hipError_t launch_linear_primal_bwd(const LinearPrimalBwdArgs& a, bool f32in, hipStream_t s);
+hipError_t launch_linear_primal_ckpt(const LinearArgs& a, hipStream_t s);  // fp32 q/k/v
+hipError_t launch_linear_primal_bwd(const LinearPrimalBwdArgs& a, hipStream_t s);  // fp32 q/k/v
 // The backward in P sequence chunks of T / P tokens (a multiple of 16, at
 // least 192): the chunks' forward maps, their backward from a zero end
 // adjoint, a serial combine over the chunks, then every chunk from its end

@@ -43,6 +43,20 @@
 // outputs unchanged) and drop their outputs the same way.  The adjoint state
 // never leaves the chip.
 //
+// Mini-batches of b = 16 n tokens (n > 1, HOLD): every gradient of a
+// mini-batch is taken at its start state W0 (§3.5), so each 16-token tile t
+// has E = W0 K - V, G = 2 E D, Z = W_t Q - G A, W_{t+1} = W_t - G K^T with
+// W_t the running state.  Backward per tile, Wb' the adjoint of W_{t+1}:
+//   Gn, Gt, Ab, dV and deta as above;  dQ = W_t^T Zb + K Ab;
+//   dK = -W0^T Gt + Q Ab^T - Wb'^T G;  Wb = Wb' + Zb Q^T, and -Gt K^T goes
+//   to the gradient point's adjoint H, added to Wb at the mini-batch start.
+// The chain waves keep H in four more accumulators.  The output waves need
+// W_t for dQ: they rebuild it in reverse, W_t = W_{t+1} + G K^T with the
+// tile's own G, restarting from the exact checkpoint at every mini-batch
+// start (the state the next tile in reverse order ends with); the last
+// mini-batch starts from W_T = W0 - sum G K^T over its tiles, formed before
+// the loop.  The checkpoints are one per mini-batch.
+//
 // Products: 16x16x32 bf16 MFMA with fp32 accumulation.  K, Q, V are exact in
 // bf16; fp32 operands (states, dz, A, G, Gt, Ab) enter as hi + lo bf16 pairs
 // and the three significant products (hi*hi, hi*lo, lo*hi) are kept, about
@@ -97,6 +111,7 @@ __device__ __forceinline__ f32x4 bf4(uint2 u) {
                __builtin_bit_cast(float, u.y << 16), __builtin_bit_cast(float, u.y & 0xffff0000u)};
 }
 
+template <bool HOLD>
 __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdArgs a) {
   using G = BwdGeom;
   __shared__ __attribute__((aligned(16))) char smem[G::LDS];
@@ -144,7 +159,9 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
     };
     // Wr[m] register r = Wb[row 16 s + c][scol(m, 4g + r)]
-    f32x4 Wr[4];
+    f32x4 Wr[4], Hr[4];  // Hr: the gradient point's adjoint (HOLD)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) Hr[m] = f32x4{0, 0, 0, 0};
     {
       const float* dwT = a.dw_T ? a.dw_T + (size_t)unit * a.dw_stride + (16 * s + c) * 64 : nullptr;
 #pragma unroll
@@ -275,9 +292,24 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
               q4a = make_uint2((q4.x & keep) | (q4a.x & ~keep), (q4.y & keep) | (q4a.y & ~keep));
               k4a = make_uint2((k4.x & keep) | (k4a.x & ~keep), (k4.y & keep) | (k4a.y & ~keep));
             }
-            const bf16x8 qk = cat8(q4, make_uint2(k4.x ^ 0x80008000u, k4.y ^ 0x80008000u));
-            Wr[m] = mfma_k32(qk, zgh, Wr[m]);
-            Wr[m] = mfma_k32(qk, zgl, Wr[m]);
+            const uint2 k4n = make_uint2(k4.x ^ 0x80008000u, k4.y ^ 0x80008000u);
+            if constexpr (HOLD) {  // Wb' + Zb Q^T here, -Gt K^T into H
+              Wr[m] = mfma_k32(cat8(q4, q4), cat44(zrs.hi, zrs.lo), Wr[m]);
+              Hr[m] = mfma_k32(cat8(k4n, k4n), cat44(gts.hi, gts.lo), Hr[m]);
+            } else {
+              const bf16x8 qk = cat8(q4, k4n);
+              Wr[m] = mfma_k32(qk, zgh, Wr[m]);
+              Wr[m] = mfma_k32(qk, zgl, Wr[m]);
+            }
+          }
+        }
+        if constexpr (HOLD) {
+          if ((ntiles - 1 - k) % a.tpm == 0) {  // a mini-batch start: W0 is this state
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              Wr[m] += Hr[m];
+              Hr[m] = f32x4{0, 0, 0, 0};
+            }
           }
         }
       }
@@ -333,14 +365,67 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
     f32x4 w[4];
     f32x4 z;
   };
+  const int nck = HOLD ? (ntiles + a.tpm - 1) / a.tpm : ntiles;  // checkpoints per unit
   auto pload = [&](int k, Pf& p) {
     const int kc = k < 0 ? 0 : (k < ntiles ? k : ntiles - 1);
-    const float* src = a.w_ckpt + ((size_t)unit * ntiles + (ntiles - 1 - kc)) * 4096 + (16 * s + c) * 64;
+    const int ci = HOLD ? (ntiles - 1 - kc) / a.tpm : ntiles - 1 - kc;
+    const float* src = a.w_ckpt + ((size_t)unit * nck + ci) * 4096 + (16 * s + c) * 64;
 #pragma unroll
     for (int m = 0; m < 4; ++m) p.w[m] = *(const f32x4*)(src + scol(m, 4 * g));
     p.z = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
               rdz, (uint32_t)(tk(tok0(k), c) * 64 + 16 * s + 4 * g) * 4, 0, 0));
   };
+  // HOLD: W <- W + sgn G K^T over one tile in Wr's layout, with
+  // G = 2 (W0 K - V) D at the gradient point W0 (split w0a, w0b); kc: the
+  // K chunks of token c, vr / er: V[t = 4g + r][row 16s + c] and eta[4g + r];
+  // neg = 0x80008000 negates K (sgn = -1)
+  auto gk_update = [&](f32x4* W, const Split8& w0a, const Split8& w0b, const bf16x8* kc, f32x4 vr,
+                       f32x4 er, uint32_t neg) {
+    f32x4 Er = mfma_k32(kc[0], w0a.hi, f32x4{0, 0, 0, 0});  // (W0 K)[row c][t = 4g + r]
+    Er = mfma_k32(kc[0], w0a.lo, Er);
+    Er = mfma_k32(kc[1], w0b.hi, Er);
+    Er = mfma_k32(kc[1], w0b.lo, Er);
+    f32x4 Gr;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Gr[r] = 2.f * er[r] * (Er[r] - vr[r]);
+    const Split4 gs = split4(Gr);
+    const bf16x8 gb = cat44(gs.hi, gs.lo);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint2 k4 = pack4(mfma_k32(kc[m >> 1], sel[m & 1], f32x4{0, 0, 0, 0}));
+      const uint2 kx = make_uint2(k4.x ^ neg, k4.y ^ neg);
+      W[m] = mfma_k32(cat8(kx, kx), gb, W[m]);
+    }
+  };
+  // HOLD: W at the end of the next tile that outputs() takes
+  f32x4 Wrun[4];
+  if constexpr (HOLD) {
+    const float* src = a.w_ckpt + ((size_t)unit * nck + nck - 1) * 4096 + (16 * s + c) * 64;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) Wrun[m] = *(const f32x4*)(src + scol(m, 4 * g));
+    const Split8 w0a = split8(Wrun[0], Wrun[1]), w0b = split8(Wrun[2], Wrun[3]);
+    const unsigned short* kg = (const unsigned short*)a.k + uoff;
+    const unsigned short* vg = (const unsigned short*)a.v + uoff;
+    const float* eg = a.eta + (size_t)unit * T;
+    for (int jf = (nck - 1) * a.tpm; jf < ntiles; ++jf) {  // the last mini-batch's tiles
+      const int t0 = 16 * jf;
+      bf16x8 kc[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 x = t0 + c < T ? *(const uint4*)(kg + (size_t)(t0 + c) * 64 + 32 * h + 8 * g)
+                                   : make_uint4(0, 0, 0, 0);
+        kc[h] = __builtin_bit_cast(bf16x8, x);
+      }
+      f32x4 vr, er;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + 4 * g + r;
+        vr[r] = t < T ? __builtin_bit_cast(float, (uint32_t)vg[(size_t)t * 64 + 16 * s + c] << 16) : 0.f;
+        er[r] = t < T ? eg[t] : 0.f;
+      }
+      gk_update(Wrun, w0a, w0b, kc, vr, er, 0x80008000u);
+    }
+  }
   // partial sums over this slice's rows for tile p (iteration order)
   auto outputs = [&](int p, const Pf& pf) {
     const char* st = smem + (p % G::NST) * G::SLOT;
@@ -350,12 +435,15 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
     const char* ho = smem + G::HOB + ((p & 1) * 4 + s) * G::HO + lane * 16;
     const f32x4 Gn = *(const f32x4*)ho;
     uint2 BBh[4], BBl[4];
+    auto load_bb = [&] {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint4 b = *(const uint4*)(ho + (1 + m) * 1024);
-      BBh[m] = make_uint2(b.x, b.y);
-      BBl[m] = make_uint2(b.z, b.w);
-    }
+      for (int m = 0; m < 4; ++m) {
+        const uint4 b = *(const uint4*)(ho + (1 + m) * 1024);
+        BBh[m] = make_uint2(b.x, b.y);
+        BBl[m] = make_uint2(b.z, b.w);
+      }
+    };
+    if constexpr (!HOLD) load_bb();
     const bf16x8 kc[2] = {row_chunk(Kt, c, 0, g), row_chunk(Kt, c, 1, g)};
     const float et = Et[c];
     const Split4 zts = split4(pf.z);
@@ -376,6 +464,32 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
     }
     dp += __shfl_xor(dp, 16);
     dp += __shfl_xor(dp, 32);
+    char* rw = smem + G::RED + ((p & 1) * 4 + s) * G::RW;
+    if constexpr (HOLD) {  // dQ reads the running state W_t, rebuilt here
+      f32x4 vr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        vr[r] = __builtin_bit_cast(float, (uint32_t)*(const unsigned short*)(Vt + swz(4 * g + r, 16 * s + c))
+                                              << 16);
+      f32x4 Wt[4] = {Wrun[0], Wrun[1], Wrun[2], Wrun[3]};
+      gk_update(Wt, wa_0, wa_1, kc, vr, *(const f32x4*)(Et + 4 * g), 0u);
+      // a mini-batch start: the tile before it ends at the exact checkpoint;
+      // iterations outside the sequence (pf not loaded) leave Wrun alone
+      const int jf = ntiles - 1 - p;
+      const bool in = jf >= 0 && jf < ntiles, start = in && jf % a.tpm == 0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) Wrun[m] = start ? pf.w[m] : (in ? Wt[m] : Wrun[m]);
+      const Split8 wt_0 = split8(Wt[0], Wt[1]), wt_1 = split8(Wt[2], Wt[3]);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {  // register r = [t = 4g + r][col scol(m, c)]: W_t^T Zb
+        const uint2 qh = pack4(mfma_k32((m >> 1) ? wt_1.hi : wt_0.hi, sel[m & 1], f32x4{0, 0, 0, 0}));
+        const uint2 ql = pack4(mfma_k32((m >> 1) ? wt_1.lo : wt_0.lo, sel[m & 1], f32x4{0, 0, 0, 0}));
+        f32x4 dq = mfma_k32(cat44(zts.hi, zts.lo), cat8(qh, qh), f32x4{0, 0, 0, 0});
+        dq = mfma_k32(cat44(zts.hi, z4), cat8(ql, ql), dq);
+        *(f32x4*)(rw + (m * 64 + lane) * 16) = dq;
+      }
+    }
+    if constexpr (HOLD) load_bb();  // (late: fewer registers live across the rebuild)
     // W with columns in lanes: WB[m] register r = W[row 16s + 4g + r][scol(m, c)]
     uint2 WBh[4], WBl[4];
 #pragma unroll
@@ -383,18 +497,19 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
       WBh[m] = pack4(mfma_k32((m >> 1) ? wa_1.hi : wa_0.hi, sel[m & 1], f32x4{0, 0, 0, 0}));
       WBl[m] = pack4(mfma_k32((m >> 1) ? wa_1.lo : wa_0.lo, sel[m & 1], f32x4{0, 0, 0, 0}));
     }
-    char* rw = smem + G::RED + ((p & 1) * 4 + s) * G::RW;
     const Split4 gts = split4(Gtt), gws = split4(Gw);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       // register r = [t = 4g + r][col scol(m, c)]
-      f32x4 dq = mfma_k32(cat44(zts.hi, zts.lo), cat8(WBh[m], WBh[m]), f32x4{0, 0, 0, 0});
-      dq = mfma_k32(cat44(zts.hi, z4), cat8(WBl[m], WBl[m]), dq);  // W^T Zb
+      if constexpr (!HOLD) {
+        f32x4 dq = mfma_k32(cat44(zts.hi, zts.lo), cat8(WBh[m], WBh[m]), f32x4{0, 0, 0, 0});
+        dq = mfma_k32(cat44(zts.hi, z4), cat8(WBl[m], WBl[m]), dq);  // W^T Zb
+        *(f32x4*)(rw + (m * 64 + lane) * 16) = dq;
+      }
       f32x4 dk = mfma_k32(cat44(gts.hi, gts.lo), cat8(WBh[m], WBh[m]), f32x4{0, 0, 0, 0});
       dk = mfma_k32(cat44(gts.hi, z4), cat8(WBl[m], WBl[m]), dk);  // W^T Gt
       dk = mfma_k32(cat44(gws.hi, gws.lo), cat8(BBh[m], BBh[m]), dk);
       dk = mfma_k32(cat44(gws.hi, z4), cat8(BBl[m], BBl[m]), dk);  // + Wb'^T G
-      *(f32x4*)(rw + (m * 64 + lane) * 16) = dq;
       *(f32x4*)(rw + G::RQ + (m * 64 + lane) * 16) = -dk;
     }
     // G^T Zb: register r = sum_rows G[row][s' = 4g + r] Zb[row][t = c]
@@ -406,18 +521,34 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
 
   // Prefetch of tile p happens at iteration p - 1 (p = 0: before the loop),
   // its use at iteration p + 1; three register sets rotate by unrolling.
-  Pf pA, pB, pC;
-  pload(0, pA);
-  auto body = [&](int k, const Pf& pc, Pf& pn) {
-    pload(k + 1, pn);
-    wg_barrier();  // B_k: tile k in LDS; hand-over of tile k - 1 complete
-    outputs(k - 1, pc);
-    wait_lgkm0();  // the partials are in LDS before the next barrier
-  };
-  for (int k = 0; k < niter; k += 3) {
-    body(k, pC, pB);
-    if (k + 1 < niter) body(k + 1, pA, pC);
-    if (k + 2 < niter) body(k + 2, pB, pA);
+  // HOLD keeps the running state in registers as well and prefetches one
+  // iteration ahead instead, with two sets.
+  if constexpr (HOLD) {
+    Pf pA, pB;  // tile -1 (iteration 0) is never loaded: outputs() ignores it
+    auto body = [&](int k, const Pf& pc, Pf& pn) {
+      pload(k, pn);
+      wg_barrier();  // B_k: tile k in LDS; hand-over of tile k - 1 complete
+      outputs(k - 1, pc);
+      wait_lgkm0();  // the partials are in LDS before the next barrier
+    };
+    for (int k = 0; k < niter; k += 2) {
+      body(k, pB, pA);
+      if (k + 1 < niter) body(k + 1, pA, pB);
+    }
+  } else {
+    Pf pA, pB, pC;
+    pload(0, pA);
+    auto body = [&](int k, const Pf& pc, Pf& pn) {
+      pload(k + 1, pn);
+      wg_barrier();  // B_k: tile k in LDS; hand-over of tile k - 1 complete
+      outputs(k - 1, pc);
+      wait_lgkm0();  // the partials are in LDS before the next barrier
+    };
+    for (int k = 0; k < niter; k += 3) {
+      body(k, pC, pB);
+      if (k + 1 < niter) body(k + 1, pA, pC);
+      if (k + 2 < niter) body(k + 2, pB, pA);
+    }
   }
 }
 
@@ -485,7 +616,8 @@ __global__ void __launch_bounds__(256) chunk_adjoint_combine_kernel(const float*
 }  // namespace
 
 hipError_t launch_linear_bwd(const LinearBwdArgs& a, hipStream_t s) {
-  return launch(linear_bwd_kernel, dim3(a.units), dim3(BwdGeom::THREADS), s, a);
+  if (a.tpm > 1) return launch(linear_bwd_kernel<true>, dim3(a.units), dim3(BwdGeom::THREADS), s, a);
+  return launch(linear_bwd_kernel<false>, dim3(a.units), dim3(BwdGeom::THREADS), s, a);
 }
 
 hipError_t launch_linear_bwd_chunked(const LinearBwdArgs& a, int P, int rows, hipStream_t s) {

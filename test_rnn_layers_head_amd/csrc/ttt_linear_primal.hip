@@ -1,7 +1,7 @@
 // TTT-Linear training support in the primal form, one token at a time, in
-// fp32 arithmetic: the checkpointing forward and the backward for every
-// mini-batch size and for fp32 q/k/v.  (bf16 q/k/v with b = 16 take the
-// dual-form kernels of ttt_linear_bf16.hip / ttt_linear_bwd.hip.)
+// fp32 arithmetic: the checkpointing forward and the backward for fp32
+// q/k/v, every mini-batch size.  (bf16 q/k/v take the dual-form kernels of
+// ttt_linear_bf16.hip / ttt_linear_bwd.hip for every b.)
 //
 // Method ("论文速览 | TTT", equinox-blog close reading of "Learning to
 // (Learn at Test Time)"): f(x) = W x (§4.4), loss ||W k_t - v_t||^2 (§3.3),
@@ -45,15 +45,10 @@ __device__ __forceinline__ float quad_sum(float v) {
   v += __shfl_xor(v, 32);
   return v;
 }
-template <bool F32IN>
-__device__ __forceinline__ float ld(const void* p, size_t i) {
-  if constexpr (F32IN) return ((const float*)p)[i];
-  else return bf16_val(((const short*)p)[i]);
-}
+__device__ __forceinline__ float ld(const void* p, size_t i) { return ((const float*)p)[i]; }
 
 // The checkpointing forward: z, the final state, and the state before every
 // mini-batch, w_ckpt [units][ceil(T/b)][64][64].
-template <bool F32IN>
 __global__ void __launch_bounds__(LTHREADS) linear_primal_ckpt_kernel(LinearArgs a) {
   const int t = threadIdx.x, wv = t >> 6, l = t & 63;
   const int qd = l >> 4, il = l & 15;
@@ -78,14 +73,14 @@ __global__ void __launch_bounds__(LTHREADS) linear_primal_ckpt_kernel(LinearArgs
     const size_t o = base + (size_t)tt * 64;
     float p = 0.f;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) p = fmaf(wg[c], ld<F32IN>(a.k, o + j0 + c), p);
-    const float g = 2.f * (quad_sum(p) - ld<F32IN>(a.v, o + i));
+    for (int c = 0; c < 16; ++c) p = fmaf(wg[c], ld(a.k, o + j0 + c), p);
+    const float g = 2.f * (quad_sum(p) - ld(a.v, o + i));
     const float eg = -a.eta[(size_t)unit * T + tt] * g;
     float zq = 0.f;
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-      w[c] = fmaf(eg, ld<F32IN>(a.k, o + j0 + c), w[c]);
-      zq = fmaf(w[c], ld<F32IN>(a.q, o + j0 + c), zq);
+      w[c] = fmaf(eg, ld(a.k, o + j0 + c), w[c]);
+      zq = fmaf(w[c], ld(a.q, o + j0 + c), zq);
     }
     zq = quad_sum(zq);
     if (qd == 0) a.z[o + i] = zq;
@@ -95,7 +90,6 @@ __global__ void __launch_bounds__(LTHREADS) linear_primal_ckpt_kernel(LinearArgs
 }
 
 // The backward: per unit, from the checkpoints of the forward above.
-template <bool F32IN>
 __global__ void __launch_bounds__(LTHREADS) linear_primal_bwd_kernel(LinearPrimalBwdArgs a) {
   __shared__ float part[2][4][129];  // [step parity][wave][dq 0..63 | dk 64..127 | deta 128]
 
@@ -127,11 +121,11 @@ __global__ void __launch_bounds__(LTHREADS) linear_primal_bwd_kernel(LinearPrima
       const size_t o = base + (size_t)tt * 64;
       float p = 0.f;
 #pragma unroll
-      for (int c = 0; c < 16; ++c) p = fmaf(wg[c], ld<F32IN>(a.k, o + j0 + c), p);
-      const float g = 2.f * (quad_sum(p) - ld<F32IN>(a.v, o + i));
+      for (int c = 0; c < 16; ++c) p = fmaf(wg[c], ld(a.k, o + j0 + c), p);
+      const float g = 2.f * (quad_sum(p) - ld(a.v, o + i));
       const float eg = -a.eta[(size_t)unit * T + tt] * g;
 #pragma unroll
-      for (int c = 0; c < 16; ++c) w[c] = fmaf(eg, ld<F32IN>(a.k, o + j0 + c), w[c]);
+      for (int c = 0; c < 16; ++c) w[c] = fmaf(eg, ld(a.k, o + j0 + c), w[c]);
     }
     // take its tokens back
     for (int tt = m1 - 1; tt >= m0; --tt, ++n) {
@@ -140,14 +134,14 @@ __global__ void __launch_bounds__(LTHREADS) linear_primal_bwd_kernel(LinearPrima
       float kv[16], qv[16];
 #pragma unroll
       for (int c = 0; c < 16; ++c) {
-        kv[c] = ld<F32IN>(a.k, o + j0 + c);
-        qv[c] = ld<F32IN>(a.q, o + j0 + c);
+        kv[c] = ld(a.k, o + j0 + c);
+        qv[c] = ld(a.q, o + j0 + c);
       }
       const float dzi = a.dz[o + i];
       float p = 0.f;
 #pragma unroll
       for (int c = 0; c < 16; ++c) p = fmaf(wg[c], kv[c], p);
-      const float g = 2.f * (quad_sum(p) - ld<F32IN>(a.v, o + i));
+      const float g = 2.f * (quad_sum(p) - ld(a.v, o + i));
       // dq (column sums of W dz over the rows); then the output's adjoint
       float dqm = 0.f, ak = 0.f;
 #pragma unroll
@@ -200,14 +194,12 @@ __global__ void __launch_bounds__(LTHREADS) linear_primal_bwd_kernel(LinearPrima
 
 }  // namespace
 
-hipError_t launch_linear_primal_ckpt(const LinearArgs& a, bool f32in, hipStream_t s) {
-  if (f32in) return launch(linear_primal_ckpt_kernel<true>, dim3(a.units), dim3(LTHREADS), s, a);
-  return launch(linear_primal_ckpt_kernel<false>, dim3(a.units), dim3(LTHREADS), s, a);
+hipError_t launch_linear_primal_ckpt(const LinearArgs& a, hipStream_t s) {
+  return launch(linear_primal_ckpt_kernel, dim3(a.units), dim3(LTHREADS), s, a);
 }
 
-hipError_t launch_linear_primal_bwd(const LinearPrimalBwdArgs& a, bool f32in, hipStream_t s) {
-  if (f32in) return launch(linear_primal_bwd_kernel<true>, dim3(a.units), dim3(LTHREADS), s, a);
-  return launch(linear_primal_bwd_kernel<false>, dim3(a.units), dim3(LTHREADS), s, a);
+hipError_t launch_linear_primal_bwd(const LinearPrimalBwdArgs& a, hipStream_t s) {
+  return launch(linear_primal_bwd_kernel, dim3(a.units), dim3(LTHREADS), s, a);
 }
 
 }  // namespace ttt

@@ -116,11 +116,14 @@ def test_backward_empty_sequence_and_rejected_arguments():
 
 # ------------------------------------------------ any b, fp32 inputs
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("b", [1, 4, 16, 32, 64])
-@pytest.mark.parametrize("T", [1, 37, 130])
+@pytest.mark.parametrize("b", [1, 4, 16, 32, 48, 64])
+@pytest.mark.parametrize("T", [1, 37, 120, 130])
 def test_any_minibatch_checkpoints_and_backward(dtype, b, T):
     """bf16 with b < 16: the b = 16 dual-form kernels with one mini-batch per
-    zero-padded tile; b > 16 or fp32 q/k/v: the primal-form kernels.
+    zero-padded tile; bf16 with b > 16: the dual-form backward with the
+    gradient point held across b / 16 tiles (T = 120 ends in a mini-batch of
+    several tiles, T = 130 in one of a single ragged tile); fp32 q/k/v: the
+    primal-form kernels.
     Checkpoints (one per mini-batch) against the oracle's states, then every
     gradient against the oracle backward, with dW_T given."""
     if dtype == "bf16" and b == 16:
@@ -154,8 +157,9 @@ def test_any_minibatch_checkpoints_and_backward(dtype, b, T):
 @pytest.mark.parametrize("b", [1, 4, 64])
 def test_backward_1p3b_workload_any_minibatch_sampled_units(b):
     """The 1.3B workload with b in {1, 4} (the dual-form kernels on padded
-    tiles) and 64 (the primal form): 16 units spread over the batch and heads
-    against the oracle backward."""
+    tiles) and 64 (the dual form with the gradient point held across four
+    tiles): 16 units spread over the batch and heads against the oracle
+    backward."""
     x = inputs.make_inputs(3)
     rng = np.random.default_rng(770 + b)
     dz = (rng.standard_normal(x.q.shape) * 0.1).astype(np.float32)
