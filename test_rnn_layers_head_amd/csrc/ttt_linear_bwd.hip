@@ -448,24 +448,8 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
     const float et = Et[c];
     const Split4 zts = split4(pf.z);
     const Split8 wa_0 = split8(pf.w[0], pf.w[1]), wa_1 = split8(pf.w[2], pf.w[3]);
-    f32x4 Ew = mfma_k32(wa_0.hi, kc[0], f32x4{0, 0, 0, 0});
-    Ew = mfma_k32(wa_0.lo, kc[0], Ew);
-    Ew = mfma_k32(wa_1.hi, kc[1], Ew);
-    Ew = mfma_k32(wa_1.lo, kc[1], Ew);
-    const f32x4 vv = bf4(*(const uint2*)(Vt + swz(c, 16 * s + 4 * g)));
-    f32x4 Gtt, Gw;
-    float dp = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float e = Ew[r] - vv[r];
-      Gtt[r] = 2.f * et * Gn[r];
-      Gw[r] = 2.f * et * e;
-      dp -= Gn[r] * 2.f * e;
-    }
-    dp += __shfl_xor(dp, 16);
-    dp += __shfl_xor(dp, 32);
-    char* rw = smem + G::RED + ((p & 1) * 4 + s) * G::RW;
     if constexpr (HOLD) {  // dQ reads the running state W_t, rebuilt here
+      char* rw = smem + G::RED + ((p & 1) * 4 + s) * G::RW;
       f32x4 vr;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -489,6 +473,23 @@ __global__ void __launch_bounds__(BwdGeom::THREADS) linear_bwd_kernel(LinearBwdA
         *(f32x4*)(rw + (m * 64 + lane) * 16) = dq;
       }
     }
+    f32x4 Ew = mfma_k32(wa_0.hi, kc[0], f32x4{0, 0, 0, 0});
+    Ew = mfma_k32(wa_0.lo, kc[0], Ew);
+    Ew = mfma_k32(wa_1.hi, kc[1], Ew);
+    Ew = mfma_k32(wa_1.lo, kc[1], Ew);
+    const f32x4 vv = bf4(*(const uint2*)(Vt + swz(c, 16 * s + 4 * g)));
+    f32x4 Gtt, Gw;
+    float dp = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float e = Ew[r] - vv[r];
+      Gtt[r] = 2.f * et * Gn[r];
+      Gw[r] = 2.f * et * e;
+      dp -= Gn[r] * 2.f * e;
+    }
+    dp += __shfl_xor(dp, 16);
+    dp += __shfl_xor(dp, 32);
+    char* rw = smem + G::RED + ((p & 1) * 4 + s) * G::RW;
     if constexpr (HOLD) load_bb();  // (late: fewer registers live across the rebuild)
     // W with columns in lanes: WB[m] register r = W[row 16s + 4g + r][scol(m, c)]
     uint2 WBh[4], WBl[4];
